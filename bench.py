@@ -1,0 +1,185 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+A step is one kda_chunk_fwd call (intra-chunk stage + chain stage) over the mid
+prefill workload: B=4, H=16, T=8192, d_k=d_v=128, C=64, bf16 q/k/v, fp32 g/beta
+and state, per-channel gates (seeded synthetic inputs, resident in HBM before
+timing).  Prints one JSON line.  The decode step (256 sequences x 32 heads,
+in-place 128x128 fp32 states) is measured as well and reported under "decode".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="mid")
+    p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    return p.parse_args()
+
+
+def prefill_bytes_per_token_head(dk, dv, in_bytes, out_bytes):
+    """Bytes the method has to move per (token, head): q, k, v in, g, beta in, o out."""
+    return (2 * dk + dv) * in_bytes + dk * 4 + 4 + dv * out_bytes
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_sequence_chunk_amd import ChunkPlan, decode_step, inputs
+
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    d = inputs.make_prefill(w)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in d.items()}
+    plan = ChunkPlan(g["q"], g["k"], g["v"], g["g"], g["beta"], g["S0"], chunk_size=w.C)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_host0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        plan.intra()
+        ev[i][1].record(stream)
+        plan.chain()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    intra_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    chain_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_per_step = sum(step_ms) / K
+    tokens = w.B * w.T
+    value = tokens / (ms_per_step / 1e3)
+
+    units = w.B * w.T * w.H                          # token-heads per launch
+    ib = 2 if w.dtype == "bf16" else 4
+    state_bytes = w.B * w.H * w.dk * w.dv * 4
+    intra_alg = units * ((2 * w.dk + w.dv) * ib + w.dk * 4 + 4)
+    chain_alg = units * (w.dv * ib) + (2 if g["S0"] is not None else 1) * state_bytes
+    step_alg = intra_alg + chain_alg
+    t_intra = sum(intra_ms) / K / 1e3
+    t_chain = sum(chain_ms) / K / 1e3
+    dom = ("chunk_intra_kernel", intra_alg, t_intra) if t_intra >= t_chain else \
+          ("chunk_chain_kernel", chain_alg, t_chain)
+    achieved = dom[1] / dom[2] / 1e9
+    roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None}
+
+    out = {
+        "metric": "KDA chunked-prefill tokens/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the mid prefill workload)",
+        "config": {"workload": f"mid prefill B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} C={w.C} "
+                               f"bf16 q/k/v, fp32 g/beta/state, channel gates",
+                   "global_batch": w.B, "seq_len": w.T, "heads": w.H, "chunk": w.C,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "path": {"step_alg_bytes": step_alg, "step_alg_GBps": round(step_alg / (ms_per_step / 1e3) / 1e9, 1),
+                 "step_frac_hbm": round(step_alg / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "intra_ms": round(t_intra * 1e3, 4), "chain_ms": round(t_chain * 1e3, 4),
+                 "host_wall_ms_per_step": round(t_host / K * 1e3, 4)},
+    }
+
+    if not args.no_decode:
+        out["decode"] = bench_decode(torch, inputs, decode_step, dev, args.decode_steps)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, w)
+
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(torch, inputs, decode_step, dev, steps):
+    """Decode: 256 sequences x 32 heads, in-place fp32 states; a pool of 16
+    input sets is cycled (the kernel has no data-dependent control flow)."""
+    wd = inputs.WORKLOADS["decode"]
+    S = inputs.decode_state(wd).to(dev)
+    pool = inputs.make_decode_steps(wd, 16)
+    pool = {k: v.to(dev) for k, v in pool.items()}
+    o = torch.empty((wd.B, wd.H, wd.dv), dtype=torch.bfloat16, device=dev)
+    for i in range(5):
+        decode_step(pool["q"][i], pool["k"][i], pool["v"][i], pool["g"][i], pool["beta"][i], S, o=o)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        j = i % 16
+        decode_step(pool["q"][j], pool["k"][j], pool["v"][j], pool["g"][j], pool["beta"][j], S, o=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    nh = wd.B * wd.H
+    byts = nh * (2 * wd.dk * wd.dv * 4 + (2 * wd.dk + wd.dv) * 2 + wd.dk * 4 + 4 + wd.dv * 2)
+    gbs = byts / t / 1e9
+    return {"metric": "decode step state GB/s", "GBps": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "us_per_step": round(t * 1e6, 2),
+            "tokens_per_s": round(wd.B / t, 1), "bytes_per_step": byts, "steps": steps,
+            "config": "256 sequences x 32 heads, dk=dv=128, bf16 q/k/v, fp32 state in place"}
+
+
+def cpu_baseline(d, w):
+    """The fp64 oracle (as it stands) on the same workload's inputs, timed on the
+    host cores; sample = the first H_s heads of every batch row, whole sequence."""
+    import numpy as np
+
+    import oracle
+
+    threads = min(os.cpu_count() or 1, 16)
+    hs = max(1, min(w.H, (2 * threads) // w.B))
+    sel = lambda x: x[:, :, :hs]
+    args = [oracle.to_f64(sel(d[k])) for k in ("q", "k", "v", "g", "beta")]
+    oracle._lib()
+    t0 = time.perf_counter()
+    oracle.recurrent(*args, S0=None if d["S0"] is None else oracle.to_f64(d["S0"][:, :hs]),
+                     nthreads=threads)
+    dt = time.perf_counter() - t0
+    used = oracle.last_threads()
+    frac = hs / w.H
+    return {"value": round(w.B * w.T * frac / dt, 1), "unit": "tokens/s", "cores": min(used, w.B * hs),
+            "threads": used, "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{w.B}x{hs} of {w.B}x{w.H} (batch x head) sequences, all {w.T} tokens; "
+                      f"tokens/s scaled to the whole workload"}
+
+
+if __name__ == "__main__":
+    main()

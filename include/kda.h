@@ -1,0 +1,154 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) / gated delta-rule
+ * state update on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   Per (batch b, head h) a d_k x d_v state S is kept; key channels index rows,
+ *   value channels index columns.  For each token t, in the order given in
+ *   section 八 of "我终于看懂了 KDA：百万 Token 的关键，不是记得更多，而是会修改记忆":
+ *     decay   S' = Diag(alpha_t) S, alpha_t = exp(g_t) per key channel
+ *             (per-channel gate: Kimi Linear paragraph of
+ *             "一个KimiK3装下22580个GPT-2，七年缩放真正改变的是记忆与检索");
+ *     read    r  = S'^T k_t                 (delta rule: section 六 of the
+ *     error   u  = beta_t (v_t - r)          explainer and the delta-rule
+ *     write   S  = S' + k_t u^T              paragraph of the KimiK3 essay)
+ *     output  o_t = S^T q_t                 (read after the token's own write)
+ *   kda_chunk_fwd evaluates this over a whole sequence with the chunkwise form
+ *   (chunk paragraph of the KimiK3 essay; sections 十六 and 十七 of the
+ *   explainer: recurrence between chunks, parallel work inside a chunk, the
+ *   chunk's rank-1 updates folded into matrix products).  kda_decode_step is the
+ *   single-token step of section 十五 (read state, compute output, update state).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     keeps no pointer after the call returns and allocates nothing.
+ *   - Layouts are contiguous row-major.  Sequence tensors are [B,T,H,d];
+ *     states are [B,H,dk,dv] with dv fastest.
+ *   - q, k, v have dtype in_dtype; o has dtype out_dtype; g, beta and every
+ *     state are fp32.  g is the log-gate: g <= 0, -inf allowed (alpha = 0).
+ *     g > 0 (alpha > 1) is outside the method's domain; results are unspecified.
+ *     NaN/Inf inputs propagate; nothing is checked on the device.
+ *   - Supported: dk, dv in {64, 128}; chunk size C in {16, 32, 64, 128}; any
+ *     T >= 0 (a last partial chunk is allowed); B, H >= 0.
+ *   - All pointers must be 16-byte aligned.
+ *   - Validation happens on the host before any HIP call; on error nothing is
+ *     launched and nothing is written.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; the return value only reports validation and launch
+ *     errors.  Setting KDA_DEBUG_SYNC=1 in the environment makes each call
+ *     synchronise the stream and report execution errors too.
+ *   - Stateless and re-entrant; concurrent calls on different streams with
+ *     disjoint outputs and workspaces are safe.  Identical inputs give
+ *     bitwise-identical outputs (no floating-point atomics).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    KDA_ERR_SHAPE = 2,       /* a size is negative or inconsistent               */
+    KDA_ERR_UNSUPPORTED = 3, /* dk, dv, C or a dtype outside the supported set   */
+    KDA_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned                 */
+    KDA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+    KDA_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap   */
+    KDA_ERR_HIP = 7          /* no usable device, or a HIP launch/execution error */
+} kda_status_t;
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *kda_status_string(int status);
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if the
+ * sizes are unsupported).  Host-only; never touches the device. */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                     int in_dtype, int C);
+
+/*
+ * kda_chunk_fwd -- chunkwise-parallel forward over a whole sequence.
+ *   q, k          [B,T,H,dk] in_dtype         queries, keys (not normalised here)
+ *   v             [B,T,H,dv] in_dtype         values
+ *   g             [B,T,H,dk] fp32             log-gate per key channel
+ *   beta          [B,T,H]    fp32             write strength (learning rate)
+ *   initial_state [B,H,dk,dv] fp32 or NULL    NULL means zeros
+ *   o             [B,T,H,dv] out_dtype        outputs o_t = S_t^T q_t
+ *   final_state   [B,H,dk,dv] fp32 or NULL    state after token T-1; may be the
+ *                                             same pointer as initial_state
+ *                                             (updated in place)
+ *   workspace     device buffer of >= kda_chunk_fwd_workspace_bytes(...) bytes
+ *   C             chunk size (tokens per chunk)
+ * o must not overlap any other argument; final_state may equal initial_state
+ * but not partially overlap it or any other argument.
+ * Intermediate values use bf16 MFMA operands with fp32 accumulation when
+ * in_dtype is BF16, fp32 MFMA operands when in_dtype is F32; the state is
+ * carried in fp32.  Log-gates below -20 are treated as -20 (alpha >= 2e-9).
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v,
+                  const float *g, const float *beta,
+                  const float *initial_state,
+                  void *o, float *final_state,
+                  int B, int T, int H, int dk, int dv,
+                  int in_dtype, int out_dtype,
+                  void *workspace, size_t workspace_bytes,
+                  void *stream, int C);
+
+/*
+ * The two stages kda_chunk_fwd runs, exposed so that callers can schedule or
+ * time them separately.  Same arguments and rules as kda_chunk_fwd.
+ *   kda_chunk_intra: everything that does not depend on the carried state
+ *     (gate prefix sums, decayed operands, the intra-chunk score matrices and
+ *     the triangular solve), for all chunks in parallel, into the workspace.
+ *     Reads q, k, v, g, beta; writes only the workspace.
+ *   kda_chunk_chain: the sequential state recurrence across chunks and the
+ *     outputs.  Reads the workspace and initial_state; writes o and final_state.
+ * kda_chunk_chain must run after kda_chunk_intra on the same workspace with the
+ * same sizes (stream order suffices).
+ */
+int kda_chunk_intra(const void *q, const void *k, const void *v,
+                    const float *g, const float *beta,
+                    const float *initial_state,
+                    void *o, float *final_state,
+                    int B, int T, int H, int dk, int dv,
+                    int in_dtype, int out_dtype,
+                    void *workspace, size_t workspace_bytes,
+                    void *stream, int C);
+int kda_chunk_chain(const void *q, const void *k, const void *v,
+                    const float *g, const float *beta,
+                    const float *initial_state,
+                    void *o, float *final_state,
+                    int B, int T, int H, int dk, int dv,
+                    int in_dtype, int out_dtype,
+                    void *workspace, size_t workspace_bytes,
+                    void *stream, int C);
+
+/*
+ * kda_decode_step -- one token per sequence, state updated IN PLACE.
+ *   q, k   [N,H,dk] in_dtype;  v [N,H,dv] in_dtype
+ *   g      [N,H,dk] fp32 log-gate;  beta [N,H] fp32
+ *   state  [N,H,dk,dv] fp32, read and overwritten with the new state
+ *   o      [N,H,dv] out_dtype
+ * Each state element is read once and written once.  o must not overlap any
+ * other argument; state must not overlap the inputs.
+ */
+int kda_decode_step(const void *q, const void *k, const void *v,
+                    const float *g, const float *beta,
+                    float *state, void *o,
+                    int N, int H, int dk, int dv,
+                    int in_dtype, int out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

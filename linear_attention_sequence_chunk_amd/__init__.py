@@ -1,2 +1,7 @@
 """libkda: MI355X (gfx950) kernels for the Kimi Delta Attention / gated delta-rule
-state update, behind a C ABI (include/kda.h) with a thin ctypes binding."""
+state update, behind a C ABI (include/kda.h) with a thin ctypes binding.
+
+    from linear_attention_sequence_chunk_amd import chunk_fwd, decode_step
+"""
+from .api import ChunkPlan, chunk_fwd, decode_step, workspace_bytes  # noqa: F401
+from ._lib import KdaError  # noqa: F401

@@ -1,0 +1,61 @@
+"""ctypes loader for libkda.so (the C ABI declared in include/kda.h).
+
+The library is built in-tree by ``__graft_entry__.build()``; there is no fallback:
+if it is missing every call raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
+
+F32, BF16 = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
+          4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP"}
+
+# Every entry point include/kda.h declares.
+SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
+           "kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain", "kda_decode_step")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_LIB = None
+_vp, _ci, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_CHUNK_ARGS = [_vp] * 8 + [_ci] * 7 + [_vp, _sz, _vp, _ci]
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kda_abi_version.argtypes, L.kda_abi_version.restype = [], _ci
+        L.kda_status_string.argtypes, L.kda_status_string.restype = [_ci], ctypes.c_char_p
+        L.kda_chunk_fwd_workspace_bytes.argtypes = [_ci] * 7
+        L.kda_chunk_fwd_workspace_bytes.restype = _sz
+        for name in ("kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain"):
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = _CHUNK_ARGS, _ci
+        L.kda_decode_step.argtypes = [_vp] * 7 + [_ci] * 6 + [_vp]
+        L.kda_decode_step.restype = _ci
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().kda_status_string(int(status)).decode()
+    except RuntimeError:
+        return "?"
+
+
+def check(status: int, where: str) -> None:
+    if status != 0:
+        raise KdaError(status, where)

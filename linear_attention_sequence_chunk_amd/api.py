@@ -1,0 +1,137 @@
+"""Thin torch binding over the C ABI: argument checks and marshalling only.
+Every step of the computation runs in the HIP kernels of libkda.so."""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def _code(dtype) -> int:
+    if dtype not in _DT:
+        raise TypeError(f"unsupported dtype {dtype}; use float32 or bfloat16")
+    return _DT[dtype]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(B, T, H, dk, dv, in_dtype, chunk_size) -> int:
+    return int(_lib.lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _code(in_dtype), chunk_size))
+
+
+def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_state, workspace):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    _check_tensor("q", q, (B, T, H, dk), q.dtype, dev)
+    _check_tensor("k", k, (B, T, H, dk), q.dtype, dev)
+    _check_tensor("v", v, (B, T, H, dv), q.dtype, dev)
+    _check_tensor("g", g, (B, T, H, dk), torch.float32, dev)
+    _check_tensor("beta", beta, (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("final_state", final_state, (B, H, dk, dv), torch.float32, dev)
+    nbytes = workspace_bytes(B, T, H, dk, dv, q.dtype, chunk_size)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    return (B, T, H, dk, dv, out_dtype, o, final_state, workspace)
+
+
+def _call_chunk(fn_name, q, k, v, g, beta, initial_state, o, final_state, B, T, H, dk, dv,
+                out_dtype, workspace, chunk_size, stream):
+    fn = getattr(_lib.lib(), fn_name)
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+            _ptr(final_state), B, T, H, dk, dv, _code(q.dtype), _code(out_dtype),
+            _ptr(workspace), workspace.numel(), _stream(stream), chunk_size)
+    _lib.check(st, fn_name)
+
+
+def chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None,
+              final_state=None, workspace=None, stream=None):
+    """Chunkwise KDA forward (kda_chunk_fwd).  q,k [B,T,H,dk], v [B,T,H,dv] in
+    fp32 or bf16; g [B,T,H,dk] and beta [B,T,H] fp32; initial_state [B,H,dk,dv]
+    fp32 or None.  Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32).
+    ``final_state`` may be given (e.g. the initial_state tensor, for in place)."""
+    B, T, H, dk, dv, out_dtype, o, fs, ws = _prep_chunk(q, k, v, g, beta, initial_state,
+                                                        chunk_size, out_dtype, final_state, workspace)
+    _call_chunk("kda_chunk_fwd", q, k, v, g, beta, initial_state, o, fs, B, T, H, dk, dv,
+                out_dtype, ws, chunk_size, stream)
+    return o, fs
+
+
+class ChunkPlan:
+    """Pre-allocated outputs and workspace for repeated kda_chunk_fwd calls on the
+    same sizes; ``run`` calls both stages, ``intra``/``chain`` one each."""
+
+    def __init__(self, q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None):
+        self.args = (q, k, v, g, beta, initial_state)
+        self.chunk_size = chunk_size
+        (self.B, self.T, self.H, self.dk, self.dv, self.out_dtype, self.o, self.final_state,
+         self.workspace) = _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, None, None)
+
+    def _go(self, name, stream=None):
+        q, k, v, g, beta, s0 = self.args
+        _call_chunk(name, q, k, v, g, beta, s0, self.o, self.final_state, self.B, self.T, self.H,
+                    self.dk, self.dv, self.out_dtype, self.workspace, self.chunk_size, stream)
+
+    def run(self, stream=None):
+        self._go("kda_chunk_fwd", stream)
+        return self.o, self.final_state
+
+    def intra(self, stream=None):
+        self._go("kda_chunk_intra", stream)
+
+    def chain(self, stream=None):
+        self._go("kda_chunk_chain", stream)
+
+
+def decode_step(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None):
+    """One decode step (kda_decode_step).  q,k [N,H,dk], v [N,H,dv]; g [N,H,dk],
+    beta [N,H] fp32; state [N,H,dk,dv] fp32 is updated in place.  Returns o."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    _check_tensor("k", k, (N, H, dk), q.dtype, dev)
+    _check_tensor("v", v, (N, H, dv), q.dtype, dev)
+    _check_tensor("g", g, (N, H, dk), torch.float32, dev)
+    _check_tensor("beta", beta, (N, H), torch.float32, dev)
+    _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    st = _lib.lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                    _ptr(o), N, H, dk, dv, _code(q.dtype), _code(out_dtype),
+                                    _stream(stream))
+    _lib.check(st, "kda_decode_step")
+    return o

@@ -1,0 +1,224 @@
+// kda_api.cpp -- the C ABI of libkda: argument validation (host only, before any
+// HIP call), dispatch to the kernels, status codes.  See include/kda.h.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;                 // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t a = (uintptr_t)p;
+    return Range{a, p ? a + bytes : a};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool debug_sync() {
+    static int cached = -1;
+    if (cached < 0) {
+        const char* e = getenv("KDA_DEBUG_SYNC");
+        cached = (e && e[0] && e[0] != '0') ? 1 : 0;
+    }
+    return cached == 1;
+}
+
+int device_ready() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+int finish(hipError_t e, hipStream_t s) {
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    if (debug_sync()) {
+        if (hipStreamSynchronize(s) != hipSuccess) return KDA_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+__global__ void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst, long n) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+struct ChunkCall {
+    const void *q, *k, *v;
+    const float *g, *beta, *s0;
+    void* o;
+    float* sT;
+    int B, T, H, dk, dv, in_dtype, out_dtype;
+    void* ws;
+    size_t ws_bytes;
+    void* stream;
+    int C;
+};
+
+bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
+size_t esize(int d) { return d == KDA_BF16 ? 2 : 4; }
+
+int validate_chunk(const ChunkCall& c) {
+    if (c.B < 0 || c.T < 0 || c.H < 0) return KDA_ERR_SHAPE;
+    if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if ((c.dk != 64 && c.dk != 128) || (c.dv != 64 && c.dv != 128)) return KDA_ERR_UNSUPPORTED;
+    if (c.C != 16 && c.C != 32 && c.C != 64 && c.C != 128) return KDA_ERR_UNSUPPORTED;
+    if (!kda::chunk_supported(c.dk, c.dv, c.C, c.in_dtype == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+
+    const size_t tok = (size_t)c.B * c.T * c.H;
+    const size_t nst = (size_t)c.B * c.H * c.dk * c.dv;
+    if (tok > 0 && (!c.q || !c.k || !c.v || !c.g || !c.beta || !c.o)) return KDA_ERR_NULL;
+
+    const void* ptrs[9] = {c.q, c.k, c.v, c.g, c.beta, c.s0, c.o, c.sT, c.ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+
+    const size_t need = kda::ws_layout(c.B, c.T, c.H, c.dk, c.dv, c.in_dtype == KDA_BF16, c.C).total;
+    if (tok > 0 && (!c.ws || c.ws_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    const size_t ei = esize(c.in_dtype), eo = esize(c.out_dtype);
+    const Range rq = range_of(c.q, tok * c.dk * ei), rk = range_of(c.k, tok * c.dk * ei),
+                rv = range_of(c.v, tok * c.dv * ei), rg = range_of(c.g, tok * c.dk * 4),
+                rb = range_of(c.beta, tok * 4), rs0 = range_of(c.s0, nst * 4),
+                ro = range_of(c.o, tok * c.dv * eo), rsT = range_of(c.sT, nst * 4),
+                rw = range_of(c.ws, tok > 0 ? need : 0);
+    const Range others_o[] = {rq, rk, rv, rg, rb, rs0, rsT, rw};
+    for (const Range& r : others_o)
+        if (overlap(ro, r)) return KDA_ERR_ALIAS;
+    const Range others_s[] = {rq, rk, rv, rg, rb, rw};
+    for (const Range& r : others_s)
+        if (overlap(rsT, r)) return KDA_ERR_ALIAS;
+    if (c.sT && c.s0 && c.sT != c.s0 && overlap(rsT, rs0)) return KDA_ERR_ALIAS;
+    const Range others_w[] = {rq, rk, rv, rg, rb, rs0};
+    for (const Range& r : others_w)
+        if (overlap(rw, r)) return KDA_ERR_ALIAS;
+    return KDA_OK;
+}
+
+kda::ChunkArgs to_args(const ChunkCall& c) {
+    kda::ChunkArgs a;
+    a.q = c.q; a.k = c.k; a.v = c.v; a.g = c.g; a.beta = c.beta;
+    a.s0 = c.s0; a.o = c.o; a.sT = c.sT;
+    a.B = c.B; a.T = c.T; a.H = c.H; a.dk = c.dk; a.dv = c.dv; a.C = c.C;
+    a.in_bf16 = c.in_dtype == KDA_BF16; a.out_bf16 = c.out_dtype == KDA_BF16;
+    a.ws = c.ws; a.ws_bytes = c.ws_bytes;
+    a.stream = (hipStream_t)c.stream;
+    return a;
+}
+
+enum Stages { STAGE_INTRA = 1, STAGE_CHAIN = 2 };
+
+int run_chunk(const ChunkCall& c, int stages) {
+    int st = validate_chunk(c);
+    if (st != KDA_OK) return st;
+    st = device_ready();
+    if (st != KDA_OK) return st;
+    const kda::ChunkArgs a = to_args(c);
+    const long nstate = (long)c.B * c.H * c.dk * c.dv;
+    if ((long)c.B * c.H == 0) return KDA_OK;
+    if (c.T == 0) {
+        // Empty sequence: the final state is the initial state (or zeros).
+        if ((stages & STAGE_CHAIN) && c.sT && c.sT != c.s0) {
+            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0,
+                               a.stream, c.s0, c.sT, nstate);
+            return finish(hipGetLastError(), a.stream);
+        }
+        return KDA_OK;
+    }
+    if (stages & STAGE_INTRA) {
+        hipError_t e = kda::run_chunk_intra(a);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (stages & STAGE_CHAIN) {
+        hipError_t e = kda::run_chunk_chain(a);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+    }
+    return finish(hipSuccess, a.stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "a size is negative or inconsistent";
+        case KDA_ERR_UNSUPPORTED: return "unsupported dk, dv, chunk size or dtype";
+        case KDA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_ALIAS: return "an output overlaps an argument it may not overlap";
+        case KDA_ERR_HIP: return "no usable HIP device, or a HIP launch/execution error";
+        default: return "unknown status";
+    }
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C) {
+    if (B < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
+    if (C != 16 && C != 32 && C != 64 && C != 128) return 0;
+    if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
+    return kda::ws_layout(B, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
+}
+
+#define KDA_CHUNK_PARAMS                                                                    \
+    const void *q, const void *k, const void *v, const float *g, const float *beta,         \
+        const float *initial_state, void *o, float *final_state, int B, int T, int H, int dk, \
+        int dv, int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes,        \
+        void *stream, int C
+#define KDA_CHUNK_CALL                                                                      \
+    ChunkCall { q, k, v, g, beta, initial_state, o, final_state, B, T, H, dk, dv, in_dtype,  \
+                out_dtype, workspace, workspace_bytes, stream, C }
+
+int kda_chunk_fwd(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL, STAGE_INTRA | STAGE_CHAIN); }
+int kda_chunk_intra(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL, STAGE_INTRA); }
+int kda_chunk_chain(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL, STAGE_CHAIN); }
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    float* state, void* o, int N, int H, int dk, int dv, int in_dtype, int out_dtype,
+                    void* stream) {
+    if (N < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
+    const size_t nh = (size_t)N * H;
+    if (nh == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    const void* ptrs[7] = {q, k, v, g, beta, state, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    const size_t ei = esize(in_dtype), eo = esize(out_dtype);
+    const Range rq = range_of(q, nh * dk * ei), rk = range_of(k, nh * dk * ei),
+                rv = range_of(v, nh * dv * ei), rg = range_of(g, nh * dk * 4), rb = range_of(beta, nh * 4),
+                rs = range_of(state, nh * dk * dv * 4), ro = range_of(o, nh * dv * eo);
+    const Range in[] = {rq, rk, rv, rg, rb};
+    for (const Range& r : in)
+        if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
+    if (overlap(ro, rs)) return KDA_ERR_ALIAS;
+
+    int st = device_ready();
+    if (st != KDA_OK) return st;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+    a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.stream = (hipStream_t)stream;
+    return finish(kda::run_decode_step(a), a.stream);
+}
+
+}  // extern "C"

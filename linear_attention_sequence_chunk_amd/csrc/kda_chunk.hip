@@ -1,0 +1,791 @@
+// kda_chunk.hip -- chunkwise-parallel KDA forward on gfx950: two stages.
+//
+// The chunkwise form (chunk paragraph of "一个KimiK3装下22580个GPT-2…";
+// sections 十六 and 十七 of "我终于看懂了 KDA…"): the sequence is cut into chunks
+// of C tokens; inside a chunk the work is parallel (masked attention scores and
+// the chunk's rank-1 updates folded into matrix products, the WY / DPLR view),
+// across chunks the state is carried sequentially.  For a chunk with local
+// positions r, i, start state S and per-channel log-gate prefix sums G:
+//
+//   A_ri = sum_c k_rc k_ic e^{G_rc - G_ic} (i < r)     P_ri = sum_c q_rc k_ic e^{G_rc - G_ic} (i <= r)
+//   T    = (I + Diag(beta) A)^-1
+//   U    = T Diag(beta) V          Wk = T Diag(beta) (e^G * K)
+//   W    = U - Wk S                (row r is the token's correction u_r)
+//   O    = (e^G * Q) S + P W
+//   S   <- Diag(e^{G_last}) S + (e^{G_last - G} * K)^T W
+//
+// Stage 1 (chunk_intra_kernel, one workgroup per (b, h, chunk), all chunks in
+// parallel) computes everything that does not depend on S into a workspace:
+// Qt = e^G*Q, Wk, Kb = e^{G_last-G}*K, P, U and gam = e^{G_last}.
+// Stage 2 (chunk_chain_kernel, one workgroup per (b, h, value-column slice))
+// walks the chunks in order with the fp32 state in MFMA accumulators.
+//
+// Exponent safety.  e^{G_r - G_i} is never formed as e^{G_r} * e^{-G_i} across a
+// whole chunk (the chunk sum of log-gates can pass -88, where e^{-G} overflows
+// fp32).  The chunk is split into 16-token sub-blocks; a pair of sub-blocks
+// (R, I), I < R, is handled at the level of the binary split where they separate,
+// with the split point m as reference: the row factor e^{G_r - G_{m-1}} and the
+// column factor e^{G_{m-1} - G_i} are both <= 1.  Diagonal sub-blocks use the
+// block start as reference; this is exact as long as the block's own log-gate sum
+// stays above -SAFE_SPAN, otherwise that block is computed term by term.
+// Prefix sums are kept block-local (16 tokens) so that exponent differences do
+// not lose digits to a large running sum.
+#include <utility>
+
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+// ------------------------------------------------------------ compile-time helpers
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+// Lower-triangular sub-block pairs (R, I), I <= R, enumerated p = R(R+1)/2 + I.
+constexpr int pair_R(int p) { int R = 0; while ((R + 1) * (R + 2) / 2 <= p) ++R; return R; }
+constexpr int pair_I(int p) { return p - pair_R(p) * (pair_R(p) + 1) / 2; }
+// Segment length (tokens) of the binary split that separates R and I; 0 = diagonal.
+constexpr int pair_level(int p) { return pair_R(p) == pair_I(p) ? 0 : 32 << ilog2(pair_R(p) ^ pair_I(p)); }
+constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr size_t smax(size_t a, size_t b) { return a > b ? a : b; }
+
+constexpr size_t LDS_LIMIT = 160 * 1024;
+
+// Two accumulators sharing the B operand: acc1 += A1 B, acc2 += A2 B.
+template <typename T>
+__device__ inline void mma_tile2(floatx4& acc1, floatx4& acc2, const T* __restrict__ a1,
+                                 const T* __restrict__ a2, int lda, const T* __restrict__ bt,
+                                 int ldb, int K, int lane) {
+    typedef typename Mma<T>::frag frag;
+    const int r = lane & 15, kg = lane >> 4;
+    const int oa = r * lda + kg * Mma<T>::KPL, ob = r * ldb + kg * Mma<T>::KPL;
+    for (int k0 = 0; k0 < K; k0 += Mma<T>::KSTEP) {
+        frag fb = *reinterpret_cast<const frag*>(bt + ob + k0);
+        frag f1 = *reinterpret_cast<const frag*>(a1 + oa + k0);
+        frag f2 = *reinterpret_cast<const frag*>(a2 + oa + k0);
+        acc1 = Mma<T>::mma(f1, fb, acc1);
+        acc2 = Mma<T>::mma(f2, fb, acc2);
+    }
+}
+
+// fp32 MFMA with both operands stored row-major: A[row][k], B[k][col].
+__device__ inline floatx4 mma_f32_rowB(floatx4 acc, const float* a, int lda, const float* b,
+                                       int ldb, int K, int lane) {
+    const int r = lane & 15, kg = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * lda + k0 + kg], b[(k0 + kg) * ldb + r], acc, 0, 0, 0);
+    return acc;
+}
+
+template <typename T> struct Pair2;
+template <> struct Pair2<bf16> {
+    __device__ static inline void load(const bf16* p, float& x, float& y) {
+        bf16x2 v = *reinterpret_cast<const bf16x2*>(p); x = (float)v[0]; y = (float)v[1];
+    }
+    __device__ static inline void store(bf16* p, float x, float y) {
+        bf16x2 v; v[0] = (bf16)x; v[1] = (bf16)y; *reinterpret_cast<bf16x2*>(p) = v;
+    }
+};
+template <> struct Pair2<float> {
+    __device__ static inline void load(const float* p, float& x, float& y) {
+        float2 v = *reinterpret_cast<const float2*>(p); x = v.x; y = v.y;
+    }
+    __device__ static inline void store(float* p, float x, float y) {
+        *reinterpret_cast<float2*>(p) = make_float2(x, y);
+    }
+};
+
+// ================================================================ stage 1: intra
+template <typename T, int DK, int DV, int C>
+struct IntraCfg {
+    static constexpr int NB = C / 16;                       // 16-token sub-blocks
+    static constexpr int NP = NB * (NB + 1) / 2;            // lower-triangular block pairs
+    static constexpr int NSLOT = (NP + 3) / 4;              // per-wave accumulator slots
+    static constexpr int NLV = ilog2(NB);                   // cross levels
+    static constexpr int HR = cmax(16, C / 2);              // rows per operand buffer
+    static constexpr int NPASS = C / HR;                    // passes of the diagonal level
+    static constexpr int PADT = sizeof(T) == 2 ? 8 : 4;     // 16-byte row padding
+    static constexpr int LDK = DK + PADT;
+    static constexpr int CK = cmax(C, Mma<T>::KSTEP);       // contraction length over positions
+    static constexpr int LDT = CK + PADT;
+    static constexpr int LDA = C + 8;
+    static constexpr size_t SZ_L = size_t(C) * DK * 4;
+    static constexpr size_t SZ_OP = size_t(HR) * LDK * sizeof(T);
+    static constexpr size_t PHASE_S = SZ_L + 3 * SZ_OP;
+    static constexpr size_t SZ_TB = align16(size_t(C) * LDT * sizeof(T));
+    static constexpr size_t SZ_A = size_t(C) * LDA * 4;
+    static constexpr size_t SZ_VK = size_t(DV + DK) * LDT * sizeof(T);
+    static constexpr size_t PHASE_W = SZ_TB + smax(SZ_A, SZ_VK);
+    static constexpr size_t OFF_TOT = align16(smax(PHASE_S, PHASE_W));
+    static constexpr size_t OFF_OFF = OFF_TOT + size_t(NB) * DK * 4;
+    static constexpr size_t OFF_BETA = OFF_OFF + size_t(NB) * DK * 4;
+    static constexpr size_t OFF_FLAG = OFF_BETA + size_t(C) * 4;
+    static constexpr size_t TOTAL = align16(OFF_FLAG + size_t(NB) * 4);
+    static constexpr bool FITS = TOTAL <= LDS_LIMIT;
+};
+
+template <typename T, int DK, int DV, int C>
+__global__ __launch_bounds__(256) void chunk_intra_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    T* __restrict__ ws_qt, T* __restrict__ ws_wk, T* __restrict__ ws_kb, T* __restrict__ ws_p,
+    float* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC) {
+    typedef IntraCfg<T, DK, DV, C> Cfg;
+    constexpr int NB = Cfg::NB, NP = Cfg::NP, HR = Cfg::HR, LDK = Cfg::LDK, LDA = Cfg::LDA,
+                  LDT = Cfg::LDT, CK = Cfg::CK;
+    constexpr int KSTEP = Mma<T>::KSTEP;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    float* sL = reinterpret_cast<float*>(smem);
+    T* sKrow = reinterpret_cast<T*>(smem + Cfg::SZ_L);
+    T* sQrow = sKrow + HR * LDK;
+    T* sKcol = sQrow + HR * LDK;
+    float* sTot = reinterpret_cast<float*>(smem + Cfg::OFF_TOT);
+    float* sOff = reinterpret_cast<float*>(smem + Cfg::OFF_OFF);
+    float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_BETA);
+    int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const long ch = blockIdx.x;
+    const int n = (int)(ch % NC);
+    const long bh = ch / NC;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int t0 = n * C;
+    auto grow = [&](int t) -> long { return ((long)b * T_len + (t0 + t)) * H + h; };
+    auto valid = [&](int t) -> bool { return t0 + t < T_len; };
+
+    // ---------------------------------------------------------------- phase 0
+    // Block-local inclusive prefix sums of the clamped log-gate (a1), block totals.
+    if (tid < NB) sFlag[tid] = 0;
+    if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
+    __syncthreads();
+    for (int u = tid; u < NB * (DK / 2); u += 256) {
+        const int R = u / (DK / 2), c = 2 * (u % (DK / 2));
+        float l0 = 0.f, l1 = 0.f;
+        for (int rr = 0; rr < 16; ++rr) {
+            const int t = R * 16 + rr;
+            float2 gg = make_float2(0.f, 0.f);
+            if (valid(t)) gg = *reinterpret_cast<const float2*>(g + grow(t) * DK + c);
+            l0 += clamp_g(gg.x);
+            l1 += clamp_g(gg.y);
+            *reinterpret_cast<float2*>(sL + t * DK + c) = make_float2(l0, l1);
+        }
+        sTot[R * DK + c] = l0;
+        sTot[R * DK + c + 1] = l1;
+        if (l0 < -SAFE_SPAN || l1 < -SAFE_SPAN) sFlag[R] = 1;
+    }
+    __syncthreads();
+
+    floatx4 accA[Cfg::NSLOT], accP[Cfg::NSLOT];
+#pragma unroll
+    for (int s = 0; s < Cfg::NSLOT; ++s) { accA[s] = zero4(); accP[s] = zero4(); }
+
+    // ---------------------------------------------------------------- phase S
+    // Cross levels: segment length n, split point in the middle.
+    static_for<Cfg::NLV>([&](auto LV) {
+        constexpr int SEG = C >> LV;
+        constexpr int HALF = SEG / 2;
+        // exponent offsets per (block, channel) relative to the split point
+        for (int u = tid; u < NB * DK; u += 256) {
+            const int R = u / DK, c = u % DK;
+            const int seg = (R * 16) / SEG, M = (seg * SEG + HALF) / 16;
+            float s = 0.f;
+            if (R >= M) { for (int J = M; J < R; ++J) s += sTot[J * DK + c]; }
+            else        { for (int J = R; J < M; ++J) s += sTot[J * DK + c]; }
+            sOff[u] = s;
+        }
+        __syncthreads();
+        for (int u = tid; u < C * (DK / 8); u += 256) {
+            const int t = u / (DK / 8), c = 8 * (u % (DK / 8));
+            const int R = t / 16, seg = t / SEG, w = t - seg * SEG;
+            float L8[8], o8[8], kv[8], x[8];
+            Vec8<float>::load(sL + t * DK + c, L8);
+            Vec8<float>::load(sOff + R * DK + c, o8);
+            if (valid(t)) Vec8<T>::load(k + grow(t) * DK + c, kv);
+            else {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) kv[m] = 0.f;
+            }
+            if (w >= HALF) {                      // row side: e^{G_r - G_{m-1}} <= 1
+                const int ri = seg * HALF + (w - HALF);
+                float qv[8];
+                if (valid(t)) Vec8<T>::load(q + grow(t) * DK + c, qv);
+                else {
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) qv[m] = 0.f;
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m) { const float e = __expf(o8[m] + L8[m]); x[m] = kv[m] * e; qv[m] *= e; }
+                Vec8<T>::store(sKrow + ri * LDK + c, x);
+                Vec8<T>::store(sQrow + ri * LDK + c, qv);
+            } else {                              // column side: e^{G_{m-1} - G_i} <= 1
+                const int ci = seg * HALF + w;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = kv[m] * __expf(o8[m] - L8[m]);
+                Vec8<T>::store(sKcol + ci * LDK + c, x);
+            }
+        }
+        __syncthreads();
+        static_for<NP>([&](auto PI) {
+            constexpr int p = PI;
+            if constexpr (pair_level(p) == SEG) {
+                if (wave == p % 4) {
+                    constexpr int R = pair_R(p), I = pair_I(p);
+                    constexpr int segR = (R * 16) / SEG, segI = (I * 16) / SEG;
+                    constexpr int ri0 = segR * HALF + (R * 16 - segR * SEG - HALF);
+                    constexpr int ci0 = segI * HALF + (I * 16 - segI * SEG);
+                    mma_tile2<T>(accA[p / 4], accP[p / 4], sKrow + ri0 * LDK, sQrow + ri0 * LDK, LDK,
+                                 sKcol + ci0 * LDK, LDK, DK, lane);
+                }
+            }
+        });
+        __syncthreads();
+    });
+
+    // Diagonal sub-blocks, block start as reference, in passes of HR rows.
+    static_for<Cfg::NPASS>([&](auto PS) {
+        constexpr int r0 = PS * HR;
+        for (int u = tid; u < HR * (DK / 8); u += 256) {
+            const int tl = u / (DK / 8), c = 8 * (u % (DK / 8));
+            const int t = r0 + tl, R = t / 16;
+            float L8[8], kv[8], qv[8], x[8];
+            Vec8<float>::load(sL + t * DK + c, L8);
+            if (valid(t)) { Vec8<T>::load(k + grow(t) * DK + c, kv); Vec8<T>::load(q + grow(t) * DK + c, qv); }
+            else {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) { kv[m] = 0.f; qv[m] = 0.f; }
+            }
+            float y[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) { const float e = __expf(L8[m]); x[m] = kv[m] * e; y[m] = qv[m] * e; }
+            Vec8<T>::store(sKrow + tl * LDK + c, x);
+            Vec8<T>::store(sQrow + tl * LDK + c, y);
+            if (!sFlag[R]) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = kv[m] * __expf(-L8[m]);
+                Vec8<T>::store(sKcol + tl * LDK + c, x);
+            }
+        }
+        __syncthreads();
+        static_for<NP>([&](auto PI) {
+            constexpr int p = PI;
+            constexpr int R = pair_R(p);
+            if constexpr (pair_level(p) == 0 && R * 16 >= r0 && R * 16 < r0 + HR) {
+                if (wave == p % 4) {
+                    constexpr int rl = R * 16 - r0;
+                    if (!sFlag[R]) {
+                        mma_tile2<T>(accA[p / 4], accP[p / 4], sKrow + rl * LDK, sQrow + rl * LDK, LDK,
+                                     sKcol + rl * LDK, LDK, DK, lane);
+                    } else {
+                        // term-by-term: e^{L_r - L_i} with both sums block-local, r >= i
+                        const int i = R * 16 + (lane & 15);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = R * 16 + 4 * (lane >> 4) + e;
+                            float sa = 0.f, sp = 0.f;
+                            if (i <= r && valid(r)) {
+                                for (int c = 0; c < DK; ++c) {
+                                    const float w = __expf(sL[r * DK + c] - sL[i * DK + c]);
+                                    const float ki = to_f32(k[grow(i) * DK + c]);
+                                    sa += to_f32(k[grow(r) * DK + c]) * ki * w;
+                                    sp += to_f32(q[grow(r) * DK + c]) * ki * w;
+                                }
+                            }
+                            accA[p / 4][e] = sa;
+                            accP[p / 4][e] = sp;
+                        }
+                    }
+                }
+            }
+        });
+        __syncthreads();
+    });
+
+    // ---------------------------------------------------------------- write A (as M = beta A) and P
+    float* sA = reinterpret_cast<float*>(smem + Cfg::SZ_TB);
+    T* gP = ws_p + ch * (long)C * C;
+    for (int u = tid; u < C * C; u += 256) {
+        const int r = u / C, i = u % C;
+        if (r / 16 < i / 16) { sA[r * LDA + i] = 0.f; gP[u] = from_f32<T>(0.f); }
+    }
+    static_for<NP>([&](auto PI) {
+        constexpr int p = PI;
+        if (wave == p % 4) {
+            constexpr int R = pair_R(p), I = pair_I(p);
+            const int i = I * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = R * 16 + 4 * (lane >> 4) + e;
+                float av = accA[p / 4][e], pv = accP[p / 4][e];
+                if (R == I) { if (i >= r) av = 0.f; if (i > r) pv = 0.f; }
+                sA[r * LDA + i] = sBeta[r] * av;
+                gP[r * C + i] = from_f32<T>(pv);
+            }
+        }
+    });
+    __syncthreads();
+
+    // ---------------------------------------------------------------- phase T
+    // T = (I + M)^-1 in place.  16x16 diagonal blocks by forward substitution (one
+    // lane per column), then doubling: T21 = -T22 M21 T11 on fp32 MFMA.
+    {
+        const int bd = wave * 4 + (lane >> 4), j = lane & 15;
+        if (bd < NB) {
+            float* Mb = sA + (bd * 16) * LDA + bd * 16;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) s -= Mb[r * LDA + i] * x[i];
+                x[r] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Mb[r * LDA + j] = x[r];
+        }
+    }
+    __syncthreads();
+    float* sX = reinterpret_cast<float*>(smem);
+    static_for<Cfg::NLV>([&](auto LH) {
+        constexpr int HH = 16 << LH;             // size of the blocks being merged
+        constexpr int NM = C / (2 * HH);
+        constexpr int HT = HH / 16;
+        constexpr int NTL = NM * HT * HT;
+        constexpr int LDX = HH + 4;
+        for (int tt = wave; tt < NTL; tt += 4) {
+            const int m = tt / (HT * HT), a = (tt / HT) % HT, bc = tt % HT, base = m * 2 * HH;
+            floatx4 acc = mma_f32_rowB(zero4(), sA + (base + HH + a * 16) * LDA + base, LDA,
+                                       sA + base * LDA + base + bc * 16, LDA, HH, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sX[m * HH * LDX + (a * 16 + 4 * (lane >> 4) + e) * LDX + bc * 16 + (lane & 15)] = acc[e];
+        }
+        __syncthreads();
+        for (int tt = wave; tt < NTL; tt += 4) {
+            const int m = tt / (HT * HT), a = (tt / HT) % HT, bc = tt % HT, base = m * 2 * HH;
+            floatx4 acc = mma_f32_rowB(zero4(), sA + (base + HH + a * 16) * LDA + base + HH, LDA,
+                                       sX + m * HH * LDX + bc * 16, LDX, HH, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sA[(base + HH + a * 16 + 4 * (lane >> 4) + e) * LDA + base + bc * 16 + (lane & 15)] = -acc[e];
+        }
+        __syncthreads();
+    });
+
+    // ---------------------------------------------------------------- phase W
+    T* sTb = reinterpret_cast<T*>(smem);
+    for (int u = tid; u < C * CK; u += 256) {
+        const int r = u / CK, i = u % CK;
+        sTb[r * LDT + i] = from_f32<T>(i < C ? sA[r * LDA + i] : 0.f);
+    }
+    __syncthreads();
+    T* sVt = reinterpret_cast<T*>(smem + Cfg::SZ_TB);     // [DV][LDT]: beta_i v_ij
+    T* sKt = sVt + DV * LDT;                                // [DK][LDT]: beta_i e^{G_i} k_i
+    for (int u = tid; u < C * (DV / 8); u += 256) {
+        const int i = u / (DV / 8), j = 8 * (u % (DV / 8));
+        float vv[8];
+        if (valid(i)) Vec8<T>::load(v + grow(i) * DV + j, vv);
+        else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) vv[m] = 0.f;
+        }
+        const float bi = sBeta[i];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sVt[(j + m) * LDT + i] = from_f32<T>(bi * vv[m]);
+    }
+    if constexpr (CK > C) {
+        for (int u = tid; u < (DV + DK) * (CK - C); u += 256) {
+            const int row = u / (CK - C), i = C + u % (CK - C);
+            sVt[row * LDT + i] = from_f32<T>(0.f);
+        }
+    }
+    T* gQt = ws_qt + ch * (long)C * DK;
+    T* gKb = ws_kb + ch * (long)C * DK;
+    for (int u = tid; u < NB * (DK / 2); u += 256) {
+        const int R = u / (DK / 2), c = 2 * (u % (DK / 2));
+        float in0 = 0.f, in1 = 0.f, out0 = 0.f, out1 = 0.f;   // G_{R,start} and G_last - G_{R,start}
+        for (int J = 0; J < NB; ++J) {
+            const float t0v = sTot[J * DK + c], t1v = sTot[J * DK + c + 1];
+            if (J < R) { in0 += t0v; in1 += t1v; } else { out0 += t0v; out1 += t1v; }
+        }
+        float l0 = 0.f, l1 = 0.f;
+        for (int rr = 0; rr < 16; ++rr) {
+            const int t = R * 16 + rr;
+            float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
+            if (valid(t)) {
+                const float2 gg = *reinterpret_cast<const float2*>(g + grow(t) * DK + c);
+                l0 += clamp_g(gg.x); l1 += clamp_g(gg.y);
+                Pair2<T>::load(k + grow(t) * DK + c, k0, k1);
+                Pair2<T>::load(q + grow(t) * DK + c, q0, q1);
+            }
+            const float ei0 = __expf(in0 + l0), ei1 = __expf(in1 + l1);
+            const float eo0 = __expf(out0 - l0), eo1 = __expf(out1 - l1);
+            const float bt = sBeta[t];
+            sKt[c * LDT + t] = from_f32<T>(bt * k0 * ei0);
+            sKt[(c + 1) * LDT + t] = from_f32<T>(bt * k1 * ei1);
+            Pair2<T>::store(gQt + t * DK + c, q0 * ei0, q1 * ei1);
+            Pair2<T>::store(gKb + t * DK + c, k0 * eo0, k1 * eo1);
+        }
+    }
+    if (tid < DK) {
+        float s = 0.f;
+        for (int J = 0; J < NB; ++J) s += sTot[J * DK + tid];
+        ws_gam[ch * DK + tid] = __expf(s);
+    }
+    __syncthreads();
+    constexpr int NTU = NB * (DV / 16), NTW = NB * (DK / 16);
+    float* gU = ws_u + ch * (long)C * DV;
+    T* gWk = ws_wk + ch * (long)C * DK;
+    for (int tt = wave; tt < NTU + NTW; tt += 4) {
+        const bool isU = tt < NTU;
+        const int t2 = isU ? tt : tt - NTU;
+        const int ncol = isU ? DV / 16 : DK / 16;
+        const int R = t2 / ncol, J = t2 % ncol;
+        const int K = ((16 * (R + 1) + KSTEP - 1) / KSTEP) * KSTEP;
+        const T* bsrc = isU ? sVt + J * 16 * LDT : sKt + J * 16 * LDT;
+        floatx4 acc = mma_tile<T>(zero4(), sTb + R * 16 * LDT, LDT, bsrc, LDT, K, lane);
+        const int col = J * 16 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = R * 16 + 4 * (lane >> 4) + e;
+            if (isU) gU[row * DV + col] = acc[e];
+            else gWk[row * DK + col] = from_f32<T>(acc[e]);
+        }
+    }
+}
+
+// ================================================================ stage 2: chain
+template <typename T, int DK, int DV, int C, int DVS>
+struct ChainCfg {
+    static constexpr int PADT = sizeof(T) == 2 ? 8 : 4;
+    static constexpr int LDK = DK + PADT;
+    static constexpr int CK = cmax(C, Mma<T>::KSTEP);
+    static constexpr int LDC = CK + PADT;
+    static constexpr int NJ = DVS / 16;
+    static constexpr int NTW = (C / 16) * NJ;               // W / O tiles
+    static constexpr int NTS = (DK / 16) * NJ;              // state tiles
+    static constexpr int NSW = (NTW + 3) / 4, NSS = (NTS + 3) / 4;
+    static constexpr size_t SZ_QT = size_t(C) * LDK * sizeof(T);
+    static constexpr size_t SZ_KBT = align16(size_t(DK) * LDC * sizeof(T));
+    static constexpr size_t SZ_P = align16(size_t(C) * LDC * sizeof(T));
+    static constexpr size_t SZ_U = size_t(C) * DVS * 4;
+    static constexpr size_t SZ_GAM = size_t(DK) * 4;
+    static constexpr size_t SZ_ST = size_t(DVS) * LDK * sizeof(T);
+    static constexpr size_t SZ_WT = align16(size_t(DVS) * LDC * sizeof(T));
+    static constexpr size_t OFF_WK = SZ_QT;
+    static constexpr size_t OFF_KBT = OFF_WK + SZ_QT;
+    static constexpr size_t OFF_P = OFF_KBT + SZ_KBT;
+    static constexpr size_t OFF_U = OFF_P + SZ_P;
+    static constexpr size_t OFF_GAM = OFF_U + SZ_U;
+    static constexpr size_t OFF_ST = OFF_GAM + SZ_GAM;
+    static constexpr size_t OFF_WT = OFF_ST + SZ_ST;
+    static constexpr size_t TOTAL = OFF_WT + SZ_WT;
+    static constexpr bool FITS = TOTAL <= LDS_LIMIT;
+};
+
+template <typename T, typename TOut, int DK, int DV, int C, int DVS>
+__global__ __launch_bounds__(256) void chunk_chain_kernel(
+    const T* __restrict__ ws_qt, const T* __restrict__ ws_wk, const T* __restrict__ ws_kb,
+    const T* __restrict__ ws_p, const float* __restrict__ ws_u, const float* __restrict__ ws_gam,
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT,
+    int T_len, int H, int NC) {
+    typedef ChainCfg<T, DK, DV, C, DVS> Cfg;
+    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, CK = Cfg::CK, NJ = Cfg::NJ;
+    constexpr int NTW = Cfg::NTW, NTS = Cfg::NTS, KSTEP = Mma<T>::KSTEP;
+    constexpr int NSL = DV / DVS;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    T* sQt = reinterpret_cast<T*>(smem);
+    T* sWk = reinterpret_cast<T*>(smem + Cfg::OFF_WK);
+    T* sKbT = reinterpret_cast<T*>(smem + Cfg::OFF_KBT);
+    T* sP = reinterpret_cast<T*>(smem + Cfg::OFF_P);
+    float* sU = reinterpret_cast<float*>(smem + Cfg::OFF_U);
+    float* sGam = reinterpret_cast<float*>(smem + Cfg::OFF_GAM);
+    T* sST = reinterpret_cast<T*>(smem + Cfg::OFF_ST);
+    T* sWT = reinterpret_cast<T*>(smem + Cfg::OFF_WT);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const long bh = blockIdx.x / NSL;
+    const int j0 = (int)(blockIdx.x % NSL) * DVS;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+
+    // zero the contraction padding once (columns C..CK never receive data)
+    if constexpr (CK > C) {
+        for (int u = tid; u < (DK + C + DVS) * (CK - C); u += 256) {
+            const int row = u / (CK - C), i = C + u % (CK - C);
+            if (row < DK) sKbT[row * LDC + i] = from_f32<T>(0.f);
+            else if (row < DK + C) sP[(row - DK) * LDC + i] = from_f32<T>(0.f);
+            else sWT[(row - DK - C) * LDC + i] = from_f32<T>(0.f);
+        }
+    }
+
+    floatx4 accS[Cfg::NSS];
+    static_for<Cfg::NSS>([&](auto SI) {
+        constexpr int s = SI;
+        const int ts = wave + 4 * s;
+        accS[s] = zero4();
+        if (ts < NTS && s0) {
+            const int ct = ts / NJ, jt = ts % NJ;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = ct * 16 + 4 * (lane >> 4) + e, j = jt * 16 + (lane & 15);
+                accS[s][e] = s0[(bh * DK + c) * (long)DV + j0 + j];
+            }
+        }
+    });
+    auto write_state_operand = [&]() {
+        static_for<Cfg::NSS>([&](auto SI) {
+            constexpr int s = SI;
+            const int ts = wave + 4 * s;
+            if (ts < NTS) {
+                const int ct = ts / NJ, jt = ts % NJ;
+                const int j = jt * 16 + (lane & 15), c = ct * 16 + 4 * (lane >> 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sST[j * LDK + c + e] = from_f32<T>(accS[s][e]);
+            }
+        });
+    };
+    write_state_operand();
+
+    for (int n = 0; n < NC; ++n) {
+        const long ch = bh * NC + n;
+        // ---- stage the chunk's operands in LDS
+        {
+            const T* gq = ws_qt + ch * (long)C * DK;
+            const T* gw = ws_wk + ch * (long)C * DK;
+            const T* gk = ws_kb + ch * (long)C * DK;
+            for (int u = tid; u < C * (DK / 8); u += 256) {
+                const int r = u / (DK / 8), c = 8 * (u % (DK / 8));
+                float x[8];
+                Vec8<T>::load(gq + r * DK + c, x); Vec8<T>::store(sQt + r * LDK + c, x);
+                Vec8<T>::load(gw + r * DK + c, x); Vec8<T>::store(sWk + r * LDK + c, x);
+                Vec8<T>::load(gk + r * DK + c, x);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) sKbT[(c + m) * LDC + r] = from_f32<T>(x[m]);
+            }
+            const T* gp = ws_p + ch * (long)C * C;
+            for (int u = tid; u < C * (C / 8 > 0 ? C / 8 : 1); u += 256) {
+                const int r = u / (C / 8), i = 8 * (u % (C / 8));
+                float x[8];
+                Vec8<T>::load(gp + r * C + i, x); Vec8<T>::store(sP + r * LDC + i, x);
+            }
+            const float* gu = ws_u + ch * (long)C * DV + j0;
+            for (int u = tid; u < C * (DVS / 4); u += 256) {
+                const int r = u / (DVS / 4), j = 4 * (u % (DVS / 4));
+                *reinterpret_cast<float4*>(sU + r * DVS + j) = *reinterpret_cast<const float4*>(gu + r * DV + j);
+            }
+            if (tid < DK) sGam[tid] = ws_gam[ch * DK + tid];
+        }
+        __syncthreads();
+
+        // ---- W = U - Wk S (to LDS, transposed) and the state part of O
+        floatx4 accO[Cfg::NSW];
+        static_for<Cfg::NSW>([&](auto SI) {
+            constexpr int s = SI;
+            const int tw = wave + 4 * s;
+            accO[s] = zero4();
+            if (tw < NTW) {
+                const int R = tw / NJ, J = tw % NJ;
+                floatx4 wk = mma_tile<T>(zero4(), sWk + R * 16 * LDK, LDK, sST + J * 16 * LDK, LDK, DK, lane);
+                accO[s] = mma_tile<T>(zero4(), sQt + R * 16 * LDK, LDK, sST + J * 16 * LDK, LDK, DK, lane);
+                const int j = J * 16 + (lane & 15), r = R * 16 + 4 * (lane >> 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sWT[j * LDC + r + e] = from_f32<T>(sU[(r + e) * DVS + j] - wk[e]);
+            }
+        });
+        __syncthreads();
+
+        // ---- O += P W, store O ; S = gam * S + Kb^T W
+        static_for<Cfg::NSW>([&](auto SI) {
+            constexpr int s = SI;
+            const int tw = wave + 4 * s;
+            if (tw < NTW) {
+                const int R = tw / NJ, J = tw % NJ;
+                const int K = ((16 * (R + 1) + KSTEP - 1) / KSTEP) * KSTEP;
+                accO[s] = mma_tile<T>(accO[s], sP + R * 16 * LDC, LDC, sWT + J * 16 * LDC, LDC, K, lane);
+                const int j = J * 16 + (lane & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = n * C + R * 16 + 4 * (lane >> 4) + e;
+                    if (t < T_len) o[(((long)b * T_len + t) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[s][e]);
+                }
+            }
+        });
+        static_for<Cfg::NSS>([&](auto SI) {
+            constexpr int s = SI;
+            const int ts = wave + 4 * s;
+            if (ts < NTS) {
+                const int ct = ts / NJ, jt = ts % NJ;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accS[s][e] *= sGam[ct * 16 + 4 * (lane >> 4) + e];
+                accS[s] = mma_tile<T>(accS[s], sKbT + ct * 16 * LDC, LDC, sWT + jt * 16 * LDC, LDC, CK, lane);
+            }
+        });
+        __syncthreads();
+        write_state_operand();
+    }
+
+    if (sT) {
+        static_for<Cfg::NSS>([&](auto SI) {
+            constexpr int s = SI;
+            const int ts = wave + 4 * s;
+            if (ts < NTS) {
+                const int ct = ts / NJ, jt = ts % NJ;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = ct * 16 + 4 * (lane >> 4) + e, j = jt * 16 + (lane & 15);
+                    sT[(bh * DK + c) * (long)DV + j0 + j] = accS[s][e];
+                }
+            }
+        });
+    }
+}
+
+// ================================================================ host side
+static inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
+    WsLayout w{};
+    const size_t es = in_bf16 ? 2 : 4;
+    const size_t NC = (size_t)((T + C - 1) / C);
+    const size_t nch = (size_t)B * H * NC;
+    size_t off = 0;
+    w.qt = off; off = al256(off + nch * C * dk * es);
+    w.wk = off; off = al256(off + nch * C * dk * es);
+    w.kb = off; off = al256(off + nch * C * dk * es);
+    w.p = off;  off = al256(off + nch * C * C * es);
+    w.u = off;  off = al256(off + nch * C * dv * 4);
+    w.gam = off; off = al256(off + nch * dk * 4);
+    w.total = off;
+    return w;
+}
+
+template <typename T, int DK, int DV, int C>
+static hipError_t launch_intra(const ChunkArgs& a) {
+    typedef IntraCfg<T, DK, DV, C> Cfg;
+    if constexpr (!Cfg::FITS) {
+        return hipErrorInvalidValue;
+    } else {
+        const int NC = (a.T + C - 1) / C;
+        const long nch = (long)a.B * a.H * NC;
+        if (nch == 0) return hipSuccess;
+        const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, sizeof(T) == 2, C);
+        char* ws = (char*)a.ws;
+        hipLaunchKernelGGL((chunk_intra_kernel<T, DK, DV, C>), dim3((unsigned)nch), dim3(256), 0, a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta,
+                           (T*)(ws + w.qt), (T*)(ws + w.wk), (T*)(ws + w.kb), (T*)(ws + w.p),
+                           (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
+        return hipGetLastError();
+    }
+}
+
+template <typename T, typename TOut, int DK, int DV, int C, int DVS>
+static hipError_t launch_chain_dvs(const ChunkArgs& a) {
+    typedef ChainCfg<T, DK, DV, C, DVS> Cfg;
+    if constexpr (!Cfg::FITS || DVS > DV) {
+        return hipErrorInvalidValue;
+    } else {
+        const int NC = (a.T + C - 1) / C;
+        const long nwg = (long)a.B * a.H * (DV / DVS);
+        if (nwg == 0) return hipSuccess;
+        const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, sizeof(T) == 2, C);
+        char* ws = (char*)a.ws;
+        hipLaunchKernelGGL((chunk_chain_kernel<T, TOut, DK, DV, C, DVS>), dim3((unsigned)nwg), dim3(256), 0,
+                           a.stream, (const T*)(ws + w.qt), (const T*)(ws + w.wk), (const T*)(ws + w.kb),
+                           (const T*)(ws + w.p), (const float*)(ws + w.u), (const float*)(ws + w.gam),
+                           a.s0, (TOut*)a.o, a.sT, a.T, a.H, NC);
+        return hipGetLastError();
+    }
+}
+
+template <typename T, int DK, int DV, int C, int DVS>
+static constexpr bool chain_fits() { return DVS <= DV && ChainCfg<T, DK, DV, C, DVS>::FITS; }
+
+// Value-column slice width: enough workgroups to cover the chip (>= 256 when
+// possible), as wide as possible otherwise, and within the LDS budget.
+template <typename T, int DK, int DV, int C>
+static int pick_dvs(long bh) {
+    int dvs = 16;
+    const int cands[3] = {64, 32, 16};
+    const bool fits[3] = {chain_fits<T, DK, DV, C, 64>(), chain_fits<T, DK, DV, C, 32>(),
+                          chain_fits<T, DK, DV, C, 16>()};
+    for (int i = 0; i < 3; ++i) {
+        if (!fits[i]) continue;
+        dvs = cands[i];
+        if (bh * (DV / cands[i]) >= 256) break;
+    }
+    return dvs;
+}
+
+template <typename T, typename TOut, int DK, int DV, int C>
+static hipError_t launch_chain(const ChunkArgs& a) {
+    const int dvs = pick_dvs<T, DK, DV, C>((long)a.B * a.H);
+    if (dvs == 64) return launch_chain_dvs<T, TOut, DK, DV, C, 64>(a);
+    if (dvs == 32) return launch_chain_dvs<T, TOut, DK, DV, C, 32>(a);
+    return launch_chain_dvs<T, TOut, DK, DV, C, 16>(a);
+}
+
+template <typename T, int DK, int DV, int C>
+static constexpr bool combo_fits() {
+    return IntraCfg<T, DK, DV, C>::FITS && chain_fits<T, DK, DV, C, 16>();
+}
+
+bool chunk_supported(int dk, int dv, int C, bool in_bf16) {
+#define KDA_FIT(T, DK, DV, CC) if (dk == DK && dv == DV && C == CC) return combo_fits<T, DK, DV, CC>();
+#define KDA_FIT_C(T, DK, DV) KDA_FIT(T, DK, DV, 16) KDA_FIT(T, DK, DV, 32) KDA_FIT(T, DK, DV, 64) KDA_FIT(T, DK, DV, 128)
+    if (in_bf16) {
+        KDA_FIT_C(bf16, 64, 64) KDA_FIT_C(bf16, 64, 128) KDA_FIT_C(bf16, 128, 64) KDA_FIT_C(bf16, 128, 128)
+    } else {
+        KDA_FIT_C(float, 64, 64) KDA_FIT_C(float, 64, 128) KDA_FIT_C(float, 128, 64) KDA_FIT_C(float, 128, 128)
+    }
+#undef KDA_FIT_C
+#undef KDA_FIT
+    return false;
+}
+
+template <typename T, int DK, int DV>
+static hipError_t intra_c(const ChunkArgs& a) {
+    switch (a.C) {
+        case 16: return launch_intra<T, DK, DV, 16>(a);
+        case 32: return launch_intra<T, DK, DV, 32>(a);
+        case 64: return launch_intra<T, DK, DV, 64>(a);
+        default: return launch_intra<T, DK, DV, 128>(a);
+    }
+}
+template <typename T>
+static hipError_t intra_dims(const ChunkArgs& a) {
+    if (a.dk == 64) return a.dv == 64 ? intra_c<T, 64, 64>(a) : intra_c<T, 64, 128>(a);
+    return a.dv == 64 ? intra_c<T, 128, 64>(a) : intra_c<T, 128, 128>(a);
+}
+hipError_t run_chunk_intra(const ChunkArgs& a) {
+    return a.in_bf16 ? intra_dims<bf16>(a) : intra_dims<float>(a);
+}
+
+template <typename T, typename TOut, int DK, int DV>
+static hipError_t chain_c(const ChunkArgs& a) {
+    switch (a.C) {
+        case 16: return launch_chain<T, TOut, DK, DV, 16>(a);
+        case 32: return launch_chain<T, TOut, DK, DV, 32>(a);
+        case 64: return launch_chain<T, TOut, DK, DV, 64>(a);
+        default: return launch_chain<T, TOut, DK, DV, 128>(a);
+    }
+}
+template <typename T, typename TOut>
+static hipError_t chain_dims(const ChunkArgs& a) {
+    if (a.dk == 64) return a.dv == 64 ? chain_c<T, TOut, 64, 64>(a) : chain_c<T, TOut, 64, 128>(a);
+    return a.dv == 64 ? chain_c<T, TOut, 128, 64>(a) : chain_c<T, TOut, 128, 128>(a);
+}
+hipError_t run_chunk_chain(const ChunkArgs& a) {
+    if (a.in_bf16) return a.out_bf16 ? chain_dims<bf16, bf16>(a) : chain_dims<bf16, float>(a);
+    return a.out_bf16 ? chain_dims<float, bf16>(a) : chain_dims<float, float>(a);
+}
+
+}  // namespace kda

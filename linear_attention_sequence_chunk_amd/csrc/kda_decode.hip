@@ -1,0 +1,119 @@
+// kda_decode.hip -- single-token KDA step with the state updated in place.
+//
+// The step of section 十五 of "我终于看懂了 KDA…" (read the state, compute the
+// output, update the state) with the order of its section 八 (decay, read, error,
+// write).  With alpha = exp(g) the update expands to
+//     r = S^T (alpha*k),  s = S^T (alpha*q),  u = beta (v - r),
+//     o = s + (q.k) u,    S_new = Diag(alpha) S + k u^T,
+// so each state element is read once and written once: the state stays in
+// registers between the column reductions and the rewrite.
+//
+// One workgroup (256 threads) per (sequence, head).  Thread (ty, tx) owns the
+// float4 of columns 4*tx..4*tx+3 in rows ty, ty+RG, ty+2RG, ...: every row read
+// is a fully coalesced DV*4-byte line.  Column sums are combined in LDS in a
+// fixed order (bitwise reproducible).
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <typename TIn, typename TOut, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    float* __restrict__ state, TOut* __restrict__ o) {
+    constexpr int NT = 256;
+    constexpr int CG = DV / 4;       // threads across one row (float4 each)
+    constexpr int RG = NT / CG;      // row groups
+    constexpr int RPT = DK / RG;     // rows per thread
+    static_assert(DK % RG == 0, "row split");
+
+    __shared__ float s_ak[DK], s_aq[DK], s_k[DK], s_a[DK];
+    __shared__ float s_red[2][RG][DV];
+    __shared__ float s_u[DV];
+    __shared__ float s_qk;
+
+    const long nh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int tx = tid % CG, ty = tid / CG;
+    float* S = state + nh * (long)DK * DV;
+
+    // Issue every state load first: RPT independent 16-byte loads in flight.
+    floatx4 sv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        sv[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (long)(ty + i * RG) * DV) + tx);
+
+    if (tid < DK) {
+        const float a = __expf(g[nh * DK + tid]);       // exp(-inf) = 0: alpha = 0 clears
+        const float kc = to_f32(k[nh * DK + tid]);
+        const float qc = to_f32(q[nh * DK + tid]);
+        s_a[tid] = a; s_k[tid] = kc; s_ak[tid] = a * kc; s_aq[tid] = a * qc;
+    }
+    if (tid < WAVE) {                                     // q.k, fixed-order wave reduction
+        float p = 0.f;
+#pragma unroll
+        for (int c = tid; c < DK; c += WAVE) p += to_f32(q[nh * DK + c]) * to_f32(k[nh * DK + c]);
+#pragma unroll
+        for (int off = WAVE / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        if (tid == 0) s_qk = p;
+    }
+    __syncthreads();
+
+    float r[4] = {0.f, 0.f, 0.f, 0.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int c = ty + i * RG;
+        const float ak = s_ak[c], aq = s_aq[c];
+        r[0] += ak * sv[i].x; r[1] += ak * sv[i].y; r[2] += ak * sv[i].z; r[3] += ak * sv[i].w;
+        s[0] += aq * sv[i].x; s[1] += aq * sv[i].y; s[2] += aq * sv[i].z; s[3] += aq * sv[i].w;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { s_red[0][ty][4 * tx + m] = r[m]; s_red[1][ty][4 * tx + m] = s[m]; }
+    __syncthreads();
+
+    if (tid < DV) {
+        float rr = 0.f, ss = 0.f;
+#pragma unroll
+        for (int y = 0; y < RG; ++y) { rr += s_red[0][y][tid]; ss += s_red[1][y][tid]; }
+        const float u = beta[nh] * (to_f32(v[nh * DV + tid]) - rr);
+        s_u[tid] = u;
+        o[nh * DV + tid] = from_f32<TOut>(ss + s_qk * u);
+    }
+    __syncthreads();
+
+    const float u0 = s_u[4 * tx], u1 = s_u[4 * tx + 1], u2 = s_u[4 * tx + 2], u3 = s_u[4 * tx + 3];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int c = ty + i * RG;
+        const float a = s_a[c], kc = s_k[c];
+        floatx4 w;
+        w.x = a * sv[i].x + kc * u0; w.y = a * sv[i].y + kc * u1;
+        w.z = a * sv[i].z + kc * u2; w.w = a * sv[i].w + kc * u3;
+        __builtin_nontemporal_store(w, reinterpret_cast<floatx4*>(S + (long)c * DV) + tx);
+    }
+}
+
+template <typename TIn, typename TOut, int DK, int DV>
+static hipError_t launch_decode(const DecodeArgs& a) {
+    const long nh = (long)a.N * a.H;
+    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV>), dim3((unsigned)nh), dim3(256), 0,
+                       a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta,
+                       a.state, (TOut*)a.o);
+    return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+static hipError_t dispatch_dims(const DecodeArgs& a) {
+    if (a.dk == 64 && a.dv == 64) return launch_decode<TIn, TOut, 64, 64>(a);
+    if (a.dk == 64 && a.dv == 128) return launch_decode<TIn, TOut, 64, 128>(a);
+    if (a.dk == 128 && a.dv == 64) return launch_decode<TIn, TOut, 128, 64>(a);
+    return launch_decode<TIn, TOut, 128, 128>(a);
+}
+
+hipError_t run_decode_step(const DecodeArgs& a) {
+    if (a.in_bf16) return a.out_bf16 ? dispatch_dims<bf16, bf16>(a) : dispatch_dims<bf16, float>(a);
+    return a.out_bf16 ? dispatch_dims<float, bf16>(a) : dispatch_dims<float, float>(a);
+}
+
+}  // namespace kda

@@ -1,0 +1,42 @@
+// kda_launch.h -- host-side interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta;
+    float* state; void* o;
+    int N, H, dk, dv;
+    bool in_bf16, out_bf16;
+    hipStream_t stream;
+};
+
+struct ChunkArgs {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta;
+    const float* s0; void* o; float* sT;
+    int B, T, H, dk, dv, C;
+    bool in_bf16, out_bf16;
+    void* ws; size_t ws_bytes;
+    hipStream_t stream;
+};
+
+// Workspace of the split chunk path, per (b, h, chunk), struct of arrays:
+//   Qt [C][dk] in, Wk [C][dk] in, Kb [C][dk] in, P [C][C] in, U [C][dv] fp32, gam [dk] fp32
+struct WsLayout {
+    size_t qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
+};
+WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C);
+
+// True when an instantiation exists for these sizes (dk, dv, C, dtype).
+bool chunk_supported(int dk, int dv, int C, bool in_bf16);
+
+hipError_t run_decode_step(const DecodeArgs& a);
+hipError_t run_chunk_intra(const ChunkArgs& a);
+hipError_t run_chunk_chain(const ChunkArgs& a);
+
+}  // namespace kda

@@ -1,0 +1,166 @@
+"""The C ABI: exported symbols, host-side validation and status codes (CPU).
+
+No compute runs here: valid calls stop at the device check (KDA_ERR_HIP on a
+machine without a GPU), invalid ones are rejected before any HIP call, so fake
+(never dereferenced) pointers are enough."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from linear_attention_sequence_chunk_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+HAS_GPU = torch.cuda.is_available()
+
+OK, NULL, SHAPE, UNSUP, MISAL, WS, ALIAS, HIP = range(8)
+
+
+def declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert set(names) == set(_lib.SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = _lib.lib()
+    for n in names:
+        getattr(L, n)
+
+
+def test_version_and_strings():
+    L = _lib.lib()
+    assert L.kda_abi_version() == 1
+    for s in range(8):
+        assert len(_lib.status_string(s)) >= 2
+    assert _lib.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    L = _lib.lib()
+    ws = L.kda_chunk_fwd_workspace_bytes
+    # per chunk-head: 3*C*dk + C*C elements in the input dtype, C*dv + dk fp32
+    n = ws(1, 64, 1, 64, 64, _lib.F32, 64)
+    assert n >= (3 * 64 * 64 + 64 * 64) * 4 + (64 * 64 + 64) * 4
+    assert ws(4, 8192, 16, 128, 128, _lib.BF16, 64) > ws(4, 8192, 16, 128, 128, _lib.BF16, 128) // 2
+    assert ws(1, 10, 1, 96, 64, _lib.F32, 64) == 0       # unsupported dk
+    assert ws(1, 10, 1, 64, 64, _lib.F32, 48) == 0       # unsupported C
+    assert ws(1, 10, 1, 64, 64, 7, 64) == 0              # bad dtype
+    assert ws(1, 100, 1, 64, 64, _lib.F32, 64) == ws(1, 128, 1, 64, 64, _lib.F32, 64)  # partial chunk
+
+
+class Fake:
+    """Non-overlapping fake device addresses (never dereferenced)."""
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes):
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+
+
+def chunk_args(B=2, T=100, H=3, dk=64, dv=64, ind=_lib.F32, outd=_lib.F32, C=64):
+    f = Fake()
+    e = 4 if ind == _lib.F32 else 2
+    eo = 4 if outd == _lib.F32 else 2
+    tok = B * T * H
+    a = dict(q=f(tok * dk * e), k=f(tok * dk * e), v=f(tok * dv * e), g=f(tok * dk * 4),
+             beta=f(tok * 4), s0=f(B * H * dk * dv * 4), o=f(tok * dv * eo),
+             sT=f(B * H * dk * dv * 4))
+    wsb = _lib.lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, ind, C)
+    a.update(ws=f(wsb), wsb=wsb, B=B, T=T, H=H, dk=dk, dv=dv, ind=ind, outd=outd, C=C)
+    return a
+
+
+def call_chunk(a, fn="kda_chunk_fwd"):
+    L = _lib.lib()
+    return getattr(L, fn)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"], a["sT"],
+                          a["B"], a["T"], a["H"], a["dk"], a["dv"], a["ind"], a["outd"],
+                          a["ws"], a["wsb"], None, a["C"])
+
+
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain"])
+def test_chunk_validation_codes(fn):
+    a = chunk_args()
+    cases = [
+        (dict(B=-1), SHAPE), (dict(T=-5), SHAPE),
+        (dict(dk=96), UNSUP), (dict(dv=32), UNSUP), (dict(C=48), UNSUP), (dict(C=256), UNSUP),
+        (dict(ind=5), UNSUP), (dict(outd=-1), UNSUP),
+        (dict(q=None), NULL), (dict(beta=None), NULL), (dict(o=None), NULL),
+        (dict(k=a["k"] + 8), MISAL), (dict(s0=a["s0"] + 4), MISAL),
+        (dict(ws=None), WS), (dict(wsb=a["wsb"] - 1), WS),
+        (dict(o=a["q"]), ALIAS), (dict(o=a["ws"]), ALIAS), (dict(sT=a["v"]), ALIAS),
+        (dict(sT=a["s0"] + 256), ALIAS), (dict(ws=a["g"]), ALIAS), (dict(o=a["sT"]), ALIAS),
+    ]
+    for change, code in cases:
+        b = dict(a)
+        b.update(change)
+        assert call_chunk(b, fn) == code, (change, code)
+
+
+def test_fp32_c128_dk128_is_unsupported():
+    a = chunk_args(dk=128, dv=128, C=128)
+    assert a["wsb"] == 0
+    a["wsb"] = 1 << 30
+    assert call_chunk(a) == UNSUP
+
+
+def test_valid_chunk_call_reaches_device_check():
+    a = chunk_args(ind=_lib.BF16, outd=_lib.BF16, dk=128, dv=128)
+    b = dict(a); b["sT"] = b["s0"]                      # in-place state is allowed
+    b2 = dict(a); b2["s0"] = None; b2["sT"] = None      # no states is allowed
+    for x in (a, b, b2):
+        st = call_chunk(x)
+        assert st == (OK if HAS_GPU else HIP) or (HAS_GPU and st == HIP)
+    if not HAS_GPU:
+        assert call_chunk(a) == HIP
+
+
+def test_empty_sizes_return_ok_without_pointers():
+    L = _lib.lib()
+    st = L.kda_chunk_fwd(None, None, None, None, None, None, None, None, 0, 5, 3, 64, 64,
+                         0, 0, None, 0, None, 64)
+    assert st in (OK, HIP)
+    assert L.kda_decode_step(None, None, None, None, None, None, None, 0, 4, 64, 64, 0, 0, None) == OK
+
+
+def test_decode_validation_codes():
+    L = _lib.lib()
+    f = Fake()
+    N, H, dk, dv = 3, 2, 128, 64
+    a = dict(q=f(N * H * dk * 2), k=f(N * H * dk * 2), v=f(N * H * dv * 2), g=f(N * H * dk * 4),
+             beta=f(N * H * 4), state=f(N * H * dk * dv * 4), o=f(N * H * dv * 2),
+             N=N, H=H, dk=dk, dv=dv, ind=_lib.BF16, outd=_lib.BF16)
+
+    def call(x):
+        return L.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], x["o"],
+                                 x["N"], x["H"], x["dk"], x["dv"], x["ind"], x["outd"], None)
+    cases = [(dict(N=-1), SHAPE), (dict(dk=100), UNSUP), (dict(ind=3), UNSUP),
+             (dict(state=None), NULL), (dict(v=a["v"] + 2), MISAL),
+             (dict(o=a["state"]), ALIAS), (dict(state=a["q"]), ALIAS), (dict(o=a["g"] + 16), ALIAS)]
+    for change, code in cases:
+        b = dict(a); b.update(change)
+        assert call(b) == code, (change, code)
+    if not HAS_GPU:
+        assert call(a) == HIP
+
+
+def test_python_binding_refuses_cpu_tensors():
+    from linear_attention_sequence_chunk_amd import chunk_fwd, decode_step
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1))
+    with pytest.raises(ValueError):
+        decode_step(x[0], x[0], x[0], x[0], torch.zeros(4, 1), torch.zeros(4, 1, 64, 64))
