@@ -28,9 +28,12 @@
  *     state are fp32.  g is the log-gate: g <= 0, -inf allowed (alpha = 0).
  *     g > 0 (alpha > 1) is outside the method's domain; results are unspecified.
  *     NaN/Inf inputs propagate; nothing is checked on the device.
- *   - Supported: dk, dv in {64, 128}; chunk size C in {16, 32, 64, 128}; any
- *     T >= 0 (a last partial chunk is allowed); B, H >= 0.
- *   - All pointers must be 16-byte aligned.
+ *   - Supported: dk, dv in {64, 128}; chunk size C in {16, 32, 64, 128} for
+ *     bf16 inputs and {16, 32, 64} for fp32 inputs; any T >= 0 (a last
+ *     partial chunk is allowed); B, H >= 0.
+ *   - Alignment: kda_chunk_fwd needs q, k, v, o and the workspace 16-byte
+ *     aligned and g 8-byte aligned; kda_decode_step needs the state 16-byte
+ *     aligned; every other pointer needs the alignment of its element type.
  *   - Validation happens on the host before any HIP call; on error nothing is
  *     launched and nothing is written.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
@@ -59,7 +62,7 @@ typedef enum {
     KDA_ERR_NULL = 1,        /* a required pointer is NULL                       */
     KDA_ERR_SHAPE = 2,       /* a size is negative or inconsistent               */
     KDA_ERR_UNSUPPORTED = 3, /* dk, dv, C or a dtype outside the supported set   */
-    KDA_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned                 */
+    KDA_ERR_MISALIGNED = 4,  /* a pointer lacks the alignment it needs          */
     KDA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
     KDA_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap   */
     KDA_ERR_HIP = 7          /* no usable device, or a HIP launch/execution error */

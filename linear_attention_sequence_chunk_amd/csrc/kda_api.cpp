@@ -22,7 +22,7 @@ Range range_of(const void* p, size_t bytes) {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 bool debug_sync() {
     static int cached = -1;
@@ -82,9 +82,15 @@ int validate_chunk(const ChunkCall& c) {
     const size_t nst = (size_t)c.B * c.H * c.dk * c.dv;
     if (tok > 0 && (!c.q || !c.k || !c.v || !c.g || !c.beta || !c.o)) return KDA_ERR_NULL;
 
-    const void* ptrs[9] = {c.q, c.k, c.v, c.g, c.beta, c.s0, c.o, c.sT, c.ws};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    // q, k, v, o and the workspace move in 16-byte vectors, g in 8-byte pairs;
+    // beta and the states only need fp32 alignment.
+    const void* p16[5] = {c.q, c.k, c.v, c.o, c.ws};
+    for (const void* p : p16)
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if (c.g && !aligned(c.g, 8)) return KDA_ERR_MISALIGNED;
+    const void* p4[3] = {c.beta, c.s0, c.sT};
+    for (const void* p : p4)
+        if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
 
     const size_t need = kda::ws_layout(c.B, c.T, c.H, c.dk, c.dv, c.in_dtype == KDA_BF16, c.C).total;
     if (tok > 0 && (!c.ws || c.ws_bytes < need)) return KDA_ERR_WORKSPACE;
@@ -161,7 +167,7 @@ const char* kda_status_string(int s) {
         case KDA_ERR_NULL: return "a required pointer is NULL";
         case KDA_ERR_SHAPE: return "a size is negative or inconsistent";
         case KDA_ERR_UNSUPPORTED: return "unsupported dk, dv, chunk size or dtype";
-        case KDA_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+        case KDA_ERR_MISALIGNED: return "a pointer lacks the alignment its argument needs";
         case KDA_ERR_WORKSPACE: return "workspace missing or too small";
         case KDA_ERR_ALIAS: return "an output overlaps an argument it may not overlap";
         case KDA_ERR_HIP: return "no usable HIP device, or a HIP launch/execution error";
@@ -199,9 +205,12 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* g,
     const size_t nh = (size_t)N * H;
     if (nh == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
-    const void* ptrs[7] = {q, k, v, g, beta, state, o};
-    for (const void* p : ptrs)
-        if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    // the state is streamed in 16-byte vectors; the rest is read element-wise
+    if (!aligned(state, 16)) return KDA_ERR_MISALIGNED;
+    const void* pe[6] = {q, k, v, g, beta, o};
+    const uintptr_t ae[6] = {esize(in_dtype), esize(in_dtype), esize(in_dtype), 4, 4, esize(out_dtype)};
+    for (int i = 0; i < 6; ++i)
+        if (!aligned(pe[i], ae[i])) return KDA_ERR_MISALIGNED;
     const size_t ei = esize(in_dtype), eo = esize(out_dtype);
     const Range rq = range_of(q, nh * dk * ei), rk = range_of(k, nh * dk * ei),
                 rv = range_of(v, nh * dv * ei), rg = range_of(g, nh * dk * 4), rb = range_of(beta, nh * 4),

@@ -432,7 +432,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             sKt[c * LDT + t] = from_f32<T>(bt * k0 * ei0);
             sKt[(c + 1) * LDT + t] = from_f32<T>(bt * k1 * ei1);
             Pair2<T>::store(gQt + t * DK + c, q0 * ei0, q1 * ei1);
-            Pair2<T>::store(gKb + t * DK + c, k0 * eo0, k1 * eo1);
+            gKb[c * C + t] = from_f32<T>(k0 * eo0);            // Kb stored transposed: [dk][C]
+            gKb[(c + 1) * C + t] = from_f32<T>(k1 * eo1);
         }
     }
     if (tid < DK) {
@@ -462,8 +463,382 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     }
 }
 
+// ================================================================ stage 1, bf16 / C = 64
+// The hot configuration.  Same workspace contents as chunk_intra_kernel, with:
+//  - 512 threads; every global load of the chunk is issued before any use;
+//  - two exponentials per (token, channel): E = e^{L} and F = e^{tot - L}
+//    (L the 16-token block-local prefix sum, tot the block sum), the other
+//    decay factors being products of per-(block, channel) factors <= 1;
+//  - all MFMA operands materialised once in LDS, every output stored from LDS
+//    staging in 16-byte rows;
+//  - beta folded into the triangular factor: U = (T Diag(beta)) V and
+//    Wk = (T Diag(beta)) (e^G * K).
+// Pairs of 16-token blocks (R, I) and their operands (Kr = k e^{L},
+// Kf = k e^{tot - L}, Kd = k e^{-L}; b_J = e^{tot_J}):
+//   (1,0) (3,2): Kr_R . Kf_I           (2,1): Kr_2 . Kf_1
+//   (2,0): Kr_2 . (b_1 Kf_0)            (3,1): (b_2 Kr_3) . Kf_1
+//   (3,0): (b_2 Kr_3) . (b_1 Kf_0)      (R,R): Kr_R . Kd_R
+template <int DK, int DV>
+struct Intra64Cfg {
+    static constexpr int C = 64, NB = 4, NT = 512, NW = 8;
+    static constexpr int LDK = DK + 8;           // bf16 rows over channels
+    static constexpr int LDT = C + 8;            // bf16 rows over positions
+    static constexpr int LDA = C + 8;            // fp32 rows of the C x C matrices
+    static constexpr int NGRP = (C / 16) * (DK / 32), NIT = NGRP / NW;     // q, k, g units
+    static constexpr int NGRPV = (C / 16) * (DV / 32), NITV = NGRPV / NW;  // v units
+    static constexpr size_t SZ_OPF = size_t(C) * LDK * 2, SZ_OPB = size_t(16) * LDK * 2;
+    static constexpr size_t OFF_G = 0;
+    static constexpr size_t OFF_KR = OFF_G + size_t(C) * DK * 4;
+    static constexpr size_t OFF_QR = OFF_KR + SZ_OPF;
+    static constexpr size_t OFF_KF = OFF_QR + SZ_OPF;
+    static constexpr size_t OFF_KD = OFF_KF + SZ_OPF;
+    static constexpr size_t OFF_KR3 = OFF_KD + SZ_OPF;
+    static constexpr size_t OFF_QR3 = OFF_KR3 + SZ_OPB;
+    static constexpr size_t OFF_KF0 = OFF_QR3 + SZ_OPB;
+    static constexpr size_t OFF_KT = OFF_KF0 + SZ_OPB;                 // (e^G k)^T [DK][LDT], kept
+    static constexpr size_t OFF_KB = OFF_KT + size_t(DK) * LDT * 2;     // Kb^T staging [DK][C]
+    static constexpr size_t OFF_TOT = OFF_KB + size_t(DK) * C * 2;
+    static constexpr size_t OFF_EBASE = OFF_TOT + size_t(NB) * DK * 4;
+    static constexpr size_t OFF_EREST = OFF_EBASE + size_t(NB) * DK * 4;
+    static constexpr size_t OFF_ENEG = OFF_EREST + size_t(NB) * DK * 4;
+    static constexpr size_t OFF_B1 = OFF_ENEG + size_t(NB) * DK * 4;
+    static constexpr size_t OFF_B2 = OFF_B1 + size_t(DK) * 4;
+    static constexpr size_t OFF_BETA = OFF_B2 + size_t(DK) * 4;
+    static constexpr size_t OFF_FLAG = OFF_BETA + size_t(C) * 4;
+    static constexpr size_t TOTAL = OFF_FLAG + 16;
+    // after the score matrices: aliases [0, OFF_KT)
+    static constexpr size_t OFF_A = 0;
+    static constexpr size_t OFF_PB = OFF_A + size_t(C) * LDA * 4;
+    static constexpr size_t OFF_X = OFF_PB + size_t(C) * C * 2;
+    static constexpr size_t OFF_TB = OFF_X + size_t(C / 2) * (C / 2 + 4) * 4;
+    static constexpr size_t OFF_VT = OFF_TB + size_t(C) * LDT * 2;
+    static constexpr size_t OFF_UO = OFF_VT + size_t(DV) * LDT * 2;
+    static constexpr size_t OFF_WO = OFF_UO + size_t(C) * DV * 4;
+    static constexpr size_t END_W = OFF_WO + size_t(C) * DK * 2;
+    static_assert(END_W <= OFF_KT, "phase-W buffers overlap the kept K~^T");
+    static_assert(TOTAL <= LDS_LIMIT, "LDS budget");
+    static_assert(NIT >= 1 && NITV >= 1 && NGRP % NW == 0 && NGRPV % NW == 0, "unit mapping");
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void chunk_intra64_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    bf16* __restrict__ ws_qt, bf16* __restrict__ ws_wk, bf16* __restrict__ ws_kb, bf16* __restrict__ ws_p,
+    float* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC) {
+    typedef Intra64Cfg<DK, DV> Cfg;
+    constexpr int C = 64, NB = 4, NT = 512, NW = 8, LDK = Cfg::LDK, LDT = Cfg::LDT, LDA = Cfg::LDA;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    float* sG = reinterpret_cast<float*>(smem + Cfg::OFF_G);
+    bf16* sKr = reinterpret_cast<bf16*>(smem + Cfg::OFF_KR);
+    bf16* sQr = reinterpret_cast<bf16*>(smem + Cfg::OFF_QR);
+    bf16* sKf = reinterpret_cast<bf16*>(smem + Cfg::OFF_KF);
+    bf16* sKd = reinterpret_cast<bf16*>(smem + Cfg::OFF_KD);
+    bf16* sKr3 = reinterpret_cast<bf16*>(smem + Cfg::OFF_KR3);
+    bf16* sQr3 = reinterpret_cast<bf16*>(smem + Cfg::OFF_QR3);
+    bf16* sKf0 = reinterpret_cast<bf16*>(smem + Cfg::OFF_KF0);
+    bf16* sKtT = reinterpret_cast<bf16*>(smem + Cfg::OFF_KT);
+    bf16* sKbT = reinterpret_cast<bf16*>(smem + Cfg::OFF_KB);
+    float* sTot = reinterpret_cast<float*>(smem + Cfg::OFF_TOT);
+    float* sEBase = reinterpret_cast<float*>(smem + Cfg::OFF_EBASE);
+    float* sERest = reinterpret_cast<float*>(smem + Cfg::OFF_EREST);
+    float* sENeg = reinterpret_cast<float*>(smem + Cfg::OFF_ENEG);
+    float* sB1 = reinterpret_cast<float*>(smem + Cfg::OFF_B1);
+    float* sB2 = reinterpret_cast<float*>(smem + Cfg::OFF_B2);
+    float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_BETA);
+    int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const long ch = blockIdx.x;
+    const int n = (int)(ch % NC);
+    const long bh = ch / NC;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int t0 = n * C;
+    auto grow = [&](int t) -> long { return ((long)b * T_len + (t0 + t)) * H + h; };
+    auto valid = [&](int t) -> bool { return t0 + t < T_len; };
+    // unit (it): 16 rows x 4 eight-channel groups per wave; lane -> row, group
+    auto unit_t = [&](int it, int ncg) { return ((wave + NW * it) / ncg) * 16 + (lane & 15); };
+    auto unit_c = [&](int it, int ncg) { return (((wave + NW * it) % ncg) * 4 + (lane >> 4)) * 8; };
+    constexpr int NCG = DK / 32, NCGV = DV / 32;
+
+    // ---------------------------------------------------------------- loads
+    bf16x8 qv[Cfg::NIT], kv[Cfg::NIT], vv[Cfg::NITV];
+    floatx4 ga[Cfg::NIT], gb[Cfg::NIT];
+#pragma unroll
+    for (int it = 0; it < Cfg::NIT; ++it) {
+        const int t = unit_t(it, NCG), c = unit_c(it, NCG);
+        if (valid(t)) {
+            const long base = grow(t) * DK + c;
+            qv[it] = *reinterpret_cast<const bf16x8*>(q + base);
+            kv[it] = *reinterpret_cast<const bf16x8*>(k + base);
+            ga[it] = *reinterpret_cast<const floatx4*>(g + base);
+            gb[it] = *reinterpret_cast<const floatx4*>(g + base + 4);
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) { qv[it][m] = (bf16)0.f; kv[it][m] = (bf16)0.f; }
+            ga[it] = zero4(); gb[it] = zero4();
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < Cfg::NITV; ++it) {
+        const int t = unit_t(it, NCGV), j = unit_c(it, NCGV);
+        if (valid(t)) vv[it] = *reinterpret_cast<const bf16x8*>(v + grow(t) * DV + j);
+        else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) vv[it][m] = (bf16)0.f;
+        }
+    }
+    if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
+    if (tid < NB) sFlag[tid] = 0;
+#pragma unroll
+    for (int it = 0; it < Cfg::NIT; ++it) {
+        const int t = unit_t(it, NCG), c = unit_c(it, NCG);
+        *reinterpret_cast<floatx4*>(sG + t * DK + c) = ga[it];
+        *reinterpret_cast<floatx4*>(sG + t * DK + c + 4) = gb[it];
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- a1: block-local scans
+    for (int u = tid; u < NB * DK; u += NT) {
+        const int R = u / DK, c = u % DK;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) x[rr] = sG[(R * 16 + rr) * DK + c];
+        float l = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) { l += clamp_g(x[rr]); x[rr] = l; }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sG[(R * 16 + rr) * DK + c] = x[rr];
+        sTot[R * DK + c] = l;
+        if (l < -SAFE_SPAN) sFlag[R] = 1;
+    }
+    __syncthreads();
+    // per-(block, channel) factors, all <= 1 except e^{-tot} (used only when safe)
+    for (int u = tid; u < NB * DK; u += NT) {
+        const int R = u / DK, c = u % DK;
+        float tb[NB];
+#pragma unroll
+        for (int J = 0; J < NB; ++J) tb[J] = sTot[J * DK + c];
+        float base = 0.f, rest = 0.f;
+#pragma unroll
+        for (int J = 0; J < NB; ++J) { if (J < R) base += tb[J]; if (J > R) rest += tb[J]; }
+        sEBase[u] = __expf(base);
+        sERest[u] = __expf(rest);
+        sENeg[u] = tb[R] >= -SAFE_SPAN ? __expf(-tb[R]) : 0.f;
+        if (R == 0) {
+            sB1[c] = __expf(tb[1]);
+            sB2[c] = __expf(tb[2]);
+            ws_gam[ch * DK + c] = __expf(tb[0] + tb[1] + tb[2] + tb[3]);
+        }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- a2: decayed operands
+    bf16* gQt = ws_qt + ch * (long)C * DK;
+#pragma unroll
+    for (int it = 0; it < Cfg::NIT; ++it) {
+        const int t = unit_t(it, NCG), c = unit_c(it, NCG);
+        const int R = t >> 4, rr = t & 15;
+        float L[8], tt[8], eb[8], er[8], en[8];
+        Vec8<float>::load(sG + t * DK + c, L);
+        Vec8<float>::load(sTot + R * DK + c, tt);
+        Vec8<float>::load(sEBase + R * DK + c, eb);
+        Vec8<float>::load(sERest + R * DK + c, er);
+        Vec8<float>::load(sENeg + R * DK + c, en);
+        float kr[8], qr[8], kf[8], o1[8], o2[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float E = __expf(L[m]), F = __expf(tt[m] - L[m]);
+            const float kk = (float)kv[it][m], qq = (float)qv[it][m];
+            kr[m] = kk * E; qr[m] = qq * E; kf[m] = kk * F;
+        }
+        Vec8<bf16>::store(sKr + t * LDK + c, kr);
+        Vec8<bf16>::store(sQr + t * LDK + c, qr);
+        Vec8<bf16>::store(sKf + t * LDK + c, kf);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o1[m] = kf[m] * en[m];
+        Vec8<bf16>::store(sKd + t * LDK + c, o1);
+        if (R == 3) {
+            float b2[8];
+            Vec8<float>::load(sB2 + c, b2);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) { o1[m] = kr[m] * b2[m]; o2[m] = qr[m] * b2[m]; }
+            Vec8<bf16>::store(sKr3 + rr * LDK + c, o1);
+            Vec8<bf16>::store(sQr3 + rr * LDK + c, o2);
+        } else if (R == 0) {
+            float b1[8];
+            Vec8<float>::load(sB1 + c, b1);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) o1[m] = kf[m] * b1[m];
+            Vec8<bf16>::store(sKf0 + rr * LDK + c, o1);
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o1[m] = qr[m] * eb[m];                  // e^G q
+        Vec8<bf16>::store(gQt + t * DK + c, o1);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]);                // e^G k
+            sKbT[(c + m) * C + t] = (bf16)(kf[m] * er[m]);                  // e^{G_last - G} k
+        }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- a3: A and P
+    {
+        bf16* gKb = ws_kb + ch * (long)DK * C;
+        for (int u = tid; u < DK * C / 8; u += NT)
+            reinterpret_cast<uint4*>(gKb)[u] = reinterpret_cast<const uint4*>(sKbT)[u];
+    }
+    floatx4 accA[2], accP[2];
+    accA[0] = accA[1] = accP[0] = accP[1] = zero4();
+    static_for<10>([&](auto PI) {
+        constexpr int p = PI;
+        constexpr int R = pair_R(p), I = pair_I(p);
+        if (wave == p % NW) {
+            constexpr int s = p / NW;
+            const bf16* rk = (R == 3 && I < 2) ? sKr3 : sKr + R * 16 * LDK;
+            const bf16* rq = (R == 3 && I < 2) ? sQr3 : sQr + R * 16 * LDK;
+            const bf16* ck = (R == I) ? sKd + I * 16 * LDK
+                           : (I == 0 && R >= 2) ? sKf0 : sKf + I * 16 * LDK;
+            if (R != I || !sFlag[R]) {
+                mma_tile2<bf16>(accA[s], accP[s], rk, rq, LDK, ck, LDK, DK, lane);
+            } else {
+                // term-by-term: e^{L_r - L_i}, both sums block-local, r >= i
+                const int i = R * 16 + (lane & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = R * 16 + 4 * (lane >> 4) + e;
+                    float sa = 0.f, sp = 0.f;
+                    if (i <= r && valid(r)) {
+                        for (int c = 0; c < DK; ++c) {
+                            const float w = __expf(sG[r * DK + c] - sG[i * DK + c]);
+                            const float ki = (float)k[grow(i) * DK + c];
+                            sa += (float)k[grow(r) * DK + c] * ki * w;
+                            sp += (float)q[grow(r) * DK + c] * ki * w;
+                        }
+                    }
+                    accA[s][e] = sa;
+                    accP[s][e] = sp;
+                }
+            }
+        }
+    });
+    __syncthreads();
+
+    // ---------------------------------------------------------------- M = Diag(beta) A, P
+    float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
+    bf16* sPb = reinterpret_cast<bf16*>(smem + Cfg::OFF_PB);
+    for (int u = tid; u < C * C; u += NT) {
+        const int r = u / C, i = u % C;
+        if (r / 16 < i / 16) { sA[r * LDA + i] = 0.f; sPb[u] = (bf16)0.f; }
+    }
+    static_for<10>([&](auto PI) {
+        constexpr int p = PI;
+        constexpr int R = pair_R(p), I = pair_I(p);
+        if (wave == p % NW) {
+            constexpr int s = p / NW;
+            const int i = I * 16 + (lane & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = R * 16 + 4 * (lane >> 4) + e;
+                float av = accA[s][e], pv = accP[s][e];
+                if (R == I) { if (i >= r) av = 0.f; if (i > r) pv = 0.f; }
+                sA[r * LDA + i] = sBeta[r] * av;
+                sPb[r * C + i] = (bf16)pv;
+            }
+        }
+    });
+    __syncthreads();
+    {
+        bf16* gP = ws_p + ch * (long)C * C;
+        for (int u = tid; u < C * C / 8; u += NT)
+            reinterpret_cast<uint4*>(gP)[u] = reinterpret_cast<const uint4*>(sPb)[u];
+    }
+
+    // ---------------------------------------------------------------- a4: T = (I + M)^-1
+    if (wave == 0) {
+        const int bd = lane >> 4, j = lane & 15;
+        float* Mb = sA + (bd * 16) * LDA + bd * 16;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) s -= Mb[r * LDA + i] * x[i];
+            x[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Mb[r * LDA + j] = x[r];
+    }
+    __syncthreads();
+    float* sX = reinterpret_cast<float*>(smem + Cfg::OFF_X);
+    static_for<2>([&](auto LH) {
+        constexpr int HH = 16 << LH, NM = C / (2 * HH), HT = HH / 16, NTL = NM * HT * HT, LDX = HH + 4;
+        for (int tt = wave; tt < NTL; tt += NW) {
+            const int m = tt / (HT * HT), a = (tt / HT) % HT, bc = tt % HT, base = m * 2 * HH;
+            floatx4 acc = mma_f32_rowB(zero4(), sA + (base + HH + a * 16) * LDA + base, LDA,
+                                       sA + base * LDA + base + bc * 16, LDA, HH, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sX[m * HH * LDX + (a * 16 + 4 * (lane >> 4) + e) * LDX + bc * 16 + (lane & 15)] = acc[e];
+        }
+        __syncthreads();
+        for (int tt = wave; tt < NTL; tt += NW) {
+            const int m = tt / (HT * HT), a = (tt / HT) % HT, bc = tt % HT, base = m * 2 * HH;
+            floatx4 acc = mma_f32_rowB(zero4(), sA + (base + HH + a * 16) * LDA + base + HH, LDA,
+                                       sX + m * HH * LDX + bc * 16, LDX, HH, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sA[(base + HH + a * 16 + 4 * (lane >> 4) + e) * LDA + base + bc * 16 + (lane & 15)] = -acc[e];
+        }
+        __syncthreads();
+    });
+
+    // ---------------------------------------------------------------- U, Wk
+    bf16* sTb = reinterpret_cast<bf16*>(smem + Cfg::OFF_TB);
+    bf16* sVt = reinterpret_cast<bf16*>(smem + Cfg::OFF_VT);
+    for (int u = tid; u < C * C; u += NT) {
+        const int r = u / C, i = u % C;
+        sTb[r * LDT + i] = (bf16)(sA[r * LDA + i] * sBeta[i]);             // T Diag(beta)
+    }
+#pragma unroll
+    for (int it = 0; it < Cfg::NITV; ++it) {
+        const int t = unit_t(it, NCGV), j = unit_c(it, NCGV);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sVt[(j + m) * LDT + t] = vv[it][m];
+    }
+    __syncthreads();
+    float* sUo = reinterpret_cast<float*>(smem + Cfg::OFF_UO);
+    bf16* sWo = reinterpret_cast<bf16*>(smem + Cfg::OFF_WO);
+    constexpr int NTU = 4 * (DV / 16), NTWK = 4 * (DK / 16);
+    for (int tt = wave; tt < NTU + NTWK; tt += NW) {
+        const bool isU = tt < NTU;
+        const int t2 = isU ? tt : tt - NTU;
+        const int ncol = isU ? DV / 16 : DK / 16;
+        const int R = t2 / ncol, J = t2 % ncol;
+        const int K = R < 2 ? 32 : 64;
+        const bf16* bsrc = isU ? sVt + J * 16 * LDT : sKtT + J * 16 * LDT;
+        floatx4 acc = mma_tile<bf16>(zero4(), sTb + R * 16 * LDT, LDT, bsrc, LDT, K, lane);
+        const int col = J * 16 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = R * 16 + 4 * (lane >> 4) + e;
+            if (isU) sUo[row * DV + col] = acc[e];
+            else sWo[row * DK + col] = (bf16)acc[e];
+        }
+    }
+    __syncthreads();
+    {
+        uint4* gU = reinterpret_cast<uint4*>(ws_u + ch * (long)C * DV);
+        for (int u = tid; u < C * DV / 4; u += NT) gU[u] = reinterpret_cast<const uint4*>(sUo)[u];
+        uint4* gW = reinterpret_cast<uint4*>(ws_wk + ch * (long)C * DK);
+        for (int u = tid; u < C * DK / 8; u += NT) gW[u] = reinterpret_cast<const uint4*>(sWo)[u];
+    }
+}
+
 // ================================================================ stage 2: chain
-template <typename T, int DK, int DV, int C, int DVS>
+template <typename T, typename TOut, int DK, int DV, int C, int DVS>
 struct ChainCfg {
     static constexpr int PADT = sizeof(T) == 2 ? 8 : 4;
     static constexpr int LDK = DK + PADT;
@@ -473,6 +848,13 @@ struct ChainCfg {
     static constexpr int NTW = (C / 16) * NJ;               // W / O tiles
     static constexpr int NTS = (DK / 16) * NJ;              // state tiles
     static constexpr int NSW = (NTW + 3) / 4, NSS = (NTS + 3) / 4;
+    // prefetch units of 16 bytes: Qt, Wk, Kb^T, P (input dtype), U slice, gam (fp32)
+    static constexpr int E16 = 16 / sizeof(T);
+    static constexpr int U_QT = C * DK / E16, U_WK = U_QT, U_KB = DK * C / E16, U_P = C * C / E16;
+    static constexpr int U_U = C * DVS / 4, U_G = DK / 4;
+    static constexpr int B1 = U_QT, B2 = B1 + U_WK, B3 = B2 + U_KB, B4 = B3 + U_P, B5 = B4 + U_U;
+    static constexpr int NU = B5 + U_G;
+    static constexpr int NUPT = (NU + 255) / 256;
     static constexpr size_t SZ_QT = size_t(C) * LDK * sizeof(T);
     static constexpr size_t SZ_KBT = align16(size_t(DK) * LDC * sizeof(T));
     static constexpr size_t SZ_P = align16(size_t(C) * LDC * sizeof(T));
@@ -480,6 +862,7 @@ struct ChainCfg {
     static constexpr size_t SZ_GAM = size_t(DK) * 4;
     static constexpr size_t SZ_ST = size_t(DVS) * LDK * sizeof(T);
     static constexpr size_t SZ_WT = align16(size_t(DVS) * LDC * sizeof(T));
+    static constexpr size_t SZ_O = align16(size_t(C) * DVS * sizeof(TOut));
     static constexpr size_t OFF_WK = SZ_QT;
     static constexpr size_t OFF_KBT = OFF_WK + SZ_QT;
     static constexpr size_t OFF_P = OFF_KBT + SZ_KBT;
@@ -487,8 +870,11 @@ struct ChainCfg {
     static constexpr size_t OFF_GAM = OFF_U + SZ_U;
     static constexpr size_t OFF_ST = OFF_GAM + SZ_GAM;
     static constexpr size_t OFF_WT = OFF_ST + SZ_ST;
-    static constexpr size_t TOTAL = OFF_WT + SZ_WT;
-    static constexpr bool FITS = TOTAL <= LDS_LIMIT;
+    static constexpr size_t OFF_O = OFF_WT + SZ_WT;
+    // outputs are staged in LDS for 16-byte row stores when there is room
+    static constexpr bool STAGE_O = OFF_O + SZ_O <= LDS_LIMIT && (DVS * sizeof(TOut)) % 16 == 0;
+    static constexpr size_t TOTAL = STAGE_O ? OFF_O + SZ_O : OFF_O;
+    static constexpr bool FITS = TOTAL <= LDS_LIMIT && NUPT <= 40 && U_G <= 256;
 };
 
 template <typename T, typename TOut, int DK, int DV, int C, int DVS>
@@ -497,8 +883,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     const T* __restrict__ ws_p, const float* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT,
     int T_len, int H, int NC) {
-    typedef ChainCfg<T, DK, DV, C, DVS> Cfg;
-    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, CK = Cfg::CK, NJ = Cfg::NJ;
+    typedef ChainCfg<T, TOut, DK, DV, C, DVS> Cfg;
+    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, CK = Cfg::CK, NJ = Cfg::NJ, E16 = Cfg::E16;
     constexpr int NTW = Cfg::NTW, NTS = Cfg::NTS, KSTEP = Mma<T>::KSTEP;
     constexpr int NSL = DV / DVS;
 
@@ -511,11 +897,89 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     float* sGam = reinterpret_cast<float*>(smem + Cfg::OFF_GAM);
     T* sST = reinterpret_cast<T*>(smem + Cfg::OFF_ST);
     T* sWT = reinterpret_cast<T*>(smem + Cfg::OFF_WT);
+    TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const long bh = blockIdx.x / NSL;
-    const int j0 = (int)(blockIdx.x % NSL) * DVS;
+    // Slices of one head share an XCD (workgroups are dealt to the 8 XCDs
+    // round-robin), so the per-chunk operands they all read come from one L2.
+    long bh;
+    int sl;
+    {
+        const long nwg = (long)gridDim.x, id = blockIdx.x;
+        if (nwg % (8 * NSL) == 0) {
+            const long xcd = id % 8, local = id / 8;
+            sl = (int)(local % NSL);
+            bh = (local / NSL) * 8 + xcd;
+        } else {
+            bh = id / NSL;
+            sl = (int)(id % NSL);
+        }
+    }
+    const int j0 = sl * DVS;
     const int b = (int)(bh / H), h = (int)(bh % H);
+
+    // ---- register prefetch of one chunk's operands (16-byte units), one
+    // statically sized register array per operand
+    constexpr int PQ = (Cfg::U_QT + 255) / 256, PK = (Cfg::U_KB + 255) / 256, PP = (Cfg::U_P + 255) / 256,
+                  PU = (Cfg::U_U + 255) / 256;
+    u32x4 preQ[PQ], preW[PQ], preK[PK], preP[PP], preU[PU], preG;
+#define KDA_CHAIN_PREFETCH(CH)                                                                     \
+    {                                                                                              \
+        const long ch_ = (CH);                                                                     \
+        const u32x4* gq_ = reinterpret_cast<const u32x4*>(ws_qt + ch_ * (long)C * DK);             \
+        const u32x4* gw_ = reinterpret_cast<const u32x4*>(ws_wk + ch_ * (long)C * DK);             \
+        const u32x4* gk_ = reinterpret_cast<const u32x4*>(ws_kb + ch_ * (long)DK * C);             \
+        const u32x4* gp_ = reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)C * C);               \
+        const float* gu_ = ws_u + ch_ * (long)C * DV + j0;                                         \
+        _Pragma("unroll") for (int i = 0; i < PQ; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_QT) { preQ[i] = gq_[u]; preW[i] = gw_[u]; }                             \
+        }                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_KB) preK[i] = gk_[u];                                                   \
+        }                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_P) preP[i] = gp_[u];                                                    \
+        }                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < PU; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_U)                                                                      \
+                preU[i] = *reinterpret_cast<const u32x4*>(gu_ + (long)(u / (DVS / 4)) * DV + 4 * (u % (DVS / 4))); \
+        }                                                                                          \
+        if (tid < Cfg::U_G) preG = reinterpret_cast<const u32x4*>(ws_gam + ch_ * (long)DK)[tid];  \
+    }
+#define KDA_CHAIN_COMMIT()                                                                         \
+    {                                                                                              \
+        _Pragma("unroll") for (int i = 0; i < PQ; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_QT) {                                                                   \
+                const int e = u * E16;                                                             \
+                *reinterpret_cast<u32x4*>(sQt + (e / DK) * LDK + e % DK) = preQ[i];                \
+                *reinterpret_cast<u32x4*>(sWk + (e / DK) * LDK + e % DK) = preW[i];                \
+            }                                                                                      \
+        }                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_KB) {                                                                   \
+                const int e = u * E16;                                                             \
+                *reinterpret_cast<u32x4*>(sKbT + (e / C) * LDC + e % C) = preK[i];                 \
+            }                                                                                      \
+        }                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_P) {                                                                    \
+                const int e = u * E16;                                                             \
+                *reinterpret_cast<u32x4*>(sP + (e / C) * LDC + e % C) = preP[i];                   \
+            }                                                                                      \
+        }                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < PU; ++i) {                                           \
+            const int u = tid + 256 * i;                                                           \
+            if (u < Cfg::U_U) reinterpret_cast<u32x4*>(sU)[u] = preU[i];                           \
+        }                                                                                          \
+        if (tid < Cfg::U_G) reinterpret_cast<u32x4*>(sGam)[tid] = preG;                            \
+    }
 
     // zero the contraction padding once (columns C..CK never receive data)
     if constexpr (CK > C) {
@@ -526,6 +990,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
             else sWT[(row - DK - C) * LDC + i] = from_f32<T>(0.f);
         }
     }
+
+    if (NC > 0) KDA_CHAIN_PREFETCH(bh * NC);
 
     floatx4 accS[Cfg::NSS];
     static_for<Cfg::NSS>([&](auto SI) {
@@ -541,6 +1007,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
             }
         }
     });
+    // S^T as the B operand of the products with S: sST[j][c], 4 consecutive c per lane
     auto write_state_operand = [&]() {
         static_for<Cfg::NSS>([&](auto SI) {
             constexpr int s = SI;
@@ -556,34 +1023,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     write_state_operand();
 
     for (int n = 0; n < NC; ++n) {
-        const long ch = bh * NC + n;
-        // ---- stage the chunk's operands in LDS
-        {
-            const T* gq = ws_qt + ch * (long)C * DK;
-            const T* gw = ws_wk + ch * (long)C * DK;
-            const T* gk = ws_kb + ch * (long)C * DK;
-            for (int u = tid; u < C * (DK / 8); u += 256) {
-                const int r = u / (DK / 8), c = 8 * (u % (DK / 8));
-                float x[8];
-                Vec8<T>::load(gq + r * DK + c, x); Vec8<T>::store(sQt + r * LDK + c, x);
-                Vec8<T>::load(gw + r * DK + c, x); Vec8<T>::store(sWk + r * LDK + c, x);
-                Vec8<T>::load(gk + r * DK + c, x);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) sKbT[(c + m) * LDC + r] = from_f32<T>(x[m]);
-            }
-            const T* gp = ws_p + ch * (long)C * C;
-            for (int u = tid; u < C * (C / 8 > 0 ? C / 8 : 1); u += 256) {
-                const int r = u / (C / 8), i = 8 * (u % (C / 8));
-                float x[8];
-                Vec8<T>::load(gp + r * C + i, x); Vec8<T>::store(sP + r * LDC + i, x);
-            }
-            const float* gu = ws_u + ch * (long)C * DV + j0;
-            for (int u = tid; u < C * (DVS / 4); u += 256) {
-                const int r = u / (DVS / 4), j = 4 * (u % (DVS / 4));
-                *reinterpret_cast<float4*>(sU + r * DVS + j) = *reinterpret_cast<const float4*>(gu + r * DV + j);
-            }
-            if (tid < DK) sGam[tid] = ws_gam[ch * DK + tid];
-        }
+        KDA_CHAIN_COMMIT();                                    // chunk n operands -> LDS
+        if (n + 1 < NC) KDA_CHAIN_PREFETCH(bh * NC + n + 1);  // in flight during this chunk
         __syncthreads();
 
         // ---- W = U - Wk S (to LDS, transposed) and the state part of O
@@ -603,7 +1044,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         });
         __syncthreads();
 
-        // ---- O += P W, store O ; S = gam * S + Kb^T W
+        // ---- O += P W ; S = gam * S + Kb^T W
         static_for<Cfg::NSW>([&](auto SI) {
             constexpr int s = SI;
             const int tw = wave + 4 * s;
@@ -614,8 +1055,13 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
                 const int j = J * 16 + (lane & 15);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = n * C + R * 16 + 4 * (lane >> 4) + e;
-                    if (t < T_len) o[(((long)b * T_len + t) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[s][e]);
+                    const int r = R * 16 + 4 * (lane >> 4) + e;
+                    if constexpr (Cfg::STAGE_O) {
+                        sO[r * DVS + j] = from_f32<TOut>(accO[s][e]);
+                    } else {
+                        const int t = n * C + r;
+                        if (t < T_len) o[(((long)b * T_len + t) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[s][e]);
+                    }
                 }
             }
         });
@@ -630,6 +1076,17 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
             }
         });
         __syncthreads();
+        if constexpr (Cfg::STAGE_O) {
+            constexpr int EO = 16 / sizeof(TOut);
+            constexpr int NUO = C * DVS / EO;
+            for (int u = tid; u < NUO; u += 256) {
+                const int r = (u * EO) / DVS, jj = (u * EO) % DVS;
+                const int t = n * C + r;
+                if (t < T_len)
+                    *reinterpret_cast<u32x4*>(o + (((long)b * T_len + t) * H + h) * DV + j0 + jj) =
+                        *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
+            }
+        }
         write_state_operand();
     }
 
@@ -648,6 +1105,9 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         });
     }
 }
+
+#undef KDA_CHAIN_PREFETCH
+#undef KDA_CHAIN_COMMIT
 
 // ================================================================ host side
 static inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -689,7 +1149,7 @@ static hipError_t launch_intra(const ChunkArgs& a) {
 
 template <typename T, typename TOut, int DK, int DV, int C, int DVS>
 static hipError_t launch_chain_dvs(const ChunkArgs& a) {
-    typedef ChainCfg<T, DK, DV, C, DVS> Cfg;
+    typedef ChainCfg<T, TOut, DK, DV, C, DVS> Cfg;
     if constexpr (!Cfg::FITS || DVS > DV) {
         return hipErrorInvalidValue;
     } else {
@@ -706,17 +1166,17 @@ static hipError_t launch_chain_dvs(const ChunkArgs& a) {
     }
 }
 
-template <typename T, int DK, int DV, int C, int DVS>
-static constexpr bool chain_fits() { return DVS <= DV && ChainCfg<T, DK, DV, C, DVS>::FITS; }
+template <typename T, typename TOut, int DK, int DV, int C, int DVS>
+static constexpr bool chain_fits() { return DVS <= DV && ChainCfg<T, TOut, DK, DV, C, DVS>::FITS; }
 
 // Value-column slice width: enough workgroups to cover the chip (>= 256 when
 // possible), as wide as possible otherwise, and within the LDS budget.
-template <typename T, int DK, int DV, int C>
+template <typename T, typename TOut, int DK, int DV, int C>
 static int pick_dvs(long bh) {
     int dvs = 16;
     const int cands[3] = {64, 32, 16};
-    const bool fits[3] = {chain_fits<T, DK, DV, C, 64>(), chain_fits<T, DK, DV, C, 32>(),
-                          chain_fits<T, DK, DV, C, 16>()};
+    const bool fits[3] = {chain_fits<T, TOut, DK, DV, C, 64>(), chain_fits<T, TOut, DK, DV, C, 32>(),
+                          chain_fits<T, TOut, DK, DV, C, 16>()};
     for (int i = 0; i < 3; ++i) {
         if (!fits[i]) continue;
         dvs = cands[i];
@@ -727,7 +1187,7 @@ static int pick_dvs(long bh) {
 
 template <typename T, typename TOut, int DK, int DV, int C>
 static hipError_t launch_chain(const ChunkArgs& a) {
-    const int dvs = pick_dvs<T, DK, DV, C>((long)a.B * a.H);
+    const int dvs = pick_dvs<T, TOut, DK, DV, C>((long)a.B * a.H);
     if (dvs == 64) return launch_chain_dvs<T, TOut, DK, DV, C, 64>(a);
     if (dvs == 32) return launch_chain_dvs<T, TOut, DK, DV, C, 32>(a);
     return launch_chain_dvs<T, TOut, DK, DV, C, 16>(a);
@@ -735,7 +1195,7 @@ static hipError_t launch_chain(const ChunkArgs& a) {
 
 template <typename T, int DK, int DV, int C>
 static constexpr bool combo_fits() {
-    return IntraCfg<T, DK, DV, C>::FITS && chain_fits<T, DK, DV, C, 16>();
+    return IntraCfg<T, DK, DV, C>::FITS && chain_fits<T, float, DK, DV, C, 16>();
 }
 
 bool chunk_supported(int dk, int dv, int C, bool in_bf16) {
@@ -751,8 +1211,27 @@ bool chunk_supported(int dk, int dv, int C, bool in_bf16) {
     return false;
 }
 
+template <int DK, int DV>
+static hipError_t launch_intra64(const ChunkArgs& a) {
+    const int NC = (a.T + 63) / 64;
+    const long nch = (long)a.B * a.H * NC;
+    if (nch == 0) return hipSuccess;
+    const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, true, 64);
+    char* ws = (char*)a.ws;
+    hipLaunchKernelGGL((chunk_intra64_kernel<DK, DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
+                       (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
+                       (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
+    return hipGetLastError();
+}
+
 template <typename T, int DK, int DV>
 static hipError_t intra_c(const ChunkArgs& a) {
+    if constexpr (sizeof(T) == 2) {
+        if constexpr (DK == 128) {
+            if (a.C == 64 && !a.generic) return launch_intra64<DK, DV>(a);
+        }
+    }
     switch (a.C) {
         case 16: return launch_intra<T, DK, DV, 16>(a);
         case 32: return launch_intra<T, DK, DV, 32>(a);

@@ -23,6 +23,7 @@ struct ChunkArgs {
     bool in_bf16, out_bf16;
     void* ws; size_t ws_bytes;
     hipStream_t stream;
+    bool generic = false;   // force the generic intra-chunk kernel (tests)
 };
 
 // Workspace of the split chunk path, per (b, h, chunk), struct of arrays:

@@ -99,7 +99,8 @@ def test_chunk_validation_codes(fn):
         (dict(dk=96), UNSUP), (dict(dv=32), UNSUP), (dict(C=48), UNSUP), (dict(C=256), UNSUP),
         (dict(ind=5), UNSUP), (dict(outd=-1), UNSUP),
         (dict(q=None), NULL), (dict(beta=None), NULL), (dict(o=None), NULL),
-        (dict(k=a["k"] + 8), MISAL), (dict(s0=a["s0"] + 4), MISAL),
+        (dict(k=a["k"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(s0=a["s0"] + 2), MISAL),
+        (dict(ws=a["ws"] + 8), MISAL), (dict(o=a["o"] + 4), MISAL),
         (dict(ws=None), WS), (dict(wsb=a["wsb"] - 1), WS),
         (dict(o=a["q"]), ALIAS), (dict(o=a["ws"]), ALIAS), (dict(sT=a["v"]), ALIAS),
         (dict(sT=a["s0"] + 256), ALIAS), (dict(ws=a["g"]), ALIAS), (dict(o=a["sT"]), ALIAS),
@@ -110,8 +111,9 @@ def test_chunk_validation_codes(fn):
         assert call_chunk(b, fn) == code, (change, code)
 
 
-def test_fp32_c128_dk128_is_unsupported():
-    a = chunk_args(dk=128, dv=128, C=128)
+@pytest.mark.parametrize("dk", [64, 128])
+def test_fp32_c128_is_unsupported(dk):
+    a = chunk_args(dk=dk, dv=128, C=128)
     assert a["wsb"] == 0
     a["wsb"] = 1 << 30
     assert call_chunk(a) == UNSUP
@@ -148,7 +150,7 @@ def test_decode_validation_codes():
         return L.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], x["o"],
                                  x["N"], x["H"], x["dk"], x["dv"], x["ind"], x["outd"], None)
     cases = [(dict(N=-1), SHAPE), (dict(dk=100), UNSUP), (dict(ind=3), UNSUP),
-             (dict(state=None), NULL), (dict(v=a["v"] + 2), MISAL),
+             (dict(state=None), NULL), (dict(v=a["v"] + 1), MISAL), (dict(state=a["state"] + 8), MISAL),
              (dict(o=a["state"]), ALIAS), (dict(state=a["q"]), ALIAS), (dict(o=a["g"] + 16), ALIAS)]
     for change, code in cases:
         b = dict(a); b.update(change)

@@ -63,8 +63,8 @@ SHAPES = [(dk, dv) for dk in (64, 128) for dv in (64, 128)]
 @pytest.mark.parametrize("dk,dv", SHAPES)
 def test_shapes_ragged(dk, dv, C, dtype):
     """Several chunks plus a ragged tail, nonzero initial state, two batches."""
-    if dtype == torch.float32 and C == 128 and dk == 128:
-        pytest.skip("fp32 with C=128 and dk=128 is not offered (LDS budget)")
+    if dtype == torch.float32 and C == 128:
+        pytest.skip("fp32 inputs are offered with C <= 64 (LDS budget)")
     _say(f"shape dk={dk} dv={dv} C={C} {dtype}")
     T = 3 * C + 11
     d = inputs.custom_prefill(C + dk + dv, 2, T, 3, dk, dv, dtype=dtype, s0_std=0.05)
