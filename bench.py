@@ -32,6 +32,8 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 512 MiB device copy (to scale FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -52,6 +54,15 @@ def main():
     from linear_attention_sequence_chunk_amd import ChunkPlan, decode_step, inputs
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 512 << 20
+        x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     d = inputs.make_prefill(w)
     g = {k: (v.to(dev) if v is not None else None) for k, v in d.items()}

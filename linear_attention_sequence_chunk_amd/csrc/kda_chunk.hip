@@ -855,6 +855,8 @@ struct ChainCfg {
     static constexpr int B1 = U_QT, B2 = B1 + U_WK, B3 = B2 + U_KB, B4 = B3 + U_P, B5 = B4 + U_U;
     static constexpr int NU = B5 + U_G;
     static constexpr int NUPT = (NU + 255) / 256;
+    // chunks in flight: as many 16-byte-unit register sets as ~160 VGPRs allow
+    static constexpr int DEPTH = (160 / (4 * NUPT)) < 1 ? 1 : ((160 / (4 * NUPT)) > 3 ? 3 : 160 / (4 * NUPT));
     static constexpr size_t SZ_QT = size_t(C) * LDK * sizeof(T);
     static constexpr size_t SZ_KBT = align16(size_t(DK) * LDC * sizeof(T));
     static constexpr size_t SZ_P = align16(size_t(C) * LDC * sizeof(T));
@@ -922,8 +924,9 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     // statically sized register array per operand
     constexpr int PQ = (Cfg::U_QT + 255) / 256, PK = (Cfg::U_KB + 255) / 256, PP = (Cfg::U_P + 255) / 256,
                   PU = (Cfg::U_U + 255) / 256;
-    u32x4 preQ[PQ], preW[PQ], preK[PK], preP[PP], preU[PU], preG;
-#define KDA_CHAIN_PREFETCH(CH)                                                                     \
+    constexpr int D = Cfg::DEPTH;
+    u32x4 preQ[D][PQ], preW[D][PQ], preK[D][PK], preP[D][PP], preU[D][PU], preG[D];
+#define KDA_CHAIN_PREFETCH(SL, CH)                                                                     \
     {                                                                                              \
         const long ch_ = (CH);                                                                     \
         const u32x4* gq_ = reinterpret_cast<const u32x4*>(ws_qt + ch_ * (long)C * DK);             \
@@ -933,52 +936,52 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         const float* gu_ = ws_u + ch_ * (long)C * DV + j0;                                         \
         _Pragma("unroll") for (int i = 0; i < PQ; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_QT) { preQ[i] = gq_[u]; preW[i] = gw_[u]; }                             \
+            if (u < Cfg::U_QT) { preQ[SL][i] = gq_[u]; preW[SL][i] = gw_[u]; }                             \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_KB) preK[i] = gk_[u];                                                   \
+            if (u < Cfg::U_KB) preK[SL][i] = gk_[u];                                                   \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_P) preP[i] = gp_[u];                                                    \
+            if (u < Cfg::U_P) preP[SL][i] = gp_[u];                                                    \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PU; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
             if (u < Cfg::U_U)                                                                      \
-                preU[i] = *reinterpret_cast<const u32x4*>(gu_ + (long)(u / (DVS / 4)) * DV + 4 * (u % (DVS / 4))); \
+                preU[SL][i] = *reinterpret_cast<const u32x4*>(gu_ + (long)(u / (DVS / 4)) * DV + 4 * (u % (DVS / 4))); \
         }                                                                                          \
-        if (tid < Cfg::U_G) preG = reinterpret_cast<const u32x4*>(ws_gam + ch_ * (long)DK)[tid];  \
+        if (tid < Cfg::U_G) preG[SL] = reinterpret_cast<const u32x4*>(ws_gam + ch_ * (long)DK)[tid];  \
     }
-#define KDA_CHAIN_COMMIT()                                                                         \
+#define KDA_CHAIN_COMMIT(SL)                                                                         \
     {                                                                                              \
         _Pragma("unroll") for (int i = 0; i < PQ; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
             if (u < Cfg::U_QT) {                                                                   \
                 const int e = u * E16;                                                             \
-                *reinterpret_cast<u32x4*>(sQt + (e / DK) * LDK + e % DK) = preQ[i];                \
-                *reinterpret_cast<u32x4*>(sWk + (e / DK) * LDK + e % DK) = preW[i];                \
+                *reinterpret_cast<u32x4*>(sQt + (e / DK) * LDK + e % DK) = preQ[SL][i];                \
+                *reinterpret_cast<u32x4*>(sWk + (e / DK) * LDK + e % DK) = preW[SL][i];                \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
             if (u < Cfg::U_KB) {                                                                   \
                 const int e = u * E16;                                                             \
-                *reinterpret_cast<u32x4*>(sKbT + (e / C) * LDC + e % C) = preK[i];                 \
+                *reinterpret_cast<u32x4*>(sKbT + (e / C) * LDC + e % C) = preK[SL][i];                 \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
             if (u < Cfg::U_P) {                                                                    \
                 const int e = u * E16;                                                             \
-                *reinterpret_cast<u32x4*>(sP + (e / C) * LDC + e % C) = preP[i];                   \
+                *reinterpret_cast<u32x4*>(sP + (e / C) * LDC + e % C) = preP[SL][i];                   \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PU; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_U) reinterpret_cast<u32x4*>(sU)[u] = preU[i];                           \
+            if (u < Cfg::U_U) reinterpret_cast<u32x4*>(sU)[u] = preU[SL][i];                           \
         }                                                                                          \
-        if (tid < Cfg::U_G) reinterpret_cast<u32x4*>(sGam)[tid] = preG;                            \
+        if (tid < Cfg::U_G) reinterpret_cast<u32x4*>(sGam)[tid] = preG[SL];                            \
     }
 
     // zero the contraction padding once (columns C..CK never receive data)
@@ -991,7 +994,9 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         }
     }
 
-    if (NC > 0) KDA_CHAIN_PREFETCH(bh * NC);
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < NC) KDA_CHAIN_PREFETCH(d, bh * NC + d);
 
     floatx4 accS[Cfg::NSS];
     static_for<Cfg::NSS>([&](auto SI) {
@@ -1022,9 +1027,13 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     };
     write_state_operand();
 
-    for (int n = 0; n < NC; ++n) {
-        KDA_CHAIN_COMMIT();                                    // chunk n operands -> LDS
-        if (n + 1 < NC) KDA_CHAIN_PREFETCH(bh * NC + n + 1);  // in flight during this chunk
+    for (int n0 = 0; n0 < NC; n0 += D) {
+      static_for<D>([&](auto DI) {
+        constexpr int d = DI;
+        const int n = n0 + d;
+        if (n >= NC) return;
+        KDA_CHAIN_COMMIT(d);                                        // chunk n operands -> LDS
+        if (n + D < NC) KDA_CHAIN_PREFETCH(d, bh * NC + n + D);    // in flight for D chunks
         __syncthreads();
 
         // ---- W = U - Wk S (to LDS, transposed) and the state part of O
@@ -1088,6 +1097,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
             }
         }
         write_state_operand();
+      });
     }
 
     if (sT) {
