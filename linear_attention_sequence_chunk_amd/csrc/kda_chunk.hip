@@ -463,91 +463,84 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     }
 }
 
-// ================================================================ stage 1, bf16 / C = 64
-// The hot configuration.  Same workspace contents as chunk_intra_kernel, with:
-//  - 512 threads; every global load of the chunk is issued before any use;
-//  - two exponentials per (token, channel): E = e^{L} and F = e^{tot - L}
-//    (L the 16-token block-local prefix sum, tot the block sum), the other
-//    decay factors being products of per-(block, channel) factors <= 1;
-//  - all MFMA operands materialised once in LDS, every output stored from LDS
-//    staging in 16-byte rows;
-//  - beta folded into the triangular factor: U = (T Diag(beta)) V and
-//    Wk = (T Diag(beta)) (e^G * K).
-// Pairs of 16-token blocks (R, I) and their operands (Kr = k e^{L},
-// Kf = k e^{tot - L}, Kd = k e^{-L}; b_J = e^{tot_J}):
-//   (1,0) (3,2): Kr_R . Kf_I           (2,1): Kr_2 . Kf_1
-//   (2,0): Kr_2 . (b_1 Kf_0)            (3,1): (b_2 Kr_3) . Kf_1
-//   (3,0): (b_2 Kr_3) . (b_1 Kf_0)      (R,R): Kr_R . Kd_R
-template <int DK, int DV>
+// ================================================================ stage 1, bf16 / C = 64 / dk = 128
+// The hot configuration.  Same workspace contents as chunk_intra_kernel.
+//  - Gate factors as products: alpha = e^{g} once per (token, channel); inside
+//    each 16-token block the inclusive prefix product E_t = e^{L_t} and the
+//    exclusive suffix product F_t = e^{tot - L_t} are formed in registers with
+//    DPP row shifts (the 16 tokens of a block sit in the 16 lanes of one DPP
+//    row).  All other decay factors are products of block totals; no factor
+//    ever exceeds 1 except e^{-L}, which is only formed for blocks whose total
+//    stays above SAFE_MIN.  g = -inf gives alpha = 0 exactly.
+//  - Two passes over halves of the key channels keep LDS at ~75 KB so that two
+//    workgroups share a CU; A and P accumulate across the passes.
+//  - MFMA operand fragments are shared across the tiles a wave computes.
+// Block pairs (R, I) and operands (Kr = k E, Kf = k F, Kd = k / E; b_J = tot_J):
+//   (1,0) (3,2): Kr_R . Kf_I      (2,1): Kr_2 . Kf_1      (2,0): Kr_2 . (b_1 Kf_0)
+//   (3,1): (b_2 Kr_3) . Kf_1      (3,0): (b_2 Kr_3) . (b_1 Kf_0)      (R,R): Kr_R . Kd_R
+constexpr float SAFE_MIN = 1.6e-28f;   // e^{-64}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_one(float src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f),
+                                                                 __builtin_bit_cast(int, src), CTRL, 0xF, 0xF, false));
+}
+// inclusive prefix / suffix products within each row of 16 lanes
+__device__ __forceinline__ float row_prefix_prod(float x) {
+    x *= dpp_or_one<0x111>(x);   // row_shr:1
+    x *= dpp_or_one<0x112>(x);   // row_shr:2
+    x *= dpp_or_one<0x114>(x);   // row_shr:4
+    x *= dpp_or_one<0x118>(x);   // row_shr:8
+    return x;
+}
+__device__ __forceinline__ float row_suffix_prod(float x) {
+    x *= dpp_or_one<0x101>(x);   // row_shl:1
+    x *= dpp_or_one<0x102>(x);   // row_shl:2
+    x *= dpp_or_one<0x104>(x);   // row_shl:4
+    x *= dpp_or_one<0x108>(x);   // row_shl:8
+    return x;
+}
+
+template <int DV>
 struct Intra64Cfg {
-    static constexpr int C = 64, NB = 4, NT = 512, NW = 8;
-    static constexpr int LDK = DK + 8;           // bf16 rows over channels
-    static constexpr int LDT = C + 8;            // bf16 rows over positions
-    static constexpr int LDA = C + 8;            // fp32 rows of the C x C matrices
-    static constexpr int NGRP = (C / 16) * (DK / 32), NIT = NGRP / NW;     // q, k, g units
-    static constexpr int NGRPV = (C / 16) * (DV / 32), NITV = NGRPV / NW;  // v units
-    static constexpr size_t SZ_OPF = size_t(C) * LDK * 2, SZ_OPB = size_t(16) * LDK * 2;
-    static constexpr size_t OFF_G = 0;
-    static constexpr size_t OFF_KR = OFF_G + size_t(C) * DK * 4;
-    static constexpr size_t OFF_QR = OFF_KR + SZ_OPF;
-    static constexpr size_t OFF_KF = OFF_QR + SZ_OPF;
-    static constexpr size_t OFF_KD = OFF_KF + SZ_OPF;
-    static constexpr size_t OFF_KR3 = OFF_KD + SZ_OPF;
-    static constexpr size_t OFF_QR3 = OFF_KR3 + SZ_OPB;
-    static constexpr size_t OFF_KF0 = OFF_QR3 + SZ_OPB;
-    static constexpr size_t OFF_KT = OFF_KF0 + SZ_OPB;                 // (e^G k)^T [DK][LDT], kept
-    static constexpr size_t OFF_KB = OFF_KT + size_t(DK) * LDT * 2;     // Kb^T staging [DK][C]
-    static constexpr size_t OFF_TOT = OFF_KB + size_t(DK) * C * 2;
-    static constexpr size_t OFF_EBASE = OFF_TOT + size_t(NB) * DK * 4;
-    static constexpr size_t OFF_EREST = OFF_EBASE + size_t(NB) * DK * 4;
-    static constexpr size_t OFF_ENEG = OFF_EREST + size_t(NB) * DK * 4;
-    static constexpr size_t OFF_B1 = OFF_ENEG + size_t(NB) * DK * 4;
-    static constexpr size_t OFF_B2 = OFF_B1 + size_t(DK) * 4;
-    static constexpr size_t OFF_BETA = OFF_B2 + size_t(DK) * 4;
-    static constexpr size_t OFF_FLAG = OFF_BETA + size_t(C) * 4;
-    static constexpr size_t TOTAL = OFF_FLAG + 16;
-    // after the score matrices: aliases [0, OFF_KT)
+    static constexpr int C = 64, NB = 4, DK = 128, NT = 512, NW = 8, HALF = 64;
+    static constexpr int LDH = HALF + 8;             // bf16 operand rows (one channel half)
+    static constexpr int LDT = C + 8;                // bf16 rows over positions
+    static constexpr int LDA = C + 8;                // fp32 rows of the C x C matrices
+    static constexpr int NITV = C * DV / 8 / NT;     // v units per thread
+    static constexpr size_t BLK = size_t(16) * LDH * 2;                 // one 16-row operand block
+    // operand blocks: Kr 0-3, Qr 4-7, Kf 8-10 (blocks 0..2), Kd 11-14, Kr3' 15, Qr3' 16, Kf0' 17
+    static constexpr size_t SZ_S = 18 * BLK;
     static constexpr size_t OFF_A = 0;
-    static constexpr size_t OFF_PB = OFF_A + size_t(C) * LDA * 4;
-    static constexpr size_t OFF_X = OFF_PB + size_t(C) * C * 2;
-    static constexpr size_t OFF_TB = OFF_X + size_t(C / 2) * (C / 2 + 4) * 4;
-    static constexpr size_t OFF_VT = OFF_TB + size_t(C) * LDT * 2;
-    static constexpr size_t OFF_UO = OFF_VT + size_t(DV) * LDT * 2;
-    static constexpr size_t OFF_WO = OFF_UO + size_t(C) * DV * 4;
-    static constexpr size_t END_W = OFF_WO + size_t(C) * DK * 2;
-    static_assert(END_W <= OFF_KT, "phase-W buffers overlap the kept K~^T");
-    static_assert(TOTAL <= LDS_LIMIT, "LDS budget");
-    static_assert(NIT >= 1 && NITV >= 1 && NGRP % NW == 0 && NGRPV % NW == 0, "unit mapping");
+    static constexpr size_t OFF_TB = OFF_A + size_t(C) * LDA * 4;
+    static constexpr size_t OFF_PB = OFF_TB + size_t(C) * LDT * 2;      // P staging, then the T temp
+    static constexpr size_t OFF_VT = OFF_PB + size_t(C) * C * 2;
+    static constexpr size_t SZ_W = OFF_VT + size_t(DV) * LDT * 2;
+    static constexpr size_t OFF_KT = SZ_S > SZ_W ? SZ_S : SZ_W;         // (e^G k)^T [DK][LDT], kept
+    static constexpr size_t OFF_TOT = OFF_KT + size_t(DK) * LDT * 2;
+    static constexpr size_t OFF_BETA = OFF_TOT + size_t(NB) * DK * 4;
+    static constexpr size_t TOTAL = OFF_BETA + size_t(C) * 4;
+    static_assert(size_t(C / 2) * (C / 2 + 4) * 4 <= size_t(C) * C * 2, "T temp fits the P staging");
+    static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
+    static_assert(NITV >= 1 && (C * DV / 8) % NT == 0, "v unit mapping");
 };
 
-template <int DK, int DV>
-__global__ __launch_bounds__(512) void chunk_intra64_kernel(
+template <int DV>
+__global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     bf16* __restrict__ ws_qt, bf16* __restrict__ ws_wk, bf16* __restrict__ ws_kb, bf16* __restrict__ ws_p,
     float* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC) {
-    typedef Intra64Cfg<DK, DV> Cfg;
-    constexpr int C = 64, NB = 4, NT = 512, NW = 8, LDK = Cfg::LDK, LDT = Cfg::LDT, LDA = Cfg::LDA;
+    typedef Intra64Cfg<DV> Cfg;
+    constexpr int C = 64, NB = 4, DK = 128, NT = 512, NW = 8, HALF = 64;
+    constexpr int LDH = Cfg::LDH, LDT = Cfg::LDT, LDA = Cfg::LDA;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
-    float* sG = reinterpret_cast<float*>(smem + Cfg::OFF_G);
-    bf16* sKr = reinterpret_cast<bf16*>(smem + Cfg::OFF_KR);
-    bf16* sQr = reinterpret_cast<bf16*>(smem + Cfg::OFF_QR);
-    bf16* sKf = reinterpret_cast<bf16*>(smem + Cfg::OFF_KF);
-    bf16* sKd = reinterpret_cast<bf16*>(smem + Cfg::OFF_KD);
-    bf16* sKr3 = reinterpret_cast<bf16*>(smem + Cfg::OFF_KR3);
-    bf16* sQr3 = reinterpret_cast<bf16*>(smem + Cfg::OFF_QR3);
-    bf16* sKf0 = reinterpret_cast<bf16*>(smem + Cfg::OFF_KF0);
+    bf16* sOp = reinterpret_cast<bf16*>(smem);
     bf16* sKtT = reinterpret_cast<bf16*>(smem + Cfg::OFF_KT);
-    bf16* sKbT = reinterpret_cast<bf16*>(smem + Cfg::OFF_KB);
     float* sTot = reinterpret_cast<float*>(smem + Cfg::OFF_TOT);
-    float* sEBase = reinterpret_cast<float*>(smem + Cfg::OFF_EBASE);
-    float* sERest = reinterpret_cast<float*>(smem + Cfg::OFF_EREST);
-    float* sENeg = reinterpret_cast<float*>(smem + Cfg::OFF_ENEG);
-    float* sB1 = reinterpret_cast<float*>(smem + Cfg::OFF_B1);
-    float* sB2 = reinterpret_cast<float*>(smem + Cfg::OFF_B2);
     float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_BETA);
-    int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);
+    auto blk = [&](int b) { return sOp + b * 16 * LDH; };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const long ch = blockIdx.x;
@@ -557,203 +550,225 @@ __global__ __launch_bounds__(512) void chunk_intra64_kernel(
     const int t0 = n * C;
     auto grow = [&](int t) -> long { return ((long)b * T_len + (t0 + t)) * H + h; };
     auto valid = [&](int t) -> bool { return t0 + t < T_len; };
-    // unit (it): 16 rows x 4 eight-channel groups per wave; lane -> row, group
-    auto unit_t = [&](int it, int ncg) { return ((wave + NW * it) / ncg) * 16 + (lane & 15); };
-    auto unit_c = [&](int it, int ncg) { return (((wave + NW * it) % ncg) * 4 + (lane >> 4)) * 8; };
-    constexpr int NCG = DK / 32, NCGV = DV / 32;
+
+    // unit of pass p: wave -> (16-row block R, 32-channel group), lane -> (row, 8 channels)
+    const int R = wave >> 1, rr = lane & 15, t = R * 16 + rr;
+    auto chan = [&](int p) { return 64 * p + 32 * (wave & 1) + 8 * (lane >> 4); };
 
     // ---------------------------------------------------------------- loads
-    bf16x8 qv[Cfg::NIT], kv[Cfg::NIT], vv[Cfg::NITV];
-    floatx4 ga[Cfg::NIT], gb[Cfg::NIT];
+    bf16x8 qv[2], kv[2], vv[Cfg::NITV];
+    floatx4 ga[2], gb[2];
 #pragma unroll
-    for (int it = 0; it < Cfg::NIT; ++it) {
-        const int t = unit_t(it, NCG), c = unit_c(it, NCG);
+    for (int p = 0; p < 2; ++p) {
         if (valid(t)) {
-            const long base = grow(t) * DK + c;
-            qv[it] = *reinterpret_cast<const bf16x8*>(q + base);
-            kv[it] = *reinterpret_cast<const bf16x8*>(k + base);
-            ga[it] = *reinterpret_cast<const floatx4*>(g + base);
-            gb[it] = *reinterpret_cast<const floatx4*>(g + base + 4);
+            const long base = grow(t) * DK + chan(p);
+            qv[p] = *reinterpret_cast<const bf16x8*>(q + base);
+            kv[p] = *reinterpret_cast<const bf16x8*>(k + base);
+            ga[p] = *reinterpret_cast<const floatx4*>(g + base);
+            gb[p] = *reinterpret_cast<const floatx4*>(g + base + 4);
         } else {
 #pragma unroll
-            for (int m = 0; m < 8; ++m) { qv[it][m] = (bf16)0.f; kv[it][m] = (bf16)0.f; }
-            ga[it] = zero4(); gb[it] = zero4();
+            for (int m = 0; m < 8; ++m) { qv[p][m] = (bf16)0.f; kv[p][m] = (bf16)0.f; }
+            ga[p] = zero4(); gb[p] = zero4();
         }
     }
 #pragma unroll
     for (int it = 0; it < Cfg::NITV; ++it) {
-        const int t = unit_t(it, NCGV), j = unit_c(it, NCGV);
-        if (valid(t)) vv[it] = *reinterpret_cast<const bf16x8*>(v + grow(t) * DV + j);
+        const int u = tid + NT * it, tv = u / (DV / 8), j = 8 * (u % (DV / 8));
+        if (valid(tv)) vv[it] = *reinterpret_cast<const bf16x8*>(v + grow(tv) * DV + j);
         else {
 #pragma unroll
             for (int m = 0; m < 8; ++m) vv[it][m] = (bf16)0.f;
         }
     }
     if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
-    if (tid < NB) sFlag[tid] = 0;
-#pragma unroll
-    for (int it = 0; it < Cfg::NIT; ++it) {
-        const int t = unit_t(it, NCG), c = unit_c(it, NCG);
-        *reinterpret_cast<floatx4*>(sG + t * DK + c) = ga[it];
-        *reinterpret_cast<floatx4*>(sG + t * DK + c + 4) = gb[it];
-    }
-    __syncthreads();
 
-    // ---------------------------------------------------------------- a1: block-local scans
-    for (int u = tid; u < NB * DK; u += NT) {
-        const int R = u / DK, c = u % DK;
-        float x[16];
+    // ---------------------------------------------------------------- a1: block products
+    // E_t = prod_{j<=t} alpha_j and F_t = prod_{j>t} alpha_j inside the block (per channel);
+    // the block totals of both channel halves go to LDS now, the second half's E and F
+    // are formed again when that half is processed (registers are tight).
+    float E[8], F[8];
+    auto block_products = [&](int p) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) x[rr] = sG[(R * 16 + rr) * DK + c];
-        float l = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) { l += clamp_g(x[rr]); x[rr] = l; }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sG[(R * 16 + rr) * DK + c] = x[rr];
-        sTot[R * DK + c] = l;
-        if (l < -SAFE_SPAN) sFlag[R] = 1;
-    }
-    __syncthreads();
-    // per-(block, channel) factors, all <= 1 except e^{-tot} (used only when safe)
-    for (int u = tid; u < NB * DK; u += NT) {
-        const int R = u / DK, c = u % DK;
-        float tb[NB];
-#pragma unroll
-        for (int J = 0; J < NB; ++J) tb[J] = sTot[J * DK + c];
-        float base = 0.f, rest = 0.f;
-#pragma unroll
-        for (int J = 0; J < NB; ++J) { if (J < R) base += tb[J]; if (J > R) rest += tb[J]; }
-        sEBase[u] = __expf(base);
-        sERest[u] = __expf(rest);
-        sENeg[u] = tb[R] >= -SAFE_SPAN ? __expf(-tb[R]) : 0.f;
-        if (R == 0) {
-            sB1[c] = __expf(tb[1]);
-            sB2[c] = __expf(tb[2]);
-            ws_gam[ch * DK + c] = __expf(tb[0] + tb[1] + tb[2] + tb[3]);
+        for (int m = 0; m < 8; ++m) {
+            const float a = __expf(m < 4 ? ga[p][m] : gb[p][m - 4]);     // alpha, exactly 0 for -inf
+            E[m] = row_prefix_prod(a);
+            F[m] = dpp_or_one<0x101>(row_suffix_prod(a));                // exclusive suffix
         }
+    };
+    block_products(1);
+    if (rr == 15) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sTot[R * DK + chan(1) + m] = E[m];
+    }
+    block_products(0);
+    if (rr == 15) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sTot[R * DK + chan(0) + m] = E[m];
     }
     __syncthreads();
 
-    // ---------------------------------------------------------------- a2: decayed operands
+    // ---------------------------------------------------------------- a2 + a3 per channel half
     bf16* gQt = ws_qt + ch * (long)C * DK;
+    bf16* gKb = ws_kb + ch * (long)DK * C;
+    floatx4 accA[2], accP[2];
+    accA[0] = accA[1] = accP[0] = accP[1] = zero4();
+    // pair assignment: w0 (0,0); w1 (1,0)(1,1); w2 (2,0)(2,1); w3 (2,2); w4 (3,0)(3,1); w5 (3,2)(3,3)
 #pragma unroll
-    for (int it = 0; it < Cfg::NIT; ++it) {
-        const int t = unit_t(it, NCG), c = unit_c(it, NCG);
-        const int R = t >> 4, rr = t & 15;
-        float L[8], tt[8], eb[8], er[8], en[8];
-        Vec8<float>::load(sG + t * DK + c, L);
-        Vec8<float>::load(sTot + R * DK + c, tt);
-        Vec8<float>::load(sEBase + R * DK + c, eb);
-        Vec8<float>::load(sERest + R * DK + c, er);
-        Vec8<float>::load(sENeg + R * DK + c, en);
+    for (int p = 0; p < 2; ++p) {
+        const int c = chan(p), cl = c - 64 * p;
+        if (p == 1) block_products(1);
+        float tt[NB][8];
+#pragma unroll
+        for (int J = 0; J < NB; ++J) Vec8<float>::load(sTot + J * DK + c, tt[J]);
         float kr[8], qr[8], kf[8], o1[8], o2[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const float E = __expf(L[m]), F = __expf(tt[m] - L[m]);
-            const float kk = (float)kv[it][m], qq = (float)qv[it][m];
-            kr[m] = kk * E; qr[m] = qq * E; kf[m] = kk * F;
+            const float kk = (float)kv[p][m], qq = (float)qv[p][m];
+            kr[m] = kk * E[m]; qr[m] = qq * E[m]; kf[m] = kk * F[m];
         }
-        Vec8<bf16>::store(sKr + t * LDK + c, kr);
-        Vec8<bf16>::store(sQr + t * LDK + c, qr);
-        Vec8<bf16>::store(sKf + t * LDK + c, kf);
+        Vec8<bf16>::store(blk(R) + rr * LDH + cl, kr);
+        Vec8<bf16>::store(blk(4 + R) + rr * LDH + cl, qr);
+        if (R < 3) Vec8<bf16>::store(blk(8 + R) + rr * LDH + cl, kf);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o1[m] = kf[m] * en[m];
-        Vec8<bf16>::store(sKd + t * LDK + c, o1);
+        for (int m = 0; m < 8; ++m) o1[m] = tt[R][m] >= SAFE_MIN ? kf[m] / tt[R][m] : 0.f;   // k e^{-L}
+        Vec8<bf16>::store(blk(11 + R) + rr * LDH + cl, o1);
         if (R == 3) {
-            float b2[8];
-            Vec8<float>::load(sB2 + c, b2);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) { o1[m] = kr[m] * b2[m]; o2[m] = qr[m] * b2[m]; }
-            Vec8<bf16>::store(sKr3 + rr * LDK + c, o1);
-            Vec8<bf16>::store(sQr3 + rr * LDK + c, o2);
+            for (int m = 0; m < 8; ++m) { o1[m] = kr[m] * tt[2][m]; o2[m] = qr[m] * tt[2][m]; }
+            Vec8<bf16>::store(blk(15) + rr * LDH + cl, o1);
+            Vec8<bf16>::store(blk(16) + rr * LDH + cl, o2);
         } else if (R == 0) {
-            float b1[8];
-            Vec8<float>::load(sB1 + c, b1);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) o1[m] = kf[m] * b1[m];
-            Vec8<bf16>::store(sKf0 + rr * LDK + c, o1);
+            for (int m = 0; m < 8; ++m) o1[m] = kf[m] * tt[1][m];
+            Vec8<bf16>::store(blk(17) + rr * LDH + cl, o1);
+        }
+        // e^G = E * prod_{J<R} tot_J ;  e^{G_last - G} = F * prod_{J>R} tot_J
+        float eb[8], er[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            eb[m] = 1.f; er[m] = 1.f;
+#pragma unroll
+            for (int J = 0; J < NB; ++J) { if (J < R) eb[m] *= tt[J][m]; if (J > R) er[m] *= tt[J][m]; }
         }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o1[m] = qr[m] * eb[m];                  // e^G q
+        for (int m = 0; m < 8; ++m) o1[m] = qr[m] * eb[m];
         Vec8<bf16>::store(gQt + t * DK + c, o1);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]);                // e^G k
-            sKbT[(c + m) * C + t] = (bf16)(kf[m] * er[m]);                  // e^{G_last - G} k
+            sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]);
+            gKb[(c + m) * C + t] = (bf16)(kf[m] * er[m]);
         }
-    }
-    __syncthreads();
+        if (p == 0 && tid < DK) {
+            float gam = 1.f;
+#pragma unroll
+            for (int J = 0; J < NB; ++J) gam *= sTot[J * DK + tid];
+            ws_gam[ch * DK + tid] = gam;
+        }
+        __syncthreads();
 
-    // ---------------------------------------------------------------- a3: A and P
-    {
-        bf16* gKb = ws_kb + ch * (long)DK * C;
-        for (int u = tid; u < DK * C / 8; u += NT)
-            reinterpret_cast<uint4*>(gKb)[u] = reinterpret_cast<const uint4*>(sKbT)[u];
-    }
-    floatx4 accA[2], accP[2];
-    accA[0] = accA[1] = accP[0] = accP[1] = zero4();
-    static_for<10>([&](auto PI) {
-        constexpr int p = PI;
-        constexpr int R = pair_R(p), I = pair_I(p);
-        if (wave == p % NW) {
-            constexpr int s = p / NW;
-            const bf16* rk = (R == 3 && I < 2) ? sKr3 : sKr + R * 16 * LDK;
-            const bf16* rq = (R == 3 && I < 2) ? sQr3 : sQr + R * 16 * LDK;
-            const bf16* ck = (R == I) ? sKd + I * 16 * LDK
-                           : (I == 0 && R >= 2) ? sKf0 : sKf + I * 16 * LDK;
-            if (R != I || !sFlag[R]) {
-                mma_tile2<bf16>(accA[s], accP[s], rk, rq, LDK, ck, LDK, DK, lane);
-            } else {
-                // term-by-term: e^{L_r - L_i}, both sums block-local, r >= i
-                const int i = R * 16 + (lane & 15);
+        // A and P over this channel half (K = 64: two MFMA steps)
+        if (wave < 6) {
+            const int Rw = wave == 0 ? 0 : (wave <= 2 ? wave : (wave == 3 ? 2 : 3));
+            const int npair = (wave == 0 || wave == 3) ? 1 : 2;
+            // operands
+            const bf16 *rk0, *rq0, *ck0, *ck1 = nullptr, *rk1 = nullptr, *rq1 = nullptr;
+            if (wave == 0)      { rk0 = blk(0);  rq0 = blk(4);  ck0 = blk(11); }
+            else if (wave == 1) { rk0 = blk(1);  rq0 = blk(5);  ck0 = blk(8);  ck1 = blk(12); }
+            else if (wave == 2) { rk0 = blk(2);  rq0 = blk(6);  ck0 = blk(17); ck1 = blk(9); }
+            else if (wave == 3) { rk0 = blk(2);  rq0 = blk(6);  ck0 = blk(13); }
+            else if (wave == 4) { rk0 = blk(15); rq0 = blk(16); ck0 = blk(17); ck1 = blk(9); }
+            else                { rk0 = blk(3);  rq0 = blk(7);  ck0 = blk(10); ck1 = blk(14); }
+            (void)Rw; (void)rk1; (void)rq1;
+            // a diagonal tile whose block total underflows is done term by term below
+            const int dslot = (wave == 0 || wave == 3) ? 0 : ((wave == 1 || wave == 5) ? 1 : -1);
+            const int dR = wave == 0 ? 0 : wave == 1 ? 1 : wave == 3 ? 2 : 3;
+            bool uns = false;
+            if (dslot >= 0) {
+                uns = sTot[dR * DK + lane] < SAFE_MIN || sTot[dR * DK + 64 + lane] < SAFE_MIN;
+                uns = __any(uns);
+            }
+            const int r = lane & 15, kg = lane >> 4;
+#pragma unroll
+            for (int k0 = 0; k0 < HALF; k0 += 32) {
+                const int o = r * LDH + k0 + 8 * kg;
+                const bf16x8 fk = *reinterpret_cast<const bf16x8*>(rk0 + o);
+                const bf16x8 fq = *reinterpret_cast<const bf16x8*>(rq0 + o);
+                const bf16x8 fc0 = *reinterpret_cast<const bf16x8*>(ck0 + o);
+                if (!(uns && dslot == 0)) {
+                    accA[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk, fc0, accA[0], 0, 0, 0);
+                    accP[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq, fc0, accP[0], 0, 0, 0);
+                }
+                if (npair == 2) {
+                    const bf16x8 fc1 = *reinterpret_cast<const bf16x8*>(ck1 + o);
+                    if (!(uns && dslot == 1)) {
+                        accA[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk, fc1, accA[1], 0, 0, 0);
+                        accP[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq, fc1, accP[1], 0, 0, 0);
+                    }
+                }
+            }
+            if (uns && p == 1) {
+                // term by term over all channels: prod_{j=i+1..r} alpha_j, from global memory
+                const int i = dR * 16 + (lane & 15);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = R * 16 + 4 * (lane >> 4) + e;
+                    const int rw = dR * 16 + 4 * (lane >> 4) + e;
                     float sa = 0.f, sp = 0.f;
-                    if (i <= r && valid(r)) {
-                        for (int c = 0; c < DK; ++c) {
-                            const float w = __expf(sG[r * DK + c] - sG[i * DK + c]);
-                            const float ki = (float)k[grow(i) * DK + c];
-                            sa += (float)k[grow(r) * DK + c] * ki * w;
-                            sp += (float)q[grow(r) * DK + c] * ki * w;
+                    if (i <= rw && valid(rw)) {
+                        for (int cc = 0; cc < DK; ++cc) {
+                            float w = 1.f;
+                            for (int j = i + 1; j <= rw; ++j) w *= __expf(g[grow(j) * DK + cc]);
+                            const float ki = (float)k[grow(i) * DK + cc];
+                            sa += (float)k[grow(rw) * DK + cc] * ki * w;
+                            sp += (float)q[grow(rw) * DK + cc] * ki * w;
                         }
                     }
-                    accA[s][e] = sa;
-                    accP[s][e] = sp;
+                    if (dslot == 0) { accA[0][e] = sa; accP[0][e] = sp; }
+                    else            { accA[1][e] = sa; accP[1][e] = sp; }
                 }
             }
         }
-    });
-    __syncthreads();
+        __syncthreads();
+    }
 
     // ---------------------------------------------------------------- M = Diag(beta) A, P
     float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
     bf16* sPb = reinterpret_cast<bf16*>(smem + Cfg::OFF_PB);
-    for (int u = tid; u < C * C; u += NT) {
-        const int r = u / C, i = u % C;
-        if (r / 16 < i / 16) { sA[r * LDA + i] = 0.f; sPb[u] = (bf16)0.f; }
+    for (int u = tid; u < 6 * 256; u += NT) {          // the six strictly-upper 16x16 blocks
+        const int bi = u >> 8, e = u & 255;
+        const int br = bi < 3 ? 0 : (bi < 5 ? 1 : 2);
+        const int bc = bi < 3 ? bi + 1 : (bi < 5 ? bi - 1 : 3);
+        const int r = br * 16 + (e >> 4), i = bc * 16 + (e & 15);
+        sA[r * LDA + i] = 0.f;
+        sPb[r * C + i] = (bf16)0.f;
     }
-    static_for<10>([&](auto PI) {
-        constexpr int p = PI;
-        constexpr int R = pair_R(p), I = pair_I(p);
-        if (wave == p % NW) {
-            constexpr int s = p / NW;
-            const int i = I * 16 + (lane & 15);
+    if (wave < 6) {
+        const int np = (wave == 0 || wave == 3) ? 1 : 2;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s >= np) break;
+            int PR, PI;
+            if (wave == 0) { PR = 0; PI = 0; }
+            else if (wave == 1) { PR = 1; PI = s; }
+            else if (wave == 2) { PR = 2; PI = s; }
+            else if (wave == 3) { PR = 2; PI = 2; }
+            else if (wave == 4) { PR = 3; PI = s; }
+            else { PR = 3; PI = 2 + s; }
+            const int i = PI * 16 + (lane & 15);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = R * 16 + 4 * (lane >> 4) + e;
+                const int r = PR * 16 + 4 * (lane >> 4) + e;
                 float av = accA[s][e], pv = accP[s][e];
-                if (R == I) { if (i >= r) av = 0.f; if (i > r) pv = 0.f; }
+                if (PR == PI) { if (i >= r) av = 0.f; if (i > r) pv = 0.f; }
                 sA[r * LDA + i] = sBeta[r] * av;
                 sPb[r * C + i] = (bf16)pv;
             }
         }
-    });
+    }
     __syncthreads();
     {
-        bf16* gP = ws_p + ch * (long)C * C;
-        for (int u = tid; u < C * C / 8; u += NT)
-            reinterpret_cast<uint4*>(gP)[u] = reinterpret_cast<const uint4*>(sPb)[u];
+        uint4* gP = reinterpret_cast<uint4*>(ws_p + ch * (long)C * C);
+        if (tid < C * C / 8) gP[tid] = reinterpret_cast<const uint4*>(sPb)[tid];
     }
 
     // ---------------------------------------------------------------- a4: T = (I + M)^-1
@@ -772,11 +787,12 @@ __global__ __launch_bounds__(512) void chunk_intra64_kernel(
         for (int r = 0; r < 16; ++r) Mb[r * LDA + j] = x[r];
     }
     __syncthreads();
-    float* sX = reinterpret_cast<float*>(smem + Cfg::OFF_X);
+    float* sX = reinterpret_cast<float*>(smem + Cfg::OFF_PB);
     static_for<2>([&](auto LH) {
         constexpr int HH = 16 << LH, NM = C / (2 * HH), HT = HH / 16, NTL = NM * HT * HT, LDX = HH + 4;
-        for (int tt = wave; tt < NTL; tt += NW) {
-            const int m = tt / (HT * HT), a = (tt / HT) % HT, bc = tt % HT, base = m * 2 * HH;
+        if (wave < NTL) {
+            const int tt2 = wave;
+            const int m = tt2 / (HT * HT), a = (tt2 / HT) % HT, bc = tt2 % HT, base = m * 2 * HH;
             floatx4 acc = mma_f32_rowB(zero4(), sA + (base + HH + a * 16) * LDA + base, LDA,
                                        sA + base * LDA + base + bc * 16, LDA, HH, lane);
 #pragma unroll
@@ -784,8 +800,9 @@ __global__ __launch_bounds__(512) void chunk_intra64_kernel(
                 sX[m * HH * LDX + (a * 16 + 4 * (lane >> 4) + e) * LDX + bc * 16 + (lane & 15)] = acc[e];
         }
         __syncthreads();
-        for (int tt = wave; tt < NTL; tt += NW) {
-            const int m = tt / (HT * HT), a = (tt / HT) % HT, bc = tt % HT, base = m * 2 * HH;
+        if (wave < NTL) {
+            const int tt2 = wave;
+            const int m = tt2 / (HT * HT), a = (tt2 / HT) % HT, bc = tt2 % HT, base = m * 2 * HH;
             floatx4 acc = mma_f32_rowB(zero4(), sA + (base + HH + a * 16) * LDA + base + HH, LDA,
                                        sX + m * HH * LDX + bc * 16, LDX, HH, lane);
 #pragma unroll
@@ -795,45 +812,55 @@ __global__ __launch_bounds__(512) void chunk_intra64_kernel(
         __syncthreads();
     });
 
-    // ---------------------------------------------------------------- U, Wk
+    // ---------------------------------------------------------------- U = (T Diag(beta)) V, Wk = (T Diag(beta)) e^G K
     bf16* sTb = reinterpret_cast<bf16*>(smem + Cfg::OFF_TB);
     bf16* sVt = reinterpret_cast<bf16*>(smem + Cfg::OFF_VT);
-    for (int u = tid; u < C * C; u += NT) {
-        const int r = u / C, i = u % C;
-        sTb[r * LDT + i] = (bf16)(sA[r * LDA + i] * sBeta[i]);             // T Diag(beta)
+    for (int u = tid; u < C * C / 2; u += NT) {
+        const int r = u / (C / 2), i = 2 * (u % (C / 2));
+        bf16x2 pr;
+        pr[0] = (bf16)(sA[r * LDA + i] * sBeta[i]);
+        pr[1] = (bf16)(sA[r * LDA + i + 1] * sBeta[i + 1]);
+        *reinterpret_cast<bf16x2*>(sTb + r * LDT + i) = pr;
     }
 #pragma unroll
     for (int it = 0; it < Cfg::NITV; ++it) {
-        const int t = unit_t(it, NCGV), j = unit_c(it, NCGV);
+        const int u = tid + NT * it, tv = u / (DV / 8), j = 8 * (u % (DV / 8));
 #pragma unroll
-        for (int m = 0; m < 8; ++m) sVt[(j + m) * LDT + t] = vv[it][m];
-    }
-    __syncthreads();
-    float* sUo = reinterpret_cast<float*>(smem + Cfg::OFF_UO);
-    bf16* sWo = reinterpret_cast<bf16*>(smem + Cfg::OFF_WO);
-    constexpr int NTU = 4 * (DV / 16), NTWK = 4 * (DK / 16);
-    for (int tt = wave; tt < NTU + NTWK; tt += NW) {
-        const bool isU = tt < NTU;
-        const int t2 = isU ? tt : tt - NTU;
-        const int ncol = isU ? DV / 16 : DK / 16;
-        const int R = t2 / ncol, J = t2 % ncol;
-        const int K = R < 2 ? 32 : 64;
-        const bf16* bsrc = isU ? sVt + J * 16 * LDT : sKtT + J * 16 * LDT;
-        floatx4 acc = mma_tile<bf16>(zero4(), sTb + R * 16 * LDT, LDT, bsrc, LDT, K, lane);
-        const int col = J * 16 + (lane & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = R * 16 + 4 * (lane >> 4) + e;
-            if (isU) sUo[row * DV + col] = acc[e];
-            else sWo[row * DK + col] = (bf16)acc[e];
-        }
+        for (int m = 0; m < 8; ++m) sVt[(j + m) * LDT + tv] = vv[it][m];
     }
     __syncthreads();
     {
-        uint4* gU = reinterpret_cast<uint4*>(ws_u + ch * (long)C * DV);
-        for (int u = tid; u < C * DV / 4; u += NT) gU[u] = reinterpret_cast<const uint4*>(sUo)[u];
-        uint4* gW = reinterpret_cast<uint4*>(ws_wk + ch * (long)C * DK);
-        for (int u = tid; u < C * DK / 8; u += NT) gW[u] = reinterpret_cast<const uint4*>(sWo)[u];
+        constexpr int NUT = DV / 16, NCT = NUT + DK / 16;        // column tiles: U then Wk
+        float* gU = ws_u + ch * (long)C * DV;
+        bf16* gW = ws_wk + ch * (long)C * DK;
+        const int r = lane & 15, kg = lane >> 4;
+        for (int ct = wave; ct < NCT; ct += NW) {
+            const bool isU = ct < NUT;
+            const bf16* bsrc = isU ? sVt + ct * 16 * LDT : sKtT + (ct - NUT) * 16 * LDT;
+            floatx4 acc[4];
+#pragma unroll
+            for (int R2 = 0; R2 < 4; ++R2) acc[R2] = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += 32) {
+                const bf16x8 fb = *reinterpret_cast<const bf16x8*>(bsrc + r * LDT + k0 + 8 * kg);
+#pragma unroll
+                for (int R2 = 0; R2 < 4; ++R2) {
+                    if (k0 >= 16 * (R2 + 1)) continue;              // T is lower triangular
+                    const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sTb + (R2 * 16 + r) * LDT + k0 + 8 * kg);
+                    acc[R2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[R2], 0, 0, 0);
+                }
+            }
+            const int col = (isU ? ct : ct - NUT) * 16 + (lane & 15);
+#pragma unroll
+            for (int R2 = 0; R2 < 4; ++R2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = R2 * 16 + 4 * (lane >> 4) + e;
+                    if (isU) gU[row * DV + col] = acc[R2][e];
+                    else gW[row * DK + col] = (bf16)acc[R2][e];
+                }
+            }
+        }
     }
 }
 
@@ -847,7 +874,8 @@ struct ChainCfg {
     static constexpr int NJ = DVS / 16;
     static constexpr int NTW = (C / 16) * NJ;               // W / O tiles
     static constexpr int NTS = (DK / 16) * NJ;              // state tiles
-    static constexpr int NSW = (NTW + 3) / 4, NSS = (NTS + 3) / 4;
+    // each wave owns whole row tiles: RPW rows of W / O, SPW rows of the state
+    static constexpr int RPW = (C / 16 + 3) / 4, SPW = DK / 64;
     // prefetch units of 16 bytes: Qt, Wk, Kb^T, P (input dtype), U slice, gam (fp32)
     static constexpr int E16 = 16 / sizeof(T);
     static constexpr int U_QT = C * DK / E16, U_WK = U_QT, U_KB = DK * C / E16, U_P = C * C / E16;
@@ -998,31 +1026,35 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     for (int d = 0; d < D; ++d)
         if (d < NC) KDA_CHAIN_PREFETCH(d, bh * NC + d);
 
-    floatx4 accS[Cfg::NSS];
-    static_for<Cfg::NSS>([&](auto SI) {
-        constexpr int s = SI;
-        const int ts = wave + 4 * s;
-        accS[s] = zero4();
-        if (ts < NTS && s0) {
-            const int ct = ts / NJ, jt = ts % NJ;
+    typedef typename Mma<T>::frag frag;
+    const int fr = lane & 15, fk = (lane >> 4) * Mma<T>::KPL;     // fragment row, k offset
+    floatx4 accS[Cfg::SPW][NJ];
+    static_for<Cfg::SPW>([&](auto SI) {
+        constexpr int si = SI;
+        const int ct = wave + 4 * si;
+        static_for<NJ>([&](auto JI) {
+            constexpr int jt = JI;
+            accS[si][jt] = zero4();
+            if (s0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = ct * 16 + 4 * (lane >> 4) + e, j = jt * 16 + (lane & 15);
-                accS[s][e] = s0[(bh * DK + c) * (long)DV + j0 + j];
+                for (int e = 0; e < 4; ++e) {
+                    const int c = ct * 16 + 4 * (lane >> 4) + e, j = jt * 16 + (lane & 15);
+                    accS[si][jt][e] = s0[(bh * DK + c) * (long)DV + j0 + j];
+                }
             }
-        }
+        });
     });
     // S^T as the B operand of the products with S: sST[j][c], 4 consecutive c per lane
     auto write_state_operand = [&]() {
-        static_for<Cfg::NSS>([&](auto SI) {
-            constexpr int s = SI;
-            const int ts = wave + 4 * s;
-            if (ts < NTS) {
-                const int ct = ts / NJ, jt = ts % NJ;
+        static_for<Cfg::SPW>([&](auto SI) {
+            constexpr int si = SI;
+            const int ct = wave + 4 * si;
+            static_for<NJ>([&](auto JI) {
+                constexpr int jt = JI;
                 const int j = jt * 16 + (lane & 15), c = ct * 16 + 4 * (lane >> 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sST[j * LDK + c + e] = from_f32<T>(accS[s][e]);
-            }
+                for (int e = 0; e < 4; ++e) sST[j * LDK + c + e] = from_f32<T>(accS[si][jt][e]);
+            });
         });
     };
     write_state_operand();
@@ -1036,52 +1068,82 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         if (n + D < NC) KDA_CHAIN_PREFETCH(d, bh * NC + n + D);    // in flight for D chunks
         __syncthreads();
 
-        // ---- W = U - Wk S (to LDS, transposed) and the state part of O
-        floatx4 accO[Cfg::NSW];
-        static_for<Cfg::NSW>([&](auto SI) {
-            constexpr int s = SI;
-            const int tw = wave + 4 * s;
-            accO[s] = zero4();
-            if (tw < NTW) {
-                const int R = tw / NJ, J = tw % NJ;
-                floatx4 wk = mma_tile<T>(zero4(), sWk + R * 16 * LDK, LDK, sST + J * 16 * LDK, LDK, DK, lane);
-                accO[s] = mma_tile<T>(zero4(), sQt + R * 16 * LDK, LDK, sST + J * 16 * LDK, LDK, DK, lane);
-                const int j = J * 16 + (lane & 15), r = R * 16 + 4 * (lane >> 4);
+        // ---- W = U - Wk S (to LDS, transposed) and the state part of O;
+        //      the Wk and Qt fragments are shared by all value-column tiles
+        floatx4 accO[Cfg::RPW][NJ];
+        static_for<Cfg::RPW>([&](auto RI) {
+            constexpr int ri = RI;
+            const int R = wave + 4 * ri;
+            if (R < C / 16) {
+                floatx4 wk[NJ];
+                static_for<NJ>([&](auto JI) { wk[JI] = zero4(); accO[ri][JI] = zero4(); });
+                for (int k0 = 0; k0 < DK; k0 += KSTEP) {
+                    const frag fw = *reinterpret_cast<const frag*>(sWk + (R * 16 + fr) * LDK + k0 + fk);
+                    const frag fq = *reinterpret_cast<const frag*>(sQt + (R * 16 + fr) * LDK + k0 + fk);
+                    static_for<NJ>([&](auto JI) {
+                        constexpr int J = JI;
+                        const frag fb = *reinterpret_cast<const frag*>(sST + (J * 16 + fr) * LDK + k0 + fk);
+                        wk[J] = Mma<T>::mma(fw, fb, wk[J]);
+                        accO[ri][J] = Mma<T>::mma(fq, fb, accO[ri][J]);
+                    });
+                }
+                static_for<NJ>([&](auto JI) {
+                    constexpr int J = JI;
+                    const int j = J * 16 + (lane & 15), r = R * 16 + 4 * (lane >> 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sWT[j * LDC + r + e] = from_f32<T>(sU[(r + e) * DVS + j] - wk[e]);
+                    for (int e = 0; e < 4; ++e) sWT[j * LDC + r + e] = from_f32<T>(sU[(r + e) * DVS + j] - wk[J][e]);
+                });
             }
         });
         __syncthreads();
 
         // ---- O += P W ; S = gam * S + Kb^T W
-        static_for<Cfg::NSW>([&](auto SI) {
-            constexpr int s = SI;
-            const int tw = wave + 4 * s;
-            if (tw < NTW) {
-                const int R = tw / NJ, J = tw % NJ;
+        static_for<Cfg::RPW>([&](auto RI) {
+            constexpr int ri = RI;
+            const int R = wave + 4 * ri;
+            if (R < C / 16) {
                 const int K = ((16 * (R + 1) + KSTEP - 1) / KSTEP) * KSTEP;
-                accO[s] = mma_tile<T>(accO[s], sP + R * 16 * LDC, LDC, sWT + J * 16 * LDC, LDC, K, lane);
-                const int j = J * 16 + (lane & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = R * 16 + 4 * (lane >> 4) + e;
-                    if constexpr (Cfg::STAGE_O) {
-                        sO[r * DVS + j] = from_f32<TOut>(accO[s][e]);
-                    } else {
-                        const int t = n * C + r;
-                        if (t < T_len) o[(((long)b * T_len + t) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[s][e]);
-                    }
+                for (int k0 = 0; k0 < K; k0 += KSTEP) {
+                    const frag fp = *reinterpret_cast<const frag*>(sP + (R * 16 + fr) * LDC + k0 + fk);
+                    static_for<NJ>([&](auto JI) {
+                        constexpr int J = JI;
+                        const frag fb = *reinterpret_cast<const frag*>(sWT + (J * 16 + fr) * LDC + k0 + fk);
+                        accO[ri][J] = Mma<T>::mma(fp, fb, accO[ri][J]);
+                    });
                 }
+                static_for<NJ>([&](auto JI) {
+                    constexpr int J = JI;
+                    const int j = J * 16 + (lane & 15);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = R * 16 + 4 * (lane >> 4) + e;
+                        if constexpr (Cfg::STAGE_O) {
+                            sO[r * DVS + j] = from_f32<TOut>(accO[ri][J][e]);
+                        } else {
+                            const int tt = n * C + r;
+                            if (tt < T_len) o[(((long)b * T_len + tt) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[ri][J][e]);
+                        }
+                    }
+                });
             }
         });
-        static_for<Cfg::NSS>([&](auto SI) {
-            constexpr int s = SI;
-            const int ts = wave + 4 * s;
-            if (ts < NTS) {
-                const int ct = ts / NJ, jt = ts % NJ;
+        static_for<Cfg::SPW>([&](auto SI) {
+            constexpr int si = SI;
+            const int ct = wave + 4 * si;
+            float gm[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) accS[s][e] *= sGam[ct * 16 + 4 * (lane >> 4) + e];
-                accS[s] = mma_tile<T>(accS[s], sKbT + ct * 16 * LDC, LDC, sWT + jt * 16 * LDC, LDC, CK, lane);
+            for (int e = 0; e < 4; ++e) gm[e] = sGam[ct * 16 + 4 * (lane >> 4) + e];
+            static_for<NJ>([&](auto JI) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accS[si][JI][e] *= gm[e];
+            });
+            for (int k0 = 0; k0 < CK; k0 += KSTEP) {
+                const frag fa = *reinterpret_cast<const frag*>(sKbT + (ct * 16 + fr) * LDC + k0 + fk);
+                static_for<NJ>([&](auto JI) {
+                    constexpr int J = JI;
+                    const frag fb = *reinterpret_cast<const frag*>(sWT + (J * 16 + fr) * LDC + k0 + fk);
+                    accS[si][J] = Mma<T>::mma(fa, fb, accS[si][J]);
+                });
             }
         });
         __syncthreads();
@@ -1090,10 +1152,10 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
             constexpr int NUO = C * DVS / EO;
             for (int u = tid; u < NUO; u += 256) {
                 const int r = (u * EO) / DVS, jj = (u * EO) % DVS;
-                const int t = n * C + r;
-                if (t < T_len)
-                    *reinterpret_cast<u32x4*>(o + (((long)b * T_len + t) * H + h) * DV + j0 + jj) =
-                        *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
+                const int tt = n * C + r;
+                if (tt < T_len)
+                    *reinterpret_cast<uint4*>(o + (((long)b * T_len + tt) * H + h) * DV + j0 + jj) =
+                        *reinterpret_cast<const uint4*>(sO + r * DVS + jj);
             }
         }
         write_state_operand();
@@ -1101,17 +1163,17 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     }
 
     if (sT) {
-        static_for<Cfg::NSS>([&](auto SI) {
-            constexpr int s = SI;
-            const int ts = wave + 4 * s;
-            if (ts < NTS) {
-                const int ct = ts / NJ, jt = ts % NJ;
+        static_for<Cfg::SPW>([&](auto SI) {
+            constexpr int si = SI;
+            const int ct = wave + 4 * si;
+            static_for<NJ>([&](auto JI) {
+                constexpr int jt = JI;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int c = ct * 16 + 4 * (lane >> 4) + e, j = jt * 16 + (lane & 15);
-                    sT[(bh * DK + c) * (long)DV + j0 + j] = accS[s][e];
+                    sT[(bh * DK + c) * (long)DV + j0 + j] = accS[si][jt][e];
                 }
-            }
+            });
         });
     }
 }
@@ -1221,14 +1283,15 @@ bool chunk_supported(int dk, int dv, int C, bool in_bf16) {
     return false;
 }
 
-template <int DK, int DV>
+template <int DV>
 static hipError_t launch_intra64(const ChunkArgs& a) {
+    constexpr int DK = 128;
     const int NC = (a.T + 63) / 64;
     const long nch = (long)a.B * a.H * NC;
     if (nch == 0) return hipSuccess;
     const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, true, 64);
     char* ws = (char*)a.ws;
-    hipLaunchKernelGGL((chunk_intra64_kernel<DK, DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL((chunk_intra64_kernel<DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
                        (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
                        (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
@@ -1239,7 +1302,7 @@ template <typename T, int DK, int DV>
 static hipError_t intra_c(const ChunkArgs& a) {
     if constexpr (sizeof(T) == 2) {
         if constexpr (DK == 128) {
-            if (a.C == 64 && !a.generic) return launch_intra64<DK, DV>(a);
+            if (a.C == 64 && !a.generic) return launch_intra64<DV>(a);
         }
     }
     switch (a.C) {
