@@ -154,9 +154,12 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // chunk-major order: workgroups running together cover all heads of the same
+    // tokens, so every token row of q, k, v, g is read whole and at once
     const long ch = blockIdx.x;
-    const int n = (int)(ch % NC);
-    const long bh = ch / NC;
+    const long BH = (long)gridDim.x / NC;
+    const int n = (int)(ch / BH);
+    const long bh = ch % BH;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const int t0 = n * C;
     auto grow = [&](int t) -> long { return ((long)b * T_len + (t0 + t)) * H + h; };
@@ -432,8 +435,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             sKt[c * LDT + t] = from_f32<T>(bt * k0 * ei0);
             sKt[(c + 1) * LDT + t] = from_f32<T>(bt * k1 * ei1);
             Pair2<T>::store(gQt + t * DK + c, q0 * ei0, q1 * ei1);
-            gKb[c * C + t] = from_f32<T>(k0 * eo0);            // Kb stored transposed: [dk][C]
-            gKb[(c + 1) * C + t] = from_f32<T>(k1 * eo1);
+            Pair2<T>::store(gKb + t * DK + c, k0 * eo0, k1 * eo1);
         }
     }
     if (tid < DK) {
@@ -522,6 +524,7 @@ struct Intra64Cfg {
     static constexpr size_t TOTAL = OFF_BETA + size_t(C) * 4;
     static_assert(size_t(C / 2) * (C / 2 + 4) * 4 <= size_t(C) * C * 2, "T temp fits the P staging");
     static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
+    static_assert(size_t(C) * DV * 4 + size_t(C) * DK * 2 <= OFF_KT, "U / Wk staging below the kept K~^T");
     static_assert(NITV >= 1 && (C * DV / 8) % NT == 0, "v unit mapping");
 };
 
@@ -543,9 +546,12 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     auto blk = [&](int b) { return sOp + b * 16 * LDH; };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // chunk-major order: workgroups running together cover all heads of the same
+    // tokens, so every token row of q, k, v, g is read whole and at once
     const long ch = blockIdx.x;
-    const int n = (int)(ch % NC);
-    const long bh = ch / NC;
+    const long BH = (long)gridDim.x / NC;
+    const int n = (int)(ch / BH);
+    const long bh = ch % BH;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const int t0 = n * C;
     auto grow = [&](int t) -> long { return ((long)b * T_len + (t0 + t)) * H + h; };
@@ -610,7 +616,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 
     // ---------------------------------------------------------------- a2 + a3 per channel half
     bf16* gQt = ws_qt + ch * (long)C * DK;
-    bf16* gKb = ws_kb + ch * (long)DK * C;
+    bf16* gKb = ws_kb + ch * (long)C * DK;
     floatx4 accA[2], accP[2];
     accA[0] = accA[1] = accP[0] = accP[1] = zero4();
     // pair assignment: w0 (0,0); w1 (1,0)(1,1); w2 (2,0)(2,1); w3 (2,2); w4 (3,0)(3,1); w5 (3,2)(3,3)
@@ -655,10 +661,8 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         for (int m = 0; m < 8; ++m) o1[m] = qr[m] * eb[m];
         Vec8<bf16>::store(gQt + t * DK + c, o1);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]);
-            gKb[(c + m) * C + t] = (bf16)(kf[m] * er[m]);
-        }
+        for (int m = 0; m < 8; ++m) { sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]); o2[m] = kf[m] * er[m]; }
+        Vec8<bf16>::store(gKb + t * DK + c, o2);
         if (p == 0 && tid < DK) {
             float gam = 1.f;
 #pragma unroll
@@ -834,37 +838,75 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         float* gU = ws_u + ch * (long)C * DV;
         bf16* gW = ws_wk + ch * (long)C * DK;
         const int r = lane & 15, kg = lane >> 4;
-        for (int ct = wave; ct < NCT; ct += NW) {
-            const bool isU = ct < NUT;
-            const bf16* bsrc = isU ? sVt + ct * 16 * LDT : sKtT + (ct - NUT) * 16 * LDT;
-            floatx4 acc[4];
+        constexpr int NTPW = (NCT + NW - 1) / NW;                  // column tiles per wave
+        floatx4 acc[NTPW][4];
 #pragma unroll
-            for (int R2 = 0; R2 < 4; ++R2) acc[R2] = zero4();
+        for (int sct = 0; sct < NTPW; ++sct) {
+            const int ct = wave + NW * sct;
 #pragma unroll
-            for (int k0 = 0; k0 < C; k0 += 32) {
-                const bf16x8 fb = *reinterpret_cast<const bf16x8*>(bsrc + r * LDT + k0 + 8 * kg);
+            for (int R2 = 0; R2 < 4; ++R2) acc[sct][R2] = zero4();
+            if (ct < NCT) {
+                const bool isU = ct < NUT;
+                const bf16* bsrc = isU ? sVt + ct * 16 * LDT : sKtT + (ct - NUT) * 16 * LDT;
 #pragma unroll
-                for (int R2 = 0; R2 < 4; ++R2) {
-                    if (k0 >= 16 * (R2 + 1)) continue;              // T is lower triangular
-                    const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sTb + (R2 * 16 + r) * LDT + k0 + 8 * kg);
-                    acc[R2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[R2], 0, 0, 0);
-                }
-            }
-            const int col = (isU ? ct : ct - NUT) * 16 + (lane & 15);
+                for (int k0 = 0; k0 < C; k0 += 32) {
+                    const bf16x8 fb = *reinterpret_cast<const bf16x8*>(bsrc + r * LDT + k0 + 8 * kg);
 #pragma unroll
-            for (int R2 = 0; R2 < 4; ++R2) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = R2 * 16 + 4 * (lane >> 4) + e;
-                    if (isU) gU[row * DV + col] = acc[R2][e];
-                    else gW[row * DK + col] = (bf16)acc[R2][e];
+                    for (int R2 = 0; R2 < 4; ++R2) {
+                        if (k0 >= 16 * (R2 + 1)) continue;              // T is lower triangular
+                        const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sTb + (R2 * 16 + r) * LDT + k0 + 8 * kg);
+                        acc[sct][R2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[sct][R2], 0, 0, 0);
+                    }
                 }
             }
         }
+        __syncthreads();                               // operands read by every wave: staging may overwrite them
+        {
+            float* sUo = reinterpret_cast<float*>(smem);
+            bf16* sWo = reinterpret_cast<bf16*>(smem + size_t(C) * DV * 4);
+#pragma unroll
+            for (int sct = 0; sct < NTPW; ++sct) {
+                const int ct = wave + NW * sct;
+                if (ct >= NCT) continue;
+                const bool isU = ct < NUT;
+                const int col = (isU ? ct : ct - NUT) * 16 + (lane & 15);
+#pragma unroll
+                for (int R2 = 0; R2 < 4; ++R2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = R2 * 16 + 4 * (lane >> 4) + e;
+                        if (isU) sUo[row * DV + col] = acc[sct][R2][e];
+                        else sWo[row * DK + col] = (bf16)acc[sct][R2][e];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        const uint4* sUo = reinterpret_cast<const uint4*>(smem);
+        const uint4* sWo = reinterpret_cast<const uint4*>(smem + size_t(C) * DV * 4);
+        for (int u = tid; u < C * DV / 4; u += NT) reinterpret_cast<uint4*>(gU)[u] = sUo[u];
+        for (int u = tid; u < C * DK / 8; u += NT) reinterpret_cast<uint4*>(gW)[u] = sWo[u];
     }
 }
 
 // ================================================================ stage 2: chain
+// 16 bytes of one row of a row-major matrix written as a column of its transpose
+template <typename T> struct TransStore;
+template <> struct TransStore<bf16> {
+    __device__ static inline void run(u32x4 v, bf16* dst, int ld) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dst[m * ld] = x[m];
+    }
+};
+template <> struct TransStore<float> {
+    __device__ static inline void run(u32x4 v, float* dst, int ld) {
+        const floatx4 x = __builtin_bit_cast(floatx4, v);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[m * ld] = x[m];
+    }
+};
+
 template <typename T, typename TOut, int DK, int DV, int C, int DVS>
 struct ChainCfg {
     static constexpr int PADT = sizeof(T) == 2 ? 8 : 4;
@@ -947,6 +989,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     }
     const int j0 = sl * DVS;
     const int b = (int)(bh / H), h = (int)(bh % H);
+    const long BH = (long)gridDim.x / NSL;       // workspace is chunk-major: (n, bh) -> n * BH + bh
 
     // ---- register prefetch of one chunk's operands (16-byte units), one
     // statically sized register array per operand
@@ -994,8 +1037,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
             if (u < Cfg::U_KB) {                                                                   \
-                const int e = u * E16;                                                             \
-                *reinterpret_cast<u32x4*>(sKbT + (e / C) * LDC + e % C) = preK[SL][i];                 \
+                const int e = u * E16;                 /* Kb is row-major [C][DK]: transpose */    \
+                TransStore<T>::run(preK[SL][i], sKbT + (e % DK) * LDC + e / DK, LDC);              \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \
@@ -1024,7 +1067,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
 
 #pragma unroll
     for (int d = 0; d < D; ++d)
-        if (d < NC) KDA_CHAIN_PREFETCH(d, bh * NC + d);
+        if (d < NC) KDA_CHAIN_PREFETCH(d, (long)d * BH + bh);
 
     typedef typename Mma<T>::frag frag;
     const int fr = lane & 15, fk = (lane >> 4) * Mma<T>::KPL;     // fragment row, k offset
@@ -1065,7 +1108,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         const int n = n0 + d;
         if (n >= NC) return;
         KDA_CHAIN_COMMIT(d);                                        // chunk n operands -> LDS
-        if (n + D < NC) KDA_CHAIN_PREFETCH(d, bh * NC + n + D);    // in flight for D chunks
+        if (n + D < NC) KDA_CHAIN_PREFETCH(d, (long)(n + D) * BH + bh);   // in flight for D chunks
         __syncthreads();
 
         // ---- W = U - Wk S (to LDS, transposed) and the state part of O;

@@ -26,7 +26,8 @@ struct ChunkArgs {
     bool generic = false;   // force the generic intra-chunk kernel (tests)
 };
 
-// Workspace of the split chunk path, per (b, h, chunk), struct of arrays:
+// Workspace of the split chunk path: struct of arrays, each indexed by the
+// chunk-major unit id n * (B*H) + (b*H + h); per unit
 //   Qt [C][dk] in, Wk [C][dk] in, Kb [C][dk] in, P [C][C] in, U [C][dv] fp32, gam [dk] fp32
 struct WsLayout {
     size_t qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
