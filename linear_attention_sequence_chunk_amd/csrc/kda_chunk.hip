@@ -435,7 +435,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             sKt[c * LDT + t] = from_f32<T>(bt * k0 * ei0);
             sKt[(c + 1) * LDT + t] = from_f32<T>(bt * k1 * ei1);
             Pair2<T>::store(gQt + t * DK + c, q0 * ei0, q1 * ei1);
-            Pair2<T>::store(gKb + t * DK + c, k0 * eo0, k1 * eo1);
+            gKb[c * C + t] = from_f32<T>(k0 * eo0);            // Kb stored transposed: [dk][C]
+            gKb[(c + 1) * C + t] = from_f32<T>(k1 * eo1);
         }
     }
     if (tid < DK) {
@@ -513,18 +514,21 @@ struct Intra64Cfg {
     static constexpr size_t BLK = size_t(16) * LDH * 2;                 // one 16-row operand block
     // operand blocks: Kr 0-3, Qr 4-7, Kf 8-10 (blocks 0..2), Kd 11-14, Kr3' 15, Qr3' 16, Kf0' 17
     static constexpr size_t SZ_S = 18 * BLK;
+    // after the score matrices (aliasing the operand blocks): M then T (fp32), later V^T
     static constexpr size_t OFF_A = 0;
-    static constexpr size_t OFF_TB = OFF_A + size_t(C) * LDA * 4;
+    static constexpr size_t OFF_VT = 0;
+    static constexpr size_t OFF_TB = size_t(C) * LDA * 4;
     static constexpr size_t OFF_PB = OFF_TB + size_t(C) * LDT * 2;      // P staging, then the T temp
-    static constexpr size_t OFF_VT = OFF_PB + size_t(C) * C * 2;
-    static constexpr size_t SZ_W = OFF_VT + size_t(DV) * LDT * 2;
-    static constexpr size_t OFF_KT = SZ_S > SZ_W ? SZ_S : SZ_W;         // (e^G k)^T [DK][LDT], kept
-    static constexpr size_t OFF_TOT = OFF_KT + size_t(DK) * LDT * 2;
+    static constexpr size_t SZ_W = OFF_PB + size_t(C) * C * 2;
+    static constexpr size_t OFF_KT = SZ_S > SZ_W ? SZ_S : SZ_W;         // (e^G k)^T [DK][LDT]
+    static constexpr size_t OFF_KB = OFF_KT + size_t(DK) * LDT * 2;     // Kb^T staging [DK][C]
+    static constexpr size_t OFF_TOT = OFF_KB + size_t(DK) * C * 2;
     static constexpr size_t OFF_BETA = OFF_TOT + size_t(NB) * DK * 4;
     static constexpr size_t TOTAL = OFF_BETA + size_t(C) * 4;
+    static_assert(size_t(DV) * LDT * 2 <= size_t(C) * LDA * 4, "V^T fits over M");
     static_assert(size_t(C / 2) * (C / 2 + 4) * 4 <= size_t(C) * C * 2, "T temp fits the P staging");
     static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
-    static_assert(size_t(C) * DV * 4 + size_t(C) * DK * 2 <= OFF_KT, "U / Wk staging below the kept K~^T");
+    static_assert(size_t(C) * DV * 4 + size_t(C) * DK * 2 <= TOTAL, "U / Wk staging");
     static_assert(NITV >= 1 && (C * DV / 8) % NT == 0, "v unit mapping");
 };
 
@@ -541,6 +545,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
     bf16* sOp = reinterpret_cast<bf16*>(smem);
     bf16* sKtT = reinterpret_cast<bf16*>(smem + Cfg::OFF_KT);
+    bf16* sKbT = reinterpret_cast<bf16*>(smem + Cfg::OFF_KB);
     float* sTot = reinterpret_cast<float*>(smem + Cfg::OFF_TOT);
     float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_BETA);
     auto blk = [&](int b) { return sOp + b * 16 * LDH; };
@@ -616,7 +621,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 
     // ---------------------------------------------------------------- a2 + a3 per channel half
     bf16* gQt = ws_qt + ch * (long)C * DK;
-    bf16* gKb = ws_kb + ch * (long)C * DK;
+    bf16* gKb = ws_kb + ch * (long)DK * C;
     floatx4 accA[2], accP[2];
     accA[0] = accA[1] = accP[0] = accP[1] = zero4();
     // pair assignment: w0 (0,0); w1 (1,0)(1,1); w2 (2,0)(2,1); w3 (2,2); w4 (3,0)(3,1); w5 (3,2)(3,3)
@@ -661,8 +666,10 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         for (int m = 0; m < 8; ++m) o1[m] = qr[m] * eb[m];
         Vec8<bf16>::store(gQt + t * DK + c, o1);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) { sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]); o2[m] = kf[m] * er[m]; }
-        Vec8<bf16>::store(gKb + t * DK + c, o2);
+        for (int m = 0; m < 8; ++m) {
+            sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]);
+            sKbT[(c + m) * C + t] = (bf16)(kf[m] * er[m]);
+        }
         if (p == 0 && tid < DK) {
             float gam = 1.f;
 #pragma unroll
@@ -671,6 +678,10 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         }
         __syncthreads();
 
+        if (p == 1) {                                  // Kb^T complete: 16-byte rows to the workspace
+            for (int u = tid; u < DK * C / 8; u += NT)
+                reinterpret_cast<uint4*>(gKb)[u] = reinterpret_cast<const uint4*>(sKbT)[u];
+        }
         // A and P over this channel half (K = 64: two MFMA steps)
         if (wave < 6) {
             const int Rw = wave == 0 ? 0 : (wave <= 2 ? wave : (wave == 3 ? 2 : 3));
@@ -826,6 +837,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         pr[1] = (bf16)(sA[r * LDA + i + 1] * sBeta[i + 1]);
         *reinterpret_cast<bf16x2*>(sTb + r * LDT + i) = pr;
     }
+    __syncthreads();                                   // M / T dead: V^T goes over it
 #pragma unroll
     for (int it = 0; it < Cfg::NITV; ++it) {
         const int u = tid + NT * it, tv = u / (DV / 8), j = 8 * (u % (DV / 8));
@@ -890,23 +902,6 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 }
 
 // ================================================================ stage 2: chain
-// 16 bytes of one row of a row-major matrix written as a column of its transpose
-template <typename T> struct TransStore;
-template <> struct TransStore<bf16> {
-    __device__ static inline void run(u32x4 v, bf16* dst, int ld) {
-        const bf16x8 x = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) dst[m * ld] = x[m];
-    }
-};
-template <> struct TransStore<float> {
-    __device__ static inline void run(u32x4 v, float* dst, int ld) {
-        const floatx4 x = __builtin_bit_cast(floatx4, v);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) dst[m * ld] = x[m];
-    }
-};
-
 template <typename T, typename TOut, int DK, int DV, int C, int DVS>
 struct ChainCfg {
     static constexpr int PADT = sizeof(T) == 2 ? 8 : 4;
@@ -1037,8 +1032,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
             const int u = tid + 256 * i;                                                           \
             if (u < Cfg::U_KB) {                                                                   \
-                const int e = u * E16;                 /* Kb is row-major [C][DK]: transpose */    \
-                TransStore<T>::run(preK[SL][i], sKbT + (e % DK) * LDC + e / DK, LDC);              \
+                const int e = u * E16;                                                             \
+                *reinterpret_cast<u32x4*>(sKbT + (e / C) * LDC + e % C) = preK[SL][i];             \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \

@@ -28,7 +28,7 @@ struct ChunkArgs {
 
 // Workspace of the split chunk path: struct of arrays, each indexed by the
 // chunk-major unit id n * (B*H) + (b*H + h); per unit
-//   Qt [C][dk] in, Wk [C][dk] in, Kb [C][dk] in, P [C][C] in, U [C][dv] fp32, gam [dk] fp32
+//   Qt [C][dk] in, Wk [C][dk] in, Kb^T [dk][C] in, P [C][C] in, U [C][dv] fp32, gam [dk] fp32
 struct WsLayout {
     size_t qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
 };
