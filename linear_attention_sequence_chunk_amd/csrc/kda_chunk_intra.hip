@@ -1,136 +1,9 @@
-// kda_chunk.hip -- chunkwise-parallel KDA forward on gfx950: two stages.
-//
-// The chunkwise form (chunk paragraph of "一个KimiK3装下22580个GPT-2…";
-// sections 十六 and 十七 of "我终于看懂了 KDA…"): the sequence is cut into chunks
-// of C tokens; inside a chunk the work is parallel (masked attention scores and
-// the chunk's rank-1 updates folded into matrix products, the WY / DPLR view),
-// across chunks the state is carried sequentially.  For a chunk with local
-// positions r, i, start state S and per-channel log-gate prefix sums G:
-//
-//   A_ri = sum_c k_rc k_ic e^{G_rc - G_ic} (i < r)     P_ri = sum_c q_rc k_ic e^{G_rc - G_ic} (i <= r)
-//   T    = (I + Diag(beta) A)^-1
-//   U    = T Diag(beta) V          Wk = T Diag(beta) (e^G * K)
-//   W    = U - Wk S                (row r is the token's correction u_r)
-//   O    = (e^G * Q) S + P W
-//   S   <- Diag(e^{G_last}) S + (e^{G_last - G} * K)^T W
-//
-// Stage 1 (chunk_intra_kernel, one workgroup per (b, h, chunk), all chunks in
-// parallel) computes everything that does not depend on S into a workspace:
-// Qt = e^G*Q, Wk, Kb = e^{G_last-G}*K, P, U and gam = e^{G_last}.
-// Stage 2 (chunk_chain_kernel, one workgroup per (b, h, value-column slice))
-// walks the chunks in order with the fp32 state in MFMA accumulators.
-//
-// Exponent safety.  e^{G_r - G_i} is never formed as e^{G_r} * e^{-G_i} across a
-// whole chunk (the chunk sum of log-gates can pass -88, where e^{-G} overflows
-// fp32).  The chunk is split into 16-token sub-blocks; a pair of sub-blocks
-// (R, I), I < R, is handled at the level of the binary split where they separate,
-// with the split point m as reference: the row factor e^{G_r - G_{m-1}} and the
-// column factor e^{G_{m-1} - G_i} are both <= 1.  Diagonal sub-blocks use the
-// block start as reference; this is exact as long as the block's own log-gate sum
-// stays above -SAFE_SPAN, otherwise that block is computed term by term.
-// Prefix sums are kept block-local (16 tokens) so that exponent differences do
-// not lose digits to a large running sum.
-#include <utility>
-
-#include "kda_common.h"
-#include "kda_launch.h"
+// kda_chunk_intra.hip -- stage 1 of the chunkwise forward (every chunk in
+// parallel) and the host-side dispatch of both stages.  The method and the
+// exponent-safety scheme are described in kda_chunk.h.
+#include "kda_chunk.h"
 
 namespace kda {
-
-// ------------------------------------------------------------ compile-time helpers
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
-    (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
-// Lower-triangular sub-block pairs (R, I), I <= R, enumerated p = R(R+1)/2 + I.
-constexpr int pair_R(int p) { int R = 0; while ((R + 1) * (R + 2) / 2 <= p) ++R; return R; }
-constexpr int pair_I(int p) { return p - pair_R(p) * (pair_R(p) + 1) / 2; }
-// Segment length (tokens) of the binary split that separates R and I; 0 = diagonal.
-constexpr int pair_level(int p) { return pair_R(p) == pair_I(p) ? 0 : 32 << ilog2(pair_R(p) ^ pair_I(p)); }
-constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr size_t smax(size_t a, size_t b) { return a > b ? a : b; }
-
-constexpr size_t LDS_LIMIT = 160 * 1024;
-
-// Two accumulators sharing the B operand: acc1 += A1 B, acc2 += A2 B.
-template <typename T>
-__device__ inline void mma_tile2(floatx4& acc1, floatx4& acc2, const T* __restrict__ a1,
-                                 const T* __restrict__ a2, int lda, const T* __restrict__ bt,
-                                 int ldb, int K, int lane) {
-    typedef typename Mma<T>::frag frag;
-    const int r = lane & 15, kg = lane >> 4;
-    const int oa = r * lda + kg * Mma<T>::KPL, ob = r * ldb + kg * Mma<T>::KPL;
-    for (int k0 = 0; k0 < K; k0 += Mma<T>::KSTEP) {
-        frag fb = *reinterpret_cast<const frag*>(bt + ob + k0);
-        frag f1 = *reinterpret_cast<const frag*>(a1 + oa + k0);
-        frag f2 = *reinterpret_cast<const frag*>(a2 + oa + k0);
-        acc1 = Mma<T>::mma(f1, fb, acc1);
-        acc2 = Mma<T>::mma(f2, fb, acc2);
-    }
-}
-
-// fp32 MFMA with both operands stored row-major: A[row][k], B[k][col].
-__device__ inline floatx4 mma_f32_rowB(floatx4 acc, const float* a, int lda, const float* b,
-                                       int ldb, int K, int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-    for (int k0 = 0; k0 < K; k0 += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * lda + k0 + kg], b[(k0 + kg) * ldb + r], acc, 0, 0, 0);
-    return acc;
-}
-
-template <typename T> struct Pair2;
-template <> struct Pair2<bf16> {
-    __device__ static inline void load(const bf16* p, float& x, float& y) {
-        bf16x2 v = *reinterpret_cast<const bf16x2*>(p); x = (float)v[0]; y = (float)v[1];
-    }
-    __device__ static inline void store(bf16* p, float x, float y) {
-        bf16x2 v; v[0] = (bf16)x; v[1] = (bf16)y; *reinterpret_cast<bf16x2*>(p) = v;
-    }
-};
-template <> struct Pair2<float> {
-    __device__ static inline void load(const float* p, float& x, float& y) {
-        float2 v = *reinterpret_cast<const float2*>(p); x = v.x; y = v.y;
-    }
-    __device__ static inline void store(float* p, float x, float y) {
-        *reinterpret_cast<float2*>(p) = make_float2(x, y);
-    }
-};
-
-// ================================================================ stage 1: intra
-template <typename T, int DK, int DV, int C>
-struct IntraCfg {
-    static constexpr int NB = C / 16;                       // 16-token sub-blocks
-    static constexpr int NP = NB * (NB + 1) / 2;            // lower-triangular block pairs
-    static constexpr int NSLOT = (NP + 3) / 4;              // per-wave accumulator slots
-    static constexpr int NLV = ilog2(NB);                   // cross levels
-    static constexpr int HR = cmax(16, C / 2);              // rows per operand buffer
-    static constexpr int NPASS = C / HR;                    // passes of the diagonal level
-    static constexpr int PADT = sizeof(T) == 2 ? 8 : 4;     // 16-byte row padding
-    static constexpr int LDK = DK + PADT;
-    static constexpr int CK = cmax(C, Mma<T>::KSTEP);       // contraction length over positions
-    static constexpr int LDT = CK + PADT;
-    static constexpr int LDA = C + 8;
-    static constexpr size_t SZ_L = size_t(C) * DK * 4;
-    static constexpr size_t SZ_OP = size_t(HR) * LDK * sizeof(T);
-    static constexpr size_t PHASE_S = SZ_L + 3 * SZ_OP;
-    static constexpr size_t SZ_TB = align16(size_t(C) * LDT * sizeof(T));
-    static constexpr size_t SZ_A = size_t(C) * LDA * 4;
-    static constexpr size_t SZ_VK = size_t(DV + DK) * LDT * sizeof(T);
-    static constexpr size_t PHASE_W = SZ_TB + smax(SZ_A, SZ_VK);
-    static constexpr size_t OFF_TOT = align16(smax(PHASE_S, PHASE_W));
-    static constexpr size_t OFF_OFF = OFF_TOT + size_t(NB) * DK * 4;
-    static constexpr size_t OFF_BETA = OFF_OFF + size_t(NB) * DK * 4;
-    static constexpr size_t OFF_FLAG = OFF_BETA + size_t(C) * 4;
-    static constexpr size_t TOTAL = align16(OFF_FLAG + size_t(NB) * 4);
-    static constexpr bool FITS = TOTAL <= LDS_LIMIT;
-};
 
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void chunk_intra_kernel(
@@ -468,39 +341,30 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
 
 // ================================================================ stage 1, bf16 / C = 64 / dk = 128
 // The hot configuration.  Same workspace contents as chunk_intra_kernel.
-//  - Gate factors as products: alpha = e^{g} once per (token, channel); inside
-//    each 16-token block the inclusive prefix product E_t = e^{L_t} and the
-//    exclusive suffix product F_t = e^{tot - L_t} are formed in registers with
-//    DPP row shifts (the 16 tokens of a block sit in the 16 lanes of one DPP
-//    row).  All other decay factors are products of block totals; no factor
-//    ever exceeds 1 except e^{-L}, which is only formed for blocks whose total
-//    stays above SAFE_MIN.  g = -inf gives alpha = 0 exactly.
-//  - Two passes over halves of the key channels keep LDS at ~75 KB so that two
-//    workgroups share a CU; A and P accumulate across the passes.
+//  - Inside each 16-token block the inclusive prefix sum L of the (floored)
+//    log-gate is formed in registers with DPP row shifts: the 16 tokens of a
+//    block sit in the 16 lanes of one DPP row.  E = e^{L} and F = e^{tot - L}
+//    (tot the block sum) are both <= 1; every other decay factor is e^{sum of
+//    block totals} <= 1, except e^{-L} which is only formed for blocks whose
+//    total stays above -SAFE_SPAN.
+//  - The block index is uniform per wave; code that depends on it is
+//    instantiated per block so that nothing indexes registers at run time.
+//  - Two passes over halves of the key channels keep LDS under 80 KB so that
+//    two workgroups share a CU; A and P accumulate across the passes.
 //  - MFMA operand fragments are shared across the tiles a wave computes.
-// Block pairs (R, I) and operands (Kr = k E, Kf = k F, Kd = k / E; b_J = tot_J):
+// Block pairs (R, I) and operands (Kr = k E, Kf = k F, Kd = k e^{-L}; b_J = e^{tot_J}):
 //   (1,0) (3,2): Kr_R . Kf_I      (2,1): Kr_2 . Kf_1      (2,0): Kr_2 . (b_1 Kf_0)
 //   (3,1): (b_2 Kr_3) . Kf_1      (3,0): (b_2 Kr_3) . (b_1 Kf_0)      (R,R): Kr_R . Kd_R
-constexpr float SAFE_MIN = 1.6e-28f;   // e^{-64}
-
 template <int CTRL>
-__device__ __forceinline__ float dpp_or_one(float src) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.0f),
-                                                                 __builtin_bit_cast(int, src), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ float dpp_or_zero(float src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src), CTRL, 0xF, 0xF, true));
 }
-// inclusive prefix / suffix products within each row of 16 lanes
-__device__ __forceinline__ float row_prefix_prod(float x) {
-    x *= dpp_or_one<0x111>(x);   // row_shr:1
-    x *= dpp_or_one<0x112>(x);   // row_shr:2
-    x *= dpp_or_one<0x114>(x);   // row_shr:4
-    x *= dpp_or_one<0x118>(x);   // row_shr:8
-    return x;
-}
-__device__ __forceinline__ float row_suffix_prod(float x) {
-    x *= dpp_or_one<0x101>(x);   // row_shl:1
-    x *= dpp_or_one<0x102>(x);   // row_shl:2
-    x *= dpp_or_one<0x104>(x);   // row_shl:4
-    x *= dpp_or_one<0x108>(x);   // row_shl:8
+// inclusive prefix sum within each row of 16 lanes (fuses into v_add_f32_dpp)
+__device__ __forceinline__ float row_prefix_sum(float x) {
+    x += dpp_or_zero<0x111>(x);   // row_shr:1
+    x += dpp_or_zero<0x112>(x);   // row_shr:2
+    x += dpp_or_zero<0x114>(x);   // row_shr:4
+    x += dpp_or_zero<0x118>(x);   // row_shr:8
     return x;
 }
 
@@ -594,28 +458,16 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     }
     if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
 
-    // ---------------------------------------------------------------- a1: block products
-    // E_t = prod_{j<=t} alpha_j and F_t = prod_{j>t} alpha_j inside the block (per channel);
-    // the block totals of both channel halves go to LDS now, the second half's E and F
-    // are formed again when that half is processed (registers are tight).
-    float E[8], F[8];
-    auto block_products = [&](int p) {
+    // ---------------------------------------------------------------- a1: block-local log-gate sums
+    float Lg[2][8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float a = __expf(m < 4 ? ga[p][m] : gb[p][m - 4]);     // alpha, exactly 0 for -inf
-            E[m] = row_prefix_prod(a);
-            F[m] = dpp_or_one<0x101>(row_suffix_prod(a));                // exclusive suffix
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) Lg[p][m] = row_prefix_sum(clamp_g(m < 4 ? ga[p][m] : gb[p][m - 4]));
+        if (rr == 15) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) sTot[R * DK + chan(p) + m] = Lg[p][m];
         }
-    };
-    block_products(1);
-    if (rr == 15) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) sTot[R * DK + chan(1) + m] = E[m];
-    }
-    block_products(0);
-    if (rr == 15) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) sTot[R * DK + chan(0) + m] = E[m];
     }
     __syncthreads();
 
@@ -628,53 +480,61 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int c = chan(p), cl = c - 64 * p;
-        if (p == 1) block_products(1);
-        float tt[NB][8];
+        static_for<NB>([&](auto RI) {
+            constexpr int RB = RI;                     // this wave's block, as a constant
+            if (R != RB) return;
+            float tR[8], kr[8], qr[8], kf[8], o1[8], o2[8];
+            Vec8<float>::load(sTot + RB * DK + c, tR);
 #pragma unroll
-        for (int J = 0; J < NB; ++J) Vec8<float>::load(sTot + J * DK + c, tt[J]);
-        float kr[8], qr[8], kf[8], o1[8], o2[8];
+            for (int m = 0; m < 8; ++m) {
+                const float E = __expf(Lg[p][m]), F = __expf(tR[m] - Lg[p][m]);
+                const float kk = (float)kv[p][m], qq = (float)qv[p][m];
+                kr[m] = kk * E; qr[m] = qq * E; kf[m] = kk * F;
+            }
+            Vec8<bf16>::store(blk(RB) + rr * LDH + cl, kr);
+            Vec8<bf16>::store(blk(4 + RB) + rr * LDH + cl, qr);
+            if constexpr (RB < 3) Vec8<bf16>::store(blk(8 + RB) + rr * LDH + cl, kf);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float kk = (float)kv[p][m], qq = (float)qv[p][m];
-            kr[m] = kk * E[m]; qr[m] = qq * E[m]; kf[m] = kk * F[m];
-        }
-        Vec8<bf16>::store(blk(R) + rr * LDH + cl, kr);
-        Vec8<bf16>::store(blk(4 + R) + rr * LDH + cl, qr);
-        if (R < 3) Vec8<bf16>::store(blk(8 + R) + rr * LDH + cl, kf);
+            for (int m = 0; m < 8; ++m)                                   // k e^{-L}, safe blocks only
+                o1[m] = tR[m] >= -SAFE_SPAN ? kf[m] * __expf(-tR[m]) : 0.f;
+            Vec8<bf16>::store(blk(11 + RB) + rr * LDH + cl, o1);
+            if constexpr (RB == 3) {
+                Vec8<float>::load(sTot + 2 * DK + c, o2);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o1[m] = tt[R][m] >= SAFE_MIN ? kf[m] / tt[R][m] : 0.f;   // k e^{-L}
-        Vec8<bf16>::store(blk(11 + R) + rr * LDH + cl, o1);
-        if (R == 3) {
+                for (int m = 0; m < 8; ++m) { const float f = __expf(o2[m]); o1[m] = kr[m] * f; o2[m] = qr[m] * f; }
+                Vec8<bf16>::store(blk(15) + rr * LDH + cl, o1);
+                Vec8<bf16>::store(blk(16) + rr * LDH + cl, o2);
+            }
+            if constexpr (RB == 0) {
+                Vec8<float>::load(sTot + 1 * DK + c, o2);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) { o1[m] = kr[m] * tt[2][m]; o2[m] = qr[m] * tt[2][m]; }
-            Vec8<bf16>::store(blk(15) + rr * LDH + cl, o1);
-            Vec8<bf16>::store(blk(16) + rr * LDH + cl, o2);
-        } else if (R == 0) {
+                for (int m = 0; m < 8; ++m) o1[m] = kf[m] * __expf(o2[m]);
+                Vec8<bf16>::store(blk(17) + rr * LDH + cl, o1);
+            }
+            // e^G = E e^{sum_{J<R} tot_J};  e^{G_last - G} = F e^{sum_{J>R} tot_J}
 #pragma unroll
-            for (int m = 0; m < 8; ++m) o1[m] = kf[m] * tt[1][m];
-            Vec8<bf16>::store(blk(17) + rr * LDH + cl, o1);
-        }
-        // e^G = E * prod_{J<R} tot_J ;  e^{G_last - G} = F * prod_{J>R} tot_J
-        float eb[8], er[8];
+            for (int m = 0; m < 8; ++m) { o1[m] = 0.f; o2[m] = 0.f; }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            eb[m] = 1.f; er[m] = 1.f;
+            for (int J = 0; J < NB; ++J) {
+                if (J == RB) continue;
+                Vec8<float>::load(sTot + J * DK + c, tR);
 #pragma unroll
-            for (int J = 0; J < NB; ++J) { if (J < R) eb[m] *= tt[J][m]; if (J > R) er[m] *= tt[J][m]; }
-        }
+                for (int m = 0; m < 8; ++m) { if (J < RB) o1[m] += tR[m]; else o2[m] += tR[m]; }
+            }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o1[m] = qr[m] * eb[m];
-        Vec8<bf16>::store(gQt + t * DK + c, o1);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb[m]);
-            sKbT[(c + m) * C + t] = (bf16)(kf[m] * er[m]);
-        }
+            for (int m = 0; m < 8; ++m) {
+                const float eb = RB > 0 ? __expf(o1[m]) : 1.f, er = RB < 3 ? __expf(o2[m]) : 1.f;
+                o1[m] = qr[m] * eb;
+                sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb);
+                sKbT[(c + m) * C + t] = (bf16)(kf[m] * er);
+            }
+            Vec8<bf16>::store(gQt + t * DK + c, o1);
+        });
         if (p == 0 && tid < DK) {
-            float gam = 1.f;
+            float lg = 0.f;
 #pragma unroll
-            for (int J = 0; J < NB; ++J) gam *= sTot[J * DK + tid];
-            ws_gam[ch * DK + tid] = gam;
+            for (int J = 0; J < NB; ++J) lg += sTot[J * DK + tid];
+            ws_gam[ch * DK + tid] = __expf(lg);
         }
         __syncthreads();
 
@@ -700,7 +560,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             const int dR = wave == 0 ? 0 : wave == 1 ? 1 : wave == 3 ? 2 : 3;
             bool uns = false;
             if (dslot >= 0) {
-                uns = sTot[dR * DK + lane] < SAFE_MIN || sTot[dR * DK + 64 + lane] < SAFE_MIN;
+                uns = sTot[dR * DK + lane] < -SAFE_SPAN || sTot[dR * DK + 64 + lane] < -SAFE_SPAN;
                 uns = __any(uns);
             }
             const int r = lane & 15, kg = lane >> 4;
@@ -732,7 +592,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                     if (i <= rw && valid(rw)) {
                         for (int cc = 0; cc < DK; ++cc) {
                             float w = 1.f;
-                            for (int j = i + 1; j <= rw; ++j) w *= __expf(g[grow(j) * DK + cc]);
+                            for (int j = i + 1; j <= rw; ++j) w *= __expf(clamp_g(g[grow(j) * DK + cc]));
                             const float ki = (float)k[grow(i) * DK + cc];
                             sa += (float)k[grow(rw) * DK + cc] * ki * w;
                             sp += (float)q[grow(rw) * DK + cc] * ki * w;
@@ -901,324 +761,6 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     }
 }
 
-// ================================================================ stage 2: chain
-template <typename T, typename TOut, int DK, int DV, int C, int DVS>
-struct ChainCfg {
-    static constexpr int PADT = sizeof(T) == 2 ? 8 : 4;
-    static constexpr int LDK = DK + PADT;
-    static constexpr int CK = cmax(C, Mma<T>::KSTEP);
-    static constexpr int LDC = CK + PADT;
-    static constexpr int NJ = DVS / 16;
-    static constexpr int NTW = (C / 16) * NJ;               // W / O tiles
-    static constexpr int NTS = (DK / 16) * NJ;              // state tiles
-    // each wave owns whole row tiles: RPW rows of W / O, SPW rows of the state
-    static constexpr int RPW = (C / 16 + 3) / 4, SPW = DK / 64;
-    // prefetch units of 16 bytes: Qt, Wk, Kb^T, P (input dtype), U slice, gam (fp32)
-    static constexpr int E16 = 16 / sizeof(T);
-    static constexpr int U_QT = C * DK / E16, U_WK = U_QT, U_KB = DK * C / E16, U_P = C * C / E16;
-    static constexpr int U_U = C * DVS / 4, U_G = DK / 4;
-    static constexpr int B1 = U_QT, B2 = B1 + U_WK, B3 = B2 + U_KB, B4 = B3 + U_P, B5 = B4 + U_U;
-    static constexpr int NU = B5 + U_G;
-    static constexpr int NUPT = (NU + 255) / 256;
-    // chunks in flight: as many 16-byte-unit register sets as ~160 VGPRs allow
-    static constexpr int DEPTH = (160 / (4 * NUPT)) < 1 ? 1 : ((160 / (4 * NUPT)) > 3 ? 3 : 160 / (4 * NUPT));
-    static constexpr size_t SZ_QT = size_t(C) * LDK * sizeof(T);
-    static constexpr size_t SZ_KBT = align16(size_t(DK) * LDC * sizeof(T));
-    static constexpr size_t SZ_P = align16(size_t(C) * LDC * sizeof(T));
-    static constexpr size_t SZ_U = size_t(C) * DVS * 4;
-    static constexpr size_t SZ_GAM = size_t(DK) * 4;
-    static constexpr size_t SZ_ST = size_t(DVS) * LDK * sizeof(T);
-    static constexpr size_t SZ_WT = align16(size_t(DVS) * LDC * sizeof(T));
-    static constexpr size_t SZ_O = align16(size_t(C) * DVS * sizeof(TOut));
-    static constexpr size_t OFF_WK = SZ_QT;
-    static constexpr size_t OFF_KBT = OFF_WK + SZ_QT;
-    static constexpr size_t OFF_P = OFF_KBT + SZ_KBT;
-    static constexpr size_t OFF_U = OFF_P + SZ_P;
-    static constexpr size_t OFF_GAM = OFF_U + SZ_U;
-    static constexpr size_t OFF_ST = OFF_GAM + SZ_GAM;
-    static constexpr size_t OFF_WT = OFF_ST + SZ_ST;
-    static constexpr size_t OFF_O = OFF_WT + SZ_WT;
-    // outputs are staged in LDS for 16-byte row stores when there is room
-    static constexpr bool STAGE_O = OFF_O + SZ_O <= LDS_LIMIT && (DVS * sizeof(TOut)) % 16 == 0;
-    static constexpr size_t TOTAL = STAGE_O ? OFF_O + SZ_O : OFF_O;
-    static constexpr bool FITS = TOTAL <= LDS_LIMIT && NUPT <= 40 && U_G <= 256;
-};
-
-template <typename T, typename TOut, int DK, int DV, int C, int DVS>
-__global__ __launch_bounds__(256) void chunk_chain_kernel(
-    const T* __restrict__ ws_qt, const T* __restrict__ ws_wk, const T* __restrict__ ws_kb,
-    const T* __restrict__ ws_p, const float* __restrict__ ws_u, const float* __restrict__ ws_gam,
-    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT,
-    int T_len, int H, int NC) {
-    typedef ChainCfg<T, TOut, DK, DV, C, DVS> Cfg;
-    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, CK = Cfg::CK, NJ = Cfg::NJ, E16 = Cfg::E16;
-    constexpr int NTW = Cfg::NTW, NTS = Cfg::NTS, KSTEP = Mma<T>::KSTEP;
-    constexpr int NSL = DV / DVS;
-
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
-    T* sQt = reinterpret_cast<T*>(smem);
-    T* sWk = reinterpret_cast<T*>(smem + Cfg::OFF_WK);
-    T* sKbT = reinterpret_cast<T*>(smem + Cfg::OFF_KBT);
-    T* sP = reinterpret_cast<T*>(smem + Cfg::OFF_P);
-    float* sU = reinterpret_cast<float*>(smem + Cfg::OFF_U);
-    float* sGam = reinterpret_cast<float*>(smem + Cfg::OFF_GAM);
-    T* sST = reinterpret_cast<T*>(smem + Cfg::OFF_ST);
-    T* sWT = reinterpret_cast<T*>(smem + Cfg::OFF_WT);
-    TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O);
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // Slices of one head share an XCD (workgroups are dealt to the 8 XCDs
-    // round-robin), so the per-chunk operands they all read come from one L2.
-    long bh;
-    int sl;
-    {
-        const long nwg = (long)gridDim.x, id = blockIdx.x;
-        if (nwg % (8 * NSL) == 0) {
-            const long xcd = id % 8, local = id / 8;
-            sl = (int)(local % NSL);
-            bh = (local / NSL) * 8 + xcd;
-        } else {
-            bh = id / NSL;
-            sl = (int)(id % NSL);
-        }
-    }
-    const int j0 = sl * DVS;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const long BH = (long)gridDim.x / NSL;       // workspace is chunk-major: (n, bh) -> n * BH + bh
-
-    // ---- register prefetch of one chunk's operands (16-byte units), one
-    // statically sized register array per operand
-    constexpr int PQ = (Cfg::U_QT + 255) / 256, PK = (Cfg::U_KB + 255) / 256, PP = (Cfg::U_P + 255) / 256,
-                  PU = (Cfg::U_U + 255) / 256;
-    constexpr int D = Cfg::DEPTH;
-    u32x4 preQ[D][PQ], preW[D][PQ], preK[D][PK], preP[D][PP], preU[D][PU], preG[D];
-#define KDA_CHAIN_PREFETCH(SL, CH)                                                                     \
-    {                                                                                              \
-        const long ch_ = (CH);                                                                     \
-        const u32x4* gq_ = reinterpret_cast<const u32x4*>(ws_qt + ch_ * (long)C * DK);             \
-        const u32x4* gw_ = reinterpret_cast<const u32x4*>(ws_wk + ch_ * (long)C * DK);             \
-        const u32x4* gk_ = reinterpret_cast<const u32x4*>(ws_kb + ch_ * (long)DK * C);             \
-        const u32x4* gp_ = reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)C * C);               \
-        const float* gu_ = ws_u + ch_ * (long)C * DV + j0;                                         \
-        _Pragma("unroll") for (int i = 0; i < PQ; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_QT) { preQ[SL][i] = gq_[u]; preW[SL][i] = gw_[u]; }                             \
-        }                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_KB) preK[SL][i] = gk_[u];                                                   \
-        }                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_P) preP[SL][i] = gp_[u];                                                    \
-        }                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < PU; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_U)                                                                      \
-                preU[SL][i] = *reinterpret_cast<const u32x4*>(gu_ + (long)(u / (DVS / 4)) * DV + 4 * (u % (DVS / 4))); \
-        }                                                                                          \
-        if (tid < Cfg::U_G) preG[SL] = reinterpret_cast<const u32x4*>(ws_gam + ch_ * (long)DK)[tid];  \
-    }
-#define KDA_CHAIN_COMMIT(SL)                                                                         \
-    {                                                                                              \
-        _Pragma("unroll") for (int i = 0; i < PQ; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_QT) {                                                                   \
-                const int e = u * E16;                                                             \
-                *reinterpret_cast<u32x4*>(sQt + (e / DK) * LDK + e % DK) = preQ[SL][i];                \
-                *reinterpret_cast<u32x4*>(sWk + (e / DK) * LDK + e % DK) = preW[SL][i];                \
-            }                                                                                      \
-        }                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < PK; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_KB) {                                                                   \
-                const int e = u * E16;                                                             \
-                *reinterpret_cast<u32x4*>(sKbT + (e / C) * LDC + e % C) = preK[SL][i];             \
-            }                                                                                      \
-        }                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < PP; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_P) {                                                                    \
-                const int e = u * E16;                                                             \
-                *reinterpret_cast<u32x4*>(sP + (e / C) * LDC + e % C) = preP[SL][i];                   \
-            }                                                                                      \
-        }                                                                                          \
-        _Pragma("unroll") for (int i = 0; i < PU; ++i) {                                           \
-            const int u = tid + 256 * i;                                                           \
-            if (u < Cfg::U_U) reinterpret_cast<u32x4*>(sU)[u] = preU[SL][i];                           \
-        }                                                                                          \
-        if (tid < Cfg::U_G) reinterpret_cast<u32x4*>(sGam)[tid] = preG[SL];                            \
-    }
-
-    // zero the contraction padding once (columns C..CK never receive data)
-    if constexpr (CK > C) {
-        for (int u = tid; u < (DK + C + DVS) * (CK - C); u += 256) {
-            const int row = u / (CK - C), i = C + u % (CK - C);
-            if (row < DK) sKbT[row * LDC + i] = from_f32<T>(0.f);
-            else if (row < DK + C) sP[(row - DK) * LDC + i] = from_f32<T>(0.f);
-            else sWT[(row - DK - C) * LDC + i] = from_f32<T>(0.f);
-        }
-    }
-
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (d < NC) KDA_CHAIN_PREFETCH(d, (long)d * BH + bh);
-
-    typedef typename Mma<T>::frag frag;
-    const int fr = lane & 15, fk = (lane >> 4) * Mma<T>::KPL;     // fragment row, k offset
-    floatx4 accS[Cfg::SPW][NJ];
-    static_for<Cfg::SPW>([&](auto SI) {
-        constexpr int si = SI;
-        const int ct = wave + 4 * si;
-        static_for<NJ>([&](auto JI) {
-            constexpr int jt = JI;
-            accS[si][jt] = zero4();
-            if (s0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = ct * 16 + 4 * (lane >> 4) + e, j = jt * 16 + (lane & 15);
-                    accS[si][jt][e] = s0[(bh * DK + c) * (long)DV + j0 + j];
-                }
-            }
-        });
-    });
-    // S^T as the B operand of the products with S: sST[j][c], 4 consecutive c per lane
-    auto write_state_operand = [&]() {
-        static_for<Cfg::SPW>([&](auto SI) {
-            constexpr int si = SI;
-            const int ct = wave + 4 * si;
-            static_for<NJ>([&](auto JI) {
-                constexpr int jt = JI;
-                const int j = jt * 16 + (lane & 15), c = ct * 16 + 4 * (lane >> 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sST[j * LDK + c + e] = from_f32<T>(accS[si][jt][e]);
-            });
-        });
-    };
-    write_state_operand();
-
-    for (int n0 = 0; n0 < NC; n0 += D) {
-      static_for<D>([&](auto DI) {
-        constexpr int d = DI;
-        const int n = n0 + d;
-        if (n >= NC) return;
-        KDA_CHAIN_COMMIT(d);                                        // chunk n operands -> LDS
-        if (n + D < NC) KDA_CHAIN_PREFETCH(d, (long)(n + D) * BH + bh);   // in flight for D chunks
-        __syncthreads();
-
-        // ---- W = U - Wk S (to LDS, transposed) and the state part of O;
-        //      the Wk and Qt fragments are shared by all value-column tiles
-        floatx4 accO[Cfg::RPW][NJ];
-        static_for<Cfg::RPW>([&](auto RI) {
-            constexpr int ri = RI;
-            const int R = wave + 4 * ri;
-            if (R < C / 16) {
-                floatx4 wk[NJ];
-                static_for<NJ>([&](auto JI) { wk[JI] = zero4(); accO[ri][JI] = zero4(); });
-                for (int k0 = 0; k0 < DK; k0 += KSTEP) {
-                    const frag fw = *reinterpret_cast<const frag*>(sWk + (R * 16 + fr) * LDK + k0 + fk);
-                    const frag fq = *reinterpret_cast<const frag*>(sQt + (R * 16 + fr) * LDK + k0 + fk);
-                    static_for<NJ>([&](auto JI) {
-                        constexpr int J = JI;
-                        const frag fb = *reinterpret_cast<const frag*>(sST + (J * 16 + fr) * LDK + k0 + fk);
-                        wk[J] = Mma<T>::mma(fw, fb, wk[J]);
-                        accO[ri][J] = Mma<T>::mma(fq, fb, accO[ri][J]);
-                    });
-                }
-                static_for<NJ>([&](auto JI) {
-                    constexpr int J = JI;
-                    const int j = J * 16 + (lane & 15), r = R * 16 + 4 * (lane >> 4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sWT[j * LDC + r + e] = from_f32<T>(sU[(r + e) * DVS + j] - wk[J][e]);
-                });
-            }
-        });
-        __syncthreads();
-
-        // ---- O += P W ; S = gam * S + Kb^T W
-        static_for<Cfg::RPW>([&](auto RI) {
-            constexpr int ri = RI;
-            const int R = wave + 4 * ri;
-            if (R < C / 16) {
-                const int K = ((16 * (R + 1) + KSTEP - 1) / KSTEP) * KSTEP;
-                for (int k0 = 0; k0 < K; k0 += KSTEP) {
-                    const frag fp = *reinterpret_cast<const frag*>(sP + (R * 16 + fr) * LDC + k0 + fk);
-                    static_for<NJ>([&](auto JI) {
-                        constexpr int J = JI;
-                        const frag fb = *reinterpret_cast<const frag*>(sWT + (J * 16 + fr) * LDC + k0 + fk);
-                        accO[ri][J] = Mma<T>::mma(fp, fb, accO[ri][J]);
-                    });
-                }
-                static_for<NJ>([&](auto JI) {
-                    constexpr int J = JI;
-                    const int j = J * 16 + (lane & 15);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = R * 16 + 4 * (lane >> 4) + e;
-                        if constexpr (Cfg::STAGE_O) {
-                            sO[r * DVS + j] = from_f32<TOut>(accO[ri][J][e]);
-                        } else {
-                            const int tt = n * C + r;
-                            if (tt < T_len) o[(((long)b * T_len + tt) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[ri][J][e]);
-                        }
-                    }
-                });
-            }
-        });
-        static_for<Cfg::SPW>([&](auto SI) {
-            constexpr int si = SI;
-            const int ct = wave + 4 * si;
-            float gm[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gm[e] = sGam[ct * 16 + 4 * (lane >> 4) + e];
-            static_for<NJ>([&](auto JI) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) accS[si][JI][e] *= gm[e];
-            });
-            for (int k0 = 0; k0 < CK; k0 += KSTEP) {
-                const frag fa = *reinterpret_cast<const frag*>(sKbT + (ct * 16 + fr) * LDC + k0 + fk);
-                static_for<NJ>([&](auto JI) {
-                    constexpr int J = JI;
-                    const frag fb = *reinterpret_cast<const frag*>(sWT + (J * 16 + fr) * LDC + k0 + fk);
-                    accS[si][J] = Mma<T>::mma(fa, fb, accS[si][J]);
-                });
-            }
-        });
-        __syncthreads();
-        if constexpr (Cfg::STAGE_O) {
-            constexpr int EO = 16 / sizeof(TOut);
-            constexpr int NUO = C * DVS / EO;
-            for (int u = tid; u < NUO; u += 256) {
-                const int r = (u * EO) / DVS, jj = (u * EO) % DVS;
-                const int tt = n * C + r;
-                if (tt < T_len)
-                    *reinterpret_cast<uint4*>(o + (((long)b * T_len + tt) * H + h) * DV + j0 + jj) =
-                        *reinterpret_cast<const uint4*>(sO + r * DVS + jj);
-            }
-        }
-        write_state_operand();
-      });
-    }
-
-    if (sT) {
-        static_for<Cfg::SPW>([&](auto SI) {
-            constexpr int si = SI;
-            const int ct = wave + 4 * si;
-            static_for<NJ>([&](auto JI) {
-                constexpr int jt = JI;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = ct * 16 + 4 * (lane >> 4) + e, j = jt * 16 + (lane & 15);
-                    sT[(bh * DK + c) * (long)DV + j0 + j] = accS[si][jt][e];
-                }
-            });
-        });
-    }
-}
-
-#undef KDA_CHAIN_PREFETCH
-#undef KDA_CHAIN_COMMIT
-
 // ================================================================ host side
 static inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -1255,52 +797,6 @@ static hipError_t launch_intra(const ChunkArgs& a) {
                            (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
         return hipGetLastError();
     }
-}
-
-template <typename T, typename TOut, int DK, int DV, int C, int DVS>
-static hipError_t launch_chain_dvs(const ChunkArgs& a) {
-    typedef ChainCfg<T, TOut, DK, DV, C, DVS> Cfg;
-    if constexpr (!Cfg::FITS || DVS > DV) {
-        return hipErrorInvalidValue;
-    } else {
-        const int NC = (a.T + C - 1) / C;
-        const long nwg = (long)a.B * a.H * (DV / DVS);
-        if (nwg == 0) return hipSuccess;
-        const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, sizeof(T) == 2, C);
-        char* ws = (char*)a.ws;
-        hipLaunchKernelGGL((chunk_chain_kernel<T, TOut, DK, DV, C, DVS>), dim3((unsigned)nwg), dim3(256), 0,
-                           a.stream, (const T*)(ws + w.qt), (const T*)(ws + w.wk), (const T*)(ws + w.kb),
-                           (const T*)(ws + w.p), (const float*)(ws + w.u), (const float*)(ws + w.gam),
-                           a.s0, (TOut*)a.o, a.sT, a.T, a.H, NC);
-        return hipGetLastError();
-    }
-}
-
-template <typename T, typename TOut, int DK, int DV, int C, int DVS>
-static constexpr bool chain_fits() { return DVS <= DV && ChainCfg<T, TOut, DK, DV, C, DVS>::FITS; }
-
-// Value-column slice width: enough workgroups to cover the chip (>= 256 when
-// possible), as wide as possible otherwise, and within the LDS budget.
-template <typename T, typename TOut, int DK, int DV, int C>
-static int pick_dvs(long bh) {
-    int dvs = 16;
-    const int cands[3] = {64, 32, 16};
-    const bool fits[3] = {chain_fits<T, TOut, DK, DV, C, 64>(), chain_fits<T, TOut, DK, DV, C, 32>(),
-                          chain_fits<T, TOut, DK, DV, C, 16>()};
-    for (int i = 0; i < 3; ++i) {
-        if (!fits[i]) continue;
-        dvs = cands[i];
-        if (bh * (DV / cands[i]) >= 256) break;
-    }
-    return dvs;
-}
-
-template <typename T, typename TOut, int DK, int DV, int C>
-static hipError_t launch_chain(const ChunkArgs& a) {
-    const int dvs = pick_dvs<T, TOut, DK, DV, C>((long)a.B * a.H);
-    if (dvs == 64) return launch_chain_dvs<T, TOut, DK, DV, C, 64>(a);
-    if (dvs == 32) return launch_chain_dvs<T, TOut, DK, DV, C, 32>(a);
-    return launch_chain_dvs<T, TOut, DK, DV, C, 16>(a);
 }
 
 template <typename T, int DK, int DV, int C>
@@ -1359,23 +855,8 @@ hipError_t run_chunk_intra(const ChunkArgs& a) {
     return a.in_bf16 ? intra_dims<bf16>(a) : intra_dims<float>(a);
 }
 
-template <typename T, typename TOut, int DK, int DV>
-static hipError_t chain_c(const ChunkArgs& a) {
-    switch (a.C) {
-        case 16: return launch_chain<T, TOut, DK, DV, 16>(a);
-        case 32: return launch_chain<T, TOut, DK, DV, 32>(a);
-        case 64: return launch_chain<T, TOut, DK, DV, 64>(a);
-        default: return launch_chain<T, TOut, DK, DV, 128>(a);
-    }
-}
-template <typename T, typename TOut>
-static hipError_t chain_dims(const ChunkArgs& a) {
-    if (a.dk == 64) return a.dv == 64 ? chain_c<T, TOut, 64, 64>(a) : chain_c<T, TOut, 64, 128>(a);
-    return a.dv == 64 ? chain_c<T, TOut, 128, 64>(a) : chain_c<T, TOut, 128, 128>(a);
-}
 hipError_t run_chunk_chain(const ChunkArgs& a) {
-    if (a.in_bf16) return a.out_bf16 ? chain_dims<bf16, bf16>(a) : chain_dims<bf16, float>(a);
-    return a.out_bf16 ? chain_dims<float, bf16>(a) : chain_dims<float, float>(a);
+    return a.in_bf16 ? run_chunk_chain_bf16(a) : run_chunk_chain_f32(a);
 }
 
 }  // namespace kda
