@@ -1,0 +1,263 @@
+// kda_chunk_chain64.hip -- stage 2 of the chunkwise forward for the hot
+// configuration (bf16 inputs, C = 64, dk = 128): the sequential state recurrence
+// across chunks and the outputs, reading the workspace that
+// chunk_intra64_kernel writes in MFMA fragment order.
+//
+// Per chunk (the chunkwise form of kda_chunk.h):
+//   W = U - Wk S,   O = Qt S + P W,   S <- Diag(gam) S + Kb^T W
+// One workgroup of 8 waves per (b, h, slice of DVS value columns).  Every
+// per-chunk operand is an MFMA A operand or the initial value of an
+// accumulator, and the workspace stores each wave's share as whole 16-byte
+// lanes, so the operands go from memory straight into registers (DEPTH chunks in
+// flight) and never through LDS.  Only S^T and W^T, the B operands that every
+// wave needs, are exchanged through LDS.
+//   waves 0-3 ("W waves"): row tile R = wave of W = U - Wk S
+//   waves 4-7 ("O waves"): row tile R = wave - 4 of O = Qt S + P W
+//   all waves           : state rows 16*wave .. +15:  S <- gam S + Kb^T W
+// Two barriers per chunk: S^T ready -> (W, Qt S) -> W^T ready -> (P W, S update).
+#include "kda_chunk.h"
+
+namespace kda {
+
+// Workspace of this configuration, per chunk unit (chunk-major, as for every layout):
+//   Qt, Wk [4 row tiles][4 k-steps][64 lanes][8 bf16]  lane l: row 16R + l%16, channels 32u + 8(l/16) + 0..7
+//   Kb^T   [8 channel tiles][2 k-steps][64][8 bf16]     lane l: channel 16c + l%16, tokens 32u + 8(l/16) + 0..7
+//   P      [4 row tiles][2 k-steps][64][8 bf16]         (row tiles 0, 1 at k-step 1 lie above the diagonal:
+//                                                        never written, never read)
+//   U      [4 row tiles][DV/16 column tiles][64][4] fp32  lane l, element e: row 16R + 4(l/16) + e, column 16J + l%16
+//   gam    [DK] fp32
+template <typename TOut, int DV, int DVS>
+struct Chain64Cfg {
+    static constexpr int C = 64, DK = 128, NT = 512, NJ = DVS / 16, NSL = DV / DVS;
+    static constexpr int LDK = DK + 8, LDC = C + 8;   // padded bf16 rows of S^T, W^T
+    static constexpr int DEPTH = 4;                    // chunks in flight
+    static constexpr size_t OFF_ST = 0;
+    static constexpr size_t OFF_WT = OFF_ST + size_t(DVS) * LDK * 2;
+    static constexpr size_t OFF_O = OFF_WT + size_t(DVS) * LDC * 2;               // per O wave: [16][DVS]
+    static constexpr size_t TOTAL = OFF_O + size_t(4) * 16 * DVS * sizeof(TOut);
+    static_assert(NJ >= 1 && NJ <= 2 && DV % DVS == 0, "slice width 16 or 32");
+    static_assert((16 * DVS * sizeof(TOut)) % 16 == 0, "output staging rows");
+};
+
+template <typename TOut, int DV, int DVS>
+__global__ __launch_bounds__(512) void chunk_chain64_kernel(
+    const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
+    const bf16* __restrict__ ws_p, const float* __restrict__ ws_u, const float* __restrict__ ws_gam,
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, int T_len, int H, int NC) {
+    typedef Chain64Cfg<TOut, DV, DVS> Cfg;
+    constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, NSL = Cfg::NSL, LDK = Cfg::LDK, LDC = Cfg::LDC;
+    constexpr int D = Cfg::DEPTH;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
+    bf16* sWT = reinterpret_cast<bf16*>(smem + Cfg::OFF_WT);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Slices of one head share an XCD (workgroups are dealt to the 8 XCDs
+    // round-robin), so the per-chunk operands they all read come from one L2.
+    long bh;
+    int sl;
+    {
+        const long nwg = (long)gridDim.x, id = blockIdx.x;
+        if (nwg % (8 * NSL) == 0) {
+            const long xcd = id % 8, local = id / 8;
+            sl = (int)(local % NSL);
+            bh = (local / NSL) * 8 + xcd;
+        } else {
+            bh = id / NSL;
+            sl = (int)(id % NSL);
+        }
+    }
+    const int j0 = sl * DVS;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const long BH = (long)gridDim.x / NSL;       // chunk-major workspace: (n, bh) -> n * BH + bh
+
+    const bool wW = wave < 4;                    // uniform per wave
+    const int R = wave & 3, ct = wave;
+    const int fr = lane & 15, fk = 8 * (lane >> 4);
+    TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O) + R * 16 * DVS;
+
+    // ---- operand registers, D chunks in flight
+    u32x4 fA[D][4];      // Wk (W waves) or Qt (O waves), row tile R, 4 k-steps
+    u32x4 fX[D][2];      // U tiles of this slice (W waves) or P k-steps (O waves)
+    u32x4 fK[D][2];      // Kb^T channel tile ct, 2 k-steps
+    u32x4 fG[D];         // gam of this lane's 4 state rows
+    // first half: what phase 1 consumes; second half: what phase 2 consumes
+#define KDA_C64_PREFETCH_1(SL, CH)                                                                  \
+    {                                                                                               \
+        const long ch_ = (CH);                                                                      \
+        const u32x4* a_ = reinterpret_cast<const u32x4*>((wW ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
+                          + R * 4 * 64 + lane;                                                      \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
+        if (wW) {                                                                                   \
+            const u32x4* u_ = reinterpret_cast<const u32x4*>(ws_u + ch_ * (long)(C * DV))           \
+                              + (R * (DV / 16) + sl * NJ) * 64 + lane;                              \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j) fX[SL][j] = u_[j * 64];                 \
+        }                                                                                           \
+    }
+#define KDA_C64_PREFETCH_2(SL, CH)                                                                  \
+    {                                                                                               \
+        const long ch_ = (CH);                                                                      \
+        if (!wW) {                                                                                  \
+            const u32x4* p_ = reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
+            fX[SL][0] = p_[0];                                                                      \
+            if (R >= 2) fX[SL][1] = p_[64];                                                         \
+        }                                                                                           \
+        const u32x4* k_ = reinterpret_cast<const u32x4*>(ws_kb + ch_ * (long)(DK * C)) + ct * 2 * 64 + lane; \
+        fK[SL][0] = k_[0];                                                                          \
+        fK[SL][1] = k_[64];                                                                         \
+        fG[SL] = *reinterpret_cast<const u32x4*>(ws_gam + ch_ * (long)DK + ct * 16 + 4 * (lane >> 4)); \
+    }
+
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < NC) {
+            KDA_C64_PREFETCH_1(d, (long)d * BH + bh);
+            KDA_C64_PREFETCH_2(d, (long)d * BH + bh);
+        }
+
+    // ---- state rows 16*ct + 4(l/16) + e, columns j0 + 16 jt + l%16, fp32 in accumulators
+    floatx4 accS[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+        accS[jt] = zero4();
+        if (s0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                accS[jt][e] = s0[(bh * DK + ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr];
+        }
+    }
+    // S^T as the B operand of Qt S and Wk S: sST[j][c], 4 consecutive c per lane
+    auto write_state_operand = [&]() {
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = (bf16)accS[jt][e];
+            *reinterpret_cast<bf16x4*>(sST + (jt * 16 + fr) * LDK + ct * 16 + 4 * (lane >> 4)) = v4;
+        }
+    };
+    write_state_operand();
+
+    for (int n0 = 0; n0 < NC; n0 += D) {
+      static_for<D>([&](auto DI) {
+        constexpr int d = DI;
+        const int n = n0 + d;
+        if (n >= NC) return;
+        __syncthreads();                                            // S^T of chunk n's start state
+
+        // ---- phase 1: W waves W = U - Wk S (to LDS as W^T); O waves O = Qt S
+        floatx4 acc[NJ];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) acc[jt] = zero4();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bf16x8 fa = __builtin_bit_cast(bf16x8, fA[d][u]);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) {
+                const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sST + (jt * 16 + fr) * LDK + u * 32 + fk);
+                acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[jt], 0, 0, 0);
+            }
+        }
+        if (wW) {
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) {
+                const floatx4 uu = __builtin_bit_cast(floatx4, fX[d][jt]);
+                bf16x4 w4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w4[e] = (bf16)(uu[e] - acc[jt][e]);
+                *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
+            }
+        }
+        if (n + D < NC) KDA_C64_PREFETCH_1(d, (long)(n + D) * BH + bh);
+        __syncthreads();                                            // W^T complete
+
+        // ---- phase 2: O waves O += P W (stored); all waves S = gam S + Kb^T W
+        if (!wW) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (u == 1 && R < 2) break;                         // P is lower triangular
+                const bf16x8 fp = __builtin_bit_cast(bf16x8, fX[d][u]);
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt) {
+                    const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sWT + (jt * 16 + fr) * LDC + u * 32 + fk);
+                    acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp, fb, acc[jt], 0, 0, 0);
+                }
+            }
+            // this wave's 16 x DVS output tile, through its own LDS rows, as 16-byte row pieces
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sO[(4 * (lane >> 4) + e) * DVS + jt * 16 + fr] = from_f32<TOut>(acc[jt][e]);
+            constexpr int EO = 16 / sizeof(TOut), PPR = DVS / EO, NUO = 16 * PPR;   // pieces per row, per tile
+#pragma unroll
+            for (int u = lane; u < NUO; u += 64) {
+                const int r = u / PPR, jj = (u % PPR) * EO;
+                const int tt = n * C + R * 16 + r;
+                if (tt < T_len)
+                    *reinterpret_cast<u32x4*>(o + (((long)b * T_len + tt) * H + h) * DV + j0 + jj) =
+                        *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
+            }
+        }
+        {
+            const floatx4 gm = __builtin_bit_cast(floatx4, fG[d]);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accS[jt][e] *= gm[e];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 fa = __builtin_bit_cast(bf16x8, fK[d][u]);
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt) {
+                    const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sWT + (jt * 16 + fr) * LDC + u * 32 + fk);
+                    accS[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, accS[jt], 0, 0, 0);
+                }
+            }
+        }
+        write_state_operand();                                      // read only after the next barrier
+        if (n + D < NC) KDA_C64_PREFETCH_2(d, (long)(n + D) * BH + bh);
+      });
+    }
+
+    if (sT) {
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sT[(bh * DK + ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr] = accS[jt][e];
+    }
+}
+
+#undef KDA_C64_PREFETCH_1
+#undef KDA_C64_PREFETCH_2
+
+template <typename TOut, int DV, int DVS>
+static hipError_t launch_chain64_dvs(const ChunkArgs& a) {
+    constexpr int C = 64, DK = 128;
+    const int NC = (a.T + C - 1) / C;
+    const long nwg = (long)a.B * a.H * (DV / DVS);
+    if (nwg == 0) return hipSuccess;
+    const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, true, C);
+    char* ws = (char*)a.ws;
+    hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
+                       (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
+                       (const bf16*)(ws + w.p), (const float*)(ws + w.u), (const float*)(ws + w.gam),
+                       a.s0, (TOut*)a.o, a.sT, a.T, a.H, NC);
+    return hipGetLastError();
+}
+
+// Slice width: 32 value columns when that gives at least 256 workgroups, else 16.
+template <typename TOut, int DV>
+static hipError_t launch_chain64(const ChunkArgs& a) {
+    const long bh = (long)a.B * a.H;
+    if (bh * (DV / 32) >= 256) return launch_chain64_dvs<TOut, DV, 32>(a);
+    return launch_chain64_dvs<TOut, DV, 16>(a);
+}
+
+hipError_t run_chunk_chain64(const ChunkArgs& a) {
+    if (a.dv == 64) return a.out_bf16 ? launch_chain64<bf16, 64>(a) : launch_chain64<float, 64>(a);
+    return a.out_bf16 ? launch_chain64<bf16, 128>(a) : launch_chain64<float, 128>(a);
+}
+
+}  // namespace kda

@@ -340,7 +340,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
 }
 
 // ================================================================ stage 1, bf16 / C = 64 / dk = 128
-// The hot configuration.  Same workspace contents as chunk_intra_kernel.
+// The hot configuration.  Same workspace contents as chunk_intra_kernel, stored in
+// the MFMA fragment order that chunk_chain64_kernel reads (kda_chunk_chain64.hip).
 //  - Inside each 16-token block the inclusive prefix sum L of the (floored)
 //    log-gate is formed in registers with DPP row shifts: the 16 tokens of a
 //    block sit in the 16 lanes of one DPP row.  E = e^{L} and F = e^{tot - L}
@@ -382,17 +383,19 @@ struct Intra64Cfg {
     static constexpr size_t OFF_A = 0;
     static constexpr size_t OFF_VT = 0;
     static constexpr size_t OFF_TB = size_t(C) * LDA * 4;
+    static constexpr int LDP = C + 8;                // bf16 rows of the P / Kb^T / Wk staging
+    static constexpr int LDW = DK + 8;
     static constexpr size_t OFF_PB = OFF_TB + size_t(C) * LDT * 2;      // P staging, then the T temp
-    static constexpr size_t SZ_W = OFF_PB + size_t(C) * C * 2;
+    static constexpr size_t SZ_W = OFF_PB + size_t(C) * LDP * 2;
     static constexpr size_t OFF_KT = SZ_S > SZ_W ? SZ_S : SZ_W;         // (e^G k)^T [DK][LDT]
-    static constexpr size_t OFF_KB = OFF_KT + size_t(DK) * LDT * 2;     // Kb^T staging [DK][C]
-    static constexpr size_t OFF_TOT = OFF_KB + size_t(DK) * C * 2;
+    static constexpr size_t OFF_KB = OFF_KT + size_t(DK) * LDT * 2;     // Kb^T staging [DK][LDP]
+    static constexpr size_t OFF_TOT = OFF_KB + size_t(DK) * LDP * 2;
     static constexpr size_t OFF_BETA = OFF_TOT + size_t(NB) * DK * 4;
     static constexpr size_t TOTAL = OFF_BETA + size_t(C) * 4;
     static_assert(size_t(DV) * LDT * 2 <= size_t(C) * LDA * 4, "V^T fits over M");
-    static_assert(size_t(C / 2) * (C / 2 + 4) * 4 <= size_t(C) * C * 2, "T temp fits the P staging");
+    static_assert(size_t(C / 2) * (C / 2 + 4) * 4 <= size_t(C) * LDP * 2, "T temp fits the P staging");
     static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
-    static_assert(size_t(C) * DV * 4 + size_t(C) * DK * 2 <= TOTAL, "U / Wk staging");
+    static_assert(size_t(C) * LDW * 2 <= OFF_KT, "Wk staging");
     static_assert(NITV >= 1 && (C * DV / 8) % NT == 0, "v unit mapping");
 };
 
@@ -526,9 +529,10 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                 const float eb = RB > 0 ? __expf(o1[m]) : 1.f, er = RB < 3 ? __expf(o2[m]) : 1.f;
                 o1[m] = qr[m] * eb;
                 sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb);
-                sKbT[(c + m) * C + t] = (bf16)(kf[m] * er);
+                sKbT[(c + m) * Cfg::LDP + t] = (bf16)(kf[m] * er);
             }
-            Vec8<bf16>::store(gQt + t * DK + c, o1);
+            // fragment order: unit (row tile R, k-step c/32), lane = row%16 + 16 * ((c%32)/8)
+            Vec8<bf16>::store(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
         });
         if (p == 0 && tid < DK) {
             float lg = 0.f;
@@ -538,9 +542,12 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         }
         __syncthreads();
 
-        if (p == 1) {                                  // Kb^T complete: 16-byte rows to the workspace
-            for (int u = tid; u < DK * C / 8; u += NT)
-                reinterpret_cast<uint4*>(gKb)[u] = reinterpret_cast<const uint4*>(sKbT)[u];
+        if (p == 1) {                                  // Kb^T complete: to the workspace in fragment order
+            for (int u = tid; u < DK * C / 8; u += NT) {
+                const int ctile = u >> 7, ks = (u >> 6) & 1, lf = u & 63;
+                reinterpret_cast<u32x4*>(gKb)[u] = *reinterpret_cast<const u32x4*>(
+                    sKbT + (ctile * 16 + (lf & 15)) * Cfg::LDP + ks * 32 + 8 * (lf >> 4));
+            }
         }
         // A and P over this channel half (K = 64: two MFMA steps)
         if (wave < 6) {
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         const int bc = bi < 3 ? bi + 1 : (bi < 5 ? bi - 1 : 3);
         const int r = br * 16 + (e >> 4), i = bc * 16 + (e & 15);
         sA[r * LDA + i] = 0.f;
-        sPb[r * C + i] = (bf16)0.f;
+        sPb[r * Cfg::LDP + i] = (bf16)0.f;
     }
     if (wave < 6) {
         const int np = (wave == 0 || wave == 3) ? 1 : 2;
@@ -636,14 +643,20 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                 float av = accA[s][e], pv = accP[s][e];
                 if (PR == PI) { if (i >= r) av = 0.f; if (i > r) pv = 0.f; }
                 sA[r * LDA + i] = sBeta[r] * av;
-                sPb[r * C + i] = (bf16)pv;
+                sPb[r * Cfg::LDP + i] = (bf16)pv;
             }
         }
     }
     __syncthreads();
     {
         uint4* gP = reinterpret_cast<uint4*>(ws_p + ch * (long)C * C);
-        if (tid < C * C / 8) gP[tid] = reinterpret_cast<const uint4*>(sPb)[tid];
+        // fragment order; the two blocks above the diagonal (row tiles 0, 1 at k-step 1) are not stored
+        if (tid < 6 * 64) {
+            const int bi = tid >> 6, lf = tid & 63;
+            const int Rt = bi < 2 ? bi : 2 + (bi - 2) / 2, ks = bi < 2 ? 0 : (bi - 2) % 2;
+            gP[(Rt * 2 + ks) * 64 + lf] = *reinterpret_cast<const uint4*>(
+                sPb + (Rt * 16 + (lf & 15)) * Cfg::LDP + ks * 32 + 8 * (lf >> 4));
+        }
     }
 
     // ---------------------------------------------------------------- a4: T = (I + M)^-1
@@ -732,32 +745,35 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                 }
             }
         }
+        // U goes out straight from the accumulators: tile (row tile, column tile) as [64 lanes][4]
+#pragma unroll
+        for (int sct = 0; sct < NTPW; ++sct) {
+            const int ct = wave + NW * sct;
+            if (ct < NUT) {
+#pragma unroll
+                for (int R2 = 0; R2 < 4; ++R2)
+                    reinterpret_cast<floatx4*>(gU)[(R2 * (DV / 16) + ct) * 64 + lane] = acc[sct][R2];
+            }
+        }
         __syncthreads();                               // operands read by every wave: staging may overwrite them
-        {
-            float* sUo = reinterpret_cast<float*>(smem);
-            bf16* sWo = reinterpret_cast<bf16*>(smem + size_t(C) * DV * 4);
+        bf16* sWo = reinterpret_cast<bf16*>(smem);
 #pragma unroll
-            for (int sct = 0; sct < NTPW; ++sct) {
-                const int ct = wave + NW * sct;
-                if (ct >= NCT) continue;
-                const bool isU = ct < NUT;
-                const int col = (isU ? ct : ct - NUT) * 16 + (lane & 15);
+        for (int sct = 0; sct < NTPW; ++sct) {
+            const int ct = wave + NW * sct;
+            if (ct < NUT || ct >= NCT) continue;
+            const int col = (ct - NUT) * 16 + (lane & 15);
 #pragma unroll
-                for (int R2 = 0; R2 < 4; ++R2) {
+            for (int R2 = 0; R2 < 4; ++R2) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = R2 * 16 + 4 * (lane >> 4) + e;
-                        if (isU) sUo[row * DV + col] = acc[sct][R2][e];
-                        else sWo[row * DK + col] = (bf16)acc[sct][R2][e];
-                    }
-                }
+                for (int e = 0; e < 4; ++e) sWo[(R2 * 16 + 4 * (lane >> 4) + e) * Cfg::LDW + col] = (bf16)acc[sct][R2][e];
             }
         }
         __syncthreads();
-        const uint4* sUo = reinterpret_cast<const uint4*>(smem);
-        const uint4* sWo = reinterpret_cast<const uint4*>(smem + size_t(C) * DV * 4);
-        for (int u = tid; u < C * DV / 4; u += NT) reinterpret_cast<uint4*>(gU)[u] = sUo[u];
-        for (int u = tid; u < C * DK / 8; u += NT) reinterpret_cast<uint4*>(gW)[u] = sWo[u];
+        for (int u = tid; u < C * DK / 8; u += NT) {  // Wk in fragment order
+            const int Rt = u >> 8, ks = (u >> 6) & 3, lf = u & 63;
+            reinterpret_cast<u32x4*>(gW)[u] = *reinterpret_cast<const u32x4*>(
+                sWo + (Rt * 16 + (lf & 15)) * Cfg::LDW + ks * 32 + 8 * (lf >> 4));
+        }
     }
 }
 
@@ -834,10 +850,8 @@ static hipError_t launch_intra64(const ChunkArgs& a) {
 
 template <typename T, int DK, int DV>
 static hipError_t intra_c(const ChunkArgs& a) {
-    if constexpr (sizeof(T) == 2) {
-        if constexpr (DK == 128) {
-            if (a.C == 64 && !a.generic) return launch_intra64<DV>(a);
-        }
+    if constexpr (sizeof(T) == 2 && DK == 128) {
+        if (hot_layout(a)) return launch_intra64<DV>(a);
     }
     switch (a.C) {
         case 16: return launch_intra<T, DK, DV, 16>(a);
@@ -856,6 +870,7 @@ hipError_t run_chunk_intra(const ChunkArgs& a) {
 }
 
 hipError_t run_chunk_chain(const ChunkArgs& a) {
+    if (hot_layout(a)) return run_chunk_chain64(a);
     return a.in_bf16 ? run_chunk_chain_bf16(a) : run_chunk_chain_f32(a);
 }
 

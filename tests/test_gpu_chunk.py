@@ -42,7 +42,10 @@ def check(d, o, S, tol, heads=None, cols=None, tag=""):
         og, Sg = og[..., cols], Sg[..., cols]
     eo = assert_close(f"{tag} o", og, o_ref, tol)
     es = assert_close(f"{tag} S", Sg, S_ref, tol)
-    _say(f"  {tag}: max err o {eo:.2e}  S {es:.2e}")
+    r_o, r_s = to64(o_ref), to64(S_ref)
+    so = max(1.0, float(np.abs(r_o).max())) if r_o.size else 1.0
+    ss = max(1.0, float(np.abs(r_s).max())) if r_s.size else 1.0
+    _say(f"  {tag}: max err o {eo:.2e} (scale {so:.3g})  S {es:.2e} (scale {ss:.3g})")
     return eo, es
 
 
@@ -176,10 +179,11 @@ def test_stages_match_fused_call():
 
 
 # ----------------------------------------------------------------- full-size workloads
-@pytest.mark.parametrize("gates", ["tiny", "none", "scalar"])
+@pytest.mark.parametrize("gates", [None, "tiny", "none", "scalar"], ids=["channel", "tiny", "none", "scalar"])
 def test_mid_workload(gates):
-    """B=4 H=16 T=8192 d=128 C=64 bf16, three gate sweeps on the same q,k,v,beta;
-    the oracle checks 6 sampled heads over the whole sequence."""
+    """B=4 H=16 T=8192 d=128 C=64 bf16: the workload's own per-channel gates and
+    three gate sweeps on the same q,k,v,beta; the oracle checks 4 sampled heads
+    over the whole sequence."""
     w = inputs.WORKLOADS["mid"]
     _say(f"mid workload gates={gates}: generating")
     d = inputs.make_prefill(w, gates=gates)
