@@ -21,6 +21,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+CSRC = os.path.join(ROOT, "linear_attention_sequence_chunk_amd", "csrc")
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a
+# plain copy of known size); valid only while the kernel's sources are unchanged
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mid_prefill.txt")
+KERNEL_SOURCES = {
+    "chunk_intra64_kernel": ["kda_common.h", "kda_launch.h", "kda_chunk.h", "kda_chunk_intra.hip"],
+    "chunk_chain64_kernel": ["kda_common.h", "kda_launch.h", "kda_chunk.h", "kda_chunk_chain64.hip"],
+}
 
 
 def parse():
@@ -35,6 +43,33 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device copy (to scale FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def source_digest(names):
+    """sha256 over the kernel's source files, in order."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch (fetch + write) from the committed counter summary,
+    or None when there is none or the kernel's sources changed since."""
+    if kernel not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = source_digest(KERNEL_SOURCES[kernel])
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) < 2 or parts[0] != "traffic" or parts[1] != kernel:
+                continue
+            kv = dict(p.split("=", 1) for p in parts[2:] if "=" in p)
+            if kv.get("sha256") == digest:
+                return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def prefill_bytes_per_token_head(dk, dv, in_bytes, out_bytes):
@@ -99,12 +134,14 @@ def main():
     step_alg = intra_alg + chain_alg
     t_intra = sum(intra_ms) / K / 1e3
     t_chain = sum(chain_ms) / K / 1e3
-    dom = ("chunk_intra_kernel", intra_alg, t_intra) if t_intra >= t_chain else \
-          ("chunk_chain_kernel", chain_alg, t_chain)
+    hot = w.dtype == "bf16" and w.dk == 128 and w.C == 64
+    names = ("chunk_intra64_kernel", "chunk_chain64_kernel") if hot else ("chunk_intra_kernel", "chunk_chain_kernel")
+    dom = (names[0], intra_alg, t_intra) if t_intra >= t_chain else (names[1], chain_alg, t_chain)
     achieved = dom[1] / dom[2] / 1e9
     roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None}
+                "traffic": measured_traffic(dom[0]) if args.workload == "mid" else None,
+                "alg_bytes": dom[1]}
 
     out = {
         "metric": "KDA chunked-prefill tokens/s",
