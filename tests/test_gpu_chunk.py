@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import oracle
-from linear_attention_sequence_chunk_amd import ChunkPlan, chunk_fwd, inputs
+from linear_attention_sequence_chunk_amd import ChunkPlan, chunk_fwd, decode_step, inputs
 from tests.parity import TOL, assert_close, cuda, max_err, to64
 
 pytestmark = pytest.mark.gpu
@@ -203,3 +203,70 @@ def test_long_workload():
     o, S = run_gpu(d, w.C)
     _say("long workload: oracle on 4 heads")
     check(d, o, S, TOL[torch.bfloat16], heads=[0, 11, 22, 31], tag="long")
+
+
+def test_1m_token_workload():
+    """B=1 H=16 T=1,048,576 d=128 C=64 bf16 (recurring address keys, fast/slow
+    channel gates, S0 = 0).  (i) One call over the whole sequence equals, bitwise,
+    a call over [0, T-16384) followed by a call over the last 16384 tokens that
+    starts from the first call's final state.  (ii) The oracle follows 2 sampled
+    heads over all 1,048,576 tokens on 4 sampled value columns (columns of the
+    recurrence are independent), from inputs regenerated on the host."""
+    w = inputs.WORKLOADS["1m"]
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    dev = "cuda:0"
+    heads, cols = [3, 12], [0, 37, 90, 127]
+    q = torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    beta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    host = {n: [] for n in ("q", "k", "v", "g", "beta")}
+    piece = 1 << 16
+    for t0 in range(0, T, piece):
+        d = inputs.make_prefill(w, t0=t0, t1=t0 + piece)
+        for n, dst in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+            dst[:, t0:t0 + piece].copy_(d[n])
+            x = d[n][:, :, heads]
+            host[n].append(x[..., cols] if n == "v" else x)
+        if t0 % (1 << 18) == 0:
+            _say(f"1m workload: inputs {t0 + piece}/{T}")
+    host = {n: torch.cat(x, dim=1) for n, x in host.items()}
+
+    _say("1m workload: single call")
+    o, S = chunk_fwd(q, k, v, g, beta, None, chunk_size=w.C)
+    T1 = T - 16384
+    _say("1m workload: split call")
+    o1, S_mid = chunk_fwd(q[:, :T1], k[:, :T1], v[:, :T1], g[:, :T1], beta[:, :T1], None, chunk_size=w.C)
+    o2, S2 = chunk_fwd(q[:, T1:], k[:, T1:], v[:, T1:], g[:, T1:], beta[:, T1:], S_mid, chunk_size=w.C)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :T1], o1), "first part of the split call differs"
+    assert torch.equal(o[:, T1:], o2) and torch.equal(S, S2), "split call differs from the single call"
+
+    _say("1m workload: oracle on 2 heads x 4 columns, all tokens")
+    o_ref, S_ref = oracle.recurrent(host["q"], host["k"], host["v"], host["g"], host["beta"], None)
+    og = o[:, :, heads][..., cols].cpu()
+    Sg = S[:, heads][..., cols].cpu()
+    eo = assert_close("1m o", og, o_ref, TOL[torch.bfloat16])
+    es = assert_close("1m S", Sg, S_ref, TOL[torch.bfloat16])
+    _say(f"  1m: max err o {eo:.2e}  S {es:.2e}")
+
+
+def test_decode_steps_match_prefill():
+    """T consecutive kda_decode_step calls and one kda_chunk_fwd over the same
+    sequence reach the same outputs and state (both are also checked against
+    the oracle)."""
+    d = inputs.custom_prefill(31, 2, 96, 3, 128, 128, dtype=torch.bfloat16, s0_std=0.05)
+    dg = cuda(d)
+    o_c, S_c = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], dg["S0"], chunk_size=64)
+    S = dg["S0"].clone()
+    o_d = torch.empty_like(o_c)
+    for t in range(d["q"].shape[1]):
+        o_d[:, t] = decode_step(dg["q"][:, t].contiguous(), dg["k"][:, t].contiguous(),
+                                dg["v"][:, t].contiguous(), dg["g"][:, t].contiguous(),
+                                dg["beta"][:, t].contiguous(), S)
+    torch.cuda.synchronize()
+    check(d, o_d.cpu(), S.cpu(), TOL[torch.bfloat16], tag="decode x T")
+    check(d, o_c.cpu(), S_c.cpu(), TOL[torch.bfloat16], tag="prefill")
+    assert_close("decode vs prefill o", o_d.cpu(), o_c.cpu(), TOL[torch.bfloat16])
+    assert_close("decode vs prefill S", S.cpu(), S_c.cpu(), TOL[torch.bfloat16])
