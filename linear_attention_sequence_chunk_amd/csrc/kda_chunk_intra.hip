@@ -369,6 +369,28 @@ __device__ __forceinline__ float row_prefix_sum(float x) {
     return x;
 }
 
+// Writes the 8 bf16 of x to rows row0 .. row0+7 of one column of a row-major LDS
+// array (a transpose), element (m + rot) & 7 in the m-th store.  Lanes whose rows
+// sit a multiple of 32 banks apart get different even rotations, so each store
+// instruction spreads them over different banks.
+__device__ __forceinline__ void store_column8(bf16* base, int ld, int row0, int col, u32x4 x, int rot) {
+    u32x4 y = x;                                   // rotate the packed pairs left by rot / 2
+    y = (rot & 2) ? u32x4{y[1], y[2], y[3], y[0]} : y;
+    y = (rot & 4) ? u32x4{y[2], y[3], y[0], y[1]} : y;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const unsigned int pr = y[m >> 1];
+        const unsigned short hv = (unsigned short)((m & 1) ? (pr >> 16) : (pr & 0xFFFFu));
+        *reinterpret_cast<unsigned short*>(base + (row0 + ((m + rot) & 7)) * ld + col) = hv;
+    }
+}
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* x) {
+    bf16x8 b;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) b[m] = (bf16)x[m];
+    return __builtin_bit_cast(u32x4, b);
+}
+
 template <int DV>
 struct Intra64Cfg {
     static constexpr int C = 64, NB = 4, DK = 128, NT = 512, NW = 8, HALF = 64;
@@ -396,7 +418,7 @@ struct Intra64Cfg {
     static_assert(size_t(C / 2) * (C / 2 + 4) * 4 <= size_t(C) * LDP * 2, "T temp fits the P staging");
     static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
     static_assert(size_t(C) * LDW * 2 <= OFF_KT, "Wk staging");
-    static_assert(NITV >= 1 && (C * DV / 8) % NT == 0, "v unit mapping");
+    static_assert(NITV >= 1 && (C * DV / 8) % NT == 0 && (DV / 8) % 4 == 0, "v unit mapping");
 };
 
 template <int DV>
@@ -450,9 +472,16 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             ga[p] = zero4(); gb[p] = zero4();
         }
     }
+    // v unit mapping: each group of 64 units covers 16 tokens x 4 groups of 8 channels
+    auto vunit = [&](int it, int& tv, int& j) {
+        const int u = tid + NT * it, w = u >> 6, l = u & 63;
+        tv = (w & 3) * 16 + (l & 15);
+        j = 8 * ((w >> 2) * 4 + (l >> 4));
+    };
 #pragma unroll
     for (int it = 0; it < Cfg::NITV; ++it) {
-        const int u = tid + NT * it, tv = u / (DV / 8), j = 8 * (u % (DV / 8));
+        int tv, j;
+        vunit(it, tv, j);
         if (valid(tv)) vv[it] = *reinterpret_cast<const bf16x8*>(v + grow(tv) * DV + j);
         else {
 #pragma unroll
@@ -528,9 +557,11 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             for (int m = 0; m < 8; ++m) {
                 const float eb = RB > 0 ? __expf(o1[m]) : 1.f, er = RB < 3 ? __expf(o2[m]) : 1.f;
                 o1[m] = qr[m] * eb;
-                sKtT[(c + m) * LDT + t] = (bf16)(kr[m] * eb);
-                sKbT[(c + m) * Cfg::LDP + t] = (bf16)(kf[m] * er);
+                kr[m] *= eb;
+                kf[m] *= er;
             }
+            store_column8(sKtT, LDT, c, t, pack_bf16x8(kr), 2 * (lane >> 4));
+            store_column8(sKbT, Cfg::LDP, c, t, pack_bf16x8(kf), 2 * (lane >> 4));
             // fragment order: unit (row tile R, k-step c/32), lane = row%16 + 16 * ((c%32)/8)
             Vec8<bf16>::store(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
         });
@@ -713,9 +744,9 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     __syncthreads();                                   // M / T dead: V^T goes over it
 #pragma unroll
     for (int it = 0; it < Cfg::NITV; ++it) {
-        const int u = tid + NT * it, tv = u / (DV / 8), j = 8 * (u % (DV / 8));
-#pragma unroll
-        for (int m = 0; m < 8; ++m) sVt[(j + m) * LDT + tv] = vv[it][m];
+        int tv, j;
+        vunit(it, tv, j);
+        store_column8(sVt, LDT, j, tv, __builtin_bit_cast(u32x4, vv[it]), 2 * (lane >> 4));
     }
     __syncthreads();
     {
