@@ -188,10 +188,9 @@ constexpr bool chain_fits() { return DVS <= DV && ChainCfg<T, TOut, DK, DV, C, D
 hipError_t run_chunk_chain_bf16(const ChunkArgs& a);
 hipError_t run_chunk_chain_f32(const ChunkArgs& a);
 
-// The hot configuration (bf16 inputs, C = 64, dk = 128) has its own pair of
-// kernels, chunk_intra64_kernel and chunk_chain64_kernel, and its own order of
-// the workspace contents (MFMA fragment order); both stages decide with this.
-inline bool hot_layout(const ChunkArgs& a) { return a.in_bf16 && a.dk == 128 && a.C == 64 && !a.generic; }
+// The hot configuration has its own pair of kernels, chunk_intra64_kernel and
+// chunk_chain64_kernel, and its own workspace format; both stages decide with this.
+inline bool hot_layout(const ChunkArgs& a) { return hot_config(a.in_bf16, a.dk, a.C); }
 hipError_t run_chunk_chain64(const ChunkArgs& a);   // kda_chunk_chain64.hip
 
 }  // namespace kda

@@ -24,7 +24,7 @@ namespace kda {
 //   Kb^T   [8 channel tiles][2 k-steps][64][8 bf16]     lane l: channel 16c + l%16, tokens 32u + 8(l/16) + 0..7
 //   P      [4 row tiles][2 k-steps][64][8 bf16]         (row tiles 0, 1 at k-step 1 lie above the diagonal:
 //                                                        never written, never read)
-//   U      [4 row tiles][DV/16 column tiles][64][4] fp32  lane l, element e: row 16R + 4(l/16) + e, column 16J + l%16
+//   U      [4 row tiles][DV/16 column tiles][64][4] bf16  lane l, element e: row 16R + 4(l/16) + e, column 16J + l%16
 //   gam    [DK] fp32
 template <typename TOut, int DV, int DVS>
 struct Chain64Cfg {
@@ -42,7 +42,7 @@ struct Chain64Cfg {
 template <typename TOut, int DV, int DVS>
 __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
-    const bf16* __restrict__ ws_p, const float* __restrict__ ws_u, const float* __restrict__ ws_gam,
+    const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, int T_len, int H, int NC) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
     constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, NSL = Cfg::NSL, LDK = Cfg::LDK, LDC = Cfg::LDC;
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
 
     // ---- operand registers, D chunks in flight
     u32x4 fA[D][4];      // Wk (W waves) or Qt (O waves), row tile R, 4 k-steps
-    u32x4 fX[D][2];      // U tiles of this slice (W waves) or P k-steps (O waves)
+    u32x4 fX[D][2];      // U tiles of this slice, 2 dwords each (W waves) or P k-steps (O waves)
     u32x4 fK[D][2];      // Kb^T channel tile ct, 2 k-steps
     u32x4 fG[D];         // gam of this lane's 4 state rows
     // first half: what phase 1 consumes; second half: what phase 2 consumes
@@ -90,9 +90,13 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
                           + R * 4 * 64 + lane;                                                      \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
         if (wW) {                                                                                   \
-            const u32x4* u_ = reinterpret_cast<const u32x4*>(ws_u + ch_ * (long)(C * DV))           \
+            const u32x2* u_ = reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))           \
                               + (R * (DV / 16) + sl * NJ) * 64 + lane;                              \
-            _Pragma("unroll") for (int j = 0; j < NJ; ++j) fX[SL][j] = u_[j * 64];                 \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                       \
+                const u32x2 w_ = u_[j * 64];                                                       \
+                fX[SL][0][2 * j] = w_[0];                                                          \
+                fX[SL][0][2 * j + 1] = w_[1];                                                      \
+            }                                                                                      \
         }                                                                                           \
     }
 #define KDA_C64_PREFETCH_2(SL, CH)                                                                  \
@@ -162,10 +166,11 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         if (wW) {
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt) {
-                const floatx4 uu = __builtin_bit_cast(floatx4, fX[d][jt]);
+                const u32x2 up = u32x2{fX[d][0][2 * jt], fX[d][0][2 * jt + 1]};
+                const bf16x4 uu = __builtin_bit_cast(bf16x4, up);
                 bf16x4 w4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w4[e] = (bf16)(uu[e] - acc[jt][e]);
+                for (int e = 0; e < 4; ++e) w4[e] = (bf16)((float)uu[e] - acc[jt][e]);
                 *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
             }
         }
@@ -242,7 +247,7 @@ static hipError_t launch_chain64_dvs(const ChunkArgs& a) {
     char* ws = (char*)a.ws;
     hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                        (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
-                       (const bf16*)(ws + w.p), (const float*)(ws + w.u), (const float*)(ws + w.gam),
+                       (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam),
                        a.s0, (TOut*)a.o, a.sT, a.T, a.H, NC);
     return hipGetLastError();
 }

@@ -426,7 +426,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     bf16* __restrict__ ws_qt, bf16* __restrict__ ws_wk, bf16* __restrict__ ws_kb, bf16* __restrict__ ws_p,
-    float* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC) {
+    bf16* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC) {
     typedef Intra64Cfg<DV> Cfg;
     constexpr int C = 64, NB = 4, DK = 128, NT = 512, NW = 8, HALF = 64;
     constexpr int LDH = Cfg::LDH, LDT = Cfg::LDT, LDA = Cfg::LDA;
@@ -751,7 +751,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     __syncthreads();
     {
         constexpr int NUT = DV / 16, NCT = NUT + DK / 16;        // column tiles: U then Wk
-        float* gU = ws_u + ch * (long)C * DV;
+        bf16* gU = ws_u + ch * (long)C * DV;
         bf16* gW = ws_wk + ch * (long)C * DK;
         const int r = lane & 15, kg = lane >> 4;
         constexpr int NTPW = (NCT + NW - 1) / NW;                  // column tiles per wave
@@ -776,14 +776,19 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                 }
             }
         }
-        // U goes out straight from the accumulators: tile (row tile, column tile) as [64 lanes][4]
+        // U goes out straight from the accumulators, in bf16: tile (row tile, column
+        // tile) as [64 lanes][4]
 #pragma unroll
         for (int sct = 0; sct < NTPW; ++sct) {
             const int ct = wave + NW * sct;
             if (ct < NUT) {
 #pragma unroll
-                for (int R2 = 0; R2 < 4; ++R2)
-                    reinterpret_cast<floatx4*>(gU)[(R2 * (DV / 16) + ct) * 64 + lane] = acc[sct][R2];
+                for (int R2 = 0; R2 < 4; ++R2) {
+                    bf16x4 u4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) u4[e] = (bf16)acc[sct][R2][e];
+                    reinterpret_cast<bf16x4*>(gU)[(R2 * (DV / 16) + ct) * 64 + lane] = u4;
+                }
             }
         }
         __syncthreads();                               // operands read by every wave: staging may overwrite them
@@ -821,7 +826,7 @@ WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
     w.wk = off; off = al256(off + nch * C * dk * es);
     w.kb = off; off = al256(off + nch * C * dk * es);
     w.p = off;  off = al256(off + nch * C * C * es);
-    w.u = off;  off = al256(off + nch * C * dv * 4);
+    w.u = off;  off = al256(off + nch * C * dv * (hot_config(in_bf16, dk, C) ? 2 : 4));
     w.gam = off; off = al256(off + nch * dk * 4);
     w.total = off;
     return w;
@@ -875,7 +880,7 @@ static hipError_t launch_intra64(const ChunkArgs& a) {
     hipLaunchKernelGGL((chunk_intra64_kernel<DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
                        (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
-                       (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
+                       (bf16*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
     return hipGetLastError();
 }
 

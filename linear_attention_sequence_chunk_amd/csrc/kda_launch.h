@@ -23,12 +23,16 @@ struct ChunkArgs {
     bool in_bf16, out_bf16;
     void* ws; size_t ws_bytes;
     hipStream_t stream;
-    bool generic = false;   // force the generic intra-chunk kernel (tests)
 };
+
+// The hot configuration (bf16 inputs, C = 64, dk = 128) has its own pair of
+// kernels and its own workspace format: contents in MFMA fragment order, U in bf16.
+inline bool hot_config(bool in_bf16, int dk, int C) { return in_bf16 && dk == 128 && C == 64; }
 
 // Workspace of the split chunk path: struct of arrays, each indexed by the
 // chunk-major unit id n * (B*H) + (b*H + h); per unit
-//   Qt [C][dk] in, Wk [C][dk] in, Kb^T [dk][C] in, P [C][C] in, U [C][dv] fp32, gam [dk] fp32
+//   Qt [C][dk] in, Wk [C][dk] in, Kb^T [dk][C] in, P [C][C] in, U [C][dv], gam [dk] fp32
+// with U in fp32, except in the hot configuration (bf16)
 struct WsLayout {
     size_t qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
 };
