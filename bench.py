@@ -167,6 +167,8 @@ def main():
                  "host_wall_ms_per_step": round(t_host / K * 1e3, 4)},
     }
 
+    out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, g, w, K, args.warmup)
+
     if not args.no_decode:
         out["decode"] = bench_decode(torch, inputs, decode_step, dev, args.decode_steps)
 
@@ -174,6 +176,29 @@ def main():
         out["cpu_baseline"] = cpu_baseline(d, w)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_gate_layouts(torch, ChunkPlan, g, w, steps, warmup):
+    """The same step with one gate per head (g [B,T,H]: the first channel's
+    gates) and with no gate (alpha = 1, g not read)."""
+    res = {}
+    for layout in ("head", "none"):
+        gl = g["g"][..., 0].contiguous() if layout == "head" else None
+        plan = ChunkPlan(g["q"], g["k"], g["v"], gl, g["beta"], g["S0"], chunk_size=w.C, gate_layout=layout)
+        for _ in range(warmup):
+            plan.run()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            plan.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[layout] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1)}
+        del plan
+    return res
 
 
 def bench_decode(torch, inputs, decode_step, dev, steps):

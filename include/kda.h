@@ -57,6 +57,21 @@ extern "C" {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
+/*
+ * Layout of the log-gate g, for the _ex entry points.  The plain entry points
+ * use KDA_GATE_CHANNEL.
+ *   KDA_GATE_CHANNEL  g holds one gate per key channel: [..., dk] fp32.  This is
+ *                     Kimi Delta Attention's fine-grained gate (Kimi Linear
+ *                     paragraph of the KimiK3 essay; section 九 of the explainer).
+ *   KDA_GATE_HEAD     g holds one gate per token and head, [...] fp32 without
+ *                     the channel axis, applied to every channel: the scalar
+ *                     decay of Gated DeltaNet (Gated DeltaNet paragraph of the
+ *                     KimiK3 essay).
+ *   KDA_GATE_NONE     no decay, alpha = 1: the plain delta rule (DeltaNet); g is
+ *                     not read and may be NULL.
+ */
+typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_gate_layout_t;
+
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,        /* a required pointer is NULL                       */
@@ -116,6 +131,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v,
  *     Reads q, k, v, g, beta; writes only the workspace.
  *   kda_chunk_chain: the sequential state recurrence across chunks and the
  *     outputs.  Reads the workspace and initial_state; writes o and final_state.
+ *     It does not read g, which may be NULL.
  * kda_chunk_chain must run after kda_chunk_intra on the same workspace with the
  * same sizes (stream order suffices).
  */
@@ -137,6 +153,30 @@ int kda_chunk_chain(const void *q, const void *k, const void *v,
                     void *stream, int C);
 
 /*
+ * kda_chunk_fwd_ex, kda_chunk_intra_ex -- kda_chunk_fwd and kda_chunk_intra
+ * with the gate layout as an argument (kda_gate_layout_t).  g is [B,T,H,dk] for
+ * KDA_GATE_CHANNEL, [B,T,H] for KDA_GATE_HEAD (fp32, 4-byte aligned) and ignored
+ * (NULL allowed) for KDA_GATE_NONE.  The chain stage, kda_chunk_chain, does not
+ * read g and serves every layout.  An unknown layout returns KDA_ERR_UNSUPPORTED.
+ */
+int kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                     const float *g, const float *beta,
+                     const float *initial_state,
+                     void *o, float *final_state,
+                     int B, int T, int H, int dk, int dv,
+                     int in_dtype, int out_dtype,
+                     void *workspace, size_t workspace_bytes,
+                     void *stream, int C, int gate_layout);
+int kda_chunk_intra_ex(const void *q, const void *k, const void *v,
+                       const float *g, const float *beta,
+                       const float *initial_state,
+                       void *o, float *final_state,
+                       int B, int T, int H, int dk, int dv,
+                       int in_dtype, int out_dtype,
+                       void *workspace, size_t workspace_bytes,
+                       void *stream, int C, int gate_layout);
+
+/*
  * kda_decode_step -- one token per sequence, state updated IN PLACE.
  *   q, k   [N,H,dk] in_dtype;  v [N,H,dv] in_dtype
  *   g      [N,H,dk] fp32 log-gate;  beta [N,H] fp32
@@ -150,6 +190,17 @@ int kda_decode_step(const void *q, const void *k, const void *v,
                     float *state, void *o,
                     int N, int H, int dk, int dv,
                     int in_dtype, int out_dtype, void *stream);
+
+/*
+ * kda_decode_step_ex -- kda_decode_step with the gate layout as an argument:
+ * g is [N,H,dk] (KDA_GATE_CHANNEL), [N,H] (KDA_GATE_HEAD) or ignored
+ * (KDA_GATE_NONE, NULL allowed).
+ */
+int kda_decode_step_ex(const void *q, const void *k, const void *v,
+                       const float *g, const float *beta,
+                       float *state, void *o,
+                       int N, int H, int dk, int dv,
+                       int in_dtype, int out_dtype, void *stream, int gate_layout);
 
 #ifdef __cplusplus
 }

@@ -11,12 +11,14 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
 
 F32, BF16 = 0, 1
+GATE = {"channel": 0, "head": 1, "none": 2}     # kda_gate_layout_t
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
           4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP"}
 
 # Every entry point include/kda.h declares.
 SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
-           "kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain", "kda_decode_step")
+           "kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain", "kda_decode_step",
+           "kda_chunk_fwd_ex", "kda_chunk_intra_ex", "kda_decode_step_ex")
 
 
 class KdaError(RuntimeError):
@@ -43,8 +45,13 @@ def lib() -> ctypes.CDLL:
         for name in ("kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain"):
             fn = getattr(L, name)
             fn.argtypes, fn.restype = _CHUNK_ARGS, _ci
+        for name in ("kda_chunk_fwd_ex", "kda_chunk_intra_ex"):
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = _CHUNK_ARGS + [_ci], _ci
         L.kda_decode_step.argtypes = [_vp] * 7 + [_ci] * 6 + [_vp]
         L.kda_decode_step.restype = _ci
+        L.kda_decode_step_ex.argtypes = [_vp] * 7 + [_ci] * 6 + [_vp, _ci]
+        L.kda_decode_step_ex.restype = _ci
         _LIB = L
     return _LIB
 

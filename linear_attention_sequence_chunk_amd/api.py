@@ -41,7 +41,22 @@ def workspace_bytes(B, T, H, dk, dv, in_dtype, chunk_size) -> int:
     return int(_lib.lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _code(in_dtype), chunk_size))
 
 
-def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_state, workspace):
+def _gate(layout) -> int:
+    if layout not in _lib.GATE:
+        raise ValueError(f"gate_layout must be one of {sorted(_lib.GATE)}")
+    return _lib.GATE[layout]
+
+
+def _check_gate(g, layout, lead, dk, dev):
+    """g is [*lead, dk] per channel, [*lead] per head, None (or ignored) without gates."""
+    if layout == "none":
+        return
+    _check_tensor("g", g, tuple(lead) + ((dk,) if layout == "channel" else ()), torch.float32, dev)
+
+
+def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_state, workspace,
+                gate_layout="channel"):
+    _gate(gate_layout)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -50,7 +65,7 @@ def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_st
     _check_tensor("q", q, (B, T, H, dk), q.dtype, dev)
     _check_tensor("k", k, (B, T, H, dk), q.dtype, dev)
     _check_tensor("v", v, (B, T, H, dv), q.dtype, dev)
-    _check_tensor("g", g, (B, T, H, dk), torch.float32, dev)
+    _check_gate(g, gate_layout, (B, T, H), dk, dev)
     _check_tensor("beta", beta, (B, T, H), torch.float32, dev)
     if initial_state is not None:
         _check_tensor("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
@@ -67,24 +82,27 @@ def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_st
 
 
 def _call_chunk(fn_name, q, k, v, g, beta, initial_state, o, final_state, B, T, H, dk, dv,
-                out_dtype, workspace, chunk_size, stream):
-    fn = getattr(_lib.lib(), fn_name)
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                out_dtype, workspace, chunk_size, stream, gate_layout="channel"):
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
             _ptr(final_state), B, T, H, dk, dv, _code(q.dtype), _code(out_dtype),
-            _ptr(workspace), workspace.numel(), _stream(stream), chunk_size)
+            _ptr(workspace), workspace.numel(), _stream(stream), chunk_size]
+    if gate_layout != "channel" and fn_name in ("kda_chunk_fwd", "kda_chunk_intra"):
+        fn_name, args = fn_name + "_ex", args + [_gate(gate_layout)]
+    st = getattr(_lib.lib(), fn_name)(*args)
     _lib.check(st, fn_name)
 
 
 def chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None,
-              final_state=None, workspace=None, stream=None):
-    """Chunkwise KDA forward (kda_chunk_fwd).  q,k [B,T,H,dk], v [B,T,H,dv] in
-    fp32 or bf16; g [B,T,H,dk] and beta [B,T,H] fp32; initial_state [B,H,dk,dv]
-    fp32 or None.  Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32).
+              final_state=None, workspace=None, stream=None, gate_layout="channel"):
+    """Chunkwise KDA forward (kda_chunk_fwd / kda_chunk_fwd_ex).  q,k [B,T,H,dk],
+    v [B,T,H,dv] in fp32 or bf16; beta [B,T,H] fp32; g fp32 [B,T,H,dk]
+    (gate_layout "channel"), [B,T,H] ("head") or None ("none"); initial_state
+    [B,H,dk,dv] fp32 or None.  Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32).
     ``final_state`` may be given (e.g. the initial_state tensor, for in place)."""
-    B, T, H, dk, dv, out_dtype, o, fs, ws = _prep_chunk(q, k, v, g, beta, initial_state,
-                                                        chunk_size, out_dtype, final_state, workspace)
+    B, T, H, dk, dv, out_dtype, o, fs, ws = _prep_chunk(q, k, v, g, beta, initial_state, chunk_size,
+                                                        out_dtype, final_state, workspace, gate_layout)
     _call_chunk("kda_chunk_fwd", q, k, v, g, beta, initial_state, o, fs, B, T, H, dk, dv,
-                out_dtype, ws, chunk_size, stream)
+                out_dtype, ws, chunk_size, stream, gate_layout)
     return o, fs
 
 
@@ -92,16 +110,20 @@ class ChunkPlan:
     """Pre-allocated outputs and workspace for repeated kda_chunk_fwd calls on the
     same sizes; ``run`` calls both stages, ``intra``/``chain`` one each."""
 
-    def __init__(self, q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None):
+    def __init__(self, q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None,
+                 gate_layout="channel"):
         self.args = (q, k, v, g, beta, initial_state)
         self.chunk_size = chunk_size
+        self.gate_layout = gate_layout
         (self.B, self.T, self.H, self.dk, self.dv, self.out_dtype, self.o, self.final_state,
-         self.workspace) = _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, None, None)
+         self.workspace) = _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, None, None,
+                                       gate_layout)
 
     def _go(self, name, stream=None):
         q, k, v, g, beta, s0 = self.args
         _call_chunk(name, q, k, v, g, beta, s0, self.o, self.final_state, self.B, self.T, self.H,
-                    self.dk, self.dv, self.out_dtype, self.workspace, self.chunk_size, stream)
+                    self.dk, self.dv, self.out_dtype, self.workspace, self.chunk_size, stream,
+                    self.gate_layout)
 
     def run(self, stream=None):
         self._go("kda_chunk_fwd", stream)
@@ -114,8 +136,9 @@ class ChunkPlan:
         self._go("kda_chunk_chain", stream)
 
 
-def decode_step(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None):
-    """One decode step (kda_decode_step).  q,k [N,H,dk], v [N,H,dv]; g [N,H,dk],
+def decode_step(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, gate_layout="channel"):
+    """One decode step (kda_decode_step / kda_decode_step_ex).  q,k [N,H,dk],
+    v [N,H,dv]; g fp32 [N,H,dk] ("channel"), [N,H] ("head") or None ("none");
     beta [N,H] fp32; state [N,H,dk,dv] fp32 is updated in place.  Returns o."""
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -124,14 +147,14 @@ def decode_step(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None):
         raise ValueError("inputs must be on a GPU")
     _check_tensor("k", k, (N, H, dk), q.dtype, dev)
     _check_tensor("v", v, (N, H, dv), q.dtype, dev)
-    _check_tensor("g", g, (N, H, dk), torch.float32, dev)
+    _check_gate(g, gate_layout, (N, H), dk, dev)
     _check_tensor("beta", beta, (N, H), torch.float32, dev)
     _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
-    st = _lib.lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                    _ptr(o), N, H, dk, dv, _code(q.dtype), _code(out_dtype),
-                                    _stream(stream))
-    _lib.check(st, "kda_decode_step")
+    st = _lib.lib().kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                       _ptr(o), N, H, dk, dv, _code(q.dtype), _code(out_dtype),
+                                       _stream(stream), _gate(gate_layout))
+    _lib.check(st, "kda_decode_step_ex")
     return o

@@ -66,28 +66,35 @@ struct ChunkCall {
     size_t ws_bytes;
     void* stream;
     int C;
+    int gate;
 };
+
+bool gate_ok(int g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
+// bytes of g per token-head for a gate layout
+size_t gate_bytes(int gate, int dk) { return gate == KDA_GATE_CHANNEL ? (size_t)dk * 4 : gate == KDA_GATE_HEAD ? 4 : 0; }
 
 bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
 size_t esize(int d) { return d == KDA_BF16 ? 2 : 4; }
 
 int validate_chunk(const ChunkCall& c) {
     if (c.B < 0 || c.T < 0 || c.H < 0) return KDA_ERR_SHAPE;
-    if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype) || !gate_ok(c.gate)) return KDA_ERR_UNSUPPORTED;
     if ((c.dk != 64 && c.dk != 128) || (c.dv != 64 && c.dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (c.C != 16 && c.C != 32 && c.C != 64 && c.C != 128) return KDA_ERR_UNSUPPORTED;
     if (!kda::chunk_supported(c.dk, c.dv, c.C, c.in_dtype == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
 
     const size_t tok = (size_t)c.B * c.T * c.H;
     const size_t nst = (size_t)c.B * c.H * c.dk * c.dv;
-    if (tok > 0 && (!c.q || !c.k || !c.v || !c.g || !c.beta || !c.o)) return KDA_ERR_NULL;
+    const bool need_g = c.gate != KDA_GATE_NONE;
+    if (tok > 0 && (!c.q || !c.k || !c.v || (need_g && !c.g) || !c.beta || !c.o)) return KDA_ERR_NULL;
+    const float* g = need_g ? c.g : nullptr;            // g is not read without gates
 
-    // q, k, v, o and the workspace move in 16-byte vectors, g in 8-byte pairs;
-    // beta and the states only need fp32 alignment.
+    // q, k, v, o and the workspace move in 16-byte vectors, per-channel g in 8-byte
+    // pairs; per-head g, beta and the states only need fp32 alignment.
     const void* p16[5] = {c.q, c.k, c.v, c.o, c.ws};
     for (const void* p : p16)
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
-    if (c.g && !aligned(c.g, 8)) return KDA_ERR_MISALIGNED;
+    if (g && !aligned(g, c.gate == KDA_GATE_CHANNEL ? 8 : 4)) return KDA_ERR_MISALIGNED;
     const void* p4[3] = {c.beta, c.s0, c.sT};
     for (const void* p : p4)
         if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
@@ -97,7 +104,7 @@ int validate_chunk(const ChunkCall& c) {
 
     const size_t ei = esize(c.in_dtype), eo = esize(c.out_dtype);
     const Range rq = range_of(c.q, tok * c.dk * ei), rk = range_of(c.k, tok * c.dk * ei),
-                rv = range_of(c.v, tok * c.dv * ei), rg = range_of(c.g, tok * c.dk * 4),
+                rv = range_of(c.v, tok * c.dv * ei), rg = range_of(g, tok * gate_bytes(c.gate, c.dk)),
                 rb = range_of(c.beta, tok * 4), rs0 = range_of(c.s0, nst * 4),
                 ro = range_of(c.o, tok * c.dv * eo), rsT = range_of(c.sT, nst * 4),
                 rw = range_of(c.ws, tok > 0 ? need : 0);
@@ -116,7 +123,8 @@ int validate_chunk(const ChunkCall& c) {
 
 kda::ChunkArgs to_args(const ChunkCall& c) {
     kda::ChunkArgs a;
-    a.q = c.q; a.k = c.k; a.v = c.v; a.g = c.g; a.beta = c.beta;
+    a.q = c.q; a.k = c.k; a.v = c.v; a.g = c.gate == KDA_GATE_NONE ? nullptr : c.g; a.beta = c.beta;
+    a.gate = c.gate;
     a.s0 = c.s0; a.o = c.o; a.sT = c.sT;
     a.B = c.B; a.T = c.T; a.H = c.H; a.dk = c.dk; a.dv = c.dv; a.C = c.C;
     a.in_bf16 = c.in_dtype == KDA_BF16; a.out_bf16 = c.out_dtype == KDA_BF16;
@@ -188,32 +196,42 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in
         const float *initial_state, void *o, float *final_state, int B, int T, int H, int dk, \
         int dv, int in_dtype, int out_dtype, void *workspace, size_t workspace_bytes,        \
         void *stream, int C
-#define KDA_CHUNK_CALL                                                                      \
+#define KDA_CHUNK_CALL(GATE)                                                                \
     ChunkCall { q, k, v, g, beta, initial_state, o, final_state, B, T, H, dk, dv, in_dtype,  \
-                out_dtype, workspace, workspace_bytes, stream, C }
+                out_dtype, workspace, workspace_bytes, stream, C, GATE }
 
-int kda_chunk_fwd(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL, STAGE_INTRA | STAGE_CHAIN); }
-int kda_chunk_intra(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL, STAGE_INTRA); }
-int kda_chunk_chain(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL, STAGE_CHAIN); }
+int kda_chunk_fwd(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL(KDA_GATE_CHANNEL), STAGE_INTRA | STAGE_CHAIN); }
+int kda_chunk_intra(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL(KDA_GATE_CHANNEL), STAGE_INTRA); }
+// the chain stage does not read g (any layout, NULL allowed)
+int kda_chunk_chain(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL(KDA_GATE_NONE), STAGE_CHAIN); }
+int kda_chunk_fwd_ex(KDA_CHUNK_PARAMS, int gate_layout) {
+    return run_chunk(KDA_CHUNK_CALL(gate_layout), STAGE_INTRA | STAGE_CHAIN);
+}
+int kda_chunk_intra_ex(KDA_CHUNK_PARAMS, int gate_layout) {
+    return run_chunk(KDA_CHUNK_CALL(gate_layout), STAGE_INTRA);
+}
 
-int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                    float* state, void* o, int N, int H, int dk, int dv, int in_dtype, int out_dtype,
-                    void* stream) {
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       float* state, void* o, int N, int H, int dk, int dv, int in_dtype, int out_dtype,
+                       void* stream, int gate_layout) {
     if (N < 0 || H < 0) return KDA_ERR_SHAPE;
-    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_layout)) return KDA_ERR_UNSUPPORTED;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
     const size_t nh = (size_t)N * H;
     if (nh == 0) return KDA_OK;
-    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    const bool need_g = gate_layout != KDA_GATE_NONE;
+    if (!q || !k || !v || (need_g && !g) || !beta || !state || !o) return KDA_ERR_NULL;
+    if (!need_g) g = nullptr;                            // g is not read without gates
     // the state is streamed in 16-byte vectors; the rest is read element-wise
     if (!aligned(state, 16)) return KDA_ERR_MISALIGNED;
     const void* pe[6] = {q, k, v, g, beta, o};
     const uintptr_t ae[6] = {esize(in_dtype), esize(in_dtype), esize(in_dtype), 4, 4, esize(out_dtype)};
     for (int i = 0; i < 6; ++i)
-        if (!aligned(pe[i], ae[i])) return KDA_ERR_MISALIGNED;
+        if (pe[i] && !aligned(pe[i], ae[i])) return KDA_ERR_MISALIGNED;
     const size_t ei = esize(in_dtype), eo = esize(out_dtype);
     const Range rq = range_of(q, nh * dk * ei), rk = range_of(k, nh * dk * ei),
-                rv = range_of(v, nh * dv * ei), rg = range_of(g, nh * dk * 4), rb = range_of(beta, nh * 4),
+                rv = range_of(v, nh * dv * ei), rg = range_of(g, nh * gate_bytes(gate_layout, dk)),
+                rb = range_of(beta, nh * 4),
                 rs = range_of(state, nh * dk * dv * 4), ro = range_of(o, nh * dv * eo);
     const Range in[] = {rq, rk, rv, rg, rb};
     for (const Range& r : in)
@@ -226,8 +244,16 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* g,
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
     a.N = N; a.H = H; a.dk = dk; a.dv = dv;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.gate = gate_layout;
     a.stream = (hipStream_t)stream;
     return finish(kda::run_decode_step(a), a.stream);
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    float* state, void* o, int N, int H, int dk, int dv, int in_dtype, int out_dtype,
+                    void* stream) {
+    return kda_decode_step_ex(q, k, v, g, beta, state, o, N, H, dk, dv, in_dtype, out_dtype, stream,
+                              KDA_GATE_CHANNEL);
 }
 
 }  // extern "C"

@@ -10,7 +10,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     T* __restrict__ ws_qt, T* __restrict__ ws_wk, T* __restrict__ ws_kb, T* __restrict__ ws_p,
-    float* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC) {
+    float* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC, int gate) {
     typedef IntraCfg<T, DK, DV, C> Cfg;
     constexpr int NB = Cfg::NB, NP = Cfg::NP, HR = Cfg::HR, LDK = Cfg::LDK, LDA = Cfg::LDA,
                   LDT = Cfg::LDT, CK = Cfg::CK;
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
         for (int rr = 0; rr < 16; ++rr) {
             const int t = R * 16 + rr;
             float2 gg = make_float2(0.f, 0.f);
-            if (valid(t)) gg = *reinterpret_cast<const float2*>(g + grow(t) * DK + c);
+            if (valid(t)) gg = gate_pair(g, gate, grow(t), DK, c);
             l0 += clamp_g(gg.x);
             l1 += clamp_g(gg.y);
             *reinterpret_cast<float2*>(sL + t * DK + c) = make_float2(l0, l1);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             const int t = R * 16 + rr;
             float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
             if (valid(t)) {
-                const float2 gg = *reinterpret_cast<const float2*>(g + grow(t) * DK + c);
+                const float2 gg = gate_pair(g, gate, grow(t), DK, c);
                 l0 += clamp_g(gg.x); l1 += clamp_g(gg.y);
                 Pair2<T>::load(k + grow(t) * DK + c, k0, k1);
                 Pair2<T>::load(q + grow(t) * DK + c, q0, q1);
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     bf16* __restrict__ ws_qt, bf16* __restrict__ ws_wk, bf16* __restrict__ ws_kb, bf16* __restrict__ ws_p,
-    bf16* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC) {
+    bf16* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC, int gate) {
     typedef Intra64Cfg<DV> Cfg;
     constexpr int C = 64, NB = 4, DK = 128, NT = 512, NW = 8, HALF = 64;
     constexpr int LDH = Cfg::LDH, LDT = Cfg::LDT, LDA = Cfg::LDA;
@@ -464,8 +464,16 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             const long base = grow(t) * DK + chan(p);
             qv[p] = *reinterpret_cast<const bf16x8*>(q + base);
             kv[p] = *reinterpret_cast<const bf16x8*>(k + base);
-            ga[p] = *reinterpret_cast<const floatx4*>(g + base);
-            gb[p] = *reinterpret_cast<const floatx4*>(g + base + 4);
+            if (gate == GATE_CHANNEL) {
+                ga[p] = *reinterpret_cast<const floatx4*>(g + base);
+                gb[p] = *reinterpret_cast<const floatx4*>(g + base + 4);
+            } else if (gate == GATE_HEAD) {
+                const float x = g[grow(t)];
+                ga[p] = floatx4{x, x, x, x};
+                gb[p] = ga[p];
+            } else {
+                ga[p] = zero4(); gb[p] = zero4();
+            }
         } else {
 #pragma unroll
             for (int m = 0; m < 8; ++m) { qv[p][m] = (bf16)0.f; kv[p][m] = (bf16)0.f; }
@@ -630,7 +638,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                     if (i <= rw && valid(rw)) {
                         for (int cc = 0; cc < DK; ++cc) {
                             float w = 1.f;
-                            for (int j = i + 1; j <= rw; ++j) w *= __expf(clamp_g(g[grow(j) * DK + cc]));
+                            for (int j = i + 1; j <= rw; ++j) w *= __expf(clamp_g(gate_at(g, gate, grow(j), DK, cc)));
                             const float ki = (float)k[grow(i) * DK + cc];
                             sa += (float)k[grow(rw) * DK + cc] * ki * w;
                             sp += (float)q[grow(rw) * DK + cc] * ki * w;
@@ -846,7 +854,7 @@ static hipError_t launch_intra(const ChunkArgs& a) {
         hipLaunchKernelGGL((chunk_intra_kernel<T, DK, DV, C>), dim3((unsigned)nch), dim3(256), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta,
                            (T*)(ws + w.qt), (T*)(ws + w.wk), (T*)(ws + w.kb), (T*)(ws + w.p),
-                           (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
+                           (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC, a.gate);
         return hipGetLastError();
     }
 }
@@ -880,7 +888,7 @@ static hipError_t launch_intra64(const ChunkArgs& a) {
     hipLaunchKernelGGL((chunk_intra64_kernel<DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
                        (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
-                       (bf16*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC);
+                       (bf16*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC, a.gate);
     return hipGetLastError();
 }
 

@@ -113,4 +113,18 @@ template <> struct Vec8<float> {
 // NaN stays NaN (the comparison is false), -inf becomes G_FLOOR.
 __device__ inline float clamp_g(float g) { return g < G_FLOOR ? G_FLOOR : g; }
 
+// The log-gate of (row, channel c) for a gate layout (GateLayout in kda_launch.h):
+// per channel g[row * dk + c], per head g[row], or none (0).
+__device__ inline float gate_at(const float* __restrict__ g, int layout, long row, int dk, int c) {
+    if (layout == 0) return g[row * dk + c];
+    if (layout == 1) return g[row];
+    return 0.f;
+}
+// Two consecutive channels c, c + 1 (c even) of the same row.
+__device__ inline float2 gate_pair(const float* __restrict__ g, int layout, long row, int dk, int c) {
+    if (layout == 0) return *reinterpret_cast<const float2*>(g + row * dk + c);
+    if (layout == 1) { const float x = g[row]; return make_float2(x, x); }
+    return make_float2(0.f, 0.f);
+}
+
 }  // namespace kda

@@ -21,7 +21,7 @@ template <typename TIn, typename TOut, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
-    float* __restrict__ state, TOut* __restrict__ o) {
+    float* __restrict__ state, TOut* __restrict__ o, int gate) {
     constexpr int NT = 256;
     constexpr int CG = DV / 4;       // threads across one row (float4 each)
     constexpr int RG = NT / CG;      // row groups
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         sv[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (long)(ty + i * RG) * DV) + tx);
 
     if (tid < DK) {
-        const float a = __expf(g[nh * DK + tid]);       // exp(-inf) = 0: alpha = 0 clears
+        const float a = __expf(gate_at(g, gate, nh, DK, tid));   // exp(-inf) = 0: alpha = 0 clears
         const float kc = to_f32(k[nh * DK + tid]);
         const float qc = to_f32(q[nh * DK + tid]);
         s_a[tid] = a; s_k[tid] = kc; s_ak[tid] = a * kc; s_aq[tid] = a * qc;
@@ -99,7 +99,7 @@ static hipError_t launch_decode(const DecodeArgs& a) {
     const long nh = (long)a.N * a.H;
     hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV>), dim3((unsigned)nh), dim3(256), 0,
                        a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta,
-                       a.state, (TOut*)a.o);
+                       a.state, (TOut*)a.o, a.gate);
     return hipGetLastError();
 }
 

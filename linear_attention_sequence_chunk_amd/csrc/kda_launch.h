@@ -6,12 +6,20 @@
 
 namespace kda {
 
+// Layout of the log-gate g (same values as kda_gate_layout_t in kda.h).
+enum GateLayout : int {
+    GATE_CHANNEL = 0,   // g[row * dk + c]: one gate per key channel
+    GATE_HEAD = 1,      // g[row]: one gate per token and head, shared by all channels
+    GATE_NONE = 2       // no decay (alpha = 1); g is not read
+};
+
 struct DecodeArgs {
     const void* q; const void* k; const void* v;
     const float* g; const float* beta;
     float* state; void* o;
     int N, H, dk, dv;
     bool in_bf16, out_bf16;
+    int gate;
     hipStream_t stream;
 };
 
@@ -21,6 +29,7 @@ struct ChunkArgs {
     const float* s0; void* o; float* sT;
     int B, T, H, dk, dv, C;
     bool in_bf16, out_bf16;
+    int gate;
     void* ws; size_t ws_bytes;
     hipStream_t stream;
 };

@@ -84,11 +84,13 @@ def chunk_args(B=2, T=100, H=3, dk=64, dv=64, ind=_lib.F32, outd=_lib.F32, C=64)
     return a
 
 
-def call_chunk(a, fn="kda_chunk_fwd"):
+def call_chunk(a, fn="kda_chunk_fwd", gate=None):
     L = _lib.lib()
-    return getattr(L, fn)(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"], a["sT"],
-                          a["B"], a["T"], a["H"], a["dk"], a["dv"], a["ind"], a["outd"],
-                          a["ws"], a["wsb"], None, a["C"])
+    args = [a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"], a["sT"],
+            a["B"], a["T"], a["H"], a["dk"], a["dv"], a["ind"], a["outd"], a["ws"], a["wsb"], None, a["C"]]
+    if gate is not None:
+        return getattr(L, fn + "_ex")(*args, gate)
+    return getattr(L, fn)(*args)
 
 
 @pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain"])
@@ -106,9 +108,34 @@ def test_chunk_validation_codes(fn):
         (dict(sT=a["s0"] + 256), ALIAS), (dict(ws=a["g"]), ALIAS), (dict(o=a["sT"]), ALIAS),
     ]
     for change, code in cases:
+        if fn == "kda_chunk_chain" and "g" in change or (fn == "kda_chunk_chain" and change.get("ws") == a["g"]):
+            continue                      # the chain stage does not read g
         b = dict(a)
         b.update(change)
         assert call_chunk(b, fn) == code, (change, code)
+
+
+@pytest.mark.skipif(HAS_GPU, reason="valid calls with fake pointers would reach a real device")
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd", "kda_chunk_intra"])
+def test_gate_layout_codes(fn):
+    a = chunk_args(ind=_lib.BF16, outd=_lib.BF16, dk=128, dv=128)
+    CH, HEAD, NONE = _lib.GATE["channel"], _lib.GATE["head"], _lib.GATE["none"]
+    tok = a["B"] * a["T"] * a["H"]
+    cases = [
+        (dict(), 3, UNSUP), (dict(), -1, UNSUP),
+        (dict(g=None), CH, NULL), (dict(g=None), HEAD, NULL), (dict(g=None), NONE, HIP),
+        (dict(g=a["g"] + 4), CH, MISAL), (dict(g=a["g"] + 4), HEAD, HIP), (dict(g=a["g"] + 2), HEAD, MISAL),
+        (dict(g=a["g"] + 2), NONE, HIP),                     # g is not read without gates
+        (dict(g=a["ws"] - tok * 4), HEAD, HIP),              # a per-head g is [B,T,H] only
+        (dict(g=a["ws"] - tok * 4), CH, ALIAS), (dict(g=a["ws"]), NONE, HIP),
+        (dict(), CH, HIP), (dict(), HEAD, HIP), (dict(), NONE, HIP),
+    ]
+    for change, gate, code in cases:
+        b = dict(a)
+        b.update(change)
+        assert call_chunk(b, fn, gate) == code, (change, gate, code)
+    b = dict(a); b["g"] = None
+    assert call_chunk(b, "kda_chunk_chain") == HIP        # the chain stage takes NULL g
 
 
 @pytest.mark.parametrize("dk", [64, 128])
@@ -157,6 +184,17 @@ def test_decode_validation_codes():
         assert call(b) == code, (change, code)
     if not HAS_GPU:
         assert call(a) == HIP
+
+    def call_ex(x, gate):
+        return L.kda_decode_step_ex(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], x["o"],
+                                    x["N"], x["H"], x["dk"], x["dv"], x["ind"], x["outd"], None, gate)
+    ex_cases = [(dict(), 3, UNSUP), (dict(g=None), 0, NULL), (dict(g=None), 1, NULL),
+                (dict(g=a["g"] + 2), 1, MISAL), (dict(o=a["g"] + 16), 0, ALIAS)]
+    if not HAS_GPU:
+        ex_cases += [(dict(g=None), 2, HIP), (dict(o=a["g"] + 4 * N * H), 1, HIP), (dict(), 1, HIP)]
+    for change, gate, code in ex_cases:
+        b = dict(a); b.update(change)
+        assert call_ex(b, gate) == code, (change, gate, code)
 
 
 def test_python_binding_refuses_cpu_tensors():
