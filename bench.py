@@ -222,12 +222,35 @@ def bench_decode(torch, inputs, decode_step, dev, steps):
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 1e3 / steps
     nh = wd.B * wd.H
-    byts = nh * (2 * wd.dk * wd.dv * 4 + (2 * wd.dk + wd.dv) * 2 + wd.dk * 4 + 4 + wd.dv * 2)
+    per_tok = (2 * wd.dk + wd.dv) * 2 + wd.dk * 4 + 4 + wd.dv * 2
+    byts = nh * (2 * wd.dk * wd.dv * 4 + per_tok)
     gbs = byts / t / 1e9
-    return {"metric": "decode step state GB/s", "GBps": round(gbs, 1),
-            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "us_per_step": round(t * 1e6, 2),
-            "tokens_per_s": round(wd.B / t, 1), "bytes_per_step": byts, "steps": steps,
-            "config": "256 sequences x 32 heads, dk=dv=128, bf16 q/k/v, fp32 state in place"}
+    out = {"metric": "decode step state GB/s", "GBps": round(gbs, 1),
+           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "us_per_step": round(t * 1e6, 2),
+           "tokens_per_s": round(wd.B / t, 1), "bytes_per_step": byts, "steps": steps,
+           "config": "256 sequences x 32 heads, dk=dv=128, bf16 q/k/v, fp32 state in place"}
+
+    # four tokens per call (kda_decode_tokens): the state moves once per call
+    from linear_attention_sequence_chunk_amd import decode_tokens
+    TT = 4
+    seq = lambda x: x.transpose(0, 1).contiguous()
+    tk = {key: seq(pool[key][:TT]) for key in pool}
+    o4 = torch.empty((wd.B, TT, wd.H, wd.dv), dtype=torch.bfloat16, device=dev)
+    calls = max(1, steps // TT)
+    for _ in range(3):
+        decode_tokens(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S, o=o4)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(calls):
+        decode_tokens(tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S, o=o4)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t4 = e0.elapsed_time(e1) / 1e3 / calls
+    b4 = nh * (2 * wd.dk * wd.dv * 4 + TT * per_tok)
+    out["tokens4"] = {"tokens_per_call": TT, "us_per_call": round(t4 * 1e6, 2),
+                      "tokens_per_s": round(wd.B * TT / t4, 1), "GBps": round(b4 / t4 / 1e9, 1),
+                      "bytes_per_call": b4}
+    return out
 
 
 def cpu_baseline(d, w):

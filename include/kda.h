@@ -202,6 +202,22 @@ int kda_decode_step_ex(const void *q, const void *k, const void *v,
                        int N, int H, int dk, int dv,
                        int in_dtype, int out_dtype, void *stream, int gate_layout);
 
+/*
+ * kda_decode_tokens -- T consecutive tokens per sequence in one call, the state
+ * updated IN PLACE: the same result, bitwise, as T kda_decode_step_ex calls, with
+ * the state read and written once instead of T times (a short prefill that
+ * continues a decoded sequence, or several tokens accepted at once).
+ *   q, k  [N,T,H,dk] in_dtype;  v [N,T,H,dv] in_dtype;  beta [N,T,H] fp32
+ *   g     [N,T,H,dk] / [N,T,H] fp32 or ignored, by gate_layout
+ *   state [N,H,dk,dv] fp32, read and overwritten;  o [N,T,H,dv] out_dtype
+ * T = 0 leaves the state unchanged.  Same rules as kda_decode_step otherwise.
+ */
+int kda_decode_tokens(const void *q, const void *k, const void *v,
+                      const float *g, const float *beta,
+                      float *state, void *o,
+                      int N, int T, int H, int dk, int dv,
+                      int in_dtype, int out_dtype, void *stream, int gate_layout);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPP
 # Every entry point include/kda.h declares.
 SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
            "kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain", "kda_decode_step",
-           "kda_chunk_fwd_ex", "kda_chunk_intra_ex", "kda_decode_step_ex")
+           "kda_chunk_fwd_ex", "kda_chunk_intra_ex", "kda_decode_step_ex", "kda_decode_tokens")
 
 
 class KdaError(RuntimeError):
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_step.restype = _ci
         L.kda_decode_step_ex.argtypes = [_vp] * 7 + [_ci] * 6 + [_vp, _ci]
         L.kda_decode_step_ex.restype = _ci
+        L.kda_decode_tokens.argtypes = [_vp] * 7 + [_ci] * 7 + [_vp, _ci]
+        L.kda_decode_tokens.restype = _ci
         _LIB = L
     return _LIB
 

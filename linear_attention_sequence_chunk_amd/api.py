@@ -158,3 +158,28 @@ def decode_step(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, ga
                                        _stream(stream), _gate(gate_layout))
     _lib.check(st, "kda_decode_step_ex")
     return o
+
+
+def decode_tokens(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, gate_layout="channel"):
+    """T tokens per sequence in one call (kda_decode_tokens).  q,k [N,T,H,dk],
+    v [N,T,H,dv]; g fp32 [N,T,H,dk] ("channel"), [N,T,H] ("head") or None
+    ("none"); beta [N,T,H] fp32; state [N,H,dk,dv] fp32 is updated in place.
+    Returns o [N,T,H,dv]."""
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    _check_tensor("k", k, (N, T, H, dk), q.dtype, dev)
+    _check_tensor("v", v, (N, T, H, dv), q.dtype, dev)
+    _check_gate(g, gate_layout, (N, T, H), dk, dev)
+    _check_tensor("beta", beta, (N, T, H), torch.float32, dev)
+    _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, T, H, dv), dtype=out_dtype, device=dev)
+    st = _lib.lib().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                      _ptr(o), N, T, H, dk, dv, _code(q.dtype), _code(out_dtype),
+                                      _stream(stream), _gate(gate_layout))
+    _lib.check(st, "kda_decode_tokens")
+    return o

@@ -211,14 +211,18 @@ int kda_chunk_intra_ex(KDA_CHUNK_PARAMS, int gate_layout) {
     return run_chunk(KDA_CHUNK_CALL(gate_layout), STAGE_INTRA);
 }
 
-int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                       float* state, void* o, int N, int H, int dk, int dv, int in_dtype, int out_dtype,
-                       void* stream, int gate_layout) {
-    if (N < 0 || H < 0) return KDA_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+
+int decode_call(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                float* state, void* o, int N, int T, int H, int dk, int dv, int in_dtype, int out_dtype,
+                void* stream, int gate_layout) {
+    if (N < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_layout)) return KDA_ERR_UNSUPPORTED;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
-    const size_t nh = (size_t)N * H;
-    if (nh == 0) return KDA_OK;
+    const size_t nh = (size_t)N * H, tok = nh * (size_t)T;
+    if (tok == 0) return KDA_OK;
     const bool need_g = gate_layout != KDA_GATE_NONE;
     if (!q || !k || !v || (need_g && !g) || !beta || !state || !o) return KDA_ERR_NULL;
     if (!need_g) g = nullptr;                            // g is not read without gates
@@ -229,10 +233,10 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
     for (int i = 0; i < 6; ++i)
         if (pe[i] && !aligned(pe[i], ae[i])) return KDA_ERR_MISALIGNED;
     const size_t ei = esize(in_dtype), eo = esize(out_dtype);
-    const Range rq = range_of(q, nh * dk * ei), rk = range_of(k, nh * dk * ei),
-                rv = range_of(v, nh * dv * ei), rg = range_of(g, nh * gate_bytes(gate_layout, dk)),
-                rb = range_of(beta, nh * 4),
-                rs = range_of(state, nh * dk * dv * 4), ro = range_of(o, nh * dv * eo);
+    const Range rq = range_of(q, tok * dk * ei), rk = range_of(k, tok * dk * ei),
+                rv = range_of(v, tok * dv * ei), rg = range_of(g, tok * gate_bytes(gate_layout, dk)),
+                rb = range_of(beta, tok * 4),
+                rs = range_of(state, nh * dk * dv * 4), ro = range_of(o, tok * dv * eo);
     const Range in[] = {rq, rk, rv, rg, rb};
     for (const Range& r : in)
         if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
@@ -242,11 +246,27 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
     if (st != KDA_OK) return st;
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
-    a.N = N; a.H = H; a.dk = dk; a.dv = dv;
+    a.N = N; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
     a.gate = gate_layout;
     a.stream = (hipStream_t)stream;
     return finish(kda::run_decode_step(a), a.stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       float* state, void* o, int N, int H, int dk, int dv, int in_dtype, int out_dtype,
+                       void* stream, int gate_layout) {
+    return decode_call(q, k, v, g, beta, state, o, N, 1, H, dk, dv, in_dtype, out_dtype, stream, gate_layout);
+}
+
+int kda_decode_tokens(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                      float* state, void* o, int N, int T, int H, int dk, int dv, int in_dtype,
+                      int out_dtype, void* stream, int gate_layout) {
+    return decode_call(q, k, v, g, beta, state, o, N, T, H, dk, dv, in_dtype, out_dtype, stream, gate_layout);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,

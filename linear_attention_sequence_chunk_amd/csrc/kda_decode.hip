@@ -12,6 +12,10 @@
 // float4 of columns 4*tx..4*tx+3 in rows ty, ty+RG, ty+2RG, ...: every row read
 // is a fully coalesced DV*4-byte line.  Column sums are combined in LDS in a
 // fixed order (bitwise reproducible).
+//
+// Several tokens per call (T > 1, inputs [N,T,H,d]): the tokens are applied in
+// order with the state kept in registers, so the state is read and written once
+// per call instead of once per token; the result equals T single steps bitwise.
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -21,19 +25,23 @@ template <typename TIn, typename TOut, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
-    float* __restrict__ state, TOut* __restrict__ o, int gate) {
+    float* __restrict__ state, TOut* __restrict__ o, int H, int T, int gate) {
     constexpr int NT = 256;
     constexpr int CG = DV / 4;       // threads across one row (float4 each)
     constexpr int RG = NT / CG;      // row groups
     constexpr int RPT = DK / RG;     // rows per thread
     static_assert(DK % RG == 0, "row split");
 
-    __shared__ float s_ak[DK], s_aq[DK], s_k[DK], s_a[DK];
+    // per-token vectors, double-buffered so that token t+1 can be staged while
+    // token t's update still reads them
+    __shared__ float s_ak[2][DK], s_aq[2][DK], s_k[2][DK], s_a[2][DK];
     __shared__ float s_red[2][RG][DV];
     __shared__ float s_u[DV];
-    __shared__ float s_qk;
+    __shared__ float s_qk[2];
 
     const long nh = blockIdx.x;
+    const long n = nh / H;
+    const int h = (int)(nh % H);
     const int tid = threadIdx.x;
     const int tx = tid % CG, ty = tid / CG;
     float* S = state + nh * (long)DK * DV;
@@ -44,54 +52,59 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int i = 0; i < RPT; ++i)
         sv[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S + (long)(ty + i * RG) * DV) + tx);
 
-    if (tid < DK) {
-        const float a = __expf(gate_at(g, gate, nh, DK, tid));   // exp(-inf) = 0: alpha = 0 clears
-        const float kc = to_f32(k[nh * DK + tid]);
-        const float qc = to_f32(q[nh * DK + tid]);
-        s_a[tid] = a; s_k[tid] = kc; s_ak[tid] = a * kc; s_aq[tid] = a * qc;
-    }
-    if (tid < WAVE) {                                     // q.k, fixed-order wave reduction
-        float p = 0.f;
+    for (int t = 0; t < T; ++t) {
+        const int pb = t & 1;
+        const long row = (n * T + t) * H + h;            // token t of (n, h); [N,T,H,d] inputs
+        if (tid < DK) {
+            const float a = __expf(gate_at(g, gate, row, DK, tid));   // exp(-inf) = 0: alpha = 0 clears
+            const float kc = to_f32(k[row * DK + tid]);
+            const float qc = to_f32(q[row * DK + tid]);
+            s_a[pb][tid] = a; s_k[pb][tid] = kc; s_ak[pb][tid] = a * kc; s_aq[pb][tid] = a * qc;
+        }
+        if (tid < WAVE) {                                 // q.k, fixed-order wave reduction
+            float p = 0.f;
 #pragma unroll
-        for (int c = tid; c < DK; c += WAVE) p += to_f32(q[nh * DK + c]) * to_f32(k[nh * DK + c]);
+            for (int c = tid; c < DK; c += WAVE) p += to_f32(q[row * DK + c]) * to_f32(k[row * DK + c]);
 #pragma unroll
-        for (int off = WAVE / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
-        if (tid == 0) s_qk = p;
-    }
-    __syncthreads();
+            for (int off = WAVE / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
+            if (tid == 0) s_qk[pb] = p;
+        }
+        __syncthreads();
 
-    float r[4] = {0.f, 0.f, 0.f, 0.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
+        float r[4] = {0.f, 0.f, 0.f, 0.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int c = ty + i * RG;
-        const float ak = s_ak[c], aq = s_aq[c];
-        r[0] += ak * sv[i].x; r[1] += ak * sv[i].y; r[2] += ak * sv[i].z; r[3] += ak * sv[i].w;
-        s[0] += aq * sv[i].x; s[1] += aq * sv[i].y; s[2] += aq * sv[i].z; s[3] += aq * sv[i].w;
-    }
+        for (int i = 0; i < RPT; ++i) {
+            const int c = ty + i * RG;
+            const float ak = s_ak[pb][c], aq = s_aq[pb][c];
+            r[0] += ak * sv[i].x; r[1] += ak * sv[i].y; r[2] += ak * sv[i].z; r[3] += ak * sv[i].w;
+            s[0] += aq * sv[i].x; s[1] += aq * sv[i].y; s[2] += aq * sv[i].z; s[3] += aq * sv[i].w;
+        }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) { s_red[0][ty][4 * tx + m] = r[m]; s_red[1][ty][4 * tx + m] = s[m]; }
-    __syncthreads();
+        for (int m = 0; m < 4; ++m) { s_red[0][ty][4 * tx + m] = r[m]; s_red[1][ty][4 * tx + m] = s[m]; }
+        __syncthreads();
 
-    if (tid < DV) {
-        float rr = 0.f, ss = 0.f;
+        if (tid < DV) {
+            float rr = 0.f, ss = 0.f;
 #pragma unroll
-        for (int y = 0; y < RG; ++y) { rr += s_red[0][y][tid]; ss += s_red[1][y][tid]; }
-        const float u = beta[nh] * (to_f32(v[nh * DV + tid]) - rr);
-        s_u[tid] = u;
-        o[nh * DV + tid] = from_f32<TOut>(ss + s_qk * u);
-    }
-    __syncthreads();
+            for (int y = 0; y < RG; ++y) { rr += s_red[0][y][tid]; ss += s_red[1][y][tid]; }
+            const float u = beta[row] * (to_f32(v[row * DV + tid]) - rr);
+            s_u[tid] = u;
+            o[row * DV + tid] = from_f32<TOut>(ss + s_qk[pb] * u);
+        }
+        __syncthreads();
 
-    const float u0 = s_u[4 * tx], u1 = s_u[4 * tx + 1], u2 = s_u[4 * tx + 2], u3 = s_u[4 * tx + 3];
+        const float u0 = s_u[4 * tx], u1 = s_u[4 * tx + 1], u2 = s_u[4 * tx + 2], u3 = s_u[4 * tx + 3];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int c = ty + i * RG;
-        const float a = s_a[c], kc = s_k[c];
-        floatx4 w;
-        w.x = a * sv[i].x + kc * u0; w.y = a * sv[i].y + kc * u1;
-        w.z = a * sv[i].z + kc * u2; w.w = a * sv[i].w + kc * u3;
-        __builtin_nontemporal_store(w, reinterpret_cast<floatx4*>(S + (long)c * DV) + tx);
+        for (int i = 0; i < RPT; ++i) {
+            const int c = ty + i * RG;
+            const float a = s_a[pb][c], kc = s_k[pb][c];
+            sv[i].x = a * sv[i].x + kc * u0; sv[i].y = a * sv[i].y + kc * u1;
+            sv[i].z = a * sv[i].z + kc * u2; sv[i].w = a * sv[i].w + kc * u3;
+        }
     }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        __builtin_nontemporal_store(sv[i], reinterpret_cast<floatx4*>(S + (long)(ty + i * RG) * DV) + tx);
 }
 
 template <typename TIn, typename TOut, int DK, int DV>
@@ -99,7 +112,7 @@ static hipError_t launch_decode(const DecodeArgs& a) {
     const long nh = (long)a.N * a.H;
     hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV>), dim3((unsigned)nh), dim3(256), 0,
                        a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta,
-                       a.state, (TOut*)a.o, a.gate);
+                       a.state, (TOut*)a.o, a.H, a.T, a.gate);
     return hipGetLastError();
 }
 

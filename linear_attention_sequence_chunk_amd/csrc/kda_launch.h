@@ -18,6 +18,7 @@ struct DecodeArgs {
     const float* g; const float* beta;
     float* state; void* o;
     int N, H, dk, dv;
+    int T;              // tokens per sequence (1 for a single step)
     bool in_bf16, out_bf16;
     int gate;
     hipStream_t stream;

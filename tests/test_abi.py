@@ -196,6 +196,24 @@ def test_decode_validation_codes():
         b = dict(a); b.update(change)
         assert call_ex(b, gate) == code, (change, gate, code)
 
+    # several tokens per call: inputs [N,T,H,d]
+    T = 4
+    t = dict(q=f(N * T * H * dk * 2), k=f(N * T * H * dk * 2), v=f(N * T * H * dv * 2),
+             g=f(N * T * H * dk * 4), beta=f(N * T * H * 4), state=f(N * H * dk * dv * 4),
+             o=f(N * T * H * dv * 2), N=N, T=T, H=H, dk=dk, dv=dv, ind=_lib.BF16, outd=_lib.BF16)
+
+    def call_t(x, gate=0):
+        return L.kda_decode_tokens(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], x["o"],
+                                   x["N"], x["T"], x["H"], x["dk"], x["dv"], x["ind"], x["outd"], None, gate)
+    t_cases = [(dict(T=-1), SHAPE), (dict(dv=96), UNSUP), (dict(beta=None), NULL),
+               (dict(o=t["v"] + (N * T * H * dv * 2) // 2), ALIAS), (dict(o=t["o"] + 1), MISAL)]
+    for change, code in t_cases:
+        b = dict(t); b.update(change)
+        assert call_t(b) == code, (change, code)
+    assert L.kda_decode_tokens(None, None, None, None, None, None, None, 3, 0, 2, 64, 64, 0, 0, None, 0) == OK
+    if not HAS_GPU:
+        assert call_t(t) == HIP
+
 
 def test_python_binding_refuses_cpu_tensors():
     from linear_attention_sequence_chunk_amd import chunk_fwd, decode_step

@@ -96,3 +96,38 @@ def test_decode_full_size_1000_steps():
     assert_close("o", o_hist.cpu().transpose(0, 1), o_ref[:, :, 0], TOL[torch.bfloat16])
     # the state path itself is fp32 end to end: much tighter than the bf16 bar
     assert_close("S@1000 (fp32 path)", snaps[1000], S_ref[:, 0], 1e-4)
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+@pytest.mark.parametrize("layout", ["channel", "head", "none"])
+def test_decode_tokens(T, layout):
+    """T tokens per call (kda_decode_tokens) equal T single steps bitwise, and the
+    oracle over the same T-token sequences."""
+    from linear_attention_sequence_chunk_amd import decode_tokens
+    w = inputs.WORKLOADS["decode"].with_(B=6, H=3)
+    d = inputs.make_decode_steps(w, T)                    # [T, N, H, ...]
+    S0 = inputs.decode_state(w)
+    seq = lambda x: x.transpose(0, 1).contiguous()        # -> [N, T, H, ...]
+    if layout == "head":
+        g_ch = d["g"][..., :1].expand_as(d["g"]).contiguous()
+        g_in = seq(d["g"][..., 0])
+    elif layout == "none":
+        g_ch, g_in = torch.zeros_like(d["g"]), None
+    else:
+        g_ch = d["g"]
+        g_in = seq(d["g"])
+    q, k, v, beta = seq(d["q"]), seq(d["k"]), seq(d["v"]), seq(d["beta"])
+    S = S0.cuda()
+    o = decode_tokens(q.cuda(), k.cuda(), v.cuda(), None if g_in is None else g_in.cuda(), beta.cuda(), S,
+                      gate_layout=layout)
+    Ss = S0.cuda()
+    steps = []
+    for t in range(T):
+        gl = None if g_in is None else g_in[:, t].contiguous().cuda()
+        steps.append(decode_step(d["q"][t].cuda(), d["k"][t].cuda(), d["v"][t].cuda(), gl,
+                                 d["beta"][t].cuda(), Ss, gate_layout=layout))
+    torch.cuda.synchronize()
+    assert torch.equal(o, torch.stack(steps, dim=1)) and torch.equal(S, Ss)
+    o_ref, S_ref = oracle.recurrent(q, k, v, seq(g_ch), beta, S0)
+    assert_close(f"tokens T={T} {layout} o", o.cpu(), o_ref, TOL[torch.bfloat16])
+    assert_close(f"tokens T={T} {layout} S", S.cpu(), S_ref, TOL[torch.bfloat16])
