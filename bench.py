@@ -168,6 +168,7 @@ def main():
     }
 
     out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, g, w, K, args.warmup)
+    out["varlen"] = bench_varlen(torch, g, w, K, args.warmup)
 
     if not args.no_decode:
         out["decode"] = bench_decode(torch, inputs, decode_step, dev, args.decode_steps)
@@ -199,6 +200,40 @@ def bench_gate_layouts(torch, ChunkPlan, g, w, steps, warmup):
         res[layout] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1)}
         del plan
     return res
+
+
+def bench_varlen(torch, g, w, steps, warmup):
+    """A packed batch of mixed lengths: the mid workload's tokens of batch row 0
+    and 1 (16384 tokens per head) cut into sequences of 64..2047 tokens (seeded),
+    one kda_chunk_fwd_varlen call."""
+    import numpy as np
+
+    from linear_attention_sequence_chunk_amd import chunk_fwd_varlen
+    T = 2 * w.T
+    rs = np.random.default_rng(11)
+    cuts = [0]
+    while cuts[-1] < T:
+        cuts.append(min(T, cuts[-1] + int(rs.integers(64, 2048))))
+    cu = torch.tensor(cuts, dtype=torch.int32, device=g["q"].device)
+    N = len(cuts) - 1
+    pk = {key: g[key][:2].reshape((T,) + tuple(g[key].shape[2:])).contiguous() for key in ("q", "k", "v", "g", "beta")}
+    ws = None
+    o, S = chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["g"], pk["beta"], cu, chunk_size=w.C)
+    for _ in range(warmup):
+        chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["g"], pk["beta"], cu, chunk_size=w.C, final_state=S)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["g"], pk["beta"], cu, chunk_size=w.C, final_state=S,
+                         workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"sequences": N, "tokens": T, "heads": w.H, "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(T / (ms / 1e3), 1),
+            "note": "includes a workspace allocation per call (torch caching allocator)"}
 
 
 def bench_decode(torch, inputs, decode_step, dev, steps):

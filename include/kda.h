@@ -177,6 +177,42 @@ int kda_chunk_intra_ex(const void *q, const void *k, const void *v,
                        void *stream, int C, int gate_layout);
 
 /*
+ * kda_chunk_fwd_varlen -- kda_chunk_fwd_ex over a packed batch of N sequences
+ * of different lengths (the chunkwise form of the chunk paragraph of the KimiK3
+ * essay and section 十六 of the explainer, applied to each sequence on its own:
+ * no chunk spans two sequences, and each sequence starts from its own state).
+ *   q, k          [T,H,dk] in_dtype   the N sequences one after another
+ *   v             [T,H,dv] in_dtype
+ *   g             [T,H,dk] / [T,H] fp32 or ignored, by gate_layout
+ *   beta          [T,H]    fp32
+ *   cu_seqlens    [N+1]    int32, DEVICE memory: sequence s is tokens
+ *                          cu_seqlens[s] .. cu_seqlens[s+1]-1; cu_seqlens[0] = 0,
+ *                          non-decreasing, cu_seqlens[N] = T.  Other values give
+ *                          unspecified results but every access stays in bounds
+ *                          (offsets are clamped to [0, T] on the device).
+ *   initial_state [N,H,dk,dv] fp32 or NULL;  final_state [N,H,dk,dv] fp32 or NULL
+ *   o             [T,H,dv] out_dtype
+ *   workspace     >= kda_chunk_varlen_workspace_bytes(N, T, H, dk, dv, in_dtype, C)
+ * Sequences of length 0 are allowed (their final state is their initial state).
+ * The result for each sequence is bitwise the same as a kda_chunk_fwd_ex call on
+ * that sequence alone.  Same rules as kda_chunk_fwd otherwise; cu_seqlens must
+ * not overlap o or final_state.
+ */
+int kda_chunk_fwd_varlen(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         const float *initial_state,
+                         void *o, float *final_state,
+                         const int *cu_seqlens, int N, int T, int H, int dk, int dv,
+                         int in_dtype, int out_dtype,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream, int C, int gate_layout);
+
+/* Bytes of device workspace kda_chunk_fwd_varlen needs (0 if unsupported);
+ * host-only.  Depends on N and T only, not on the individual lengths. */
+size_t kda_chunk_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
+                                        int in_dtype, int C);
+
+/*
  * kda_decode_step -- one token per sequence, state updated IN PLACE.
  *   q, k   [N,H,dk] in_dtype;  v [N,H,dv] in_dtype
  *   g      [N,H,dk] fp32 log-gate;  beta [N,H] fp32

@@ -106,6 +106,48 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=Non
     return o, fs
 
 
+def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, chunk_size=64, out_dtype=None,
+                     final_state=None, workspace=None, stream=None, gate_layout="channel"):
+    """Packed variable-length batch (kda_chunk_fwd_varlen).  q,k [T,H,dk],
+    v [T,H,dv], beta [T,H]: N sequences one after another, sequence s being
+    tokens cu_seqlens[s]..cu_seqlens[s+1]-1 (cu_seqlens: int32 [N+1] on the same
+    GPU); g fp32 [T,H,dk] ("channel"), [T,H] ("head") or None ("none");
+    initial_state [N,H,dk,dv] fp32 or None.  Returns (o [T,H,dv], final_state
+    [N,H,dk,dv] fp32)."""
+    _gate(gate_layout)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    _check_tensor("k", k, (T, H, dk), q.dtype, dev)
+    _check_tensor("v", v, (T, H, dv), q.dtype, dev)
+    _check_gate(g, gate_layout, (T, H), dk, dev)
+    _check_tensor("beta", beta, (T, H), torch.float32, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    o = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
+    L = _lib.lib()
+    nbytes = int(L.kda_chunk_varlen_workspace_bytes(N, T, H, dk, dv, _code(q.dtype), chunk_size))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = L.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                _ptr(final_state), _ptr(cu_seqlens), N, T, H, dk, dv, _code(q.dtype),
+                                _code(out_dtype), _ptr(workspace), workspace.numel(), _stream(stream),
+                                chunk_size, _gate(gate_layout))
+    _lib.check(st, "kda_chunk_fwd_varlen")
+    return o, final_state
+
+
 class ChunkPlan:
     """Pre-allocated outputs and workspace for repeated kda_chunk_fwd calls on the
     same sizes; ``run`` calls both stages, ``intra``/``chain`` one each."""

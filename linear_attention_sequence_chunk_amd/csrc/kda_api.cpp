@@ -67,6 +67,9 @@ struct ChunkCall {
     void* stream;
     int C;
     int gate;
+    const int* cu_seqlens = nullptr;   // packed variable-length batch (B = 1, N sequences)
+    int N = 0;
+    bool packed = false;
 };
 
 bool gate_ok(int g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
@@ -77,14 +80,17 @@ bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
 size_t esize(int d) { return d == KDA_BF16 ? 2 : 4; }
 
 int validate_chunk(const ChunkCall& c) {
-    if (c.B < 0 || c.T < 0 || c.H < 0) return KDA_ERR_SHAPE;
+    if (c.B < 0 || c.T < 0 || c.H < 0 || c.N < 0) return KDA_ERR_SHAPE;
     if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype) || !gate_ok(c.gate)) return KDA_ERR_UNSUPPORTED;
     if ((c.dk != 64 && c.dk != 128) || (c.dv != 64 && c.dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (c.C != 16 && c.C != 32 && c.C != 64 && c.C != 128) return KDA_ERR_UNSUPPORTED;
     if (!kda::chunk_supported(c.dk, c.dv, c.C, c.in_dtype == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
 
-    const size_t tok = (size_t)c.B * c.T * c.H;
-    const size_t nst = (size_t)c.B * c.H * c.dk * c.dv;
+    // token rows: [B,T,H] (fixed-length) or [T,H] (packed); states: [B,H] or [N,H]
+    const size_t tok = (size_t)(c.packed ? 1 : c.B) * c.T * c.H;
+    const size_t nst = (size_t)(c.packed ? c.N : c.B) * c.H * c.dk * c.dv;
+    if (c.packed && c.N > 0 && c.H > 0 && !c.cu_seqlens) return KDA_ERR_NULL;
+    if (c.packed && c.cu_seqlens && !aligned(c.cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
     const bool need_g = c.gate != KDA_GATE_NONE;
     if (tok > 0 && (!c.q || !c.k || !c.v || (need_g && !c.g) || !c.beta || !c.o)) return KDA_ERR_NULL;
     const float* g = need_g ? c.g : nullptr;            // g is not read without gates
@@ -99,23 +105,26 @@ int validate_chunk(const ChunkCall& c) {
     for (const void* p : p4)
         if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
 
-    const size_t need = kda::ws_layout(c.B, c.T, c.H, c.dk, c.dv, c.in_dtype == KDA_BF16, c.C).total;
-    if (tok > 0 && (!c.ws || c.ws_bytes < need)) return KDA_ERR_WORKSPACE;
+    const size_t need = c.packed ? kda::ws_layout_packed(c.N, c.T, c.H, c.dk, c.dv, c.in_dtype == KDA_BF16, c.C).total
+                                 : kda::ws_layout(c.B, c.T, c.H, c.dk, c.dv, c.in_dtype == KDA_BF16, c.C).total;
+    const bool uses_ws = c.packed ? (size_t)c.N * c.H > 0 : tok > 0;
+    if (uses_ws && (!c.ws || c.ws_bytes < need)) return KDA_ERR_WORKSPACE;
 
     const size_t ei = esize(c.in_dtype), eo = esize(c.out_dtype);
     const Range rq = range_of(c.q, tok * c.dk * ei), rk = range_of(c.k, tok * c.dk * ei),
                 rv = range_of(c.v, tok * c.dv * ei), rg = range_of(g, tok * gate_bytes(c.gate, c.dk)),
                 rb = range_of(c.beta, tok * 4), rs0 = range_of(c.s0, nst * 4),
                 ro = range_of(c.o, tok * c.dv * eo), rsT = range_of(c.sT, nst * 4),
-                rw = range_of(c.ws, tok > 0 ? need : 0);
-    const Range others_o[] = {rq, rk, rv, rg, rb, rs0, rsT, rw};
+                rw = range_of(c.ws, uses_ws ? need : 0),
+                rcu = range_of(c.packed ? c.cu_seqlens : nullptr, ((size_t)c.N + 1) * 4);
+    const Range others_o[] = {rq, rk, rv, rg, rb, rs0, rsT, rw, rcu};
     for (const Range& r : others_o)
         if (overlap(ro, r)) return KDA_ERR_ALIAS;
-    const Range others_s[] = {rq, rk, rv, rg, rb, rw};
+    const Range others_s[] = {rq, rk, rv, rg, rb, rw, rcu};
     for (const Range& r : others_s)
         if (overlap(rsT, r)) return KDA_ERR_ALIAS;
     if (c.sT && c.s0 && c.sT != c.s0 && overlap(rsT, rs0)) return KDA_ERR_ALIAS;
-    const Range others_w[] = {rq, rk, rv, rg, rb, rs0};
+    const Range others_w[] = {rq, rk, rv, rg, rb, rs0, rcu};
     for (const Range& r : others_w)
         if (overlap(rw, r)) return KDA_ERR_ALIAS;
     return KDA_OK;
@@ -126,7 +135,9 @@ kda::ChunkArgs to_args(const ChunkCall& c) {
     a.q = c.q; a.k = c.k; a.v = c.v; a.g = c.gate == KDA_GATE_NONE ? nullptr : c.g; a.beta = c.beta;
     a.gate = c.gate;
     a.s0 = c.s0; a.o = c.o; a.sT = c.sT;
-    a.B = c.B; a.T = c.T; a.H = c.H; a.dk = c.dk; a.dv = c.dv; a.C = c.C;
+    a.B = c.packed ? 1 : c.B; a.T = c.T; a.H = c.H; a.dk = c.dk; a.dv = c.dv; a.C = c.C;
+    a.cu_seqlens = c.packed ? c.cu_seqlens : nullptr;
+    a.N = c.packed ? c.N : 0;
     a.in_bf16 = c.in_dtype == KDA_BF16; a.out_bf16 = c.out_dtype == KDA_BF16;
     a.ws = c.ws; a.ws_bytes = c.ws_bytes;
     a.stream = (hipStream_t)c.stream;
@@ -138,11 +149,12 @@ enum Stages { STAGE_INTRA = 1, STAGE_CHAIN = 2 };
 int run_chunk(const ChunkCall& c, int stages) {
     int st = validate_chunk(c);
     if (st != KDA_OK) return st;
+    const long nseqh = (long)(c.packed ? c.N : c.B) * c.H;
+    const long nstate = nseqh * c.dk * c.dv;
+    if (nseqh == 0) return KDA_OK;                      // nothing to do: no device needed
     st = device_ready();
     if (st != KDA_OK) return st;
     const kda::ChunkArgs a = to_args(c);
-    const long nstate = (long)c.B * c.H * c.dk * c.dv;
-    if ((long)c.B * c.H == 0) return KDA_OK;
     if (c.T == 0) {
         // Empty sequence: the final state is the initial state (or zeros).
         if ((stages & STAGE_CHAIN) && c.sT && c.sT != c.s0) {
@@ -181,6 +193,26 @@ const char* kda_status_string(int s) {
         case KDA_ERR_HIP: return "no usable HIP device, or a HIP launch/execution error";
         default: return "unknown status";
     }
+}
+
+size_t kda_chunk_varlen_workspace_bytes(int N, int T, int H, int dk, int dv, int in_dtype, int C) {
+    if (N < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
+    if (C != 16 && C != 32 && C != 64 && C != 128) return 0;
+    if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
+    return kda::ws_layout_packed(N, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
+}
+
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* initial_state, void* o, float* final_state, const int* cu_seqlens,
+                         int N, int T, int H, int dk, int dv, int in_dtype, int out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream, int C, int gate_layout) {
+    ChunkCall c{q, k, v, g, beta, initial_state, o, final_state, 1, T, H, dk, dv, in_dtype,
+                out_dtype, workspace, workspace_bytes, stream, C, gate_layout};
+    c.cu_seqlens = cu_seqlens;
+    c.N = N;
+    c.packed = true;
+    return run_chunk(c, STAGE_INTRA | STAGE_CHAIN);
 }
 
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C) {

@@ -184,6 +184,76 @@ struct ChainCfg {
 template <typename T, typename TOut, int DK, int DV, int C, int DVS>
 constexpr bool chain_fits() { return DVS <= DV && ChainCfg<T, TOut, DK, DV, C, DVS>::FITS; }
 
+// ------------------------------------------------------------ chunk units
+// Fixed-length batches [B,T,H,d]: chunk n of sequence b and head h is unit
+// n * (B*H) + b*H + h (chunk-major).  Packed variable-length batches [T,H,d]
+// with token offsets cu_seqlens[N+1]: chunk j, counted over all sequences in
+// order, of head h is unit j*H + h; cu_chunks[s], built on the device, is the
+// first chunk of sequence s.  Offsets read from cu_seqlens are clamped to
+// [0, T] and made non-decreasing, so no access leaves the tensors whatever
+// they hold.
+struct UnitMap {
+    int T_len;                 // tokens per sequence (fixed) or in all (packed)
+    int H, C, NC;              // NC: chunks per sequence (fixed)
+    long BH;                   // B*H (fixed)
+    const int* cu_seqlens;     // NULL for fixed-length batches
+    const int* cu_chunks;
+    int nseq;
+};
+struct SeqRange { long tok_begin, tok_end, chunk0; int nchunks; };
+struct UnitPos { long tok0; int count, h; };
+
+__device__ inline long clamp_tok(long x, long lo, long hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Tokens and chunks of sequence s (b for fixed-length batches).
+__device__ inline SeqRange seq_range(const UnitMap& m, int s) {
+    SeqRange r;
+    if (!m.cu_seqlens) {
+        r.tok_begin = (long)s * m.T_len; r.tok_end = r.tok_begin + m.T_len;
+        r.chunk0 = 0; r.nchunks = m.NC;
+    } else {
+        r.tok_begin = clamp_tok(m.cu_seqlens[s], 0, m.T_len);
+        r.tok_end = clamp_tok(m.cu_seqlens[s + 1], r.tok_begin, m.T_len);
+        r.chunk0 = m.cu_chunks[s];
+        r.nchunks = m.cu_chunks[s + 1] - m.cu_chunks[s];
+    }
+    return r;
+}
+// Unit id of chunk n of (sequence s, head h); chunk0 from seq_range.
+__device__ inline long unit_id(const UnitMap& m, int s, int h, int n, long chunk0) {
+    return m.cu_seqlens ? (chunk0 + n) * m.H + h : (long)n * m.BH + (long)s * m.H + h;
+}
+// First token and token count of a unit; false for a unit past the last chunk
+// of a packed batch (the grid is sized for the most chunks there can be).
+__device__ inline bool unit_pos(const UnitMap& m, long unit, UnitPos& p) {
+    if (!m.cu_seqlens) {
+        const int n = (int)(unit / m.BH);
+        const long bh = unit % m.BH;
+        p.h = (int)(bh % m.H);
+        p.tok0 = (bh / m.H) * (long)m.T_len + (long)n * m.C;
+        p.count = m.T_len - n * m.C < m.C ? m.T_len - n * m.C : m.C;
+        return true;
+    }
+    const long j = unit / m.H;
+    p.h = (int)(unit % m.H);
+    if (j >= m.cu_chunks[m.nseq]) return false;
+    int lo = 0, hi = m.nseq;                     // cu_chunks[lo] <= j < cu_chunks[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (m.cu_chunks[mid] <= j) lo = mid; else hi = mid;
+    }
+    const SeqRange r = seq_range(m, lo);
+    p.tok0 = r.tok_begin + (j - r.chunk0) * m.C;
+    const long left = r.tok_end - p.tok0;
+    p.count = left < m.C ? (int)left : m.C;
+    return true;
+}
+
+// Host side: the map for a call (cu_chunks inside the workspace for packed batches).
+UnitMap unit_map(const ChunkArgs& a);
+long unit_count(const ChunkArgs& a);          // workgroups of the intra stage
+long seq_head_count(const ChunkArgs& a);      // (sequence, head) pairs of the chain stage
+
 // Stage 2 for each input dtype (kda_chunk_chain_bf16.hip, kda_chunk_chain_f32.hip).
 hipError_t run_chunk_chain_bf16(const ChunkArgs& a);
 hipError_t run_chunk_chain_f32(const ChunkArgs& a);

@@ -10,8 +10,7 @@ template <typename T, typename TOut, int DK, int DV, int C, int DVS>
 __global__ __launch_bounds__(256) void chunk_chain_kernel(
     const T* __restrict__ ws_qt, const T* __restrict__ ws_wk, const T* __restrict__ ws_kb,
     const T* __restrict__ ws_p, const float* __restrict__ ws_u, const float* __restrict__ ws_gam,
-    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT,
-    int T_len, int H, int NC) {
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um) {
     typedef ChainCfg<T, TOut, DK, DV, C, DVS> Cfg;
     constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, CK = Cfg::CK, NJ = Cfg::NJ, E16 = Cfg::E16;
     constexpr int NTW = Cfg::NTW, NTS = Cfg::NTS, KSTEP = Mma<T>::KSTEP;
@@ -35,7 +34,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     int sl;
     {
         const long nwg = (long)gridDim.x, id = blockIdx.x;
-        if (nwg % (8 * NSL) == 0) {
+        if (!um.cu_seqlens && nwg % (8 * NSL) == 0) {
             const long xcd = id % 8, local = id / 8;
             sl = (int)(local % NSL);
             bh = (local / NSL) * 8 + xcd;
@@ -45,8 +44,11 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         }
     }
     const int j0 = sl * DVS;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const long BH = (long)gridDim.x / NSL;       // workspace is chunk-major: (n, bh) -> n * BH + bh
+    // sequence (batch row, or packed sequence) and head; its chunks and tokens
+    const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
+    const SeqRange sr = seq_range(um, sq);
+    const int NC = sr.nchunks;
+    auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, n, sr.chunk0); };
 
     // ---- register prefetch of one chunk's operands (16-byte units), one
     // statically sized register array per operand
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
 
 #pragma unroll
     for (int d = 0; d < D; ++d)
-        if (d < NC) KDA_CHAIN_PREFETCH(d, (long)d * BH + bh);
+        if (d < NC) KDA_CHAIN_PREFETCH(d, unit_of(d));
 
     typedef typename Mma<T>::frag frag;
     const int fr = lane & 15, fk = (lane >> 4) * Mma<T>::KPL;     // fragment row, k offset
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         const int n = n0 + d;
         if (n >= NC) return;
         KDA_CHAIN_COMMIT(d);                                        // chunk n operands -> LDS
-        if (n + D < NC) KDA_CHAIN_PREFETCH(d, (long)(n + D) * BH + bh);   // in flight for D chunks
+        if (n + D < NC) KDA_CHAIN_PREFETCH(d, unit_of(n + D));   // in flight for D chunks
         __syncthreads();
 
         // ---- W = U - Wk S (to LDS, transposed) and the state part of O;
@@ -221,7 +223,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
                             sO[r * DVS + j] = from_f32<TOut>(accO[ri][J][e]);
                         } else {
                             const int tt = n * C + r;
-                            if (tt < T_len) o[(((long)b * T_len + tt) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[ri][J][e]);
+                            if (sr.tok_begin + tt < sr.tok_end)
+                                o[((sr.tok_begin + tt) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[ri][J][e]);
                         }
                     }
                 });
@@ -253,8 +256,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
             for (int u = tid; u < NUO; u += 256) {
                 const int r = (u * EO) / DVS, jj = (u * EO) % DVS;
                 const int tt = n * C + r;
-                if (tt < T_len)
-                    *reinterpret_cast<uint4*>(o + (((long)b * T_len + tt) * H + h) * DV + j0 + jj) =
+                if (sr.tok_begin + tt < sr.tok_end)
+                    *reinterpret_cast<uint4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj) =
                         *reinterpret_cast<const uint4*>(sO + r * DVS + jj);
             }
         }
@@ -288,15 +291,14 @@ static hipError_t launch_chain_dvs(const ChunkArgs& a) {
     if constexpr (!Cfg::FITS || DVS > DV) {
         return hipErrorInvalidValue;
     } else {
-        const int NC = (a.T + C - 1) / C;
-        const long nwg = (long)a.B * a.H * (DV / DVS);
+        const long nwg = seq_head_count(a) * (DV / DVS);
         if (nwg == 0) return hipSuccess;
-        const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, sizeof(T) == 2, C);
+        const WsLayout w = ws_layout_of(a);
         char* ws = (char*)a.ws;
         hipLaunchKernelGGL((chunk_chain_kernel<T, TOut, DK, DV, C, DVS>), dim3((unsigned)nwg), dim3(256), 0,
                            a.stream, (const T*)(ws + w.qt), (const T*)(ws + w.wk), (const T*)(ws + w.kb),
                            (const T*)(ws + w.p), (const float*)(ws + w.u), (const float*)(ws + w.gam),
-                           a.s0, (TOut*)a.o, a.sT, a.T, a.H, NC);
+                           a.s0, (TOut*)a.o, a.sT, unit_map(a));
         return hipGetLastError();
     }
 }
@@ -319,7 +321,7 @@ static int pick_dvs(long bh) {
 
 template <typename T, typename TOut, int DK, int DV, int C>
 static hipError_t launch_chain(const ChunkArgs& a) {
-    const int dvs = pick_dvs<T, TOut, DK, DV, C>((long)a.B * a.H);
+    const int dvs = pick_dvs<T, TOut, DK, DV, C>(seq_head_count(a));
     if (dvs == 64) return launch_chain_dvs<T, TOut, DK, DV, C, 64>(a);
     if (dvs == 32) return launch_chain_dvs<T, TOut, DK, DV, C, 32>(a);
     return launch_chain_dvs<T, TOut, DK, DV, C, 16>(a);

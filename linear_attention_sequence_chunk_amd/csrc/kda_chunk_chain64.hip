@@ -43,7 +43,7 @@ template <typename TOut, int DV, int DVS>
 __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
-    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, int T_len, int H, int NC) {
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
     constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, NSL = Cfg::NSL, LDK = Cfg::LDK, LDC = Cfg::LDC;
     constexpr int D = Cfg::DEPTH;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     int sl;
     {
         const long nwg = (long)gridDim.x, id = blockIdx.x;
-        if (nwg % (8 * NSL) == 0) {
+        if (!um.cu_seqlens && nwg % (8 * NSL) == 0) {
             const long xcd = id % 8, local = id / 8;
             sl = (int)(local % NSL);
             bh = (local / NSL) * 8 + xcd;
@@ -69,8 +69,11 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         }
     }
     const int j0 = sl * DVS;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const long BH = (long)gridDim.x / NSL;       // chunk-major workspace: (n, bh) -> n * BH + bh
+    // sequence (batch row, or packed sequence) and head; its chunks and tokens
+    const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
+    const SeqRange sr = seq_range(um, sq);
+    const int NC = sr.nchunks;
+    auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, n, sr.chunk0); };
 
     const bool wW = wave < 4;                    // uniform per wave
     const int R = wave & 3, ct = wave;
@@ -116,8 +119,8 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
 #pragma unroll
     for (int d = 0; d < D; ++d)
         if (d < NC) {
-            KDA_C64_PREFETCH_1(d, (long)d * BH + bh);
-            KDA_C64_PREFETCH_2(d, (long)d * BH + bh);
+            KDA_C64_PREFETCH_1(d, unit_of(d));
+            KDA_C64_PREFETCH_2(d, unit_of(d));
         }
 
     // ---- state rows 16*ct + 4(l/16) + e, columns j0 + 16 jt + l%16, fp32 in accumulators
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
                 *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
             }
         }
-        if (n + D < NC) KDA_C64_PREFETCH_1(d, (long)(n + D) * BH + bh);
+        if (n + D < NC) KDA_C64_PREFETCH_1(d, unit_of(n + D));
         __syncthreads();                                            // W^T complete
 
         // ---- phase 2: O waves O += P W (stored); all waves S = gam S + Kb^T W
@@ -199,8 +202,8 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
             for (int u = lane; u < NUO; u += 64) {
                 const int r = u / PPR, jj = (u % PPR) * EO;
                 const int tt = n * C + R * 16 + r;
-                if (tt < T_len)
-                    *reinterpret_cast<u32x4*>(o + (((long)b * T_len + tt) * H + h) * DV + j0 + jj) =
+                if (sr.tok_begin + tt < sr.tok_end)
+                    *reinterpret_cast<u32x4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj) =
                         *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
             }
         }
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
             }
         }
         write_state_operand();                                      // read only after the next barrier
-        if (n + D < NC) KDA_C64_PREFETCH_2(d, (long)(n + D) * BH + bh);
+        if (n + D < NC) KDA_C64_PREFETCH_2(d, unit_of(n + D));
       });
     }
 
@@ -240,22 +243,21 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
 template <typename TOut, int DV, int DVS>
 static hipError_t launch_chain64_dvs(const ChunkArgs& a) {
     constexpr int C = 64, DK = 128;
-    const int NC = (a.T + C - 1) / C;
-    const long nwg = (long)a.B * a.H * (DV / DVS);
+    const long nwg = seq_head_count(a) * (DV / DVS);
     if (nwg == 0) return hipSuccess;
-    const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, true, C);
+    const WsLayout w = ws_layout_of(a);
     char* ws = (char*)a.ws;
     hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                        (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
                        (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam),
-                       a.s0, (TOut*)a.o, a.sT, a.T, a.H, NC);
+                       a.s0, (TOut*)a.o, a.sT, unit_map(a));
     return hipGetLastError();
 }
 
 // Slice width: 32 value columns when that gives at least 256 workgroups, else 16.
 template <typename TOut, int DV>
 static hipError_t launch_chain64(const ChunkArgs& a) {
-    const long bh = (long)a.B * a.H;
+    const long bh = seq_head_count(a);
     if (bh * (DV / 32) >= 256) return launch_chain64_dvs<TOut, DV, 32>(a);
     return launch_chain64_dvs<TOut, DV, 16>(a);
 }

@@ -10,7 +10,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     T* __restrict__ ws_qt, T* __restrict__ ws_wk, T* __restrict__ ws_kb, T* __restrict__ ws_p,
-    float* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC, int gate) {
+    float* __restrict__ ws_u, float* __restrict__ ws_gam, UnitMap um, int gate) {
     typedef IntraCfg<T, DK, DV, C> Cfg;
     constexpr int NB = Cfg::NB, NP = Cfg::NP, HR = Cfg::HR, LDK = Cfg::LDK, LDA = Cfg::LDA,
                   LDT = Cfg::LDT, CK = Cfg::CK;
@@ -27,16 +27,15 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // chunk-major order: workgroups running together cover all heads of the same
-    // tokens, so every token row of q, k, v, g is read whole and at once
+    // chunk-major order (fixed-length batches): workgroups running together cover
+    // all heads of the same tokens, so every token row of q, k, v, g is read whole
     const long ch = blockIdx.x;
-    const long BH = (long)gridDim.x / NC;
-    const int n = (int)(ch / BH);
-    const long bh = ch % BH;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const int t0 = n * C;
-    auto grow = [&](int t) -> long { return ((long)b * T_len + (t0 + t)) * H + h; };
-    auto valid = [&](int t) -> bool { return t0 + t < T_len; };
+    UnitPos up;
+    if (!unit_pos(um, ch, up)) return;             // past the last chunk of a packed batch
+    const int H = um.H, h = up.h, cnt = up.count;
+    const long tok0 = up.tok0;
+    auto grow = [&](int t) -> long { return (tok0 + t) * H + h; };
+    auto valid = [&](int t) -> bool { return t < cnt; };
 
     // ---------------------------------------------------------------- phase 0
     // Block-local inclusive prefix sums of the clamped log-gate (a1), block totals.
@@ -426,7 +425,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     bf16* __restrict__ ws_qt, bf16* __restrict__ ws_wk, bf16* __restrict__ ws_kb, bf16* __restrict__ ws_p,
-    bf16* __restrict__ ws_u, float* __restrict__ ws_gam, int T_len, int H, int NC, int gate) {
+    bf16* __restrict__ ws_u, float* __restrict__ ws_gam, UnitMap um, int gate) {
     typedef Intra64Cfg<DV> Cfg;
     constexpr int C = 64, NB = 4, DK = 128, NT = 512, NW = 8, HALF = 64;
     constexpr int LDH = Cfg::LDH, LDT = Cfg::LDT, LDA = Cfg::LDA;
@@ -440,16 +439,15 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     auto blk = [&](int b) { return sOp + b * 16 * LDH; };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // chunk-major order: workgroups running together cover all heads of the same
-    // tokens, so every token row of q, k, v, g is read whole and at once
+    // chunk-major order (fixed-length batches): workgroups running together cover
+    // all heads of the same tokens, so every token row of q, k, v, g is read whole
     const long ch = blockIdx.x;
-    const long BH = (long)gridDim.x / NC;
-    const int n = (int)(ch / BH);
-    const long bh = ch % BH;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const int t0 = n * C;
-    auto grow = [&](int t) -> long { return ((long)b * T_len + (t0 + t)) * H + h; };
-    auto valid = [&](int t) -> bool { return t0 + t < T_len; };
+    UnitPos up;
+    if (!unit_pos(um, ch, up)) return;             // past the last chunk of a packed batch
+    const int H = um.H, h = up.h, cnt = up.count;
+    const long tok0 = up.tok0;
+    auto grow = [&](int t) -> long { return (tok0 + t) * H + h; };
+    auto valid = [&](int t) -> bool { return t < cnt; };
 
     // unit of pass p: wave -> (16-row block R, 32-channel group), lane -> (row, 8 channels)
     const int R = wave >> 1, rr = lane & 15, t = R * 16 + rr;
@@ -824,12 +822,11 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 // ================================================================ host side
 static inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
+static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_bf16, int C) {
     WsLayout w{};
     const size_t es = in_bf16 ? 2 : 4;
-    const size_t NC = (size_t)((T + C - 1) / C);
-    const size_t nch = (size_t)B * H * NC;
     size_t off = 0;
+    w.cu = off; off = al256(off + header);
     w.qt = off; off = al256(off + nch * C * dk * es);
     w.wk = off; off = al256(off + nch * C * dk * es);
     w.kb = off; off = al256(off + nch * C * dk * es);
@@ -840,21 +837,86 @@ WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
     return w;
 }
 
+WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
+    const size_t NC = (size_t)((T + C - 1) / C);
+    return layout_units((size_t)B * H * NC, 0, dk, dv, in_bf16, C);
+}
+
+WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C) {
+    const size_t chunks = (size_t)((T + C - 1) / C) + (size_t)N;
+    return layout_units(chunks * H, ((size_t)N + 1) * 4, dk, dv, in_bf16, C);
+}
+
+WsLayout ws_layout_of(const ChunkArgs& a) {
+    return a.cu_seqlens ? ws_layout_packed(a.N, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C)
+                        : ws_layout(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C);
+}
+
+UnitMap unit_map(const ChunkArgs& a) {
+    UnitMap m;
+    m.T_len = a.T; m.H = a.H; m.C = a.C;
+    m.NC = (a.T + a.C - 1) / a.C;
+    m.BH = (long)a.B * a.H;
+    m.cu_seqlens = a.cu_seqlens;
+    m.cu_chunks = a.cu_seqlens ? reinterpret_cast<const int*>((const char*)a.ws + ws_layout_of(a).cu) : nullptr;
+    m.nseq = a.N;
+    return m;
+}
+
+long unit_count(const ChunkArgs& a) {
+    if (a.cu_seqlens) return ((long)(a.T + a.C - 1) / a.C + a.N) * a.H;
+    return (long)a.B * a.H * ((a.T + a.C - 1) / a.C);
+}
+
+long seq_head_count(const ChunkArgs& a) { return (long)(a.cu_seqlens ? a.N : a.B) * a.H; }
+
+// Chunk offsets of a packed batch: cu_chunks[s] = sum over s' < s of the chunk
+// count of sequence s' (its clamped token range, rounded up to chunks).
+// One workgroup of 1024 threads, in blocks of 1024 sequences.
+__global__ __launch_bounds__(1024) void packed_chunks_kernel(const int* __restrict__ cu_seqlens, int nseq,
+                                                             int T_len, int C, int* __restrict__ cu_chunks) {
+    __shared__ int sc[1024];
+    __shared__ int carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) { carry = 0; cu_chunks[0] = 0; }
+    __syncthreads();
+    for (int base = 0; base < nseq; base += 1024) {
+        const int s = base + tid;
+        int c = 0;
+        if (s < nseq) {
+            const long b0 = clamp_tok(cu_seqlens[s], 0, T_len);
+            const long e0 = clamp_tok(cu_seqlens[s + 1], b0, T_len);
+            c = (int)((e0 - b0 + C - 1) / C);
+        }
+        sc[tid] = c;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {        // inclusive scan
+            const int x = tid >= off ? sc[tid - off] : 0;
+            __syncthreads();
+            sc[tid] += x;
+            __syncthreads();
+        }
+        if (s < nseq) cu_chunks[s + 1] = carry + sc[tid];
+        __syncthreads();
+        if (tid == 0) carry += sc[1023];
+        __syncthreads();
+    }
+}
+
 template <typename T, int DK, int DV, int C>
 static hipError_t launch_intra(const ChunkArgs& a) {
     typedef IntraCfg<T, DK, DV, C> Cfg;
     if constexpr (!Cfg::FITS) {
         return hipErrorInvalidValue;
     } else {
-        const int NC = (a.T + C - 1) / C;
-        const long nch = (long)a.B * a.H * NC;
+        const long nch = unit_count(a);
         if (nch == 0) return hipSuccess;
-        const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, sizeof(T) == 2, C);
+        const WsLayout w = ws_layout_of(a);
         char* ws = (char*)a.ws;
         hipLaunchKernelGGL((chunk_intra_kernel<T, DK, DV, C>), dim3((unsigned)nch), dim3(256), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta,
                            (T*)(ws + w.qt), (T*)(ws + w.wk), (T*)(ws + w.kb), (T*)(ws + w.p),
-                           (float*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC, a.gate);
+                           (float*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate);
         return hipGetLastError();
     }
 }
@@ -880,15 +942,14 @@ bool chunk_supported(int dk, int dv, int C, bool in_bf16) {
 template <int DV>
 static hipError_t launch_intra64(const ChunkArgs& a) {
     constexpr int DK = 128;
-    const int NC = (a.T + 63) / 64;
-    const long nch = (long)a.B * a.H * NC;
+    const long nch = unit_count(a);
     if (nch == 0) return hipSuccess;
-    const WsLayout w = ws_layout(a.B, a.T, a.H, DK, DV, true, 64);
+    const WsLayout w = ws_layout_of(a);
     char* ws = (char*)a.ws;
     hipLaunchKernelGGL((chunk_intra64_kernel<DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
                        (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
-                       (bf16*)(ws + w.u), (float*)(ws + w.gam), a.T, a.H, NC, a.gate);
+                       (bf16*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate);
     return hipGetLastError();
 }
 
@@ -910,6 +971,13 @@ static hipError_t intra_dims(const ChunkArgs& a) {
     return a.dv == 64 ? intra_c<T, 128, 64>(a) : intra_c<T, 128, 128>(a);
 }
 hipError_t run_chunk_intra(const ChunkArgs& a) {
+    if (a.cu_seqlens && a.N > 0) {
+        int* cu_chunks = reinterpret_cast<int*>((char*)a.ws + ws_layout_of(a).cu);
+        hipLaunchKernelGGL(packed_chunks_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.N, a.T,
+                           a.C, cu_chunks);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     return a.in_bf16 ? intra_dims<bf16>(a) : intra_dims<float>(a);
 }
 

@@ -33,6 +33,10 @@ struct ChunkArgs {
     int gate;
     void* ws; size_t ws_bytes;
     hipStream_t stream;
+    // packed variable-length batch: B = 1, T = total tokens, N sequences with
+    // token offsets cu_seqlens[N+1] (device memory); NULL for [B,T,H,d] batches
+    const int* cu_seqlens = nullptr;
+    int N = 0;
 };
 
 // The hot configuration (bf16 inputs, C = 64, dk = 128) has its own pair of
@@ -44,9 +48,14 @@ inline bool hot_config(bool in_bf16, int dk, int C) { return in_bf16 && dk == 12
 //   Qt [C][dk] in, Wk [C][dk] in, Kb^T [dk][C] in, P [C][C] in, U [C][dv], gam [dk] fp32
 // with U in fp32, except in the hot configuration (bf16)
 struct WsLayout {
-    size_t qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
+    size_t cu, qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
 };
 WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C);
+// Packed variable-length batch of N sequences, T tokens in all: room for every
+// possible chunk (at most ceil(T/C) + N) and, first, the chunk offsets int [N+1].
+WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C);
+// The layout for a call's arguments (fixed-length or packed).
+WsLayout ws_layout_of(const ChunkArgs& a);
 
 // True when an instantiation exists for these sizes (dk, dv, C, dtype).
 bool chunk_supported(int dk, int dv, int C, bool in_bf16);

@@ -222,3 +222,34 @@ def test_python_binding_refuses_cpu_tensors():
         chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1))
     with pytest.raises(ValueError):
         decode_step(x[0], x[0], x[0], x[0], torch.zeros(4, 1), torch.zeros(4, 1, 64, 64))
+
+
+def test_varlen_validation_codes():
+    L = _lib.lib()
+    f = Fake()
+    N, T, H, dk, dv = 4, 300, 2, 128, 128
+    tok = T * H
+    wsb = L.kda_chunk_varlen_workspace_bytes(N, T, H, dk, dv, _lib.BF16, 64)
+    assert wsb > L.kda_chunk_fwd_workspace_bytes(1, T, H, dk, dv, _lib.BF16, 64)   # room for N extra chunks
+    assert L.kda_chunk_varlen_workspace_bytes(N, T, H, 96, dv, _lib.BF16, 64) == 0
+    a = dict(q=f(tok * dk * 2), k=f(tok * dk * 2), v=f(tok * dv * 2), g=f(tok * dk * 4), beta=f(tok * 4),
+             s0=f(N * H * dk * dv * 4), o=f(tok * dv * 2), sT=f(N * H * dk * dv * 4), cu=f((N + 1) * 4),
+             N=N, T=T, H=H, ws=f(wsb), wsb=wsb, gate=0)
+
+    def call(x):
+        return L.kda_chunk_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], x["o"], x["sT"],
+                                      x["cu"], x["N"], x["T"], x["H"], dk, dv, _lib.BF16, _lib.BF16,
+                                      x["ws"], x["wsb"], None, 64, x["gate"])
+    cases = [(dict(N=-1), SHAPE), (dict(gate=5), UNSUP), (dict(cu=None), NULL), (dict(cu=a["cu"] + 2), MISAL),
+             (dict(wsb=wsb - 1), WS), (dict(o=a["cu"]), ALIAS), (dict(sT=a["cu"]), ALIAS),
+             (dict(ws=a["cu"] - 16), ALIAS), (dict(g=None), NULL)]
+    for change, code in cases:
+        b = dict(a); b.update(change)
+        assert call(b) == code, (change, code)
+    # nothing to do: no sequences, or no heads
+    assert L.kda_chunk_fwd_varlen(None, None, None, None, None, None, None, None, None, 0, 0, 2, dk, dv,
+                                  1, 1, None, 0, None, 64, 0) == OK
+    if not HAS_GPU:
+        assert call(a) == HIP
+        b = dict(a); b["g"] = None; b["gate"] = 2
+        assert call(b) == HIP
