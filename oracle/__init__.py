@@ -50,6 +50,8 @@ def _lib():
         lib.kda_oracle_recurrent.restype = None
         lib.kda_oracle_last_threads.argtypes = []
         lib.kda_oracle_last_threads.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [ctypes.c_int] * 5 + [dp] * 14 + [ctypes.c_int, ctypes.c_int]
+        lib.kda_oracle_backward.restype = None
         _LIB = lib
     return _LIB
 
@@ -90,6 +92,20 @@ def recurrent(q, k, v, g, beta, S0=None, delta=True, dump_u=False, nthreads=0):
                                 _ptr(beta), _ptr(S0), _ptr(o), _ptr(ST),
                                 1 if delta else 0, _ptr(u), int(nthreads))
     return (o, ST, u) if dump_u else (o, ST)
+
+
+def backward(q, k, v, g, beta, S0=None, dO=None, dST=None, seg=64, nthreads=0):
+    """fp64 adjoint of ``recurrent`` for L = sum(dO * o) + sum(dST * S_T).
+    Returns dict(dq, dk, dv, dg, dbeta, dS0) as fp64 arrays."""
+    q, k, v, g, beta, S0, dO, dST = (to_f64(a) for a in (q, k, v, g, beta, S0, dO, dST))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    out = {"dq": np.zeros((B, T, H, dk)), "dk": np.zeros((B, T, H, dk)), "dv": np.zeros((B, T, H, dv)),
+           "dg": np.zeros((B, T, H, dk)), "dbeta": np.zeros((B, T, H)), "dS0": np.zeros((B, H, dk, dv))}
+    _lib().kda_oracle_backward(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                               _ptr(dO), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                               _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dS0"]), int(seg), int(nthreads))
+    return out
 
 
 def last_threads() -> int:

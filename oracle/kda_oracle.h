@@ -50,6 +50,21 @@ void kda_oracle_recurrent(int B, int T, int H, int dk, int dv,
 /* Number of threads the last kda_oracle_recurrent call ran with. */
 int kda_oracle_last_threads(void);
 
+/* Reverse-mode derivative (the adjoint) of kda_oracle_recurrent (delta = 1) for
+ * the scalar  L = sum(dO * o) + sum(dST * S_T):  given the output cotangents dO
+ * [B,T,H,dv] and dST [B,H,dk,dv] (either may be NULL: zeros), returns dq, dk, dg
+ * [B,T,H,dk], dv [B,T,H,dv], dbeta [B,T,H] and dS0 [B,H,dk,dv] (any output may
+ * be NULL).  It applies, token by token in reverse order, the derivative of each
+ * step of the recurrence (output read, write, error, read, decay).  States are
+ * kept at every `seg`-th token and the states inside a segment are recomputed
+ * from it (seg <= 0 means 64).  Parallel over (b,h) like the forward. */
+void kda_oracle_backward(int B, int T, int H, int dk, int dv,
+                         const double *q, const double *k, const double *v,
+                         const double *g, const double *beta, const double *S0,
+                         const double *dO, const double *dST,
+                         double *dq, double *dk_out, double *dv_out, double *dg,
+                         double *dbeta, double *dS0, int seg, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
