@@ -213,6 +213,42 @@ size_t kda_chunk_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
                                         int in_dtype, int C);
 
 /*
+ * kda_chunk_bwd -- the backward pass of kda_chunk_fwd_ex (training): for the
+ * scalar L = sum(dO * o) + sum(dST * final_state) it returns the gradients of L
+ * with respect to every input.  The chunkwise form is trained by the same
+ * chunking (chunk paragraph of the KimiK3 essay; sections 十六 and 十七 of the
+ * explainer): a recurrence over the chunks in reverse order carries the
+ * cotangent of the state, and every chunk's gradients are then formed in
+ * parallel.  The forward stages are run again inside the call.
+ *   q, k, v, g, beta, initial_state   as for kda_chunk_fwd_ex (initial_state may be NULL)
+ *   dO            [B,T,H,dv] fp32     cotangent of o
+ *   dST           [B,H,dk,dv] fp32    cotangent of the final state, or NULL (zeros)
+ *   dq, dk        [B,T,H,dk] fp32     outputs
+ *   dv            [B,T,H,dv] fp32
+ *   dg            [B,T,H,dk] / [B,T,H] fp32 by gate_layout (NULL allowed without gates);
+ *                                    zero where the forward floored the log-gate
+ *   dbeta         [B,T,H]    fp32
+ *   dS0           [B,H,dk,dv] fp32 or NULL
+ *   workspace     >= kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, in_dtype, C)
+ * Supported: C in {16, 32, 64}; dk, dv in {64, 128}; in_dtype BF16 or F32 (the
+ * gradient arithmetic is fp32).  Outputs must not overlap any input, the
+ * workspace or each other.  Alignment: q, k, v and the workspace 16 bytes,
+ * per-channel g 8 bytes, everything else 4 bytes.  Deterministic (no
+ * floating-point atomics).
+ */
+int kda_chunk_bwd(const void *q, const void *k, const void *v,
+                  const float *g, const float *beta, const float *initial_state,
+                  const float *dO, const float *dST,
+                  float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                  int B, int T, int H, int dk_size, int dv_size, int in_dtype,
+                  void *workspace, size_t workspace_bytes,
+                  void *stream, int C, int gate_layout);
+
+/* Bytes of device workspace kda_chunk_bwd needs (0 if unsupported); host-only. */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                     int in_dtype, int C);
+
+/*
  * kda_decode_step -- one token per sequence, state updated IN PLACE.
  *   q, k   [N,H,dk] in_dtype;  v [N,H,dv] in_dtype
  *   g      [N,H,dk] fp32 log-gate;  beta [N,H] fp32

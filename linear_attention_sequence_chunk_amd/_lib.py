@@ -19,7 +19,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPP
 SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes",
            "kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain", "kda_decode_step",
            "kda_chunk_fwd_ex", "kda_chunk_intra_ex", "kda_decode_step_ex", "kda_decode_tokens",
-           "kda_chunk_fwd_varlen", "kda_chunk_varlen_workspace_bytes")
+           "kda_chunk_fwd_varlen", "kda_chunk_varlen_workspace_bytes",
+           "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes")
 
 
 class KdaError(RuntimeError):
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_varlen.restype = _ci
         L.kda_chunk_varlen_workspace_bytes.argtypes = [_ci] * 7
         L.kda_chunk_varlen_workspace_bytes.restype = _sz
+        L.kda_chunk_bwd.argtypes = [_vp] * 14 + [_ci] * 6 + [_vp, _sz, _vp, _ci, _ci]
+        L.kda_chunk_bwd.restype = _ci
+        L.kda_chunk_bwd_workspace_bytes.argtypes = [_ci] * 7
+        L.kda_chunk_bwd_workspace_bytes.restype = _sz
         _LIB = L
     return _LIB
 

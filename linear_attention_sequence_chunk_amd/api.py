@@ -148,6 +148,47 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, chunk_siz
     return o, final_state
 
 
+def chunk_bwd(q, k, v, g, beta, dO, initial_state=None, dST=None, chunk_size=64, gate_layout="channel",
+              workspace=None, stream=None):
+    """Backward pass (kda_chunk_bwd): gradients of L = sum(dO * o) + sum(dST * S_T)
+    for the forward chunk_fwd(q, k, v, g, beta, initial_state, gate_layout=...).
+    dO [B,T,H,dv] fp32, dST [B,H,dk,dv] fp32 or None.  Returns a dict of fp32
+    tensors dq, dk, dv, dg (None without gates), dbeta, dS0."""
+    _gate(gate_layout)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    _check_tensor("k", k, (B, T, H, dk), q.dtype, dev)
+    _check_tensor("v", v, (B, T, H, dv), q.dtype, dev)
+    _check_gate(g, gate_layout, (B, T, H), dk, dev)
+    _check_tensor("beta", beta, (B, T, H), torch.float32, dev)
+    _check_tensor("dO", dO, (B, T, H, dv), torch.float32, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
+    if dST is not None:
+        _check_tensor("dST", dST, (B, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+           "dv": torch.empty((B, T, H, dv), **f32), "dbeta": torch.empty((B, T, H), **f32),
+           "dS0": torch.empty((B, H, dk, dv), **f32),
+           "dg": None if gate_layout == "none" else
+           torch.empty((B, T, H, dk) if gate_layout == "channel" else (B, T, H), **f32)}
+    L = _lib.lib()
+    nbytes = int(L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _code(q.dtype), chunk_size))
+    if nbytes == 0 and B * T * H > 0:
+        raise _lib.KdaError(3, "kda_chunk_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = L.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dO),
+                         _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                         _ptr(out["dbeta"]), _ptr(out["dS0"]), B, T, H, dk, dv, _code(q.dtype),
+                         _ptr(workspace), workspace.numel(), _stream(stream), chunk_size, _gate(gate_layout))
+    _lib.check(st, "kda_chunk_bwd")
+    return out
+
+
 class ChunkPlan:
     """Pre-allocated outputs and workspace for repeated kda_chunk_fwd calls on the
     same sizes; ``run`` calls both stages, ``intra``/``chain`` one each."""

@@ -215,6 +215,84 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const floa
     return run_chunk(c, STAGE_INTRA | STAGE_CHAIN);
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C) {
+    if (B < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    if (!kda::bwd_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
+    if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
+    return kda::bwd_layout(B, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* initial_state, const float* dO, const float* dST, float* dq, float* dk_out,
+                  float* dv_out, float* dg, float* dbeta, float* dS0, int B, int T, int H, int dk, int dv,
+                  int in_dtype, void* workspace, size_t workspace_bytes, void* stream, int C, int gate_layout) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (!dtype_ok(in_dtype) || !gate_ok(gate_layout)) return KDA_ERR_UNSUPPORTED;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
+    if (!kda::bwd_supported(dk, dv, C, in_dtype == KDA_BF16) || !kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    const size_t tok = (size_t)B * T * H, nst = (size_t)B * H * dk * dv;
+    const bool need_g = gate_layout != KDA_GATE_NONE;
+    if (!need_g) g = nullptr;
+    if (!need_g) dg = nullptr;
+    if (tok > 0 && (!q || !k || !v || (need_g && (!g || !dg)) || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta))
+        return KDA_ERR_NULL;
+    const void* p16[4] = {q, k, v, workspace};
+    for (const void* p : p16)
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if (g && !aligned(g, gate_layout == KDA_GATE_CHANNEL ? 8 : 4)) return KDA_ERR_MISALIGNED;
+    const void* p4[11] = {beta, initial_state, dO, dST, dq, dk_out, dv_out, dg, dbeta, dS0, nullptr};
+    for (const void* p : p4)
+        if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
+    const kda::BwdLayout L = kda::bwd_layout(B, T, H, dk, dv, in_dtype == KDA_BF16, C);
+    if (tok > 0 && (!workspace || workspace_bytes < L.total)) return KDA_ERR_WORKSPACE;
+    const size_t ei = esize(in_dtype), gb = gate_bytes(gate_layout, dk);
+    const Range rq = range_of(q, tok * dk * ei), rk = range_of(k, tok * dk * ei), rv = range_of(v, tok * dv * ei),
+                rg = range_of(g, tok * gb), rb = range_of(beta, tok * 4), rs0 = range_of(initial_state, nst * 4),
+                rdo = range_of(dO, tok * dv * 4), rdst = range_of(dST, nst * 4), rw = range_of(workspace, tok > 0 ? L.total : 0);
+    const Range outs[] = {range_of(dq, tok * dk * 4), range_of(dk_out, tok * dk * 4), range_of(dv_out, tok * dv * 4),
+                          range_of(dg, tok * gb), range_of(dbeta, tok * 4), range_of(dS0, nst * 4)};
+    const Range ins[] = {rq, rk, rv, rg, rb, rs0, rdo, rdst, rw};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return KDA_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return KDA_ERR_ALIAS;
+    }
+    const Range fwd_in[] = {rq, rk, rv, rg, rb, rs0, rdo, rdst};
+    for (const Range& r : fwd_in)
+        if (overlap(rw, r)) return KDA_ERR_ALIAS;
+
+    const long nseqh = (long)B * H;
+    if (nseqh == 0) return KDA_OK;
+    int st = device_ready();
+    if (st != KDA_OK) return st;
+    if (T == 0) {                                          // dS0 = dS_T: nothing happens in between
+        if (dS0) {
+            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0,
+                               (hipStream_t)stream, dST, dS0, (long)nst);
+            return finish(hipGetLastError(), (hipStream_t)stream);
+        }
+        return KDA_OK;
+    }
+    char* ws = (char*)workspace;
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.s0 = initial_state; a.o = nullptr; a.sT = nullptr;
+    a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.C = C;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = false; a.gate = gate_layout;
+    a.ws = ws; a.ws_bytes = L.fwd.total; a.stream = (hipStream_t)stream;
+    a.generic = true;
+    a.ck_t = (float*)(ws + L.t); a.ck_a = (float*)(ws + L.a);
+    a.ck_state = (float*)(ws + L.state); a.ck_w = (float*)(ws + L.w);
+    if (kda::run_chunk_intra(a) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::run_chunk_chain(a) != hipSuccess) return KDA_ERR_HIP;
+    kda::BwdArgs bw;
+    bw.fwd = a; bw.dO = dO; bw.dST = dST;
+    bw.dq = dq; bw.dk = dk_out; bw.dv = dv_out; bw.dg = dg; bw.dbeta = dbeta; bw.dS0 = dS0;
+    bw.ck_dS = (float*)(ws + L.dS); bw.ck_dW = (float*)(ws + L.dW); bw.scratch = (float*)(ws + L.scr);
+    return finish(kda::run_chunk_bwd_stages(bw), (hipStream_t)stream);
+}
+
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C) {
     if (B < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;

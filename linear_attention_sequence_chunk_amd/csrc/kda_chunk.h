@@ -260,7 +260,7 @@ hipError_t run_chunk_chain_f32(const ChunkArgs& a);
 
 // The hot configuration has its own pair of kernels, chunk_intra64_kernel and
 // chunk_chain64_kernel, and its own workspace format; both stages decide with this.
-inline bool hot_layout(const ChunkArgs& a) { return hot_config(a.in_bf16, a.dk, a.C); }
+inline bool hot_layout(const ChunkArgs& a) { return hot_config(a.in_bf16, a.dk, a.C) && !a.generic; }
 hipError_t run_chunk_chain64(const ChunkArgs& a);   // kda_chunk_chain64.hip
 
 }  // namespace kda

@@ -10,7 +10,11 @@ template <typename T, typename TOut, int DK, int DV, int C, int DVS>
 __global__ __launch_bounds__(256) void chunk_chain_kernel(
     const T* __restrict__ ws_qt, const T* __restrict__ ws_wk, const T* __restrict__ ws_kb,
     const T* __restrict__ ws_p, const float* __restrict__ ws_u, const float* __restrict__ ws_gam,
-    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um) {
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um,
+    float* __restrict__ ck_state, float* __restrict__ ck_w) {
+    // ck_state / ck_w (NULL in the forward pass): per unit, the fp32 state at the
+    // chunk's start [dk][dv] and the chunk's W = U - Wk S [C][dv], kept for the
+    // backward pass.  o may be NULL (outputs not stored).
     typedef ChainCfg<T, TOut, DK, DV, C, DVS> Cfg;
     constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, CK = Cfg::CK, NJ = Cfg::NJ, E16 = Cfg::E16;
     constexpr int NTW = Cfg::NTW, NTS = Cfg::NTS, KSTEP = Mma<T>::KSTEP;
@@ -166,6 +170,19 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
         constexpr int d = DI;
         const int n = n0 + d;
         if (n >= NC) return;
+        if (ck_state) {                                             // the state this chunk starts from
+            float* cks = ck_state + unit_of(n) * (long)DK * DV;
+            static_for<Cfg::SPW>([&](auto SI) {
+                constexpr int si = SI;
+                const int ct = wave + 4 * si;
+                static_for<NJ>([&](auto JI) {
+                    constexpr int jt = JI;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        cks[(ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + (lane & 15)] = accS[si][jt][e];
+                });
+            });
+        }
         KDA_CHAIN_COMMIT(d);                                        // chunk n operands -> LDS
         if (n + D < NC) KDA_CHAIN_PREFETCH(d, unit_of(n + D));   // in flight for D chunks
         __syncthreads();
@@ -194,6 +211,11 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
                     const int j = J * 16 + (lane & 15), r = R * 16 + 4 * (lane >> 4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) sWT[j * LDC + r + e] = from_f32<T>(sU[(r + e) * DVS + j] - wk[J][e]);
+                    if (ck_w) {
+                        float* ckw = ck_w + unit_of(n) * (long)C * DV;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ckw[(r + e) * (long)DV + j0 + j] = sU[(r + e) * DVS + j] - wk[J][e];
+                    }
                 });
             }
         });
@@ -223,7 +245,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
                             sO[r * DVS + j] = from_f32<TOut>(accO[ri][J][e]);
                         } else {
                             const int tt = n * C + r;
-                            if (sr.tok_begin + tt < sr.tok_end)
+                            if (o && sr.tok_begin + tt < sr.tok_end)
                                 o[((sr.tok_begin + tt) * H + h) * DV + j0 + j] = from_f32<TOut>(accO[ri][J][e]);
                         }
                     }
@@ -256,7 +278,7 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
             for (int u = tid; u < NUO; u += 256) {
                 const int r = (u * EO) / DVS, jj = (u * EO) % DVS;
                 const int tt = n * C + r;
-                if (sr.tok_begin + tt < sr.tok_end)
+                if (o && sr.tok_begin + tt < sr.tok_end)
                     *reinterpret_cast<uint4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj) =
                         *reinterpret_cast<const uint4*>(sO + r * DVS + jj);
             }
@@ -298,7 +320,7 @@ static hipError_t launch_chain_dvs(const ChunkArgs& a) {
         hipLaunchKernelGGL((chunk_chain_kernel<T, TOut, DK, DV, C, DVS>), dim3((unsigned)nwg), dim3(256), 0,
                            a.stream, (const T*)(ws + w.qt), (const T*)(ws + w.wk), (const T*)(ws + w.kb),
                            (const T*)(ws + w.p), (const float*)(ws + w.u), (const float*)(ws + w.gam),
-                           a.s0, (TOut*)a.o, a.sT, unit_map(a));
+                           a.s0, (TOut*)a.o, a.sT, unit_map(a), a.ck_state, a.ck_w);
         return hipGetLastError();
     }
 }

@@ -10,7 +10,10 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     T* __restrict__ ws_qt, T* __restrict__ ws_wk, T* __restrict__ ws_kb, T* __restrict__ ws_p,
-    float* __restrict__ ws_u, float* __restrict__ ws_gam, UnitMap um, int gate) {
+    float* __restrict__ ws_u, float* __restrict__ ws_gam, UnitMap um, int gate,
+    float* __restrict__ ck_t, float* __restrict__ ck_a) {
+    // ck_t / ck_a (NULL in the forward pass): per unit, T and A in fp32 [C][C],
+    // kept for the backward pass
     typedef IntraCfg<T, DK, DV, C> Cfg;
     constexpr int NB = Cfg::NB, NP = Cfg::NP, HR = Cfg::HR, LDK = Cfg::LDK, LDA = Cfg::LDA,
                   LDT = Cfg::LDT, CK = Cfg::CK;
@@ -189,7 +192,10 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     T* gP = ws_p + ch * (long)C * C;
     for (int u = tid; u < C * C; u += 256) {
         const int r = u / C, i = u % C;
-        if (r / 16 < i / 16) { sA[r * LDA + i] = 0.f; gP[u] = from_f32<T>(0.f); }
+        if (r / 16 < i / 16) {
+            sA[r * LDA + i] = 0.f; gP[u] = from_f32<T>(0.f);
+            if (ck_a) ck_a[ch * (long)C * C + u] = 0.f;
+        }
     }
     static_for<NP>([&](auto PI) {
         constexpr int p = PI;
@@ -203,6 +209,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
                 if (R == I) { if (i >= r) av = 0.f; if (i > r) pv = 0.f; }
                 sA[r * LDA + i] = sBeta[r] * av;
                 gP[r * C + i] = from_f32<T>(pv);
+                if (ck_a) ck_a[ch * (long)C * C + r * C + i] = av;
             }
         }
     });
@@ -254,6 +261,9 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
         }
         __syncthreads();
     });
+    if (ck_t) {
+        for (int u = tid; u < C * C; u += 256) ck_t[ch * (long)C * C + u] = sA[(u / C) * LDA + u % C];
+    }
 
     // ---------------------------------------------------------------- phase W
     T* sTb = reinterpret_cast<T*>(smem);
@@ -822,7 +832,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 // ================================================================ host side
 static inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_bf16, int C) {
+static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_bf16, int C, bool generic) {
     WsLayout w{};
     const size_t es = in_bf16 ? 2 : 4;
     size_t off = 0;
@@ -831,25 +841,25 @@ static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_
     w.wk = off; off = al256(off + nch * C * dk * es);
     w.kb = off; off = al256(off + nch * C * dk * es);
     w.p = off;  off = al256(off + nch * C * C * es);
-    w.u = off;  off = al256(off + nch * C * dv * (hot_config(in_bf16, dk, C) ? 2 : 4));
+    w.u = off;  off = al256(off + nch * C * dv * (hot_config(in_bf16, dk, C) && !generic ? 2 : 4));
     w.gam = off; off = al256(off + nch * dk * 4);
     w.total = off;
     return w;
 }
 
-WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
+WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
     const size_t NC = (size_t)((T + C - 1) / C);
-    return layout_units((size_t)B * H * NC, 0, dk, dv, in_bf16, C);
+    return layout_units((size_t)B * H * NC, 0, dk, dv, in_bf16, C, generic);
 }
 
-WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C) {
+WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
     const size_t chunks = (size_t)((T + C - 1) / C) + (size_t)N;
-    return layout_units(chunks * H, ((size_t)N + 1) * 4, dk, dv, in_bf16, C);
+    return layout_units(chunks * H, ((size_t)N + 1) * 4, dk, dv, in_bf16, C, generic);
 }
 
 WsLayout ws_layout_of(const ChunkArgs& a) {
-    return a.cu_seqlens ? ws_layout_packed(a.N, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C)
-                        : ws_layout(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C);
+    return a.cu_seqlens ? ws_layout_packed(a.N, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.generic)
+                        : ws_layout(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.generic);
 }
 
 UnitMap unit_map(const ChunkArgs& a) {
@@ -916,7 +926,7 @@ static hipError_t launch_intra(const ChunkArgs& a) {
         hipLaunchKernelGGL((chunk_intra_kernel<T, DK, DV, C>), dim3((unsigned)nch), dim3(256), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta,
                            (T*)(ws + w.qt), (T*)(ws + w.wk), (T*)(ws + w.kb), (T*)(ws + w.p),
-                           (float*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate);
+                           (float*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate, a.ck_t, a.ck_a);
         return hipGetLastError();
     }
 }

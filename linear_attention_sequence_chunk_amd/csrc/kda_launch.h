@@ -37,6 +37,13 @@ struct ChunkArgs {
     // token offsets cu_seqlens[N+1] (device memory); NULL for [B,T,H,d] batches
     const int* cu_seqlens = nullptr;
     int N = 0;
+    // backward pass only: the generic (row-major, fp32 U) workspace format even in
+    // the hot configuration, and fp32 checkpoints kept by the stages
+    bool generic = false;
+    float* ck_state = nullptr;   // chain: state at each chunk start, [unit][dk][dv]
+    float* ck_w = nullptr;       // chain: W of each chunk, [unit][C][dv]
+    float* ck_t = nullptr;       // intra: T = (I + Diag(beta) A)^-1, [unit][C][C]
+    float* ck_a = nullptr;       // intra: A (strictly lower), [unit][C][C]
 };
 
 // The hot configuration (bf16 inputs, C = 64, dk = 128) has its own pair of
@@ -50,15 +57,40 @@ inline bool hot_config(bool in_bf16, int dk, int C) { return in_bf16 && dk == 12
 struct WsLayout {
     size_t cu, qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
 };
-WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C);
+// generic = true: the format of the generic kernels even in the hot configuration
+WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic = false);
 // Packed variable-length batch of N sequences, T tokens in all: room for every
 // possible chunk (at most ceil(T/C) + N) and, first, the chunk offsets int [N+1].
-WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C);
+WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic = false);
 // The layout for a call's arguments (fixed-length or packed).
 WsLayout ws_layout_of(const ChunkArgs& a);
 
 // True when an instantiation exists for these sizes (dk, dv, C, dtype).
 bool chunk_supported(int dk, int dv, int C, bool in_bf16);
+
+// Backward pass (kda_chunk_bwd.hip).  fwd: the forward arguments with
+// generic = true and the four checkpoint arrays; the rest is the backward's.
+struct BwdArgs {
+    ChunkArgs fwd;
+    const float* dO;            // [B,T,H,dv] cotangent of o
+    const float* dST;           // [B,H,dk,dv] cotangent of the final state, or NULL
+    float *dq, *dk, *dv;        // [B,T,H,dk], [B,T,H,dk], [B,T,H,dv]
+    float* dg;                  // [B,T,H,dk] / [B,T,H] by gate layout, NULL without gates
+    float* dbeta;               // [B,T,H]
+    float* dS0;                 // [B,H,dk,dv] or NULL
+    float* ck_dS;               // cotangent of each chunk's end state, [unit][dk][dv]
+    float* ck_dW;               // dW of each chunk, [unit][C][dv]
+    float* scratch;             // [unit][4][C][dk]
+};
+// Workspace of the backward pass: the forward workspace (generic format) then
+// the checkpoints and scratch, per unit.
+struct BwdLayout {
+    WsLayout fwd;
+    size_t t, a, state, w, dS, dW, scr, total;
+};
+BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C);
+bool bwd_supported(int dk, int dv, int C, bool in_bf16);
+hipError_t run_chunk_bwd_stages(const BwdArgs& b);
 
 hipError_t run_decode_step(const DecodeArgs& a);
 hipError_t run_chunk_intra(const ChunkArgs& a);

@@ -1,0 +1,86 @@
+"""Backward pass (kda_chunk_bwd) on the GPU against the oracle's fp64 adjoint.
+
+Gradients of L = sum(dO * o) + sum(dST * S_T) for every input; ragged lengths
+(partial last chunk), several chunks, every supported chunk size, both input
+dtypes, all gate layouts."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_sequence_chunk_amd import chunk_bwd, inputs
+from tests.parity import assert_close, cuda
+
+pytestmark = pytest.mark.gpu
+
+# the gradient arithmetic is fp32; with bf16 inputs the forward stages that are
+# re-run for the backward use bf16 MFMA operands (as in the forward pass)
+BWD_TOL = {torch.float32: 1e-3, torch.bfloat16: 2e-2}
+
+
+def _say(m):
+    print(m, flush=True)
+
+
+def _run(d, C, layout, dtype, seed, tag):
+    rs = np.random.default_rng(seed)
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    dO = torch.tensor(rs.standard_normal((B, T, H, dv)), dtype=torch.float32)
+    dST = torch.tensor(rs.standard_normal((B, H, dk, dv)), dtype=torch.float32)
+    if layout == "head":
+        g_in = d["g"][..., 0].contiguous()
+        g_ref = g_in[..., None].expand_as(d["g"]).contiguous()
+    elif layout == "none":
+        g_in, g_ref = None, torch.zeros_like(d["g"])
+    else:
+        g_in = g_ref = d["g"]
+    dg = cuda(d)
+    got = chunk_bwd(dg["q"], dg["k"], dg["v"], None if g_in is None else g_in.cuda(), dg["beta"],
+                    dO.cuda(), dg["S0"], dST.cuda(), chunk_size=C, gate_layout=layout)
+    torch.cuda.synchronize()
+    ref = oracle.backward(d["q"], d["k"], d["v"], g_ref, d["beta"], d["S0"], dO, dST)
+    tol = BWD_TOL[dtype]
+    errs = {}
+    for name in ("dq", "dk", "dv", "dbeta", "dS0"):
+        errs[name] = assert_close(f"{tag} {name}", got[name].cpu(), ref[name], tol)
+    if layout == "channel":
+        errs["dg"] = assert_close(f"{tag} dg", got["dg"].cpu(), ref["dg"], tol)
+    elif layout == "head":
+        errs["dg"] = assert_close(f"{tag} dg", got["dg"].cpu(), ref["dg"].sum(-1), tol)
+    else:
+        assert got["dg"] is None
+    _say(f"  {tag}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("dk,dv,C,dtype", [(64, 64, 64, torch.float32), (64, 128, 32, torch.float32),
+                                           (128, 64, 16, torch.float32), (128, 128, 64, torch.bfloat16),
+                                           (128, 128, 32, torch.bfloat16), (64, 64, 16, torch.bfloat16)])
+def test_backward_shapes(dk, dv, C, dtype):
+    T = 3 * C + 11
+    _say(f"backward dk={dk} dv={dv} C={C} {dtype} T={T}")
+    d = inputs.custom_prefill(70 + C + dk + dv, 2, T, 2, dk, dv, dtype=dtype, s0_std=0.05)
+    _run(d, C, "channel", dtype, 1, f"bwd dk{dk} dv{dv} C{C}")
+
+
+@pytest.mark.parametrize("layout", ["head", "none"])
+def test_backward_gate_layouts(layout):
+    d = inputs.custom_prefill(81, 1, 150, 3, 128, 128, dtype=torch.bfloat16,
+                              gates="scalar" if layout == "head" else "none", s0_std=0.05)
+    _run(d, 64, layout, torch.bfloat16, 2, f"bwd {layout}")
+
+
+def test_backward_longer_sequence():
+    """1024 tokens, 16 chunks of 64: the reverse chain over many chunks."""
+    d = inputs.custom_prefill(83, 1, 1024, 4, 128, 128, dtype=torch.bfloat16, s0_std=0.02)
+    _run(d, 64, "channel", torch.bfloat16, 3, "bwd T1024")
+
+
+def test_backward_is_deterministic():
+    d = cuda(inputs.custom_prefill(85, 1, 200, 2, 64, 64, dtype=torch.float32, s0_std=0.05))
+    dO = torch.randn((1, 200, 2, 64), generator=torch.Generator().manual_seed(0)).cuda()
+    a = chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dO, d["S0"], chunk_size=32)
+    b = chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dO, d["S0"], chunk_size=32)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
