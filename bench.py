@@ -169,6 +169,7 @@ def main():
 
     out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, g, w, K, args.warmup)
     out["varlen"] = bench_varlen(torch, g, w, K, args.warmup)
+    out["backward"] = bench_backward(torch, g, w)
 
     if not args.no_decode:
         out["decode"] = bench_decode(torch, inputs, decode_step, dev, args.decode_steps)
@@ -234,6 +235,28 @@ def bench_varlen(torch, g, w, steps, warmup):
     return {"sequences": N, "tokens": T, "heads": w.H, "ms_per_call": round(ms, 4),
             "tokens_per_s": round(T / (ms / 1e3), 1),
             "note": "includes a workspace allocation per call (torch caching allocator)"}
+
+
+def bench_backward(torch, g, w, steps=5, warmup=2):
+    """kda_chunk_bwd on the same workload: gradients of sum(dO * o) for every
+    input (the forward stages are re-run inside the call)."""
+    from linear_attention_sequence_chunk_amd import chunk_bwd
+    gen = torch.Generator(device=g["q"].device).manual_seed(0)
+    dO = torch.randn(g["v"].shape, generator=gen, device=g["q"].device, dtype=torch.float32)
+    ws = None
+    for _ in range(warmup):
+        chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], dO, g["S0"], chunk_size=w.C, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], dO, g["S0"], chunk_size=w.C, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_call": round(ms, 3), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1), "calls": steps,
+            "note": "fp32 gradient arithmetic; includes re-running the forward stages"}
 
 
 def bench_decode(torch, inputs, decode_step, dev, steps):

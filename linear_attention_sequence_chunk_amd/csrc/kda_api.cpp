@@ -289,7 +289,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
     kda::BwdArgs bw;
     bw.fwd = a; bw.dO = dO; bw.dST = dST;
     bw.dq = dq; bw.dk = dk_out; bw.dv = dv_out; bw.dg = dg; bw.dbeta = dbeta; bw.dS0 = dS0;
-    bw.ck_dS = (float*)(ws + L.dS); bw.ck_dW = (float*)(ws + L.dW); bw.scratch = (float*)(ws + L.scr);
+    bw.ck_dS = (float*)(ws + L.dS); bw.ck_dW = (float*)(ws + L.dW);
     return finish(kda::run_chunk_bwd_stages(bw), (hipStream_t)stream);
 }
 

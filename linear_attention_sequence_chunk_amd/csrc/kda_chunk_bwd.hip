@@ -20,152 +20,359 @@
 
 namespace kda {
 
+// ================================================================ fp32 MFMA helpers
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][slot] and B[slot][l%16], and
+// accumulator element e of lane l is D[4(l/16)+e][l%16].  A 16-deep contraction
+// is four instructions in which lane l covers k = 4(l/16) + m (m = 0..3): the same
+// slot assignment on both operands, so four consecutive k come from one 16-byte
+// load where k is the contiguous index.
+__device__ __forceinline__ floatx4 mfma4(floatx4 acc, float a, float b) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(floatx4 acc, floatx4 a, floatx4 b) {
+    acc = mfma4(acc, a[0], b[0]);
+    acc = mfma4(acc, a[1], b[1]);
+    acc = mfma4(acc, a[2], b[2]);
+    return mfma4(acc, a[3], b[3]);
+}
+template <typename T> __device__ __forceinline__ floatx4 load4(const T* p);
+template <> __device__ __forceinline__ floatx4 load4<float>(const float* p) {
+    return *reinterpret_cast<const floatx4*>(p);
+}
+template <> __device__ __forceinline__ floatx4 load4<bf16>(const bf16* p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ __forceinline__ floatx4 lds4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+// Four consecutive rows of one column of an LDS matrix with row stride ld.
+__device__ __forceinline__ floatx4 col4(const float* p, int ld) {
+    return floatx4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+// Sum over the 16 lanes holding one accumulator row.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    return x + __shfl_xor(x, 8);
+}
+// Sum over the four lanes holding one accumulator column.
+__device__ __forceinline__ float col_sum4(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+// 16 bytes of T as fp32 (8 values for bf16, 4 for fp32).
+template <typename T> struct Unpack16;
+template <> struct Unpack16<bf16> {
+    static constexpr int N = 8;
+    __device__ static __forceinline__ void run(u32x4 x, float* o) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(x[i] << 16);
+            o[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Unpack16<float> {
+    static constexpr int N = 4;
+    __device__ static __forceinline__ void run(u32x4 x, float* o) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(x[i]);
+    }
+};
+
 // ================================================================ reverse chain
-// One workgroup of 256 threads per (sequence, head, slice of 32 value columns).
-// Thread t owns column t % 32 and rows 16 (t / 32) .. + 15 of the slice's dS.
+// One workgroup of 256 threads (4 waves) per (sequence, head, slice of 32 value
+// columns), walking the chunks from last to first.  The slice of dS (DK x 32)
+// stays in MFMA accumulators, wave w owning the 16-channel blocks w, w + 4, ...
+// The earlier chunk's operands are loaded into registers while a chunk computes.
 template <typename T, int DK, int DV, int C>
 struct BwdChainCfg {
-    static constexpr int DVS = 32, NSL = DV / DVS;
-    static constexpr size_t OFF_KB = size_t(DK) * DVS * 4;                 // sS [DK][DVS]
-    static constexpr size_t OFF_P = OFF_KB + size_t(DK) * C * 4;           // sKb [DK][C]
-    static constexpr size_t OFF_WK = OFF_P + size_t(C) * C * 4;            // sP [C][C]
-    static constexpr size_t OFF_QT = OFF_WK + size_t(C) * DK * 4;          // sWk [C][DK]
-    static constexpr size_t OFF_DO = OFF_QT + size_t(C) * DK * 4;          // sQt [C][DK]
-    static constexpr size_t OFF_DW = OFF_DO + size_t(C) * DVS * 4;         // sdO [C][DVS]
-    static constexpr size_t OFF_G = OFF_DW + size_t(C) * DVS * 4;          // sdW [C][DVS]
-    static constexpr size_t TOTAL = OFF_G + size_t(DK) * 4;                // sG [DK]
-    static constexpr bool FITS = TOTAL <= LDS_LIMIT && DK * DVS % 256 == 0 && C * DVS % 256 == 0;
+    static constexpr int DVS = 32, NSL = DV / DVS, NB = C / 16, NKB = DK / 16, KPW = NKB / 4;
+    static constexpr int LKB = C + 4, LP = C + 4, LWK = DK + 4, LJ = DVS + 4;
+    static constexpr int F_KB = 0;                                          // sKb [DK][C]: Kb^T
+    static constexpr int F_P = F_KB + DK * LKB;                             // sP  [C][C]
+    static constexpr int F_WK = F_P + C * LP;                               // sWk [C][DK]
+    static constexpr int F_QT = F_WK + C * LWK;                             // sQt [C][DK]
+    static constexpr int F_DO = F_QT + C * LWK;                             // sdO [C][DVS]
+    static constexpr int F_S = F_DO + C * LJ;                               // sS  [DK][DVS]: dS'
+    static constexpr int F_DW = F_S + DK * LJ;                              // sdW [C][DVS]
+    static constexpr int F_G = F_DW + C * LJ;                               // sGam [DK]
+    static constexpr int FLOATS = F_G + DK;
+    static constexpr int EPU = 16 / (int)sizeof(T);                         // elements per 16 bytes
+    static constexpr int U_KB = DK * C / EPU, U_P = C * C / EPU, U_DO = C * DVS / 4;
+    static constexpr int PKB = (U_KB + 255) / 256, PP = (U_P + 255) / 256, PDO = (U_DO + 255) / 256;
+    static constexpr bool FITS = size_t(FLOATS) * 4 <= LDS_LIMIT && NKB % 4 == 0;
 };
 
 template <typename T, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void chunk_bwd_chain_kernel(
+__global__ __launch_bounds__(256, 1) void chunk_bwd_chain_kernel(
     const T* __restrict__ ws_qt, const T* __restrict__ ws_wk, const T* __restrict__ ws_kb,
     const T* __restrict__ ws_p, const float* __restrict__ ws_gam, const float* __restrict__ dO,
     const float* __restrict__ dST, float* __restrict__ dS0, float* __restrict__ ck_dS,
     float* __restrict__ ck_dW, UnitMap um) {
     typedef BwdChainCfg<T, DK, DV, C> Cfg;
-    constexpr int DVS = Cfg::DVS, NSL = Cfg::NSL, RPT = DK * DVS / 256, WPT = C * DVS / 256;
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
-    float* sS = reinterpret_cast<float*>(smem);
-    float* sKb = reinterpret_cast<float*>(smem + Cfg::OFF_KB);
-    float* sP = reinterpret_cast<float*>(smem + Cfg::OFF_P);
-    float* sWk = reinterpret_cast<float*>(smem + Cfg::OFF_WK);
-    float* sQt = reinterpret_cast<float*>(smem + Cfg::OFF_QT);
-    float* sdO = reinterpret_cast<float*>(smem + Cfg::OFF_DO);
-    float* sdW = reinterpret_cast<float*>(smem + Cfg::OFF_DW);
-    float* sG = reinterpret_cast<float*>(smem + Cfg::OFF_G);
+    constexpr int DVS = Cfg::DVS, NSL = Cfg::NSL, NB = Cfg::NB, KPW = Cfg::KPW, EPU = Cfg::EPU;
+    constexpr int LKB = Cfg::LKB, LP = Cfg::LP, LWK = Cfg::LWK, LJ = Cfg::LJ;
+    constexpr int PKB = Cfg::PKB, PP = Cfg::PP, PDO = Cfg::PDO;
+    __shared__ __attribute__((aligned(16))) float smem[Cfg::FLOATS];
+    float* sKb = smem + Cfg::F_KB;
+    float* sP = smem + Cfg::F_P;
+    float* sWk = smem + Cfg::F_WK;
+    float* sQt = smem + Cfg::F_QT;
+    float* sdO = smem + Cfg::F_DO;
+    float* sS = smem + Cfg::F_S;
+    float* sdW = smem + Cfg::F_DW;
+    float* sGam = smem + Cfg::F_G;
 
-    const int tid = threadIdx.x;
-    const long bh = blockIdx.x / NSL;
-    const int sl = blockIdx.x % NSL, j0 = sl * DVS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, kg = lane >> 4;
+    // the slices of one head share an XCD (workgroups are dealt to the 8 XCDs
+    // round-robin), so the chunk operands they all read come from one L2
+    long bh;
+    int sl;
+    {
+        const long nwg = (long)gridDim.x, id = blockIdx.x;
+        if (nwg % 8 == 0) {
+            const long o = (id % 8) * (nwg / 8) + id / 8;
+            bh = o / NSL;
+            sl = (int)(o % NSL);
+        } else {
+            bh = id / NSL;
+            sl = (int)(id % NSL);
+        }
+    }
+    const int j0 = sl * DVS;
     const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
     const SeqRange sr = seq_range(um, sq);
     const int NC = sr.nchunks;
-    const int j = tid % DVS, rb = (tid / DVS) * RPT;       // this thread's column and first row
 
-    float ds[RPT];
+    floatx4 ds[KPW][2];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) ds[m] = dST ? dST[(bh * DK + rb + m) * (long)DV + j0 + j] : 0.f;
+    for (int p = 0; p < KPW; ++p)
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * (wave + 4 * p) + 4 * kg + e;
+                ds[p][J][e] = dST ? dST[(bh * DK + c) * (long)DV + j0 + 16 * J + lr] : 0.f;
+            }
 
+    u32x4 rKb[PKB], rWk[PKB], rQt[PKB], rP[PP];
+    floatx4 rdO[PDO];
+    float rG = 0.f;
+#define KDA_BWD_FETCH(N)                                                                          \
+    {                                                                                             \
+        const long un = unit_id(um, sq, h, (N), sr.chunk0);                                      \
+        const u32x4* gkb = reinterpret_cast<const u32x4*>(ws_kb + un * (long)DK * C);             \
+        const u32x4* gwk = reinterpret_cast<const u32x4*>(ws_wk + un * (long)C * DK);             \
+        const u32x4* gqt = reinterpret_cast<const u32x4*>(ws_qt + un * (long)C * DK);             \
+        const u32x4* gp = reinterpret_cast<const u32x4*>(ws_p + un * (long)C * C);                \
+        _Pragma("unroll") for (int x = 0; x < PKB; ++x) {                                         \
+            const int u = tid + 256 * x;                                                          \
+            if (Cfg::U_KB % 256 == 0 || u < Cfg::U_KB) {                                          \
+                rKb[x] = gkb[u];                                                                  \
+                rWk[x] = gwk[u];                                                                  \
+                rQt[x] = gqt[u];                                                                  \
+            }                                                                                     \
+        }                                                                                         \
+        _Pragma("unroll") for (int x = 0; x < PP; ++x) {                                          \
+            const int u = tid + 256 * x;                                                          \
+            if (Cfg::U_P % 256 == 0 || u < Cfg::U_P) rP[x] = gp[u];                               \
+        }                                                                                         \
+        const long t0 = sr.tok_begin + (long)(N) * C;                                             \
+        _Pragma("unroll") for (int x = 0; x < PDO; ++x) {                                         \
+            const int u = tid + 256 * x, r = u / (DVS / 4), q4 = u % (DVS / 4);                   \
+            if (Cfg::U_DO % 256 == 0 || u < Cfg::U_DO)                                            \
+                rdO[x] = t0 + r < sr.tok_end                                                      \
+                             ? *reinterpret_cast<const floatx4*>(dO + ((t0 + r) * H + h) * DV + j0 + 4 * q4) \
+                             : zero4();                                                           \
+        }                                                                                         \
+        if (tid < DK) rG = ws_gam[un * DK + tid];                                                 \
+    }
+#define KDA_BWD_STORE()                                                                           \
+    {                                                                                             \
+        _Pragma("unroll") for (int x = 0; x < PKB; ++x) {                                         \
+            const int u = tid + 256 * x, e0 = u * EPU;                                            \
+            if (Cfg::U_KB % 256 == 0 || u < Cfg::U_KB) {                                          \
+                float f[EPU];                                                                     \
+                Unpack16<T>::run(rKb[x], f);                                                      \
+                _Pragma("unroll") for (int i = 0; i < EPU; i += 4)                                \
+                    *reinterpret_cast<floatx4*>(sKb + (e0 / C) * LKB + e0 % C + i) =              \
+                        floatx4{f[i], f[i + 1], f[i + 2], f[i + 3]};                              \
+                Unpack16<T>::run(rWk[x], f);                                                      \
+                _Pragma("unroll") for (int i = 0; i < EPU; i += 4)                                \
+                    *reinterpret_cast<floatx4*>(sWk + (e0 / DK) * LWK + e0 % DK + i) =            \
+                        floatx4{-f[i], -f[i + 1], -f[i + 2], -f[i + 3]};                          \
+                Unpack16<T>::run(rQt[x], f);                                                      \
+                _Pragma("unroll") for (int i = 0; i < EPU; i += 4)                                \
+                    *reinterpret_cast<floatx4*>(sQt + (e0 / DK) * LWK + e0 % DK + i) =            \
+                        floatx4{f[i], f[i + 1], f[i + 2], f[i + 3]};                              \
+            }                                                                                     \
+        }                                                                                         \
+        _Pragma("unroll") for (int x = 0; x < PP; ++x) {                                          \
+            const int u = tid + 256 * x, e0 = u * EPU;                                            \
+            if (Cfg::U_P % 256 == 0 || u < Cfg::U_P) {                                            \
+                float f[EPU];                                                                     \
+                Unpack16<T>::run(rP[x], f);                                                       \
+                _Pragma("unroll") for (int i = 0; i < EPU; i += 4)                                \
+                    *reinterpret_cast<floatx4*>(sP + (e0 / C) * LP + e0 % C + i) =                \
+                        floatx4{f[i], f[i + 1], f[i + 2], f[i + 3]};                              \
+            }                                                                                     \
+        }                                                                                         \
+        _Pragma("unroll") for (int x = 0; x < PDO; ++x) {                                         \
+            const int u = tid + 256 * x, r = u / (DVS / 4), q4 = u % (DVS / 4);                   \
+            if (Cfg::U_DO % 256 == 0 || u < Cfg::U_DO)                                            \
+                *reinterpret_cast<floatx4*>(sdO + r * LJ + 4 * q4) = rdO[x];                      \
+        }                                                                                         \
+        if (tid < DK) sGam[tid] = rG;                                                             \
+    }
+
+    if (NC > 0) KDA_BWD_FETCH(NC - 1);
     for (int n = NC - 1; n >= 0; --n) {
         const long unit = unit_id(um, sq, h, n, sr.chunk0);
-        // the cotangent of this chunk's end state
+        __syncthreads();                                    // the later chunk's readers are done
+        KDA_BWD_STORE();
+        // dS', the cotangent of this chunk's end state: to LDS and to its checkpoint
         float* cds = ck_dS + unit * (long)DK * DV;
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            cds[(rb + m) * (long)DV + j0 + j] = ds[m];
-            sS[(rb + m) * DVS + j] = ds[m];
-        }
-        const T* gkb = ws_kb + unit * (long)DK * C;
-        const T* gp = ws_p + unit * (long)C * C;
-        const T* gwk = ws_wk + unit * (long)C * DK;
-        const T* gqt = ws_qt + unit * (long)C * DK;
-        for (int u = tid; u < DK * C; u += 256) {
-            sKb[u] = to_f32(gkb[u]);
-            sWk[u] = to_f32(gwk[u]);
-            sQt[u] = to_f32(gqt[u]);
-        }
-        for (int u = tid; u < C * C; u += 256) sP[u] = to_f32(gp[u]);
-        if (tid < DK) sG[tid] = ws_gam[unit * DK + tid];
-        const long t0 = sr.tok_begin + (long)n * C;
-        for (int u = tid; u < C * DVS; u += 256) {
-            const int r = u / DVS, jj = u % DVS;
-            sdO[u] = t0 + r < sr.tok_end ? dO[((t0 + r) * H + h) * DV + j0 + jj] : 0.f;
-        }
+        for (int p = 0; p < KPW; ++p)
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * (wave + 4 * p) + 4 * kg + e, j = 16 * J + lr;
+                    sS[c * LJ + j] = ds[p][J][e];
+                    cds[c * (long)DV + j0 + j] = ds[p][J][e];
+                }
+        if (n > 0) KDA_BWD_FETCH(n - 1);
         __syncthreads();
 
-        // dW = Kb dS' + P^T dO   (Kb[r][c] = sKb[c][r];  P^T[r][i] = sP[i][r], zero above the diagonal)
+        // dW = Kb dS' + P^T dO: output tiles (R, J), wave w taking w, w + 4, ...
         float* cdw = ck_dW + unit * (long)C * DV;
-        const int wr = (tid / DVS) * WPT;
+        for (int t = wave; t < 2 * NB; t += 4) {
+            const int R = t >> 1, J = t & 1;
+            floatx4 acc = zero4();
+#pragma unroll 4
+            for (int c0 = 0; c0 < DK; c0 += 16)
 #pragma unroll
-        for (int m = 0; m < WPT; ++m) {
-            const int r = wr + m;
-            float acc = 0.f;
-            for (int c = 0; c < DK; ++c) acc += sKb[c * C + r] * sS[c * DVS + j];
-            for (int i = r; i < C; ++i) acc += sP[i * C + r] * sdO[i * DVS + j];
-            sdW[r * DVS + j] = acc;
-            cdw[r * (long)DV + j0 + j] = acc;
+                for (int m = 0; m < 4; ++m) {
+                    const int c = c0 + 4 * kg + m;
+                    acc = mfma4(acc, sKb[c * LKB + 16 * R + lr], sS[c * LJ + 16 * J + lr]);
+                }
+            for (int i0 = 16 * R; i0 < C; i0 += 16)             // P[i][r] = 0 for i < r
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int i = i0 + 4 * kg + m;
+                    acc = mfma4(acc, sP[i * LP + 16 * R + lr], sdO[i * LJ + 16 * J + lr]);
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e, j = 16 * J + lr;
+                sdW[r * LJ + j] = acc[e];
+                cdw[r * (long)DV + j0 + j] = acc[e];
+            }
         }
         __syncthreads();
 
-        // dS = Diag(gam) dS' - Wk^T dW + Qt^T dO
+        // dS = Diag(gam) dS' - Wk^T dW + Qt^T dO  (sWk holds -Wk)
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int c = rb + m;
-            float acc = sG[c] * ds[m];
-            for (int r = 0; r < C; ++r) acc += sQt[r * DK + c] * sdO[r * DVS + j] - sWk[r * DK + c] * sdW[r * DVS + j];
-            ds[m] = acc;
+        for (int p = 0; p < KPW; ++p) {
+            const int cb = 16 * (wave + 4 * p);
+#pragma unroll
+            for (int J = 0; J < 2; ++J) {
+                floatx4 acc = ds[p][J];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= sGam[cb + 4 * kg + e];
+#pragma unroll 2
+                for (int r0 = 0; r0 < C; r0 += 16)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int r = r0 + 4 * kg + m;
+                        acc = mfma4(acc, sQt[r * LWK + cb + lr], sdO[r * LJ + 16 * J + lr]);
+                        acc = mfma4(acc, sWk[r * LWK + cb + lr], sdW[r * LJ + 16 * J + lr]);
+                    }
+                ds[p][J] = acc;
+            }
         }
-        __syncthreads();
     }
+#undef KDA_BWD_FETCH
+#undef KDA_BWD_STORE
     if (dS0) {
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) dS0[(bh * DK + rb + m) * (long)DV + j0 + j] = ds[m];
+        for (int p = 0; p < KPW; ++p)
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * (wave + 4 * p) + 4 * kg + e;
+                    dS0[(bh * DK + c) * (long)DV + j0 + 16 * J + lr] = ds[p][J][e];
+                }
     }
 }
 
 // ================================================================ per-chunk gradients
-// One workgroup of 256 threads per chunk unit.  C x C matrices live in LDS; the
-// C x DK intermediates go through per-unit scratch in the workspace.
+// One workgroup of 256 threads (4 waves) per chunk unit; every contraction runs
+// on fp32 MFMA.  Wave w owns the channel blocks w, w + 4, ... from start to end:
+// dQt, dKb and T^T dWk of its channels stay in its registers (rows 16R + 4(l/16) + e,
+// channel l%16 of each block), and the last phase (decays, pairwise decays, the
+// prefix-sum adjoint) runs per wave without workgroup barriers.  Phase 1 loads its
+// fragments straight from global memory; the C x C products are split by column
+// block (wave w: block w) and go through LDS.
 template <int DK, int DV, int C>
 struct BwdIntraCfg {
-    static constexpr int NB = C / 16;
-    static constexpr int DKT = 16;                                          // channels per tile (phase 5)
-    static constexpr size_t SZ_CC = size_t(C) * C * 4;
-    static constexpr size_t OFF_T = 0, OFF_A = SZ_CC, OFF_DP = 2 * SZ_CC, OFF_DT = 3 * SZ_CC;
-    static constexpr size_t OFF_G = 4 * SZ_CC;                             // sG [C][DK]: prefix sums
-    static constexpr size_t OFF_ST = OFF_G + size_t(C) * DK * 4;          // staging
-    static constexpr int DM = DK > DV ? DK : DV;
-    static constexpr size_t ST_FLOATS = size_t(C) * DM > size_t(6) * C * DKT ? size_t(C) * DM : size_t(6) * C * DKT;
-    static constexpr size_t OFF_BETA = OFF_ST + ST_FLOATS * 4;
-    static constexpr size_t OFF_DB = OFF_BETA + size_t(C) * 4;            // dbeta accumulators [C]
-    static constexpr size_t OFF_DGM = OFF_DB + size_t(C) * 4;             // dgam [DK]
-    static constexpr size_t TOTAL = OFF_DGM + size_t(DK) * 4;
-    static constexpr bool FITS = TOTAL <= LDS_LIMIT;
+    static constexpr int NB = C / 16, NKB = DK / 16, NVB = DV / 16, KPW = NKB / 4, VPW = NVB / 4;
+    static constexpr int LC = C + 4, LK = DK + 4;
+    static constexpr int TL = 16 * LC;                                      // one [16 channels][C] array
+    static constexpr int F_T = 0, F_DP = C * LC, F_DA = 2 * C * LC, F_G = 3 * C * LC;
+    static constexpr int F_X = F_G + C * DK;                                // shared by phases 3, 4, 5
+    static constexpr int X3 = 2 * C * LK;                                   // dWk, Kt
+    static constexpr int X4 = C * LC;                                       // X = T^T dT
+    static constexpr int X5 = 4 * 4 * TL;                                   // per wave: Km, Ks, Qs, Ki
+    static constexpr int XN = X3 > X4 ? (X3 > X5 ? X3 : X5) : (X4 > X5 ? X4 : X5);
+    static constexpr int F_BETA = F_X + XN;
+    static constexpr int F_DB1 = F_BETA + C;                                // [C]
+    static constexpr int F_DB2 = F_DB1 + C;                                 // [4][C]
+    static constexpr int F_DB3 = F_DB2 + 4 * C;                             // [4][C]
+    static constexpr int F_HD = F_DB3 + 4 * C;                              // [4][C] per-head dg partials
+    static constexpr int FLOATS = F_HD + 4 * C;
+    static constexpr bool FITS = size_t(FLOATS) * 4 <= LDS_LIMIT && NKB % 4 == 0 && NVB % 4 == 0;
 };
 
+template <int NB, int KPW>
+struct BwdFrag {                          // one 16-deep k step of phase 1
+    floatx4 o[NB], w[NB], dw[NB], s[KPW], ds[KPW], wi, v;
+};
+
+// Make one wave's LDS writes visible to its other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename T, int DK, int DV, int C>
-__global__ __launch_bounds__(256) void chunk_bwd_intra_kernel(
+__global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ dO,
     const float* __restrict__ ck_state, const float* __restrict__ ck_dS, const float* __restrict__ ck_w,
     const float* __restrict__ ck_dW, const float* __restrict__ ck_t, const float* __restrict__ ck_a,
-    float* __restrict__ scr, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta, UnitMap um, int gate) {
     typedef BwdIntraCfg<DK, DV, C> Cfg;
-    constexpr int NB = Cfg::NB, DKT = Cfg::DKT;
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
-    float* sT = reinterpret_cast<float*>(smem + Cfg::OFF_T);
-    float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
-    float* sdP = reinterpret_cast<float*>(smem + Cfg::OFF_DP);
-    float* sdT = reinterpret_cast<float*>(smem + Cfg::OFF_DT);
-    float* sG = reinterpret_cast<float*>(smem + Cfg::OFF_G);
-    float* sSt = reinterpret_cast<float*>(smem + Cfg::OFF_ST);
-    float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_BETA);
-    float* sDb = reinterpret_cast<float*>(smem + Cfg::OFF_DB);
-    float* sDgm = reinterpret_cast<float*>(smem + Cfg::OFF_DGM);
+    constexpr int NB = Cfg::NB, NVB = Cfg::NVB, KPW = Cfg::KPW, VPW = Cfg::VPW;
+    constexpr int LC = Cfg::LC, LK = Cfg::LK, TL = Cfg::TL;
+    __shared__ __attribute__((aligned(16))) float smem[Cfg::FLOATS];
+    float* sT = smem + Cfg::F_T;            // T [C][C]
+    float* sdP = smem + Cfg::F_DP;          // dP (lower)
+    float* sdA = smem + Cfg::F_DA;          // dW V^T -> dT -> dA (lower)
+    float* sG = smem + Cfg::F_G;            // prefix sums of the clamped log-gate [C][DK]
+    float* sXa = smem + Cfg::F_X;
+    float* sBeta = smem + Cfg::F_BETA;
+    float* sDb1 = smem + Cfg::F_DB1;
+    float* sDb2 = smem + Cfg::F_DB2;
+    float* sDb3 = smem + Cfg::F_DB3;
+    float* sHd = smem + Cfg::F_HD;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, kg = lane >> 4;
     const long unit = blockIdx.x;
     UnitPos up;
     if (!unit_pos(um, unit, up)) return;
@@ -173,280 +380,442 @@ __global__ __launch_bounds__(256) void chunk_bwd_intra_kernel(
     const long tok0 = up.tok0;
     auto grow = [&](int t) -> long { return (tok0 + t) * H + h; };
     auto valid = [&](int t) -> bool { return t < cnt; };
+    const bool tri = wave < NB;             // owns the C x C column block I = wave
 
     const float* S = ck_state + unit * (long)DK * DV;      // start state [DK][DV]
     const float* dSn = ck_dS + unit * (long)DK * DV;       // cotangent of the end state
     const float* W = ck_w + unit * (long)C * DV;
     const float* dW = ck_dW + unit * (long)C * DV;
-    float* xdQt = scr + unit * (long)4 * C * DK;            // scratch: dQt, dWk, dKb, T^T dWk  [C][DK] each
-    float* xdWk = xdQt + C * DK;
-    float* xdKb = xdWk + C * DK;
-    float* xTdWk = xdKb + C * DK;
-    auto dOat = [&](int r, int jj) -> float { return valid(r) ? dO[grow(r) * DV + jj] : 0.f; };
 
-    // ---- load T, A, beta; prefix sums G of the clamped log-gate (chunk-local)
-    for (int u = tid; u < C * C; u += 256) {
-        sT[u] = ck_t[unit * (long)C * C + u];
-        sA[u] = ck_a[unit * (long)C * C + u];
+    // ---- phase 0: T, beta, prefix sums G of the clamped log-gate (chunk-local)
+    for (int u = tid; u < C * C; u += 256) sT[(u / C) * LC + u % C] = ck_t[unit * (long)C * C + u];
+    if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
+    for (int u = tid; u < 4 * C; u += 256) sDb3[u] = 0.f;
+    for (int u = tid; u < C * DK; u += 256) {
+        const int r = u / DK;
+        sG[u] = valid(r) ? clamp_g(gate_at(g, gate, grow(r), DK, u % DK)) : 0.f;
     }
-    if (tid < C) { sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f; sDb[tid] = 0.f; }
+    __syncthreads();
     for (int c = tid; c < DK; c += 256) {
         float s = 0.f;
         for (int r = 0; r < C; ++r) {
-            if (valid(r)) s += clamp_g(gate_at(g, gate, grow(r), DK, c));
+            s += sG[r * DK + c];
             sG[r * DK + c] = s;
         }
     }
     __syncthreads();
 
-    // ---- phase 1: contractions over the value channels
-    // dP = lower(dO W^T);  dT = dW (beta V)^T (the dWk part is added in phase 3)
-    for (int u = tid; u < C * C; u += 256) {
-        const int r = u / C, i = u % C;
-        float p = 0.f, t = 0.f;
-        if (i <= r) {
-            for (int jj = 0; jj < DV; ++jj) p += dOat(r, jj) * W[i * DV + jj];
-            if (valid(i)) {
-                for (int jj = 0; jj < DV; ++jj) t += dW[r * DV + jj] * to_f32(v[grow(i) * DV + jj]);
-                t *= sBeta[i];
+    // ---- phase 1: dQt = dO S^T, dWk = -dW S^T, dKb = W dS'^T, dgam, dP = dO W^T,
+    // dW V^T, contracted over the DV value channels 16 at a time
+    float* sWk = sXa;                       // dWk [C][DK]  (phase 3 operand)
+    float* sKt = sXa + C * LK;              // Kt = e^G K [C][DK]
+    floatx4 aQ[NB][KPW], aKb[NB][KPW];      // kept to the end
+    float dgam[KPW];
+    {
+        floatx4 aWk[NB][KPW], aP[NB], aV[NB];
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            aP[R] = zero4(); aV[R] = zero4();
+#pragma unroll
+            for (int p = 0; p < KPW; ++p) { aQ[R][p] = zero4(); aWk[R][p] = zero4(); aKb[R][p] = zero4(); }
+        }
+#pragma unroll
+        for (int p = 0; p < KPW; ++p) dgam[p] = 0.f;
+
+#define KDA_BWD_LOAD1(F, JS)                                                                      \
+    {                                                                                             \
+        const int jb = 16 * (JS) + 4 * kg;                                                        \
+        _Pragma("unroll") for (int R = 0; R < NB; ++R) {                                          \
+            const int r = 16 * R + lr;                                                            \
+            F.o[R] = valid(r) ? *reinterpret_cast<const floatx4*>(dO + grow(r) * DV + jb) : zero4(); \
+            F.w[R] = *reinterpret_cast<const floatx4*>(W + r * DV + jb);                          \
+            F.dw[R] = *reinterpret_cast<const floatx4*>(dW + r * DV + jb);                        \
+        }                                                                                         \
+        _Pragma("unroll") for (int p = 0; p < KPW; ++p) {                                         \
+            const int c = 16 * (wave + 4 * p) + lr;                                               \
+            F.s[p] = *reinterpret_cast<const floatx4*>(S + c * DV + jb);                          \
+            F.ds[p] = *reinterpret_cast<const floatx4*>(dSn + c * DV + jb);                       \
+        }                                                                                         \
+        if (tri) {                                                                                \
+            const int i = 16 * wave + lr;                                                         \
+            F.wi = *reinterpret_cast<const floatx4*>(W + i * DV + jb);                            \
+            F.v = valid(i) ? load4<T>(v + grow(i) * DV + jb) : zero4();                           \
+        }                                                                                         \
+    }
+#define KDA_BWD_MMA1(F)                                                                           \
+    {                                                                                             \
+        _Pragma("unroll") for (int R = 0; R < NB; ++R) {                                          \
+            _Pragma("unroll") for (int p = 0; p < KPW; ++p) {                                     \
+                aQ[R][p] = mfma16(aQ[R][p], F.o[R], F.s[p]);                                      \
+                aWk[R][p] = mfma16(aWk[R][p], F.dw[R], F.s[p]);                                   \
+                aKb[R][p] = mfma16(aKb[R][p], F.w[R], F.ds[p]);                                   \
+            }                                                                                     \
+            if (tri && R >= wave) {                                                               \
+                aP[R] = mfma16(aP[R], F.o[R], F.wi);                                              \
+                aV[R] = mfma16(aV[R], F.dw[R], F.v);                                              \
+            }                                                                                     \
+        }                                                                                         \
+        _Pragma("unroll") for (int p = 0; p < KPW; ++p)                                           \
+            dgam[p] += F.s[p][0] * F.ds[p][0] + F.s[p][1] * F.ds[p][1] + F.s[p][2] * F.ds[p][2] + \
+                       F.s[p][3] * F.ds[p][3];                                                    \
+    }
+        BwdFrag<NB, KPW> fa, fb;
+        fa.wi = zero4(); fa.v = zero4(); fb.wi = zero4(); fb.v = zero4();
+        KDA_BWD_LOAD1(fa, 0);
+#pragma unroll 1
+        for (int js = 0; js < NVB; js += 2) {
+            KDA_BWD_LOAD1(fb, js + 1);
+            KDA_BWD_MMA1(fa);
+            KDA_BWD_LOAD1(fa, js + 2 < NVB ? js + 2 : js);  // the last one is a harmless reload
+            KDA_BWD_MMA1(fb);
+        }
+#undef KDA_BWD_LOAD1
+#undef KDA_BWD_MMA1
+
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int p = 0; p < KPW; ++p)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sWk[(16 * R + 4 * kg + e) * LK + 16 * (wave + 4 * p) + lr] = -aWk[R][p][e];
+#pragma unroll
+        for (int p = 0; p < KPW; ++p) dgam[p] = col_sum4(dgam[p]);
+        if (tri) {
+            // column block I = wave of dP and dW V^T (lower part; zero above), and
+            // the first dbeta term: (T^T dW V^T)_ii = sum_r T_ri (dW V^T)_ri
+            const int i = 16 * wave + lr;
+            float db = 0.f;
+#pragma unroll
+            for (int R = 0; R < NB; ++R)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * R + 4 * kg + e;
+                    float pv = 0.f, vv = 0.f;
+                    if (R >= wave && i <= r) { pv = aP[R][e]; vv = aV[R][e]; }
+                    sdP[r * LC + i] = pv;
+                    sdA[r * LC + i] = vv;
+                    db += sT[r * LC + i] * vv;
+                }
+            db = col_sum4(db);
+            if (kg == 0) sDb1[i] = db;
+        }
+    }
+    // dV = Diag(beta) T^T dW: output tiles (R, J), wave w taking J = w, w + 4, ...
+#pragma unroll
+    for (int qv = 0; qv < VPW; ++qv) {
+        const int J = wave + 4 * qv;
+        float bcol[NB][4];
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) bcol[I][m] = dW[(16 * I + 4 * kg + m) * DV + 16 * J + lr];
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int I = R; I < NB; ++I)                            // T[i][r] = 0 for i < r
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc = mfma4(acc, sT[(16 * I + 4 * kg + m) * LC + 16 * R + lr], bcol[I][m]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                if (valid(r)) dv[grow(r) * DV + 16 * J + lr] = sBeta[r] * acc[e];
             }
         }
-        sdP[u] = p;
-        sdT[u] = t;
     }
-    // dV = beta T^T dW;  dbeta += rows of (T^T dW) V (row sums in a fixed order)
-    for (int u = tid; u < C * DV; u += 256) {
-        const int r = u / DV, jj = u % DV;
-        float x = 0.f;
-        for (int i = r; i < C; ++i) x += sT[i * C + r] * dW[i * DV + jj];
-        float pr = 0.f;
-        if (valid(r)) {
-            dv[grow(r) * DV + jj] = sBeta[r] * x;
-            pr = x * to_f32(v[grow(r) * DV + jj]);
-        }
-        sSt[u] = pr;
-    }
-    __syncthreads();
-    if (tid < C) {
-        float x = 0.f;
-        for (int jj = 0; jj < DV; ++jj) x += sSt[tid * DV + jj];
-        sDb[tid] = x;
-    }
-    __syncthreads();
-    // ---- phase 2: dQt = dO S^T, dWk = -dW S^T, dKb = W dS'^T, dgam = rows of dS' * S
-    for (int u = tid; u < C * DK; u += 256) {
-        const int r = u / DK, c = u % DK;
-        float a = 0.f, b = 0.f, e = 0.f;
-        for (int jj = 0; jj < DV; ++jj) {
-            const float s = S[c * DV + jj];
-            a += dOat(r, jj) * s;
-            b += dW[r * DV + jj] * s;
-            e += W[r * DV + jj] * dSn[c * DV + jj];
-        }
-        xdQt[u] = a;
-        xdWk[u] = -b;
-        xdKb[u] = e;
-    }
-    for (int c = tid; c < DK; c += 256) {
-        float x = 0.f;
-        for (int jj = 0; jj < DV; ++jj) x += dSn[c * DV + jj] * S[c * DV + jj];
-        sDgm[c] = x;
-    }
-    // Kt = e^G K into the staging area
-    for (int u = tid; u < C * DK; u += 256) {
-        const int r = u / DK, c = u % DK;
-        sSt[u] = valid(r) ? __expf(sG[u]) * to_f32(k[grow(r) * DK + c]) : 0.f;
-    }
-    __syncthreads();                                        // scratch, sdT, sSt complete
-
-    // ---- phase 3: dT += dWk (beta Kt)^T;  T^T dWk;  dbeta += rows of (T^T dWk) Kt
-    for (int u = tid; u < C * C; u += 256) {
-        const int r = u / C, i = u % C;
-        if (i <= r) {
-            float t = 0.f;
-            for (int c = 0; c < DK; ++c) t += xdWk[r * DK + c] * sSt[i * DK + c];
-            sdT[u] += sBeta[i] * t;
-        }
-    }
-    for (int u = tid; u < C * DK; u += 256) {
-        const int r = u / DK, c = u % DK;
-        float x = 0.f;
-        for (int i = r; i < C; ++i) x += sT[i * C + r] * xdWk[i * DK + c];
-        xTdWk[u] = x;
-    }
-    __syncthreads();
-    if (tid < C) {                                          // dbeta += rows of (T^T dWk) Kt
-        float x = 0.f;
-        for (int c = 0; c < DK; ++c) x += xTdWk[tid * DK + c] * sSt[tid * DK + c];
-        sDb[tid] += x;
+    // ---- phase 2: Kt = e^G K
+    for (int u = tid; u < C * DK / 4; u += 256) {
+        const int r = (4 * u) / DK, c0 = (4 * u) % DK;
+        floatx4 kk = valid(r) ? load4<T>(k + grow(r) * DK + c0) : zero4();
+#pragma unroll
+        for (int x = 0; x < 4; ++x) kk[x] *= __expf(sG[r * DK + c0 + x]);
+        *reinterpret_cast<floatx4*>(sKt + r * LK + c0) = kk;
     }
     __syncthreads();
 
-    // ---- phase 4: dM = -strict_lower(T^T dT T^T);  X = T^T dT into the staging area
-    for (int u = tid; u < C * C; u += 256) {
-        const int r = u / C, i = u % C;
-        float x = 0.f;
-        for (int m = r; m < C; ++m) x += sT[m * C + r] * sdT[m * C + i];   // T lower: T^T[r][m] = T[m][r], m >= r
-        sSt[u] = x;
-    }
-    __syncthreads();
-    for (int u = tid; u < C * C; u += 256) {
-        const int r = u / C, i = u % C;
-        float x = 0.f;
-        if (i < r) {
-            for (int m = 0; m <= i; ++m) x += sSt[r * C + m] * sT[i * C + m];  // (X T^T)[r][i]: T[i][m], m <= i
+    // ---- phase 3: dT = Diag-columns(beta) (dW V^T + dWk Kt^T) on the lower tiles
+    // (R, I = wave); T^T dWk on this wave's channel blocks, with the second dbeta
+    // term, rows of (T^T dWk) Kt
+    if (tri) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            if (R < wave) continue;
+            floatx4 acc = zero4();
+#pragma unroll 4
+            for (int c0 = 0; c0 < DK; c0 += 16)
+                acc = mfma16(acc, lds4(sWk + (16 * R + lr) * LK + c0 + 4 * kg),
+                             lds4(sKt + (16 * wave + lr) * LK + c0 + 4 * kg));
+            const int i = 16 * wave + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                if (i <= r) sdA[r * LC + i] = sBeta[i] * (sdA[r * LC + i] + acc[e]);
+            }
         }
-        sdT[u] = -x;                                                          // dM (strictly lower)
     }
-    __syncthreads();
-    // dbeta += rows of dM A;  dA = Diag(beta) dM (in place)
-    if (tid < C) {
-        float x = 0.f;
-        for (int i = 0; i < C; ++i) x += sdT[tid * C + i] * sA[tid * C + i];
-        sDb[tid] += x;
+    floatx4 aTd[NB][KPW];                   // T^T dWk, kept to the end
+    {
+        float db[NB][4];
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) db[R][e] = 0.f;
+#pragma unroll
+        for (int p = 0; p < KPW; ++p) {
+            const int cb = 16 * (wave + 4 * p);
+#pragma unroll
+            for (int R = 0; R < NB; ++R) {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int I = R; I < NB; ++I)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int i = 16 * I + 4 * kg + m;
+                        acc = mfma4(acc, sT[i * LC + 16 * R + lr], sWk[i * LK + cb + lr]);
+                    }
+                aTd[R][p] = acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) db[R][e] += acc[e] * sKt[(16 * R + 4 * kg + e) * LK + cb + lr];
+            }
+        }
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = row_sum16(db[R][e]);
+                if (lr == 0) sDb2[wave * C + 16 * R + 4 * kg + e] = x;
+            }
     }
-    __syncthreads();
-    for (int u = tid; u < C * C; u += 256) sdT[u] *= sBeta[u / C];
+    // inputs of the last phase for this wave's elements, loaded ahead
+    float kv[KPW][NB][4], qv[KPW][NB][4], gv[KPW][NB][4];
+#pragma unroll
+    for (int p = 0; p < KPW; ++p)
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e, c = 16 * (wave + 4 * p) + lr;
+                const bool ok = valid(r);
+                kv[p][R][e] = ok ? to_f32(k[grow(r) * DK + c]) : 0.f;
+                qv[p][R][e] = ok ? to_f32(q[grow(r) * DK + c]) : 0.f;
+                gv[p][R][e] = ok && gate == GATE_CHANNEL ? g[grow(r) * DK + c] : 0.f;
+            }
     __syncthreads();
 
-    // ---- phase 5: per tile of DKT channels: decays, pairwise decays, prefix-sum adjoint.
-    // Pairwise factors e^{G_r - G_i} (i <= r) are split at 16-row block boundaries
-    // so that every stored factor is <= 1: with Gs(R) the prefix sum before block R
-    // and Gm(I) the one at the end of block I,
+    // ---- phase 4: X = T^T dT (lower tiles), then dM = -strict_lower(X T^T),
+    // dbeta += rows of dM A, dA = Diag(beta) dM
+    float* sXm = sXa;
+    if (tri) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            if (R < wave) continue;
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int M = R; M < NB; ++M)                            // T[m][r] = 0 for m < r
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const int m = 16 * M + 4 * kg + mm;
+                    acc = mfma4(acc, sT[m * LC + 16 * R + lr], sdA[m * LC + 16 * wave + lr]);
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sXm[(16 * R + 4 * kg + e) * LC + 16 * wave + lr] = acc[e];
+        }
+    }
+    __syncthreads();
+    if (tri) {
+        const int i = 16 * wave + lr;
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            if (R < wave) continue;
+            float av[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) av[e] = ck_a[unit * (long)C * C + (16 * R + 4 * kg + e) * C + i];
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int M = 0; M < NB; ++M) {                          // T[i][m] = 0 for m > i
+                if (M > wave) break;
+                acc = mfma16(acc, lds4(sXm + (16 * R + lr) * LC + 16 * M + 4 * kg),
+                             lds4(sT + (16 * wave + lr) * LC + 16 * M + 4 * kg));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                const float dm = i < r ? -acc[e] : 0.f;
+                const float x = row_sum16(dm * av[e]);
+                if (lr == 0) sDb3[wave * C + r] = x;
+                sdA[r * LC + i] = sBeta[r] * dm;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 5, per wave over its channel blocks: the decays, the pairwise decays
+    // of A and P, the prefix-sum adjoint.  Pairwise factors e^{G_r - G_i} (i <= r)
+    // are split at 16-row block boundaries so that every stored factor is <= 1: with
+    // Gs(R) the prefix sum before block R and Gm(I) the one at the end of block I,
     //   Er_r = e^{G_r - Gs(R(r))},  Ei_r = e^{Gm(R(r)) - G_r},  B_RI = e^{Gs(R) - Gm(I)} (I < R).
     // Inside one block, e^{G_r - G_i} = Er_r / Er_i, exact while the block's log-gate
     // sum stays above -SAFE_SPAN; otherwise that channel's block is done term by term.
-    constexpr int NTILE = C * DKT;
-    float* sEr = sSt;                      // [C][DKT] each
-    float* sKm = sEr + NTILE;              // K Ei   (K scaled to its block end)
-    float* sKs = sKm + NTILE;              // K Er
-    float* sQs = sKs + NTILE;              // Q Er
-    float* sKi = sQs + NTILE;              // K / Er (safe blocks)
-    float* sdG = sKi + NTILE;              // dG, then dg
-    static_assert(6 * NTILE <= Cfg::ST_FLOATS, "phase 5 staging");
-    static_assert(NTILE % 256 == 0, "phase 5 thread mapping");
-    for (int c0 = 0; c0 < DK; c0 += DKT) {
-        for (int u = tid; u < NTILE; u += 256) {
-            const int r = u / DKT, c = c0 + u % DKT, R = r / 16;
-            const float G = sG[r * DK + c];
-            const float Gs = R ? sG[(16 * R - 1) * DK + c] : 0.f, Gm = sG[(16 * R + 15) * DK + c];
-            const float er = __expf(G - Gs), ei = __expf(Gm - G);
-            const float kk = valid(r) ? to_f32(k[grow(r) * DK + c]) : 0.f;
-            const float qq = valid(r) ? to_f32(q[grow(r) * DK + c]) : 0.f;
-            sEr[u] = er;
-            sKm[u] = kk * ei;
-            sKs[u] = kk * er;
-            sQs[u] = qq * er;
-            sKi[u] = Gm - Gs >= -SAFE_SPAN ? kk / er : 0.f;
-        }
-        __syncthreads();
-        {
-            constexpr int RPT = NTILE / 256;
-            const int cc = tid % DKT, c = c0 + cc, rq = (tid / DKT) * RPT;
-            const float GC = sG[(C - 1) * DK + c];
+    float* sKm = sXa + wave * 4 * TL;       // [16 channels][C] each: K Ei
+    float* sKs = sKm + TL;                  // K Er
+    float* sQs = sKs + TL;                  // Q Er
+    float* sKi = sQs + TL;                  // K / Er (safe blocks)
+    float hsum[NB][4];
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                const int r = rq + m, R = r / 16, u = r * DKT + cc;
-                const float G = sG[r * DK + c], E = __expf(G), F = __expf(GC - G);
-                const float Gs_R = R ? sG[(16 * R - 1) * DK + c] : 0.f, Gm_R = sG[(16 * R + 15) * DK + c];
-                const float er = sEr[u];
-                const float kc = valid(r) ? to_f32(k[grow(r) * DK + c]) : 0.f;
-                const float qc = valid(r) ? to_f32(q[grow(r) * DK + c]) : 0.f;
-                const float dKt = sBeta[r] * xTdWk[r * DK + c], dQt = xdQt[r * DK + c], dKb = xdKb[r * DK + c];
-                float dK = E * dKt + F * dKb, dQ = E * dQt;
-                float dG = E * kc * dKt + E * qc * dQt - F * kc * dKb;
-                float XA = 0.f, XP = 0.f, YA = 0.f, YP = 0.f;
-                for (int I = 0; I < R; ++I) {                      // earlier column blocks
-                    const float Gm_I = sG[(16 * I + 15) * DK + c];
-                    float xa = 0.f, xp = 0.f;
-                    for (int i = 16 * I; i < 16 * I + 16; ++i) {
-                        xa += sdT[r * C + i] * sKm[i * DKT + cc];
-                        xp += sdP[r * C + i] * sKm[i * DKT + cc];
-                    }
-                    const float f = __expf(Gs_R - Gm_I);
-                    XA += f * xa; XP += f * xp;
-                }
-                XA *= er; XP *= er;
-                for (int I = R + 1; I < NB; ++I) {                 // later row blocks
-                    const float Gs_I = sG[(16 * I - 1) * DK + c];
-                    float ya = 0.f, yp = 0.f;
-                    for (int rr = 16 * I; rr < 16 * I + 16; ++rr) {
-                        ya += sdT[rr * C + r] * sKs[rr * DKT + cc];
-                        yp += sdP[rr * C + r] * sQs[rr * DKT + cc];
-                    }
-                    const float f = __expf(Gs_I - Gm_R);
-                    YA += f * ya; YP += f * yp;
-                }
-                YA *= __expf(Gm_R - G);
-                YP *= __expf(Gm_R - G);
-                // the diagonal block
-                if (Gm_R - Gs_R >= -SAFE_SPAN) {
-                    float xa = 0.f, xp = 0.f, ya = 0.f, yp = 0.f;
+    for (int R = 0; R < NB; ++R)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hsum[R][e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < KPW; ++p) {
+        const int c = 16 * (wave + 4 * p) + lr;
+        float gs[NB], gm[NB];
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            gs[R] = R ? sG[(16 * R - 1) * DK + c] : 0.f;
+            gm[R] = sG[(16 * R + 15) * DK + c];
+        }
+        const float GC = sG[(C - 1) * DK + c];
+        wave_lds_sync();                                    // the previous block's readers are done
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            floatx4 km, ks, qs, ki;
+            const bool safe = gm[R] - gs[R] >= -SAFE_SPAN;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float G = sG[(16 * R + 4 * kg + e) * DK + c];
+                const float er = __expf(G - gs[R]), ei = __expf(gm[R] - G);
+                km[e] = kv[p][R][e] * ei;
+                ks[e] = kv[p][R][e] * er;
+                qs[e] = qv[p][R][e] * er;
+                ki[e] = safe ? kv[p][R][e] / er : 0.f;
+            }
+            const int o = lr * LC + 16 * R + 4 * kg;
+            *reinterpret_cast<floatx4*>(sKm + o) = km;
+            *reinterpret_cast<floatx4*>(sKs + o) = ks;
+            *reinterpret_cast<floatx4*>(sQs + o) = qs;
+            *reinterpret_cast<floatx4*>(sKi + o) = ki;
+        }
+        wave_lds_sync();
+        float dGv[NB][4], gcp = 0.f;
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            floatx4 xa = zero4(), xp = zero4(), ya = zero4(), yp = zero4();
+#pragma unroll
+            for (int I = 0; I < R; ++I) {                          // earlier column blocks
+                const floatx4 fk = lds4(sKm + lr * LC + 16 * I + 4 * kg);
+                const floatx4 ta = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * I + 4 * kg), fk);
+                const floatx4 tp = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * I + 4 * kg), fk);
+                const float b = __expf(gs[R] - gm[I]);
+                xa += b * ta;
+                xp += b * tp;
+            }
+#pragma unroll
+            for (int I = R + 1; I < NB; ++I) {                     // later row blocks
+                const floatx4 ta = mfma16(zero4(), col4(sdA + (16 * I + 4 * kg) * LC + 16 * R + lr, LC),
+                                          lds4(sKs + lr * LC + 16 * I + 4 * kg));
+                const floatx4 tp = mfma16(zero4(), col4(sdP + (16 * I + 4 * kg) * LC + 16 * R + lr, LC),
+                                          lds4(sQs + lr * LC + 16 * I + 4 * kg));
+                const float b = __expf(gs[I] - gm[R]);
+                ya += b * ta;
+                yp += b * tp;
+            }
+            // the diagonal block
+            const floatx4 fki = lds4(sKi + lr * LC + 16 * R + 4 * kg);
+            const floatx4 xad = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * R + 4 * kg), fki);
+            const floatx4 xpd = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * R + 4 * kg), fki);
+            const floatx4 yad = mfma16(zero4(), col4(sdA + (16 * R + 4 * kg) * LC + 16 * R + lr, LC),
+                                       lds4(sKs + lr * LC + 16 * R + 4 * kg));
+            const floatx4 ypd = mfma16(zero4(), col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC),
+                                       lds4(sQs + lr * LC + 16 * R + 4 * kg));
+            const bool safe = gm[R] - gs[R] >= -SAFE_SPAN;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                const float G = sG[r * DK + c];
+                const float er = __expf(G - gs[R]), ei = __expf(gm[R] - G);
+                float XA = er * xa[e], XP = er * xp[e], YA = ei * ya[e], YP = ei * yp[e];
+                if (safe) {
+                    XA += er * xad[e];
+                    XP += er * xpd[e];
+                    YA += yad[e] / er;
+                    YP += ypd[e] / er;
+                } else {                                            // term by term
                     for (int i = 16 * R; i < 16 * R + 16; ++i) {
-                        if (i < r) xa += sdT[r * C + i] * sKi[i * DKT + cc];
-                        if (i <= r) xp += sdP[r * C + i] * sKi[i * DKT + cc];
-                        if (i > r) ya += sdT[i * C + r] * sKs[i * DKT + cc];
-                        if (i >= r) yp += sdP[i * C + r] * sQs[i * DKT + cc];
-                    }
-                    XA += er * xa; XP += er * xp;
-                    YA += ya / er; YP += yp / er;
-                } else {                                           // term by term
-                    for (int i = 16 * R; i < 16 * R + 16; ++i) {
+                        const float Gi = sG[i * DK + c];
                         const float ki = valid(i) ? to_f32(k[grow(i) * DK + c]) : 0.f;
                         const float qi = valid(i) ? to_f32(q[grow(i) * DK + c]) : 0.f;
-                        const float wd = __expf(G - sG[i * DK + c]), wu = __expf(sG[i * DK + c] - G);
-                        if (i < r) XA += sdT[r * C + i] * ki * wd;
-                        if (i <= r) XP += sdP[r * C + i] * ki * wd;
-                        if (i > r) YA += sdT[i * C + r] * ki * wu;
-                        if (i >= r) YP += sdP[i * C + r] * qi * wu;
+                        if (i <= r) {
+                            const float wd = __expf(G - Gi);
+                            if (i < r) XA += sdA[r * LC + i] * ki * wd;
+                            XP += sdP[r * LC + i] * ki * wd;
+                        }
+                        if (i >= r) {
+                            const float wu = __expf(Gi - G);
+                            if (i > r) YA += sdA[i * LC + r] * ki * wu;
+                            YP += sdP[i * LC + r] * qi * wu;
+                        }
                     }
                 }
-                dK += XA + YA + YP;
-                dQ += XP;
-                dG += kc * XA - kc * YA + qc * XP - kc * YP;
+                const float E = __expf(G), F = __expf(GC - G);
+                const float kc = kv[p][R][e], qc = qv[p][R][e];
+                const float dKt = sBeta[r] * aTd[R][p][e], dQt = aQ[R][p][e], dKb = aKb[R][p][e];
+                const float dK = E * dKt + F * dKb + XA + YA + YP, dQ = E * dQt + XP;
+                dGv[R][e] = E * kc * dKt + E * qc * dQt - F * kc * dKb + kc * XA - kc * YA + qc * XP - kc * YP;
+                gcp += F * kc * dKb;
                 if (valid(r)) {
                     dq[grow(r) * DK + c] = dQ;
                     dk[grow(r) * DK + c] = dK;
                 }
-                sdG[u] = dG;
             }
         }
-        __syncthreads();
-        // prefix-sum adjoint: dg_t = dG_C + sum_{r >= t} dG_r (G_C is the last row's
-        // prefix sum; rows past the end of the sequence have g = 0 and add nothing)
-        if (tid < DKT) {
-            const int c = c0 + tid;
-            const float GC = sG[(C - 1) * DK + c];
-            float dGC = sDgm[c] * __expf(GC);                  // gam = e^{G_C}
-            for (int r = 0; r < C; ++r) {                      // Kb = e^{G_C - G} K
-                const float kr = valid(r) ? to_f32(k[grow(r) * DK + c]) : 0.f;
-                dGC += __expf(GC - sG[r * DK + c]) * kr * xdKb[r * DK + c];
-            }
-            float run = dGC;
-            for (int r = C - 1; r >= 0; --r) {
-                run += sdG[r * DKT + tid];
-                float gr = run;
-                if (valid(r) && gate != GATE_NONE && gate_at(g, gate, grow(r), DK, c) < G_FLOOR) gr = 0.f;
-                sdG[r * DKT + tid] = gr;                       // the forward floors the log-gate
-            }
-        }
-        __syncthreads();
-        if (gate == GATE_CHANNEL) {
-            for (int u = tid; u < NTILE; u += 256) {
-                const int r = u / DKT, c = c0 + u % DKT;
-                if (valid(r)) dg[grow(r) * DK + c] = sdG[u];
-            }
-        } else if (gate == GATE_HEAD) {
-            if (tid < C && valid(tid)) {
-                float sum = 0.f;
-                for (int cc = 0; cc < DKT; ++cc) sum += sdG[tid * DKT + cc];
-                if (c0 == 0) dg[grow(tid)] = sum;
-                else dg[grow(tid)] += sum;
+        // prefix-sum adjoint: dg_t = dG_C + sum_{r >= t} dG_r, with dG_C from gam =
+        // e^{G_C} and Kb = e^{G_C - G} K; a suffix sum over the rows, last block first
+        // (rows past the sequence end have dG = 0)
+        float carry = dgam[p] * __expf(GC) + col_sum4(gcp);
+#pragma unroll
+        for (int R = NB - 1; R >= 0; --R) {
+            float sfx[4];
+            sfx[3] = dGv[R][3];
+            sfx[2] = sfx[3] + dGv[R][2];
+            sfx[1] = sfx[2] + dGv[R][1];
+            sfx[0] = sfx[1] + dGv[R][0];
+            const float t1 = __shfl(sfx[0], lane + 16), t2 = __shfl(sfx[0], lane + 32), t3 = __shfl(sfx[0], lane + 48);
+            const float after = (kg < 3 ? t1 : 0.f) + (kg < 2 ? t2 : 0.f) + (kg < 1 ? t3 : 0.f);
+            const float base = carry + after;
+            carry += col_sum4(sfx[0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                const float val = base + sfx[e];
+                if (gate == GATE_CHANNEL) {
+                    // the forward floors the log-gate at G_FLOOR: no gradient below it
+                    if (valid(r)) dg[grow(r) * DK + c] = gv[p][R][e] < G_FLOOR ? 0.f : val;
+                } else {
+                    hsum[R][e] += row_sum16(val);
+                }
             }
         }
-        __syncthreads();
     }
-    if (tid < C && valid(tid)) dbeta[grow(tid)] = sDb[tid];
+    if (gate == GATE_HEAD) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (lr == 0) sHd[wave * C + 16 * R + 4 * kg + e] = hsum[R][e];
+    }
+    __syncthreads();
+    if (tid < C && valid(tid)) {
+        float db = sDb1[tid];
+        for (int w = 0; w < 4; ++w) db += sDb2[w * C + tid];
+        for (int w = 0; w < 4; ++w) db += sDb3[w * C + tid];
+        dbeta[grow(tid)] = db;
+        if (gate == GATE_HEAD) {
+            float s = 0.f;
+            for (int w = 0; w < 4; ++w) s += sHd[w * C + tid];
+            dg[grow(tid)] = g[grow(tid)] < G_FLOOR ? 0.f : s;
+        }
+    }
 }
 
 // ================================================================ host side
@@ -471,7 +840,7 @@ static hipError_t launch_bwd(const BwdArgs& b) {
         if (e != hipSuccess || units == 0) return e;
         hipLaunchKernelGGL((chunk_bwd_intra_kernel<T, DK, DV, C>), dim3((unsigned)units), dim3(256), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, b.dO, a.ck_state, b.ck_dS,
-                           a.ck_w, b.ck_dW, a.ck_t, a.ck_a, b.scratch, b.dq, b.dk, b.dv, b.dg, b.dbeta,
+                           a.ck_w, b.ck_dW, a.ck_t, a.ck_a, b.dq, b.dk, b.dv, b.dg, b.dbeta,
                            unit_map(a), a.gate);
         return hipGetLastError();
     }
@@ -505,7 +874,6 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
     L.w = off;     off = al(off + units * C * dv * 4);
     L.dS = off;    off = al(off + units * dk * dv * 4);
     L.dW = off;    off = al(off + units * C * dv * 4);
-    L.scr = off;   off = al(off + units * 4 * C * dk * 4);
     L.total = off;
     return L;
 }

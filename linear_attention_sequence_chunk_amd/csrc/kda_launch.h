@@ -80,13 +80,12 @@ struct BwdArgs {
     float* dS0;                 // [B,H,dk,dv] or NULL
     float* ck_dS;               // cotangent of each chunk's end state, [unit][dk][dv]
     float* ck_dW;               // dW of each chunk, [unit][C][dv]
-    float* scratch;             // [unit][4][C][dk]
 };
 // Workspace of the backward pass: the forward workspace (generic format) then
-// the checkpoints and scratch, per unit.
+// the checkpoints, per unit.
 struct BwdLayout {
     WsLayout fwd;
-    size_t t, a, state, w, dS, dW, scr, total;
+    size_t t, a, state, w, dS, dW, total;
 };
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C);
 bool bwd_supported(int dk, int dv, int C, bool in_bf16);
