@@ -380,6 +380,9 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     const long tok0 = up.tok0;
     auto grow = [&](int t) -> long { return (tok0 + t) * H + h; };
     auto valid = [&](int t) -> bool { return t < cnt; };
+    // a row past the sequence end reads row 0 (and the value is then dropped), so
+    // that loads need no branch and can all be in flight together
+    auto crow = [&](int t) -> long { return grow(t < cnt ? t : 0); };
     const bool tri = wave < NB;             // owns the C x C column block I = wave
 
     const float* S = ck_state + unit * (long)DK * DV;      // start state [DK][DV]
@@ -388,20 +391,50 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     const float* dW = ck_dW + unit * (long)C * DV;
 
     // ---- phase 0: T, beta, prefix sums G of the clamped log-gate (chunk-local)
-    for (int u = tid; u < C * C; u += 256) sT[(u / C) * LC + u % C] = ck_t[unit * (long)C * C + u];
-    if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
-    for (int u = tid; u < 4 * C; u += 256) sDb3[u] = 0.f;
-    for (int u = tid; u < C * DK; u += 256) {
-        const int r = u / DK;
-        sG[u] = valid(r) ? clamp_g(gate_at(g, gate, grow(r), DK, u % DK)) : 0.f;
-    }
-    __syncthreads();
-    for (int c = tid; c < DK; c += 256) {
-        float s = 0.f;
-        for (int r = 0; r < C; ++r) {
-            s += sG[r * DK + c];
-            sG[r * DK + c] = s;
+    {
+        constexpr int NT = C * C / 256 > 0 ? C * C / 256 : 1, NG = C * DK / 256;
+        float tv[NT], gl[NG];
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int u = tid + 256 * x;
+            tv[x] = u < C * C ? ck_t[unit * (long)C * C + u] : 0.f;
         }
+#pragma unroll
+        for (int x = 0; x < NG; ++x) {
+            const int u = tid + 256 * x, r = u / DK;
+            gl[x] = gate_at(g, gate, crow(r), DK, u % DK);
+        }
+        const float bt = tid < C ? beta[crow(tid)] : 0.f;
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int u = tid + 256 * x;
+            if (u < C * C) sT[(u / C) * LC + u % C] = tv[x];
+        }
+        if (tid < C) sBeta[tid] = valid(tid) ? bt : 0.f;
+        for (int u = tid; u < 4 * C; u += 256) sDb3[u] = 0.f;
+        // prefix sums down the rows: thread t holds channel t % DK of rows
+        // NSEG x + t / DK; running sums of its own rows, then the other threads'
+        // running sums of the same channel complete each prefix
+        constexpr int NSEG = 256 / DK;
+        const int hs = tid / DK;
+        float run = 0.f;
+#pragma unroll
+        for (int x = 0; x < NG; ++x) {
+            run += valid(NSEG * x + hs) ? clamp_g(gl[x]) : 0.f;
+            gl[x] = run;
+            sG[tid + 256 * x] = run;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < NG; ++x)
+#pragma unroll
+            for (int h2 = 0; h2 < NSEG; ++h2) {
+                if (h2 < hs) gl[x] += sG[(NSEG * x + h2) * DK + tid % DK];
+                else if (h2 > hs && x > 0) gl[x] += sG[(NSEG * (x - 1) + h2) * DK + tid % DK];
+            }
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < NG; ++x) sG[tid + 256 * x] = gl[x];
     }
     __syncthreads();
 
@@ -427,7 +460,8 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
         const int jb = 16 * (JS) + 4 * kg;                                                        \
         _Pragma("unroll") for (int R = 0; R < NB; ++R) {                                          \
             const int r = 16 * R + lr;                                                            \
-            F.o[R] = valid(r) ? *reinterpret_cast<const floatx4*>(dO + grow(r) * DV + jb) : zero4(); \
+            const floatx4 o_ = *reinterpret_cast<const floatx4*>(dO + crow(r) * DV + jb);         \
+            F.o[R] = valid(r) ? o_ : zero4();                                                     \
             F.w[R] = *reinterpret_cast<const floatx4*>(W + r * DV + jb);                          \
             F.dw[R] = *reinterpret_cast<const floatx4*>(dW + r * DV + jb);                        \
         }                                                                                         \
@@ -439,7 +473,8 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
         if (tri) {                                                                                \
             const int i = 16 * wave + lr;                                                         \
             F.wi = *reinterpret_cast<const floatx4*>(W + i * DV + jb);                            \
-            F.v = valid(i) ? load4<T>(v + grow(i) * DV + jb) : zero4();                           \
+            const floatx4 v_ = load4<T>(v + crow(i) * DV + jb);                                   \
+            F.v = valid(i) ? v_ : zero4();                                                        \
         }                                                                                         \
     }
 #define KDA_BWD_MMA1(F)                                                                           \
@@ -525,12 +560,24 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
         }
     }
     // ---- phase 2: Kt = e^G K
-    for (int u = tid; u < C * DK / 4; u += 256) {
-        const int r = (4 * u) / DK, c0 = (4 * u) % DK;
-        floatx4 kk = valid(r) ? load4<T>(k + grow(r) * DK + c0) : zero4();
+    {
+        constexpr int NK = C * DK / 4 / 256 > 0 ? C * DK / 4 / 256 : 1;
+        floatx4 kl[NK];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) kk[x] *= __expf(sG[r * DK + c0 + x]);
-        *reinterpret_cast<floatx4*>(sKt + r * LK + c0) = kk;
+        for (int x = 0; x < NK; ++x) {
+            const int u = tid + 256 * x, r = (4 * u) / DK, c0 = (4 * u) % DK;
+            kl[x] = u < C * DK / 4 ? load4<T>(k + crow(r < C ? r : 0) * DK + c0) : zero4();
+        }
+#pragma unroll
+        for (int x = 0; x < NK; ++x) {
+            const int u = tid + 256 * x, r = (4 * u) / DK, c0 = (4 * u) % DK;
+            if (u < C * DK / 4) {
+                floatx4 kk = valid(r) ? kl[x] : zero4();
+#pragma unroll
+                for (int y = 0; y < 4; ++y) kk[y] *= __expf(sG[r * DK + c0 + y]);
+                *reinterpret_cast<floatx4*>(sKt + r * LK + c0) = kk;
+            }
+        }
     }
     __syncthreads();
 
@@ -597,9 +644,12 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * R + 4 * kg + e, c = 16 * (wave + 4 * p) + lr;
                 const bool ok = valid(r);
-                kv[p][R][e] = ok ? to_f32(k[grow(r) * DK + c]) : 0.f;
-                qv[p][R][e] = ok ? to_f32(q[grow(r) * DK + c]) : 0.f;
-                gv[p][R][e] = ok && gate == GATE_CHANNEL ? g[grow(r) * DK + c] : 0.f;
+                const long o = crow(r) * DK + c;
+                const float kx = to_f32(k[o]), qx = to_f32(q[o]);
+                const float gx = gate == GATE_CHANNEL ? g[o] : 0.f;
+                kv[p][R][e] = ok ? kx : 0.f;
+                qv[p][R][e] = ok ? qx : 0.f;
+                gv[p][R][e] = gx;
             }
     __syncthreads();
 
@@ -625,12 +675,15 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     __syncthreads();
     if (tri) {
         const int i = 16 * wave + lr;
+        float avs[NB][4];
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) avs[R][e] = ck_a[unit * (long)C * C + (16 * R + 4 * kg + e) * C + i];
 #pragma unroll
         for (int R = 0; R < NB; ++R) {
             if (R < wave) continue;
-            float av[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) av[e] = ck_a[unit * (long)C * C + (16 * R + 4 * kg + e) * C + i];
+            const float* av = avs[R];
             floatx4 acc = zero4();
 #pragma unroll
             for (int M = 0; M < NB; ++M) {                          // T[i][m] = 0 for m > i
@@ -688,7 +741,7 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
                 km[e] = kv[p][R][e] * ei;
                 ks[e] = kv[p][R][e] * er;
                 qs[e] = qv[p][R][e] * er;
-                ki[e] = safe ? kv[p][R][e] / er : 0.f;
+                ki[e] = safe ? kv[p][R][e] * __expf(gs[R] - G) : 0.f;
             }
             const int o = lr * LC + 16 * R + 4 * kg;
             *reinterpret_cast<floatx4*>(sKm + o) = km;
@@ -729,39 +782,56 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
             const floatx4 ypd = mfma16(zero4(), col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC),
                                        lds4(sQs + lr * LC + 16 * R + 4 * kg));
             const bool safe = gm[R] - gs[R] >= -SAFE_SPAN;
+            float XA[4], XP[4], YA[4], YP[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float G = sG[(16 * R + 4 * kg + e) * DK + c];
+                const float er = __expf(G - gs[R]), ei = __expf(gm[R] - G);
+                XA[e] = er * xa[e];
+                XP[e] = er * xp[e];
+                YA[e] = ei * ya[e];
+                YP[e] = ei * yp[e];
+                if (safe) {
+                    const float ier = __expf(gs[R] - G);            // 1 / er
+                    XA[e] += er * xad[e];
+                    XP[e] += er * xpd[e];
+                    YA[e] += yad[e] * ier;
+                    YP[e] += ypd[e] * ier;
+                }
+            }
+            if (!safe) {                                            // the diagonal block term by term
+#pragma unroll 1
+                for (int i = 16 * R; i < 16 * R + 16; ++i) {
+                    const float Gi = sG[i * DK + c];
+                    const float ki = valid(i) ? to_f32(k[grow(i) * DK + c]) : 0.f;
+                    const float qi = valid(i) ? to_f32(q[grow(i) * DK + c]) : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * R + 4 * kg + e;
+                        const float G = sG[r * DK + c];
+                        if (i <= r) {
+                            const float wd = __expf(G - Gi);
+                            if (i < r) XA[e] += sdA[r * LC + i] * ki * wd;
+                            XP[e] += sdP[r * LC + i] * ki * wd;
+                        }
+                        if (i >= r) {
+                            const float wu = __expf(Gi - G);
+                            if (i > r) YA[e] += sdA[i * LC + r] * ki * wu;
+                            YP[e] += sdP[i * LC + r] * qi * wu;
+                        }
+                    }
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * R + 4 * kg + e;
                 const float G = sG[r * DK + c];
-                const float er = __expf(G - gs[R]), ei = __expf(gm[R] - G);
-                float XA = er * xa[e], XP = er * xp[e], YA = ei * ya[e], YP = ei * yp[e];
-                if (safe) {
-                    XA += er * xad[e];
-                    XP += er * xpd[e];
-                    YA += yad[e] / er;
-                    YP += ypd[e] / er;
-                } else {                                            // term by term
-                    for (int i = 16 * R; i < 16 * R + 16; ++i) {
-                        const float Gi = sG[i * DK + c];
-                        const float ki = valid(i) ? to_f32(k[grow(i) * DK + c]) : 0.f;
-                        const float qi = valid(i) ? to_f32(q[grow(i) * DK + c]) : 0.f;
-                        if (i <= r) {
-                            const float wd = __expf(G - Gi);
-                            if (i < r) XA += sdA[r * LC + i] * ki * wd;
-                            XP += sdP[r * LC + i] * ki * wd;
-                        }
-                        if (i >= r) {
-                            const float wu = __expf(Gi - G);
-                            if (i > r) YA += sdA[i * LC + r] * ki * wu;
-                            YP += sdP[i * LC + r] * qi * wu;
-                        }
-                    }
-                }
                 const float E = __expf(G), F = __expf(GC - G);
                 const float kc = kv[p][R][e], qc = qv[p][R][e];
                 const float dKt = sBeta[r] * aTd[R][p][e], dQt = aQ[R][p][e], dKb = aKb[R][p][e];
-                const float dK = E * dKt + F * dKb + XA + YA + YP, dQ = E * dQt + XP;
-                dGv[R][e] = E * kc * dKt + E * qc * dQt - F * kc * dKb + kc * XA - kc * YA + qc * XP - kc * YP;
+                const float dK = E * dKt + F * dKb + XA[e] + YA[e] + YP[e], dQ = E * dQt + XP[e];
+                dGv[R][e] = E * kc * dKt + E * qc * dQt - F * kc * dKb + kc * XA[e] - kc * YA[e] + qc * XP[e] -
+                            kc * YP[e];
                 gcp += F * kc * dKb;
                 if (valid(r)) {
                     dq[grow(r) * DK + c] = dQ;
