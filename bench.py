@@ -168,6 +168,7 @@ def main():
     }
 
     out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, g, w, K, args.warmup)
+    out["fused_pre"] = bench_fused_pre(torch, ChunkPlan, g, w, K, args.warmup)
     out["varlen"] = bench_varlen(torch, g, w, K, args.warmup)
     out["backward"] = bench_backward(torch, g, w)
 
@@ -201,6 +202,29 @@ def bench_gate_layouts(torch, ChunkPlan, g, w, steps, warmup):
         res[layout] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1)}
         del plan
     return res
+
+
+def bench_fused_pre(torch, ChunkPlan, g, w, steps, warmup):
+    """The same step with the fused pre-processing: q and k normalised in the
+    kernels and the gate given as a bf16 pre-activation a = log(e^{-g} - 1),
+    whose -softplus is the workload's log-gate (up to bf16 rounding)."""
+    a = torch.log(torch.expm1(-g["g"])).to(torch.bfloat16)
+    plan = ChunkPlan(g["q"], g["k"], g["v"], a, g["beta"], g["S0"], chunk_size=w.C, qk_l2norm=True,
+                     gate_act="softplus")
+    for _ in range(warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        plan.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del plan, a
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1),
+            "note": "raw q/k L2-normalised and g = -softplus(a), bf16 a, inside the intra kernel"}
 
 
 def bench_varlen(torch, g, w, steps, warmup):

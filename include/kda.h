@@ -290,6 +290,62 @@ int kda_decode_tokens(const void *q, const void *k, const void *v,
                       int N, int T, int H, int dk, int dv,
                       int in_dtype, int out_dtype, void *stream, int gate_layout);
 
+/*
+ * Fused pre-processing (the steps that produce the path's inputs in the recipe
+ * of the method's workloads: q and k L2-normalised per token and head, the
+ * log-gate g = -softplus(a) of a pre-activation a).  Flags, OR-ed together:
+ *   KDA_PRE_QK_L2NORM      q and k are raw; each [dk] row is divided by its L2
+ *                          norm inside the kernels (a zero row stays zero)
+ *   KDA_PRE_GATE_SOFTPLUS  g holds a, and the log-gate is -softplus(a) =
+ *                          -log(1 + e^a) (alpha = sigmoid(-a) in (0, 1))
+ *   KDA_PRE_GATE_BF16      g (log-gate or a) is bf16 instead of fp32; a per-channel
+ *                          bf16 g must be 16-byte aligned, a per-head one 2-byte
+ * The normalised q, k and the activated gate exist only inside the kernels; the
+ * result equals the plain call on the pre-processed inputs up to rounding.
+ * Unknown flag bits return KDA_ERR_UNSUPPORTED.  The backward pass
+ * (kda_chunk_bwd) takes pre-processed inputs.
+ */
+typedef enum {
+    KDA_PRE_NONE = 0,
+    KDA_PRE_QK_L2NORM = 1,
+    KDA_PRE_GATE_SOFTPLUS = 2,
+    KDA_PRE_GATE_BF16 = 4
+} kda_pre_flags_t;
+
+/*
+ * kda_chunk_fwd_pre, kda_chunk_intra_pre -- kda_chunk_fwd_ex / kda_chunk_intra_ex
+ * with pre-processing flags (kda_pre_flags_t).  g points to fp32 or bf16 data by
+ * KDA_PRE_GATE_BF16.  The chain stage (kda_chunk_chain) reads none of q, k, g
+ * and serves these calls unchanged.  Arguments and errors as kda_chunk_fwd_ex.
+ */
+int kda_chunk_fwd_pre(const void *q, const void *k, const void *v,
+                      const void *g, const float *beta,
+                      const float *initial_state,
+                      void *o, float *final_state,
+                      int B, int T, int H, int dk, int dv,
+                      int in_dtype, int out_dtype,
+                      void *workspace, size_t workspace_bytes,
+                      void *stream, int C, int gate_layout, int pre_flags);
+int kda_chunk_intra_pre(const void *q, const void *k, const void *v,
+                        const void *g, const float *beta,
+                        const float *initial_state,
+                        void *o, float *final_state,
+                        int B, int T, int H, int dk, int dv,
+                        int in_dtype, int out_dtype,
+                        void *workspace, size_t workspace_bytes,
+                        void *stream, int C, int gate_layout, int pre_flags);
+
+/*
+ * kda_decode_tokens_pre -- kda_decode_tokens with pre-processing flags; T = 1 is
+ * the single decode step.  Arguments and errors as kda_decode_tokens.
+ */
+int kda_decode_tokens_pre(const void *q, const void *k, const void *v,
+                          const void *g, const float *beta,
+                          float *state, void *o,
+                          int N, int T, int H, int dk, int dv,
+                          int in_dtype, int out_dtype, void *stream,
+                          int gate_layout, int pre_flags);
+
 #ifdef __cplusplus
 }
 #endif

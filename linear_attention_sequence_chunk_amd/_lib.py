@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
 
 F32, BF16 = 0, 1
 GATE = {"channel": 0, "head": 1, "none": 2}     # kda_gate_layout_t
+PRE_QK_L2NORM, PRE_GATE_SOFTPLUS, PRE_GATE_BF16 = 1, 2, 4   # kda_pre_flags_t
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
           4: "KDA_ERR_MISALIGNED", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIAS", 7: "KDA_ERR_HIP"}
 
@@ -20,7 +21,8 @@ SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_byte
            "kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain", "kda_decode_step",
            "kda_chunk_fwd_ex", "kda_chunk_intra_ex", "kda_decode_step_ex", "kda_decode_tokens",
            "kda_chunk_fwd_varlen", "kda_chunk_varlen_workspace_bytes",
-           "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes")
+           "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
+           "kda_chunk_fwd_pre", "kda_chunk_intra_pre", "kda_decode_tokens_pre")
 
 
 class KdaError(RuntimeError):
@@ -50,12 +52,17 @@ def lib() -> ctypes.CDLL:
         for name in ("kda_chunk_fwd_ex", "kda_chunk_intra_ex"):
             fn = getattr(L, name)
             fn.argtypes, fn.restype = _CHUNK_ARGS + [_ci], _ci
+        for name in ("kda_chunk_fwd_pre", "kda_chunk_intra_pre"):
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = _CHUNK_ARGS + [_ci, _ci], _ci
         L.kda_decode_step.argtypes = [_vp] * 7 + [_ci] * 6 + [_vp]
         L.kda_decode_step.restype = _ci
         L.kda_decode_step_ex.argtypes = [_vp] * 7 + [_ci] * 6 + [_vp, _ci]
         L.kda_decode_step_ex.restype = _ci
         L.kda_decode_tokens.argtypes = [_vp] * 7 + [_ci] * 7 + [_vp, _ci]
         L.kda_decode_tokens.restype = _ci
+        L.kda_decode_tokens_pre.argtypes = [_vp] * 7 + [_ci] * 7 + [_vp, _ci, _ci]
+        L.kda_decode_tokens_pre.restype = _ci
         L.kda_chunk_fwd_varlen.argtypes = [_vp] * 9 + [_ci] * 7 + [_vp, _sz, _vp, _ci, _ci]
         L.kda_chunk_fwd_varlen.restype = _ci
         L.kda_chunk_varlen_workspace_bytes.argtypes = [_ci] * 7

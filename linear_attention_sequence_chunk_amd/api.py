@@ -47,15 +47,32 @@ def _gate(layout) -> int:
     return _lib.GATE[layout]
 
 
-def _check_gate(g, layout, lead, dk, dev):
-    """g is [*lead, dk] per channel, [*lead] per head, None (or ignored) without gates."""
+def _check_gate(g, layout, lead, dk, dev, allow_bf16=False):
+    """g is [*lead, dk] per channel, [*lead] per head, None (or ignored) without
+    gates; fp32, or bf16 where the call takes pre-processing flags."""
     if layout == "none":
         return
-    _check_tensor("g", g, tuple(lead) + ((dk,) if layout == "channel" else ()), torch.float32, dev)
+    dt = g.dtype if allow_bf16 and isinstance(g, torch.Tensor) and g.dtype == torch.bfloat16 else torch.float32
+    _check_tensor("g", g, tuple(lead) + ((dk,) if layout == "channel" else ()), dt, dev)
+
+
+def _pre_flags(qk_l2norm, gate_act, g, layout) -> int:
+    """kda_pre_flags_t for the binding's keywords: q/k normalised in the kernels,
+    the gate given as a pre-activation ("softplus": log-gate = -softplus(g)), and
+    a bf16 gate tensor."""
+    if gate_act not in (None, "softplus"):
+        raise ValueError('gate_act must be None or "softplus"')
+    f = _lib.PRE_QK_L2NORM if qk_l2norm else 0
+    if layout != "none":
+        if gate_act == "softplus":
+            f |= _lib.PRE_GATE_SOFTPLUS
+        if isinstance(g, torch.Tensor) and g.dtype == torch.bfloat16:
+            f |= _lib.PRE_GATE_BF16
+    return f
 
 
 def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_state, workspace,
-                gate_layout="channel"):
+                gate_layout="channel", allow_bf16_gate=False):
     _gate(gate_layout)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -65,7 +82,7 @@ def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_st
     _check_tensor("q", q, (B, T, H, dk), q.dtype, dev)
     _check_tensor("k", k, (B, T, H, dk), q.dtype, dev)
     _check_tensor("v", v, (B, T, H, dv), q.dtype, dev)
-    _check_gate(g, gate_layout, (B, T, H), dk, dev)
+    _check_gate(g, gate_layout, (B, T, H), dk, dev, allow_bf16_gate)
     _check_tensor("beta", beta, (B, T, H), torch.float32, dev)
     if initial_state is not None:
         _check_tensor("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
@@ -82,27 +99,35 @@ def _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, final_st
 
 
 def _call_chunk(fn_name, q, k, v, g, beta, initial_state, o, final_state, B, T, H, dk, dv,
-                out_dtype, workspace, chunk_size, stream, gate_layout="channel"):
+                out_dtype, workspace, chunk_size, stream, gate_layout="channel", pre=0):
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
             _ptr(final_state), B, T, H, dk, dv, _code(q.dtype), _code(out_dtype),
             _ptr(workspace), workspace.numel(), _stream(stream), chunk_size]
-    if gate_layout != "channel" and fn_name in ("kda_chunk_fwd", "kda_chunk_intra"):
+    if pre and fn_name in ("kda_chunk_fwd", "kda_chunk_intra"):
+        fn_name, args = fn_name + "_pre", args + [_gate(gate_layout), pre]
+    elif gate_layout != "channel" and fn_name in ("kda_chunk_fwd", "kda_chunk_intra"):
         fn_name, args = fn_name + "_ex", args + [_gate(gate_layout)]
     st = getattr(_lib.lib(), fn_name)(*args)
     _lib.check(st, fn_name)
 
 
 def chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None,
-              final_state=None, workspace=None, stream=None, gate_layout="channel"):
-    """Chunkwise KDA forward (kda_chunk_fwd / kda_chunk_fwd_ex).  q,k [B,T,H,dk],
+              final_state=None, workspace=None, stream=None, gate_layout="channel",
+              qk_l2norm=False, gate_act=None):
+    """Chunkwise KDA forward (kda_chunk_fwd / _ex / _pre).  q,k [B,T,H,dk],
     v [B,T,H,dv] in fp32 or bf16; beta [B,T,H] fp32; g fp32 [B,T,H,dk]
     (gate_layout "channel"), [B,T,H] ("head") or None ("none"); initial_state
     [B,H,dk,dv] fp32 or None.  Returns (o [B,T,H,dv], final_state [B,H,dk,dv] fp32).
-    ``final_state`` may be given (e.g. the initial_state tensor, for in place)."""
+    ``final_state`` may be given (e.g. the initial_state tensor, for in place).
+    Fused pre-processing: ``qk_l2norm`` normalises q and k rows in the kernels;
+    ``gate_act="softplus"`` takes g as a pre-activation (log-gate -softplus(g));
+    g may then also be bf16."""
+    pre = _pre_flags(qk_l2norm, gate_act, g, gate_layout)
     B, T, H, dk, dv, out_dtype, o, fs, ws = _prep_chunk(q, k, v, g, beta, initial_state, chunk_size,
-                                                        out_dtype, final_state, workspace, gate_layout)
+                                                        out_dtype, final_state, workspace, gate_layout,
+                                                        allow_bf16_gate=True)
     _call_chunk("kda_chunk_fwd", q, k, v, g, beta, initial_state, o, fs, B, T, H, dk, dv,
-                out_dtype, ws, chunk_size, stream, gate_layout)
+                out_dtype, ws, chunk_size, stream, gate_layout, pre)
     return o, fs
 
 
@@ -194,19 +219,20 @@ class ChunkPlan:
     same sizes; ``run`` calls both stages, ``intra``/``chain`` one each."""
 
     def __init__(self, q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None,
-                 gate_layout="channel"):
+                 gate_layout="channel", qk_l2norm=False, gate_act=None):
         self.args = (q, k, v, g, beta, initial_state)
         self.chunk_size = chunk_size
         self.gate_layout = gate_layout
+        self.pre = _pre_flags(qk_l2norm, gate_act, g, gate_layout)
         (self.B, self.T, self.H, self.dk, self.dv, self.out_dtype, self.o, self.final_state,
          self.workspace) = _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, None, None,
-                                       gate_layout)
+                                       gate_layout, allow_bf16_gate=True)
 
     def _go(self, name, stream=None):
         q, k, v, g, beta, s0 = self.args
         _call_chunk(name, q, k, v, g, beta, s0, self.o, self.final_state, self.B, self.T, self.H,
                     self.dk, self.dv, self.out_dtype, self.workspace, self.chunk_size, stream,
-                    self.gate_layout)
+                    self.gate_layout, self.pre)
 
     def run(self, stream=None):
         self._go("kda_chunk_fwd", stream)
@@ -243,11 +269,13 @@ def decode_step(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, ga
     return o
 
 
-def decode_tokens(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, gate_layout="channel"):
-    """T tokens per sequence in one call (kda_decode_tokens).  q,k [N,T,H,dk],
-    v [N,T,H,dv]; g fp32 [N,T,H,dk] ("channel"), [N,T,H] ("head") or None
-    ("none"); beta [N,T,H] fp32; state [N,H,dk,dv] fp32 is updated in place.
-    Returns o [N,T,H,dv]."""
+def decode_tokens(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, gate_layout="channel",
+                  qk_l2norm=False, gate_act=None):
+    """T tokens per sequence in one call (kda_decode_tokens / _pre).  q,k
+    [N,T,H,dk], v [N,T,H,dv]; g fp32 [N,T,H,dk] ("channel"), [N,T,H] ("head") or
+    None ("none"); beta [N,T,H] fp32; state [N,H,dk,dv] fp32 is updated in place.
+    Returns o [N,T,H,dv].  ``qk_l2norm`` and ``gate_act`` as in chunk_fwd."""
+    pre = _pre_flags(qk_l2norm, gate_act, g, gate_layout)
     N, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -255,14 +283,15 @@ def decode_tokens(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, 
         raise ValueError("inputs must be on a GPU")
     _check_tensor("k", k, (N, T, H, dk), q.dtype, dev)
     _check_tensor("v", v, (N, T, H, dv), q.dtype, dev)
-    _check_gate(g, gate_layout, (N, T, H), dk, dev)
+    _check_gate(g, gate_layout, (N, T, H), dk, dev, allow_bf16=True)
     _check_tensor("beta", beta, (N, T, H), torch.float32, dev)
     _check_tensor("state", state, (N, H, dk, dv), torch.float32, dev)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if o is None:
         o = torch.empty((N, T, H, dv), dtype=out_dtype, device=dev)
-    st = _lib.lib().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                      _ptr(o), N, T, H, dk, dv, _code(q.dtype), _code(out_dtype),
-                                      _stream(stream), _gate(gate_layout))
-    _lib.check(st, "kda_decode_tokens")
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, T, H, dk, dv,
+            _code(q.dtype), _code(out_dtype), _stream(stream), _gate(gate_layout)]
+    name = "kda_decode_tokens_pre" if pre else "kda_decode_tokens"
+    st = getattr(_lib.lib(), name)(*(args + [pre] if pre else args))
+    _lib.check(st, name)
     return o

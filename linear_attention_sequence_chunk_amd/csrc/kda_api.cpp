@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "kda_common.h"
 #include "kda_launch.h"
 
 namespace {
@@ -70,18 +71,31 @@ struct ChunkCall {
     const int* cu_seqlens = nullptr;   // packed variable-length batch (B = 1, N sequences)
     int N = 0;
     bool packed = false;
+    int pre = 0;                       // kda_pre_flags_t
 };
 
 bool gate_ok(int g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
-// bytes of g per token-head for a gate layout
-size_t gate_bytes(int gate, int dk) { return gate == KDA_GATE_CHANNEL ? (size_t)dk * 4 : gate == KDA_GATE_HEAD ? 4 : 0; }
+constexpr int PRE_ALL = KDA_PRE_QK_L2NORM | KDA_PRE_GATE_SOFTPLUS | KDA_PRE_GATE_BF16;
+bool pre_ok(int pre) { return (pre & ~PRE_ALL) == 0; }
+// bytes of g per token-head for a gate layout (bf16 gates: half)
+size_t gate_bytes(int gate, int dk, int pre = 0) {
+    const size_t e = (pre & KDA_PRE_GATE_BF16) ? 2 : 4;
+    return gate == KDA_GATE_CHANNEL ? (size_t)dk * e : gate == KDA_GATE_HEAD ? e : 0;
+}
+// the kernels' mode bits for the ABI's pre-processing flags
+int pre_mode(int pre) {
+    return ((pre & KDA_PRE_QK_L2NORM) ? kda::MODE_QK_L2NORM : 0) |
+           ((pre & KDA_PRE_GATE_SOFTPLUS) ? kda::MODE_GATE_SOFTPLUS : 0) |
+           ((pre & KDA_PRE_GATE_BF16) ? kda::MODE_GATE_BF16 : 0);
+}
 
 bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
 size_t esize(int d) { return d == KDA_BF16 ? 2 : 4; }
 
 int validate_chunk(const ChunkCall& c) {
     if (c.B < 0 || c.T < 0 || c.H < 0 || c.N < 0) return KDA_ERR_SHAPE;
-    if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype) || !gate_ok(c.gate)) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype) || !gate_ok(c.gate) || !pre_ok(c.pre))
+        return KDA_ERR_UNSUPPORTED;
     if ((c.dk != 64 && c.dk != 128) || (c.dv != 64 && c.dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (c.C != 16 && c.C != 32 && c.C != 64 && c.C != 128) return KDA_ERR_UNSUPPORTED;
     if (!kda::chunk_supported(c.dk, c.dv, c.C, c.in_dtype == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
@@ -100,7 +114,9 @@ int validate_chunk(const ChunkCall& c) {
     const void* p16[5] = {c.q, c.k, c.v, c.o, c.ws};
     for (const void* p : p16)
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
-    if (g && !aligned(g, c.gate == KDA_GATE_CHANNEL ? 8 : 4)) return KDA_ERR_MISALIGNED;
+    if (g && !aligned(g, c.gate == KDA_GATE_CHANNEL ? ((c.pre & KDA_PRE_GATE_BF16) ? 16 : 8)
+                                                     : ((c.pre & KDA_PRE_GATE_BF16) ? 2 : 4)))
+        return KDA_ERR_MISALIGNED;
     const void* p4[3] = {c.beta, c.s0, c.sT};
     for (const void* p : p4)
         if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
@@ -112,7 +128,7 @@ int validate_chunk(const ChunkCall& c) {
 
     const size_t ei = esize(c.in_dtype), eo = esize(c.out_dtype);
     const Range rq = range_of(c.q, tok * c.dk * ei), rk = range_of(c.k, tok * c.dk * ei),
-                rv = range_of(c.v, tok * c.dv * ei), rg = range_of(g, tok * gate_bytes(c.gate, c.dk)),
+                rv = range_of(c.v, tok * c.dv * ei), rg = range_of(g, tok * gate_bytes(c.gate, c.dk, c.pre)),
                 rb = range_of(c.beta, tok * 4), rs0 = range_of(c.s0, nst * 4),
                 ro = range_of(c.o, tok * c.dv * eo), rsT = range_of(c.sT, nst * 4),
                 rw = range_of(c.ws, uses_ws ? need : 0),
@@ -134,6 +150,7 @@ kda::ChunkArgs to_args(const ChunkCall& c) {
     kda::ChunkArgs a;
     a.q = c.q; a.k = c.k; a.v = c.v; a.g = c.gate == KDA_GATE_NONE ? nullptr : c.g; a.beta = c.beta;
     a.gate = c.gate;
+    a.pre = pre_mode(c.pre);
     a.s0 = c.s0; a.o = c.o; a.sT = c.sT;
     a.B = c.packed ? 1 : c.B; a.T = c.T; a.H = c.H; a.dk = c.dk; a.dv = c.dv; a.C = c.C;
     a.cu_seqlens = c.packed ? c.cu_seqlens : nullptr;
@@ -320,6 +337,27 @@ int kda_chunk_fwd_ex(KDA_CHUNK_PARAMS, int gate_layout) {
 int kda_chunk_intra_ex(KDA_CHUNK_PARAMS, int gate_layout) {
     return run_chunk(KDA_CHUNK_CALL(gate_layout), STAGE_INTRA);
 }
+#define KDA_CHUNK_PRE_CALL(GATE, PRE)                                                       \
+    [&] {                                                                                   \
+        ChunkCall c_ = KDA_CHUNK_CALL(GATE);                                                \
+        c_.pre = (PRE);                                                                     \
+        return c_;                                                                          \
+    }()
+int kda_chunk_fwd_pre(const void* q, const void* k, const void* v, const void* g_any, const float* beta,
+                      const float* initial_state, void* o, float* final_state, int B, int T, int H, int dk,
+                      int dv, int in_dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream, int C, int gate_layout, int pre_flags) {
+    const float* g = static_cast<const float*>(g_any);
+    return run_chunk(KDA_CHUNK_PRE_CALL(gate_layout, pre_flags), STAGE_INTRA | STAGE_CHAIN);
+}
+int kda_chunk_intra_pre(const void* q, const void* k, const void* v, const void* g_any, const float* beta,
+                        const float* initial_state, void* o, float* final_state, int B, int T, int H, int dk,
+                        int dv, int in_dtype, int out_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream, int C, int gate_layout, int pre_flags) {
+    const float* g = static_cast<const float*>(g_any);
+    return run_chunk(KDA_CHUNK_PRE_CALL(gate_layout, pre_flags), STAGE_INTRA);
+}
+#undef KDA_CHUNK_PRE_CALL
 
 }  // extern "C"
 
@@ -327,9 +365,10 @@ namespace {
 
 int decode_call(const void* q, const void* k, const void* v, const float* g, const float* beta,
                 float* state, void* o, int N, int T, int H, int dk, int dv, int in_dtype, int out_dtype,
-                void* stream, int gate_layout) {
+                void* stream, int gate_layout, int pre = 0) {
     if (N < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
-    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_layout)) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype) || !gate_ok(gate_layout) || !pre_ok(pre))
+        return KDA_ERR_UNSUPPORTED;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
     const size_t nh = (size_t)N * H, tok = nh * (size_t)T;
     if (tok == 0) return KDA_OK;
@@ -339,12 +378,13 @@ int decode_call(const void* q, const void* k, const void* v, const float* g, con
     // the state is streamed in 16-byte vectors; the rest is read element-wise
     if (!aligned(state, 16)) return KDA_ERR_MISALIGNED;
     const void* pe[6] = {q, k, v, g, beta, o};
-    const uintptr_t ae[6] = {esize(in_dtype), esize(in_dtype), esize(in_dtype), 4, 4, esize(out_dtype)};
+    const uintptr_t ae[6] = {esize(in_dtype), esize(in_dtype), esize(in_dtype),
+                             (uintptr_t)((pre & KDA_PRE_GATE_BF16) ? 2 : 4), 4, esize(out_dtype)};
     for (int i = 0; i < 6; ++i)
         if (pe[i] && !aligned(pe[i], ae[i])) return KDA_ERR_MISALIGNED;
     const size_t ei = esize(in_dtype), eo = esize(out_dtype);
     const Range rq = range_of(q, tok * dk * ei), rk = range_of(k, tok * dk * ei),
-                rv = range_of(v, tok * dv * ei), rg = range_of(g, tok * gate_bytes(gate_layout, dk)),
+                rv = range_of(v, tok * dv * ei), rg = range_of(g, tok * gate_bytes(gate_layout, dk, pre)),
                 rb = range_of(beta, tok * 4),
                 rs = range_of(state, nh * dk * dv * 4), ro = range_of(o, tok * dv * eo);
     const Range in[] = {rq, rk, rv, rg, rb};
@@ -359,6 +399,7 @@ int decode_call(const void* q, const void* k, const void* v, const float* g, con
     a.N = N; a.T = T; a.H = H; a.dk = dk; a.dv = dv;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
     a.gate = gate_layout;
+    a.pre = pre_mode(pre);
     a.stream = (hipStream_t)stream;
     return finish(kda::run_decode_step(a), a.stream);
 }
@@ -377,6 +418,13 @@ int kda_decode_tokens(const void* q, const void* k, const void* v, const float* 
                       float* state, void* o, int N, int T, int H, int dk, int dv, int in_dtype,
                       int out_dtype, void* stream, int gate_layout) {
     return decode_call(q, k, v, g, beta, state, o, N, T, H, dk, dv, in_dtype, out_dtype, stream, gate_layout);
+}
+
+int kda_decode_tokens_pre(const void* q, const void* k, const void* v, const void* g, const float* beta,
+                          float* state, void* o, int N, int T, int H, int dk, int dv, int in_dtype,
+                          int out_dtype, void* stream, int gate_layout, int pre_flags) {
+    return decode_call(q, k, v, static_cast<const float*>(g), beta, state, o, N, T, H, dk, dv, in_dtype,
+                       out_dtype, stream, gate_layout, pre_flags);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,

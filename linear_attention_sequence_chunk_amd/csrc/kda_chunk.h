@@ -134,7 +134,8 @@ struct IntraCfg {
     static constexpr size_t OFF_OFF = OFF_TOT + size_t(NB) * DK * 4;
     static constexpr size_t OFF_BETA = OFF_OFF + size_t(NB) * DK * 4;
     static constexpr size_t OFF_FLAG = OFF_BETA + size_t(C) * 4;
-    static constexpr size_t TOTAL = align16(OFF_FLAG + size_t(NB) * 4);
+    static constexpr size_t OFF_QN = align16(OFF_FLAG + size_t(NB) * 4);   // 1/||q||, 1/||k|| [2][C]
+    static constexpr size_t TOTAL = align16(OFF_QN + size_t(2) * C * 4);
     static constexpr bool FITS = TOTAL <= LDS_LIMIT;
 };
 

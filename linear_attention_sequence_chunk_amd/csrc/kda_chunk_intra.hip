@@ -28,6 +28,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     float* sOff = reinterpret_cast<float*>(smem + Cfg::OFF_OFF);
     float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_BETA);
     int* sFlag = reinterpret_cast<int*>(smem + Cfg::OFF_FLAG);
+    float* sQn = reinterpret_cast<float*>(smem + Cfg::OFF_QN);   // 1/||q_t||, 1/||k_t|| (or 1)
+    float* sKn = sQn + C;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // chunk-major order (fixed-length batches): workgroups running together cover
@@ -44,6 +46,27 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     // Block-local inclusive prefix sums of the clamped log-gate (a1), block totals.
     if (tid < NB) sFlag[tid] = 0;
     if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
+    if (gate & MODE_QK_L2NORM) {
+        // inverse L2 norms of the q and k rows: 256 / C threads per row
+        constexpr int TPR = 256 / C, CPT = DK / TPR;
+        const int r = tid / TPR, c0 = (tid % TPR) * CPT;
+        float sq = 0.f, sk = 0.f;
+        if (valid(r)) {
+            for (int c = c0; c < c0 + CPT; c += 2) {
+                float q0, q1, k0, k1;
+                Pair2<T>::load(q + grow(r) * DK + c, q0, q1);
+                Pair2<T>::load(k + grow(r) * DK + c, k0, k1);
+                sq += q0 * q0 + q1 * q1;
+                sk += k0 * k0 + k1 * k1;
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < TPR; off <<= 1) { sq += __shfl_xor(sq, off); sk += __shfl_xor(sk, off); }
+        if (tid % TPR == 0) { sQn[r] = inv_norm(sq); sKn[r] = inv_norm(sk); }
+    } else if (tid < C) {
+        sQn[tid] = 1.f;
+        sKn[tid] = 1.f;
+    }
     __syncthreads();
     for (int u = tid; u < NB * (DK / 2); u += 256) {
         const int R = u / (DK / 2), c = 2 * (u % (DK / 2));
@@ -87,16 +110,22 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             float L8[8], o8[8], kv[8], x[8];
             Vec8<float>::load(sL + t * DK + c, L8);
             Vec8<float>::load(sOff + R * DK + c, o8);
-            if (valid(t)) Vec8<T>::load(k + grow(t) * DK + c, kv);
-            else {
+            if (valid(t)) {
+                Vec8<T>::load(k + grow(t) * DK + c, kv);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) kv[m] *= sKn[t];
+            } else {
 #pragma unroll
                 for (int m = 0; m < 8; ++m) kv[m] = 0.f;
             }
             if (w >= HALF) {                      // row side: e^{G_r - G_{m-1}} <= 1
                 const int ri = seg * HALF + (w - HALF);
                 float qv[8];
-                if (valid(t)) Vec8<T>::load(q + grow(t) * DK + c, qv);
-                else {
+                if (valid(t)) {
+                    Vec8<T>::load(q + grow(t) * DK + c, qv);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) qv[m] *= sQn[t];
+                } else {
 #pragma unroll
                     for (int m = 0; m < 8; ++m) qv[m] = 0.f;
                 }
@@ -136,8 +165,12 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             const int t = r0 + tl, R = t / 16;
             float L8[8], kv[8], qv[8], x[8];
             Vec8<float>::load(sL + t * DK + c, L8);
-            if (valid(t)) { Vec8<T>::load(k + grow(t) * DK + c, kv); Vec8<T>::load(q + grow(t) * DK + c, qv); }
-            else {
+            if (valid(t)) {
+                Vec8<T>::load(k + grow(t) * DK + c, kv);
+                Vec8<T>::load(q + grow(t) * DK + c, qv);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) { kv[m] *= sKn[t]; qv[m] *= sQn[t]; }
+            } else {
 #pragma unroll
                 for (int m = 0; m < 8; ++m) { kv[m] = 0.f; qv[m] = 0.f; }
             }
@@ -177,8 +210,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
                                     sp += to_f32(q[grow(r) * DK + c]) * ki * w;
                                 }
                             }
-                            accA[p / 4][e] = sa;
-                            accP[p / 4][e] = sp;
+                            accA[p / 4][e] = i <= r && valid(r) ? sa * sKn[r] * sKn[i] : 0.f;
+                            accP[p / 4][e] = i <= r && valid(r) ? sp * sQn[r] * sKn[i] : 0.f;
                         }
                     }
                 }
@@ -310,6 +343,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
                 l0 += clamp_g(gg.x); l1 += clamp_g(gg.y);
                 Pair2<T>::load(k + grow(t) * DK + c, k0, k1);
                 Pair2<T>::load(q + grow(t) * DK + c, q0, q1);
+                k0 *= sKn[t]; k1 *= sKn[t]; q0 *= sQn[t]; q1 *= sQn[t];
             }
             const float ei0 = __expf(in0 + l0), ei1 = __expf(in1 + l1);
             const float eo0 = __expf(out0 - l0), eo1 = __expf(out1 - l1);
@@ -422,7 +456,8 @@ struct Intra64Cfg {
     static constexpr size_t OFF_KB = OFF_KT + size_t(DK) * LDT * 2;     // Kb^T staging [DK][LDP]
     static constexpr size_t OFF_TOT = OFF_KB + size_t(DK) * LDP * 2;
     static constexpr size_t OFF_BETA = OFF_TOT + size_t(NB) * DK * 4;
-    static constexpr size_t TOTAL = OFF_BETA + size_t(C) * 4;
+    static constexpr size_t OFF_NP = OFF_BETA + size_t(C) * 4;          // q, k sums of squares [2][2][C]
+    static constexpr size_t TOTAL = OFF_NP + size_t(4) * C * 4;
     static_assert(size_t(DV) * LDT * 2 <= size_t(C) * LDA * 4, "V^T fits over M");
     static_assert(size_t(C / 2) * (C / 2 + 4) * 4 <= size_t(C) * LDP * 2, "T temp fits the P staging");
     static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
@@ -446,6 +481,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     bf16* sKbT = reinterpret_cast<bf16*>(smem + Cfg::OFF_KB);
     float* sTot = reinterpret_cast<float*>(smem + Cfg::OFF_TOT);
     float* sBeta = reinterpret_cast<float*>(smem + Cfg::OFF_BETA);
+    float* sNp = reinterpret_cast<float*>(smem + Cfg::OFF_NP);   // [q|k][channel half][row]
     auto blk = [&](int b) { return sOp + b * 16 * LDH; };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -472,11 +508,21 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             const long base = grow(t) * DK + chan(p);
             qv[p] = *reinterpret_cast<const bf16x8*>(q + base);
             kv[p] = *reinterpret_cast<const bf16x8*>(k + base);
-            if (gate == GATE_CHANNEL) {
-                ga[p] = *reinterpret_cast<const floatx4*>(g + base);
-                gb[p] = *reinterpret_cast<const floatx4*>(g + base + 4);
-            } else if (gate == GATE_HEAD) {
-                const float x = g[grow(t)];
+            if (gate_layout(gate) == GATE_CHANNEL) {
+                if (gate & MODE_GATE_BF16) {
+                    const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(g) + base);
+                    ga[p] = floatx4{(float)g8[0], (float)g8[1], (float)g8[2], (float)g8[3]};
+                    gb[p] = floatx4{(float)g8[4], (float)g8[5], (float)g8[6], (float)g8[7]};
+                } else {
+                    ga[p] = *reinterpret_cast<const floatx4*>(g + base);
+                    gb[p] = *reinterpret_cast<const floatx4*>(g + base + 4);
+                }
+                if (gate & MODE_GATE_SOFTPLUS) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) { ga[p][m] = neg_softplus(ga[p][m]); gb[p][m] = neg_softplus(gb[p][m]); }
+                }
+            } else if (gate_layout(gate) == GATE_HEAD) {
+                const float x = gate_at(g, gate, grow(t), DK, 0);
                 ga[p] = floatx4{x, x, x, x};
                 gb[p] = ga[p];
             } else {
@@ -505,6 +551,26 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         }
     }
     if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
+    // q and k row norms (pre-processing): a token's 128 channels are spread over the
+    // four lane groups of this wave and the partner wave (wave ^ 1)
+    const bool qknorm = gate & MODE_QK_L2NORM;
+    if (qknorm) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float a = (float)qv[p][m], b = (float)kv[p][m];
+                sq += a * a;
+                sk += b * b;
+            }
+        sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
+        sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+        if (lane < 16) {
+            sNp[(wave & 1) * C + t] = sq;
+            sNp[2 * C + (wave & 1) * C + t] = sk;
+        }
+    }
 
     // ---------------------------------------------------------------- a1: block-local log-gate sums
     float Lg[2][8];
@@ -518,6 +584,9 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         }
     }
     __syncthreads();
+    auto qn = [&](int r) { return inv_norm(sNp[r] + sNp[C + r]); };          // 1/||q_r||
+    auto kn = [&](int r) { return inv_norm(sNp[2 * C + r] + sNp[3 * C + r]); };  // 1/||k_r||
+    const float iqn = qknorm ? qn(t) : 1.f, ikn = qknorm ? kn(t) : 1.f;
 
     // ---------------------------------------------------------------- a2 + a3 per channel half
     bf16* gQt = ws_qt + ch * (long)C * DK;
@@ -536,7 +605,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const float E = __expf(Lg[p][m]), F = __expf(tR[m] - Lg[p][m]);
-                const float kk = (float)kv[p][m], qq = (float)qv[p][m];
+                const float kk = (float)kv[p][m] * ikn, qq = (float)qv[p][m] * iqn;
                 kr[m] = kk * E; qr[m] = qq * E; kf[m] = kk * F;
             }
             Vec8<bf16>::store(blk(RB) + rr * LDH + cl, kr);
@@ -651,6 +720,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                             sa += (float)k[grow(rw) * DK + cc] * ki * w;
                             sp += (float)q[grow(rw) * DK + cc] * ki * w;
                         }
+                        if (qknorm) { sa *= kn(rw) * kn(i); sp *= qn(rw) * kn(i); }
                     }
                     if (dslot == 0) { accA[0][e] = sa; accP[0][e] = sp; }
                     else            { accA[1][e] = sa; accP[1][e] = sp; }
@@ -926,7 +996,7 @@ static hipError_t launch_intra(const ChunkArgs& a) {
         hipLaunchKernelGGL((chunk_intra_kernel<T, DK, DV, C>), dim3((unsigned)nch), dim3(256), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta,
                            (T*)(ws + w.qt), (T*)(ws + w.wk), (T*)(ws + w.kb), (T*)(ws + w.p),
-                           (float*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate, a.ck_t, a.ck_a);
+                           (float*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate | a.pre, a.ck_t, a.ck_a);
         return hipGetLastError();
     }
 }
@@ -959,7 +1029,7 @@ static hipError_t launch_intra64(const ChunkArgs& a) {
     hipLaunchKernelGGL((chunk_intra64_kernel<DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
                        (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
-                       (bf16*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate);
+                       (bf16*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate | a.pre);
     return hipGetLastError();
 }
 

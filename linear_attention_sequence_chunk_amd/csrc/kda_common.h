@@ -113,18 +113,55 @@ template <> struct Vec8<float> {
 // NaN stays NaN (the comparison is false), -inf becomes G_FLOOR.
 __device__ inline float clamp_g(float g) { return g < G_FLOOR ? G_FLOOR : g; }
 
-// The log-gate of (row, channel c) for a gate layout (GateLayout in kda_launch.h):
-// per channel g[row * dk + c], per head g[row], or none (0).
-__device__ inline float gate_at(const float* __restrict__ g, int layout, long row, int dk, int c) {
-    if (layout == 0) return g[row * dk + c];
-    if (layout == 1) return g[row];
+// ---------------------------------------------------------------- gate and pre-processing
+// Kernels that read q, k or g take a mode word: the gate layout (GateLayout in
+// kda_launch.h) in bits 0-3 and pre-processing flags above it.
+constexpr int MODE_QK_L2NORM = 1 << 4;       // q and k rows are L2-normalised in the kernel
+constexpr int MODE_GATE_SOFTPLUS = 1 << 5;   // the gate tensor holds a; the log-gate is -softplus(a)
+constexpr int MODE_GATE_BF16 = 1 << 6;       // the gate tensor is bf16
+
+__device__ inline int gate_layout(int mode) { return mode & 15; }
+
+// -softplus(a) = -log(1 + e^a) = -(max(a, 0) + log(1 + e^{-|a|})): no overflow, and
+// the hardware exp2 / log2 (~1 ulp); the absolute error of the log-gate stays
+// below ~1e-7, also where e^{-|a|} is small and 1 + e^{-|a|} rounds.
+__device__ inline float neg_softplus(float a) {
+    return -(fmaxf(a, 0.f) + __logf(1.f + __expf(-fabsf(a))));
+}
+
+__device__ inline float gate_load(const void* __restrict__ g, int mode, long idx) {
+    const float a = (mode & MODE_GATE_BF16) ? (float)reinterpret_cast<const bf16*>(g)[idx]
+                                            : reinterpret_cast<const float*>(g)[idx];
+    return (mode & MODE_GATE_SOFTPLUS) ? neg_softplus(a) : a;
+}
+
+// The log-gate of (row, channel c): per channel g[row * dk + c], per head g[row],
+// or none (0).
+__device__ inline float gate_at(const void* __restrict__ g, int mode, long row, int dk, int c) {
+    const int layout = gate_layout(mode);
+    if (layout == 0) return gate_load(g, mode, row * dk + c);
+    if (layout == 1) return gate_load(g, mode, row);
     return 0.f;
 }
 // Two consecutive channels c, c + 1 (c even) of the same row.
-__device__ inline float2 gate_pair(const float* __restrict__ g, int layout, long row, int dk, int c) {
-    if (layout == 0) return *reinterpret_cast<const float2*>(g + row * dk + c);
-    if (layout == 1) { const float x = g[row]; return make_float2(x, x); }
+__device__ inline float2 gate_pair(const void* __restrict__ g, int mode, long row, int dk, int c) {
+    const int layout = gate_layout(mode);
+    if (layout == 0) {
+        float2 x;
+        if (mode & MODE_GATE_BF16) {
+            const bf16x2 b = *reinterpret_cast<const bf16x2*>(reinterpret_cast<const bf16*>(g) + row * dk + c);
+            x = make_float2((float)b[0], (float)b[1]);
+        } else {
+            x = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(g) + row * dk + c);
+        }
+        if (mode & MODE_GATE_SOFTPLUS) { x.x = neg_softplus(x.x); x.y = neg_softplus(x.y); }
+        return x;
+    }
+    if (layout == 1) { const float x = gate_load(g, mode, row); return make_float2(x, x); }
     return make_float2(0.f, 0.f);
 }
+
+// 1 / ||x|| from the sum of squares, with a zero row mapped to zero.
+__device__ inline float inv_norm(float sumsq) { return sumsq > 0.f ? rsqrtf(sumsq) : 0.f; }
 
 }  // namespace kda

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     __shared__ float s_ak[2][DK], s_aq[2][DK], s_k[2][DK], s_a[2][DK];
     __shared__ float s_red[2][RG][DV];
     __shared__ float s_u[DV];
-    __shared__ float s_qk[2];
+    __shared__ float s_qk[2], s_iq[2], s_ik[2];
 
     const long nh = blockIdx.x;
     const long n = nh / H;
@@ -45,6 +45,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int tid = threadIdx.x;
     const int tx = tid % CG, ty = tid / CG;
     float* S = state + nh * (long)DK * DV;
+    // With in-kernel L2 normalisation of q and k, the raw vectors go through the
+    // state products and the scalars 1/||q||, 1/||k|| are applied to the results:
+    // r = S^T(alpha*k)/||k||, s = S^T(alpha*q)/||q||, and the write k u^T uses
+    // u/||k||.  Without it both scalars are 1 and change nothing.
+    const bool qknorm = gate & MODE_QK_L2NORM;
 
     // Issue every state load first: RPT independent 16-byte loads in flight.
     floatx4 sv[RPT];
@@ -61,13 +66,27 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             const float qc = to_f32(q[row * DK + tid]);
             s_a[pb][tid] = a; s_k[pb][tid] = kc; s_ak[pb][tid] = a * kc; s_aq[pb][tid] = a * qc;
         }
-        if (tid < WAVE) {                                 // q.k, fixed-order wave reduction
-            float p = 0.f;
+        if (tid < WAVE) {                                 // q.k and the norms, fixed-order wave reduction
+            float p = 0.f, nq = 0.f, nk = 0.f;
 #pragma unroll
-            for (int c = tid; c < DK; c += WAVE) p += to_f32(q[row * DK + c]) * to_f32(k[row * DK + c]);
+            for (int c = tid; c < DK; c += WAVE) {
+                const float qc = to_f32(q[row * DK + c]), kc = to_f32(k[row * DK + c]);
+                p += qc * kc;
+                nq += qc * qc;
+                nk += kc * kc;
+            }
 #pragma unroll
-            for (int off = WAVE / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
-            if (tid == 0) s_qk[pb] = p;
+            for (int off = WAVE / 2; off > 0; off >>= 1) {
+                p += __shfl_xor(p, off);
+                nq += __shfl_xor(nq, off);
+                nk += __shfl_xor(nk, off);
+            }
+            if (tid == 0) {
+                const float iq = qknorm ? inv_norm(nq) : 1.f, ik = qknorm ? inv_norm(nk) : 1.f;
+                s_qk[pb] = p * iq * ik;
+                s_iq[pb] = iq;
+                s_ik[pb] = ik;
+            }
         }
         __syncthreads();
 
@@ -87,9 +106,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             float rr = 0.f, ss = 0.f;
 #pragma unroll
             for (int y = 0; y < RG; ++y) { rr += s_red[0][y][tid]; ss += s_red[1][y][tid]; }
-            const float u = beta[row] * (to_f32(v[row * DV + tid]) - rr);
-            s_u[tid] = u;
-            o[row * DV + tid] = from_f32<TOut>(ss + s_qk[pb] * u);
+            const float ik = s_ik[pb];
+            const float u = beta[row] * (to_f32(v[row * DV + tid]) - rr * ik);
+            s_u[tid] = u * ik;
+            o[row * DV + tid] = from_f32<TOut>(ss * s_iq[pb] + s_qk[pb] * u);
         }
         __syncthreads();
 
@@ -112,7 +132,7 @@ static hipError_t launch_decode(const DecodeArgs& a) {
     const long nh = (long)a.N * a.H;
     hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV>), dim3((unsigned)nh), dim3(256), 0,
                        a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta,
-                       a.state, (TOut*)a.o, a.H, a.T, a.gate);
+                       a.state, (TOut*)a.o, a.H, a.T, a.gate | a.pre);
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct DecodeArgs {
     bool in_bf16, out_bf16;
     int gate;
     hipStream_t stream;
+    int pre = 0;        // pre-processing flags (MODE_* in kda_common.h)
 };
 
 struct ChunkArgs {
@@ -33,6 +34,7 @@ struct ChunkArgs {
     int gate;
     void* ws; size_t ws_bytes;
     hipStream_t stream;
+    int pre = 0;        // pre-processing flags (MODE_* in kda_common.h): intra stage only
     // packed variable-length batch: B = 1, T = total tokens, N sequences with
     // token offsets cu_seqlens[N+1] (device memory); NULL for [B,T,H,d] batches
     const int* cu_seqlens = nullptr;

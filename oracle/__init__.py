@@ -21,6 +21,10 @@ Functions and the passages they follow (pages cited by title and section):
                     Uses direct pairwise decays exp(G_r - G_i), no factoring.
 ``recurrent_exact`` exact rational arithmetic (fractions) of the definition,
                     taking alpha directly, for tiny sizes.
+``l2_normalize``    the steps that produce q, k and g in the method's workloads
+``gate_softplus``   (inputs of the path, not the path): each [d] row divided by
+                    its Euclidean norm, and the log-gate -softplus(a) =
+                    -log(1 + e^a); the oracle side of the fused pre-processing.
 
 Parity pins: every function here is pinned by tests/test_oracle_pins.py to
 closed forms, special cases and library routines (least squares, finite
@@ -194,6 +198,20 @@ def recurrent_exact(q, k, v, alpha, beta, S0=None, delta=True):
         S = [[S[c][j] + kt[c] * u[j] for j in range(dv)] for c in range(dk)]
         out.append([sum((qt[c] * S[c][j] for c in range(dk)), F(0)) for j in range(dv)])
     return out, S
+
+
+def l2_normalize(x):
+    """Each row (last axis) divided by its Euclidean norm, in fp64; a zero row
+    stays zero."""
+    x = to_f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def gate_softplus(a):
+    """The log-gate -softplus(a) = -log(1 + e^a), in fp64 (alpha = 1/(1 + e^a))."""
+    a = to_f64(a)
+    return -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
 
 
 def lib_path() -> str:

@@ -253,3 +253,55 @@ def test_varlen_validation_codes():
         assert call(a) == HIP
         b = dict(a); b["g"] = None; b["gate"] = 2
         assert call(b) == HIP
+
+
+@pytest.mark.parametrize("fn", ["kda_chunk_fwd_pre", "kda_chunk_intra_pre"])
+def test_pre_flag_codes(fn):
+    """Pre-processing flags: unknown bits, and the bf16 gate's size and alignment."""
+    L = _lib.lib()
+    a = chunk_args(ind=_lib.BF16, outd=_lib.BF16, dk=128, dv=128)
+    CH, HEAD = _lib.GATE["channel"], _lib.GATE["head"]
+    QK, SP, GB = _lib.PRE_QK_L2NORM, _lib.PRE_GATE_SOFTPLUS, _lib.PRE_GATE_BF16
+    tok = a["B"] * a["T"] * a["H"]
+
+    def call(x, gate, pre):
+        args = [x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], x["o"], x["sT"], x["B"], x["T"], x["H"],
+                x["dk"], x["dv"], x["ind"], x["outd"], x["ws"], x["wsb"], None, x["C"], gate, pre]
+        return getattr(L, fn)(*args)
+    cases = [(dict(), CH, 8, UNSUP), (dict(), CH, -1, UNSUP),
+             (dict(g=a["g"] + 8), CH, GB, MISAL),            # a per-channel bf16 g needs 16 bytes
+             (dict(g=a["g"] + 1), HEAD, GB, MISAL),
+             (dict(g=None), CH, SP, NULL),
+             (dict(q=None), CH, QK, NULL)]
+    if not HAS_GPU:
+        cases += [(dict(), CH, QK | SP | GB, HIP), (dict(g=a["g"] + 16), CH, GB, HIP),
+                  (dict(g=a["g"] + 2), HEAD, GB | SP, HIP),
+                  # a bf16 per-channel g covers half the bytes: o may follow it
+                  (dict(o=a["g"] + tok * 128 * 2), CH, GB, HIP),
+                  (dict(o=a["g"] + tok * 128 * 2), CH, 0, ALIAS)]
+    for change, gate, pre, code in cases:
+        b = dict(a)
+        b.update(change)
+        if pre == 0:
+            assert call_chunk(b, fn.replace("_pre", ""), gate) == code, (change, gate, pre, code)
+        else:
+            assert call(b, gate, pre) == code, (change, gate, pre, code)
+
+
+def test_decode_pre_flag_codes():
+    L = _lib.lib()
+    f = Fake()
+    N, T, H, dk, dv = 3, 2, 2, 128, 64
+    t = dict(q=f(N * T * H * dk * 2), k=f(N * T * H * dk * 2), v=f(N * T * H * dv * 2),
+             g=f(N * T * H * dk * 2), beta=f(N * T * H * 4), state=f(N * H * dk * dv * 4),
+             o=f(N * T * H * dv * 2))
+
+    def call(x, gate, pre):
+        return L.kda_decode_tokens_pre(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], x["o"],
+                                       N, T, H, dk, dv, _lib.BF16, _lib.BF16, None, gate, pre)
+    assert call(t, 0, 16) == UNSUP
+    assert call(dict(t, g=t["g"] + 1), 0, _lib.PRE_GATE_BF16) == MISAL
+    assert call(dict(t, g=t["g"] + 2), 0, 0) == MISAL          # fp32 g needs 4 bytes
+    if not HAS_GPU:
+        assert call(dict(t, g=t["g"] + 2), 0, _lib.PRE_GATE_BF16 | _lib.PRE_GATE_SOFTPLUS) == HIP
+        assert call(t, 2, _lib.PRE_QK_L2NORM) == HIP
