@@ -1,6 +1,6 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-extras]
 
 A step is one kda_chunk_fwd call (intra-chunk stage + chain stage) over the mid
 prefill workload: B=4, H=16, T=8192, d_k=d_v=128, C=64, bf16 q/k/v, fp32 g/beta
@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="only the step (and decode): no gate-layout, fused, varlen or backward lines")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device copy (to scale FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
@@ -167,10 +169,11 @@ def main():
                  "host_wall_ms_per_step": round(t_host / K * 1e3, 4)},
     }
 
-    out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, g, w, K, args.warmup)
-    out["fused_pre"] = bench_fused_pre(torch, ChunkPlan, g, w, K, args.warmup)
-    out["varlen"] = bench_varlen(torch, g, w, K, args.warmup)
-    out["backward"] = bench_backward(torch, g, w)
+    if not args.no_extras:
+        out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, g, w, K, args.warmup)
+        out["fused_pre"] = bench_fused_pre(torch, ChunkPlan, g, w, K, args.warmup)
+        out["varlen"] = bench_varlen(torch, g, w, K, args.warmup)
+        out["backward"] = bench_backward(torch, g, w)
 
     if not args.no_decode:
         out["decode"] = bench_decode(torch, inputs, decode_step, dev, args.decode_steps)
