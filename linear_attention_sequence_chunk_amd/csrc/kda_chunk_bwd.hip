@@ -35,14 +35,6 @@ __device__ __forceinline__ floatx4 mfma16(floatx4 acc, floatx4 a, floatx4 b) {
     acc = mfma4(acc, a[2], b[2]);
     return mfma4(acc, a[3], b[3]);
 }
-template <typename T> __device__ __forceinline__ floatx4 load4(const T* p);
-template <> __device__ __forceinline__ floatx4 load4<float>(const float* p) {
-    return *reinterpret_cast<const floatx4*>(p);
-}
-template <> __device__ __forceinline__ floatx4 load4<bf16>(const bf16* p) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-    return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
 __device__ __forceinline__ floatx4 lds4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
 // Four consecutive rows of one column of an LDS matrix with row stride ld.
 __device__ __forceinline__ floatx4 col4(const float* p, int ld) {
@@ -337,9 +329,24 @@ struct BwdIntraCfg {
     static constexpr bool FITS = size_t(FLOATS) * 4 <= LDS_LIMIT && NKB % 4 == 0 && NVB % 4 == 0;
 };
 
-template <int NB, int KPW>
+// Four consecutive values of T as loaded (converted to fp32 where used, so that a
+// load never has to complete where it is issued).
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+    typedef floatx4 type;
+    __device__ static __forceinline__ floatx4 f32(floatx4 x) { return x; }
+};
+template <> struct Raw4<bf16> {
+    typedef bf16x4 type;
+    __device__ static __forceinline__ floatx4 f32(bf16x4 x) {
+        return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    }
+};
+
+template <typename T, int NB, int KPW>
 struct BwdFrag {                          // one 16-deep k step of phase 1
-    floatx4 o[NB], w[NB], dw[NB], s[KPW], ds[KPW], wi, v;
+    floatx4 o[NB], w[NB], dw[NB], s[KPW], ds[KPW], wi;
+    typename Raw4<T>::type v;
 };
 
 // Make one wave's LDS writes visible to its other lanes.
@@ -399,10 +406,16 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
             const int u = tid + 256 * x;
             tv[x] = u < C * C ? ck_t[unit * (long)C * C + u] : 0.f;
         }
+        // one branch on the layout outside the loops, so that all loads are in flight
+        if (gate == GATE_CHANNEL) {
 #pragma unroll
-        for (int x = 0; x < NG; ++x) {
-            const int u = tid + 256 * x, r = u / DK;
-            gl[x] = gate_at(g, gate, crow(r), DK, u % DK);
+            for (int x = 0; x < NG; ++x) gl[x] = g[crow((tid + 256 * x) / DK) * DK + tid % DK];
+        } else if (gate == GATE_HEAD) {
+#pragma unroll
+            for (int x = 0; x < NG; ++x) gl[x] = g[crow((tid + 256 * x) / DK)];
+        } else {
+#pragma unroll
+            for (int x = 0; x < NG; ++x) gl[x] = 0.f;
         }
         const float bt = tid < C ? beta[crow(tid)] : 0.f;
 #pragma unroll
@@ -470,11 +483,10 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
             F.s[p] = *reinterpret_cast<const floatx4*>(S + c * DV + jb);                          \
             F.ds[p] = *reinterpret_cast<const floatx4*>(dSn + c * DV + jb);                       \
         }                                                                                         \
-        if (tri) {                                                                                \
-            const int i = 16 * wave + lr;                                                         \
+        {                                                                                         \
+            const int i = 16 * (tri ? wave : 0) + lr;                                             \
             F.wi = *reinterpret_cast<const floatx4*>(W + i * DV + jb);                            \
-            const floatx4 v_ = load4<T>(v + crow(i) * DV + jb);                                   \
-            F.v = valid(i) ? v_ : zero4();                                                        \
+            F.v = *reinterpret_cast<const typename Raw4<T>::type*>(v + crow(i) * DV + jb);        \
         }                                                                                         \
     }
 #define KDA_BWD_MMA1(F)                                                                           \
@@ -486,16 +498,17 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
                 aKb[R][p] = mfma16(aKb[R][p], F.w[R], F.ds[p]);                                   \
             }                                                                                     \
             if (tri && R >= wave) {                                                               \
+                const floatx4 vf_ = vrow_ok ? Raw4<T>::f32(F.v) : zero4();                         \
                 aP[R] = mfma16(aP[R], F.o[R], F.wi);                                              \
-                aV[R] = mfma16(aV[R], F.dw[R], F.v);                                              \
+                aV[R] = mfma16(aV[R], F.dw[R], vf_);                                              \
             }                                                                                     \
         }                                                                                         \
         _Pragma("unroll") for (int p = 0; p < KPW; ++p)                                           \
             dgam[p] += F.s[p][0] * F.ds[p][0] + F.s[p][1] * F.ds[p][1] + F.s[p][2] * F.ds[p][2] + \
                        F.s[p][3] * F.ds[p][3];                                                    \
     }
-        BwdFrag<NB, KPW> fa, fb;
-        fa.wi = zero4(); fa.v = zero4(); fb.wi = zero4(); fb.v = zero4();
+        BwdFrag<T, NB, KPW> fa, fb;
+        const bool vrow_ok = valid(16 * wave + lr);
         KDA_BWD_LOAD1(fa, 0);
 #pragma unroll 1
         for (int js = 0; js < NVB; js += 2) {
@@ -561,18 +574,18 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     }
     // ---- phase 2: Kt = e^G K
     {
-        constexpr int NK = C * DK / 4 / 256 > 0 ? C * DK / 4 / 256 : 1;
-        floatx4 kl[NK];
+        constexpr int NK = (C * DK / 4 + 255) / 256;
+        typename Raw4<T>::type kl[NK];
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
-            const int u = tid + 256 * x, r = (4 * u) / DK, c0 = (4 * u) % DK;
-            kl[x] = u < C * DK / 4 ? load4<T>(k + crow(r < C ? r : 0) * DK + c0) : zero4();
+            const int u = tid + 256 * x, uu = u < C * DK / 4 ? u : 0, r = (4 * uu) / DK, c0 = (4 * uu) % DK;
+            kl[x] = *reinterpret_cast<const typename Raw4<T>::type*>(k + crow(r) * DK + c0);
         }
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
             const int u = tid + 256 * x, r = (4 * u) / DK, c0 = (4 * u) % DK;
             if (u < C * DK / 4) {
-                floatx4 kk = valid(r) ? kl[x] : zero4();
+                floatx4 kk = valid(r) ? Raw4<T>::f32(kl[x]) : zero4();
 #pragma unroll
                 for (int y = 0; y < 4; ++y) kk[y] *= __expf(sG[r * DK + c0 + y]);
                 *reinterpret_cast<floatx4*>(sKt + r * LK + c0) = kk;
@@ -646,11 +659,25 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
                 const bool ok = valid(r);
                 const long o = crow(r) * DK + c;
                 const float kx = to_f32(k[o]), qx = to_f32(q[o]);
-                const float gx = gate == GATE_CHANNEL ? g[o] : 0.f;
                 kv[p][R][e] = ok ? kx : 0.f;
                 qv[p][R][e] = ok ? qx : 0.f;
-                gv[p][R][e] = gx;
             }
+    if (gate == GATE_CHANNEL) {
+#pragma unroll
+        for (int p = 0; p < KPW; ++p)
+#pragma unroll
+            for (int R = 0; R < NB; ++R)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gv[p][R][e] = g[crow(16 * R + 4 * kg + e) * DK + 16 * (wave + 4 * p) + lr];
+    } else {
+#pragma unroll
+        for (int p = 0; p < KPW; ++p)
+#pragma unroll
+            for (int R = 0; R < NB; ++R)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gv[p][R][e] = 0.f;
+    }
     __syncthreads();
 
     // ---- phase 4: X = T^T dT (lower tiles), then dM = -strict_lower(X T^T),

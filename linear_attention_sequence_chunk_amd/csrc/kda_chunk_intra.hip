@@ -41,6 +41,9 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     const long tok0 = up.tok0;
     auto grow = [&](int t) -> long { return (tok0 + t) * H + h; };
     auto valid = [&](int t) -> bool { return t < cnt; };
+    // a row past the sequence end reads row 0 (the value is then dropped), so that
+    // loads need no branch and can all be in flight together
+    auto crow = [&](int t) -> long { return grow(t < cnt ? t : 0); };
 
     // ---------------------------------------------------------------- phase 0
     // Block-local inclusive prefix sums of the clamped log-gate (a1), block totals.
@@ -70,13 +73,19 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     __syncthreads();
     for (int u = tid; u < NB * (DK / 2); u += 256) {
         const int R = u / (DK / 2), c = 2 * (u % (DK / 2));
+        long rows[16];
+        float2 gg[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) rows[rr] = crow(R * 16 + rr);
+        gate_pair_rows<16>(g, gate, rows, DK, c, gg);
         float l0 = 0.f, l1 = 0.f;
+#pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             const int t = R * 16 + rr;
-            float2 gg = make_float2(0.f, 0.f);
-            if (valid(t)) gg = gate_pair(g, gate, grow(t), DK, c);
-            l0 += clamp_g(gg.x);
-            l1 += clamp_g(gg.y);
+            if (valid(t)) {
+                l0 += clamp_g(gg[rr].x);
+                l1 += clamp_g(gg[rr].y);
+            }
             *reinterpret_cast<float2*>(sL + t * DK + c) = make_float2(l0, l1);
         }
         sTot[R * DK + c] = l0;
@@ -334,16 +343,25 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             const float t0v = sTot[J * DK + c], t1v = sTot[J * DK + c + 1];
             if (J < R) { in0 += t0v; in1 += t1v; } else { out0 += t0v; out1 += t1v; }
         }
+        long rows[16];
+        float2 gg[16], kp[16], qp[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) rows[rr] = crow(R * 16 + rr);
+        gate_pair_rows<16>(g, gate, rows, DK, c, gg);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            Pair2<T>::load(k + rows[rr] * DK + c, kp[rr].x, kp[rr].y);
+            Pair2<T>::load(q + rows[rr] * DK + c, qp[rr].x, qp[rr].y);
+        }
         float l0 = 0.f, l1 = 0.f;
+#pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             const int t = R * 16 + rr;
             float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f;
             if (valid(t)) {
-                const float2 gg = gate_pair(g, gate, grow(t), DK, c);
-                l0 += clamp_g(gg.x); l1 += clamp_g(gg.y);
-                Pair2<T>::load(k + grow(t) * DK + c, k0, k1);
-                Pair2<T>::load(q + grow(t) * DK + c, q0, q1);
-                k0 *= sKn[t]; k1 *= sKn[t]; q0 *= sQn[t]; q1 *= sQn[t];
+                l0 += clamp_g(gg[rr].x); l1 += clamp_g(gg[rr].y);
+                k0 = kp[rr].x * sKn[t]; k1 = kp[rr].y * sKn[t];
+                q0 = qp[rr].x * sQn[t]; q1 = qp[rr].y * sQn[t];
             }
             const float ei0 = __expf(in0 + l0), ei1 = __expf(in1 + l1);
             const float eo0 = __expf(out0 - l0), eo1 = __expf(out1 - l1);

@@ -161,6 +161,41 @@ __device__ inline float2 gate_pair(const void* __restrict__ g, int mode, long ro
     return make_float2(0.f, 0.f);
 }
 
+// The log-gates of N rows (row indices rows[i]) at channels c, c + 1 (c even),
+// decided once for the mode so that every load is issued before any is used.
+template <int N>
+__device__ inline void gate_pair_rows(const void* __restrict__ g, int mode, const long* rows, int dk, int c,
+                                      float2* out) {
+    const int layout = gate_layout(mode);
+    if (layout == 0 && (mode & MODE_GATE_BF16)) {
+        const bf16* gb = reinterpret_cast<const bf16*>(g);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const bf16x2 b = *reinterpret_cast<const bf16x2*>(gb + rows[i] * dk + c);
+            out[i] = make_float2((float)b[0], (float)b[1]);
+        }
+    } else if (layout == 0) {
+        const float* gf = reinterpret_cast<const float*>(g);
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = *reinterpret_cast<const float2*>(gf + rows[i] * dk + c);
+    } else if (layout == 1 && (mode & MODE_GATE_BF16)) {
+        const bf16* gb = reinterpret_cast<const bf16*>(g);
+#pragma unroll
+        for (int i = 0; i < N; ++i) { const float x = (float)gb[rows[i]]; out[i] = make_float2(x, x); }
+    } else if (layout == 1) {
+        const float* gf = reinterpret_cast<const float*>(g);
+#pragma unroll
+        for (int i = 0; i < N; ++i) { const float x = gf[rows[i]]; out[i] = make_float2(x, x); }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = make_float2(0.f, 0.f);
+    }
+    if (mode & MODE_GATE_SOFTPLUS) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = make_float2(neg_softplus(out[i].x), neg_softplus(out[i].y));
+    }
+}
+
 // 1 / ||x|| from the sum of squares, with a zero row mapped to zero.
 __device__ inline float inv_norm(float sumsq) { return sumsq > 0.f ? rsqrtf(sumsq) : 0.f; }
 
