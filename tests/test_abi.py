@@ -305,3 +305,37 @@ def test_decode_pre_flag_codes():
     if not HAS_GPU:
         assert call(dict(t, g=t["g"] + 2), 0, _lib.PRE_GATE_BF16 | _lib.PRE_GATE_SOFTPLUS) == HIP
         assert call(t, 2, _lib.PRE_QK_L2NORM) == HIP
+
+
+def test_backward_validation_codes():
+    L = _lib.lib()
+    f = Fake()
+    B, T, H, dk, dv, C = 2, 100, 3, 128, 64, 64
+    tok, nst = B * T * H, B * H * dk * dv
+    wsb = L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, C)
+    assert wsb > L.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, C)   # + checkpoints
+    assert L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, 128) == 0  # C <= 64
+    a = dict(q=f(tok * dk * 2), k=f(tok * dk * 2), v=f(tok * dv * 2), g=f(tok * dk * 4), beta=f(tok * 4),
+             s0=f(nst * 4), dO=f(tok * dv * 4), dST=f(nst * 4), dq=f(tok * dk * 4), dk=f(tok * dk * 4),
+             dv=f(tok * dv * 4), dg=f(tok * dk * 4), dbeta=f(tok * 4), dS0=f(nst * 4),
+             B=B, T=T, H=H, dkk=dk, dvv=dv, ind=_lib.BF16, ws=f(wsb), wsb=wsb, C=C, gate=0)
+
+    def call(x):
+        return L.kda_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], x["dO"], x["dST"],
+                               x["dq"], x["dk"], x["dv"], x["dg"], x["dbeta"], x["dS0"], x["B"], x["T"],
+                               x["H"], x["dkk"], x["dvv"], x["ind"], x["ws"], x["wsb"], None, x["C"], x["gate"])
+    cases = [(dict(T=-1), SHAPE), (dict(dkk=96), UNSUP), (dict(C=128), UNSUP), (dict(ind=7), UNSUP),
+             (dict(gate=5), UNSUP), (dict(dq=None), NULL), (dict(dO=None), NULL), (dict(dg=None), NULL),
+             (dict(q=a["q"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(dbeta=a["dbeta"] + 2), MISAL),
+             (dict(ws=None), WS), (dict(wsb=wsb - 1), WS),
+             (dict(dq=a["q"]), ALIAS), (dict(dk=a["dq"] + 256), ALIAS), (dict(dS0=a["dST"]), ALIAS),
+             (dict(ws=a["dO"]), ALIAS), (dict(dg=a["ws"]), ALIAS)]
+    if not HAS_GPU:
+        cases += [(dict(), HIP), (dict(gate=2, g=None, dg=None), HIP),   # no gates: g and dg may be NULL
+                  (dict(dST=None, s0=None, dS0=None), HIP)]
+    for change, code in cases:
+        b = dict(a)
+        b.update(change)
+        assert call(b) == code, (change, code)
+    empty = dict(a, B=0)
+    assert call(empty) == OK

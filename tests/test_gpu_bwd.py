@@ -84,3 +84,37 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for name in a:
         assert torch.equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("T,dk,dv,C,dtype", [(1, 128, 128, 64, torch.bfloat16), (5, 128, 128, 64, torch.bfloat16),
+                                             (31, 64, 64, 32, torch.float32), (17, 64, 128, 16, torch.float32)])
+def test_backward_short_sequences(T, dk, dv, C, dtype):
+    """A single partial chunk (T < C), or a full one and a partial one."""
+    d = inputs.custom_prefill(90 + T, 2, T, 3, dk, dv, dtype=dtype, s0_std=0.05)
+    _run(d, C, "channel", dtype, 5, f"bwd T{T} C{C}")
+
+
+def test_backward_empty_sequence():
+    """T = 0: dS0 is dS_T, nothing else is written."""
+    dk = dv = 64
+    q = torch.zeros((2, 0, 3, dk), device="cuda")
+    beta = torch.zeros((2, 0, 3), device="cuda")
+    dO = torch.zeros((2, 0, 3, dv), device="cuda")
+    dST = torch.randn((2, 3, dk, dv), generator=torch.Generator().manual_seed(1)).cuda()
+    out = chunk_bwd(q, q, dO.clone(), q, beta, dO, None, dST, chunk_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dS0"], dST)
+    assert out["dq"].numel() == 0 and out["dg"].numel() == 0
+
+
+def test_backward_strong_gates():
+    """Log-gates ~ -U(0, 8): many 16-token blocks sum below -SAFE_SPAN (the
+    term-by-term diagonal paths of the forward and the backward), and a few gates
+    below the -20 floor (gradient 0 there; the oracle's exact value is ~e^g)."""
+    import numpy as np
+    B, T, H, dk, dv = 1, 200, 2, 128, 128
+    d = inputs.custom_prefill(97, B, T, H, dk, dv, dtype=torch.float32, s0_std=0.05)
+    g = -np.random.default_rng(6).uniform(0.0, 8.0, (B, T, H, dk))
+    g[0, 40:42, 0, :5] = -30.0
+    d["g"] = torch.tensor(g, dtype=torch.float32)
+    _run(d, 64, "channel", torch.float32, 6, "bwd strong gates")
