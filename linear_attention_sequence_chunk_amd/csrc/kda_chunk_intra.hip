@@ -5,6 +5,32 @@
 
 namespace kda {
 
+// Eight consecutive values of T as loaded; converted to fp32 (times a scale) where
+// used, so that all of a thread's loads can be in flight at once.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    u32x4 x;
+    __device__ __forceinline__ void load(const bf16* p) { x = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void get(float* o, float s) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(x[i] << 16) * s;
+            o[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u) * s;
+        }
+    }
+};
+template <> struct Raw8<float> {
+    floatx4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const floatx4*>(p);
+        b = *reinterpret_cast<const floatx4*>(p + 4);
+    }
+    __device__ __forceinline__ void get(float* o, float s) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o[i] = a[i] * s; o[4 + i] = b[i] * s; }
+    }
+};
+
 template <typename T, int DK, int DV, int C>
 __global__ __launch_bounds__(256) void chunk_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -99,6 +125,16 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     for (int s = 0; s < Cfg::NSLOT; ++s) { accA[s] = zero4(); accP[s] = zero4(); }
 
     // ---------------------------------------------------------------- phase S
+    // This thread's q and k units (row t, 8 channels) for every level below, loaded
+    // once: unit it is u = tid + 256 it of the C x (DK/8) units.
+    constexpr int NU8 = C * (DK / 8), NIT8 = (NU8 + 255) / 256;
+    Raw8<T> kraw[NIT8], qraw[NIT8];
+#pragma unroll
+    for (int it = 0; it < NIT8; ++it) {
+        const int u = tid + 256 * it, uu = u < NU8 ? u : 0, t = uu / (DK / 8), c = 8 * (uu % (DK / 8));
+        kraw[it].load(k + crow(t) * DK + c);
+        qraw[it].load(q + crow(t) * DK + c);
+    }
     // Cross levels: segment length n, split point in the middle.
     static_for<Cfg::NLV>([&](auto LV) {
         constexpr int SEG = C >> LV;
@@ -113,31 +149,20 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
             sOff[u] = s;
         }
         __syncthreads();
-        for (int u = tid; u < C * (DK / 8); u += 256) {
+#pragma unroll
+        for (int it = 0; it < NIT8; ++it) {
+            const int u = tid + 256 * it;
+            if (NU8 % 256 != 0 && u >= NU8) continue;
             const int t = u / (DK / 8), c = 8 * (u % (DK / 8));
             const int R = t / 16, seg = t / SEG, w = t - seg * SEG;
             float L8[8], o8[8], kv[8], x[8];
             Vec8<float>::load(sL + t * DK + c, L8);
             Vec8<float>::load(sOff + R * DK + c, o8);
-            if (valid(t)) {
-                Vec8<T>::load(k + grow(t) * DK + c, kv);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) kv[m] *= sKn[t];
-            } else {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) kv[m] = 0.f;
-            }
+            kraw[it].get(kv, valid(t) ? sKn[t] : 0.f);
             if (w >= HALF) {                      // row side: e^{G_r - G_{m-1}} <= 1
                 const int ri = seg * HALF + (w - HALF);
                 float qv[8];
-                if (valid(t)) {
-                    Vec8<T>::load(q + grow(t) * DK + c, qv);
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) qv[m] *= sQn[t];
-                } else {
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) qv[m] = 0.f;
-                }
+                qraw[it].get(qv, valid(t) ? sQn[t] : 0.f);
 #pragma unroll
                 for (int m = 0; m < 8; ++m) { const float e = __expf(o8[m] + L8[m]); x[m] = kv[m] * e; qv[m] *= e; }
                 Vec8<T>::store(sKrow + ri * LDK + c, x);
@@ -169,20 +194,15 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     // Diagonal sub-blocks, block start as reference, in passes of HR rows.
     static_for<Cfg::NPASS>([&](auto PS) {
         constexpr int r0 = PS * HR;
-        for (int u = tid; u < HR * (DK / 8); u += 256) {
-            const int tl = u / (DK / 8), c = 8 * (u % (DK / 8));
-            const int t = r0 + tl, R = t / 16;
+#pragma unroll
+        for (int it = 0; it < NIT8; ++it) {           // this thread's units whose row is in the pass
+            const int u = tid + 256 * it, t = u / (DK / 8), c = 8 * (u % (DK / 8));
+            if (u >= NU8 || t < r0 || t >= r0 + HR) continue;
+            const int tl = t - r0, R = t / 16;
             float L8[8], kv[8], qv[8], x[8];
             Vec8<float>::load(sL + t * DK + c, L8);
-            if (valid(t)) {
-                Vec8<T>::load(k + grow(t) * DK + c, kv);
-                Vec8<T>::load(q + grow(t) * DK + c, qv);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) { kv[m] *= sKn[t]; qv[m] *= sQn[t]; }
-            } else {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) { kv[m] = 0.f; qv[m] = 0.f; }
-            }
+            kraw[it].get(kv, valid(t) ? sKn[t] : 0.f);
+            qraw[it].get(qv, valid(t) ? sQn[t] : 0.f);
             float y[8];
 #pragma unroll
             for (int m = 0; m < 8; ++m) { const float e = __expf(L8[m]); x[m] = kv[m] * e; y[m] = qv[m] * e; }
@@ -316,17 +336,24 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
     __syncthreads();
     T* sVt = reinterpret_cast<T*>(smem + Cfg::SZ_TB);     // [DV][LDT]: beta_i v_ij
     T* sKt = sVt + DV * LDT;                                // [DK][LDT]: beta_i e^{G_i} k_i
-    for (int u = tid; u < C * (DV / 8); u += 256) {
-        const int i = u / (DV / 8), j = 8 * (u % (DV / 8));
-        float vv[8];
-        if (valid(i)) Vec8<T>::load(v + grow(i) * DV + j, vv);
-        else {
+    {
+        constexpr int NUV = C * (DV / 8), NITV = (NUV + 255) / 256;
+        Raw8<T> vraw[NITV];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) vv[m] = 0.f;
+        for (int it = 0; it < NITV; ++it) {
+            const int u = tid + 256 * it, uu = u < NUV ? u : 0;
+            vraw[it].load(v + crow(uu / (DV / 8)) * DV + 8 * (uu % (DV / 8)));
         }
-        const float bi = sBeta[i];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) sVt[(j + m) * LDT + i] = from_f32<T>(bi * vv[m]);
+        for (int it = 0; it < NITV; ++it) {
+            const int u = tid + 256 * it;
+            if (NUV % 256 != 0 && u >= NUV) continue;
+            const int i = u / (DV / 8), j = 8 * (u % (DV / 8));
+            float vv[8];
+            vraw[it].get(vv, valid(i) ? sBeta[i] : 0.f);     // beta_i v_i (0 past the end)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) sVt[(j + m) * LDT + i] = from_f32<T>(vv[m]);
+        }
     }
     if constexpr (CK > C) {
         for (int u = tid; u < (DV + DK) * (CK - C); u += 256) {
