@@ -545,39 +545,36 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     auto chan = [&](int p) { return 64 * p + 32 * (wave & 1) + 8 * (lane >> 4); };
 
     // ---------------------------------------------------------------- loads
-    bf16x8 qv[2], kv[2], vv[Cfg::NITV];
+    // Every load is issued before any value is used: a row past the sequence end
+    // reads row 0 and is zeroed afterwards, and the gate's layout and storage are
+    // decided once for the whole block of loads.
+    const bool tok_ok = valid(t);
+    const long trow = grow(tok_ok ? t : 0);
+    const int glay = gate_layout(gate);
+    bf16x8 qv[2], kv[2], vv[Cfg::NITV], g8[2];
     floatx4 ga[2], gb[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        if (valid(t)) {
-            const long base = grow(t) * DK + chan(p);
-            qv[p] = *reinterpret_cast<const bf16x8*>(q + base);
-            kv[p] = *reinterpret_cast<const bf16x8*>(k + base);
-            if (gate_layout(gate) == GATE_CHANNEL) {
-                if (gate & MODE_GATE_BF16) {
-                    const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(g) + base);
-                    ga[p] = floatx4{(float)g8[0], (float)g8[1], (float)g8[2], (float)g8[3]};
-                    gb[p] = floatx4{(float)g8[4], (float)g8[5], (float)g8[6], (float)g8[7]};
-                } else {
-                    ga[p] = *reinterpret_cast<const floatx4*>(g + base);
-                    gb[p] = *reinterpret_cast<const floatx4*>(g + base + 4);
-                }
-                if (gate & MODE_GATE_SOFTPLUS) {
+        qv[p] = *reinterpret_cast<const bf16x8*>(q + trow * DK + chan(p));
+        kv[p] = *reinterpret_cast<const bf16x8*>(k + trow * DK + chan(p));
+    }
+    if (glay == GATE_CHANNEL && (gate & MODE_GATE_BF16)) {
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) { ga[p][m] = neg_softplus(ga[p][m]); gb[p][m] = neg_softplus(gb[p][m]); }
-                }
-            } else if (gate_layout(gate) == GATE_HEAD) {
-                const float x = gate_at(g, gate, grow(t), DK, 0);
-                ga[p] = floatx4{x, x, x, x};
-                gb[p] = ga[p];
-            } else {
-                ga[p] = zero4(); gb[p] = zero4();
-            }
-        } else {
+        for (int p = 0; p < 2; ++p)
+            g8[p] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(g) + trow * DK + chan(p));
+    } else if (glay == GATE_CHANNEL) {
 #pragma unroll
-            for (int m = 0; m < 8; ++m) { qv[p][m] = (bf16)0.f; kv[p][m] = (bf16)0.f; }
-            ga[p] = zero4(); gb[p] = zero4();
+        for (int p = 0; p < 2; ++p) {
+            ga[p] = *reinterpret_cast<const floatx4*>(g + trow * DK + chan(p));
+            gb[p] = *reinterpret_cast<const floatx4*>(g + trow * DK + chan(p) + 4);
         }
+    } else if (glay == GATE_HEAD) {
+        const float x = (gate & MODE_GATE_BF16) ? (float)reinterpret_cast<const bf16*>(g)[trow] : g[trow];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) { ga[p] = floatx4{x, x, x, x}; gb[p] = ga[p]; }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) { ga[p] = zero4(); gb[p] = zero4(); }
     }
     // v unit mapping: each group of 64 units covers 16 tokens x 4 groups of 8 channels
     auto vunit = [&](int it, int& tv, int& j) {
@@ -589,13 +586,41 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     for (int it = 0; it < Cfg::NITV; ++it) {
         int tv, j;
         vunit(it, tv, j);
-        if (valid(tv)) vv[it] = *reinterpret_cast<const bf16x8*>(v + grow(tv) * DV + j);
-        else {
+        vv[it] = *reinterpret_cast<const bf16x8*>(v + grow(valid(tv) ? tv : 0) * DV + j);
+    }
+    const float bt = beta[grow(tid < C && valid(tid) ? tid : 0)];
+    // decode and mask, now that every load is in flight
+    if (tid < C) sBeta[tid] = valid(tid) ? bt : 0.f;
+    if (glay == GATE_CHANNEL && (gate & MODE_GATE_BF16)) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            ga[p] = floatx4{(float)g8[p][0], (float)g8[p][1], (float)g8[p][2], (float)g8[p][3]};
+            gb[p] = floatx4{(float)g8[p][4], (float)g8[p][5], (float)g8[p][6], (float)g8[p][7]};
+        }
+    }
+    if (glay != GATE_NONE && (gate & MODE_GATE_SOFTPLUS)) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) { ga[p][m] = neg_softplus(ga[p][m]); gb[p][m] = neg_softplus(gb[p][m]); }
+    }
+    if (!tok_ok) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) { qv[p][m] = (bf16)0.f; kv[p][m] = (bf16)0.f; }
+            ga[p] = zero4(); gb[p] = zero4();
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < Cfg::NITV; ++it) {
+        int tv, j;
+        vunit(it, tv, j);
+        if (!valid(tv)) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) vv[it][m] = (bf16)0.f;
         }
     }
-    if (tid < C) sBeta[tid] = valid(tid) ? beta[grow(tid)] : 0.f;
     // q and k row norms (pre-processing): a token's 128 channels are spread over the
     // four lane groups of this wave and the partner wave (wave ^ 1)
     const bool qknorm = gate & MODE_QK_L2NORM;
