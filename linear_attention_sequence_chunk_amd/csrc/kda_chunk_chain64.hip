@@ -81,8 +81,13 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O) + R * 16 * DVS;
 
     // ---- operand registers, D chunks in flight
+    // Every wave issues the same loads in every chunk (W waves load P and O waves
+    // load U too, unused; past the last chunk the last one is loaded again), so
+    // that the number of loads in flight is the same on every path and each
+    // chunk waits only for its own operands, D - 1 chunks of loads staying in flight.
     u32x4 fA[D][4];      // Wk (W waves) or Qt (O waves), row tile R, 4 k-steps
-    u32x4 fX[D][2];      // U tiles of this slice, 2 dwords each (W waves) or P k-steps (O waves)
+    u32x2 fU[D][NJ];     // U tiles of this slice (W waves)
+    u32x4 fX[D][2];      // P k-steps (O waves; k-step 1 of row tiles 0, 1 is not used)
     u32x4 fK[D][2];      // Kb^T channel tile ct, 2 k-steps
     u32x4 fG[D];         // gam of this lane's 4 state rows
     // first half: what phase 1 consumes; second half: what phase 2 consumes
@@ -92,23 +97,17 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         const u32x4* a_ = reinterpret_cast<const u32x4*>((wW ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
                           + R * 4 * 64 + lane;                                                      \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
-        if (wW) {                                                                                   \
-            const u32x2* u_ = reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))           \
-                              + (R * (DV / 16) + sl * NJ) * 64 + lane;                              \
-            _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                       \
-                const u32x2 w_ = u_[j * 64];                                                       \
-                fX[SL][0][2 * j] = w_[0];                                                          \
-                fX[SL][0][2 * j + 1] = w_[1];                                                      \
-            }                                                                                      \
-        }                                                                                           \
+        const u32x2* u_ = reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))               \
+                          + (R * (DV / 16) + sl * NJ) * 64 + lane;                                  \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) fU[SL][j] = u_[j * 64];                     \
     }
 #define KDA_C64_PREFETCH_2(SL, CH)                                                                  \
     {                                                                                               \
         const long ch_ = (CH);                                                                      \
-        if (!wW) {                                                                                  \
+        {                                                                                           \
             const u32x4* p_ = reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
             fX[SL][0] = p_[0];                                                                      \
-            if (R >= 2) fX[SL][1] = p_[64];                                                         \
+            fX[SL][1] = p_[64];                                                                     \
         }                                                                                           \
         const u32x4* k_ = reinterpret_cast<const u32x4*>(ws_kb + ch_ * (long)(DK * C)) + ct * 2 * 64 + lane; \
         fK[SL][0] = k_[0];                                                                          \
@@ -116,12 +115,13 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         fG[SL] = *reinterpret_cast<const u32x4*>(ws_gam + ch_ * (long)DK + ct * 16 + 4 * (lane >> 4)); \
     }
 
+    if (NC > 0) {                                                   // an empty sequence loads nothing
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (d < NC) {
-            KDA_C64_PREFETCH_1(d, unit_of(d));
-            KDA_C64_PREFETCH_2(d, unit_of(d));
+        for (int d = 0; d < D; ++d) {
+            KDA_C64_PREFETCH_1(d, unit_of(d < NC ? d : NC - 1));
+            KDA_C64_PREFETCH_2(d, unit_of(d < NC ? d : NC - 1));
         }
+    }
 
     // ---- state rows 16*ct + 4(l/16) + e, columns j0 + 16 jt + l%16, fp32 in accumulators
     floatx4 accS[NJ];
@@ -146,11 +146,9 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     };
     write_state_operand();
 
-    for (int n0 = 0; n0 < NC; n0 += D) {
-      static_for<D>([&](auto DI) {
+    // one chunk n whose operands sit in register slot d
+    auto step = [&](auto DI, int n) {
         constexpr int d = DI;
-        const int n = n0 + d;
-        if (n >= NC) return;
         __syncthreads();                                            // S^T of chunk n's start state
 
         // ---- phase 1: W waves W = U - Wk S (to LDS as W^T); O waves O = Qt S
@@ -169,15 +167,14 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         if (wW) {
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt) {
-                const u32x2 up = u32x2{fX[d][0][2 * jt], fX[d][0][2 * jt + 1]};
-                const bf16x4 uu = __builtin_bit_cast(bf16x4, up);
+                const bf16x4 uu = __builtin_bit_cast(bf16x4, fU[d][jt]);
                 bf16x4 w4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w4[e] = (bf16)((float)uu[e] - acc[jt][e]);
                 *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
             }
         }
-        if (n + D < NC) KDA_C64_PREFETCH_1(d, unit_of(n + D));
+        KDA_C64_PREFETCH_1(d, unit_of(n + D < NC ? n + D : NC - 1));
         __syncthreads();                                            // W^T complete
 
         // ---- phase 2: O waves O += P W (stored); all waves S = gam S + Kb^T W
@@ -224,9 +221,15 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
             }
         }
         write_state_operand();                                      // read only after the next barrier
-        if (n + D < NC) KDA_C64_PREFETCH_2(d, unit_of(n + D));
-      });
-    }
+        KDA_C64_PREFETCH_2(d, unit_of(n + D < NC ? n + D : NC - 1));
+    };
+    // whole rounds of D chunks with no condition inside (the loads in flight are
+    // then the same on every path), then the last NC % D chunks
+    int n0 = 0;
+    for (; n0 + D <= NC; n0 += D) static_for<D>([&](auto DI) { step(DI, n0 + DI); });
+    static_for<D>([&](auto DI) {
+        if (n0 + DI < NC) step(DI, n0 + DI);
+    });
 
     if (sT) {
 #pragma unroll
