@@ -69,3 +69,20 @@ def test_decode_gate_layouts(layout):
     ref = {"q": seq(d["q"]), "k": seq(d["k"]), "v": seq(d["v"]), "g": seq(g_channel),
            "beta": seq(d["beta"]), "S0": S0}
     check(ref, seq(o.cpu()), S.cpu(), TOL[torch.bfloat16], tag=f"decode {layout}")
+
+
+@pytest.mark.parametrize("dk,dv,C,dtype", [(128, 128, 64, torch.bfloat16), (64, 64, 32, torch.float32),
+                                           (128, 64, 16, torch.float32)])
+def test_prefill_without_decay_every_chunk_count(dk, dv, C, dtype):
+    """alpha = 1 (no gate): nothing decays, so an error anywhere in the chain of
+    states stays visible to the end; every chunk count 1..11 (all positions of the
+    last chunk within the chain kernels' prefetch rounds), full and partial."""
+    for nc in range(1, 12):
+        for T in (nc * C, nc * C - 5):
+            d = inputs.custom_prefill(200 + nc, 1, T, 2, dk, dv, dtype=dtype, gates="none", s0_std=0.05)
+            dg = cuda(d)
+            o, S = chunk_fwd(dg["q"], dg["k"], dg["v"], None, dg["beta"], dg["S0"], chunk_size=C, gate_layout="none")
+            torch.cuda.synchronize()
+            ref = dict(d)
+            ref["g"] = torch.zeros_like(d["g"])
+            check(ref, o.cpu(), S.cpu(), TOL[dtype], tag=f"no decay dk{dk} dv{dv} C{C} T{T}")
