@@ -249,6 +249,38 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv,
                                      int in_dtype, int C);
 
 /*
+ * kda_chunk_bwd_varlen -- the backward pass of kda_chunk_fwd_varlen: kda_chunk_bwd
+ * over a packed batch of N sequences of different lengths.  Each sequence is
+ * differentiated on its own (no chunk spans two sequences; the reverse
+ * recurrence over the chunks starts from each sequence's own dST and ends in its
+ * own dS0), as in the chunkwise training form of the chunk paragraph of the
+ * KimiK3 essay and sections 十六 and 十七 of the explainer.
+ *   q, k, v, g, beta, initial_state, cu_seqlens   as for kda_chunk_fwd_varlen
+ *   dO            [T,H,dv] fp32       cotangent of o
+ *   dST           [N,H,dk,dv] fp32    cotangent of the final states, or NULL (zeros)
+ *   dq, dk        [T,H,dk] fp32;  dv [T,H,dv] fp32;  dbeta [T,H] fp32
+ *   dg            [T,H,dk] / [T,H] fp32 by gate_layout (NULL allowed without gates)
+ *   dS0           [N,H,dk,dv] fp32 or NULL
+ *   workspace     >= kda_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, in_dtype, C)
+ * Tokens outside every sequence (cu_seqlens[N] < T) are not written.  The result
+ * for each sequence equals a kda_chunk_bwd call on that sequence alone.  Same
+ * rules as kda_chunk_bwd otherwise; cu_seqlens must not overlap an output or the
+ * workspace.
+ */
+int kda_chunk_bwd_varlen(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *initial_state,
+                         const float *dO, const float *dST,
+                         float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                         const int *cu_seqlens, int N, int T, int H, int dk_size, int dv_size,
+                         int in_dtype, void *workspace, size_t workspace_bytes,
+                         void *stream, int C, int gate_layout);
+
+/* Bytes of device workspace kda_chunk_bwd_varlen needs (0 if unsupported);
+ * host-only.  Depends on N and T only, not on the individual lengths. */
+size_t kda_chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
+                                            int in_dtype, int C);
+
+/*
  * kda_decode_step -- one token per sequence, state updated IN PLACE.
  *   q, k   [N,H,dk] in_dtype;  v [N,H,dv] in_dtype
  *   g      [N,H,dk] fp32 log-gate;  beta [N,H] fp32

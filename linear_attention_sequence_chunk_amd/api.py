@@ -214,6 +214,52 @@ def chunk_bwd(q, k, v, g, beta, dO, initial_state=None, dST=None, chunk_size=64,
     return out
 
 
+def chunk_bwd_varlen(q, k, v, g, beta, dO, cu_seqlens, initial_state=None, dST=None, chunk_size=64,
+                     gate_layout="channel", workspace=None, stream=None):
+    """Backward pass of chunk_fwd_varlen (kda_chunk_bwd_varlen).  q,k [T,H,dk],
+    v [T,H,dv], beta [T,H], dO [T,H,dv] fp32, cu_seqlens int32 [N+1];
+    initial_state and dST [N,H,dk,dv] fp32 or None.  Returns a dict of fp32
+    tensors dq, dk, dv, dg (None without gates), dbeta, dS0 [N,H,dk,dv]."""
+    _gate(gate_layout)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    _check_tensor("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    _check_tensor("k", k, (T, H, dk), q.dtype, dev)
+    _check_tensor("v", v, (T, H, dv), q.dtype, dev)
+    _check_gate(g, gate_layout, (T, H), dk, dev)
+    _check_tensor("beta", beta, (T, H), torch.float32, dev)
+    _check_tensor("dO", dO, (T, H, dv), torch.float32, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
+    if dST is not None:
+        _check_tensor("dST", dST, (N, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((T, H, dk), **f32), "dk": torch.empty((T, H, dk), **f32),
+           "dv": torch.empty((T, H, dv), **f32), "dbeta": torch.empty((T, H), **f32),
+           "dS0": torch.empty((N, H, dk, dv), **f32),
+           "dg": None if gate_layout == "none" else
+           torch.empty((T, H, dk) if gate_layout == "channel" else (T, H), **f32)}
+    L = _lib.lib()
+    nbytes = int(L.kda_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, _code(q.dtype), chunk_size))
+    if nbytes == 0 and N * T * H > 0:
+        raise _lib.KdaError(3, "kda_chunk_bwd_varlen_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = L.kda_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dO),
+                                _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                                _ptr(out["dbeta"]), _ptr(out["dS0"]), _ptr(cu_seqlens), N, T, H, dk, dv,
+                                _code(q.dtype), _ptr(workspace), workspace.numel(), _stream(stream), chunk_size,
+                                _gate(gate_layout))
+    _lib.check(st, "kda_chunk_bwd_varlen")
+    return out
+
+
 class ChunkPlan:
     """Pre-allocated outputs and workspace for repeated kda_chunk_fwd calls on the
     same sizes; ``run`` calls both stages, ``intra``/``chain`` one each."""

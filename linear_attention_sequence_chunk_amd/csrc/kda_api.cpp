@@ -192,6 +192,101 @@ int run_chunk(const ChunkCall& c, int stages) {
     return finish(hipSuccess, a.stream);
 }
 
+struct BwdCall {
+    const void *q, *k, *v;
+    const float *g, *beta, *s0, *dO, *dST;
+    float *dq, *dk, *dv, *dg, *dbeta, *dS0;
+    int B, T, H, dk_size, dv_size, in_dtype;
+    void* ws;
+    size_t ws_bytes;
+    void* stream;
+    int C, gate;
+    const int* cu_seqlens = nullptr;   // packed variable-length batch (B = 1, N sequences)
+    int N = 0;
+    bool packed = false;
+};
+
+// The backward pass: validation, the forward stages again (generic workspace
+// format, with checkpoints), then the backward stages.
+int run_bwd(BwdCall c) {
+    const int dk = c.dk_size, dv = c.dv_size;
+    if (c.B < 0 || c.T < 0 || c.H < 0 || c.N < 0) return KDA_ERR_SHAPE;
+    if (!dtype_ok(c.in_dtype) || !gate_ok(c.gate)) return KDA_ERR_UNSUPPORTED;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
+    const bool bf = c.in_dtype == KDA_BF16;
+    if (!kda::bwd_supported(dk, dv, c.C, bf) || !kda::chunk_supported(dk, dv, c.C, bf)) return KDA_ERR_UNSUPPORTED;
+    // token rows: [B,T,H] (fixed-length) or [T,H] (packed); states: [B,H] or [N,H]
+    const long nseqh = (long)(c.packed ? c.N : c.B) * c.H;
+    const size_t tok = (size_t)(c.packed ? 1 : c.B) * c.T * c.H, nst = (size_t)nseqh * dk * dv;
+    const bool need_g = c.gate != KDA_GATE_NONE;
+    if (!need_g) c.g = nullptr;
+    if (!need_g) c.dg = nullptr;
+    if (c.packed && nseqh > 0 && !c.cu_seqlens) return KDA_ERR_NULL;
+    if (c.packed && c.cu_seqlens && !aligned(c.cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
+    if (tok > 0 && (!c.q || !c.k || !c.v || (need_g && (!c.g || !c.dg)) || !c.beta || !c.dO || !c.dq || !c.dk ||
+                    !c.dv || !c.dbeta))
+        return KDA_ERR_NULL;
+    const void* p16[4] = {c.q, c.k, c.v, c.ws};
+    for (const void* p : p16)
+        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
+    if (c.g && !aligned(c.g, c.gate == KDA_GATE_CHANNEL ? 8 : 4)) return KDA_ERR_MISALIGNED;
+    const void* p4[10] = {c.beta, c.s0, c.dO, c.dST, c.dq, c.dk, c.dv, c.dg, c.dbeta, c.dS0};
+    for (const void* p : p4)
+        if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
+    const kda::BwdLayout L = c.packed ? kda::bwd_layout_packed(c.N, c.T, c.H, dk, dv, bf, c.C)
+                                      : kda::bwd_layout(c.B, c.T, c.H, dk, dv, bf, c.C);
+    const bool uses_ws = tok > 0 && nseqh > 0;
+    if (uses_ws && (!c.ws || c.ws_bytes < L.total)) return KDA_ERR_WORKSPACE;
+    const size_t ei = esize(c.in_dtype), gb = gate_bytes(c.gate, dk);
+    const Range rq = range_of(c.q, tok * dk * ei), rk = range_of(c.k, tok * dk * ei), rv = range_of(c.v, tok * dv * ei),
+                rg = range_of(c.g, tok * gb), rb = range_of(c.beta, tok * 4), rs0 = range_of(c.s0, nst * 4),
+                rdo = range_of(c.dO, tok * dv * 4), rdst = range_of(c.dST, nst * 4),
+                rw = range_of(c.ws, uses_ws ? L.total : 0),
+                rcu = range_of(c.packed ? c.cu_seqlens : nullptr, ((size_t)c.N + 1) * 4);
+    const Range outs[] = {range_of(c.dq, tok * dk * 4), range_of(c.dk, tok * dk * 4), range_of(c.dv, tok * dv * 4),
+                          range_of(c.dg, tok * gb), range_of(c.dbeta, tok * 4), range_of(c.dS0, nst * 4)};
+    const Range ins[] = {rq, rk, rv, rg, rb, rs0, rdo, rdst, rw, rcu};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return KDA_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return KDA_ERR_ALIAS;
+    }
+    const Range fwd_in[] = {rq, rk, rv, rg, rb, rs0, rdo, rdst, rcu};
+    for (const Range& r : fwd_in)
+        if (overlap(rw, r)) return KDA_ERR_ALIAS;
+
+    if (nseqh == 0) return KDA_OK;
+    int st = device_ready();
+    if (st != KDA_OK) return st;
+    if (c.T == 0) {                                        // dS0 = dS_T: nothing happens in between
+        if (c.dS0) {
+            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0,
+                               (hipStream_t)c.stream, c.dST, c.dS0, (long)nst);
+            return finish(hipGetLastError(), (hipStream_t)c.stream);
+        }
+        return KDA_OK;
+    }
+    char* ws = (char*)c.ws;
+    kda::ChunkArgs a;
+    a.q = c.q; a.k = c.k; a.v = c.v; a.g = c.g; a.beta = c.beta; a.s0 = c.s0; a.o = nullptr; a.sT = nullptr;
+    a.B = c.packed ? 1 : c.B; a.T = c.T; a.H = c.H; a.dk = dk; a.dv = dv; a.C = c.C;
+    a.in_bf16 = bf; a.out_bf16 = false; a.gate = c.gate;
+    a.ws = ws; a.ws_bytes = L.fwd.total; a.stream = (hipStream_t)c.stream;
+    a.cu_seqlens = c.packed ? c.cu_seqlens : nullptr;
+    a.N = c.packed ? c.N : 0;
+    a.generic = true;
+    a.ck_t = (float*)(ws + L.t); a.ck_a = (float*)(ws + L.a);
+    a.ck_state = (float*)(ws + L.state); a.ck_w = (float*)(ws + L.w);
+    if (kda::run_chunk_intra(a) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::run_chunk_chain(a) != hipSuccess) return KDA_ERR_HIP;
+    kda::BwdArgs bw;
+    bw.fwd = a; bw.dO = c.dO; bw.dST = c.dST;
+    bw.dq = c.dq; bw.dk = c.dk; bw.dv = c.dv; bw.dg = c.dg; bw.dbeta = c.dbeta; bw.dS0 = c.dS0;
+    bw.ck_dS = (float*)(ws + L.dS); bw.ck_dW = (float*)(ws + L.dW);
+    return finish(kda::run_chunk_bwd_stages(bw), (hipStream_t)c.stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,75 +334,33 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in
     return kda::bwd_layout(B, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
 }
 
+size_t kda_chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv, int in_dtype, int C) {
+    if (N < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    if (!kda::bwd_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
+    if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
+    return kda::bwd_layout_packed(N, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
+}
+
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const float* initial_state, const float* dO, const float* dST, float* dq, float* dk_out,
                   float* dv_out, float* dg, float* dbeta, float* dS0, int B, int T, int H, int dk, int dv,
                   int in_dtype, void* workspace, size_t workspace_bytes, void* stream, int C, int gate_layout) {
-    if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
-    if (!dtype_ok(in_dtype) || !gate_ok(gate_layout)) return KDA_ERR_UNSUPPORTED;
-    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
-    if (!kda::bwd_supported(dk, dv, C, in_dtype == KDA_BF16) || !kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16))
-        return KDA_ERR_UNSUPPORTED;
-    const size_t tok = (size_t)B * T * H, nst = (size_t)B * H * dk * dv;
-    const bool need_g = gate_layout != KDA_GATE_NONE;
-    if (!need_g) g = nullptr;
-    if (!need_g) dg = nullptr;
-    if (tok > 0 && (!q || !k || !v || (need_g && (!g || !dg)) || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta))
-        return KDA_ERR_NULL;
-    const void* p16[4] = {q, k, v, workspace};
-    for (const void* p : p16)
-        if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
-    if (g && !aligned(g, gate_layout == KDA_GATE_CHANNEL ? 8 : 4)) return KDA_ERR_MISALIGNED;
-    const void* p4[11] = {beta, initial_state, dO, dST, dq, dk_out, dv_out, dg, dbeta, dS0, nullptr};
-    for (const void* p : p4)
-        if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
-    const kda::BwdLayout L = kda::bwd_layout(B, T, H, dk, dv, in_dtype == KDA_BF16, C);
-    if (tok > 0 && (!workspace || workspace_bytes < L.total)) return KDA_ERR_WORKSPACE;
-    const size_t ei = esize(in_dtype), gb = gate_bytes(gate_layout, dk);
-    const Range rq = range_of(q, tok * dk * ei), rk = range_of(k, tok * dk * ei), rv = range_of(v, tok * dv * ei),
-                rg = range_of(g, tok * gb), rb = range_of(beta, tok * 4), rs0 = range_of(initial_state, nst * 4),
-                rdo = range_of(dO, tok * dv * 4), rdst = range_of(dST, nst * 4), rw = range_of(workspace, tok > 0 ? L.total : 0);
-    const Range outs[] = {range_of(dq, tok * dk * 4), range_of(dk_out, tok * dk * 4), range_of(dv_out, tok * dv * 4),
-                          range_of(dg, tok * gb), range_of(dbeta, tok * 4), range_of(dS0, nst * 4)};
-    const Range ins[] = {rq, rk, rv, rg, rb, rs0, rdo, rdst, rw};
-    for (int i = 0; i < 6; ++i) {
-        for (const Range& r : ins)
-            if (overlap(outs[i], r)) return KDA_ERR_ALIAS;
-        for (int j = i + 1; j < 6; ++j)
-            if (overlap(outs[i], outs[j])) return KDA_ERR_ALIAS;
-    }
-    const Range fwd_in[] = {rq, rk, rv, rg, rb, rs0, rdo, rdst};
-    for (const Range& r : fwd_in)
-        if (overlap(rw, r)) return KDA_ERR_ALIAS;
+    BwdCall c{q, k, v, g, beta, initial_state, dO, dST, dq, dk_out, dv_out, dg, dbeta, dS0,
+              B, T, H, dk, dv, in_dtype, workspace, workspace_bytes, stream, C, gate_layout};
+    return run_bwd(c);
+}
 
-    const long nseqh = (long)B * H;
-    if (nseqh == 0) return KDA_OK;
-    int st = device_ready();
-    if (st != KDA_OK) return st;
-    if (T == 0) {                                          // dS0 = dS_T: nothing happens in between
-        if (dS0) {
-            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0,
-                               (hipStream_t)stream, dST, dS0, (long)nst);
-            return finish(hipGetLastError(), (hipStream_t)stream);
-        }
-        return KDA_OK;
-    }
-    char* ws = (char*)workspace;
-    kda::ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.s0 = initial_state; a.o = nullptr; a.sT = nullptr;
-    a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.C = C;
-    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = false; a.gate = gate_layout;
-    a.ws = ws; a.ws_bytes = L.fwd.total; a.stream = (hipStream_t)stream;
-    a.generic = true;
-    a.ck_t = (float*)(ws + L.t); a.ck_a = (float*)(ws + L.a);
-    a.ck_state = (float*)(ws + L.state); a.ck_w = (float*)(ws + L.w);
-    if (kda::run_chunk_intra(a) != hipSuccess) return KDA_ERR_HIP;
-    if (kda::run_chunk_chain(a) != hipSuccess) return KDA_ERR_HIP;
-    kda::BwdArgs bw;
-    bw.fwd = a; bw.dO = dO; bw.dST = dST;
-    bw.dq = dq; bw.dk = dk_out; bw.dv = dv_out; bw.dg = dg; bw.dbeta = dbeta; bw.dS0 = dS0;
-    bw.ck_dS = (float*)(ws + L.dS); bw.ck_dW = (float*)(ws + L.dW);
-    return finish(kda::run_chunk_bwd_stages(bw), (hipStream_t)stream);
+int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* initial_state, const float* dO, const float* dST, float* dq,
+                         float* dk_out, float* dv_out, float* dg, float* dbeta, float* dS0,
+                         const int* cu_seqlens, int N, int T, int H, int dk, int dv, int in_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream, int C, int gate_layout) {
+    BwdCall c{q, k, v, g, beta, initial_state, dO, dST, dq, dk_out, dv_out, dg, dbeta, dS0,
+              1, T, H, dk, dv, in_dtype, workspace, workspace_bytes, stream, C, gate_layout};
+    c.cu_seqlens = cu_seqlens;
+    c.N = N;
+    c.packed = true;
+    return run_bwd(c);
 }
 
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C) {

@@ -959,10 +959,10 @@ static hipError_t bwd_dims(const BwdArgs& b) {
     return a.dv == 64 ? bwd_c<T, 128, 64>(b) : bwd_c<T, 128, 128>(b);
 }
 
-BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
+// The checkpoints follow the forward workspace, one slot per unit of the grid.
+static BwdLayout bwd_units(const WsLayout& fwd, size_t units, int dk, int dv, int C) {
     BwdLayout L{};
-    L.fwd = ws_layout(B, T, H, dk, dv, in_bf16, C, true);
-    const size_t units = (size_t)B * H * (size_t)((T + C - 1) / C);
+    L.fwd = fwd;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     size_t off = al(L.fwd.total);
     L.t = off;     off = al(off + units * C * C * 4);
@@ -973,6 +973,16 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
     L.dW = off;    off = al(off + units * C * dv * 4);
     L.total = off;
     return L;
+}
+
+BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C) {
+    const size_t units = (size_t)B * H * (size_t)((T + C - 1) / C);
+    return bwd_units(ws_layout(B, T, H, dk, dv, in_bf16, C, true), units, dk, dv, C);
+}
+
+BwdLayout bwd_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C) {
+    const size_t units = ((size_t)((T + C - 1) / C) + (size_t)N) * H;     // as unit_count
+    return bwd_units(ws_layout_packed(N, T, H, dk, dv, in_bf16, C, true), units, dk, dv, C);
 }
 
 hipError_t run_chunk_bwd_stages(const BwdArgs& b) {

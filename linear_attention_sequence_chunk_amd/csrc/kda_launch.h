@@ -90,6 +90,8 @@ struct BwdLayout {
     size_t t, a, state, w, dS, dW, total;
 };
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C);
+// Packed variable-length batch of N sequences, T tokens in all (units as ws_layout_packed).
+BwdLayout bwd_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C);
 bool bwd_supported(int dk, int dv, int C, bool in_bf16);
 hipError_t run_chunk_bwd_stages(const BwdArgs& b);
 

@@ -339,3 +339,41 @@ def test_backward_validation_codes():
         assert call(b) == code, (change, code)
     empty = dict(a, B=0)
     assert call(empty) == OK
+
+
+def test_backward_varlen_validation_codes():
+    """kda_chunk_bwd_varlen: sizes, NULLs, alignment, workspace and aliasing,
+    including cu_seqlens, all decided on the host."""
+    L = _lib.lib()
+    f = Fake()
+    N, T, H, dk, dv, C = 3, 250, 2, 128, 64, 64
+    tok, nst = T * H, N * H * dk * dv
+    wsb = L.kda_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, _lib.BF16, C)
+    assert wsb > L.kda_chunk_bwd_workspace_bytes(1, T, H, dk, dv, _lib.BF16, C)   # room for N extra chunks
+    assert L.kda_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, _lib.BF16, 128) == 0
+    assert L.kda_chunk_bwd_varlen_workspace_bytes(-1, T, H, dk, dv, _lib.BF16, C) == 0
+    a = dict(q=f(tok * dk * 2), k=f(tok * dk * 2), v=f(tok * dv * 2), g=f(tok * dk * 4), beta=f(tok * 4),
+             s0=f(nst * 4), dO=f(tok * dv * 4), dST=f(nst * 4), dq=f(tok * dk * 4), dk=f(tok * dk * 4),
+             dv=f(tok * dv * 4), dg=f(tok * dk * 4), dbeta=f(tok * 4), dS0=f(nst * 4), cu=f((N + 1) * 4),
+             N=N, T=T, H=H, ws=f(wsb), wsb=wsb, C=C, gate=0)
+
+    def call(x):
+        return L.kda_chunk_bwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], x["dO"], x["dST"],
+                                      x["dq"], x["dk"], x["dv"], x["dg"], x["dbeta"], x["dS0"], x["cu"],
+                                      x["N"], x["T"], x["H"], dk, dv, _lib.BF16, x["ws"], x["wsb"], None,
+                                      x["C"], x["gate"])
+    cases = [(dict(N=-1), SHAPE), (dict(C=128), UNSUP), (dict(gate=5), UNSUP), (dict(cu=None), NULL),
+             (dict(dO=None), NULL), (dict(cu=a["cu"] + 2), MISAL), (dict(wsb=wsb - 1), WS),
+             (dict(ws=None), WS), (dict(dq=a["cu"]), ALIAS), (dict(dS0=a["cu"]), ALIAS),
+             (dict(ws=a["cu"] - 16), ALIAS), (dict(dS0=a["dST"]), ALIAS), (dict(dg=None), NULL)]
+    for change, code in cases:
+        b = dict(a)
+        b.update(change)
+        assert call(b) == code, (change, code)
+    # nothing to do: no sequences, or no heads
+    assert call(dict(a, N=0, T=0)) == OK
+    assert call(dict(a, H=0)) == OK
+    if not HAS_GPU:
+        assert call(a) == HIP
+        assert call(dict(a, g=None, dg=None, gate=2)) == HIP
+        assert call(dict(a, T=0)) == HIP          # the dS0 = dST copy still needs a device

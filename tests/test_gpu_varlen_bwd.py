@@ -1,0 +1,127 @@
+"""Backward pass over packed variable-length batches (kda_chunk_bwd_varlen) on
+the GPU.
+
+Each sequence's gradients must equal, bitwise, a fixed-length kda_chunk_bwd call
+on that sequence alone, and the oracle's fp64 adjoint of that sequence to the
+backward bar.  Lengths cover empty sequences, one token, chunk boundaries +- 1
+and several chunks."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_sequence_chunk_amd import chunk_bwd, chunk_bwd_varlen, inputs
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = {torch.float32: 1e-3, torch.bfloat16: 2e-2}
+NAMES = ("dq", "dk", "dv", "dbeta", "dg")
+
+
+def _say(m):
+    print(m, flush=True)
+
+
+def _packed(lengths, H, dk, dv, dtype, gates, s0_std, seed):
+    seqs = []
+    for i, L in enumerate(lengths):
+        d = inputs.custom_prefill(seed * 100 + i, 1, max(L, 1), H, dk, dv, dtype=dtype, gates=gates,
+                                  s0_std=s0_std)
+        seqs.append({k: (v[:, :L] if k != "S0" and v is not None else v) for k, v in d.items()})
+    cat = lambda key: torch.cat([s[key][0] for s in seqs], dim=0)      # [T, H, ...]
+    S0 = torch.cat([s["S0"] for s in seqs], dim=0) if s0_std else None
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+    return seqs, {k: cat(k) for k in ("q", "k", "v", "g", "beta")}, S0, cu
+
+
+def _run_and_check(lengths, H, dk, dv, C, dtype, layout="channel", s0_std=0.05, seed=1, with_dst=True,
+                   oracle_every=1):
+    gates = {"channel": "tiny", "head": "scalar", "none": "none"}[layout]
+    seqs, p, S0, cu = _packed(lengths, H, dk, dv, dtype, gates, s0_std, seed)
+    N, T = len(lengths), int(cu[-1])
+    rs = np.random.default_rng(seed + 1000)
+    dO = torch.tensor(rs.standard_normal((T, H, dv)), dtype=torch.float32)
+    dST = torch.tensor(rs.standard_normal((N, H, dk, dv)), dtype=torch.float32) if with_dst else None
+    dev = "cuda:0"
+    gsel = lambda g: None if layout == "none" else (g[..., 0].contiguous() if layout == "head" else g)
+    to = lambda x: None if x is None else x.to(dev)
+    got = chunk_bwd_varlen(to(p["q"]), to(p["k"]), to(p["v"]), to(gsel(p["g"])), to(p["beta"]), to(dO),
+                           to(cu), to(S0), to(dST), chunk_size=C, gate_layout=layout)
+    torch.cuda.synchronize()
+    got = {k: None if v is None else v.cpu() for k, v in got.items()}
+    offs = cu.tolist()
+    for i, (L, d) in enumerate(zip(lengths, seqs)):
+        a, b = offs[i], offs[i + 1]
+        s0 = None if S0 is None else S0[i:i + 1]
+        dst = None if dST is None else dST[i:i + 1]
+        if L:
+            own = chunk_bwd(to(d["q"]), to(d["k"]), to(d["v"]), to(gsel(d["g"])), to(d["beta"]),
+                            to(dO[a:b][None]), to(s0), to(dst), chunk_size=C, gate_layout=layout)
+            torch.cuda.synchronize()
+            for name in NAMES:
+                if got[name] is None:
+                    assert own[name] is None
+                    continue
+                assert torch.equal(got[name][a:b], own[name][0].cpu()), \
+                    f"sequence {i} (length {L}): {name} differs from its own call"
+            assert torch.equal(got["dS0"][i], own["dS0"][0].cpu()), f"sequence {i}: dS0 differs"
+        else:                                   # nothing happens in between: dS0 = dST
+            want = torch.zeros((H, dk, dv)) if dst is None else dst[0]
+            assert torch.equal(got["dS0"][i], want), f"empty sequence {i}: dS0 is not dST"
+        if L and i % oracle_every == 0:
+            g_ref = torch.zeros_like(d["g"]) if layout == "none" else d["g"]
+            ref = oracle.backward(d["q"], d["k"], d["v"], g_ref, d["beta"], s0, dO[a:b][None], dst)
+            tol = BWD_TOL[dtype]
+            errs = {}
+            for name in ("dq", "dk", "dv", "dbeta"):
+                errs[name] = assert_close(f"seq {i} {name}", got[name][a:b][None], ref[name], tol)
+            errs["dS0"] = assert_close(f"seq {i} dS0", got["dS0"][i:i + 1], ref["dS0"], tol)
+            if layout == "channel":
+                errs["dg"] = assert_close(f"seq {i} dg", got["dg"][a:b][None], ref["dg"], tol)
+            elif layout == "head":
+                errs["dg"] = assert_close(f"seq {i} dg", got["dg"][a:b][None], ref["dg"].sum(-1), tol)
+            _say(f"  seq {i} (L={L}): " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("dk,dv,C,dtype", [(128, 128, 64, torch.bfloat16), (64, 64, 32, torch.float32),
+                                           (128, 64, 16, torch.float32), (64, 128, 64, torch.bfloat16)])
+def test_backward_varlen_edge_lengths(dk, dv, C, dtype):
+    lengths = [0, 1, C - 1, C, C + 1, 2 * C + 5, 0, 9]
+    _say(f"backward varlen dk={dk} dv={dv} C={C} {dtype} lengths={lengths}")
+    _run_and_check(lengths, 2, dk, dv, C, dtype)
+
+
+@pytest.mark.parametrize("layout", ["head", "none"])
+def test_backward_varlen_gate_layouts(layout):
+    _say(f"backward varlen gates={layout}")
+    _run_and_check([5, 64, 0, 130, 1], 2, 128, 128, 64, torch.bfloat16, layout=layout, seed=2)
+
+
+def test_backward_varlen_no_states():
+    """No initial states and no dST (zeros), an empty sequence among them."""
+    _say("backward varlen without states")
+    _run_and_check([70, 0, 33], 3, 128, 128, 64, torch.bfloat16, s0_std=0.0, seed=3, with_dst=False)
+
+
+def test_backward_varlen_many_sequences():
+    """300 sequences of 0..150 tokens: many partial chunks, the unit grid sized
+    for the most chunks there can be."""
+    rs = np.random.default_rng(7)
+    lengths = [int(x) for x in rs.integers(0, 150, 300)]
+    _say(f"backward varlen many: {len(lengths)} sequences, {sum(lengths)} tokens")
+    _run_and_check(lengths, 2, 128, 128, 64, torch.bfloat16, s0_std=0.02, seed=4, oracle_every=37)
+
+
+def test_backward_varlen_all_empty():
+    """T = 0: every dS0 is its dST."""
+    _say("backward varlen all empty")
+    dev = "cuda:0"
+    q = torch.zeros((0, 2, 64), device=dev)
+    beta = torch.zeros((0, 2), device=dev)
+    dO = torch.zeros((0, 2, 64), device=dev)
+    cu = torch.zeros(4, dtype=torch.int32, device=dev)
+    dST = torch.randn((3, 2, 64, 64), generator=torch.Generator().manual_seed(2)).to(dev)
+    out = chunk_bwd_varlen(q, q, dO.clone(), q, beta, dO, cu, None, dST, chunk_size=32)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dS0"], dST)
