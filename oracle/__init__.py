@@ -21,10 +21,18 @@ Functions and the passages they follow (pages cited by title and section):
                     Uses direct pairwise decays exp(G_r - G_i), no factoring.
 ``recurrent_exact`` exact rational arithmetic (fractions) of the definition,
                     taking alpha directly, for tiny sizes.
+``backward``        C implementation: the fp64 adjoint of ``recurrent`` (reverse
+                    sweep over the tokens of the same per-token update), giving
+                    the gradients of sum(dO * o) + sum(dST * S_T) for training
+                    the chunkwise form (sections 十六 and 十七 of the explainer).
 ``l2_normalize``    the steps that produce q, k and g in the method's workloads
 ``gate_softplus``   (inputs of the path, not the path): each [d] row divided by
                     its Euclidean norm, and the log-gate -softplus(a) =
                     -log(1 + e^a); the oracle side of the fused pre-processing.
+``l2_normalize_vjp``  their vector-Jacobian products, written out from the
+``gate_softplus_vjp`` derivatives of those definitions: (I - y y^T)/|x| for
+                    y = x/|x|, and -sigmoid(a); the oracle side of the backward
+                    pass through the fused pre-processing.
 
 Parity pins: every function here is pinned by tests/test_oracle_pins.py to
 closed forms, special cases and library routines (least squares, finite
@@ -212,6 +220,26 @@ def gate_softplus(a):
     """The log-gate -softplus(a) = -log(1 + e^a), in fp64 (alpha = 1/(1 + e^a))."""
     a = to_f64(a)
     return -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a))))
+
+
+def l2_normalize_vjp(x, dy):
+    """Gradient with respect to x of sum(dy * l2_normalize(x)), in fp64.  With
+    y = x/|x| the Jacobian is (I - y y^T)/|x|, so dx = (dy - y (y . dy))/|x|.  A
+    zero row, where the normalisation is defined as zero, gets zero."""
+    x, dy = to_f64(x), to_f64(dy)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    y = np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+    inv = np.divide(1.0, n, out=np.zeros_like(n), where=n > 0)
+    return (dy - y * np.sum(y * dy, axis=-1, keepdims=True)) * inv
+
+
+def gate_softplus_vjp(a, dg):
+    """Gradient with respect to a of sum(dg * gate_softplus(a)), in fp64: the
+    derivative of -log(1 + e^a) is -1/(1 + e^-a) = -sigmoid(a)."""
+    a, dg = to_f64(a), to_f64(dg)
+    e = np.exp(-np.abs(a))
+    sig = np.where(a >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return -dg * sig
 
 
 def lib_path() -> str:
