@@ -266,24 +266,36 @@ def bench_varlen(torch, g, w, steps, warmup):
 
 def bench_backward(torch, g, w, steps=5, warmup=2):
     """kda_chunk_bwd on the same workload: gradients of sum(dO * o) for every
-    input (the forward stages are re-run inside the call)."""
+    input (the forward stages are re-run inside the call); and kda_chunk_bwd_pre,
+    the same through the fused pre-processing (raw q, k; bf16 gate
+    pre-activation a = log(e^{-g} - 1))."""
     from linear_attention_sequence_chunk_amd import chunk_bwd
     gen = torch.Generator(device=g["q"].device).manual_seed(0)
     dO = torch.randn(g["v"].shape, generator=gen, device=g["q"].device, dtype=torch.float32)
-    ws = None
-    for _ in range(warmup):
-        chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], dO, g["S0"], chunk_size=w.C, workspace=ws)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], dO, g["S0"], chunk_size=w.C, workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    return {"ms_per_call": round(ms, 3), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1), "calls": steps,
-            "note": "fp32 gradient arithmetic; includes re-running the forward stages"}
+    a = torch.log(torch.expm1(-g["g"])).to(torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], dO, g["S0"], chunk_size=w.C))
+    ms_pre = timed(lambda: chunk_bwd(g["q"], g["k"], g["v"], a, g["beta"], dO, g["S0"], chunk_size=w.C,
+                                     qk_l2norm=True, gate_act="softplus"))
+    del a, dO
+    tps = lambda t: round(w.B * w.T / (t / 1e3), 1)
+    return {"ms_per_call": round(ms, 3), "tokens_per_s": tps(ms), "calls": steps,
+            "note": "fp32 gradient arithmetic; includes re-running the forward stages",
+            "fused_pre": {"ms_per_call": round(ms_pre, 3), "tokens_per_s": tps(ms_pre),
+                          "note": "gradients of raw q, k and the bf16 gate pre-activation"}}
 
 
 def bench_decode(torch, inputs, decode_step, dev, steps):

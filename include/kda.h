@@ -334,8 +334,8 @@ int kda_decode_tokens(const void *q, const void *k, const void *v,
  *                          bf16 g must be 16-byte aligned, a per-head one 2-byte
  * The normalised q, k and the activated gate exist only inside the kernels; the
  * result equals the plain call on the pre-processed inputs up to rounding.
- * Unknown flag bits return KDA_ERR_UNSUPPORTED.  The backward pass
- * (kda_chunk_bwd) takes pre-processed inputs.
+ * Unknown flag bits return KDA_ERR_UNSUPPORTED.  kda_chunk_bwd takes
+ * pre-processed inputs; kda_chunk_bwd_pre differentiates through the flags.
  */
 typedef enum {
     KDA_PRE_NONE = 0,
@@ -377,6 +377,34 @@ int kda_decode_tokens_pre(const void *q, const void *k, const void *v,
                           int N, int T, int H, int dk, int dv,
                           int in_dtype, int out_dtype, void *stream,
                           int gate_layout, int pre_flags);
+
+/*
+ * kda_chunk_bwd_pre -- kda_chunk_bwd with pre-processing flags: the backward
+ * pass of kda_chunk_fwd_pre.  The gradients are those of the raw inputs: dq and
+ * dk of the rows before L2 normalisation (KDA_PRE_QK_L2NORM), dg of the gate
+ * tensor as given, i.e. of the pre-activation a under KDA_PRE_GATE_SOFTPLUS
+ * (dg is fp32 whatever the gate tensor's storage).  The pre-processed q, k and
+ * log-gate are formed in the workspace, the backward stages run on them, and
+ * the chain rule of the two steps is applied to the gradients in place:
+ *   y = x/|x|:         dx = (dy - y (y . dy)) / |x|    (a zero row gets zero)
+ *   g = -softplus(a):  da = -dg * sigmoid(a)
+ *   workspace  >= kda_chunk_bwd_pre_workspace_bytes(B, T, H, dk, dv, in_dtype, C,
+ *                                                   gate_layout, pre_flags)
+ * A gate tensor that the flags transform needs only its element's alignment.
+ * Arguments and errors as kda_chunk_bwd and kda_chunk_fwd_pre otherwise.
+ */
+int kda_chunk_bwd_pre(const void *q, const void *k, const void *v,
+                      const void *g, const float *beta, const float *initial_state,
+                      const float *dO, const float *dST,
+                      float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                      int B, int T, int H, int dk_size, int dv_size, int in_dtype,
+                      void *workspace, size_t workspace_bytes,
+                      void *stream, int C, int gate_layout, int pre_flags);
+
+/* Bytes of device workspace kda_chunk_bwd_pre needs (0 if unsupported); host-only. */
+size_t kda_chunk_bwd_pre_workspace_bytes(int B, int T, int H, int dk, int dv,
+                                         int in_dtype, int C, int gate_layout,
+                                         int pre_flags);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,8 @@ SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_byte
            "kda_chunk_fwd_varlen", "kda_chunk_varlen_workspace_bytes",
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
            "kda_chunk_fwd_pre", "kda_chunk_intra_pre", "kda_decode_tokens_pre",
-           "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_bytes")
+           "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_bytes",
+           "kda_chunk_bwd_pre", "kda_chunk_bwd_pre_workspace_bytes")
 
 
 class KdaError(RuntimeError):
@@ -76,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_bwd_varlen.restype = _ci
         L.kda_chunk_bwd_varlen_workspace_bytes.argtypes = [_ci] * 7
         L.kda_chunk_bwd_varlen_workspace_bytes.restype = _sz
+        L.kda_chunk_bwd_pre.argtypes = [_vp] * 14 + [_ci] * 6 + [_vp, _sz, _vp, _ci, _ci, _ci]
+        L.kda_chunk_bwd_pre.restype = _ci
+        L.kda_chunk_bwd_pre_workspace_bytes.argtypes = [_ci] * 9
+        L.kda_chunk_bwd_pre_workspace_bytes.restype = _sz
         _LIB = L
     return _LIB
 

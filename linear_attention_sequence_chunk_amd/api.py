@@ -174,20 +174,24 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, chunk_siz
 
 
 def chunk_bwd(q, k, v, g, beta, dO, initial_state=None, dST=None, chunk_size=64, gate_layout="channel",
-              workspace=None, stream=None):
+              workspace=None, stream=None, qk_l2norm=False, gate_act=None):
     """Backward pass (kda_chunk_bwd): gradients of L = sum(dO * o) + sum(dST * S_T)
     for the forward chunk_fwd(q, k, v, g, beta, initial_state, gate_layout=...).
     dO [B,T,H,dv] fp32, dST [B,H,dk,dv] fp32 or None.  Returns a dict of fp32
-    tensors dq, dk, dv, dg (None without gates), dbeta, dS0."""
+    tensors dq, dk, dv, dg (None without gates), dbeta, dS0.  With qk_l2norm or
+    gate_act="softplus" (or a bf16 g), the forward is the one with those
+    keywords (kda_chunk_bwd_pre) and dq, dk, dg are the gradients of the raw
+    q, k and gate tensor."""
     _gate(gate_layout)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU")
+    pre = _pre_flags(qk_l2norm, gate_act, g, gate_layout)
     _check_tensor("k", k, (B, T, H, dk), q.dtype, dev)
     _check_tensor("v", v, (B, T, H, dv), q.dtype, dev)
-    _check_gate(g, gate_layout, (B, T, H), dk, dev)
+    _check_gate(g, gate_layout, (B, T, H), dk, dev, allow_bf16=True)
     _check_tensor("beta", beta, (B, T, H), torch.float32, dev)
     _check_tensor("dO", dO, (B, T, H, dv), torch.float32, dev)
     if initial_state is not None:
@@ -201,16 +205,23 @@ def chunk_bwd(q, k, v, g, beta, dO, initial_state=None, dST=None, chunk_size=64,
            "dg": None if gate_layout == "none" else
            torch.empty((B, T, H, dk) if gate_layout == "channel" else (B, T, H), **f32)}
     L = _lib.lib()
-    nbytes = int(L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _code(q.dtype), chunk_size))
+    gl = _gate(gate_layout)
+    if pre:
+        nbytes = int(L.kda_chunk_bwd_pre_workspace_bytes(B, T, H, dk, dv, _code(q.dtype), chunk_size, gl, pre))
+    else:
+        nbytes = int(L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _code(q.dtype), chunk_size))
     if nbytes == 0 and B * T * H > 0:
         raise _lib.KdaError(3, "kda_chunk_bwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    st = L.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dO),
-                         _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
-                         _ptr(out["dbeta"]), _ptr(out["dS0"]), B, T, H, dk, dv, _code(q.dtype),
-                         _ptr(workspace), workspace.numel(), _stream(stream), chunk_size, _gate(gate_layout))
-    _lib.check(st, "kda_chunk_bwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dO), _ptr(dST),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+            _ptr(out["dS0"]), B, T, H, dk, dv, _code(q.dtype), _ptr(workspace), workspace.numel(),
+            _stream(stream), chunk_size, gl)
+    if pre:
+        _lib.check(L.kda_chunk_bwd_pre(*args, pre), "kda_chunk_bwd_pre")
+    else:
+        _lib.check(L.kda_chunk_bwd(*args), "kda_chunk_bwd")
     return out
 
 

@@ -13,7 +13,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk_intra.hip", "kda_chunk_chain_bf16.hip",
            "kda_chunk_chain_f32.hip", "kda_chunk_chain64.hip",
-           "kda_chunk_bwd.hip"]
+           "kda_chunk_bwd.hip", "kda_pre_bwd.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU forms are disabled for all device code.

@@ -193,8 +193,8 @@ int run_chunk(const ChunkCall& c, int stages) {
 }
 
 struct BwdCall {
-    const void *q, *k, *v;
-    const float *g, *beta, *s0, *dO, *dST;
+    const void *q, *k, *v, *g;
+    const float *beta, *s0, *dO, *dST;
     float *dq, *dk, *dv, *dg, *dbeta, *dS0;
     int B, T, H, dk_size, dv_size, in_dtype;
     void* ws;
@@ -204,14 +204,36 @@ struct BwdCall {
     const int* cu_seqlens = nullptr;   // packed variable-length batch (B = 1, N sequences)
     int N = 0;
     bool packed = false;
+    int pre = 0;                       // kda_pre_flags_t: raw q, k and gate tensor
 };
+
+// Room after the backward's workspace for the pre-processed inputs (pre != 0):
+// normalised q and k in the input dtype, their inverse row norms, the fp32 log-gate.
+struct PreLayout {
+    size_t qn, kn, inv, gact, total;
+};
+bool pre_gate_materialised(int gate, int pre) {
+    return gate != KDA_GATE_NONE && (pre & (KDA_PRE_GATE_SOFTPLUS | KDA_PRE_GATE_BF16));
+}
+PreLayout pre_layout(size_t base, size_t tok, int dk, int in_dtype, int gate, int pre) {
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const bool qk = pre & KDA_PRE_QK_L2NORM;
+    PreLayout P{};
+    size_t off = al(base);
+    P.qn = off;   off = al(off + (qk ? tok * dk * esize(in_dtype) : 0));
+    P.kn = off;   off = al(off + (qk ? tok * dk * esize(in_dtype) : 0));
+    P.inv = off;  off = al(off + (qk ? 2 * tok * 4 : 0));
+    P.gact = off; off = al(off + (pre_gate_materialised(gate, pre) ? tok * gate_bytes(gate, dk) : 0));
+    P.total = pre ? off : base;
+    return P;
+}
 
 // The backward pass: validation, the forward stages again (generic workspace
 // format, with checkpoints), then the backward stages.
 int run_bwd(BwdCall c) {
     const int dk = c.dk_size, dv = c.dv_size;
     if (c.B < 0 || c.T < 0 || c.H < 0 || c.N < 0) return KDA_ERR_SHAPE;
-    if (!dtype_ok(c.in_dtype) || !gate_ok(c.gate)) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(c.in_dtype) || !gate_ok(c.gate) || !pre_ok(c.pre)) return KDA_ERR_UNSUPPORTED;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
     const bool bf = c.in_dtype == KDA_BF16;
     if (!kda::bwd_supported(dk, dv, c.C, bf) || !kda::chunk_supported(dk, dv, c.C, bf)) return KDA_ERR_UNSUPPORTED;
@@ -229,19 +251,23 @@ int run_bwd(BwdCall c) {
     const void* p16[4] = {c.q, c.k, c.v, c.ws};
     for (const void* p : p16)
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
-    if (c.g && !aligned(c.g, c.gate == KDA_GATE_CHANNEL ? 8 : 4)) return KDA_ERR_MISALIGNED;
+    // a gate tensor read only by the elementwise pre-processing needs its element's alignment
+    const bool g_mat = pre_gate_materialised(c.gate, c.pre);
+    if (c.g && !aligned(c.g, g_mat ? ((c.pre & KDA_PRE_GATE_BF16) ? 2 : 4) : (c.gate == KDA_GATE_CHANNEL ? 8 : 4)))
+        return KDA_ERR_MISALIGNED;
     const void* p4[10] = {c.beta, c.s0, c.dO, c.dST, c.dq, c.dk, c.dv, c.dg, c.dbeta, c.dS0};
     for (const void* p : p4)
         if (p && !aligned(p, 4)) return KDA_ERR_MISALIGNED;
     const kda::BwdLayout L = c.packed ? kda::bwd_layout_packed(c.N, c.T, c.H, dk, dv, bf, c.C)
                                       : kda::bwd_layout(c.B, c.T, c.H, dk, dv, bf, c.C);
+    const PreLayout P = pre_layout(L.total, tok, dk, c.in_dtype, c.gate, c.pre);
     const bool uses_ws = tok > 0 && nseqh > 0;
-    if (uses_ws && (!c.ws || c.ws_bytes < L.total)) return KDA_ERR_WORKSPACE;
+    if (uses_ws && (!c.ws || c.ws_bytes < P.total)) return KDA_ERR_WORKSPACE;
     const size_t ei = esize(c.in_dtype), gb = gate_bytes(c.gate, dk);
     const Range rq = range_of(c.q, tok * dk * ei), rk = range_of(c.k, tok * dk * ei), rv = range_of(c.v, tok * dv * ei),
-                rg = range_of(c.g, tok * gb), rb = range_of(c.beta, tok * 4), rs0 = range_of(c.s0, nst * 4),
-                rdo = range_of(c.dO, tok * dv * 4), rdst = range_of(c.dST, nst * 4),
-                rw = range_of(c.ws, uses_ws ? L.total : 0),
+                rg = range_of(c.g, tok * gate_bytes(c.gate, dk, c.pre)), rb = range_of(c.beta, tok * 4),
+                rs0 = range_of(c.s0, nst * 4), rdo = range_of(c.dO, tok * dv * 4), rdst = range_of(c.dST, nst * 4),
+                rw = range_of(c.ws, uses_ws ? P.total : 0),
                 rcu = range_of(c.packed ? c.cu_seqlens : nullptr, ((size_t)c.N + 1) * 4);
     const Range outs[] = {range_of(c.dq, tok * dk * 4), range_of(c.dk, tok * dk * 4), range_of(c.dv, tok * dv * 4),
                           range_of(c.dg, tok * gb), range_of(c.dbeta, tok * 4), range_of(c.dS0, nst * 4)};
@@ -269,7 +295,20 @@ int run_bwd(BwdCall c) {
     }
     char* ws = (char*)c.ws;
     kda::ChunkArgs a;
-    a.q = c.q; a.k = c.k; a.v = c.v; a.g = c.g; a.beta = c.beta; a.s0 = c.s0; a.o = nullptr; a.sT = nullptr;
+    a.q = c.q; a.k = c.k; a.v = c.v; a.g = (const float*)c.g; a.beta = c.beta; a.s0 = c.s0;
+    a.o = nullptr; a.sT = nullptr;
+    // pre-processing: the stages below see the normalised q, k and the fp32 log-gate
+    kda::PreBwdArgs pb{};
+    if (c.pre) {
+        pb.q = c.q; pb.k = c.k; pb.g = c.g;
+        pb.qn = ws + P.qn; pb.kn = ws + P.kn; pb.inv = (float*)(ws + P.inv); pb.g_act = (float*)(ws + P.gact);
+        pb.dq = c.dq; pb.dk = c.dk; pb.dg = c.dg;
+        pb.rows = (long)tok; pb.dk_size = dk; pb.in_bf16 = bf; pb.gate = c.gate; pb.mode = pre_mode(c.pre);
+        pb.stream = (hipStream_t)c.stream;
+        if (kda::run_pre_bwd_inputs(pb) != hipSuccess) return KDA_ERR_HIP;
+        if (c.pre & KDA_PRE_QK_L2NORM) { a.q = pb.qn; a.k = pb.kn; }
+        if (g_mat) a.g = pb.g_act;
+    }
     a.B = c.packed ? 1 : c.B; a.T = c.T; a.H = c.H; a.dk = dk; a.dv = dv; a.C = c.C;
     a.in_bf16 = bf; a.out_bf16 = false; a.gate = c.gate;
     a.ws = ws; a.ws_bytes = L.fwd.total; a.stream = (hipStream_t)c.stream;
@@ -284,7 +323,9 @@ int run_bwd(BwdCall c) {
     bw.fwd = a; bw.dO = c.dO; bw.dST = c.dST;
     bw.dq = c.dq; bw.dk = c.dk; bw.dv = c.dv; bw.dg = c.dg; bw.dbeta = c.dbeta; bw.dS0 = c.dS0;
     bw.ck_dS = (float*)(ws + L.dS); bw.ck_dW = (float*)(ws + L.dW);
-    return finish(kda::run_chunk_bwd_stages(bw), (hipStream_t)c.stream);
+    if (kda::run_chunk_bwd_stages(bw) != hipSuccess) return KDA_ERR_HIP;
+    if (c.pre && kda::run_pre_bwd_grads(pb) != hipSuccess) return KDA_ERR_HIP;
+    return finish(hipSuccess, (hipStream_t)c.stream);
 }
 
 }  // namespace
@@ -347,6 +388,25 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
                   int in_dtype, void* workspace, size_t workspace_bytes, void* stream, int C, int gate_layout) {
     BwdCall c{q, k, v, g, beta, initial_state, dO, dST, dq, dk_out, dv_out, dg, dbeta, dS0,
               B, T, H, dk, dv, in_dtype, workspace, workspace_bytes, stream, C, gate_layout};
+    return run_bwd(c);
+}
+
+size_t kda_chunk_bwd_pre_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C, int gate_layout,
+                                         int pre_flags) {
+    if (!gate_ok(gate_layout) || !pre_ok(pre_flags)) return 0;
+    const size_t base = kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, in_dtype, C);
+    if (base == 0) return 0;
+    return pre_layout(base, (size_t)B * T * H, dk, in_dtype, gate_layout, pre_flags).total;
+}
+
+int kda_chunk_bwd_pre(const void* q, const void* k, const void* v, const void* g, const float* beta,
+                      const float* initial_state, const float* dO, const float* dST, float* dq, float* dk_out,
+                      float* dv_out, float* dg, float* dbeta, float* dS0, int B, int T, int H, int dk, int dv,
+                      int in_dtype, void* workspace, size_t workspace_bytes, void* stream, int C, int gate_layout,
+                      int pre_flags) {
+    BwdCall c{q, k, v, g, beta, initial_state, dO, dST, dq, dk_out, dv_out, dg, dbeta, dS0,
+              B, T, H, dk, dv, in_dtype, workspace, workspace_bytes, stream, C, gate_layout};
+    c.pre = pre_flags;
     return run_bwd(c);
 }
 

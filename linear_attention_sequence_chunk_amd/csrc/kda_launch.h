@@ -95,6 +95,25 @@ BwdLayout bwd_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, i
 bool bwd_supported(int dk, int dv, int C, bool in_bf16);
 hipError_t run_chunk_bwd_stages(const BwdArgs& b);
 
+// Backward pass through the fused pre-processing (kda_pre_bwd.hip).  mode: the
+// MODE_* bits of kda_common.h.  The inputs pass writes the pre-processed q, k
+// (input dtype) and log-gate (fp32) to the workspace; the grads pass turns the
+// gradients of those into gradients of the raw q, k and gate tensor, in place.
+struct PreBwdArgs {
+    const void *q, *k, *g;       // raw inputs, [rows][dk] (g by gate layout, fp32 or bf16 by mode)
+    void *qn, *kn;               // [rows][dk] input dtype (L2-normalised), or unused
+    float* g_act;                // [rows][dk] / [rows] fp32 log-gate, or unused
+    float* inv;                  // [2][rows]: 1/|q row|, 1/|k row| (0 for a zero row)
+    float *dq, *dk, *dg;         // gradients, updated in place
+    long rows;                   // token-heads
+    int dk_size;
+    bool in_bf16;
+    int gate, mode;
+    hipStream_t stream;
+};
+hipError_t run_pre_bwd_inputs(const PreBwdArgs& p);
+hipError_t run_pre_bwd_grads(const PreBwdArgs& p);
+
 hipError_t run_decode_step(const DecodeArgs& a);
 hipError_t run_chunk_intra(const ChunkArgs& a);
 hipError_t run_chunk_chain(const ChunkArgs& a);

@@ -377,3 +377,46 @@ def test_backward_varlen_validation_codes():
         assert call(a) == HIP
         assert call(dict(a, g=None, dg=None, gate=2)) == HIP
         assert call(dict(a, T=0)) == HIP          # the dS0 = dST copy still needs a device
+
+
+def test_backward_pre_validation_codes():
+    """kda_chunk_bwd_pre: flag bits, the larger workspace, the bf16 gate's size
+    and alignment, all decided on the host."""
+    L = _lib.lib()
+    f = Fake()
+    B, T, H, dk, dv, C = 2, 100, 3, 128, 64, 64
+    tok, nst = B * T * H, B * H * dk * dv
+    QK, SP, GB = _lib.PRE_QK_L2NORM, _lib.PRE_GATE_SOFTPLUS, _lib.PRE_GATE_BF16
+    plain = L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, C)
+    ws_of = lambda gate, pre: L.kda_chunk_bwd_pre_workspace_bytes(B, T, H, dk, dv, _lib.BF16, C, gate, pre)
+    assert ws_of(0, 0) == plain
+    assert ws_of(0, QK) >= plain + 2 * tok * dk * 2 + 2 * tok * 4        # normalised q, k and 1/|row|
+    assert ws_of(0, SP) >= plain + tok * dk * 4                          # the fp32 log-gate
+    assert ws_of(1, SP) < ws_of(0, SP)                                   # per-head gate: [tok] only
+    assert ws_of(2, SP | GB) == plain                                    # no gate: nothing to form
+    assert ws_of(0, 8) == 0 and ws_of(5, 0) == 0
+    wsb = ws_of(0, QK | SP | GB)
+    # g's fake extent has room for a dg right after a bf16 gate tensor
+    a = dict(q=f(tok * dk * 2), k=f(tok * dk * 2), v=f(tok * dv * 2), g=f(tok * dk * 6), beta=f(tok * 4),
+             s0=f(nst * 4), dO=f(tok * dv * 4), dST=f(nst * 4), dq=f(tok * dk * 4), dk=f(tok * dk * 4),
+             dv=f(tok * dv * 4), dg=f(tok * dk * 4), dbeta=f(tok * 4), dS0=f(nst * 4),
+             ws=f(wsb), wsb=wsb, gate=0, pre=QK | SP | GB)
+
+    def call(x):
+        return L.kda_chunk_bwd_pre(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], x["dO"], x["dST"],
+                                   x["dq"], x["dk"], x["dv"], x["dg"], x["dbeta"], x["dS0"], B, T, H, dk, dv,
+                                   _lib.BF16, x["ws"], x["wsb"], None, C, x["gate"], x["pre"])
+    cases = [(dict(pre=8), UNSUP), (dict(pre=QK | 16), UNSUP), (dict(wsb=plain), WS), (dict(wsb=wsb - 1), WS),
+             (dict(g=a["g"] + 1), MISAL), (dict(g=None), NULL),
+             (dict(dg=a["g"] + tok * dk * 2 - 4), ALIAS),       # the bf16 gate's last element
+             (dict(pre=QK, g=a["g"] + 4), MISAL),              # fp32 gate read by the stages: 8 bytes
+             (dict(pre=QK | SP, dg=a["g"] + tok * dk * 2), ALIAS)]   # an fp32 gate tensor is twice as long
+    for change, code in cases:
+        b = dict(a)
+        b.update(change)
+        assert call(b) == code, (change, code)
+    if not HAS_GPU:
+        assert call(a) == HIP
+        assert call(dict(a, g=a["g"] + 2)) == HIP               # element alignment is enough here
+        assert call(dict(a, dg=a["g"] + tok * dk * 2)) == HIP   # just past the bf16 gate: no overlap
+        assert call(dict(a, pre=SP, g=a["g"] + 4)) == HIP       # fp32 a, only read elementwise
