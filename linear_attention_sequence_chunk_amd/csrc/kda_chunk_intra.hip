@@ -284,14 +284,13 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
         const int bd = wave * 4 + (lane >> 4), j = lane & 15;
         if (bd < NB) {
             float* Mb = sA + (bd * 16) * LDA + bd * 16;
-            float x[16];
+            float x[16];                 // right-looking: 15 dependent steps
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == j) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) s -= Mb[r * LDA + i] * x[i];
-                x[r] = s;
-            }
+            for (int i = 0; i < 15; ++i)
+#pragma unroll
+                for (int r = i + 1; r < 16; ++r) x[r] -= Mb[r * LDA + i] * x[i];
 #pragma unroll
             for (int r = 0; r < 16; ++r) Mb[r * LDA + j] = x[r];
         }
@@ -436,6 +435,8 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
 //    (tot the block sum) are both <= 1; every other decay factor is e^{sum of
 //    block totals} <= 1, except e^{-L} which is only formed for blocks whose
 //    total stays above -SAFE_SPAN.
+//  - The sums are kept in base 2 (the log-gate scaled by log2 e as it enters the
+//    prefix sum), so that every decay factor is a single v_exp_f32.
 //  - The block index is uniform per wave; code that depends on it is
 //    instantiated per block so that nothing indexes registers at run time.
 //  - Two passes over halves of the key channels keep LDS under 80 KB so that
@@ -444,9 +445,17 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
 // Block pairs (R, I) and operands (Kr = k E, Kf = k F, Kd = k e^{-L}; b_J = e^{tot_J}):
 //   (1,0) (3,2): Kr_R . Kf_I      (2,1): Kr_2 . Kf_1      (2,0): Kr_2 . (b_1 Kf_0)
 //   (3,1): (b_2 Kr_3) . Kf_1      (3,0): (b_2 Kr_3) . (b_1 Kf_0)      (R,R): Kr_R . Kd_R
+constexpr float LOG2E = 1.44269504088896341f;
+constexpr float SAFE_SPAN2 = SAFE_SPAN * LOG2E;      // SAFE_SPAN in base-2 units
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 template <int CTRL>
 __device__ __forceinline__ float dpp_or_zero(float src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src), CTRL, 0xF, 0xF, true));
+}
+// lane N of each row of 16 lanes, to the whole row (DPP row_newbcast)
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
 }
 // inclusive prefix sum within each row of 16 lanes (fuses into v_add_f32_dpp)
 __device__ __forceinline__ float row_prefix_sum(float x) {
@@ -647,7 +656,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) Lg[p][m] = row_prefix_sum(clamp_g(m < 4 ? ga[p][m] : gb[p][m - 4]));
+        for (int m = 0; m < 8; ++m) Lg[p][m] = row_prefix_sum(clamp_g(m < 4 ? ga[p][m] : gb[p][m - 4]) * LOG2E);
         if (rr == 15) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) sTot[R * DK + chan(p) + m] = Lg[p][m];
@@ -674,47 +683,61 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             Vec8<float>::load(sTot + RB * DK + c, tR);
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                const float E = __expf(Lg[p][m]), F = __expf(tR[m] - Lg[p][m]);
+                const float E = exp2_fast(Lg[p][m]), F = exp2_fast(tR[m] - Lg[p][m]);
                 const float kk = (float)kv[p][m] * ikn, qq = (float)qv[p][m] * iqn;
                 kr[m] = kk * E; qr[m] = qq * E; kf[m] = kk * F;
             }
             Vec8<bf16>::store(blk(RB) + rr * LDH + cl, kr);
             Vec8<bf16>::store(blk(4 + RB) + rr * LDH + cl, qr);
             if constexpr (RB < 3) Vec8<bf16>::store(blk(8 + RB) + rr * LDH + cl, kf);
-#pragma unroll
-            for (int m = 0; m < 8; ++m)                                   // k e^{-L}, safe blocks only
-                o1[m] = tR[m] >= -SAFE_SPAN ? kf[m] * __expf(-tR[m]) : 0.f;
+            // Factors that depend on the channel only, shared by the block's 16 rows:
+            //   D = e^{-tot_RB} (0 where the block is unsafe),
+            //   X = e^{sum_{J<RB} tot_J}, or e^{tot_1} for RB = 0,
+            //   Y = e^{sum_{J>RB} tot_J}, or e^{tot_2} for RB = 3.
+            // Lane rr of each 16-lane row forms two of the row's 24 (channel rr % 8):
+            // fa holds D (lanes 0-7) or X (lanes 8-15), fb holds Y; DPP row
+            // broadcasts hand each lane the ones it needs where it needs them.
+            float fa, fb;
+            {
+                const int cm = c + (rr & 7);
+                const float t0 = sTot[cm], t1 = sTot[DK + cm], t2 = sTot[2 * DK + cm], t3 = sTot[3 * DK + cm];
+                const float tb = RB == 0 ? t0 : RB == 1 ? t1 : RB == 2 ? t2 : t3;
+                const float ax = RB == 0 ? t1 : RB == 1 ? t0 : RB == 2 ? t0 + t1 : t0 + t1 + t2;
+                const float ay = RB == 0 ? t1 + t2 + t3 : RB == 1 ? t2 + t3 : RB == 2 ? t3 : t2;
+                const float ad = tb >= -SAFE_SPAN2 ? -tb : -INFINITY;
+                fa = exp2_fast(rr < 8 ? ad : ax);
+                fb = exp2_fast(ay);
+            }
+            static_for<8>([&](auto MI) {                                 // k e^{-L}, safe blocks only
+                constexpr int M = MI;
+                o1[M] = kf[M] * row_bcast<M>(fa);
+            });
             Vec8<bf16>::store(blk(11 + RB) + rr * LDH + cl, o1);
             if constexpr (RB == 3) {
-                Vec8<float>::load(sTot + 2 * DK + c, o2);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) { const float f = __expf(o2[m]); o1[m] = kr[m] * f; o2[m] = qr[m] * f; }
+                static_for<8>([&](auto MI) {
+                    constexpr int M = MI;
+                    const float y = row_bcast<M>(fb);
+                    o1[M] = kr[M] * y;
+                    o2[M] = qr[M] * y;
+                });
                 Vec8<bf16>::store(blk(15) + rr * LDH + cl, o1);
                 Vec8<bf16>::store(blk(16) + rr * LDH + cl, o2);
             }
             if constexpr (RB == 0) {
-                Vec8<float>::load(sTot + 1 * DK + c, o2);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) o1[m] = kf[m] * __expf(o2[m]);
+                static_for<8>([&](auto MI) {
+                    constexpr int M = MI;
+                    o1[M] = kf[M] * row_bcast<8 + M>(fa);
+                });
                 Vec8<bf16>::store(blk(17) + rr * LDH + cl, o1);
             }
             // e^G = E e^{sum_{J<R} tot_J};  e^{G_last - G} = F e^{sum_{J>R} tot_J}
-#pragma unroll
-            for (int m = 0; m < 8; ++m) { o1[m] = 0.f; o2[m] = 0.f; }
-#pragma unroll
-            for (int J = 0; J < NB; ++J) {
-                if (J == RB) continue;
-                Vec8<float>::load(sTot + J * DK + c, tR);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) { if (J < RB) o1[m] += tR[m]; else o2[m] += tR[m]; }
-            }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const float eb = RB > 0 ? __expf(o1[m]) : 1.f, er = RB < 3 ? __expf(o2[m]) : 1.f;
-                o1[m] = qr[m] * eb;
-                kr[m] *= eb;
-                kf[m] *= er;
-            }
+            static_for<8>([&](auto MI) {
+                constexpr int M = MI;
+                const float eb = RB > 0 ? row_bcast<8 + M>(fa) : 1.f, er = RB < 3 ? row_bcast<M>(fb) : 1.f;
+                o1[M] = qr[M] * eb;
+                kr[M] *= eb;
+                kf[M] *= er;
+            });
             store_column8(sKtT, LDT, c, t, pack_bf16x8(kr), 2 * (lane >> 4));
             store_column8(sKbT, Cfg::LDP, c, t, pack_bf16x8(kf), 2 * (lane >> 4));
             // fragment order: unit (row tile R, k-step c/32), lane = row%16 + 16 * ((c%32)/8)
@@ -724,7 +747,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             float lg = 0.f;
 #pragma unroll
             for (int J = 0; J < NB; ++J) lg += sTot[J * DK + tid];
-            ws_gam[ch * DK + tid] = __expf(lg);
+            ws_gam[ch * DK + tid] = exp2_fast(lg);
         }
         __syncthreads();
 
@@ -753,7 +776,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             const int dR = wave == 0 ? 0 : wave == 1 ? 1 : wave == 3 ? 2 : 3;
             bool uns = false;
             if (dslot >= 0) {
-                uns = sTot[dR * DK + lane] < -SAFE_SPAN || sTot[dR * DK + 64 + lane] < -SAFE_SPAN;
+                uns = sTot[dR * DK + lane] < -SAFE_SPAN2 || sTot[dR * DK + 64 + lane] < -SAFE_SPAN2;
                 uns = __any(uns);
             }
             const int r = lane & 15, kg = lane >> 4;
@@ -848,16 +871,18 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 
     // ---------------------------------------------------------------- a4: T = (I + M)^-1
     if (wave == 0) {
+        // column j of one diagonal block's inverse by forward substitution, in the
+        // right-looking order: once x_i is final it updates every later row, so
+        // the updates of one step are independent (15 dependent steps, not 120)
         const int bd = lane >> 4, j = lane & 15;
         float* Mb = sA + (bd * 16) * LDA + bd * 16;
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = (r == j) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < r; ++i) s -= Mb[r * LDA + i] * x[i];
-            x[r] = s;
-        }
+        for (int i = 0; i < 15; ++i)
+#pragma unroll
+            for (int r = i + 1; r < 16; ++r) x[r] -= Mb[r * LDA + i] * x[i];
 #pragma unroll
         for (int r = 0; r < 16; ++r) Mb[r * LDA + j] = x[r];
     }
