@@ -81,13 +81,15 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O) + R * 16 * DVS;
 
     // ---- operand registers, D chunks in flight
-    // Every wave issues the same loads in every chunk (W waves load P and O waves
-    // load U too, unused; past the last chunk the last one is loaded again), so
-    // that the number of loads in flight is the same on every path and each
-    // chunk waits only for its own operands, D - 1 chunks of loads staying in flight.
+    // Every wave issues the same load instructions in every chunk (past the last
+    // chunk the last one is loaded again), so that the number of loads in flight is
+    // the same on every path and each chunk waits only for its own operands, D - 1
+    // chunks of loads staying in flight.  The loads a role does not need (U for the
+    // O waves, P for the W waves) repeat an address the wave has just requested, so
+    // they cost no L1 miss.
     u32x4 fA[D][4];      // Wk (W waves) or Qt (O waves), row tile R, 4 k-steps
-    u32x2 fU[D][NJ];     // U tiles of this slice (W waves)
-    u32x4 fX[D][2];      // P k-steps (O waves; k-step 1 of row tiles 0, 1 is not used)
+    u32x2 fU[D][NJ];     // U tiles of this slice (W waves; a repeat of fA on O waves)
+    u32x4 fX[D][2];      // P k-steps (O waves, k-step 1 of row tiles 0, 1 not used; a repeat of fK on W waves)
     u32x4 fK[D][2];      // Kb^T channel tile ct, 2 k-steps
     u32x4 fG[D];         // gam of this lane's 4 state rows
     // first half: what phase 1 consumes; second half: what phase 2 consumes
@@ -97,19 +99,20 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         const u32x4* a_ = reinterpret_cast<const u32x4*>((wW ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
                           + R * 4 * 64 + lane;                                                      \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
-        const u32x2* u_ = reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))               \
-                          + (R * (DV / 16) + sl * NJ) * 64 + lane;                                  \
-        _Pragma("unroll") for (int j = 0; j < NJ; ++j) fU[SL][j] = u_[j * 64];                     \
+        const u32x2* u_ = wW ? reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))          \
+                                   + (R * (DV / 16) + sl * NJ) * 64 + lane                          \
+                             : reinterpret_cast<const u32x2*>(a_);                                  \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) fU[SL][j] = u_[wW ? j * 64 : 0];             \
     }
 #define KDA_C64_PREFETCH_2(SL, CH)                                                                  \
     {                                                                                               \
         const long ch_ = (CH);                                                                      \
-        {                                                                                           \
-            const u32x4* p_ = reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
-            fX[SL][0] = p_[0];                                                                      \
-            fX[SL][1] = p_[64];                                                                     \
-        }                                                                                           \
         const u32x4* k_ = reinterpret_cast<const u32x4*>(ws_kb + ch_ * (long)(DK * C)) + ct * 2 * 64 + lane; \
+        {                                                                                           \
+            const u32x4* p_ = wW ? k_ : reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
+            fX[SL][0] = p_[0];                                                                      \
+            fX[SL][1] = p_[wW ? 0 : 64];                                                            \
+        }                                                                                           \
         fK[SL][0] = k_[0];                                                                          \
         fK[SL][1] = k_[64];                                                                         \
         fG[SL] = *reinterpret_cast<const u32x4*>(ws_gam + ch_ * (long)DK + ct * 16 + 4 * (lane >> 4)); \
