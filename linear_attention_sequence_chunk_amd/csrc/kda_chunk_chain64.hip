@@ -111,7 +111,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         {                                                                                           \
             const u32x4* p_ = wW ? k_ : reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
             fX[SL][0] = p_[0];                                                                      \
-            fX[SL][1] = p_[wW ? 0 : 64];                                                            \
+            fX[SL][1] = p_[wave >= 6 ? 64 : 0];     /* O waves of row tiles 2, 3 only */          \
         }                                                                                           \
         fK[SL][0] = k_[0];                                                                          \
         fK[SL][1] = k_[64];                                                                         \
