@@ -301,6 +301,286 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_chain_kernel(
     }
 }
 
+// ================================================================ reverse chain, bf16 inputs
+// The same recurrence for bf16 inputs, on bf16 MFMA (16x16x32).  The chunk operands
+// Kb^T, P, Wk and Qt are bf16 in the workspace, so exact as MFMA operands; the fp32
+// ones (dS', dO, dW) are split into bf16 hi + lo parts (hi = bf16(x), lo =
+// bf16(x - hi), about 16 significant bits) and each product takes two MFMAs.
+// Every product here contracts over the index that is not the contiguous one of
+// the forward's layout, so those operands are read with the LDS transpose read
+// (ds_read_b64_tr_b16) and every array is staged as it lies in memory.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+// One operand fragment of v_mfma_f32_16x16x32_bf16 (8 consecutive k of row or
+// column mn0 + l%16 in lane l, k = k0 + 8(l/16) + 0..7) from X[k][mn] stored
+// row-major with mn contiguous.  Within each group of 16 lanes the transpose read
+// hands lane d, element e the element d%4 of lane 4e + d/4, so lane s points at
+// X[k0 + 8g + s/4][mn0 + 4(s%4)] (and four rows further for elements 4..7).
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int k0, int mn0, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const bf16* p0 = X + (k0 + 8 * g + (s >> 2)) * ld + mn0 + 4 * (s & 3);
+    const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)const_cast<bf16*>(p0));
+    const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)const_cast<bf16*>(p0 + 4 * ld));
+    const short8v c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, c);
+}
+// The same fragment from Z[mn][k] stored row-major with k contiguous: one 16-byte read.
+__device__ __forceinline__ bf16x8 frag_n(const bf16* Z, int ld, int k0, int mn0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(Z + (mn0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+__device__ __forceinline__ floatx4 mfma32(floatx4 acc, bf16x8 a, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split4(floatx4 x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hi[e] = (bf16)x[e];
+        lo[e] = (bf16)(x[e] - (float)hi[e]);
+    }
+}
+
+template <int DK, int DV, int C>
+struct BwdChainHCfg {
+    static constexpr int DVS = 32, NSL = DV / DVS, NB = C / 16, KPW = DK / 64;
+    // row lengths in bf16: the four rows one transpose read touches fall into
+    // separate bank windows; the 16-byte reads stay aligned
+    static constexpr int LKB = C + 8;                 // Kb^T [DK][C]
+    static constexpr int LP = C + 8;                  // P    [C][C]
+    static constexpr int LW = DK + 16;                // Wk (negated), Qt  [C][DK]
+    static constexpr int LO = DVS + 16;               // dO hi, lo         [C][DVS]
+    static constexpr int LS = DK + 8;                 // dS'^T hi, lo      [DVS][DK]
+    static constexpr int LD = C + 8;                  // dW^T hi, lo       [DVS][C]
+    static constexpr size_t O_KB = 0;
+    static constexpr size_t O_P = O_KB + size_t(DK) * LKB * 2;
+    static constexpr size_t O_WK = O_P + size_t(C) * LP * 2;
+    static constexpr size_t O_QT = O_WK + size_t(C) * LW * 2;
+    static constexpr size_t O_OH = O_QT + size_t(C) * LW * 2;
+    static constexpr size_t O_OL = O_OH + size_t(C) * LO * 2;
+    static constexpr size_t O_SH = O_OL + size_t(C) * LO * 2;
+    static constexpr size_t O_SL = O_SH + size_t(DVS) * LS * 2;
+    static constexpr size_t O_WH = O_SL + size_t(DVS) * LS * 2;
+    static constexpr size_t O_WL = O_WH + size_t(DVS) * LD * 2;
+    static constexpr size_t O_G = O_WL + size_t(DVS) * LD * 2;
+    static constexpr size_t BYTES = O_G + size_t(DK) * 4;
+    static constexpr int U_KB = DK * C / 8, U_P = C * C / 8, U_DO = C * DVS / 4;   // 16-byte units
+    static constexpr int PKB = (U_KB + 255) / 256, PP = (U_P + 255) / 256, PDO = (U_DO + 255) / 256;
+    static constexpr bool FITS = (C == 32 || C == 64) && BYTES <= LDS_LIMIT && DK % 64 == 0 && DV % DVS == 0;
+};
+
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(256, 1) void chunk_bwd_chain_h_kernel(
+    const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
+    const bf16* __restrict__ ws_p, const float* __restrict__ ws_gam, const float* __restrict__ dO,
+    const float* __restrict__ dST, float* __restrict__ dS0, float* __restrict__ ck_dS,
+    float* __restrict__ ck_dW, UnitMap um) {
+    typedef BwdChainHCfg<DK, DV, C> Cfg;
+    constexpr int DVS = Cfg::DVS, NSL = Cfg::NSL, NB = Cfg::NB, KPW = Cfg::KPW;
+    constexpr int LKB = Cfg::LKB, LP = Cfg::LP, LW = Cfg::LW, LO = Cfg::LO, LS = Cfg::LS, LD = Cfg::LD;
+    constexpr int PKB = Cfg::PKB, PP = Cfg::PP, PDO = Cfg::PDO;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
+    bf16* sKb = reinterpret_cast<bf16*>(smem + Cfg::O_KB);
+    bf16* sP = reinterpret_cast<bf16*>(smem + Cfg::O_P);
+    bf16* sWk = reinterpret_cast<bf16*>(smem + Cfg::O_WK);
+    bf16* sQt = reinterpret_cast<bf16*>(smem + Cfg::O_QT);
+    bf16* sOh = reinterpret_cast<bf16*>(smem + Cfg::O_OH);
+    bf16* sOl = reinterpret_cast<bf16*>(smem + Cfg::O_OL);
+    bf16* sSh = reinterpret_cast<bf16*>(smem + Cfg::O_SH);
+    bf16* sSl = reinterpret_cast<bf16*>(smem + Cfg::O_SL);
+    bf16* sWh = reinterpret_cast<bf16*>(smem + Cfg::O_WH);
+    bf16* sWl = reinterpret_cast<bf16*>(smem + Cfg::O_WL);
+    float* sGam = reinterpret_cast<float*>(smem + Cfg::O_G);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, kg = lane >> 4;
+    // the slices of one head share an XCD (workgroups are dealt to the 8 XCDs
+    // round-robin), so the chunk operands they all read come from one L2
+    long bh;
+    int sl;
+    {
+        const long nwg = (long)gridDim.x, id = blockIdx.x;
+        if (nwg % 8 == 0) {
+            const long o = (id % 8) * (nwg / 8) + id / 8;
+            bh = o / NSL;
+            sl = (int)(o % NSL);
+        } else {
+            bh = id / NSL;
+            sl = (int)(id % NSL);
+        }
+    }
+    const int j0 = sl * DVS;
+    const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
+    const SeqRange sr = seq_range(um, sq);
+    const int NC = sr.nchunks;
+
+    // dS slice in accumulators: rows 16(wave + 4p) + 4(l/16) + e, columns 16J + l%16
+    floatx4 ds[KPW][2];
+#pragma unroll
+    for (int p = 0; p < KPW; ++p)
+#pragma unroll
+        for (int J = 0; J < 2; ++J)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * (wave + 4 * p) + 4 * kg + e;
+                ds[p][J][e] = dST ? dST[(bh * DK + c) * (long)DV + j0 + 16 * J + lr] : 0.f;
+            }
+
+    // the next chunk's operands, in registers while a chunk computes
+    u32x4 rKb[PKB], rWk[PKB], rQt[PKB], rP[PP];
+    floatx4 rdO[PDO];
+    float rG = 0.f;
+#define KDA_BWDH_FETCH(N)                                                                         \
+    {                                                                                             \
+        const long un = unit_id(um, sq, h, (N), sr.chunk0);                                      \
+        const u32x4* gkb = reinterpret_cast<const u32x4*>(ws_kb + un * (long)DK * C);             \
+        const u32x4* gwk = reinterpret_cast<const u32x4*>(ws_wk + un * (long)C * DK);             \
+        const u32x4* gqt = reinterpret_cast<const u32x4*>(ws_qt + un * (long)C * DK);             \
+        const u32x4* gp = reinterpret_cast<const u32x4*>(ws_p + un * (long)C * C);                \
+        _Pragma("unroll") for (int x = 0; x < PKB; ++x) {                                         \
+            const int u = tid + 256 * x;                                                          \
+            if (Cfg::U_KB % 256 == 0 || u < Cfg::U_KB) {                                          \
+                rKb[x] = gkb[u];                                                                  \
+                rWk[x] = gwk[u];                                                                  \
+                rQt[x] = gqt[u];                                                                  \
+            }                                                                                     \
+        }                                                                                         \
+        _Pragma("unroll") for (int x = 0; x < PP; ++x) {                                          \
+            const int u = tid + 256 * x;                                                          \
+            if (Cfg::U_P % 256 == 0 || u < Cfg::U_P) rP[x] = gp[u];                               \
+        }                                                                                         \
+        const long t0 = sr.tok_begin + (long)(N) * C;                                             \
+        _Pragma("unroll") for (int x = 0; x < PDO; ++x) {                                         \
+            const int u = tid + 256 * x, r = u / (DVS / 4), q4 = u % (DVS / 4);                   \
+            const long tr = t0 + r < sr.tok_end ? t0 + r : t0;                                    \
+            if (Cfg::U_DO % 256 == 0 || u < Cfg::U_DO)                                            \
+                rdO[x] = *reinterpret_cast<const floatx4*>(dO + (tr * H + h) * DV + j0 + 4 * q4); \
+        }                                                                                         \
+        if (tid < DK) rG = ws_gam[un * DK + tid];                                                 \
+    }
+    // to LDS as they lie in memory (Wk negated; dO split, rows past the end zero)
+#define KDA_BWDH_STORE(N)                                                                         \
+    {                                                                                             \
+        _Pragma("unroll") for (int x = 0; x < PKB; ++x) {                                         \
+            const int u = tid + 256 * x;                                                          \
+            if (Cfg::U_KB % 256 == 0 || u < Cfg::U_KB) {                                          \
+                const int e0 = 8 * u;                                                             \
+                *reinterpret_cast<u32x4*>(sKb + (e0 / C) * LKB + e0 % C) = rKb[x];                \
+                const u32x4 nw = {rWk[x][0] ^ 0x80008000u, rWk[x][1] ^ 0x80008000u,               \
+                                  rWk[x][2] ^ 0x80008000u, rWk[x][3] ^ 0x80008000u};              \
+                *reinterpret_cast<u32x4*>(sWk + (e0 / DK) * LW + e0 % DK) = nw;                   \
+                *reinterpret_cast<u32x4*>(sQt + (e0 / DK) * LW + e0 % DK) = rQt[x];               \
+            }                                                                                     \
+        }                                                                                         \
+        _Pragma("unroll") for (int x = 0; x < PP; ++x) {                                          \
+            const int u = tid + 256 * x;                                                          \
+            if (Cfg::U_P % 256 == 0 || u < Cfg::U_P) {                                            \
+                const int e0 = 8 * u;                                                             \
+                *reinterpret_cast<u32x4*>(sP + (e0 / C) * LP + e0 % C) = rP[x];                   \
+            }                                                                                     \
+        }                                                                                         \
+        const long t0 = sr.tok_begin + (long)(N) * C;                                             \
+        _Pragma("unroll") for (int x = 0; x < PDO; ++x) {                                         \
+            const int u = tid + 256 * x, r = u / (DVS / 4), q4 = u % (DVS / 4);                   \
+            if (Cfg::U_DO % 256 == 0 || u < Cfg::U_DO) {                                          \
+                const floatx4 o4 = t0 + r < sr.tok_end ? rdO[x] : zero4();                        \
+                bf16x4 hi, lo;                                                                    \
+                split4(o4, hi, lo);                                                               \
+                *reinterpret_cast<bf16x4*>(sOh + r * LO + 4 * q4) = hi;                           \
+                *reinterpret_cast<bf16x4*>(sOl + r * LO + 4 * q4) = lo;                           \
+            }                                                                                     \
+        }                                                                                         \
+        if (tid < DK) sGam[tid] = rG;                                                             \
+    }
+
+    if (NC > 0) KDA_BWDH_FETCH(NC - 1);
+    for (int n = NC - 1; n >= 0; --n) {
+        const long unit = unit_id(um, sq, h, n, sr.chunk0);
+        __syncthreads();                                    // the later chunk's readers are done
+        KDA_BWDH_STORE(n);
+        // dS', the cotangent of this chunk's end state: split to LDS (transposed
+        // rows, four channels a lane) and to its checkpoint
+        float* cds = ck_dS + unit * (long)DK * DV;
+#pragma unroll
+        for (int p = 0; p < KPW; ++p)
+#pragma unroll
+            for (int J = 0; J < 2; ++J) {
+                const int c0 = 16 * (wave + 4 * p) + 4 * kg, j = 16 * J + lr;
+                bf16x4 hi, lo;
+                split4(ds[p][J], hi, lo);
+                *reinterpret_cast<bf16x4*>(sSh + j * LS + c0) = hi;
+                *reinterpret_cast<bf16x4*>(sSl + j * LS + c0) = lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cds[(c0 + e) * (long)DV + j0 + j] = ds[p][J][e];
+            }
+        if (n > 0) KDA_BWDH_FETCH(n - 1);
+        __syncthreads();
+
+        // dW = Kb dS' + P^T dO: output tiles (R, J), wave w taking w, w + 4, ...
+        float* cdw = ck_dW + unit * (long)C * DV;
+#pragma unroll
+        for (int t = wave; t < 2 * NB; t += 4) {
+            const int R = t >> 1, J = t & 1;
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int c0 = 0; c0 < DK; c0 += 32) {
+                const bf16x8 a = frag_tr(sKb, LKB, c0, 16 * R, lane);          // Kb[r][c] = Kb^T[c][r]
+                acc = mfma32(acc, a, frag_n(sSh, LS, c0, 16 * J, lane));
+                acc = mfma32(acc, a, frag_n(sSl, LS, c0, 16 * J, lane));
+            }
+#pragma unroll
+            for (int i0 = 0; i0 < C; i0 += 32) {
+                if (i0 + 32 <= 16 * R) continue;                                // P[i][r] = 0 for i < r
+                const bf16x8 a = frag_tr(sP, LP, i0, 16 * R, lane);            // P^T[r][i] = P[i][r]
+                acc = mfma32(acc, a, frag_tr(sOh, LO, i0, 16 * J, lane));
+                acc = mfma32(acc, a, frag_tr(sOl, LO, i0, 16 * J, lane));
+            }
+            bf16x4 hi, lo;
+            split4(acc, hi, lo);
+            *reinterpret_cast<bf16x4*>(sWh + (16 * J + lr) * LD + 16 * R + 4 * kg) = hi;
+            *reinterpret_cast<bf16x4*>(sWl + (16 * J + lr) * LD + 16 * R + 4 * kg) = lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cdw[(16 * R + 4 * kg + e) * (long)DV + j0 + 16 * J + lr] = acc[e];
+        }
+        __syncthreads();
+
+        // dS = Diag(gam) dS' - Wk^T dW + Qt^T dO  (sWk holds -Wk)
+#pragma unroll
+        for (int p = 0; p < KPW; ++p) {
+            const int cb = 16 * (wave + 4 * p);
+#pragma unroll
+            for (int J = 0; J < 2; ++J) {
+                floatx4 acc = ds[p][J];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= sGam[cb + 4 * kg + e];
+#pragma unroll
+                for (int r0 = 0; r0 < C; r0 += 32) {
+                    const bf16x8 aq = frag_tr(sQt, LW, r0, cb, lane);            // Qt^T[c][r]
+                    acc = mfma32(acc, aq, frag_tr(sOh, LO, r0, 16 * J, lane));
+                    acc = mfma32(acc, aq, frag_tr(sOl, LO, r0, 16 * J, lane));
+                    const bf16x8 aw = frag_tr(sWk, LW, r0, cb, lane);            // -Wk^T[c][r]
+                    acc = mfma32(acc, aw, frag_n(sWh, LD, r0, 16 * J, lane));
+                    acc = mfma32(acc, aw, frag_n(sWl, LD, r0, 16 * J, lane));
+                }
+                ds[p][J] = acc;
+            }
+        }
+    }
+#undef KDA_BWDH_FETCH
+#undef KDA_BWDH_STORE
+    if (dS0) {
+#pragma unroll
+        for (int p = 0; p < KPW; ++p)
+#pragma unroll
+            for (int J = 0; J < 2; ++J)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * (wave + 4 * p) + 4 * kg + e;
+                    dS0[(bh * DK + c) * (long)DV + j0 + 16 * J + lr] = ds[p][J][e];
+                }
+    }
+}
+
 // ================================================================ per-chunk gradients
 // One workgroup of 256 threads (4 waves) per chunk unit; every contraction runs
 // on fp32 MFMA.  Wave w owns the channel blocks w, w + 4, ... from start to end:
@@ -929,10 +1209,18 @@ static hipError_t launch_bwd(const BwdArgs& b) {
         const long units = unit_count(a);
         const long nsh = seq_head_count(a);
         if (nsh == 0) return hipSuccess;
-        hipLaunchKernelGGL((chunk_bwd_chain_kernel<T, DK, DV, C>), dim3((unsigned)(nsh * CC::NSL)), dim3(256), 0,
-                           a.stream, (const T*)(ws + w.qt), (const T*)(ws + w.wk), (const T*)(ws + w.kb),
-                           (const T*)(ws + w.p), (const float*)(ws + w.gam), b.dO, b.dST, b.dS0, b.ck_dS,
-                           b.ck_dW, unit_map(a));
+        typedef BwdChainHCfg<DK, DV, C> HC;
+        if constexpr (sizeof(T) == 2 && HC::FITS) {
+            hipLaunchKernelGGL((chunk_bwd_chain_h_kernel<DK, DV, C>), dim3((unsigned)(nsh * HC::NSL)), dim3(256), 0,
+                               a.stream, (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk),
+                               (const bf16*)(ws + w.kb), (const bf16*)(ws + w.p), (const float*)(ws + w.gam), b.dO,
+                               b.dST, b.dS0, b.ck_dS, b.ck_dW, unit_map(a));
+        } else {
+            hipLaunchKernelGGL((chunk_bwd_chain_kernel<T, DK, DV, C>), dim3((unsigned)(nsh * CC::NSL)), dim3(256), 0,
+                               a.stream, (const T*)(ws + w.qt), (const T*)(ws + w.wk), (const T*)(ws + w.kb),
+                               (const T*)(ws + w.p), (const float*)(ws + w.gam), b.dO, b.dST, b.dS0, b.ck_dS,
+                               b.ck_dW, unit_map(a));
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || units == 0) return e;
         hipLaunchKernelGGL((chunk_bwd_intra_kernel<T, DK, DV, C>), dim3((unsigned)units), dim3(256), 0, a.stream,
