@@ -519,12 +519,16 @@ struct Intra64Cfg {
     static_assert(NITV >= 1 && (C * DV / 8) % NT == 0 && (DV / 8) % 4 == 0, "v unit mapping");
 };
 
-template <int DV>
+// GEN: the backward pass's forward stage.  The same results stored in the generic
+// workspace format (row-major, U in fp32) that the generic chain and the backward
+// kernels read, plus the fp32 checkpoints T and A per unit.
+template <int DV, bool GEN>
 __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     bf16* __restrict__ ws_qt, bf16* __restrict__ ws_wk, bf16* __restrict__ ws_kb, bf16* __restrict__ ws_p,
-    bf16* __restrict__ ws_u, float* __restrict__ ws_gam, UnitMap um, int gate) {
+    void* __restrict__ ws_u, float* __restrict__ ws_gam, UnitMap um, int gate,
+    float* __restrict__ ck_t, float* __restrict__ ck_a) {
     typedef Intra64Cfg<DV> Cfg;
     constexpr int C = 64, NB = 4, DK = 128, NT = 512, NW = 8, HALF = 64;
     constexpr int LDH = Cfg::LDH, LDT = Cfg::LDT, LDA = Cfg::LDA;
@@ -741,7 +745,8 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             store_column8(sKtT, LDT, c, t, pack_bf16x8(kr), 2 * (lane >> 4));
             store_column8(sKbT, Cfg::LDP, c, t, pack_bf16x8(kf), 2 * (lane >> 4));
             // fragment order: unit (row tile R, k-step c/32), lane = row%16 + 16 * ((c%32)/8)
-            Vec8<bf16>::store(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
+            if constexpr (GEN) Vec8<bf16>::store(gQt + t * DK + c, o1);
+            else Vec8<bf16>::store(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
         });
         if (p == 0 && tid < DK) {
             float lg = 0.f;
@@ -753,9 +758,14 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 
         if (p == 1) {                                  // Kb^T complete: to the workspace in fragment order
             for (int u = tid; u < DK * C / 8; u += NT) {
-                const int ctile = u >> 7, ks = (u >> 6) & 1, lf = u & 63;
-                reinterpret_cast<u32x4*>(gKb)[u] = *reinterpret_cast<const u32x4*>(
-                    sKbT + (ctile * 16 + (lf & 15)) * Cfg::LDP + ks * 32 + 8 * (lf >> 4));
+                if constexpr (GEN) {                   // row-major [DK][C]
+                    reinterpret_cast<u32x4*>(gKb)[u] =
+                        *reinterpret_cast<const u32x4*>(sKbT + (u >> 3) * Cfg::LDP + 8 * (u & 7));
+                } else {
+                    const int ctile = u >> 7, ks = (u >> 6) & 1, lf = u & 63;
+                    reinterpret_cast<u32x4*>(gKb)[u] = *reinterpret_cast<const u32x4*>(
+                        sKbT + (ctile * 16 + (lf & 15)) * Cfg::LDP + ks * 32 + 8 * (lf >> 4));
+                }
             }
         }
         // A and P over this channel half (K = 64: two MFMA steps)
@@ -833,6 +843,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         const int r = br * 16 + (e >> 4), i = bc * 16 + (e & 15);
         sA[r * LDA + i] = 0.f;
         sPb[r * Cfg::LDP + i] = (bf16)0.f;
+        if constexpr (GEN) ck_a[ch * (long)(C * C) + r * C + i] = 0.f;
     }
     if (wave < 6) {
         const int np = (wave == 0 || wave == 3) ? 1 : 2;
@@ -854,14 +865,18 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                 if (PR == PI) { if (i >= r) av = 0.f; if (i > r) pv = 0.f; }
                 sA[r * LDA + i] = sBeta[r] * av;
                 sPb[r * Cfg::LDP + i] = (bf16)pv;
+                if constexpr (GEN) ck_a[ch * (long)(C * C) + r * C + i] = av;
             }
         }
     }
     __syncthreads();
     {
         uint4* gP = reinterpret_cast<uint4*>(ws_p + ch * (long)C * C);
+        if constexpr (GEN) {                           // row-major [C][C], zeros above the diagonal
+            gP[tid] = *reinterpret_cast<const uint4*>(sPb + (tid >> 3) * Cfg::LDP + 8 * (tid & 7));
+        }
         // fragment order; the two blocks above the diagonal (row tiles 0, 1 at k-step 1) are not stored
-        if (tid < 6 * 64) {
+        else if (tid < 6 * 64) {
             const int bi = tid >> 6, lf = tid & 63;
             const int Rt = bi < 2 ? bi : 2 + (bi - 2) / 2, ks = bi < 2 ? 0 : (bi - 2) % 2;
             gP[(Rt * 2 + ks) * 64 + lf] = *reinterpret_cast<const uint4*>(
@@ -912,6 +927,10 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         __syncthreads();
     });
 
+    if constexpr (GEN) {                               // T, for the backward pass
+        for (int u = tid; u < C * C; u += NT) ck_t[ch * (long)(C * C) + u] = sA[(u >> 6) * LDA + (u & 63)];
+    }
+
     // ---------------------------------------------------------------- U = (T Diag(beta)) V, Wk = (T Diag(beta)) e^G K
     bf16* sTb = reinterpret_cast<bf16*>(smem + Cfg::OFF_TB);
     bf16* sVt = reinterpret_cast<bf16*>(smem + Cfg::OFF_VT);
@@ -932,7 +951,8 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     __syncthreads();
     {
         constexpr int NUT = DV / 16, NCT = NUT + DK / 16;        // column tiles: U then Wk
-        bf16* gU = ws_u + ch * (long)C * DV;
+        bf16* gU = reinterpret_cast<bf16*>(ws_u) + ch * (long)C * DV;
+        float* gUf = reinterpret_cast<float*>(ws_u) + ch * (long)C * DV;
         bf16* gW = ws_wk + ch * (long)C * DK;
         const int r = lane & 15, kg = lane >> 4;
         constexpr int NTPW = (NCT + NW - 1) / NW;                  // column tiles per wave
@@ -965,10 +985,16 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             if (ct < NUT) {
 #pragma unroll
                 for (int R2 = 0; R2 < 4; ++R2) {
-                    bf16x4 u4;
+                    if constexpr (GEN) {                 // fp32 [C][DV]
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) u4[e] = (bf16)acc[sct][R2][e];
-                    reinterpret_cast<bf16x4*>(gU)[(R2 * (DV / 16) + ct) * 64 + lane] = u4;
+                        for (int e = 0; e < 4; ++e)
+                            gUf[(R2 * 16 + 4 * kg + e) * DV + ct * 16 + r] = acc[sct][R2][e];
+                    } else {
+                        bf16x4 u4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) u4[e] = (bf16)acc[sct][R2][e];
+                        reinterpret_cast<bf16x4*>(gU)[(R2 * (DV / 16) + ct) * 64 + lane] = u4;
+                    }
                 }
             }
         }
@@ -986,10 +1012,15 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             }
         }
         __syncthreads();
-        for (int u = tid; u < C * DK / 8; u += NT) {  // Wk in fragment order
-            const int Rt = u >> 8, ks = (u >> 6) & 3, lf = u & 63;
-            reinterpret_cast<u32x4*>(gW)[u] = *reinterpret_cast<const u32x4*>(
-                sWo + (Rt * 16 + (lf & 15)) * Cfg::LDW + ks * 32 + 8 * (lf >> 4));
+        for (int u = tid; u < C * DK / 8; u += NT) {  // Wk in fragment order (GEN: row-major [C][DK])
+            if constexpr (GEN) {
+                reinterpret_cast<u32x4*>(gW)[u] =
+                    *reinterpret_cast<const u32x4*>(sWo + (u >> 4) * Cfg::LDW + 8 * (u & 15));
+            } else {
+                const int Rt = u >> 8, ks = (u >> 6) & 3, lf = u & 63;
+                reinterpret_cast<u32x4*>(gW)[u] = *reinterpret_cast<const u32x4*>(
+                    sWo + (Rt * 16 + (lf & 15)) * Cfg::LDW + ks * 32 + 8 * (lf >> 4));
+            }
         }
     }
 }
@@ -1114,24 +1145,28 @@ bool chunk_supported(int dk, int dv, int C, bool in_bf16) {
     return false;
 }
 
-template <int DV>
+template <int DV, bool GEN>
 static hipError_t launch_intra64(const ChunkArgs& a) {
     constexpr int DK = 128;
     const long nch = unit_count(a);
     if (nch == 0) return hipSuccess;
+    if (GEN && (!a.ck_t || !a.ck_a)) return hipErrorInvalidValue;
     const WsLayout w = ws_layout_of(a);
     char* ws = (char*)a.ws;
-    hipLaunchKernelGGL((chunk_intra64_kernel<DV>), dim3((unsigned)nch), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL((chunk_intra64_kernel<DV, GEN>), dim3((unsigned)nch), dim3(512), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
                        (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
-                       (bf16*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate | a.pre);
+                       (void*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate | a.pre, a.ck_t, a.ck_a);
     return hipGetLastError();
 }
 
 template <typename T, int DK, int DV>
 static hipError_t intra_c(const ChunkArgs& a) {
     if constexpr (sizeof(T) == 2 && DK == 128) {
-        if (hot_layout(a)) return launch_intra64<DV>(a);
+        if (hot_layout(a)) return launch_intra64<DV, false>(a);
+        // the backward pass's forward stage in this configuration: the same kernel,
+        // storing the generic format and the checkpoints
+        if (hot_config(a.in_bf16, DK, a.C) && a.generic) return launch_intra64<DV, true>(a);
     }
     switch (a.C) {
         case 16: return launch_intra<T, DK, DV, 16>(a);
