@@ -13,8 +13,10 @@ from tests.parity import assert_close, cuda
 
 pytestmark = pytest.mark.gpu
 
-# the gradient arithmetic is fp32; with bf16 inputs the forward stages that are
-# re-run for the backward use bf16 MFMA operands (as in the forward pass)
+# the gradient arithmetic is fp32 (for bf16 inputs with C >= 32 the reverse chain
+# runs on bf16 MFMA with its fp32 operands split into bf16 hi + lo parts); with
+# bf16 inputs the forward stages that are re-run for the backward use bf16 MFMA
+# operands (as in the forward pass)
 BWD_TOL = {torch.float32: 1e-3, torch.bfloat16: 2e-2}
 
 
@@ -55,7 +57,8 @@ def _run(d, C, layout, dtype, seed, tag):
 
 @pytest.mark.parametrize("dk,dv,C,dtype", [(64, 64, 64, torch.float32), (64, 128, 32, torch.float32),
                                            (128, 64, 16, torch.float32), (128, 128, 64, torch.bfloat16),
-                                           (128, 128, 32, torch.bfloat16), (64, 64, 16, torch.bfloat16)])
+                                           (128, 128, 32, torch.bfloat16), (64, 64, 16, torch.bfloat16),
+                                           (64, 128, 32, torch.bfloat16), (128, 64, 64, torch.bfloat16)])
 def test_backward_shapes(dk, dv, C, dtype):
     T = 3 * C + 11
     _say(f"backward dk={dk} dv={dv} C={C} {dtype} T={T}")
