@@ -44,6 +44,9 @@ def parse():
                    help="only the step (and decode): no gate-layout, fused, varlen or backward lines")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device copy (to scale FETCH_SIZE/WRITE_SIZE counters)")
+    p.add_argument("--survey", action="store_true",
+                   help="only time the prefill step of other head sizes, chunk sizes and dtypes "
+                        "(one JSON line each)")
     return p.parse_args()
 
 
@@ -99,6 +102,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
+    if args.survey:
+        bench_survey(torch, ChunkPlan, dev, args.steps)
         return
     w = inputs.WORKLOADS[args.workload]
     d = inputs.make_prefill(w)
@@ -296,6 +302,49 @@ def bench_backward(torch, g, w, steps=5, warmup=2):
             "note": "fp32 gradient arithmetic; includes re-running the forward stages",
             "fused_pre": {"ms_per_call": round(ms_pre, 3), "tokens_per_s": tps(ms_pre),
                           "note": "gradients of raw q, k and the bf16 gate pre-activation"}}
+
+
+SURVEY_CONFIGS = [(128, 128, 64, "bf16"), (128, 64, 64, "bf16"), (64, 64, 64, "bf16"), (64, 128, 64, "bf16"),
+                  (128, 128, 32, "bf16"), (128, 128, 16, "bf16"), (128, 128, 128, "bf16"),
+                  (128, 128, 64, "fp32"), (64, 64, 64, "fp32")]
+
+
+def bench_survey(torch, ChunkPlan, dev, steps):
+    """The prefill step (both stages) for other head sizes, chunk sizes and input
+    dtypes, at the mid workload's B=4, T=8192, H=16: random inputs drawn on the
+    device (timing only), unit-norm q/k rows, log-gates in (-0.05, 0)."""
+    B, T, H = 4, 8192, 16
+    for dk, dv, C, dt in SURVEY_CONFIGS:
+        dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+        gen = torch.Generator(device=dev).manual_seed(0)
+        rn = lambda *shape: torch.randn(shape, generator=gen, device=dev)
+        q = torch.nn.functional.normalize(rn(B, T, H, dk), dim=-1).to(dtype)
+        k = torch.nn.functional.normalize(rn(B, T, H, dk), dim=-1).to(dtype)
+        v = rn(B, T, H, dv).to(dtype)
+        g = -0.05 * torch.rand((B, T, H, dk), generator=gen, device=dev)
+        beta = torch.rand((B, T, H), generator=gen, device=dev)
+        plan = ChunkPlan(q, k, v, g, beta, None, chunk_size=C)
+        for _ in range(2):
+            plan.run()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ti = tc = 0.0
+        for _ in range(steps):
+            ev[0].record(stream)
+            plan.intra()
+            ev[1].record(stream)
+            plan.chain()
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            ti += ev[0].elapsed_time(ev[1])
+            tc += ev[1].elapsed_time(ev[2])
+        ti, tc = ti / steps, tc / steps
+        print(json.dumps({"survey": {"dk": dk, "dv": dv, "chunk": C, "dtype": dt, "B": B, "T": T, "H": H,
+                                     "intra_ms": round(ti, 4), "chain_ms": round(tc, 4),
+                                     "tokens_per_s": round(B * T / ((ti + tc) / 1e3), 1)}}), flush=True)
+        del plan, q, k, v, g, beta
+        torch.cuda.empty_cache()
 
 
 def bench_decode(torch, inputs, decode_step, dev, steps):

@@ -558,37 +558,36 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     auto chan = [&](int p) { return 64 * p + 32 * (wave & 1) + 8 * (lane >> 4); };
 
     // ---------------------------------------------------------------- loads
-    // Every load is issued before any value is used: a row past the sequence end
-    // reads row 0 and is zeroed afterwards, and the gate's layout and storage are
-    // decided once for the whole block of loads.
+    // Every load is issued before any value is used, channel half 0 first: a row
+    // past the sequence end reads row 0 and is zeroed afterwards, and the gate's
+    // layout and storage are decided once per half.  Half 1 is decoded and masked
+    // only when pass 0 is done with half 0, so its loads stay in flight meanwhile.
     const bool tok_ok = valid(t);
     const long trow = grow(tok_ok ? t : 0);
     const int glay = gate_layout(gate);
     bf16x8 qv[2], kv[2], vv[Cfg::NITV], g8[2];
     floatx4 ga[2], gb[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        qv[p] = *reinterpret_cast<const bf16x8*>(q + trow * DK + chan(p));
-        kv[p] = *reinterpret_cast<const bf16x8*>(k + trow * DK + chan(p));
-    }
-    if (glay == GATE_CHANNEL && (gate & MODE_GATE_BF16)) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
+    // the per-head gate value, raw (no default value: a register written on one
+    // path while a load into it is in flight on another makes the compiler wait)
+    float gh32;
+    bf16 gh16;
+    auto load_half = [&](auto PI) {
+        constexpr int p = PI;
+        if (glay == GATE_CHANNEL && (gate & MODE_GATE_BF16)) {
             g8[p] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(g) + trow * DK + chan(p));
-    } else if (glay == GATE_CHANNEL) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        } else if (glay == GATE_CHANNEL) {
             ga[p] = *reinterpret_cast<const floatx4*>(g + trow * DK + chan(p));
             gb[p] = *reinterpret_cast<const floatx4*>(g + trow * DK + chan(p) + 4);
+        } else if (glay == GATE_HEAD && (gate & MODE_GATE_BF16)) {
+            if constexpr (p == 0) gh16 = reinterpret_cast<const bf16*>(g)[trow];
+        } else if (glay == GATE_HEAD) {
+            if constexpr (p == 0) gh32 = g[trow];
         }
-    } else if (glay == GATE_HEAD) {
-        const float x = (gate & MODE_GATE_BF16) ? (float)reinterpret_cast<const bf16*>(g)[trow] : g[trow];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) { ga[p] = floatx4{x, x, x, x}; gb[p] = ga[p]; }
-    } else {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) { ga[p] = zero4(); gb[p] = zero4(); }
-    }
+        qv[p] = *reinterpret_cast<const bf16x8*>(q + trow * DK + chan(p));
+        kv[p] = *reinterpret_cast<const bf16x8*>(k + trow * DK + chan(p));
+    };
+    load_half(std::integral_constant<int, 0>{});
+    load_half(std::integral_constant<int, 1>{});
     // v unit mapping: each group of 64 units covers 16 tokens x 4 groups of 8 channels
     auto vunit = [&](int it, int& tv, int& j) {
         const int u = tid + NT * it, w = u >> 6, l = u & 63;
@@ -602,38 +601,32 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         vv[it] = *reinterpret_cast<const bf16x8*>(v + grow(valid(tv) ? tv : 0) * DV + j);
     }
     const float bt = beta[grow(tid < C && valid(tid) ? tid : 0)];
-    // decode and mask, now that every load is in flight
-    if (tid < C) sBeta[tid] = valid(tid) ? bt : 0.f;
-    if (glay == GATE_CHANNEL && (gate & MODE_GATE_BF16)) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
+    // decode and mask channel half p (just before its values are first used)
+    auto prep_half = [&](auto PI) {
+        constexpr int p = PI;
+        if (glay == GATE_CHANNEL && (gate & MODE_GATE_BF16)) {
             ga[p] = floatx4{(float)g8[p][0], (float)g8[p][1], (float)g8[p][2], (float)g8[p][3]};
             gb[p] = floatx4{(float)g8[p][4], (float)g8[p][5], (float)g8[p][6], (float)g8[p][7]};
+        } else if (glay == GATE_HEAD) {
+            const float gh = (gate & MODE_GATE_BF16) ? (float)gh16 : gh32;
+            ga[p] = floatx4{gh, gh, gh, gh};
+            gb[p] = ga[p];
+        } else if (glay != GATE_CHANNEL) {
+            ga[p] = zero4();
+            gb[p] = zero4();
         }
-    }
-    if (glay != GATE_NONE && (gate & MODE_GATE_SOFTPLUS)) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
+        if (glay != GATE_NONE && (gate & MODE_GATE_SOFTPLUS)) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) { ga[p][m] = neg_softplus(ga[p][m]); gb[p][m] = neg_softplus(gb[p][m]); }
-    }
-    if (!tok_ok) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        }
+        if (!tok_ok) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) { qv[p][m] = (bf16)0.f; kv[p][m] = (bf16)0.f; }
-            ga[p] = zero4(); gb[p] = zero4();
+            ga[p] = zero4();
+            gb[p] = zero4();
         }
-    }
-#pragma unroll
-    for (int it = 0; it < Cfg::NITV; ++it) {
-        int tv, j;
-        vunit(it, tv, j);
-        if (!valid(tv)) {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) vv[it][m] = (bf16)0.f;
-        }
-    }
+    };
+    prep_half(std::integral_constant<int, 0>{});
     // q and k row norms (pre-processing): a token's 128 channels are spread over the
     // four lane groups of this wave and the partner wave (wave ^ 1)
     const bool qknorm = gate & MODE_QK_L2NORM;
@@ -647,6 +640,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                 sq += a * a;
                 sk += b * b;
             }
+        if (!tok_ok) { sq = 0.f; sk = 0.f; }            // half 1 is masked later
         sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
         sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
         if (lane < 16) {
@@ -657,15 +651,15 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 
     // ---------------------------------------------------------------- a1: block-local log-gate sums
     float Lg[2][8];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    auto a1_half = [&](int p) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) Lg[p][m] = row_prefix_sum(clamp_g(m < 4 ? ga[p][m] : gb[p][m - 4]) * LOG2E);
         if (rr == 15) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) sTot[R * DK + chan(p) + m] = Lg[p][m];
         }
-    }
+    };
+    a1_half(0);                                        // half 1 follows pass 0's a2
     __syncthreads();
     auto qn = [&](int r) { return inv_norm(sNp[r] + sNp[C + r]); };          // 1/||q_r||
     auto kn = [&](int r) { return inv_norm(sNp[2 * C + r] + sNp[3 * C + r]); };  // 1/||k_r||
@@ -748,7 +742,12 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             if constexpr (GEN) Vec8<bf16>::store(gQt + t * DK + c, o1);
             else Vec8<bf16>::store(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
         });
-        if (p == 0 && tid < DK) {
+        if (p == 0) {                                  // channel half 1, and beta
+            prep_half(std::integral_constant<int, 1>{});
+            a1_half(1);
+            if (tid < C) sBeta[tid] = valid(tid) ? bt : 0.f;
+        }
+        if (p == 1 && tid < DK) {
             float lg = 0.f;
 #pragma unroll
             for (int J = 0; J < NB; ++J) lg += sTot[J * DK + tid];
@@ -946,6 +945,10 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     for (int it = 0; it < Cfg::NITV; ++it) {
         int tv, j;
         vunit(it, tv, j);
+        if (!valid(tv)) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) vv[it][m] = (bf16)0.f;
+        }
         store_column8(sVt, LDT, j, tv, __builtin_bit_cast(u32x4, vv[it]), 2 * (lane >> 4));
     }
     __syncthreads();
