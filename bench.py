@@ -146,10 +146,15 @@ def main():
     names = ("chunk_intra64_kernel", "chunk_chain64_kernel") if hot else ("chunk_intra_kernel", "chunk_chain_kernel")
     dom = (names[0], intra_alg, t_intra) if t_intra >= t_chain else (names[1], chain_alg, t_chain)
     achieved = dom[1] / dom[2] / 1e9
+    traffic = measured_traffic(dom[0]) if args.workload == "mid" else None
     roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom[0]) if args.workload == "mid" else None,
-                "alg_bytes": dom[1]}
+                "traffic": traffic, "alg_bytes": dom[1]}
+    if traffic:
+        # the counter bytes (inputs and the workspace the kernel writes) at the same
+        # measured duration: how close the kernel runs to the HBM limit for what it moves
+        roofline["traffic_GBps"] = round(traffic / dom[2] / 1e9, 1)
+        roofline["traffic_frac"] = round(traffic / dom[2] / 1e9 / HBM_PEAK_GBS, 4)
 
     out = {
         "metric": "KDA chunked-prefill tokens/s",
