@@ -8,7 +8,11 @@
 // so each state element is read once and written once: the state stays in
 // registers between the column reductions and the rewrite.
 //
-// One workgroup (256 threads) per (sequence, head).  Thread (ty, tx) owns the
+// One workgroup per (sequence, head): 1024 threads (16 waves) for a single token,
+// where more waves in flight per CU measured faster than more rows per thread
+// (6.2 against 5.6 TB/s), and 256 for several tokens (measured faster there).
+// Both shapes form the column sums the same way (below), so that a call with T
+// tokens equals T single steps bitwise.  Thread (ty, tx) owns the
 // float4 of columns 4*tx..4*tx+3 in rows ty, ty+RG, ty+2RG, ...: every row read
 // is a fully coalesced DV*4-byte line.  Column sums are combined in LDS in a
 // fixed order (bitwise reproducible).
@@ -21,21 +25,29 @@
 
 namespace kda {
 
-template <typename TIn, typename TOut, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+template <typename TIn, typename TOut, int DK, int DV, int NT>
+__global__ __launch_bounds__(NT) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     float* __restrict__ state, TOut* __restrict__ o, int H, int T, int gate) {
-    constexpr int NT = 256;
+    // No implicit multiply-add contraction: the fused operations are the explicit
+    // fmaf calls, so that every launch shape performs the same arithmetic.
+#pragma clang fp contract(off)
     constexpr int CG = DV / 4;       // threads across one row (float4 each)
     constexpr int RG = NT / CG;      // row groups
     constexpr int RPT = DK / RG;     // rows per thread
-    static_assert(DK % RG == 0, "row split");
+    // The column sums are formed as RED partial sums whatever NT is: partial y
+    // covers rows y, y + RED, y + 2 RED, ... in that order, and the partials are
+    // added in the order y = 0, 1, ...  A thread forms P of them, so every
+    // launch shape gives the same result bitwise.
+    constexpr int RED = 1024 / CG;
+    constexpr int P = RED / RG;
+    static_assert(DK % RG == 0 && RED % RG == 0 && DK % RED == 0, "row split");
 
     // per-token vectors, double-buffered so that token t+1 can be staged while
     // token t's update still reads them
     __shared__ float s_ak[2][DK], s_aq[2][DK], s_k[2][DK], s_a[2][DK];
-    __shared__ float s_red[2][RG][DV];
+    __shared__ float s_red[2][RED][DV];
     __shared__ float s_u[DV];
     __shared__ float s_qk[2], s_iq[2], s_ik[2];
 
@@ -90,22 +102,33 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         }
         __syncthreads();
 
-        float r[4] = {0.f, 0.f, 0.f, 0.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
+        float r[P][4], s[P][4];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int c = ty + i * RG;
+        for (int j = 0; j < P; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) { r[j][m] = 0.f; s[j][m] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {              // row ty + i RG: partial ty + (i % P) RG
+            const int c = ty + i * RG, j = i % P;
             const float ak = s_ak[pb][c], aq = s_aq[pb][c];
-            r[0] += ak * sv[i].x; r[1] += ak * sv[i].y; r[2] += ak * sv[i].z; r[3] += ak * sv[i].w;
-            s[0] += aq * sv[i].x; s[1] += aq * sv[i].y; s[2] += aq * sv[i].z; s[3] += aq * sv[i].w;
+            r[j][0] = fmaf(ak, sv[i].x, r[j][0]); r[j][1] = fmaf(ak, sv[i].y, r[j][1]);
+            r[j][2] = fmaf(ak, sv[i].z, r[j][2]); r[j][3] = fmaf(ak, sv[i].w, r[j][3]);
+            s[j][0] = fmaf(aq, sv[i].x, s[j][0]); s[j][1] = fmaf(aq, sv[i].y, s[j][1]);
+            s[j][2] = fmaf(aq, sv[i].z, s[j][2]); s[j][3] = fmaf(aq, sv[i].w, s[j][3]);
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) { s_red[0][ty][4 * tx + m] = r[m]; s_red[1][ty][4 * tx + m] = s[m]; }
+        for (int j = 0; j < P; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                s_red[0][ty + j * RG][4 * tx + m] = r[j][m];
+                s_red[1][ty + j * RG][4 * tx + m] = s[j][m];
+            }
         __syncthreads();
 
         if (tid < DV) {
             float rr = 0.f, ss = 0.f;
 #pragma unroll
-            for (int y = 0; y < RG; ++y) { rr += s_red[0][y][tid]; ss += s_red[1][y][tid]; }
+            for (int y = 0; y < RED; ++y) { rr += s_red[0][y][tid]; ss += s_red[1][y][tid]; }
             const float ik = s_ik[pb];
             const float u = beta[row] * (to_f32(v[row * DV + tid]) - rr * ik);
             s_u[tid] = u * ik;
@@ -118,8 +141,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         for (int i = 0; i < RPT; ++i) {
             const int c = ty + i * RG;
             const float a = s_a[pb][c], kc = s_k[pb][c];
-            sv[i].x = a * sv[i].x + kc * u0; sv[i].y = a * sv[i].y + kc * u1;
-            sv[i].z = a * sv[i].z + kc * u2; sv[i].w = a * sv[i].w + kc * u3;
+            sv[i].x = fmaf(a, sv[i].x, kc * u0); sv[i].y = fmaf(a, sv[i].y, kc * u1);
+            sv[i].z = fmaf(a, sv[i].z, kc * u2); sv[i].w = fmaf(a, sv[i].w, kc * u3);
         }
     }
 #pragma unroll
@@ -130,9 +153,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <typename TIn, typename TOut, int DK, int DV>
 static hipError_t launch_decode(const DecodeArgs& a) {
     const long nh = (long)a.N * a.H;
-    hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV>), dim3((unsigned)nh), dim3(256), 0,
-                       a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta,
-                       a.state, (TOut*)a.o, a.H, a.T, a.gate | a.pre);
+    if (a.T == 1)
+        hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, 1024>), dim3((unsigned)nh), dim3(1024), 0,
+                           a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta,
+                           a.state, (TOut*)a.o, a.H, a.T, a.gate | a.pre);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<TIn, TOut, DK, DV, 256>), dim3((unsigned)nh), dim3(256), 0,
+                           a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta,
+                           a.state, (TOut*)a.o, a.H, a.T, a.gate | a.pre);
     return hipGetLastError();
 }
 
