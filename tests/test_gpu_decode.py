@@ -103,8 +103,19 @@ def test_decode_full_size_1000_steps():
 def test_decode_tokens(T, layout):
     """T tokens per call (kda_decode_tokens) equal T single steps bitwise, and the
     oracle over the same T-token sequences."""
+    _tokens_case(T, layout, 128, 128)
+
+
+@pytest.mark.parametrize("T,dk,dv", [(2, 64, 64), (3, 64, 128), (2, 128, 64), (4, 64, 64)])
+def test_decode_tokens_head_sizes(T, dk, dv):
+    """The same for the other head sizes (each workgroup shape of the several-token
+    kernel: 512 threads for two tokens, 256 from three on)."""
+    _tokens_case(T, "channel", dk, dv)
+
+
+def _tokens_case(T, layout, dk, dv):
     from linear_attention_sequence_chunk_amd import decode_tokens
-    w = inputs.WORKLOADS["decode"].with_(B=6, H=3)
+    w = inputs.WORKLOADS["decode"].with_(B=6, H=3, dk=dk, dv=dv)
     d = inputs.make_decode_steps(w, T)                    # [T, N, H, ...]
     S0 = inputs.decode_state(w)
     seq = lambda x: x.transpose(0, 1).contiguous()        # -> [N, T, H, ...]

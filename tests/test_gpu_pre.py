@@ -114,3 +114,33 @@ def test_decode_pre(T, dtype, layout, gdtype):
     eo = assert_close(f"{tag} o", o.cpu(), o_ref, TOL[dtype])
     es = assert_close(f"{tag} S", S.cpu(), S_ref, TOL[dtype])
     _say(f"  {tag}: max err o {eo:.2e}  S {es:.2e}")
+
+
+@pytest.mark.parametrize("T,dk,dv,layout,gdtype,sp,qk", [(2, 128, 128, "channel", torch.bfloat16, False, False),
+                                                         (2, 64, 128, "head", torch.bfloat16, False, True),
+                                                         (5, 64, 64, "channel", torch.bfloat16, True, False),
+                                                         (1, 128, 64, "head", torch.float32, True, True),
+                                                         (3, 128, 64, "channel", torch.bfloat16, False, True)])
+def test_decode_gate_forms(T, dk, dv, layout, gdtype, sp, qk):
+    """Decode over each gate storage the kernels read (fp32 or bf16, per channel or
+    per head, log-gate or pre-activation), head sizes 64 and 128, one or several
+    tokens per call; the flags one at a time."""
+    N, H = 5, 3
+    d = _raw(60 + T + dk, (N, T), H, dk, dv, torch.bfloat16, gdtype, layout, zero_rows=False)
+    if not sp:                                            # a log-gate in (-3, 0), stored as given
+        d["a"] = (-torch.nn.functional.softplus(d["a"].float())).to(gdtype)
+    dg = {key: x.cuda() for key, x in d.items()}
+    S = dg["S0"].clone()
+    o = decode_tokens(dg["q"], dg["k"], dg["v"], dg["a"], dg["beta"], S, gate_layout=layout,
+                      qk_l2norm=qk, gate_act="softplus" if sp else None)
+    torch.cuda.synchronize()
+    q = oracle.l2_normalize(d["q"]) if qk else oracle.to_f64(d["q"])
+    k = oracle.l2_normalize(d["k"]) if qk else oracle.to_f64(d["k"])
+    g = oracle.gate_softplus(d["a"]) if sp else oracle.to_f64(d["a"])
+    if layout == "head":
+        g = np.ascontiguousarray(np.broadcast_to(g[..., None], q.shape))
+    o_ref, S_ref = oracle.recurrent(q, k, d["v"], g, d["beta"], d["S0"])
+    tag = f"decode T{T} dk{dk} dv{dv} {layout} {gdtype} softplus={sp} norm={qk}"
+    eo = assert_close(f"{tag} o", o.cpu(), o_ref, TOL[torch.bfloat16])
+    es = assert_close(f"{tag} S", S.cpu(), S_ref, TOL[torch.bfloat16])
+    _say(f"  {tag}: max err o {eo:.2e}  S {es:.2e}")
