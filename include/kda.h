@@ -287,7 +287,8 @@ size_t kda_chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
  *   state  [N,H,dk,dv] fp32, read and overwritten with the new state
  *   o      [N,H,dv] out_dtype
  * Each state element is read once and written once.  o must not overlap any
- * other argument; state must not overlap the inputs.
+ * other argument; state must not overlap the inputs.  N*H above 2^31 - 1
+ * returns KDA_ERR_SHAPE (one workgroup per sequence and head).
  */
 int kda_decode_step(const void *q, const void *k, const void *v,
                     const float *g, const float *beta,

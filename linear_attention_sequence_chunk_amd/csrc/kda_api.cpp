@@ -26,12 +26,11 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 bool debug_sync() {
-    static int cached = -1;
-    if (cached < 0) {
+    static const bool on = [] {                       // read once, thread-safe initialisation
         const char* e = getenv("KDA_DEBUG_SYNC");
-        cached = (e && e[0] && e[0] != '0') ? 1 : 0;
-    }
-    return cached == 1;
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
 }
 
 int device_ready() {
@@ -485,6 +484,7 @@ int decode_call(const void* q, const void* k, const void* v, const float* g, con
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
     const size_t nh = (size_t)N * H, tok = nh * (size_t)T;
     if (tok == 0) return KDA_OK;
+    if (nh > 0x7fffffff) return KDA_ERR_SHAPE;           // one workgroup per (n, h)
     const bool need_g = gate_layout != KDA_GATE_NONE;
     if (!q || !k || !v || (need_g && !g) || !beta || !state || !o) return KDA_ERR_NULL;
     if (!need_g) g = nullptr;                            // g is not read without gates

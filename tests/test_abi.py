@@ -178,7 +178,8 @@ def test_decode_validation_codes():
                                  x["N"], x["H"], x["dk"], x["dv"], x["ind"], x["outd"], None)
     cases = [(dict(N=-1), SHAPE), (dict(dk=100), UNSUP), (dict(ind=3), UNSUP),
              (dict(state=None), NULL), (dict(v=a["v"] + 1), MISAL), (dict(state=a["state"] + 8), MISAL),
-             (dict(o=a["state"]), ALIAS), (dict(state=a["q"]), ALIAS), (dict(o=a["g"] + 16), ALIAS)]
+             (dict(o=a["state"]), ALIAS), (dict(state=a["q"]), ALIAS), (dict(o=a["g"] + 16), ALIAS),
+             (dict(N=1 << 16, H=(1 << 15) + 1), SHAPE)]                 # N*H beyond one grid dimension
     for change, code in cases:
         b = dict(a); b.update(change)
         assert call(b) == code, (change, code)
