@@ -407,7 +407,10 @@ def bench_decode(torch, inputs, decode_step, dev, steps):
 def cpu_baseline(d, w):
     """The fp64 oracle (as it stands) on the same workload's inputs, timed on the
     host cores: every (batch row, head) sequence, whole length (about a second on
-    16 threads, ~16 CPU-seconds)."""
+    16 threads, ~16 CPU-seconds); then one thread on two sequences, and the host's
+    CPU model."""
+    import numpy as np
+
     import oracle
 
     threads = min(os.cpu_count() or 1, 16)
@@ -417,9 +420,29 @@ def cpu_baseline(d, w):
     oracle.recurrent(*args, S0=None if d["S0"] is None else oracle.to_f64(d["S0"]), nthreads=threads)
     dt = time.perf_counter() - t0
     used = oracle.last_threads()
+    # one thread on two of the sequences, in the same unit (a token is all H heads)
+    one = [np.ascontiguousarray(a[:1, :, :2]) for a in args]
+    s0 = None if d["S0"] is None else np.ascontiguousarray(oracle.to_f64(d["S0"])[:1, :2])
+    t1 = time.perf_counter()
+    oracle.recurrent(*one, S0=s0, nthreads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": round(w.B * w.T / dt, 1), "unit": "tokens/s", "cores": min(used, w.B * w.H),
             "threads": used, "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"the whole workload: {w.B}x{w.H} (batch x head) sequences of {w.T} tokens"}
+            "sample": f"the whole workload: {w.B}x{w.H} (batch x head) sequences of {w.T} tokens",
+            "single_thread_value": round(2 * w.T / w.H / dt1, 1),
+            "single_thread_sample": f"2 of the {w.H} heads of one batch row, one thread",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
