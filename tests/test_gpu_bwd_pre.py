@@ -102,3 +102,33 @@ def test_backward_pre_short_and_no_gate():
     assert_close("no-gate dq", got["dq"].cpu(), oracle.l2_normalize_vjp(d["q"], ref["dq"]), 1e-3)
     assert_close("no-gate dk", got["dk"].cpu(), oracle.l2_normalize_vjp(d["k"], ref["dk"]), 1e-3)
     assert_close("no-gate dv", got["dv"].cpu(), ref["dv"], 1e-3)
+
+
+def test_backward_pre_gate_alignment_and_odd_counts():
+    """Per-head bf16 pre-activations given at element alignment only (a view two
+    bytes into a buffer), and a count of gate values that is not a multiple of 8:
+    the one-value-per-lane forms, which must agree bitwise with the eight-per-lane
+    ones on the same values, and with the oracle."""
+    _say("backward pre: gate alignment / odd counts")
+    dev = "cuda:0"
+    for T in (40, 37):                                    # 2*40*3 values: multiple of 8; 2*37*3: not
+        d = _raw(70 + T, (2, T), 3, 64, 64, torch.float32, torch.bfloat16, "head", zero_rows=False)
+        rs = np.random.default_rng(T)
+        dO = torch.tensor(rs.standard_normal((2, T, 3, 64)), dtype=torch.float32)
+        buf = torch.empty(d["a"].numel() + 1, dtype=torch.bfloat16)
+        buf[1:] = d["a"].reshape(-1)
+        a_mis = buf.to(dev)[1:].view(d["a"].shape)        # 2-byte aligned
+        assert a_mis.data_ptr() % 16 != 0
+        args = [d["q"].to(dev), d["k"].to(dev), d["v"].to(dev)]
+        kw = dict(chunk_size=32, gate_layout="head", qk_l2norm=True, gate_act="softplus")
+        got = chunk_bwd(*args, a_mis, d["beta"].to(dev), dO.to(dev), d["S0"].to(dev), **kw)
+        ref = chunk_bwd(*args, d["a"].to(dev), d["beta"].to(dev), dO.to(dev), d["S0"].to(dev), **kw)
+        torch.cuda.synchronize()
+        for n in ("dq", "dk", "dv", "dbeta", "dS0", "dg"):
+            assert torch.equal(got[n], ref[n]), n
+        qn, kn = oracle.l2_normalize(d["q"]), oracle.l2_normalize(d["k"])
+        g = oracle.gate_softplus(d["a"])
+        g = np.ascontiguousarray(np.broadcast_to(g[..., None], qn.shape))
+        o = oracle.backward(qn, kn, d["v"], g, d["beta"], d["S0"], dO, None)
+        assert_close(f"T={T} dq", got["dq"].cpu(), oracle.l2_normalize_vjp(d["q"], o["dq"]), 1e-3)
+        assert_close(f"T={T} dg", got["dg"].cpu(), oracle.gate_softplus_vjp(d["a"], o["dg"].sum(-1)), 1e-3)
