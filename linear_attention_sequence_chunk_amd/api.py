@@ -19,8 +19,10 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream(stream, device) -> int:
+    """The raw HIP stream: the given one, else torch's current stream on the
+    tensors' device."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
 
 
@@ -102,7 +104,7 @@ def _call_chunk(fn_name, q, k, v, g, beta, initial_state, o, final_state, B, T, 
                 out_dtype, workspace, chunk_size, stream, gate_layout="channel", pre=0):
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
             _ptr(final_state), B, T, H, dk, dv, _code(q.dtype), _code(out_dtype),
-            _ptr(workspace), workspace.numel(), _stream(stream), chunk_size]
+            _ptr(workspace), workspace.numel(), _stream(stream, q.device), chunk_size]
     if pre and fn_name in ("kda_chunk_fwd", "kda_chunk_intra"):
         fn_name, args = fn_name + "_pre", args + [_gate(gate_layout), pre]
     elif gate_layout != "channel" and fn_name in ("kda_chunk_fwd", "kda_chunk_intra"):
@@ -167,7 +169,7 @@ def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, chunk_siz
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     st = L.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
                                 _ptr(final_state), _ptr(cu_seqlens), N, T, H, dk, dv, _code(q.dtype),
-                                _code(out_dtype), _ptr(workspace), workspace.numel(), _stream(stream),
+                                _code(out_dtype), _ptr(workspace), workspace.numel(), _stream(stream, dev),
                                 chunk_size, _gate(gate_layout))
     _lib.check(st, "kda_chunk_fwd_varlen")
     return o, final_state
@@ -217,7 +219,7 @@ def chunk_bwd(q, k, v, g, beta, dO, initial_state=None, dST=None, chunk_size=64,
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dO), _ptr(dST),
             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
             _ptr(out["dS0"]), B, T, H, dk, dv, _code(q.dtype), _ptr(workspace), workspace.numel(),
-            _stream(stream), chunk_size, gl)
+            _stream(stream, dev), chunk_size, gl)
     if pre:
         _lib.check(L.kda_chunk_bwd_pre(*args, pre), "kda_chunk_bwd_pre")
     else:
@@ -265,7 +267,7 @@ def chunk_bwd_varlen(q, k, v, g, beta, dO, cu_seqlens, initial_state=None, dST=N
     st = L.kda_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(dO),
                                 _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                                 _ptr(out["dbeta"]), _ptr(out["dS0"]), _ptr(cu_seqlens), N, T, H, dk, dv,
-                                _code(q.dtype), _ptr(workspace), workspace.numel(), _stream(stream), chunk_size,
+                                _code(q.dtype), _ptr(workspace), workspace.numel(), _stream(stream, dev), chunk_size,
                                 _gate(gate_layout))
     _lib.check(st, "kda_chunk_bwd_varlen")
     return out
@@ -321,7 +323,7 @@ def decode_step(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, ga
         o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     st = _lib.lib().kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                        _ptr(o), N, H, dk, dv, _code(q.dtype), _code(out_dtype),
-                                       _stream(stream), _gate(gate_layout))
+                                       _stream(stream, dev), _gate(gate_layout))
     _lib.check(st, "kda_decode_step_ex")
     return o
 
@@ -347,7 +349,7 @@ def decode_tokens(q, k, v, g, beta, state, out_dtype=None, o=None, stream=None, 
     if o is None:
         o = torch.empty((N, T, H, dv), dtype=out_dtype, device=dev)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, T, H, dk, dv,
-            _code(q.dtype), _code(out_dtype), _stream(stream), _gate(gate_layout)]
+            _code(q.dtype), _code(out_dtype), _stream(stream, dev), _gate(gate_layout)]
     name = "kda_decode_tokens_pre" if pre else "kda_decode_tokens"
     st = getattr(_lib.lib(), name)(*(args + [pre] if pre else args))
     _lib.check(st, name)
