@@ -25,6 +25,12 @@ CSRC = os.path.join(ROOT, "linear_attention_sequence_chunk_amd", "csrc")
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a
 # plain copy of known size); valid only while the kernel's sources are unchanged
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mid_prefill.txt")
+# MFMA counters per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES,
+# GRBM_GUI_ACTIVE), under the same rule
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_valu_mid_prefill.txt")
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+SIMDS = 1024                # 256 CUs x 4
+XCDS = 8                    # GRBM_GUI_ACTIVE is summed over them
 KERNEL_SOURCES = {
     "chunk_intra64_kernel": ["kda_common.h", "kda_launch.h", "kda_chunk.h", "kda_chunk_intra.hip"],
     "chunk_chain64_kernel": ["kda_common.h", "kda_launch.h", "kda_chunk.h", "kda_chunk_chain64.hip"],
@@ -75,6 +81,41 @@ def measured_traffic(kernel):
             if kv.get("sha256") == digest:
                 return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
     return None
+
+
+def measured_mfma(kernel, seconds):
+    """bf16 MFMA work and utilisation of one launch from the committed counter
+    summary (flops = 512 per MOPS unit; busy = MFMA-busy cycles over all SIMD
+    cycles), the rate at the live duration; None when absent or stale."""
+    if kernel not in KERNEL_SOURCES or not os.path.exists(MFMA_FILE):
+        return None
+    digest = source_digest(KERNEL_SOURCES[kernel])
+    with open(MFMA_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) < 2 or parts[0] != "mfma" or parts[1] != kernel:
+                continue
+            kv = dict(p.split("=", 1) for p in parts[2:] if "=" in p)
+            if kv.get("sha256") != digest:
+                continue
+            flops = 512.0 * float(kv["mops_bf16"])
+            busy = float(kv["busy_cycles"]) / (float(kv["gui_active"]) / XCDS * SIMDS)
+            tflops = flops / seconds / 1e12
+            return {"kernel": kernel, "flops_per_launch": round(flops), "tflops": round(tflops, 1),
+                    "frac_bf16_peak": round(tflops / MFMA_PEAK_TFLOPS, 4), "busy_pct": round(100 * busy, 2),
+                    "source": "profiles/mfma_valu_mid_prefill.txt"}
+    return None
+
+
+def mfma_summary(names, t_intra, t_chain, t_step):
+    """Counted bf16 MFMA work of both prefill kernels at the live durations, and
+    over the whole step; None when the counters are absent or stale."""
+    intra, chain = measured_mfma(names[0], t_intra), measured_mfma(names[1], t_chain)
+    if intra is None or chain is None:
+        return None
+    step = (intra["flops_per_launch"] + chain["flops_per_launch"]) / t_step / 1e12
+    return {"intra": intra, "chain": chain, "step_tflops": round(step, 1),
+            "step_frac_bf16_peak": round(step / MFMA_PEAK_TFLOPS, 4)}
 
 
 def prefill_bytes_per_token_head(dk, dv, in_bytes, out_bytes):
@@ -157,7 +198,7 @@ def main():
         roofline["traffic_frac"] = round(traffic / dom[2] / 1e9 / HBM_PEAK_GBS, 4)
 
     out = {
-        "metric": "KDA chunked-prefill tokens/s",
+        "metric": "KDA chunked-prefill tokens/s (MFMA util %); decode step state GB/s (% HBM)",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -174,6 +215,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "chunk": w.C,
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "mfma": mfma_summary(names, t_intra, t_chain, ms_per_step / 1e3) if args.workload == "mid" else None,
         "path": {"step_alg_bytes": step_alg, "step_alg_GBps": round(step_alg / (ms_per_step / 1e3) / 1e9, 1),
                  "step_frac_hbm": round(step_alg / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                  "intra_ms": round(t_intra * 1e3, 4), "chain_ms": round(t_chain * 1e3, 4),
