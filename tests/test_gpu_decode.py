@@ -142,3 +142,30 @@ def _tokens_case(T, layout, dk, dv):
     o_ref, S_ref = oracle.recurrent(q, k, v, seq(g_ch), beta, S0)
     assert_close(f"tokens T={T} {layout} o", o.cpu(), o_ref, TOL[torch.bfloat16])
     assert_close(f"tokens T={T} {layout} S", S.cpu(), S_ref, TOL[torch.bfloat16])
+
+
+def test_decode_tokens_full_size():
+    """The four-token call bench.py times, at full size (256 sequences x 32 heads):
+    bitwise equal to four single steps on every state and output, and the oracle
+    on 8 sampled (sequence, head) pairs."""
+    from linear_attention_sequence_chunk_amd import decode_tokens
+    w = inputs.WORKLOADS["decode"]
+    T = 4
+    _say("decode tokens full size")
+    d = inputs.make_decode_steps(w, T)                    # [T, N, H, ...]
+    S0 = inputs.decode_state(w)
+    seq = lambda x: x.transpose(0, 1).contiguous()        # -> [N, T, H, ...]
+    dg = cuda(d)
+    S = S0.cuda()
+    o = decode_tokens(seq(dg["q"]), seq(dg["k"]), seq(dg["v"]), seq(dg["g"]), seq(dg["beta"]), S)
+    Ss = S0.cuda()
+    steps = [decode_step(dg["q"][t], dg["k"][t], dg["v"][t], dg["g"][t], dg["beta"][t], Ss) for t in range(T)]
+    torch.cuda.synchronize()
+    assert torch.equal(o, torch.stack(steps, dim=1)) and torch.equal(S, Ss)
+    rs = np.random.default_rng(9)
+    seqs, heads = rs.choice(w.B, 8, replace=False), rs.integers(0, w.H, 8)
+    pick = lambda x: x[:, seqs, heads][:, :, None]        # [T, 8, 1, d]
+    o_ref, S_ref = _oracle_steps(pick(d["q"]), pick(d["k"]), pick(d["v"]), pick(d["g"]), pick(d["beta"]),
+                                 S0[seqs, heads][:, None])
+    assert_close("S sampled", S[seqs, heads].cpu(), S_ref[:, 0], TOL[torch.bfloat16])
+    assert_close("o sampled", o[seqs, :, heads].cpu(), o_ref[:, :, 0], TOL[torch.bfloat16])   # [8, T, dv]
