@@ -31,8 +31,9 @@
  *   - Supported: dk, dv in {64, 128}; chunk size C in {16, 32, 64, 128} for
  *     bf16 inputs and {16, 32, 64} for fp32 inputs; any T >= 0 (a last
  *     partial chunk is allowed); B, H >= 0.
- *   - Alignment: kda_chunk_fwd needs q, k, v, o and the workspace 16-byte
- *     aligned and g 8-byte aligned; kda_decode_step needs the state 16-byte
+ *   - Alignment: kda_chunk_fwd needs q, k, v, o, the workspace and a
+ *     per-channel g 16-byte aligned (true of any [..., dk] row of a tensor whose
+ *     storage is 16-byte aligned); kda_decode_step needs the state 16-byte
  *     aligned; every other pointer needs the alignment of its element type.
  *   - Validation happens on the host before any HIP call; on error nothing is
  *     launched and nothing is written.
@@ -188,8 +189,10 @@ int kda_chunk_intra_ex(const void *q, const void *k, const void *v,
  *   cu_seqlens    [N+1]    int32, DEVICE memory: sequence s is tokens
  *                          cu_seqlens[s] .. cu_seqlens[s+1]-1; cu_seqlens[0] = 0,
  *                          non-decreasing, cu_seqlens[N] = T.  Other values give
- *                          unspecified results but every access stays in bounds
- *                          (offsets are clamped to [0, T] on the device).
+ *                          unspecified results but every access stays in bounds:
+ *                          on the device each offset becomes the running maximum
+ *                          of the offsets so far, clamped to [0, T], so sequences
+ *                          never overlap.
  *   initial_state [N,H,dk,dv] fp32 or NULL;  final_state [N,H,dk,dv] fp32 or NULL
  *   o             [T,H,dv] out_dtype
  *   workspace     >= kda_chunk_varlen_workspace_bytes(N, T, H, dk, dv, in_dtype, C)
@@ -233,7 +236,7 @@ size_t kda_chunk_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
  * Supported: C in {16, 32, 64}; dk, dv in {64, 128}; in_dtype BF16 or F32 (the
  * gradient arithmetic is fp32).  Outputs must not overlap any input, the
  * workspace or each other.  Alignment: q, k, v and the workspace 16 bytes,
- * per-channel g 8 bytes, everything else 4 bytes.  Deterministic (no
+ * per-channel g 16 bytes, everything else 4 bytes.  Deterministic (no
  * floating-point atomics).
  */
 int kda_chunk_bwd(const void *q, const void *k, const void *v,
@@ -287,8 +290,10 @@ size_t kda_chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
  *   state  [N,H,dk,dv] fp32, read and overwritten with the new state
  *   o      [N,H,dv] out_dtype
  * Each state element is read once and written once.  o must not overlap any
- * other argument; state must not overlap the inputs.  N*H above 2^31 - 1
- * returns KDA_ERR_SHAPE (one workgroup per sequence and head).
+ * other argument; state must not overlap the inputs.  One workgroup of 1024
+ * threads runs per sequence and head (512 for two tokens per call, 256 for
+ * more, in kda_decode_tokens); N*H beyond 2^32 - 1 work-items at that size
+ * (4,194,303 pairs for one token) returns KDA_ERR_SHAPE.
  */
 int kda_decode_step(const void *q, const void *k, const void *v,
                     const float *g, const float *beta,

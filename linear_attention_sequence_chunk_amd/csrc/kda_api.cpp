@@ -108,13 +108,13 @@ int validate_chunk(const ChunkCall& c) {
     if (tok > 0 && (!c.q || !c.k || !c.v || (need_g && !c.g) || !c.beta || !c.o)) return KDA_ERR_NULL;
     const float* g = need_g ? c.g : nullptr;            // g is not read without gates
 
-    // q, k, v, o and the workspace move in 16-byte vectors, per-channel g in 8-byte
-    // pairs; per-head g, beta and the states only need fp32 alignment.
+    // q, k, v, o, the workspace and a per-channel g move in 16-byte vectors (the
+    // C = 64 intra kernel reads four fp32 or eight bf16 gates at once); per-head g,
+    // beta and the states only need their element's alignment.
     const void* p16[5] = {c.q, c.k, c.v, c.o, c.ws};
     for (const void* p : p16)
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
-    if (g && !aligned(g, c.gate == KDA_GATE_CHANNEL ? ((c.pre & KDA_PRE_GATE_BF16) ? 16 : 8)
-                                                     : ((c.pre & KDA_PRE_GATE_BF16) ? 2 : 4)))
+    if (g && !aligned(g, c.gate == KDA_GATE_CHANNEL ? 16 : ((c.pre & KDA_PRE_GATE_BF16) ? 2 : 4)))
         return KDA_ERR_MISALIGNED;
     const void* p4[3] = {c.beta, c.s0, c.sT};
     for (const void* p : p4)
@@ -250,9 +250,10 @@ int run_bwd(BwdCall c) {
     const void* p16[4] = {c.q, c.k, c.v, c.ws};
     for (const void* p : p16)
         if (p && !aligned(p, 16)) return KDA_ERR_MISALIGNED;
-    // a gate tensor read only by the elementwise pre-processing needs its element's alignment
+    // a gate tensor read only by the elementwise pre-processing needs its element's
+    // alignment; one the forward stages read directly, as kda_chunk_fwd_ex
     const bool g_mat = pre_gate_materialised(c.gate, c.pre);
-    if (c.g && !aligned(c.g, g_mat ? ((c.pre & KDA_PRE_GATE_BF16) ? 2 : 4) : (c.gate == KDA_GATE_CHANNEL ? 8 : 4)))
+    if (c.g && !aligned(c.g, g_mat ? ((c.pre & KDA_PRE_GATE_BF16) ? 2 : 4) : (c.gate == KDA_GATE_CHANNEL ? 16 : 4)))
         return KDA_ERR_MISALIGNED;
     const void* p4[10] = {c.beta, c.s0, c.dO, c.dST, c.dq, c.dk, c.dv, c.dg, c.dbeta, c.dS0};
     for (const void* p : p4)
@@ -484,7 +485,9 @@ int decode_call(const void* q, const void* k, const void* v, const float* g, con
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
     const size_t nh = (size_t)N * H, tok = nh * (size_t)T;
     if (tok == 0) return KDA_OK;
-    if (nh > 0x7fffffff) return KDA_ERR_SHAPE;           // one workgroup per (n, h)
+    // one workgroup per (n, h) in a 1-D grid: the work-items, nh times the
+    // workgroup size the token count selects, must fit in 32 bits
+    if (nh > 0xffffffffull / (size_t)kda::decode_block_threads(T)) return KDA_ERR_SHAPE;
     const bool need_g = gate_layout != KDA_GATE_NONE;
     if (!q || !k || !v || (need_g && !g) || !beta || !state || !o) return KDA_ERR_NULL;
     if (!need_g) g = nullptr;                            // g is not read without gates

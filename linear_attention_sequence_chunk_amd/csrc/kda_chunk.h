@@ -189,16 +189,20 @@ constexpr bool chain_fits() { return DVS <= DV && ChainCfg<T, TOut, DK, DV, C, D
 // Fixed-length batches [B,T,H,d]: chunk n of sequence b and head h is unit
 // n * (B*H) + b*H + h (chunk-major).  Packed variable-length batches [T,H,d]
 // with token offsets cu_seqlens[N+1]: chunk j, counted over all sequences in
-// order, of head h is unit j*H + h; cu_chunks[s], built on the device, is the
-// first chunk of sequence s.  Offsets read from cu_seqlens are clamped to
-// [0, T] and made non-decreasing, so no access leaves the tensors whatever
-// they hold.
+// order, of head h is unit j*H + h.  A device pass (packed_chunks_kernel) first
+// turns the offsets into cu_tok[s] = min(T, max(0, cu_seqlens[0..s])), a
+// running maximum clamped to [0, T], and cu_chunks[s], the first chunk of
+// sequence s; every kernel reads only those.  Sequence s is tokens
+// [cu_tok[s], cu_tok[s+1]): the ranges are disjoint and lie inside [0, T]
+// whatever cu_seqlens holds, so the chunks of all sequences number at most
+// ceil(T/C) + N, the units the workspace and the grids are sized for.
 struct UnitMap {
     int T_len;                 // tokens per sequence (fixed) or in all (packed)
     int H, C, NC;              // NC: chunks per sequence (fixed)
     long BH;                   // B*H (fixed)
-    const int* cu_seqlens;     // NULL for fixed-length batches
-    const int* cu_chunks;
+    const int* cu_seqlens;     // NULL for fixed-length batches (only tested against NULL)
+    const int* cu_chunks;      // [N+1] first chunk of each sequence, then the total
+    const int* cu_tok;         // [N+1] clamped, non-decreasing token offsets
     int nseq;
 };
 struct SeqRange { long tok_begin, tok_end, chunk0; int nchunks; };
@@ -213,8 +217,8 @@ __device__ inline SeqRange seq_range(const UnitMap& m, int s) {
         r.tok_begin = (long)s * m.T_len; r.tok_end = r.tok_begin + m.T_len;
         r.chunk0 = 0; r.nchunks = m.NC;
     } else {
-        r.tok_begin = clamp_tok(m.cu_seqlens[s], 0, m.T_len);
-        r.tok_end = clamp_tok(m.cu_seqlens[s + 1], r.tok_begin, m.T_len);
+        r.tok_begin = m.cu_tok[s];
+        r.tok_end = m.cu_tok[s + 1];
         r.chunk0 = m.cu_chunks[s];
         r.nchunks = m.cu_chunks[s + 1] - m.cu_chunks[s];
     }

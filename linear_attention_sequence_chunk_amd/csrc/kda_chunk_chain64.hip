@@ -15,6 +15,22 @@
 //   waves 4-7 ("O waves"): row tile R = wave - 4 of O = Qt S + P W
 //   all waves           : state rows 16*wave .. +15:  S <- gam S + Kb^T W
 // Two barriers per chunk: S^T ready -> (W, Qt S) -> W^T ready -> (P W, S update).
+//
+// Long sequences with few (sequence, head) pairs are cut into segments of L
+// chunks that run side by side (segment-affine form).  A segment maps its start
+// state to its end state affinely, S -> M S + E, with M = prod over its chunks of
+// (Diag(gam) - Kb^T Wk) and E its end state from a zero start.  Three launches:
+//   maps  (CHAIN_MAPS): each segment but the last runs the chain, without
+//         outputs, on the augmented state [S | I]: value columns from a zero
+//         start (segment 0 from the call's initial state) give E, the dk extra
+//         columns from the identity with U taken as 0 give M;
+//   scan  (chain_seg_scan_kernel): start states Sst_0 = S0, Sst_1 = E_0,
+//         Sst_{s+1} = M_s Sst_s + E_s, in fp32;
+//   outputs (CHAIN_SEG): every segment runs the chain with outputs from its
+//         start state; the last writes the final state.
+// This is the chunk recurrence regrouped (the state after a chunk is an affine
+// function of the state before it), so the result equals the sequential chain
+// up to rounding; the extra cost is the maps launch.
 #include "kda_chunk.h"
 
 namespace kda {
@@ -26,54 +42,80 @@ namespace kda {
 //                                                        never written, never read)
 //   U      [4 row tiles][DV/16 column tiles][64][4] bf16  lane l, element e: row 16R + 4(l/16) + e, column 16J + l%16
 //   gam    [DK] fp32
+enum ChainMode { CHAIN_PLAIN = 0, CHAIN_MAPS = 1, CHAIN_SEG = 2 };
+
 template <typename TOut, int DV, int DVS>
 struct Chain64Cfg {
     static constexpr int C = 64, DK = 128, NT = 512, NJ = DVS / 16, NSL = DV / DVS;
     static constexpr int LDK = DK + 8, LDC = C + 8;   // padded bf16 rows of S^T, W^T
-    static constexpr int DEPTH = 4;                    // chunks in flight
+    // chunks in flight: four for slices of 16 or 32 columns; fewer for wider
+    // slices, whose accumulators take the registers
+    static constexpr int DEPTH = NJ <= 2 ? 4 : (NJ <= 4 ? 3 : 2);
     static constexpr size_t OFF_ST = 0;
     static constexpr size_t OFF_WT = OFF_ST + size_t(DVS) * LDK * 2;
     static constexpr size_t OFF_O = OFF_WT + size_t(DVS) * LDC * 2;               // per O wave: [16][DVS]
     static constexpr size_t TOTAL = OFF_O + size_t(4) * 16 * DVS * sizeof(TOut);
-    static_assert(NJ >= 1 && NJ <= 2 && DV % DVS == 0, "slice width 16 or 32");
+    static_assert((NJ == 1 || NJ == 2 || NJ == 4 || NJ == 8) && DV % DVS == 0, "slice width 16 .. 128");
     static_assert((16 * DVS * sizeof(TOut)) % 16 == 0, "output staging rows");
 };
 
-template <typename TOut, int DV, int DVS>
+// Segments of a long sequence (CHAIN_MAPS, CHAIN_SEG); per (sequence, head) pair
+// bh and segment s, the arrays hold [bh][s][DK][...] fp32.
+struct Seg64 {
+    int L;                  // chunks per segment
+    int nseg;               // segments per (sequence, head)
+    float* E;               // end state from a zero start (segment 0: from S0), [.][.][DK][DV]
+    float* M;               // linear part of the segment's map, [.][.][DK][DK]
+    float* Sst;             // start state of each segment, [.][.][DK][DV]
+};
+
+template <typename TOut, int DV, int DVS, int MODE>
 __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
-    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um) {
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um, Seg64 sg) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
     constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, NSL = Cfg::NSL, LDK = Cfg::LDK, LDC = Cfg::LDC;
     constexpr int D = Cfg::DEPTH;
+    constexpr bool MAPS = MODE == CHAIN_MAPS, OUT = MODE != CHAIN_MAPS;
+    // slices per work item: the maps launch also runs the DK identity columns
+    constexpr int NSLW = MAPS ? (DV + DK) / DVS : NSL;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
     bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
     bf16* sWT = reinterpret_cast<bf16*>(smem + Cfg::OFF_WT);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // Slices of one head share an XCD (workgroups are dealt to the 8 XCDs
-    // round-robin), so the per-chunk operands they all read come from one L2.
-    long bh;
+    // Slices of one work item (a (sequence, head) pair, or one of its segments)
+    // share an XCD (workgroups are dealt to the 8 XCDs round-robin), so the
+    // per-chunk operands they all read come from one L2.
+    long item;
     int sl;
     {
         const long nwg = (long)gridDim.x, id = blockIdx.x;
-        if (!um.cu_seqlens && nwg % (8 * NSL) == 0) {
+        if (!um.cu_seqlens && nwg % (8 * NSLW) == 0) {
             const long xcd = id % 8, local = id / 8;
-            sl = (int)(local % NSL);
-            bh = (local / NSL) * 8 + xcd;
+            sl = (int)(local % NSLW);
+            item = (local / NSLW) * 8 + xcd;
         } else {
-            bh = id / NSL;
-            sl = (int)(id % NSL);
+            item = id / NSLW;
+            sl = (int)(id % NSLW);
         }
     }
-    const int j0 = sl * DVS;
+    // work item -> (sequence, head) pair and segment
+    const int nsegw = MODE == CHAIN_PLAIN ? 1 : (MAPS ? sg.nseg - 1 : sg.nseg);
+    const long bh = item / nsegw;
+    const int seg = (int)(item % nsegw);
+    const bool ident = MAPS && sl >= NSL;                // identity columns (maps launch only)
+    if (ident && seg == 0) return;                       // segment 0 starts from a known state: no M
+    const int j0 = (ident ? sl - NSL : sl) * DVS;        // first column (of the value or the identity block)
     // sequence (batch row, or packed sequence) and head; its chunks and tokens
     const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
     const SeqRange sr = seq_range(um, sq);
-    const int NC = sr.nchunks;
-    auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, n, sr.chunk0); };
+    const int c0 = MODE == CHAIN_PLAIN ? 0 : seg * sg.L;                      // first chunk of the segment
+    const int NC = MODE == CHAIN_PLAIN ? sr.nchunks
+                                       : (sr.nchunks - c0 < sg.L ? sr.nchunks - c0 : sg.L);
+    auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, c0 + n, sr.chunk0); };
 
     const bool wW = wave < 4;                    // uniform per wave
     const int R = wave & 3, ct = wave;
@@ -93,23 +135,27 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     u32x4 fK[D][2];      // Kb^T channel tile ct, 2 k-steps
     u32x4 fG[D];         // gam of this lane's 4 state rows
     // first half: what phase 1 consumes; second half: what phase 2 consumes
+    // In the maps launch the O waves compute nothing: their operand loads repeat
+    // the W waves' (Wk of the same row tile, Kb^T), and identity slices, whose U
+    // is 0, repeat the Wk address for their U loads.
 #define KDA_C64_PREFETCH_1(SL, CH)                                                                  \
     {                                                                                               \
         const long ch_ = (CH);                                                                      \
-        const u32x4* a_ = reinterpret_cast<const u32x4*>((wW ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
+        const u32x4* a_ = reinterpret_cast<const u32x4*>((wW || MAPS ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
                           + R * 4 * 64 + lane;                                                      \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
-        const u32x2* u_ = wW ? reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))          \
-                                   + (R * (DV / 16) + sl * NJ) * 64 + lane                          \
-                             : reinterpret_cast<const u32x2*>(a_);                                  \
-        _Pragma("unroll") for (int j = 0; j < NJ; ++j) fU[SL][j] = u_[wW ? j * 64 : 0];             \
+        const bool uu_ = wW && !ident;                                                              \
+        const u32x2* u_ = uu_ ? reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))         \
+                                    + (R * (DV / 16) + (j0 / 16)) * 64 + lane                       \
+                              : reinterpret_cast<const u32x2*>(a_);                                 \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) fU[SL][j] = u_[uu_ ? j * 64 : 0];            \
     }
 #define KDA_C64_PREFETCH_2(SL, CH)                                                                  \
     {                                                                                               \
         const long ch_ = (CH);                                                                      \
         const u32x4* k_ = reinterpret_cast<const u32x4*>(ws_kb + ch_ * (long)(DK * C)) + ct * 2 * 64 + lane; \
         {                                                                                           \
-            const u32x4* p_ = wW ? k_ : reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
+            const u32x4* p_ = wW || MAPS ? k_ : reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
             fX[SL][0] = p_[0];                                                                      \
             fX[SL][1] = p_[wave >= 6 ? 64 : 0];     /* O waves of row tiles 2, 3 only */          \
         }                                                                                           \
@@ -127,18 +173,28 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     }
 
     // ---- state rows 16*ct + 4(l/16) + e, columns j0 + 16 jt + l%16, fp32 in accumulators
+    // start: the call's initial state (plain; segment 0 of the maps launch), the
+    // segment's start state (outputs launch), zero (other segments' E), the
+    // identity (M)
+    const float* init = MODE == CHAIN_SEG ? sg.Sst + (bh * sg.nseg + seg) * (long)(DK * DV)
+                                          : (MODE == CHAIN_PLAIN || seg == 0 ? (s0 ? s0 + bh * (long)(DK * DV) : nullptr)
+                                                                             : nullptr);
     floatx4 accS[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
         accS[jt] = zero4();
-        if (s0) {
+        if (ident) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                accS[jt][e] = s0[(bh * DK + ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr];
+                accS[jt][e] = (ct * 16 + 4 * (lane >> 4) + e == j0 + jt * 16 + fr) ? 1.f : 0.f;
+        } else if (init) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                accS[jt][e] = init[(ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr];
         }
     }
     // S^T as the B operand of Qt S and Wk S: sST[j][c], 4 consecutive c per lane
-    auto write_state_operand = [&]() {
+    auto write_state_operand = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
             bf16x4 v4;
@@ -150,7 +206,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     write_state_operand();
 
     // one chunk n whose operands sit in register slot d
-    auto step = [&](auto DI, int n) {
+    auto step = [&](auto DI, int n) __attribute__((always_inline)) {
         constexpr int d = DI;
         __syncthreads();                                            // S^T of chunk n's start state
 
@@ -158,13 +214,15 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         floatx4 acc[NJ];
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) acc[jt] = zero4();
+        if (OUT || wW) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bf16x8 fa = __builtin_bit_cast(bf16x8, fA[d][u]);
+            for (int u = 0; u < 4; ++u) {
+                const bf16x8 fa = __builtin_bit_cast(bf16x8, fA[d][u]);
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) {
-                const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sST + (jt * 16 + fr) * LDK + u * 32 + fk);
-                acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[jt], 0, 0, 0);
+                for (int jt = 0; jt < NJ; ++jt) {
+                    const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sST + (jt * 16 + fr) * LDK + u * 32 + fk);
+                    acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[jt], 0, 0, 0);
+                }
             }
         }
         if (wW) {
@@ -173,7 +231,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
                 const bf16x4 uu = __builtin_bit_cast(bf16x4, fU[d][jt]);
                 bf16x4 w4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w4[e] = (bf16)((float)uu[e] - acc[jt][e]);
+                for (int e = 0; e < 4; ++e) w4[e] = (bf16)((ident ? 0.f : (float)uu[e]) - acc[jt][e]);
                 *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
             }
         }
@@ -181,7 +239,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         __syncthreads();                                            // W^T complete
 
         // ---- phase 2: O waves O += P W (stored); all waves S = gam S + Kb^T W
-        if (!wW) {
+        if (OUT && !wW) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 if (u == 1 && R < 2) break;                         // P is lower triangular
@@ -201,7 +259,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
 #pragma unroll
             for (int u = lane; u < NUO; u += 64) {
                 const int r = u / PPR, jj = (u % PPR) * EO;
-                const int tt = n * C + R * 16 + r;
+                const int tt = (c0 + n) * C + R * 16 + r;
                 if (sr.tok_begin + tt < sr.tok_end)
                     *reinterpret_cast<u32x4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj) =
                         *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
@@ -234,29 +292,90 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         if (n0 + DI < NC) step(DI, n0 + DI);
     });
 
-    if (sT) {
+    // end state: the call's final state (plain; the last segment of the outputs
+    // launch), or the segment's E or M (maps launch)
+    float* fin = nullptr;
+    long ld = DV;
+    if constexpr (MAPS) {
+        fin = ident ? sg.M + (bh * sg.nseg + seg) * (long)(DK * DK) : sg.E + (bh * sg.nseg + seg) * (long)(DK * DV);
+        ld = ident ? DK : DV;
+    } else if (MODE == CHAIN_PLAIN || seg == sg.nseg - 1) {
+        fin = sT ? sT + bh * (long)(DK * DV) : nullptr;
+    }
+    if (fin) {
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sT[(bh * DK + ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr] = accS[jt][e];
+                fin[(ct * 16 + 4 * (lane >> 4) + e) * ld + j0 + jt * 16 + fr] = accS[jt][e];
+    }
+}
+
+// Start states of the segments from their maps: Sst_0 = S0 (zeros when NULL),
+// Sst_1 = E_0 (segment 0 ran from S0 itself), Sst_{s+1} = M_s Sst_s + E_s.
+// One workgroup per ((sequence, head), 16 value columns); thread t holds column
+// t % 16 of DK/16 rows; the sum over the DK channels runs in a fixed order in
+// fp32.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void chain_seg_scan_kernel(const float* __restrict__ s0, Seg64 sg) {
+    constexpr int RPT = DK / 16;
+    __shared__ float sS[DK][16];
+    const int cb = (int)(blockIdx.x % (DV / 16));
+    const long bh = blockIdx.x / (DV / 16);
+    const int tid = threadIdx.x, j = tid & 15, r0 = (tid >> 4) * RPT, col = cb * 16 + j;
+    const long base = bh * sg.nseg;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = r0 + i;
+        const float x = s0 ? s0[(bh * DK + r) * (long)DV + col] : 0.f;
+        sS[r][j] = x;
+        sg.Sst[(base * DK + r) * (long)DV + col] = x;
+    }
+    __syncthreads();
+    for (int s = 1; s < sg.nseg; ++s) {
+        const float* E = sg.E + (base + s - 1) * (long)(DK * DV);
+        const float* M = sg.M + (base + s - 1) * (long)(DK * DK);
+        float acc[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = r0 + i;
+            float a = 0.f;
+            if (s > 1) {
+                for (int c = 0; c < DK; c += 4) {
+                    const float4 m4 = *reinterpret_cast<const float4*>(M + r * DK + c);
+                    a = fmaf(m4.x, sS[c][j], a);
+                    a = fmaf(m4.y, sS[c + 1][j], a);
+                    a = fmaf(m4.z, sS[c + 2][j], a);
+                    a = fmaf(m4.w, sS[c + 3][j], a);
+                }
+            }
+            acc[i] = a + E[r * DV + col];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            sS[r0 + i][j] = acc[i];
+            sg.Sst[((base + s) * DK + r0 + i) * (long)DV + col] = acc[i];
+        }
+        __syncthreads();
     }
 }
 
 #undef KDA_C64_PREFETCH_1
 #undef KDA_C64_PREFETCH_2
 
-template <typename TOut, int DV, int DVS>
-static hipError_t launch_chain64_dvs(const ChunkArgs& a) {
+template <typename TOut, int DV, int DVS, int MODE>
+static hipError_t launch_chain64_mode(const ChunkArgs& a, long items, const Seg64& sg) {
     constexpr int C = 64, DK = 128;
-    const long nwg = seq_head_count(a) * (DV / DVS);
+    constexpr int NSLW = MODE == CHAIN_MAPS ? (DV + DK) / DVS : DV / DVS;
+    const long nwg = items * NSLW;
     if (nwg == 0) return hipSuccess;
     const WsLayout w = ws_layout_of(a);
     char* ws = (char*)a.ws;
-    hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS, MODE>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                        (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
                        (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam),
-                       a.s0, (TOut*)a.o, a.sT, unit_map(a));
+                       a.s0, (TOut*)a.o, a.sT, unit_map(a), sg);
     return hipGetLastError();
 }
 
@@ -264,8 +383,24 @@ static hipError_t launch_chain64_dvs(const ChunkArgs& a) {
 template <typename TOut, int DV>
 static hipError_t launch_chain64(const ChunkArgs& a) {
     const long bh = seq_head_count(a);
-    if (bh * (DV / 32) >= 256) return launch_chain64_dvs<TOut, DV, 32>(a);
-    return launch_chain64_dvs<TOut, DV, 16>(a);
+    const SegPlan plan = seg_plan_of(a);
+    if (plan.nseg > 1) {
+        // segments: maps of all but the last, their scan, then every segment's outputs
+        constexpr int DVS = SEG_DVS < DV ? SEG_DVS : DV;
+        const WsLayout w = ws_layout_of(a);
+        char* ws = (char*)a.ws;
+        Seg64 sg{plan.L, plan.nseg, (float*)(ws + w.seg_e), (float*)(ws + w.seg_m), (float*)(ws + w.seg_s)};
+        hipError_t e = launch_chain64_mode<TOut, DV, DVS, CHAIN_MAPS>(a, bh * (plan.nseg - 1), sg);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((chain_seg_scan_kernel<128, DV>), dim3((unsigned)(bh * (DV / 16))), dim3(256), 0,
+                           a.stream, a.s0, sg);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_chain64_mode<TOut, DV, DVS, CHAIN_SEG>(a, bh * plan.nseg, sg);
+    }
+    const Seg64 none{0, 1, nullptr, nullptr, nullptr};
+    if (bh * (DV / 32) >= 256) return launch_chain64_mode<TOut, DV, 32, CHAIN_PLAIN>(a, bh, none);
+    return launch_chain64_mode<TOut, DV, 16, CHAIN_PLAIN>(a, bh, none);
 }
 
 hipError_t run_chunk_chain64(const ChunkArgs& a) {

@@ -1042,18 +1042,51 @@ static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_
     w.p = off;  off = al256(off + nch * C * C * es);
     w.u = off;  off = al256(off + nch * C * dv * (hot_config(in_bf16, dk, C) && !generic ? 2 : 4));
     w.gam = off; off = al256(off + nch * dk * 4);
+    w.seg_e = w.seg_m = w.seg_s = off;
     w.total = off;
     return w;
 }
 
+// Segments for the hot chain.  The plain chain runs one workgroup per (sequence,
+// head, 32 value columns); when those number fewer than the 256 CUs and the
+// sequence is long, the chunks are cut into segments of at least SEG_MIN_CHUNKS
+// so that about SEG_TARGET_WG workgroups of SEG_DVS columns run the outputs.
+SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
+    const int NC = (T + C - 1) / C;
+    SegPlan p{NC, 1};
+    if (!hot_config(in_bf16, dk, C) || generic || NC < 2 * SEG_MIN_CHUNKS) return p;
+    const long bh = (long)B * H;
+    if (bh == 0 || bh * (dv / 32) >= 256) return p;
+    const long nsl = dv / (SEG_DVS < dv ? SEG_DVS : dv);
+    long nseg = (SEG_TARGET_WG + bh * nsl - 1) / (bh * nsl);
+    if (nseg > NC / SEG_MIN_CHUNKS) nseg = NC / SEG_MIN_CHUNKS;
+    if (nseg < 2) return p;
+    const int L = (int)((NC + nseg - 1) / nseg);
+    return SegPlan{L, (NC + L - 1) / L};
+}
+
+SegPlan seg_plan_of(const ChunkArgs& a) {
+    if (a.cu_seqlens) return SegPlan{0, 1};
+    return seg_plan(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.generic);
+}
+
 WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
     const size_t NC = (size_t)((T + C - 1) / C);
-    return layout_units((size_t)B * H * NC, 0, dk, dv, in_bf16, C, generic);
+    WsLayout w = layout_units((size_t)B * H * NC, 0, dk, dv, in_bf16, C, generic);
+    const SegPlan sp = seg_plan(B, T, H, dk, dv, in_bf16, C, generic);
+    if (sp.nseg > 1) {
+        const size_t items = (size_t)B * H * sp.nseg;
+        w.seg_e = w.total;
+        w.seg_m = al256(w.seg_e + items * dk * dv * 4);
+        w.seg_s = al256(w.seg_m + items * dk * dk * 4);
+        w.total = al256(w.seg_s + items * dk * dv * 4);
+    }
+    return w;
 }
 
 WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
     const size_t chunks = (size_t)((T + C - 1) / C) + (size_t)N;
-    return layout_units(chunks * H, ((size_t)N + 1) * 4, dk, dv, in_bf16, C, generic);
+    return layout_units(chunks * H, 2 * ((size_t)N + 1) * 4, dk, dv, in_bf16, C, generic);   // cu_chunks, cu_tok
 }
 
 WsLayout ws_layout_of(const ChunkArgs& a) {
@@ -1068,6 +1101,7 @@ UnitMap unit_map(const ChunkArgs& a) {
     m.BH = (long)a.B * a.H;
     m.cu_seqlens = a.cu_seqlens;
     m.cu_chunks = a.cu_seqlens ? reinterpret_cast<const int*>((const char*)a.ws + ws_layout_of(a).cu) : nullptr;
+    m.cu_tok = m.cu_chunks ? m.cu_chunks + (a.N + 1) : nullptr;
     m.nseq = a.N;
     return m;
 }
@@ -1079,35 +1113,51 @@ long unit_count(const ChunkArgs& a) {
 
 long seq_head_count(const ChunkArgs& a) { return (long)(a.cu_seqlens ? a.N : a.B) * a.H; }
 
-// Chunk offsets of a packed batch: cu_chunks[s] = sum over s' < s of the chunk
-// count of sequence s' (its clamped token range, rounded up to chunks).
-// One workgroup of 1024 threads, in blocks of 1024 sequences.
+// Offsets of a packed batch.  cu_tok[i] = min(T, max(0, cu_seqlens[0..i])) for
+// i = 0..N: a running maximum, so sequence s = [cu_tok[s], cu_tok[s+1]) never
+// overlaps another and the lengths sum to at most T.  cu_chunks[0] = 0 and
+// cu_chunks[s+1] = cu_chunks[s] + ceil(length of s / C).  One workgroup of 1024
+// threads walks the N+1 offsets in blocks of 1024, carrying the running maximum
+// and the chunk sum from block to block.
 __global__ __launch_bounds__(1024) void packed_chunks_kernel(const int* __restrict__ cu_seqlens, int nseq,
-                                                             int T_len, int C, int* __restrict__ cu_chunks) {
+                                                             int T_len, int C, int* __restrict__ cu_chunks,
+                                                             int* __restrict__ cu_tok) {
+    __shared__ int sm[1024];
     __shared__ int sc[1024];
-    __shared__ int carry;
+    __shared__ int carry_max, carry_sum;
     const int tid = threadIdx.x;
-    if (tid == 0) { carry = 0; cu_chunks[0] = 0; }
+    if (tid == 0) { carry_max = 0; carry_sum = 0; }
     __syncthreads();
-    for (int base = 0; base < nseq; base += 1024) {
-        const int s = base + tid;
-        int c = 0;
-        if (s < nseq) {
-            const long b0 = clamp_tok(cu_seqlens[s], 0, T_len);
-            const long e0 = clamp_tok(cu_seqlens[s + 1], b0, T_len);
-            c = (int)((e0 - b0 + C - 1) / C);
-        }
-        sc[tid] = c;
+    for (int base = 0; base <= nseq; base += 1024) {
+        const int i = base + tid;
+        const bool in = i <= nseq;
+        const int prev_last = carry_max;                      // clamped offset of index base - 1 (0 at start)
+        sm[tid] = in ? (int)clamp_tok(cu_seqlens[i], 0, T_len) : 0;
         __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {        // inclusive scan
+        for (int off = 1; off < 1024; off <<= 1) {            // inclusive running maximum
+            const int x = tid >= off ? sm[tid - off] : 0;
+            __syncthreads();
+            sm[tid] = sm[tid] > x ? sm[tid] : x;
+            __syncthreads();
+        }
+        const int m = sm[tid] > prev_last ? sm[tid] : prev_last;
+        const int mp = tid > 0 ? (sm[tid - 1] > prev_last ? sm[tid - 1] : prev_last) : prev_last;
+        // chunks of sequence i - 1 (index 0 ends no sequence)
+        sc[tid] = (in && i >= 1) ? (m - mp + C - 1) / C : 0;
+        if (in) cu_tok[i] = m;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {            // inclusive sum
             const int x = tid >= off ? sc[tid - off] : 0;
             __syncthreads();
             sc[tid] += x;
             __syncthreads();
         }
-        if (s < nseq) cu_chunks[s + 1] = carry + sc[tid];
+        if (in) cu_chunks[i] = carry_sum + sc[tid];
         __syncthreads();
-        if (tid == 0) carry += sc[1023];
+        if (tid == 0) {
+            carry_sum += sc[1023];
+            carry_max = sm[1023] > prev_last ? sm[1023] : prev_last;
+        }
         __syncthreads();
     }
 }
@@ -1187,7 +1237,7 @@ hipError_t run_chunk_intra(const ChunkArgs& a) {
     if (a.cu_seqlens && a.N > 0) {
         int* cu_chunks = reinterpret_cast<int*>((char*)a.ws + ws_layout_of(a).cu);
         hipLaunchKernelGGL(packed_chunks_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.N, a.T,
-                           a.C, cu_chunks);
+                           a.C, cu_chunks, cu_chunks + (a.N + 1));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -234,9 +234,11 @@ static void launch_decode_nt(const DecodeArgs& a) {
 
 template <typename TIn, typename TOut, int DK, int DV>
 static hipError_t launch_decode(const DecodeArgs& a) {
-    if (a.T == 1) launch_decode_nt<TIn, TOut, DK, DV, 1024, false>(a);
-    else if (a.T == 2) launch_decode_nt<TIn, TOut, DK, DV, 512, true>(a);
-    else launch_decode_nt<TIn, TOut, DK, DV, 256, true>(a);
+    switch (decode_block_threads(a.T)) {
+        case 1024: launch_decode_nt<TIn, TOut, DK, DV, 1024, false>(a); break;
+        case 512: launch_decode_nt<TIn, TOut, DK, DV, 512, true>(a); break;
+        default: launch_decode_nt<TIn, TOut, DK, DV, 256, true>(a); break;
+    }
     return hipGetLastError();
 }
 

@@ -56,9 +56,22 @@ inline bool hot_config(bool in_bf16, int dk, int C) { return in_bf16 && dk == 12
 // chunk-major unit id n * (B*H) + (b*H + h); per unit
 //   Qt [C][dk] in, Wk [C][dk] in, Kb^T [dk][C] in, P [C][C] in, U [C][dv], gam [dk] fp32
 // with U in fp32, except in the hot configuration (bf16)
+// Fixed-length batches whose chain would run on too few workgroups (long
+// sequences, few heads) in the hot configuration also hold, per (sequence,
+// head) pair and segment, the segment-affine chain's E, M and start states
+// (fp32 [DK][DV], [DK][DK], [DK][DV]); seg_* are 0-sized otherwise.
 struct WsLayout {
-    size_t cu, qt, wk, kb, p, u, gam, total;   // byte offsets of each array, total bytes
+    size_t cu, qt, wk, kb, p, u, gam, seg_e, seg_m, seg_s, total;   // byte offsets of each array, total bytes
 };
+// Segments of the hot chain: nseg segments of L chunks per (sequence, head);
+// nseg = 1 is the plain sequential chain.
+struct SegPlan {
+    int L, nseg;
+};
+SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic);
+constexpr int SEG_DVS = 128;         // value columns per workgroup of the segmented chain
+constexpr int SEG_TARGET_WG = 256;   // segments enough for this many output workgroups
+constexpr int SEG_MIN_CHUNKS = 32;   // no segment shorter than this
 // generic = true: the format of the generic kernels even in the hot configuration
 WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic = false);
 // Packed variable-length batch of N sequences, T tokens in all: room for every
@@ -66,6 +79,7 @@ WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, boo
 WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic = false);
 // The layout for a call's arguments (fixed-length or packed).
 WsLayout ws_layout_of(const ChunkArgs& a);
+SegPlan seg_plan_of(const ChunkArgs& a);
 
 // True when an instantiation exists for these sizes (dk, dv, C, dtype).
 bool chunk_supported(int dk, int dv, int C, bool in_bf16);
@@ -115,6 +129,9 @@ hipError_t run_pre_bwd_inputs(const PreBwdArgs& p);
 hipError_t run_pre_bwd_grads(const PreBwdArgs& p);
 
 hipError_t run_decode_step(const DecodeArgs& a);
+// Threads per decode workgroup for T tokens per call (one workgroup per
+// (sequence, head)), as measured: 1024 for one token, 512 for two, 256 from three on.
+inline int decode_block_threads(int T) { return T == 1 ? 1024 : (T == 2 ? 512 : 256); }
 hipError_t run_chunk_intra(const ChunkArgs& a);
 hipError_t run_chunk_chain(const ChunkArgs& a);
 

@@ -101,7 +101,8 @@ def test_chunk_validation_codes(fn):
         (dict(dk=96), UNSUP), (dict(dv=32), UNSUP), (dict(C=48), UNSUP), (dict(C=256), UNSUP),
         (dict(ind=5), UNSUP), (dict(outd=-1), UNSUP),
         (dict(q=None), NULL), (dict(beta=None), NULL), (dict(o=None), NULL),
-        (dict(k=a["k"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(s0=a["s0"] + 2), MISAL),
+        (dict(k=a["k"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(g=a["g"] + 8), MISAL),
+        (dict(s0=a["s0"] + 2), MISAL),
         (dict(ws=a["ws"] + 8), MISAL), (dict(o=a["o"] + 4), MISAL),
         (dict(ws=None), WS), (dict(wsb=a["wsb"] - 1), WS),
         (dict(o=a["q"]), ALIAS), (dict(o=a["ws"]), ALIAS), (dict(sT=a["v"]), ALIAS),
@@ -124,7 +125,8 @@ def test_gate_layout_codes(fn):
     cases = [
         (dict(), 3, UNSUP), (dict(), -1, UNSUP),
         (dict(g=None), CH, NULL), (dict(g=None), HEAD, NULL), (dict(g=None), NONE, HIP),
-        (dict(g=a["g"] + 4), CH, MISAL), (dict(g=a["g"] + 4), HEAD, HIP), (dict(g=a["g"] + 2), HEAD, MISAL),
+        (dict(g=a["g"] + 4), CH, MISAL), (dict(g=a["g"] + 8), CH, MISAL), (dict(g=a["g"] + 16), CH, HIP),
+        (dict(g=a["g"] + 4), HEAD, HIP), (dict(g=a["g"] + 2), HEAD, MISAL),
         (dict(g=a["g"] + 2), NONE, HIP),                     # g is not read without gates
         (dict(g=a["ws"] - tok * 4), HEAD, HIP),              # a per-head g is [B,T,H] only
         (dict(g=a["ws"] - tok * 4), CH, ALIAS), (dict(g=a["ws"]), NONE, HIP),
@@ -186,6 +188,16 @@ def test_decode_validation_codes():
     if not HAS_GPU:
         assert call(a) == HIP
 
+    def sized(n, T=1):
+        g = Fake()
+        return dict(q=g(n * T * dk * 2), k=g(n * T * dk * 2), v=g(n * T * dv * 2), g=g(n * T * dk * 4),
+                    beta=g(n * T * 4), state=g(n * dk * dv * 4), o=g(n * T * dv * 2),
+                    N=n, T=T, H=1, dk=dk, dv=dv, ind=_lib.BF16, outd=_lib.BF16)
+    # one token per call: 1024-thread workgroups, so 2^22 pairs are 2^32 work-items
+    assert call(sized(4194304)) == SHAPE
+    if not HAS_GPU:
+        assert call(sized(4194303)) == HIP              # the largest single-token grid
+
     def call_ex(x, gate):
         return L.kda_decode_step_ex(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], x["o"],
                                     x["N"], x["H"], x["dk"], x["dv"], x["ind"], x["outd"], None, gate)
@@ -214,6 +226,9 @@ def test_decode_validation_codes():
     assert L.kda_decode_tokens(None, None, None, None, None, None, None, 3, 0, 2, 64, 64, 0, 0, None, 0) == OK
     if not HAS_GPU:
         assert call_t(t) == HIP
+        # several tokens per call run 256-thread workgroups: 2^22 pairs still fit
+        assert call_t(sized(4194304, T)) == HIP
+    assert call_t(sized(1 << 24, T)) == SHAPE
 
 
 def test_python_binding_refuses_cpu_tensors():
@@ -327,7 +342,8 @@ def test_backward_validation_codes():
                                x["H"], x["dkk"], x["dvv"], x["ind"], x["ws"], x["wsb"], None, x["C"], x["gate"])
     cases = [(dict(T=-1), SHAPE), (dict(dkk=96), UNSUP), (dict(C=128), UNSUP), (dict(ind=7), UNSUP),
              (dict(gate=5), UNSUP), (dict(dq=None), NULL), (dict(dO=None), NULL), (dict(dg=None), NULL),
-             (dict(q=a["q"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(dbeta=a["dbeta"] + 2), MISAL),
+             (dict(q=a["q"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(g=a["g"] + 8), MISAL),
+             (dict(dbeta=a["dbeta"] + 2), MISAL),
              (dict(ws=None), WS), (dict(wsb=wsb - 1), WS),
              (dict(dq=a["q"]), ALIAS), (dict(dk=a["dq"] + 256), ALIAS), (dict(dS0=a["dST"]), ALIAS),
              (dict(ws=a["dO"]), ALIAS), (dict(dg=a["ws"]), ALIAS)]

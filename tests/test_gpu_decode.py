@@ -64,8 +64,10 @@ def test_decode_alpha_zero_and_beta_zero():
 
 
 def test_decode_full_size_1000_steps():
-    """256 sequences x 32 heads x 128x128 states, 1000 consecutive steps; the
-    oracle follows 12 sampled (sequence, head) states through all 1000 steps."""
+    """256 sequences x 32 heads x 128x128 states, 1000 consecutive steps.  The
+    oracle checks every one of the 8192 states after steps 1 and 10 and every
+    output of the first 10 steps, and follows 12 sampled (sequence, head)
+    states through all 1000 steps."""
     w = inputs.WORKLOADS["decode"]
     steps = w.steps
     _say(f"decode full size: generating {steps} steps of inputs")
@@ -78,14 +80,29 @@ def test_decode_full_size_1000_steps():
     dg = cuda(d)
     sel = (torch.as_tensor(seqs).cuda(), torch.as_tensor(heads).cuda())
     o_hist = torch.empty((steps, 12, w.dv), dtype=torch.bfloat16, device="cuda")
-    snaps = {}
+    snaps, full, o_first = {}, {}, []
     _say("decode full size: running 1000 steps")
     for s in range(steps):
         o = decode_step(dg["q"][s], dg["k"][s], dg["v"][s], dg["g"][s], dg["beta"][s], S)
         o_hist[s] = o[sel]
+        if s < 10:
+            o_first.append(o.cpu())
+        if s + 1 in (1, 10):
+            full[s + 1] = S.cpu()
         if s + 1 in (1, 10, 100, 1000):
             snaps[s + 1] = S[sel].cpu()
     torch.cuda.synchronize()
+    _say("decode full size: oracle on all 8192 states, steps 1 and 10")
+    for upto in (1, 10):
+        o_ref, S_ref = _oracle_steps(d["q"][:upto], d["k"][:upto], d["v"][:upto], d["g"][:upto],
+                                     d["beta"][:upto], S0)
+        es = assert_close(f"all S@{upto}", full[upto], S_ref, TOL[torch.bfloat16])
+        eo = assert_close(f"all o, steps 1..{upto}", torch.stack(o_first[:upto]).transpose(0, 1), o_ref,
+                          TOL[torch.bfloat16])
+        assert_close(f"all S@{upto} (fp32 path)", full[upto], S_ref, 1e-4)
+        _say(f"  step {upto}: max err S {es:.2e}, o {eo:.2e} over 8192 states")
+        del o_ref, S_ref
+    del full
     _say("decode full size: oracle on sampled states")
     pick = lambda x: x[:, seqs, heads][:, :, None]           # [steps, 12, 1, d]
     S0s = S0[seqs, heads][:, None]

@@ -1,0 +1,76 @@
+"""The segment-affine chain on the GPU: long sequences with few (sequence, head)
+pairs, where the sequential chain alone would occupy only a few CUs.
+
+Each sequence is cut into segments whose affine maps S -> M S + E are composed
+first; every segment then runs from its true start state.  That regroups the
+chunk recurrence (chunk paragraph of the KimiK3 essay; sections 十五 and 十六 of
+the explainer: the state after a chunk is an affine function of the state
+before it), so the result is the oracle's up to rounding.  Checked here: every
+output and final state against the fp64 oracle, a packed call on the same
+tokens (packed batches run the plain sequential chain) at the same bar,
+bitwise reruns and an in-place final state."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_sequence_chunk_amd import _lib, chunk_fwd, chunk_fwd_varlen, inputs
+from tests.parity import TOL, assert_close, cuda
+
+pytestmark = pytest.mark.gpu
+
+# B, H, T, dv, out dtype, gates, S0 std
+CASES = [
+    (1, 2, 16384 + 37, 128, torch.bfloat16, "tiny", 0.05),
+    (2, 1, 8192 + 64, 64, torch.bfloat16, "tiny", 0.0),
+    (1, 3, 12000, 128, torch.float32, "none", 0.02),       # alpha = 1: M is not damped by decay
+    (1, 1, 4096, 128, torch.bfloat16, "scalar", 0.05),      # 64 chunks: two segments
+    (3, 2, 9000, 128, torch.bfloat16, "long", 0.01),
+]
+
+
+def _segmented(B, T, H, dv):
+    """The segmented chain's extra workspace appears exactly when it is used."""
+    L = _lib.lib()
+    per_pair = lambda b, h: L.kda_chunk_fwd_workspace_bytes(b, T, h, 128, dv, _lib.BF16, 64) / (b * h)
+    # 256 workgroups of 32 value columns fill the GPU: no segments there;
+    # segments add E, M and a start state (at least 96 KB) per pair and segment
+    full = 256 * 32 // dv
+    return per_pair(B, H) > per_pair(1, full) + 65536
+
+
+@pytest.mark.parametrize("B,H,T,dv,out_dtype,gates,s0", CASES)
+def test_segmented_chain(B, H, T, dv, out_dtype, gates, s0):
+    print(f"segments B={B} H={H} T={T} dv={dv} {out_dtype} gates={gates}", flush=True)
+    assert _segmented(B, T, H, dv)
+    d = inputs.custom_prefill(61 + T, B, T, H, 128, dv, dtype=torch.bfloat16, gates=gates, s0_std=s0)
+    dg = cuda(d)
+    o, S = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], dg["S0"], chunk_size=64, out_dtype=out_dtype)
+    o2, S2 = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], dg["S0"], chunk_size=64, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2), "reruns differ"
+
+    # in place: the final state overwrites the initial state
+    if dg["S0"] is not None:
+        S_io = dg["S0"].clone()
+        o3, S3 = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], S_io, chunk_size=64,
+                           out_dtype=out_dtype, final_state=S_io)
+        torch.cuda.synchronize()
+        assert torch.equal(o3, o) and torch.equal(S3, S), "in-place call differs"
+
+    # the plain sequential chain on the same tokens: one packed batch of the B rows
+    pk = lambda x: x.reshape((B * T,) + tuple(x.shape[2:])).contiguous()
+    cu = torch.arange(0, B * T + 1, T, dtype=torch.int32, device="cuda:0")
+    op, Sp = chunk_fwd_varlen(pk(dg["q"]), pk(dg["k"]), pk(dg["v"]), pk(dg["g"]), pk(dg["beta"]), cu,
+                              dg["S0"], chunk_size=64, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+
+    o_ref, S_ref = oracle.recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"])
+    tol = TOL[torch.bfloat16]
+    eo = assert_close("o", o.cpu(), o_ref, tol)
+    es = assert_close("S", S.cpu(), S_ref, tol)
+    eop = assert_close("o (sequential chain)", op.cpu().reshape(o.shape), o_ref, tol)
+    esp = assert_close("S (sequential chain)", Sp.cpu(), S_ref, tol)
+    assert_close("o segmented vs sequential", o.cpu(), op.cpu().reshape(o.shape), tol)
+    assert_close("S segmented vs sequential", S.cpu(), Sp.cpu(), tol)
+    print(f"  segmented: o {eo:.2e} S {es:.2e};  sequential: o {eop:.2e} S {esp:.2e}", flush=True)
