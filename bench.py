@@ -2,11 +2,13 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-extras]
 
-A step is one kda_chunk_fwd call (intra-chunk stage + chain stage) over the mid
-prefill workload: B=4, H=16, T=8192, d_k=d_v=128, C=64, bf16 q/k/v, fp32 g/beta
-and state, per-channel gates (seeded synthetic inputs, resident in HBM before
-timing).  Prints one JSON line.  The decode step (256 sequences x 32 heads,
-in-place 128x128 fp32 states) is measured as well and reported under "decode".
+A step is one kda_chunk_fwd call (intra-chunk stage + chain stage) over the
+1M-token prefill workload: B=1, H=16, T=1,048,576, d_k=d_v=128, C=64, bf16 q/k/v,
+fp32 g/beta and state, recurring address keys, fast/slow channel gates (seeded
+synthetic inputs, resident in HBM before timing).  Prints one JSON line.  The
+mid (B=4, H=16, T=8192, C=64) and long (B=1, H=32, T=65536, C=128) prefill
+workloads are timed as well ("workloads"), and the decode step (256 sequences x
+32 heads, in-place 128x128 fp32 states) is reported under "decode".
 """
 from __future__ import annotations
 
@@ -24,10 +26,10 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 CSRC = os.path.join(ROOT, "linear_attention_sequence_chunk_amd", "csrc")
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a
 # plain copy of known size); valid only while the kernel's sources are unchanged
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mid_prefill.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_1m_prefill.txt")
 # MFMA counters per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES,
 # GRBM_GUI_ACTIVE), under the same rule
-MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_valu_mid_prefill.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_valu_1m_prefill.txt")
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 SIMDS = 1024                # 256 CUs x 4
 XCDS = 8                    # GRBM_GUI_ACTIVE is summed over them
@@ -42,14 +44,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="mid")
+    p.add_argument("--workload", default="1m")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="only the headline workload: no mid and long prefill lines")
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-extras", action="store_true",
                    help="only the step (and decode): no gate-layout, fused, varlen or backward lines")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="only run a plain 512 MiB device copy (to scale FETCH_SIZE/WRITE_SIZE counters)")
+                   help="only run a plain 4 GiB device copy (to scale FETCH_SIZE/WRITE_SIZE counters)")
     p.add_argument("--survey", action="store_true",
                    help="only time the prefill step of other head sizes, chunk sizes and dtypes "
                         "(one JSON line each)")
@@ -89,6 +93,7 @@ def measured_mfma(kernel, seconds):
     cycles), the rate at the live duration; None when absent or stale."""
     if kernel not in KERNEL_SOURCES or not os.path.exists(MFMA_FILE):
         return None
+    src = os.path.relpath(MFMA_FILE, ROOT)
     digest = source_digest(KERNEL_SOURCES[kernel])
     with open(MFMA_FILE) as f:
         for line in f:
@@ -103,7 +108,7 @@ def measured_mfma(kernel, seconds):
             tflops = flops / seconds / 1e12
             return {"kernel": kernel, "flops_per_launch": round(flops), "tflops": round(tflops, 1),
                     "frac_bf16_peak": round(tflops / MFMA_PEAK_TFLOPS, 4), "busy_pct": round(100 * busy, 2),
-                    "source": "profiles/mfma_valu_mid_prefill.txt"}
+                    "source": src}
     return None
 
 
@@ -118,9 +123,81 @@ def mfma_summary(names, t_intra, t_chain, t_step):
             "step_frac_bf16_peak": round(step / MFMA_PEAK_TFLOPS, 4)}
 
 
+def mfma_summary_segmented(t_intra, t_step):
+    """bf16 MFMA work of the intra kernel from the committed counters when the
+    chain runs in segments (its kernels have no counter lines of their own)."""
+    intra = measured_mfma("chunk_intra64_kernel", t_intra)
+    return None if intra is None else {"intra": intra}
+
+
 def prefill_bytes_per_token_head(dk, dv, in_bytes, out_bytes):
     """Bytes the method has to move per (token, head): q, k, v in, g, beta in, o out."""
     return (2 * dk + dv) * in_bytes + dk * 4 + 4 + dv * out_bytes
+
+
+def device_inputs(torch, inputs, w, dev, t0=0, t1=None):
+    """A workload's inputs for tokens [t0, t1), generated block by block on the
+    host and copied into device tensors (a few GB at a time for the 1M workload)."""
+    t1 = w.T if t1 is None else t1
+    Tn = t1 - t0
+    sd = w.torch_dtype
+    g = {"q": torch.empty((w.B, Tn, w.H, w.dk), dtype=sd, device=dev),
+         "k": torch.empty((w.B, Tn, w.H, w.dk), dtype=sd, device=dev),
+         "v": torch.empty((w.B, Tn, w.H, w.dv), dtype=sd, device=dev),
+         "g": torch.empty((w.B, Tn, w.H, w.dk), dtype=torch.float32, device=dev),
+         "beta": torch.empty((w.B, Tn, w.H), dtype=torch.float32, device=dev)}
+    piece = 1 << 16
+    for a in range(t0, t1, piece):
+        b = min(t1, a + piece)
+        d = inputs.make_prefill(w, t0=a, t1=b)
+        for n in ("q", "k", "v", "g", "beta"):
+            g[n][:, a - t0:b - t0].copy_(d[n])
+    S0 = inputs.make_state(w)
+    g["S0"] = None if S0 is None else S0.to(dev)
+    return g
+
+
+def time_step(torch, plan, steps, warmup):
+    """Warm-up steps, then ``steps`` timed steps with HIP events on the launch
+    stream around each stage: (mean step ms, mean intra ms, mean chain ms, host ms)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t_host0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        plan.intra()
+        ev[i][1].record(stream)
+        plan.chain()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_host = (time.perf_counter() - t_host0) / steps * 1e3
+    intra = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)) / steps
+    chain = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)) / steps
+    step = sum(ev[i][0].elapsed_time(ev[i][2]) for i in range(steps)) / steps
+    return step, intra, chain, t_host
+
+
+def alg_bytes(w, has_s0):
+    """Algorithmic bytes of one call (intra stage, chain stage): q, k, v, g, beta
+    read once; o written once, the initial state read (when given) and the
+    final state written."""
+    units = w.B * w.T * w.H                          # token-heads
+    ib = 2 if w.dtype == "bf16" else 4
+    state = w.B * w.H * w.dk * w.dv * 4
+    intra = units * ((2 * w.dk + w.dv) * ib + w.dk * 4 + 4)
+    chain = units * (w.dv * ib) + (2 if has_s0 else 1) * state
+    return intra, chain
+
+
+def workload_label(w):
+    keys = ", recurring address keys" if w.keys == "address" else ""
+    gates = {"tiny": "channel gates", "long": "fast/slow channel gates", "none": "no gate",
+             "scalar": "per-head gates"}[w.gates]
+    return (f"{w.name} prefill B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} C={w.C} "
+            f"{'bf16' if w.dtype == 'bf16' else 'fp32'} q/k/v, fp32 g/beta/state, {gates}{keys}")
 
 
 def main():
@@ -136,7 +213,7 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
-        n = 512 << 20
+        n = 4 << 30          # 16x the 256 MB memory-side cache: every byte comes from HBM
         x = torch.ones(n // 4, dtype=torch.float32, device=dev)
         y = torch.empty_like(x)
         for _ in range(3):
@@ -148,49 +225,29 @@ def main():
         bench_survey(torch, ChunkPlan, dev, args.steps)
         return
     w = inputs.WORKLOADS[args.workload]
-    d = inputs.make_prefill(w)
-    g = {k: (v.to(dev) if v is not None else None) for k, v in d.items()}
+    g = device_inputs(torch, inputs, w, dev)
     plan = ChunkPlan(g["q"], g["k"], g["v"], g["g"], g["beta"], g["S0"], chunk_size=w.C)
-    stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        plan.run()
-    torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_host0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        plan.intra()
-        ev[i][1].record(stream)
-        plan.chain()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host0
-    intra_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    chain_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
-    ms_per_step = sum(step_ms) / K
+    ms_per_step, intra_ms, chain_ms, host_ms = time_step(torch, plan, K, args.warmup)
     tokens = w.B * w.T
     value = tokens / (ms_per_step / 1e3)
 
-    units = w.B * w.T * w.H                          # token-heads per launch
-    ib = 2 if w.dtype == "bf16" else 4
-    state_bytes = w.B * w.H * w.dk * w.dv * 4
-    intra_alg = units * ((2 * w.dk + w.dv) * ib + w.dk * 4 + 4)
-    chain_alg = units * (w.dv * ib) + (2 if g["S0"] is not None else 1) * state_bytes
+    intra_alg, chain_alg = alg_bytes(w, g["S0"] is not None)
     step_alg = intra_alg + chain_alg
-    t_intra = sum(intra_ms) / K / 1e3
-    t_chain = sum(chain_ms) / K / 1e3
+    t_intra, t_chain = intra_ms / 1e3, chain_ms / 1e3
     hot = w.dtype == "bf16" and w.dk == 128 and w.C == 64
     names = ("chunk_intra64_kernel", "chunk_chain64_kernel") if hot else ("chunk_intra_kernel", "chunk_chain_kernel")
-    dom = (names[0], intra_alg, t_intra) if t_intra >= t_chain else (names[1], chain_alg, t_chain)
+    # The dominant kernel: the intra stage is one kernel; the chain stage is one
+    # kernel, or three (maps, scan, outputs) when the sequence runs in segments,
+    # none of them longer than the intra kernel there (profiles/kernel_stats_1m_prefill.txt).
+    segmented = plan.segmented
+    dom = (names[0], intra_alg, t_intra) if (t_intra >= t_chain or segmented) else (names[1], chain_alg, t_chain)
     achieved = dom[1] / dom[2] / 1e9
-    traffic = measured_traffic(dom[0]) if args.workload == "mid" else None
+    traffic = measured_traffic(dom[0])
     roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "alg_bytes": dom[1]}
+                "traffic": traffic, "alg_bytes": dom[1], "ms": round(dom[2] * 1e3, 4)}
     if traffic:
         # the counter bytes (inputs and the workspace the kernel writes) at the same
         # measured duration: how close the kernel runs to the HBM limit for what it moves
@@ -208,33 +265,66 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; shapes and distributions of the mid prefill workload)",
-        "config": {"workload": f"mid prefill B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} C={w.C} "
-                               f"bf16 q/k/v, fp32 g/beta/state, channel gates",
-                   "global_batch": w.B, "seq_len": w.T, "heads": w.H, "chunk": w.C,
-                   "parallelism": "single GPU"},
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": f"synthetic (seeded; shapes and distributions of the {w.name} prefill workload)",
+        "config": {"workload": workload_label(w), "global_batch": w.B, "seq_len": w.T, "heads": w.H,
+                   "chunk": w.C, "parallelism": "single GPU"},
         "roofline": roofline,
-        "mfma": mfma_summary(names, t_intra, t_chain, ms_per_step / 1e3) if args.workload == "mid" else None,
+        "mfma": mfma_summary(names, t_intra, t_chain, ms_per_step / 1e3) if hot and not segmented else None,
         "path": {"step_alg_bytes": step_alg, "step_alg_GBps": round(step_alg / (ms_per_step / 1e3) / 1e9, 1),
                  "step_frac_hbm": round(step_alg / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "intra_ms": round(t_intra * 1e3, 4), "chain_ms": round(t_chain * 1e3, 4),
-                 "host_wall_ms_per_step": round(t_host / K * 1e3, 4)},
+                 "intra_ms": round(intra_ms, 4), "chain_ms": round(chain_ms, 4),
+                 "chain_segments": plan.segments, "host_wall_ms_per_step": round(host_ms, 4)},
     }
+    if segmented:
+        out["mfma"] = mfma_summary_segmented(t_intra, ms_per_step / 1e3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(torch, inputs, w, g, dev)
+    del plan, g
+    torch.cuda.empty_cache()
+
+    if not args.no_workloads:
+        out["workloads"] = {}
+        for name in ("mid", "long"):
+            if name != args.workload:
+                out["workloads"][name] = bench_workload(torch, inputs, ChunkPlan, inputs.WORKLOADS[name], dev, K,
+                                                        args.warmup)
 
     if not args.no_extras:
-        out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, g, w, K, args.warmup)
-        out["fused_pre"] = bench_fused_pre(torch, ChunkPlan, g, w, K, args.warmup)
-        out["varlen"] = bench_varlen(torch, g, w, K, args.warmup)
-        out["backward"] = bench_backward(torch, g, w)
+        wm = inputs.WORKLOADS["mid"]
+        gm = device_inputs(torch, inputs, wm, dev)
+        out["gate_layouts"] = bench_gate_layouts(torch, ChunkPlan, gm, wm, K, args.warmup)
+        out["fused_pre"] = bench_fused_pre(torch, ChunkPlan, gm, wm, K, args.warmup)
+        out["varlen"] = bench_varlen(torch, gm, wm, K, args.warmup)
+        out["backward"] = bench_backward(torch, gm, wm)
+        del gm
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         out["decode"] = bench_decode(torch, inputs, decode_step, dev, args.decode_steps)
 
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(d, w)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
 
     print(json.dumps(out), flush=True)
+
+
+def bench_workload(torch, inputs, ChunkPlan, w, dev, steps, warmup):
+    """One more prefill workload: step time, tokens/s and the fraction of the HBM
+    roofline the whole step reaches for its algorithmic bytes."""
+    g = device_inputs(torch, inputs, w, dev)
+    plan = ChunkPlan(g["q"], g["k"], g["v"], g["g"], g["beta"], g["S0"], chunk_size=w.C)
+    ms, intra, chain, _ = time_step(torch, plan, steps, warmup)
+    ia, ca = alg_bytes(w, g["S0"] is not None)
+    res = {"config": workload_label(w), "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1),
+           "intra_ms": round(intra, 4), "chain_ms": round(chain, 4), "chain_segments": plan.segments,
+           "step_alg_bytes": ia + ca, "step_frac_hbm": round((ia + ca) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "hbm_floor_ms": round((ia + ca) / HBM_PEAK_GBS / 1e6, 4)}
+    del plan, g
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_gate_layouts(torch, ChunkPlan, g, w, steps, warmup):
@@ -450,33 +540,51 @@ def bench_decode(torch, inputs, decode_step, dev, steps):
     return out
 
 
-def cpu_baseline(d, w):
-    """The fp64 oracle (as it stands) on the same workload's inputs, timed on the
-    host cores: every (batch row, head) sequence, whole length (about a second on
-    16 threads, ~16 CPU-seconds); then one thread on two sequences, and the host's
-    CPU model."""
+CPU_TAIL = 65536       # tokens of the 1M workload the oracle baseline runs
+
+
+def cpu_baseline(torch, inputs, w, g, dev):
+    """The fp64 oracle (as it stands) timed on the host cores.  For the 1M-token
+    workload: the last CPU_TAIL tokens of all 16 heads, from the GPU state at
+    T - CPU_TAIL (a split call, untimed), about 25 CPU-seconds; for the smaller
+    workloads the whole workload.  Threads: os.cpu_count(); the oracle runs one
+    (batch, head) sequence per thread, so ``cores`` is the threads it used.  Also
+    one thread on one sequence, and the host's CPU model."""
     import numpy as np
 
     import oracle
+    from linear_attention_sequence_chunk_amd import chunk_fwd
 
-    threads = min(os.cpu_count() or 1, 16)
+    host_cpus = os.cpu_count() or 1
+    t0 = max(0, w.T - CPU_TAIL) if w.T > 4 * CPU_TAIL else 0
+    if t0:
+        _, S_mid = chunk_fwd(g["q"][:, :t0], g["k"][:, :t0], g["v"][:, :t0], g["g"][:, :t0], g["beta"][:, :t0],
+                             g["S0"], chunk_size=w.C)
+        torch.cuda.synchronize()
+        S0 = oracle.to_f64(S_mid.cpu())
+        sample = (f"the last {w.T - t0} tokens of all {w.B * w.H} (batch, head) sequences, from the GPU "
+                  f"state at token {t0}")
+    else:
+        S0 = None if g["S0"] is None else oracle.to_f64(g["S0"].cpu())
+        sample = f"the whole workload: {w.B}x{w.H} (batch x head) sequences of {w.T} tokens"
+    d = inputs.make_prefill(w, t0=t0, t1=w.T)
     args = [oracle.to_f64(d[k]) for k in ("q", "k", "v", "g", "beta")]
     oracle._lib()
-    t0 = time.perf_counter()
-    oracle.recurrent(*args, S0=None if d["S0"] is None else oracle.to_f64(d["S0"]), nthreads=threads)
-    dt = time.perf_counter() - t0
-    used = oracle.last_threads()
-    # one thread on two of the sequences, in the same unit (a token is all H heads)
-    one = [np.ascontiguousarray(a[:1, :, :2]) for a in args]
-    s0 = None if d["S0"] is None else np.ascontiguousarray(oracle.to_f64(d["S0"])[:1, :2])
-    t1 = time.perf_counter()
+    ta = time.perf_counter()
+    oracle.recurrent(*args, S0=S0, nthreads=host_cpus)
+    dt = time.perf_counter() - ta
+    used = min(oracle.last_threads(), w.B * w.H)
+    one = [np.ascontiguousarray(a[:1, :, :1]) for a in args]
+    s0 = None if S0 is None else np.ascontiguousarray(S0[:1, :1])
+    tb = time.perf_counter()
     oracle.recurrent(*one, S0=s0, nthreads=1)
-    dt1 = time.perf_counter() - t1
-    return {"value": round(w.B * w.T / dt, 1), "unit": "tokens/s", "cores": min(used, w.B * w.H),
-            "threads": used, "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"the whole workload: {w.B}x{w.H} (batch x head) sequences of {w.T} tokens",
-            "single_thread_value": round(2 * w.T / w.H / dt1, 1),
-            "single_thread_sample": f"2 of the {w.H} heads of one batch row, one thread",
+    dt1 = time.perf_counter() - tb
+    tokens = w.B * (w.T - t0)
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": used, "threads": used,
+            "host_cpus": host_cpus, "kind": "oracle", "seconds": round(dt, 3),
+            "cpu_seconds": round(dt * used, 1), "sample": sample,
+            "single_thread_value": round((w.T - t0) / w.H / dt1, 1),
+            "single_thread_sample": f"1 of the {w.H} heads of one batch row, one thread (a token is all heads)",
             "cpu_model": _cpu_model()}
 
 

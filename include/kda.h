@@ -96,6 +96,19 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
                                      int in_dtype, int C);
 
 /*
+ * Segments the chain stage of kda_chunk_fwd / kda_chunk_fwd_ex runs each
+ * sequence in, for these sizes (0 if unsupported); host-only.  The recurrence
+ * across chunks is serial (section 十五 of the explainer: one step at a time);
+ * when B*H is too small to fill the GPU and T is long, each sequence is cut
+ * into segments whose affine state maps S -> M S + E are computed side by side,
+ * composed in order, and every segment then re-runs from its true start state.
+ * 1 means the plain sequential chain.  The result equals the sequential chain
+ * up to rounding; the workspace (kda_chunk_fwd_workspace_bytes) includes the
+ * segments' maps and start states.
+ */
+int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int in_dtype, int C);
+
+/*
  * kda_chunk_fwd -- chunkwise-parallel forward over a whole sequence.
  *   q, k          [B,T,H,dk] in_dtype         queries, keys (not normalised here)
  *   v             [B,T,H,dv] in_dtype         values

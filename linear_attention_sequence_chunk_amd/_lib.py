@@ -24,7 +24,7 @@ SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_byte
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
            "kda_chunk_fwd_pre", "kda_chunk_intra_pre", "kda_decode_tokens_pre",
            "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_bytes",
-           "kda_chunk_bwd_pre", "kda_chunk_bwd_pre_workspace_bytes")
+           "kda_chunk_bwd_pre", "kda_chunk_bwd_pre_workspace_bytes", "kda_chunk_fwd_segments")
 
 
 class KdaError(RuntimeError):
@@ -48,6 +48,7 @@ def lib() -> ctypes.CDLL:
         L.kda_status_string.argtypes, L.kda_status_string.restype = [_ci], ctypes.c_char_p
         L.kda_chunk_fwd_workspace_bytes.argtypes = [_ci] * 7
         L.kda_chunk_fwd_workspace_bytes.restype = _sz
+        L.kda_chunk_fwd_segments.argtypes, L.kda_chunk_fwd_segments.restype = [_ci] * 7, _ci
         for name in ("kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain"):
             fn = getattr(L, name)
             fn.argtypes, fn.restype = _CHUNK_ARGS, _ci

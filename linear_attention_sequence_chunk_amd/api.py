@@ -286,6 +286,10 @@ class ChunkPlan:
         (self.B, self.T, self.H, self.dk, self.dv, self.out_dtype, self.o, self.final_state,
          self.workspace) = _prep_chunk(q, k, v, g, beta, initial_state, chunk_size, out_dtype, None, None,
                                        gate_layout, allow_bf16_gate=True)
+        # segments the chain stage runs each sequence in (1: the plain sequential chain)
+        self.segments = int(_lib.lib().kda_chunk_fwd_segments(self.B, self.T, self.H, self.dk, self.dv,
+                                                              _code(q.dtype), chunk_size))
+        self.segmented = self.segments > 1
 
     def _go(self, name, stream=None):
         q, k, v, g, beta, s0 = self.args

@@ -431,6 +431,11 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in
     return kda::ws_layout(B, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
 }
 
+int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int in_dtype, int C) {
+    if (kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, in_dtype, C) == 0) return 0;
+    return kda::seg_plan(B, T, H, dk, dv, in_dtype == KDA_BF16, C, false).nseg;
+}
+
 #define KDA_CHUNK_PARAMS                                                                    \
     const void *q, const void *k, const void *v, const float *g, const float *beta,         \
         const float *initial_state, void *o, float *final_state, int B, int T, int H, int dk, \

@@ -69,15 +69,17 @@ struct Seg64 {
     float* Sst;             // start state of each segment, [.][.][DK][DV]
 };
 
+// The maps launch keeps one chunk in flight and fits two workgroups per CU (its
+// workgroups outnumber the CUs); the other modes keep DEPTH chunks in flight.
 template <typename TOut, int DV, int DVS, int MODE>
-__global__ __launch_bounds__(512) void chunk_chain64_kernel(
+__global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um, Seg64 sg) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
     constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, NSL = Cfg::NSL, LDK = Cfg::LDK, LDC = Cfg::LDC;
-    constexpr int D = Cfg::DEPTH;
     constexpr bool MAPS = MODE == CHAIN_MAPS, OUT = MODE != CHAIN_MAPS;
+    constexpr int D = MAPS && NJ >= 4 ? 1 : Cfg::DEPTH;
     // slices per work item: the maps launch also runs the DK identity columns
     constexpr int NSLW = MAPS ? (DV + DK) / DVS : NSL;
 
@@ -119,6 +121,11 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
 
     const bool wW = wave < 4;                    // uniform per wave
     const int R = wave & 3, ct = wave;
+    // W = U - Wk S: the W waves, all column tiles; in the maps launch, where the O
+    // waves have no outputs to form, every wave, half the column tiles each
+    constexpr int NJW = MAPS && NJ >= 2 ? NJ / 2 : NJ;
+    const bool isW = MAPS || wW;
+    const int jw0 = MAPS && NJ >= 2 ? (wave >> 2) * NJW : 0;
     const int fr = lane & 15, fk = 8 * (lane >> 4);
     TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O) + R * 16 * DVS;
 
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
     // O waves, P for the W waves) repeat an address the wave has just requested, so
     // they cost no L1 miss.
     u32x4 fA[D][4];      // Wk (W waves) or Qt (O waves), row tile R, 4 k-steps
-    u32x2 fU[D][NJ];     // U tiles of this slice (W waves; a repeat of fA on O waves)
+    u32x2 fU[D][NJW];    // U tiles of this wave's W columns (a repeat of fA where U is not needed)
     u32x4 fX[D][2];      // P k-steps (O waves, k-step 1 of row tiles 0, 1 not used; a repeat of fK on W waves)
     u32x4 fK[D][2];      // Kb^T channel tile ct, 2 k-steps
     u32x4 fG[D];         // gam of this lane's 4 state rows
@@ -144,11 +151,11 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         const u32x4* a_ = reinterpret_cast<const u32x4*>((wW || MAPS ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
                           + R * 4 * 64 + lane;                                                      \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
-        const bool uu_ = wW && !ident;                                                              \
+        const bool uu_ = isW && !ident;                                                             \
         const u32x2* u_ = uu_ ? reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))         \
-                                    + (R * (DV / 16) + (j0 / 16)) * 64 + lane                       \
+                                    + (R * (DV / 16) + (j0 / 16) + jw0) * 64 + lane                 \
                               : reinterpret_cast<const u32x2*>(a_);                                 \
-        _Pragma("unroll") for (int j = 0; j < NJ; ++j) fU[SL][j] = u_[uu_ ? j * 64 : 0];            \
+        _Pragma("unroll") for (int j = 0; j < NJW; ++j) fU[SL][j] = u_[uu_ ? j * 64 : 0];           \
     }
 #define KDA_C64_PREFETCH_2(SL, CH)                                                                  \
     {                                                                                               \
@@ -211,28 +218,27 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
         __syncthreads();                                            // S^T of chunk n's start state
 
         // ---- phase 1: W waves W = U - Wk S (to LDS as W^T); O waves O = Qt S
-        floatx4 acc[NJ];
+        floatx4 acc[NJW];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) acc[jt] = zero4();
-        if (OUT || wW) {
+        for (int jt = 0; jt < NJW; ++jt) acc[jt] = zero4();
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bf16x8 fa = __builtin_bit_cast(bf16x8, fA[d][u]);
+        for (int u = 0; u < 4; ++u) {
+            const bf16x8 fa = __builtin_bit_cast(bf16x8, fA[d][u]);
 #pragma unroll
-                for (int jt = 0; jt < NJ; ++jt) {
-                    const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sST + (jt * 16 + fr) * LDK + u * 32 + fk);
-                    acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[jt], 0, 0, 0);
-                }
+            for (int jt = 0; jt < NJW; ++jt) {
+                const bf16x8 fb =
+                    *reinterpret_cast<const bf16x8*>(sST + ((jw0 + jt) * 16 + fr) * LDK + u * 32 + fk);
+                acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[jt], 0, 0, 0);
             }
         }
-        if (wW) {
+        if (isW) {
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) {
+            for (int jt = 0; jt < NJW; ++jt) {
                 const bf16x4 uu = __builtin_bit_cast(bf16x4, fU[d][jt]);
                 bf16x4 w4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w4[e] = (bf16)((ident ? 0.f : (float)uu[e]) - acc[jt][e]);
-                *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
+                *reinterpret_cast<bf16x4*>(sWT + ((jw0 + jt) * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
             }
         }
         KDA_C64_PREFETCH_1(d, unit_of(n + D < NC ? n + D : NC - 1));
@@ -313,51 +319,65 @@ __global__ __launch_bounds__(512) void chunk_chain64_kernel(
 
 // Start states of the segments from their maps: Sst_0 = S0 (zeros when NULL),
 // Sst_1 = E_0 (segment 0 ran from S0 itself), Sst_{s+1} = M_s Sst_s + E_s.
-// One workgroup per ((sequence, head), 16 value columns); thread t holds column
-// t % 16 of DK/16 rows; the sum over the DK channels runs in a fixed order in
-// fp32.
+// One workgroup per ((sequence, head), 4 value columns); thread t holds row t/2,
+// columns 2(t%2) and 2(t%2)+1.  M_s is staged transposed in LDS (padded rows, so
+// a wave's 32 rows read 32 banks), the next map is loaded into registers while
+// the current one is used, and the sum over the DK channels runs in a fixed
+// order in fp32.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void chain_seg_scan_kernel(const float* __restrict__ s0, Seg64 sg) {
-    constexpr int RPT = DK / 16;
-    __shared__ float sS[DK][16];
-    const int cb = (int)(blockIdx.x % (DV / 16));
-    const long bh = blockIdx.x / (DV / 16);
-    const int tid = threadIdx.x, j = tid & 15, r0 = (tid >> 4) * RPT, col = cb * 16 + j;
+    constexpr int NCOL = 4, PER = DK * DK / 4 / 256;       // float4 of a map per thread
+    static_assert(DK == 128 && DV % NCOL == 0, "128 rows, 2 threads per row");
+    __shared__ float sMT[DK][DK + 1];
+    __shared__ float sS[DK][NCOL];
+    const int cb = (int)(blockIdx.x % (DV / NCOL));
+    const long bh = blockIdx.x / (DV / NCOL);
+    const int tid = threadIdx.x, r = tid >> 1, jp = 2 * (tid & 1), col = cb * NCOL + jp;
     const long base = bh * sg.nseg;
+    if (tid < DK) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = r0 + i;
-        const float x = s0 ? s0[(bh * DK + r) * (long)DV + col] : 0.f;
-        sS[r][j] = x;
-        sg.Sst[(base * DK + r) * (long)DV + col] = x;
+        for (int j = 0; j < NCOL; ++j) {
+            const float x = s0 ? s0[(bh * DK + tid) * (long)DV + cb * NCOL + j] : 0.f;
+            sS[tid][j] = x;
+            sg.Sst[(base * DK + tid) * (long)DV + cb * NCOL + j] = x;
+        }
     }
-    __syncthreads();
+    floatx4 mreg[PER];
+    auto load_map = [&](int s) {
+        const floatx4* M = reinterpret_cast<const floatx4*>(sg.M + (base + s) * (long)(DK * DK));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) mreg[i] = M[tid + 256 * i];
+    };
+    if (sg.nseg > 2) load_map(1);                          // M_1 is first used for Sst_2
     for (int s = 1; s < sg.nseg; ++s) {
         const float* E = sg.E + (base + s - 1) * (long)(DK * DV);
-        const float* M = sg.M + (base + s - 1) * (long)(DK * DK);
-        float acc[RPT];
+        const float e0 = E[r * DV + col], e1 = E[r * DV + col + 1];
+        if (s > 1) {                                       // M_{s-1}, in registers, to LDS
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = r0 + i;
-            float a = 0.f;
-            if (s > 1) {
-                for (int c = 0; c < DK; c += 4) {
-                    const float4 m4 = *reinterpret_cast<const float4*>(M + r * DK + c);
-                    a = fmaf(m4.x, sS[c][j], a);
-                    a = fmaf(m4.y, sS[c + 1][j], a);
-                    a = fmaf(m4.z, sS[c + 2][j], a);
-                    a = fmaf(m4.w, sS[c + 3][j], a);
-                }
+            for (int i = 0; i < PER; ++i) {
+                const int u = tid + 256 * i, row = u >> 5, c0 = (u & 31) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sMT[c0 + e][row] = mreg[i][e];
             }
-            acc[i] = a + E[r * DV + col];
+            if (s + 1 < sg.nseg) load_map(s);              // the next step's map
         }
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            sS[r0 + i][j] = acc[i];
-            sg.Sst[((base + s) * DK + r0 + i) * (long)DV + col] = acc[i];
+        float a0 = 0.f, a1 = 0.f;
+        if (s > 1) {
+            for (int c = 0; c < DK; ++c) {
+                const float m = sMT[c][r];
+                a0 = fmaf(m, sS[c][jp], a0);
+                a1 = fmaf(m, sS[c][jp + 1], a1);
+            }
         }
+        a0 += e0;
+        a1 += e1;
         __syncthreads();
+        sS[r][jp] = a0;
+        sS[r][jp + 1] = a1;
+        float* dst = sg.Sst + ((base + s) * DK + r) * (long)DV + col;
+        dst[0] = a0;
+        dst[1] = a1;
     }
 }
 
@@ -375,7 +395,7 @@ static hipError_t launch_chain64_mode(const ChunkArgs& a, long items, const Seg6
     hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS, MODE>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                        (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
                        (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam),
-                       a.s0, (TOut*)a.o, a.sT, unit_map(a), sg);
+                       a.s0, MODE == CHAIN_MAPS ? nullptr : (TOut*)a.o, a.sT, unit_map(a), sg);
     return hipGetLastError();
 }
 
@@ -390,9 +410,10 @@ static hipError_t launch_chain64(const ChunkArgs& a) {
         const WsLayout w = ws_layout_of(a);
         char* ws = (char*)a.ws;
         Seg64 sg{plan.L, plan.nseg, (float*)(ws + w.seg_e), (float*)(ws + w.seg_m), (float*)(ws + w.seg_s)};
-        hipError_t e = launch_chain64_mode<TOut, DV, DVS, CHAIN_MAPS>(a, bh * (plan.nseg - 1), sg);
+        // (the maps write no outputs: one instantiation serves both output types)
+        hipError_t e = launch_chain64_mode<bf16, DV, DVS, CHAIN_MAPS>(a, bh * (plan.nseg - 1), sg);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((chain_seg_scan_kernel<128, DV>), dim3((unsigned)(bh * (DV / 16))), dim3(256), 0,
+        hipLaunchKernelGGL((chain_seg_scan_kernel<128, DV>), dim3((unsigned)(bh * (DV / 4))), dim3(256), 0,
                            a.stream, a.s0, sg);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
