@@ -191,6 +191,31 @@ int kda_chunk_intra_ex(const void *q, const void *k, const void *v,
                        void *stream, int C, int gate_layout);
 
 /*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd_ex without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  It allocates
+ * nothing: its workspace is a static device array of
+ * KDA_NOALLOC_WORKSPACE_MAX bytes inside the library, one per GPU, held until
+ * the process ends.  Sizes whose workspace (kda_chunk_fwd_workspace_bytes)
+ * exceeds it return KDA_ERR_WORKSPACE before any HIP call; at d = 128 and
+ * C = 64 that is about 1,800 (batch, head, chunk) units, e.g. 16 heads of
+ * 7,000 tokens.  The work runs on the current device, and `stream` must belong
+ * to it.  Nothing in the array needs to start at zero (every call writes what it
+ * reads), but every call on a GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (other streams, other host threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Arguments, results and
+ * errors otherwise as kda_chunk_fwd_ex, bitwise the same results.
+ */
+#define KDA_NOALLOC_WORKSPACE_MAX ((size_t)128 << 20)
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *initial_state,
+                          void *o, float *final_state,
+                          int B, int T, int H, int dk, int dv,
+                          int in_dtype, int out_dtype,
+                          void *stream, int C, int gate_layout);
+
+/*
  * kda_chunk_fwd_varlen -- kda_chunk_fwd_ex over a packed batch of N sequences
  * of different lengths (the chunkwise form of the chunk paragraph of the KimiK3
  * essay and section 十六 of the explainer, applied to each sequence on its own:

@@ -11,6 +11,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
 
 F32, BF16 = 0, 1
+NOALLOC_WORKSPACE_MAX = 128 << 20                # KDA_NOALLOC_WORKSPACE_MAX in kda.h
 GATE = {"channel": 0, "head": 1, "none": 2}     # kda_gate_layout_t
 PRE_QK_L2NORM, PRE_GATE_SOFTPLUS, PRE_GATE_BF16 = 1, 2, 4   # kda_pre_flags_t
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
@@ -24,7 +25,8 @@ SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_byte
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes",
            "kda_chunk_fwd_pre", "kda_chunk_intra_pre", "kda_decode_tokens_pre",
            "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_bytes",
-           "kda_chunk_bwd_pre", "kda_chunk_bwd_pre_workspace_bytes", "kda_chunk_fwd_segments")
+           "kda_chunk_bwd_pre", "kda_chunk_bwd_pre_workspace_bytes", "kda_chunk_fwd_segments",
+           "kda_chunk_fwd_noalloc")
 
 
 class KdaError(RuntimeError):
@@ -49,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_bytes.argtypes = [_ci] * 7
         L.kda_chunk_fwd_workspace_bytes.restype = _sz
         L.kda_chunk_fwd_segments.argtypes, L.kda_chunk_fwd_segments.restype = [_ci] * 7, _ci
+        L.kda_chunk_fwd_noalloc.argtypes = [_vp] * 8 + [_ci] * 7 + [_vp, _ci, _ci]
+        L.kda_chunk_fwd_noalloc.restype = _ci
         for name in ("kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain"):
             fn = getattr(L, name)
             fn.argtypes, fn.restype = _CHUNK_ARGS, _ci

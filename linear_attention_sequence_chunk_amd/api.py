@@ -133,6 +133,40 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=Non
     return o, fs
 
 
+def chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, chunk_size=64, out_dtype=None, o=None,
+                      final_state=None, stream=None, gate_layout="channel"):
+    """kda_chunk_fwd_noalloc: chunk_fwd with the library's static workspace (no
+    workspace argument; sizes whose workspace exceeds NOALLOC_WORKSPACE_MAX
+    raise).  ``o`` and ``final_state`` may be given so that nothing is allocated
+    here either.  Returns (o, final_state)."""
+    _gate(gate_layout)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    _check_tensor("k", k, (B, T, H, dk), q.dtype, dev)
+    _check_tensor("v", v, (B, T, H, dv), q.dtype, dev)
+    _check_gate(g, gate_layout, (B, T, H), dk, dev)
+    _check_tensor("beta", beta, (B, T, H), torch.float32, dev)
+    if initial_state is not None:
+        _check_tensor("initial_state", initial_state, (B, H, dk, dv), torch.float32, dev)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _check_tensor("o", o, (B, T, H, dv), out_dtype, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("final_state", final_state, (B, H, dk, dv), torch.float32, dev)
+    st = _lib.lib().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                          _ptr(o), _ptr(final_state), B, T, H, dk, dv, _code(q.dtype),
+                                          _code(out_dtype), _stream(stream, dev), chunk_size, _gate(gate_layout))
+    _lib.check(st, "kda_chunk_fwd_noalloc")
+    return o, final_state
+
+
 def chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, chunk_size=64, out_dtype=None,
                      final_state=None, workspace=None, stream=None, gate_layout="channel"):
     """Packed variable-length batch (kda_chunk_fwd_varlen).  q,k [T,H,dk],

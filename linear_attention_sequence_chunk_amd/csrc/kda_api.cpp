@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -71,6 +73,7 @@ struct ChunkCall {
     int N = 0;
     bool packed = false;
     int pre = 0;                       // kda_pre_flags_t
+    bool static_ws = false;            // workspace: the library's static device array (ws is ignored)
 };
 
 bool gate_ok(int g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
@@ -123,14 +126,19 @@ int validate_chunk(const ChunkCall& c) {
     const size_t need = c.packed ? kda::ws_layout_packed(c.N, c.T, c.H, c.dk, c.dv, c.in_dtype == KDA_BF16, c.C).total
                                  : kda::ws_layout(c.B, c.T, c.H, c.dk, c.dv, c.in_dtype == KDA_BF16, c.C).total;
     const bool uses_ws = c.packed ? (size_t)c.N * c.H > 0 : tok > 0;
-    if (uses_ws && (!c.ws || c.ws_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (c.static_ws) {
+        // the library's own array: nothing of the caller's can overlap it
+        if (uses_ws && need > KDA_NOALLOC_WORKSPACE_MAX) return KDA_ERR_WORKSPACE;
+    } else if (uses_ws && (!c.ws || c.ws_bytes < need)) {
+        return KDA_ERR_WORKSPACE;
+    }
 
     const size_t ei = esize(c.in_dtype), eo = esize(c.out_dtype);
     const Range rq = range_of(c.q, tok * c.dk * ei), rk = range_of(c.k, tok * c.dk * ei),
                 rv = range_of(c.v, tok * c.dv * ei), rg = range_of(g, tok * gate_bytes(c.gate, c.dk, c.pre)),
                 rb = range_of(c.beta, tok * 4), rs0 = range_of(c.s0, nst * 4),
                 ro = range_of(c.o, tok * c.dv * eo), rsT = range_of(c.sT, nst * 4),
-                rw = range_of(c.ws, uses_ws ? need : 0),
+                rw = range_of(c.static_ws ? nullptr : c.ws, uses_ws ? need : 0),
                 rcu = range_of(c.packed ? c.cu_seqlens : nullptr, ((size_t)c.N + 1) * 4);
     const Range others_o[] = {rq, rk, rv, rg, rb, rs0, rsT, rw, rcu};
     for (const Range& r : others_o)
@@ -162,7 +170,40 @@ kda::ChunkArgs to_args(const ChunkCall& c) {
 
 enum Stages { STAGE_INTRA = 1, STAGE_CHAIN = 2 };
 
-int run_chunk(const ChunkCall& c, int stages) {
+}  // namespace
+
+// Workspace of kda_chunk_fwd_noalloc: one array per device, held until the
+// process ends.  Host code uses only the device address hipGetSymbolAddress
+// returns for the current device (the name alone is a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_WORKSPACE_MAX];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current; NULL on failure.
+void* scratch_address() {
+    static std::mutex mu;
+    static void* addr[MAX_DEVICES] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+int run_chunk(ChunkCall c, int stages) {
     int st = validate_chunk(c);
     if (st != KDA_OK) return st;
     const long nseqh = (long)(c.packed ? c.N : c.B) * c.H;
@@ -170,6 +211,11 @@ int run_chunk(const ChunkCall& c, int stages) {
     if (nseqh == 0) return KDA_OK;                      // nothing to do: no device needed
     st = device_ready();
     if (st != KDA_OK) return st;
+    if (c.static_ws) {
+        c.ws = scratch_address();
+        c.ws_bytes = KDA_NOALLOC_WORKSPACE_MAX;
+        if (!c.ws) return KDA_ERR_HIP;
+    }
     const kda::ChunkArgs a = to_args(c);
     if (c.T == 0) {
         // Empty sequence: the final state is the initial state (or zeros).
@@ -451,6 +497,14 @@ int kda_chunk_intra(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL(KDA_GATE
 int kda_chunk_chain(KDA_CHUNK_PARAMS) { return run_chunk(KDA_CHUNK_CALL(KDA_GATE_NONE), STAGE_CHAIN); }
 int kda_chunk_fwd_ex(KDA_CHUNK_PARAMS, int gate_layout) {
     return run_chunk(KDA_CHUNK_CALL(gate_layout), STAGE_INTRA | STAGE_CHAIN);
+}
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const float* initial_state, void* o, float* final_state, int B, int T, int H, int dk,
+                          int dv, int in_dtype, int out_dtype, void* stream, int C, int gate_layout) {
+    ChunkCall c{q, k, v, g, beta, initial_state, o, final_state, B, T, H, dk, dv, in_dtype,
+                out_dtype, nullptr, 0, stream, C, gate_layout};
+    c.static_ws = true;
+    return run_chunk(c, STAGE_INTRA | STAGE_CHAIN);
 }
 int kda_chunk_intra_ex(KDA_CHUNK_PARAMS, int gate_layout) {
     return run_chunk(KDA_CHUNK_CALL(gate_layout), STAGE_INTRA);

@@ -140,6 +140,29 @@ def test_gate_layout_codes(fn):
     assert call_chunk(b, "kda_chunk_chain") == HIP        # the chain stage takes NULL g
 
 
+def test_noalloc_rejects_sizes_beyond_its_array():
+    """kda_chunk_fwd_noalloc: a workspace larger than the static array is refused
+    on the host (KDA_ERR_WORKSPACE) before any HIP call; sizes within it reach
+    the device check; the usual argument checks apply."""
+    L = _lib.lib()
+    big = chunk_args(B=1, T=9000, H=16, dk=128, dv=128, ind=_lib.BF16, outd=_lib.BF16)
+    assert big["wsb"] > _lib.NOALLOC_WORKSPACE_MAX
+
+    def call(a, gate=0):
+        return L.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"], a["sT"],
+                                       a["B"], a["T"], a["H"], a["dk"], a["dv"], a["ind"], a["outd"], None,
+                                       a["C"], gate)
+    assert call(big) == WS
+    small = chunk_args(B=2, T=300, H=3, dk=128, dv=128, ind=_lib.BF16, outd=_lib.BF16)
+    assert call(dict(small, C=48)) == UNSUP
+    assert call(dict(small, q=None)) == NULL
+    assert call(dict(small, o=small["q"])) == ALIAS
+    assert call(dict(small, g=small["g"] + 8)) == MISAL
+    assert call(dict(small, B=0)) == OK
+    if not HAS_GPU:
+        assert call(small) == HIP
+
+
 @pytest.mark.parametrize("dk", [64, 128])
 def test_fp32_c128_is_unsupported(dk):
     a = chunk_args(dk=dk, dv=128, C=128)
