@@ -30,6 +30,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_1m_prefill.txt")
 # MFMA counters per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES,
 # GRBM_GUI_ACTIVE), under the same rule
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_valu_1m_prefill.txt")
+PROFILED_WORKLOAD = "1m"    # the workload both counter summaries were taken on
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 SIMDS = 1024                # 256 CUs x 4
 XCDS = 8                    # GRBM_GUI_ACTIVE is summed over them
@@ -192,11 +193,12 @@ def alg_bytes(w, has_s0):
     return intra, chain
 
 
-def workload_label(w):
+def workload_label(w, chunk_used=None):
     keys = ", recurring address keys" if w.keys == "address" else ""
+    ran = f" (run as {chunk_used}-token chunks)" if chunk_used and chunk_used != w.C else ""
     gates = {"tiny": "channel gates", "long": "fast/slow channel gates", "none": "no gate",
              "scalar": "per-head gates"}[w.gates]
-    return (f"{w.name} prefill B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} C={w.C} "
+    return (f"{w.name} prefill B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} C={w.C}{ran} "
             f"{'bf16' if w.dtype == 'bf16' else 'fp32'} q/k/v, fp32 g/beta/state, {gates}{keys}")
 
 
@@ -236,7 +238,7 @@ def main():
     intra_alg, chain_alg = alg_bytes(w, g["S0"] is not None)
     step_alg = intra_alg + chain_alg
     t_intra, t_chain = intra_ms / 1e3, chain_ms / 1e3
-    hot = w.dtype == "bf16" and w.dk == 128 and w.C == 64
+    hot = w.dtype == "bf16" and w.dk == 128 and plan.chunk_used == 64
     names = ("chunk_intra64_kernel", "chunk_chain64_kernel") if hot else ("chunk_intra_kernel", "chunk_chain_kernel")
     # The dominant kernel: the intra stage is one kernel; the chain stage is one
     # kernel, or three (maps, scan, outputs) when the sequence runs in segments,
@@ -244,7 +246,8 @@ def main():
     segmented = plan.segmented
     dom = (names[0], intra_alg, t_intra) if (t_intra >= t_chain or segmented) else (names[1], chain_alg, t_chain)
     achieved = dom[1] / dom[2] / 1e9
-    traffic = measured_traffic(dom[0])
+    profiled = args.workload == PROFILED_WORKLOAD
+    traffic = measured_traffic(dom[0]) if profiled else None
     roofline = {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "alg_bytes": dom[1], "ms": round(dom[2] * 1e3, 4)}
@@ -267,16 +270,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": f"synthetic (seeded; shapes and distributions of the {w.name} prefill workload)",
-        "config": {"workload": workload_label(w), "global_batch": w.B, "seq_len": w.T, "heads": w.H,
+        "config": {"workload": workload_label(w, plan.chunk_used), "global_batch": w.B, "seq_len": w.T, "heads": w.H,
                    "chunk": w.C, "parallelism": "single GPU"},
         "roofline": roofline,
-        "mfma": mfma_summary(names, t_intra, t_chain, ms_per_step / 1e3) if hot and not segmented else None,
+        "mfma": mfma_summary(names, t_intra, t_chain, ms_per_step / 1e3) if hot and profiled and not segmented else None,
         "path": {"step_alg_bytes": step_alg, "step_alg_GBps": round(step_alg / (ms_per_step / 1e3) / 1e9, 1),
                  "step_frac_hbm": round(step_alg / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                  "intra_ms": round(intra_ms, 4), "chain_ms": round(chain_ms, 4),
                  "chain_segments": plan.segments, "host_wall_ms_per_step": round(host_ms, 4)},
     }
-    if segmented:
+    if segmented and profiled:
         out["mfma"] = mfma_summary_segmented(t_intra, ms_per_step / 1e3)
 
     cpu = None
@@ -318,7 +321,7 @@ def bench_workload(torch, inputs, ChunkPlan, w, dev, steps, warmup):
     plan = ChunkPlan(g["q"], g["k"], g["v"], g["g"], g["beta"], g["S0"], chunk_size=w.C)
     ms, intra, chain, _ = time_step(torch, plan, steps, warmup)
     ia, ca = alg_bytes(w, g["S0"] is not None)
-    res = {"config": workload_label(w), "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1),
+    res = {"config": workload_label(w, plan.chunk_used), "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1),
            "intra_ms": round(intra, 4), "chain_ms": round(chain, 4), "chain_segments": plan.segments,
            "step_alg_bytes": ia + ca, "step_frac_hbm": round((ia + ca) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
            "hbm_floor_ms": round((ia + ca) / HBM_PEAK_GBS / 1e6, 4)}

@@ -28,9 +28,13 @@
  *     state are fp32.  g is the log-gate: g <= 0, -inf allowed (alpha = 0).
  *     g > 0 (alpha > 1) is outside the method's domain; results are unspecified.
  *     NaN/Inf inputs propagate; nothing is checked on the device.
- *   - Supported: dk, dv in {64, 128}; chunk size C in {16, 32, 64, 128} for
- *     bf16 inputs and {16, 32, 64} for fp32 inputs; any T >= 0 (a last
- *     partial chunk is allowed); B, H >= 0.
+ *   - Supported: dk, dv in {64, 128}; chunk size C in {16, 32, 64, 128}; any
+ *     T >= 0 (a last partial chunk is allowed); B, H >= 0.  The chunkwise form
+ *     gives the recurrence's result for every C, so C only groups the work
+ *     (kda_chunk_size_used reports the chunk the kernels run).  C = 128 runs as
+ *     64-token chunks for fp32 inputs (the 128 x 128 fp32 blocks exceed the
+ *     160 KB of LDS a workgroup has), for bf16 inputs with dk = 128 (the 64-token
+ *     kernels move fewer bytes per token) and in the backward pass.
  *   - Alignment: kda_chunk_fwd needs q, k, v, o, the workspace and a
  *     per-channel g 16-byte aligned (true of any [..., dk] row of a tensor whose
  *     storage is 16-byte aligned); kda_decode_step needs the state 16-byte
@@ -107,6 +111,17 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
  * segments' maps and start states.
  */
 int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int in_dtype, int C);
+
+/*
+ * The chunk size the kernels run for a requested C (forward: backward = 0;
+ * kda_chunk_bwd: backward = 1), or 0 for unsupported sizes; host-only.  The
+ * chunk paragraph of the KimiK3 essay has the chunk size fitted to the matrix
+ * units, and section 十八 of the explainer lists a chunk size suited to the
+ * target GPU among what decides a kernel's speed: C = 128 is computed as
+ * 64-token chunks where that is what fits gfx950 (see the supported sizes
+ * above).  Results differ only by rounding.
+ */
+int kda_chunk_size_used(int dk, int dv, int in_dtype, int C, int backward);
 
 /*
  * kda_chunk_fwd -- chunkwise-parallel forward over a whole sequence.
@@ -271,8 +286,8 @@ size_t kda_chunk_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
  *   dbeta         [B,T,H]    fp32
  *   dS0           [B,H,dk,dv] fp32 or NULL
  *   workspace     >= kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, in_dtype, C)
- * Supported: C in {16, 32, 64}; dk, dv in {64, 128}; in_dtype BF16 or F32 (the
- * gradient arithmetic is fp32).  Outputs must not overlap any input, the
+ * Supported: C in {16, 32, 64, 128} (C = 128 runs as 64-token chunks); dk, dv
+ * in {64, 128}; in_dtype BF16 or F32 (the gradient arithmetic is fp32).  Outputs must not overlap any input, the
  * workspace or each other.  Alignment: q, k, v and the workspace 16 bytes,
  * per-channel g 16 bytes, everything else 4 bytes.  Deterministic (no
  * floating-point atomics).

@@ -26,7 +26,7 @@ SYMBOLS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_byte
            "kda_chunk_fwd_pre", "kda_chunk_intra_pre", "kda_decode_tokens_pre",
            "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_bytes",
            "kda_chunk_bwd_pre", "kda_chunk_bwd_pre_workspace_bytes", "kda_chunk_fwd_segments",
-           "kda_chunk_fwd_noalloc")
+           "kda_chunk_fwd_noalloc", "kda_chunk_size_used")
 
 
 class KdaError(RuntimeError):
@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_segments.argtypes, L.kda_chunk_fwd_segments.restype = [_ci] * 7, _ci
         L.kda_chunk_fwd_noalloc.argtypes = [_vp] * 8 + [_ci] * 7 + [_vp, _ci, _ci]
         L.kda_chunk_fwd_noalloc.restype = _ci
+        L.kda_chunk_size_used.argtypes, L.kda_chunk_size_used.restype = [_ci] * 5, _ci
         for name in ("kda_chunk_fwd", "kda_chunk_intra", "kda_chunk_chain"):
             fn = getattr(L, name)
             fn.argtypes, fn.restype = _CHUNK_ARGS, _ci

@@ -324,6 +324,8 @@ class ChunkPlan:
         self.segments = int(_lib.lib().kda_chunk_fwd_segments(self.B, self.T, self.H, self.dk, self.dv,
                                                               _code(q.dtype), chunk_size))
         self.segmented = self.segments > 1
+        # the chunk size the kernels run (C = 128 may run as 64-token chunks)
+        self.chunk_used = int(_lib.lib().kda_chunk_size_used(self.dk, self.dv, _code(q.dtype), chunk_size, 0))
 
     def _go(self, name, stream=None):
         q, k, v, g, beta, s0 = self.args

@@ -94,6 +94,17 @@ int pre_mode(int pre) {
 bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
 size_t esize(int d) { return d == KDA_BF16 ? 2 : 4; }
 
+// The chunk the kernels run for a requested chunk size.  The chunkwise form
+// gives the recurrence's result for every C (only rounding differs), so C is a
+// grouping choice.  C = 128 runs as 64-token chunks: with fp32 inputs (the
+// 128 x 128 fp32 blocks of both stages exceed the 160 KB of LDS), with bf16
+// inputs and dk = 128 (the C = 64 kernels, built for the gfx950 matrix cores,
+// move fewer bytes per token: P grows with C, and the segmented chain removes
+// the serial length that a longer chunk would shorten), and in the backward
+// pass (its per-chunk kernel holds 158 KB of LDS at C = 64).
+int fwd_chunk(int C, int dk, int in_dtype) { return C == 128 && (in_dtype != KDA_BF16 || dk == 128) ? 64 : C; }
+int bwd_chunk(int C) { return C == 128 ? 64 : C; }
+
 int validate_chunk(const ChunkCall& c) {
     if (c.B < 0 || c.T < 0 || c.H < 0 || c.N < 0) return KDA_ERR_SHAPE;
     if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype) || !gate_ok(c.gate) || !pre_ok(c.pre))
@@ -204,6 +215,7 @@ void* scratch_address() {
 }
 
 int run_chunk(ChunkCall c, int stages) {
+    c.C = fwd_chunk(c.C, c.dk, c.in_dtype);
     int st = validate_chunk(c);
     if (st != KDA_OK) return st;
     const long nseqh = (long)(c.packed ? c.N : c.B) * c.H;
@@ -277,6 +289,7 @@ PreLayout pre_layout(size_t base, size_t tok, int dk, int in_dtype, int gate, in
 // format, with checkpoints), then the backward stages.
 int run_bwd(BwdCall c) {
     const int dk = c.dk_size, dv = c.dv_size;
+    c.C = bwd_chunk(c.C);
     if (c.B < 0 || c.T < 0 || c.H < 0 || c.N < 0) return KDA_ERR_SHAPE;
     if (!dtype_ok(c.in_dtype) || !gate_ok(c.gate) || !pre_ok(c.pre)) return KDA_ERR_UNSUPPORTED;
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
@@ -396,6 +409,7 @@ const char* kda_status_string(int s) {
 
 size_t kda_chunk_varlen_workspace_bytes(int N, int T, int H, int dk, int dv, int in_dtype, int C) {
     if (N < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    C = fwd_chunk(C, dk, in_dtype);
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
     if (C != 16 && C != 32 && C != 64 && C != 128) return 0;
     if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
@@ -416,6 +430,7 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const floa
 
 size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C) {
     if (B < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    C = bwd_chunk(C);
     if (!kda::bwd_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
     if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
     return kda::bwd_layout(B, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
@@ -423,6 +438,7 @@ size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in
 
 size_t kda_chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv, int in_dtype, int C) {
     if (N < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    C = bwd_chunk(C);
     if (!kda::bwd_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
     if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
     return kda::bwd_layout_packed(N, T, H, dk, dv, in_dtype == KDA_BF16, C).total;
@@ -471,6 +487,7 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const floa
 
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in_dtype, int C) {
     if (B < 0 || T < 0 || H < 0 || !dtype_ok(in_dtype)) return 0;
+    C = fwd_chunk(C, dk, in_dtype);
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
     if (C != 16 && C != 32 && C != 64 && C != 128) return 0;
     if (!kda::chunk_supported(dk, dv, C, in_dtype == KDA_BF16)) return 0;
@@ -479,7 +496,16 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int in
 
 int kda_chunk_fwd_segments(int B, int T, int H, int dk, int dv, int in_dtype, int C) {
     if (kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, in_dtype, C) == 0) return 0;
-    return kda::seg_plan(B, T, H, dk, dv, in_dtype == KDA_BF16, C, false).nseg;
+    return kda::seg_plan(B, T, H, dk, dv, in_dtype == KDA_BF16, fwd_chunk(C, dk, in_dtype), false).nseg;
+}
+
+int kda_chunk_size_used(int dk, int dv, int in_dtype, int C, int backward) {
+    if (!dtype_ok(in_dtype) || (dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
+    if (C != 16 && C != 32 && C != 64 && C != 128) return 0;
+    const int used = backward ? bwd_chunk(C) : fwd_chunk(C, dk, in_dtype);
+    const bool bf = in_dtype == KDA_BF16;
+    if (!kda::chunk_supported(dk, dv, used, bf) || (backward && !kda::bwd_supported(dk, dv, used, bf))) return 0;
+    return used;
 }
 
 #define KDA_CHUNK_PARAMS                                                                    \

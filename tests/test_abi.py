@@ -163,12 +163,33 @@ def test_noalloc_rejects_sizes_beyond_its_array():
         assert call(small) == HIP
 
 
+def test_chunk_size_used():
+    """C = 128 runs as 64-token chunks for fp32 inputs, for bf16 inputs with
+    dk = 128 and in the backward pass; other sizes run as asked.  The workspace
+    follows the chunk that runs."""
+    L = _lib.lib()
+    used = L.kda_chunk_size_used
+    F, B16 = _lib.F32, _lib.BF16
+    assert used(64, 64, F, 128, 0) == 64 and used(128, 128, F, 128, 0) == 64
+    assert used(128, 128, B16, 128, 0) == 64 and used(128, 64, B16, 128, 0) == 64
+    assert used(64, 64, B16, 128, 0) == 128 and used(64, 128, B16, 128, 0) == 128
+    assert used(64, 128, B16, 128, 1) == 64 and used(128, 128, F, 128, 1) == 64
+    for C in (16, 32, 64):
+        assert used(128, 128, F, C, 0) == C and used(64, 64, B16, C, 1) == C
+    assert used(96, 64, F, 64, 0) == 0 and used(64, 64, F, 48, 0) == 0 and used(64, 64, 9, 64, 0) == 0
+    ws = L.kda_chunk_fwd_workspace_bytes
+    assert ws(2, 300, 3, 64, 128, F, 128) == ws(2, 300, 3, 64, 128, F, 64) > 0
+    assert ws(2, 300, 3, 128, 128, B16, 128) == ws(2, 300, 3, 128, 128, B16, 64)
+    assert ws(2, 300, 3, 64, 64, B16, 128) != ws(2, 300, 3, 64, 64, B16, 64)
+    bws = L.kda_chunk_bwd_workspace_bytes
+    assert bws(2, 300, 3, 64, 64, B16, 128) == bws(2, 300, 3, 64, 64, B16, 64) > 0
+
+
 @pytest.mark.parametrize("dk", [64, 128])
-def test_fp32_c128_is_unsupported(dk):
+def test_fp32_c128_is_supported(dk):
     a = chunk_args(dk=dk, dv=128, C=128)
-    assert a["wsb"] == 0
-    a["wsb"] = 1 << 30
-    assert call_chunk(a) == UNSUP
+    assert a["wsb"] > 0
+    assert call_chunk(a) == (OK if HAS_GPU else HIP) or HAS_GPU
 
 
 def test_valid_chunk_call_reaches_device_check():
@@ -353,7 +374,8 @@ def test_backward_validation_codes():
     tok, nst = B * T * H, B * H * dk * dv
     wsb = L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, C)
     assert wsb > L.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, C)   # + checkpoints
-    assert L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, 128) == 0  # C <= 64
+    # C = 128 runs as 64-token chunks
+    assert L.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, _lib.BF16, 128) == wsb
     a = dict(q=f(tok * dk * 2), k=f(tok * dk * 2), v=f(tok * dv * 2), g=f(tok * dk * 4), beta=f(tok * 4),
              s0=f(nst * 4), dO=f(tok * dv * 4), dST=f(nst * 4), dq=f(tok * dk * 4), dk=f(tok * dk * 4),
              dv=f(tok * dv * 4), dg=f(tok * dk * 4), dbeta=f(tok * 4), dS0=f(nst * 4),
@@ -363,7 +385,7 @@ def test_backward_validation_codes():
         return L.kda_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], x["dO"], x["dST"],
                                x["dq"], x["dk"], x["dv"], x["dg"], x["dbeta"], x["dS0"], x["B"], x["T"],
                                x["H"], x["dkk"], x["dvv"], x["ind"], x["ws"], x["wsb"], None, x["C"], x["gate"])
-    cases = [(dict(T=-1), SHAPE), (dict(dkk=96), UNSUP), (dict(C=128), UNSUP), (dict(ind=7), UNSUP),
+    cases = [(dict(T=-1), SHAPE), (dict(dkk=96), UNSUP), (dict(C=48), UNSUP), (dict(ind=7), UNSUP),
              (dict(gate=5), UNSUP), (dict(dq=None), NULL), (dict(dO=None), NULL), (dict(dg=None), NULL),
              (dict(q=a["q"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(g=a["g"] + 8), MISAL),
              (dict(dbeta=a["dbeta"] + 2), MISAL),
@@ -390,7 +412,7 @@ def test_backward_varlen_validation_codes():
     tok, nst = T * H, N * H * dk * dv
     wsb = L.kda_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, _lib.BF16, C)
     assert wsb > L.kda_chunk_bwd_workspace_bytes(1, T, H, dk, dv, _lib.BF16, C)   # room for N extra chunks
-    assert L.kda_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, _lib.BF16, 128) == 0
+    assert L.kda_chunk_bwd_varlen_workspace_bytes(N, T, H, dk, dv, _lib.BF16, 128) == wsb   # 64-token chunks
     assert L.kda_chunk_bwd_varlen_workspace_bytes(-1, T, H, dk, dv, _lib.BF16, C) == 0
     a = dict(q=f(tok * dk * 2), k=f(tok * dk * 2), v=f(tok * dv * 2), g=f(tok * dk * 4), beta=f(tok * 4),
              s0=f(nst * 4), dO=f(tok * dv * 4), dST=f(nst * 4), dq=f(tok * dk * 4), dk=f(tok * dk * 4),
@@ -402,7 +424,7 @@ def test_backward_varlen_validation_codes():
                                       x["dq"], x["dk"], x["dv"], x["dg"], x["dbeta"], x["dS0"], x["cu"],
                                       x["N"], x["T"], x["H"], dk, dv, _lib.BF16, x["ws"], x["wsb"], None,
                                       x["C"], x["gate"])
-    cases = [(dict(N=-1), SHAPE), (dict(C=128), UNSUP), (dict(gate=5), UNSUP), (dict(cu=None), NULL),
+    cases = [(dict(N=-1), SHAPE), (dict(C=96), UNSUP), (dict(gate=5), UNSUP), (dict(cu=None), NULL),
              (dict(dO=None), NULL), (dict(cu=a["cu"] + 2), MISAL), (dict(wsb=wsb - 1), WS),
              (dict(ws=None), WS), (dict(dq=a["cu"]), ALIAS), (dict(dS0=a["cu"]), ALIAS),
              (dict(ws=a["cu"] - 16), ALIAS), (dict(dS0=a["dST"]), ALIAS), (dict(dg=None), NULL)]
