@@ -55,7 +55,10 @@ struct Chain64Cfg {
     static constexpr size_t OFF_WT = OFF_ST + size_t(DVS) * LDK * 2;
     static constexpr size_t OFF_O = OFF_WT + size_t(DVS) * LDC * 2;               // per O wave: [16][DVS]
     static constexpr size_t TOTAL = OFF_O + size_t(4) * 16 * DVS * sizeof(TOut);
-    static_assert((NJ == 1 || NJ == 2 || NJ == 4 || NJ == 8) && DV % DVS == 0, "slice width 16 .. 128");
+    // slices of 16 .. 128 value columns; the maps launch may also take all DV + DK
+    // augmented columns in one workgroup (DVS = 256 with DV = DK = 128)
+    static_assert(((NJ == 1 || NJ == 2 || NJ == 4 || NJ == 8) && DV % DVS == 0) || (DV == 128 && DVS == 256),
+                  "slice width 16 .. 128, or the whole augmented state");
     static_assert((16 * DVS * sizeof(TOut)) % 16 == 0, "output staging rows");
 };
 
@@ -69,10 +72,10 @@ struct Seg64 {
     float* Sst;             // start state of each segment, [.][.][DK][DV]
 };
 
-// The maps launch keeps one chunk in flight and fits two workgroups per CU (its
-// workgroups outnumber the CUs); the other modes keep DEPTH chunks in flight.
+// The maps launch keeps one chunk in flight; with slices of at most 128 columns
+// two of its workgroups share a CU.  The other modes keep DEPTH chunks in flight.
 template <typename TOut, int DV, int DVS, int MODE>
-__global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64_kernel(
+__global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void chunk_chain64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um, Seg64 sg) {
@@ -108,9 +111,10 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64
     const int nsegw = MODE == CHAIN_PLAIN ? 1 : (MAPS ? sg.nseg - 1 : sg.nseg);
     const long bh = item / nsegw;
     const int seg = (int)(item % nsegw);
-    const bool ident = MAPS && sl >= NSL;                // identity columns (maps launch only)
-    if (ident && seg == 0) return;                       // segment 0 starts from a known state: no M
-    const int j0 = (ident ? sl - NSL : sl) * DVS;        // first column (of the value or the identity block)
+    // first column of the slice; in the maps launch, of the augmented state
+    // [value columns 0 .. DV-1 | identity columns DV .. DV+DK-1]
+    const int j0 = sl * DVS;
+    if (MAPS && j0 >= DV && seg == 0) return;            // segment 0 starts from a known state: no M
     // sequence (batch row, or packed sequence) and head; its chunks and tokens
     const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
     const SeqRange sr = seq_range(um, sq);
@@ -126,6 +130,8 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64
     constexpr int NJW = MAPS && NJ >= 2 ? NJ / 2 : NJ;
     const bool isW = MAPS || wW;
     const int jw0 = MAPS && NJ >= 2 ? (wave >> 2) * NJW : 0;
+    // this wave's W columns are identity columns (maps launch): U is 0 there
+    const bool identW = MAPS && j0 + 16 * jw0 >= DV;
     const int fr = lane & 15, fk = 8 * (lane >> 4);
     TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O) + R * 16 * DVS;
 
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64
         const u32x4* a_ = reinterpret_cast<const u32x4*>((wW || MAPS ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
                           + R * 4 * 64 + lane;                                                      \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
-        const bool uu_ = isW && !ident;                                                             \
+        const bool uu_ = isW && !identW;                                                            \
         const u32x2* u_ = uu_ ? reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))         \
                                     + (R * (DV / 16) + (j0 / 16) + jw0) * 64 + lane                 \
                               : reinterpret_cast<const u32x2*>(a_);                                 \
@@ -190,10 +196,10 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
         accS[jt] = zero4();
-        if (ident) {
+        if (MAPS && j0 + jt * 16 >= DV) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                accS[jt][e] = (ct * 16 + 4 * (lane >> 4) + e == j0 + jt * 16 + fr) ? 1.f : 0.f;
+                accS[jt][e] = (ct * 16 + 4 * (lane >> 4) + e == j0 + jt * 16 - DV + fr) ? 1.f : 0.f;
         } else if (init) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64
                 const bf16x4 uu = __builtin_bit_cast(bf16x4, fU[d][jt]);
                 bf16x4 w4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w4[e] = (bf16)((ident ? 0.f : (float)uu[e]) - acc[jt][e]);
+                for (int e = 0; e < 4; ++e) w4[e] = (bf16)((identW ? 0.f : (float)uu[e]) - acc[jt][e]);
                 *reinterpret_cast<bf16x4*>(sWT + ((jw0 + jt) * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
             }
         }
@@ -300,20 +306,29 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS ? 2 : 1) void chunk_chain64
 
     // end state: the call's final state (plain; the last segment of the outputs
     // launch), or the segment's E or M (maps launch)
-    float* fin = nullptr;
-    long ld = DV;
     if constexpr (MAPS) {
-        fin = ident ? sg.M + (bh * sg.nseg + seg) * (long)(DK * DK) : sg.E + (bh * sg.nseg + seg) * (long)(DK * DV);
-        ld = ident ? DK : DV;
+        float* E = sg.E + (bh * sg.nseg + seg) * (long)(DK * DV);
+        float* M = sg.M + (bh * sg.nseg + seg) * (long)(DK * DK);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            const int col = j0 + jt * 16;
+            if (col >= DV && seg == 0) continue;           // M of segment 0 is never used
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = ct * 16 + 4 * (lane >> 4) + e;
+                if (col >= DV) M[row * (long)DK + col - DV + fr] = accS[jt][e];
+                else E[row * (long)DV + col + fr] = accS[jt][e];
+            }
+        }
     } else if (MODE == CHAIN_PLAIN || seg == sg.nseg - 1) {
-        fin = sT ? sT + bh * (long)(DK * DV) : nullptr;
-    }
-    if (fin) {
+        if (sT) {
+            float* fin = sT + bh * (long)(DK * DV);
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
+            for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                fin[(ct * 16 + 4 * (lane >> 4) + e) * ld + j0 + jt * 16 + fr] = accS[jt][e];
+                for (int e = 0; e < 4; ++e)
+                    fin[(ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr] = accS[jt][e];
+        }
     }
 }
 
@@ -410,8 +425,11 @@ static hipError_t launch_chain64(const ChunkArgs& a) {
         const WsLayout w = ws_layout_of(a);
         char* ws = (char*)a.ws;
         Seg64 sg{plan.L, plan.nseg, (float*)(ws + w.seg_e), (float*)(ws + w.seg_m), (float*)(ws + w.seg_s)};
-        // (the maps write no outputs: one instantiation serves both output types)
-        hipError_t e = launch_chain64_mode<bf16, DV, DVS, CHAIN_MAPS>(a, bh * (plan.nseg - 1), sg);
+        // (the maps write no outputs: one instantiation serves both output types);
+        // with DV = DK every segment's whole augmented state is one workgroup, so
+        // its Wk and Kb^T are fetched once
+        constexpr int DVS_MAPS = DV == 128 ? 256 : DVS;
+        hipError_t e = launch_chain64_mode<bf16, DV, DVS_MAPS, CHAIN_MAPS>(a, bh * (plan.nseg - 1), sg);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((chain_seg_scan_kernel<128, DV>), dim3((unsigned)(bh * (DV / 4))), dim3(256), 0,
                            a.stream, a.s0, sg);
