@@ -559,7 +559,8 @@ def cpu_baseline(torch, inputs, w, g, dev):
     from linear_attention_sequence_chunk_amd import chunk_fwd
 
     host_cpus = os.cpu_count() or 1
-    t0 = max(0, w.T - CPU_TAIL) if w.T > 4 * CPU_TAIL else 0
+    # a tail from the GPU state needs the prefix call on a contiguous slice: B = 1
+    t0 = max(0, w.T - CPU_TAIL) if (w.T > 4 * CPU_TAIL and w.B == 1) else 0
     if t0:
         _, S_mid = chunk_fwd(g["q"][:, :t0], g["k"][:, :t0], g["v"][:, :t0], g["g"][:, :t0], g["beta"][:, :t0],
                              g["S0"], chunk_size=w.C)

@@ -29,20 +29,15 @@ CASES = [
 ]
 
 
-def _segmented(B, T, H, dv):
-    """The segmented chain's extra workspace appears exactly when it is used."""
-    L = _lib.lib()
-    per_pair = lambda b, h: L.kda_chunk_fwd_workspace_bytes(b, T, h, 128, dv, _lib.BF16, 64) / (b * h)
-    # 256 workgroups of 32 value columns fill the GPU: no segments there;
-    # segments add E, M and a start state (at least 96 KB) per pair and segment
-    full = 256 * 32 // dv
-    return per_pair(B, H) > per_pair(1, full) + 65536
+def _segments(B, T, H, dv):
+    return _lib.lib().kda_chunk_fwd_segments(B, T, H, 128, dv, _lib.BF16, 64)
 
 
 @pytest.mark.parametrize("B,H,T,dv,out_dtype,gates,s0", CASES)
 def test_segmented_chain(B, H, T, dv, out_dtype, gates, s0):
-    print(f"segments B={B} H={H} T={T} dv={dv} {out_dtype} gates={gates}", flush=True)
-    assert _segmented(B, T, H, dv)
+    nseg = _segments(B, T, H, dv)
+    assert nseg > 1, nseg
+    print(f"segments B={B} H={H} T={T} dv={dv} {out_dtype} gates={gates}: {nseg} segments", flush=True)
     d = inputs.custom_prefill(61 + T, B, T, H, 128, dv, dtype=torch.bfloat16, gates=gates, s0_std=s0)
     dg = cuda(d)
     o, S = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], dg["S0"], chunk_size=64, out_dtype=out_dtype)
