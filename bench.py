@@ -282,6 +282,8 @@ def main():
     if segmented and profiled:
         out["mfma"] = mfma_summary_segmented(t_intra, ms_per_step / 1e3)
 
+    out["gpu_clocks"] = gpu_clocks(torch, plan)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(torch, inputs, w, g, dev)
@@ -312,6 +314,38 @@ def main():
         out["cpu_baseline"] = cpu
 
     print(json.dumps(out), flush=True)
+
+
+def gpu_clocks(torch, plan, steps=40, samples=8):
+    """GPU clocks while the step runs (amd-smi's library, in this process, after
+    the timed region): untimed steps are queued, and the graphics and memory
+    clocks are sampled while they execute.  None where the library is missing."""
+    try:
+        import amdsmi
+    except Exception:
+        return None
+    try:
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        for _ in range(steps):
+            plan.run()
+        gfx, mem = [], []
+        for _ in range(samples):
+            gfx.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+            mem.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"])
+            time.sleep(0.02)
+        gmax = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["max_clk"]
+        torch.cuda.synchronize()
+        return {"gfx_mhz_samples": gfx, "gfx_max_mhz": gmax, "mem_mhz": max(mem),
+                "note": "sampled during untimed steps, after the timed region"}
+    except Exception as e:                 # a clock reading must never fail the bench
+        torch.cuda.synchronize()
+        return {"error": type(e).__name__}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def bench_workload(torch, inputs, ChunkPlan, w, dev, steps, warmup):
