@@ -69,3 +69,51 @@ def test_segmented_chain(B, H, T, dv, out_dtype, gates, s0):
     assert_close("o segmented vs sequential", o.cpu(), op.cpu().reshape(o.shape), tol)
     assert_close("S segmented vs sequential", S.cpu(), Sp.cpu(), tol)
     print(f"  segmented: o {eo:.2e} S {es:.2e};  sequential: o {eop:.2e} S {esp:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_segmented_chain_random(seed):
+    """Seeded random shapes that run in segments, with every gate layout and the
+    fused pre-processing (raw q, k and a softplus pre-activation): outputs and
+    final states against the oracle, on all heads and columns."""
+    r = np.random.default_rng(400 + seed)
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+    dv = int(r.choice([64, 128]))
+    T = int(r.integers(64 * 64, 64 * 160)) + int(r.integers(0, 64))
+    layout = ["channel", "head", "none"][seed % 3]
+    pre = seed >= 3
+    nseg = _segments(B, T, H, dv)
+    assert nseg > 1
+    print(f"random segments seed={seed}: B={B} H={H} T={T} dv={dv} gates={layout} pre={pre}: {nseg} segments",
+          flush=True)
+    d = inputs.custom_prefill(500 + seed, B, T, H, 128, dv, dtype=torch.bfloat16,
+                              gates={"channel": "tiny", "head": "scalar", "none": "none"}[layout], s0_std=0.03)
+    q, k, g = d["q"], d["k"], d["g"]
+    if pre:
+        # raw rows of varied scale, and the pre-activation whose -softplus is the gate
+        sc = torch.tensor(r.uniform(0.2, 5.0, (B, T, H, 1)), dtype=torch.float32)
+        q = (q.float() * sc).to(torch.bfloat16)
+        k = (k.float() * sc.flip(1)).to(torch.bfloat16)
+        a = torch.log(torch.expm1(-g.double())).float()
+        g_in = a
+    else:
+        g_in = g
+    if layout == "head":
+        g_in = g_in[..., 0].contiguous()
+    dg = cuda({"q": q, "k": k, "v": d["v"], "g": None if layout == "none" else g_in, "beta": d["beta"],
+               "S0": d["S0"]})
+    o, S = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], dg["S0"], chunk_size=64, gate_layout=layout,
+                     qk_l2norm=pre, gate_act="softplus" if pre else None)
+    torch.cuda.synchronize()
+    qn = oracle.l2_normalize(q) if pre else q
+    kn = oracle.l2_normalize(k) if pre else k
+    if layout == "none":
+        g_ref = np.zeros(tuple(q.shape))
+    else:
+        g_ref = oracle.gate_softplus(g_in) if pre else oracle.to_f64(g_in)
+        if layout == "head":
+            g_ref = np.ascontiguousarray(np.broadcast_to(g_ref[..., None], tuple(q.shape)))
+    o_ref, S_ref = oracle.recurrent(qn, kn, d["v"], g_ref, d["beta"], d["S0"])
+    eo = assert_close("o", o.cpu(), o_ref, TOL[torch.bfloat16])
+    es = assert_close("S", S.cpu(), S_ref, TOL[torch.bfloat16])
+    print(f"  max err o {eo:.2e} S {es:.2e}", flush=True)
