@@ -47,7 +47,9 @@ enum ChainMode { CHAIN_PLAIN = 0, CHAIN_MAPS = 1, CHAIN_SEG = 2 };
 template <typename TOut, int DV, int DVS>
 struct Chain64Cfg {
     static constexpr int C = 64, DK = 128, NT = 512, NJ = DVS / 16, NSL = DV / DVS;
-    static constexpr int LDK = DK + 8, LDC = C + 8;   // padded bf16 rows of S^T, W^T
+    // padded bf16 rows of S^T and W^T: 24 and 16 elements, measured against 8 and 8
+    // (bank conflicts: the 1M workload's chain 8.4 -> 7.9 ms; 32-element pads are worst)
+    static constexpr int LDK = DK + 24, LDC = C + 16;
     // chunks in flight: four for slices of 16 or 32 columns; fewer for wider
     // slices, whose accumulators take the registers
     static constexpr int DEPTH = NJ <= 2 ? 4 : (NJ <= 4 ? 3 : 2);
