@@ -316,10 +316,11 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def gpu_clocks(torch, plan, steps=40, samples=8):
+def gpu_clocks(torch, plan, steps=60, samples=12):
     """GPU clocks while the step runs (amd-smi's library, in this process, after
     the timed region): untimed steps are queued, and the graphics and memory
-    clocks are sampled while they execute.  None where the library is missing."""
+    clocks are sampled only while the stream still has work pending.  None where
+    the library is missing."""
     try:
         import amdsmi
     except Exception:
@@ -327,17 +328,19 @@ def gpu_clocks(torch, plan, steps=40, samples=8):
     try:
         amdsmi.amdsmi_init()
         h = amdsmi.amdsmi_get_processor_handles()[0]
+        gmax = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["max_clk"]
+        stream = torch.cuda.current_stream()
         for _ in range(steps):
             plan.run()
+        time.sleep(0.05)
         gfx, mem = [], []
-        for _ in range(samples):
+        while len(gfx) < samples and not stream.query():
             gfx.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
             mem.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"])
             time.sleep(0.02)
-        gmax = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["max_clk"]
         torch.cuda.synchronize()
-        return {"gfx_mhz_samples": gfx, "gfx_max_mhz": gmax, "mem_mhz": max(mem),
-                "note": "sampled during untimed steps, after the timed region"}
+        return {"gfx_mhz_samples": gfx, "gfx_max_mhz": gmax, "mem_mhz": max(mem) if mem else None,
+                "note": "sampled while untimed steps ran, after the timed region"}
     except Exception as e:                 # a clock reading must never fail the bench
         torch.cuda.synchronize()
         return {"error": type(e).__name__}
