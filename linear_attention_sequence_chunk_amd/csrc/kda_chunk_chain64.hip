@@ -20,10 +20,10 @@
 // chunks that run side by side (segment-affine form).  A segment maps its start
 // state to its end state affinely, S -> M S + E, with M = prod over its chunks of
 // (Diag(gam) - Kb^T Wk) and E its end state from a zero start.  Three launches:
-//   maps  (CHAIN_MAPS): each segment but the last runs the chain, without
-//         outputs, on the augmented state [S | I]: value columns from a zero
-//         start (segment 0 from the call's initial state) give E, the dk extra
-//         columns from the identity with U taken as 0 give M;
+//   maps  (chain_maps64_kernel): each segment but the last runs the chain,
+//         without outputs, on the augmented state [S | I]: value columns from a
+//         zero start (segment 0 from the call's initial state) give E, the dk
+//         extra columns from the identity with U taken as 0 give M;
 //   scan  (chain_seg_scan_kernel): start states Sst_0 = S0, Sst_1 = E_0,
 //         Sst_{s+1} = M_s Sst_s + E_s, in fp32;
 //   outputs (CHAIN_SEG): every segment runs the chain with outputs from its
@@ -42,7 +42,7 @@ namespace kda {
 //                                                        never written, never read)
 //   U      [4 row tiles][DV/16 column tiles][64][4] bf16  lane l, element e: row 16R + 4(l/16) + e, column 16J + l%16
 //   gam    [DK] fp32
-enum ChainMode { CHAIN_PLAIN = 0, CHAIN_MAPS = 1, CHAIN_SEG = 2 };
+enum ChainMode { CHAIN_PLAIN = 0, CHAIN_SEG = 1 };
 
 template <typename TOut, int DV, int DVS>
 struct Chain64Cfg {
@@ -57,14 +57,11 @@ struct Chain64Cfg {
     static constexpr size_t OFF_WT = OFF_ST + size_t(DVS) * LDK * 2;
     static constexpr size_t OFF_O = OFF_WT + size_t(DVS) * LDC * 2;               // per O wave: [16][DVS]
     static constexpr size_t TOTAL = OFF_O + size_t(4) * 16 * DVS * sizeof(TOut);
-    // slices of 16 .. 128 value columns; the maps launch may also take all DV + DK
-    // augmented columns in one workgroup (DVS = 256 with DV = DK = 128)
-    static_assert(((NJ == 1 || NJ == 2 || NJ == 4 || NJ == 8) && DV % DVS == 0) || (DV == 128 && DVS == 256),
-                  "slice width 16 .. 128, or the whole augmented state");
+    static_assert((NJ == 1 || NJ == 2 || NJ == 4 || NJ == 8) && DV % DVS == 0, "slice width 16 .. 128");
     static_assert((16 * DVS * sizeof(TOut)) % 16 == 0, "output staging rows");
 };
 
-// Segments of a long sequence (CHAIN_MAPS, CHAIN_SEG); per (sequence, head) pair
+// Segments of a long sequence (maps and CHAIN_SEG launches); per (sequence, head) pair
 // bh and segment s, the arrays hold [bh][s][DK][...] fp32.
 struct Seg64 {
     int L;                  // chunks per segment
@@ -74,19 +71,14 @@ struct Seg64 {
     float* Sst;             // start state of each segment, [.][.][DK][DV]
 };
 
-// The maps launch keeps one chunk in flight; with slices of at most 128 columns
-// two of its workgroups share a CU.  The other modes keep DEPTH chunks in flight.
 template <typename TOut, int DV, int DVS, int MODE>
-__global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void chunk_chain64_kernel(
+__global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um, Seg64 sg) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
     constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, NSL = Cfg::NSL, LDK = Cfg::LDK, LDC = Cfg::LDC;
-    constexpr bool MAPS = MODE == CHAIN_MAPS, OUT = MODE != CHAIN_MAPS;
-    constexpr int D = MAPS && NJ >= 4 ? 1 : Cfg::DEPTH;
-    // slices per work item: the maps launch also runs the DK identity columns
-    constexpr int NSLW = MAPS ? (DV + DK) / DVS : NSL;
+    constexpr int D = Cfg::DEPTH;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
     bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
@@ -100,23 +92,20 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void
     int sl;
     {
         const long nwg = (long)gridDim.x, id = blockIdx.x;
-        if (!um.cu_seqlens && nwg % (8 * NSLW) == 0) {
+        if (!um.cu_seqlens && nwg % (8 * NSL) == 0) {
             const long xcd = id % 8, local = id / 8;
-            sl = (int)(local % NSLW);
-            item = (local / NSLW) * 8 + xcd;
+            sl = (int)(local % NSL);
+            item = (local / NSL) * 8 + xcd;
         } else {
-            item = id / NSLW;
-            sl = (int)(id % NSLW);
+            item = id / NSL;
+            sl = (int)(id % NSL);
         }
     }
     // work item -> (sequence, head) pair and segment
-    const int nsegw = MODE == CHAIN_PLAIN ? 1 : (MAPS ? sg.nseg - 1 : sg.nseg);
+    const int nsegw = MODE == CHAIN_PLAIN ? 1 : sg.nseg;
     const long bh = item / nsegw;
     const int seg = (int)(item % nsegw);
-    // first column of the slice; in the maps launch, of the augmented state
-    // [value columns 0 .. DV-1 | identity columns DV .. DV+DK-1]
-    const int j0 = sl * DVS;
-    if (MAPS && j0 >= DV && seg == 0) return;            // segment 0 starts from a known state: no M
+    const int j0 = sl * DVS;                      // first value column of the slice
     // sequence (batch row, or packed sequence) and head; its chunks and tokens
     const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
     const SeqRange sr = seq_range(um, sq);
@@ -127,13 +116,6 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void
 
     const bool wW = wave < 4;                    // uniform per wave
     const int R = wave & 3, ct = wave;
-    // W = U - Wk S: the W waves, all column tiles; in the maps launch, where the O
-    // waves have no outputs to form, every wave, half the column tiles each
-    constexpr int NJW = MAPS && NJ >= 2 ? NJ / 2 : NJ;
-    const bool isW = MAPS || wW;
-    const int jw0 = MAPS && NJ >= 2 ? (wave >> 2) * NJW : 0;
-    // this wave's W columns are identity columns (maps launch): U is 0 there
-    const bool identW = MAPS && j0 + 16 * jw0 >= DV;
     const int fr = lane & 15, fk = 8 * (lane >> 4);
     TOut* sO = reinterpret_cast<TOut*>(smem + Cfg::OFF_O) + R * 16 * DVS;
 
@@ -145,32 +127,28 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void
     // O waves, P for the W waves) repeat an address the wave has just requested, so
     // they cost no L1 miss.
     u32x4 fA[D][4];      // Wk (W waves) or Qt (O waves), row tile R, 4 k-steps
-    u32x2 fU[D][NJW];    // U tiles of this wave's W columns (a repeat of fA where U is not needed)
+    u32x2 fU[D][NJ];     // U tiles of the slice (W waves; a repeat of fA on O waves)
     u32x4 fX[D][2];      // P k-steps (O waves, k-step 1 of row tiles 0, 1 not used; a repeat of fK on W waves)
     u32x4 fK[D][2];      // Kb^T channel tile ct, 2 k-steps
     u32x4 fG[D];         // gam of this lane's 4 state rows
     // first half: what phase 1 consumes; second half: what phase 2 consumes
-    // In the maps launch the O waves compute nothing: their operand loads repeat
-    // the W waves' (Wk of the same row tile, Kb^T), and identity slices, whose U
-    // is 0, repeat the Wk address for their U loads.
 #define KDA_C64_PREFETCH_1(SL, CH)                                                                  \
     {                                                                                               \
         const long ch_ = (CH);                                                                      \
-        const u32x4* a_ = reinterpret_cast<const u32x4*>((wW || MAPS ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
+        const u32x4* a_ = reinterpret_cast<const u32x4*>((wW ? ws_wk : ws_qt) + ch_ * (long)(C * DK)) \
                           + R * 4 * 64 + lane;                                                      \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) fA[SL][u] = a_[u * 64];                       \
-        const bool uu_ = isW && !identW;                                                            \
-        const u32x2* u_ = uu_ ? reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))         \
-                                    + (R * (DV / 16) + (j0 / 16) + jw0) * 64 + lane                 \
-                              : reinterpret_cast<const u32x2*>(a_);                                 \
-        _Pragma("unroll") for (int j = 0; j < NJW; ++j) fU[SL][j] = u_[uu_ ? j * 64 : 0];           \
+        const u32x2* u_ = wW ? reinterpret_cast<const u32x2*>(ws_u + ch_ * (long)(C * DV))          \
+                                   + (R * (DV / 16) + (j0 / 16)) * 64 + lane                        \
+                             : reinterpret_cast<const u32x2*>(a_);                                  \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) fU[SL][j] = u_[wW ? j * 64 : 0];             \
     }
 #define KDA_C64_PREFETCH_2(SL, CH)                                                                  \
     {                                                                                               \
         const long ch_ = (CH);                                                                      \
         const u32x4* k_ = reinterpret_cast<const u32x4*>(ws_kb + ch_ * (long)(DK * C)) + ct * 2 * 64 + lane; \
         {                                                                                           \
-            const u32x4* p_ = wW || MAPS ? k_ : reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
+            const u32x4* p_ = wW ? k_ : reinterpret_cast<const u32x4*>(ws_p + ch_ * (long)(C * C)) + R * 2 * 64 + lane; \
             fX[SL][0] = p_[0];                                                                      \
             fX[SL][1] = p_[wave >= 6 ? 64 : 0];     /* O waves of row tiles 2, 3 only */          \
         }                                                                                           \
@@ -188,21 +166,14 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void
     }
 
     // ---- state rows 16*ct + 4(l/16) + e, columns j0 + 16 jt + l%16, fp32 in accumulators
-    // start: the call's initial state (plain; segment 0 of the maps launch), the
-    // segment's start state (outputs launch), zero (other segments' E), the
-    // identity (M)
+    // start: the call's initial state (plain), or the segment's start state (outputs launch)
     const float* init = MODE == CHAIN_SEG ? sg.Sst + (bh * sg.nseg + seg) * (long)(DK * DV)
-                                          : (MODE == CHAIN_PLAIN || seg == 0 ? (s0 ? s0 + bh * (long)(DK * DV) : nullptr)
-                                                                             : nullptr);
+                                          : (s0 ? s0 + bh * (long)(DK * DV) : nullptr);
     floatx4 accS[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
         accS[jt] = zero4();
-        if (MAPS && j0 + jt * 16 >= DV) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                accS[jt][e] = (ct * 16 + 4 * (lane >> 4) + e == j0 + jt * 16 - DV + fr) ? 1.f : 0.f;
-        } else if (init) {
+        if (init) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 accS[jt][e] = init[(ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr];
@@ -226,34 +197,33 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void
         __syncthreads();                                            // S^T of chunk n's start state
 
         // ---- phase 1: W waves W = U - Wk S (to LDS as W^T); O waves O = Qt S
-        floatx4 acc[NJW];
+        floatx4 acc[NJ];
 #pragma unroll
-        for (int jt = 0; jt < NJW; ++jt) acc[jt] = zero4();
+        for (int jt = 0; jt < NJ; ++jt) acc[jt] = zero4();
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const bf16x8 fa = __builtin_bit_cast(bf16x8, fA[d][u]);
 #pragma unroll
-            for (int jt = 0; jt < NJW; ++jt) {
-                const bf16x8 fb =
-                    *reinterpret_cast<const bf16x8*>(sST + ((jw0 + jt) * 16 + fr) * LDK + u * 32 + fk);
+            for (int jt = 0; jt < NJ; ++jt) {
+                const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sST + (jt * 16 + fr) * LDK + u * 32 + fk);
                 acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc[jt], 0, 0, 0);
             }
         }
-        if (isW) {
+        if (wW) {
 #pragma unroll
-            for (int jt = 0; jt < NJW; ++jt) {
+            for (int jt = 0; jt < NJ; ++jt) {
                 const bf16x4 uu = __builtin_bit_cast(bf16x4, fU[d][jt]);
                 bf16x4 w4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w4[e] = (bf16)((identW ? 0.f : (float)uu[e]) - acc[jt][e]);
-                *reinterpret_cast<bf16x4*>(sWT + ((jw0 + jt) * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
+                for (int e = 0; e < 4; ++e) w4[e] = (bf16)((float)uu[e] - acc[jt][e]);
+                *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
             }
         }
         KDA_C64_PREFETCH_1(d, unit_of(n + D < NC ? n + D : NC - 1));
         __syncthreads();                                            // W^T complete
 
         // ---- phase 2: O waves O += P W (stored); all waves S = gam S + Kb^T W
-        if (OUT && !wW) {
+        if (!wW) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 if (u == 1 && R < 2) break;                         // P is lower triangular
@@ -306,23 +276,8 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void
         if (n0 + DI < NC) step(DI, n0 + DI);
     });
 
-    // end state: the call's final state (plain; the last segment of the outputs
-    // launch), or the segment's E or M (maps launch)
-    if constexpr (MAPS) {
-        float* E = sg.E + (bh * sg.nseg + seg) * (long)(DK * DV);
-        float* M = sg.M + (bh * sg.nseg + seg) * (long)(DK * DK);
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) {
-            const int col = j0 + jt * 16;
-            if (col >= DV && seg == 0) continue;           // M of segment 0 is never used
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = ct * 16 + 4 * (lane >> 4) + e;
-                if (col >= DV) M[row * (long)DK + col - DV + fr] = accS[jt][e];
-                else E[row * (long)DV + col + fr] = accS[jt][e];
-            }
-        }
-    } else if (MODE == CHAIN_PLAIN || seg == sg.nseg - 1) {
+    // end state: the call's final state (plain; the last segment of the outputs launch)
+    if (MODE == CHAIN_PLAIN || seg == sg.nseg - 1) {
         if (sT) {
             float* fin = sT + bh * (long)(DK * DV);
 #pragma unroll
@@ -332,6 +287,223 @@ __global__ __launch_bounds__(512, MODE == CHAIN_MAPS && DVS <= 128 ? 2 : 1) void
                     fin[(ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr] = accS[jt][e];
         }
     }
+}
+
+// The maps launch with the whole augmented state [S | I] (DV + DK columns) in one
+// workgroup of 8 waves, register-tiled so that every S^T or W^T fragment read from
+// LDS feeds two MFMAs (one per row tile a wave holds):
+//   W = U - Wk S (64 x N):      wave w, row tiles 2(w%2), 2(w%2)+1, column tiles
+//                               NJ1 (w/2) .. +NJ1-1 (U taken as 0 on identity columns)
+//   S <- gam S + Kb^T W (DK x N): wave w, state row tiles 2(w%4), 2(w%4)+1, column
+//                               tiles NJ2 (w/4) .. +NJ2-1, fp32 in accumulators
+// Operands, MD chunks ahead: Wk, U and gam (read by several waves) come in once
+// per workgroup, 16 bytes a lane, and are copied to LDS one chunk before their
+// use (gam, read after the middle barrier, into one of two buffers by chunk
+// parity); each wave's Kb^T fragments go from memory straight into registers.
+// Two barriers per chunk, as in chunk_chain64_kernel.
+template <int DV>
+struct Maps64Cfg {
+    static constexpr int C = 64, DK = 128, N = DV + DK, NCT = N / 16, NVT = DV / 16;
+    static constexpr int NJ1 = NCT / 4, NJ2 = NCT / 2;
+    static constexpr int LDK = DK + 24, LDC = C + 16;           // as Chain64Cfg
+    static constexpr int NWK = C * DK * 2 / 16 / 512, NUV = C * DV * 2 / 16 / 512;   // 16-byte loads a lane
+    static constexpr size_t OFF_ST = 0;                                          // S^T [N][LDK]
+    static constexpr size_t OFF_WT = OFF_ST + size_t(N) * LDK * 2;               // W^T [N][LDC]
+    static constexpr size_t OFF_WK = OFF_WT + size_t(N) * LDC * 2;               // Wk, fragment order
+    static constexpr size_t OFF_U = OFF_WK + size_t(C) * DK * 2;                 // U, fragment order
+    static constexpr size_t OFF_G = OFF_U + size_t(C) * DV * 2;                 // gam [2][DK] fp32
+    static constexpr size_t TOTAL = OFF_G + size_t(2) * DK * 4;
+    static_assert(NCT % 4 == 0 && NWK >= 1 && NUV >= 1, "tile and load mapping");
+    static_assert(TOTAL <= 160 * 1024, "LDS");
+};
+
+template <int DV, int MD>
+__global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
+    const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb, const bf16* __restrict__ ws_u,
+    const float* __restrict__ ws_gam, const float* __restrict__ s0, UnitMap um, Seg64 sg) {
+    typedef Maps64Cfg<DV> Cfg;
+    constexpr int C = Cfg::C, DK = Cfg::DK, NVT = Cfg::NVT, NJ1 = Cfg::NJ1, NJ2 = Cfg::NJ2;
+    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, NWK = Cfg::NWK, NUV = Cfg::NUV;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
+    bf16* sWT = reinterpret_cast<bf16*>(smem + Cfg::OFF_WT);
+    u32x4* sWk = reinterpret_cast<u32x4*>(smem + Cfg::OFF_WK);
+    u32x4* sU = reinterpret_cast<u32x4*>(smem + Cfg::OFF_U);
+    u32x4* sG = reinterpret_cast<u32x4*>(smem + Cfg::OFF_G);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int fr = lane & 15, fk = 8 * (lane >> 4), fe = 4 * (lane >> 4);
+    const long item = blockIdx.x;
+    const int nsegw = sg.nseg - 1;                   // the last segment needs no map
+    const long bh = item / nsegw;
+    const int seg = (int)(item % nsegw);
+    const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
+    const SeqRange sr = seq_range(um, sq);
+    const int c0 = seg * sg.L;
+    const int NC = sr.nchunks - c0 < sg.L ? sr.nchunks - c0 : sg.L;
+    auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, c0 + (n < NC ? n : NC - 1), sr.chunk0); };
+
+    const int R1 = 2 * (wave & 1), J1 = NJ1 * (wave >> 1);   // phase 1 tiles
+    const int R2 = 2 * (wave & 3), J2 = NJ2 * (wave >> 2);   // phase 2 (state) tiles
+
+    // register slots, chunk m in slot m % MD (past the last chunk, the last one again)
+    u32x4 fW[MD][NWK], fV[MD][NUV];      // Wk and U, 16 bytes a lane of the whole chunk
+    u32x4 fG[MD];                        // gam, 16 bytes a lane (lane l: channels 4(l%32) ..)
+    u32x4 fK[MD][2][2];                  // Kb^T channel tiles R2, R2 + 1, 2 k-steps
+    auto load_shared = [&](auto DI, long ch) __attribute__((always_inline)) {
+        constexpr int d = DI;
+        const u32x4* a = reinterpret_cast<const u32x4*>(ws_wk + ch * (long)(C * DK)) + tid;
+        const u32x4* u = reinterpret_cast<const u32x4*>(ws_u + ch * (long)(C * DV)) + tid;
+#pragma unroll
+        for (int i = 0; i < NWK; ++i) fW[d][i] = a[512 * i];
+#pragma unroll
+        for (int i = 0; i < NUV; ++i) fV[d][i] = u[512 * i];
+        fG[d] = reinterpret_cast<const u32x4*>(ws_gam + ch * (long)DK)[tid & (DK / 4 - 1)];
+    };
+    auto stage_shared = [&](auto DI, int buf) __attribute__((always_inline)) {
+        constexpr int d = DI;
+#pragma unroll
+        for (int i = 0; i < NWK; ++i) sWk[tid + 512 * i] = fW[d][i];
+#pragma unroll
+        for (int i = 0; i < NUV; ++i) sU[tid + 512 * i] = fV[d][i];
+        if (tid < DK / 4) sG[buf * (DK / 4) + tid] = fG[d];
+    };
+    auto load_own = [&](auto DI, long ch) __attribute__((always_inline)) {
+        constexpr int d = DI;
+        const u32x4* k = reinterpret_cast<const u32x4*>(ws_kb + ch * (long)(DK * C)) + lane;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            fK[d][i][0] = k[((R2 + i) * 2) * 64];
+            fK[d][i][1] = k[((R2 + i) * 2 + 1) * 64];
+        }
+    };
+    if (NC > 0) {
+        static_for<MD>([&](auto DI) {
+            load_shared(DI, unit_of(DI));
+            load_own(DI, unit_of(DI));
+        });
+        stage_shared(std::integral_constant<int, 0>{}, 0);         // chunk 0
+        load_shared(std::integral_constant<int, 0>{}, unit_of(MD));
+    }
+
+    // state tiles (R2 + i, J2 + jt): rows 16(R2 + i) + fe + e, column 16(J2 + jt) + fr
+    // of [S | I]; value columns start from S0 (segment 0) or zero, identity columns
+    // from the identity
+    const float* init = seg == 0 && s0 ? s0 + bh * (long)(DK * DV) : nullptr;
+    floatx4 accS[2][NJ2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jt = 0; jt < NJ2; ++jt) {
+            const int col = 16 * (J2 + jt) + fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * (R2 + i) + fe + e;
+                accS[i][jt][e] = col >= DV ? (row == col - DV ? 1.f : 0.f) : (init ? init[row * (long)DV + col] : 0.f);
+            }
+        }
+    auto write_state_operand = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jt = 0; jt < NJ2; ++jt) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = (bf16)accS[i][jt][e];
+                *reinterpret_cast<bf16x4*>(sST + (16 * (J2 + jt) + fr) * LDK + 16 * (R2 + i) + fe) = v4;
+            }
+    };
+    write_state_operand();
+
+    // chunk n: Wk, U and gam in LDS, Kb^T in register slot d = n % MD
+    auto step = [&](auto DI, int n) __attribute__((always_inline)) {
+        constexpr int d = DI, d1 = (DI + 1) % MD;
+        __syncthreads();                                   // S^T, Wk, U and gam of chunk n in LDS
+
+        // ---- W = U - Wk S on tiles (R1 + i, J1 + jt), to LDS as W^T, in two
+        // halves of the column tiles (fewer live accumulators)
+        const u32x2* sU2 = reinterpret_cast<const u32x2*>(sU);
+        static_for<2>([&](auto HI) {
+            constexpr int NH = NJ1 / 2 + (HI == 0 ? NJ1 % 2 : 0), JH = HI == 0 ? 0 : NJ1 / 2 + NJ1 % 2;
+            floatx4 acc[2][NH];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jt = 0; jt < NH; ++jt) acc[i][jt] = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 fa0 = __builtin_bit_cast(bf16x8, sWk[(R1 * 4 + s) * 64 + lane]);
+                const bf16x8 fa1 = __builtin_bit_cast(bf16x8, sWk[((R1 + 1) * 4 + s) * 64 + lane]);
+#pragma unroll
+                for (int jt = 0; jt < NH; ++jt) {
+                    const bf16x8 fb =
+                        *reinterpret_cast<const bf16x8*>(sST + (16 * (J1 + JH + jt) + fr) * LDK + 32 * s + fk);
+                    acc[0][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, fb, acc[0][jt], 0, 0, 0);
+                    acc[1][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, fb, acc[1][jt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jt = 0; jt < NH; ++jt) {
+                    const int J = J1 + JH + jt;
+                    bf16x4 uu{};
+                    if (J < NVT) uu = __builtin_bit_cast(bf16x4, sU2[((R1 + i) * NVT + J) * 64 + lane]);   // wave-uniform
+                    bf16x4 w4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w4[e] = (bf16)((float)uu[e] - acc[i][jt][e]);
+                    *reinterpret_cast<bf16x4*>(sWT + (16 * J + fr) * LDC + 16 * (R1 + i) + fe) = w4;
+                }
+        });
+        __syncthreads();                                   // W^T complete; Wk and U of chunk n read
+
+        // ---- S <- gam S + Kb^T W on tiles (R2 + i, J2 + jt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const floatx4 gm = __builtin_bit_cast(floatx4, sG[(n & 1) * (DK / 4) + (R2 + i) * 4 + (lane >> 4)]);
+#pragma unroll
+            for (int jt = 0; jt < NJ2; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accS[i][jt][e] *= gm[e];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const bf16x8 fk0 = __builtin_bit_cast(bf16x8, fK[d][0][s]), fk1 = __builtin_bit_cast(bf16x8, fK[d][1][s]);
+#pragma unroll
+            for (int jt = 0; jt < NJ2; ++jt) {
+                const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sWT + (16 * (J2 + jt) + fr) * LDC + 32 * s + fk);
+                accS[0][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk0, fb, accS[0][jt], 0, 0, 0);
+                accS[1][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk1, fb, accS[1][jt], 0, 0, 0);
+            }
+        }
+        write_state_operand();                             // read only after the next barrier
+        load_own(DI, unit_of(n + MD));
+        stage_shared(std::integral_constant<int, d1>{}, (n + 1) & 1);   // chunk n + 1, read after the next barrier
+        load_shared(std::integral_constant<int, d1>{}, unit_of(n + 1 + MD));
+    };
+    // whole rounds of MD chunks, then the last NC % MD
+    int n0 = 0;
+    for (; n0 + MD <= NC; n0 += MD) static_for<MD>([&](auto DI) { step(DI, n0 + DI); });
+    static_for<MD>([&](auto DI) {
+        if (n0 + DI < NC) step(DI, n0 + DI);
+    });
+
+    // E (value columns) and M (identity columns; segment 0's is never used)
+    float* E = sg.E + (bh * sg.nseg + seg) * (long)(DK * DV);
+    float* M = sg.M + (bh * sg.nseg + seg) * (long)(DK * DK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jt = 0; jt < NJ2; ++jt) {
+            const int col = 16 * (J2 + jt) + fr;
+            if (col >= DV && seg == 0) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * (R2 + i) + fe + e;
+                if (col >= DV) M[row * (long)DK + col - DV] = accS[i][jt][e];
+                else E[row * (long)DV + col] = accS[i][jt][e];
+            }
+        }
 }
 
 // Start states of the segments from their maps: Sst_0 = S0 (zeros when NULL),
@@ -403,16 +575,14 @@ __global__ __launch_bounds__(256) void chain_seg_scan_kernel(const float* __rest
 
 template <typename TOut, int DV, int DVS, int MODE>
 static hipError_t launch_chain64_mode(const ChunkArgs& a, long items, const Seg64& sg) {
-    constexpr int C = 64, DK = 128;
-    constexpr int NSLW = MODE == CHAIN_MAPS ? (DV + DK) / DVS : DV / DVS;
-    const long nwg = items * NSLW;
+    const long nwg = items * (DV / DVS);
     if (nwg == 0) return hipSuccess;
     const WsLayout w = ws_layout_of(a);
     char* ws = (char*)a.ws;
     hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS, MODE>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                        (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
                        (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam),
-                       a.s0, MODE == CHAIN_MAPS ? nullptr : (TOut*)a.o, a.sT, unit_map(a), sg);
+                       a.s0, (TOut*)a.o, a.sT, unit_map(a), sg);
     return hipGetLastError();
 }
 
@@ -427,11 +597,14 @@ static hipError_t launch_chain64(const ChunkArgs& a) {
         const WsLayout w = ws_layout_of(a);
         char* ws = (char*)a.ws;
         Seg64 sg{plan.L, plan.nseg, (float*)(ws + w.seg_e), (float*)(ws + w.seg_m), (float*)(ws + w.seg_s)};
-        // (the maps write no outputs: one instantiation serves both output types);
-        // with DV = DK every segment's whole augmented state is one workgroup, so
-        // its Wk and Kb^T are fetched once
-        constexpr int DVS_MAPS = DV == 128 ? 256 : DVS;
-        hipError_t e = launch_chain64_mode<bf16, DV, DVS_MAPS, CHAIN_MAPS>(a, bh * (plan.nseg - 1), sg);
+        // (the maps write no outputs: one kernel serves both output types); every
+        // segment's whole augmented state is one workgroup, so its Wk and Kb^T are
+        // fetched once
+        const long nmaps = bh * (plan.nseg - 1);
+        hipLaunchKernelGGL((chain_maps64_kernel<DV, 2>), dim3((unsigned)nmaps), dim3(512), 0, a.stream,
+                           (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb), (const bf16*)(ws + w.u),
+                           (const float*)(ws + w.gam), a.s0, unit_map(a), sg);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((chain_seg_scan_kernel<128, DV>), dim3((unsigned)(bh * (DV / 4))), dim3(256), 0,
                            a.stream, a.s0, sg);
