@@ -582,62 +582,78 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_chain_h_kernel(
 }
 
 // ================================================================ per-chunk gradients
-// One workgroup of 256 threads (4 waves) per chunk unit; every contraction runs
-// on fp32 MFMA.  Wave w owns the channel blocks w, w + 4, ... from start to end:
-// dQt, dKb and T^T dWk of its channels stay in its registers (rows 16R + 4(l/16) + e,
-// channel l%16 of each block), and the last phase (decays, pairwise decays, the
-// prefix-sum adjoint) runs per wave without workgroup barriers.  Phase 1 loads its
-// fragments straight from global memory; the C x C products are split by column
-// block (wave w: block w) and go through LDS.
+// One workgroup per chunk unit with one wave per 16-channel block (8 waves for
+// dk = 128, two to a SIMD).  Wave w owns channels 16w .. 16w + 15 from start to
+// end: its elements are rows 16R + 4(l/16) + e, channel 16w + l%16 (the MFMA
+// accumulator layout), and dQt, dKb, T^T dWk, the raw k and q, the prefix sums G
+// of the log-gate and the decayed operands of the last phase stay in its
+// registers, so the last phase (decays, pairwise decays, the prefix-sum adjoint)
+// runs without workgroup barriers or LDS of its own.  The C x C products are split
+// by column block (wave w < C/16: block w) and go through LDS.
+//   phase 1  the products over the value channels (dQt, dWk, dKb, dgam, dP,
+//            dW V^T) on bf16 MFMA with fp32 operands split into bf16 hi + lo:
+//            the rows of dO, W and dW are staged in LDS once per workgroup, each
+//            wave's S and dS' blocks come straight into registers
+//   then     dV = Diag(beta) T^T dW;  G and Kt = e^G K;  dT, T^T dWk;  dM, dA;
+//            the per-wave last phase;  dbeta from per-wave partial sums
 template <int DK, int DV, int C>
 struct BwdIntraCfg {
-    static constexpr int NB = C / 16, NKB = DK / 16, NVB = DV / 16, KPW = NKB / 4, VPW = NVB / 4;
+    static constexpr int NB = C / 16, NKB = DK / 16, NVB = DV / 16;
+    static constexpr int NW = NKB, NT = 64 * NW;                            // one wave per channel block
     static constexpr int LC = C + 4, LK = DK + 4;
-    static constexpr int TL = 16 * LC;                                      // one [16 channels][C] array
-    static constexpr int F_T = 0, F_DP = C * LC, F_DA = 2 * C * LC, F_G = 3 * C * LC;
-    static constexpr int F_X = F_G + C * DK;                                // shared by phases 3, 4, 5
+    static constexpr int LS1 = 40;                                          // staged bf16 row of phase 1
+    static constexpr int F_T = 0, F_DP = C * LC, F_DA = 2 * C * LC;
+    static constexpr int F_X = 3 * C * LC;                                  // shared by phases 1, 3, 4
+    static constexpr int X1 = 2 * 3 * 2 * C * LS1 / 2;                      // phase 1: [2][3][hi, lo][C][LS1] bf16
     static constexpr int X3 = 2 * C * LK;                                   // dWk, Kt
     static constexpr int X4 = C * LC;                                       // X = T^T dT
-    static constexpr int X5 = 4 * 4 * TL;                                   // per wave: Km, Ks, Qs, Ki
-    static constexpr int XN = X3 > X4 ? (X3 > X5 ? X3 : X5) : (X4 > X5 ? X4 : X5);
+    static constexpr int XN = X1 > X3 ? (X1 > X4 ? X1 : X4) : (X3 > X4 ? X3 : X4);
     static constexpr int F_BETA = F_X + XN;
     static constexpr int F_DB1 = F_BETA + C;                                // [C]
-    static constexpr int F_DB2 = F_DB1 + C;                                 // [4][C]
-    static constexpr int F_DB3 = F_DB2 + 4 * C;                             // [4][C]
-    static constexpr int F_HD = F_DB3 + 4 * C;                              // [4][C] per-head dg partials
-    static constexpr int FLOATS = F_HD + 4 * C;
-    static constexpr bool FITS = size_t(FLOATS) * 4 <= LDS_LIMIT && NKB % 4 == 0 && NVB % 4 == 0;
+    static constexpr int F_DB2 = F_DB1 + C;                                 // [NW][C]
+    static constexpr int F_DB3 = F_DB2 + NW * C;                            // [NW][C]
+    static constexpr int F_HD = F_DB3 + NW * C;                             // [NW][C] per-head dg partials
+    static constexpr int FLOATS = F_HD + NW * C;
+    static constexpr bool FITS = size_t(FLOATS) * 4 <= LDS_LIMIT && NB <= NW;
 };
 
-// Four consecutive values of T as loaded (converted to fp32 where used, so that a
-// load never has to complete where it is issued).
-template <typename T> struct Raw4;
-template <> struct Raw4<float> {
-    typedef floatx4 type;
-    __device__ static __forceinline__ floatx4 f32(floatx4 x) { return x; }
+// Eight consecutive values of T as loaded, and their bf16 hi + lo parts (bf16
+// inputs are exact: lo = 0, and the product with them takes one MFMA fewer).
+template <typename T> struct Raw8;
+template <> struct Raw8<float> {
+    typedef floatx4 type[2];
+    static constexpr bool EXACT = false;
 };
-template <> struct Raw4<bf16> {
-    typedef bf16x4 type;
-    __device__ static __forceinline__ floatx4 f32(bf16x4 x) {
-        return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+template <> struct Raw8<bf16> {
+    typedef bf16x8 type[1];
+    static constexpr bool EXACT = true;
+};
+// x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) for 8 fp32 values
+__device__ __forceinline__ void split8(const floatx4 (&x)[2], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float v = x[m >> 2][m & 3];
+        hi[m] = (bf16)v;
+        lo[m] = (bf16)(v - (float)hi[m]);
     }
-};
-
-template <typename T, int NB, int KPW>
-struct BwdFrag {                          // one 16-deep k step of phase 1
-    floatx4 o[NB], w[NB], dw[NB], s[KPW], ds[KPW], wi;
-    typename Raw4<T>::type v;
-};
-
-// Make one wave's LDS writes visible to its other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// a . b with a = ah + al, b = bh + bl in fp32 accumulation, the al.bl term dropped
+__device__ __forceinline__ floatx4 mfma_x3(floatx4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
 }
 
+// One 32-deep k step of phase 1, the operands a wave reads alone: its channel
+// block of S and dS', and row block I of W and V (8 values a lane)
+template <typename T>
+struct BwdFragB {
+    floatx4 s[2], ds[2], wi[2];
+    typename Raw8<T>::type v;
+};
+
 template <typename T, int DK, int DV, int C>
-__global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
+__global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* __restrict__ dO,
     const float* __restrict__ ck_state, const float* __restrict__ ck_dS, const float* __restrict__ ck_w,
@@ -645,13 +661,13 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ dg, float* __restrict__ dbeta, UnitMap um, int gate) {
     typedef BwdIntraCfg<DK, DV, C> Cfg;
-    constexpr int NB = Cfg::NB, NVB = Cfg::NVB, KPW = Cfg::KPW, VPW = Cfg::VPW;
-    constexpr int LC = Cfg::LC, LK = Cfg::LK, TL = Cfg::TL;
+    constexpr int NB = Cfg::NB, NVB = Cfg::NVB, NW = Cfg::NW, NT = Cfg::NT;
+    constexpr int LC = Cfg::LC, LK = Cfg::LK;
+    static_assert(NT == DK * 4, "launch bounds");
     __shared__ __attribute__((aligned(16))) float smem[Cfg::FLOATS];
     float* sT = smem + Cfg::F_T;            // T [C][C]
     float* sdP = smem + Cfg::F_DP;          // dP (lower)
     float* sdA = smem + Cfg::F_DA;          // dW V^T -> dT -> dA (lower)
-    float* sG = smem + Cfg::F_G;            // prefix sums of the clamped log-gate [C][DK]
     float* sXa = smem + Cfg::F_X;
     float* sBeta = smem + Cfg::F_BETA;
     float* sDb1 = smem + Cfg::F_DB1;
@@ -671,144 +687,189 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     // that loads need no branch and can all be in flight together
     auto crow = [&](int t) -> long { return grow(t < cnt ? t : 0); };
     const bool tri = wave < NB;             // owns the C x C column block I = wave
+    const int cw = 16 * wave + lr;          // this lane's channel
 
     const float* S = ck_state + unit * (long)DK * DV;      // start state [DK][DV]
     const float* dSn = ck_dS + unit * (long)DK * DV;       // cotangent of the end state
     const float* W = ck_w + unit * (long)C * DV;
     const float* dW = ck_dW + unit * (long)C * DV;
 
-    // ---- phase 0: T, beta, prefix sums G of the clamped log-gate (chunk-local)
+    // ---- phase 0: T and beta to LDS, the dbeta partials cleared
     {
-        constexpr int NT = C * C / 256 > 0 ? C * C / 256 : 1, NG = C * DK / 256;
-        float tv[NT], gl[NG];
+        constexpr int NTT = (C * C + NT - 1) / NT;
+        float tv[NTT];
 #pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int u = tid + 256 * x;
-            tv[x] = u < C * C ? ck_t[unit * (long)C * C + u] : 0.f;
-        }
-        // one branch on the layout outside the loops, so that all loads are in flight
-        if (gate == GATE_CHANNEL) {
-#pragma unroll
-            for (int x = 0; x < NG; ++x) gl[x] = g[crow((tid + 256 * x) / DK) * DK + tid % DK];
-        } else if (gate == GATE_HEAD) {
-#pragma unroll
-            for (int x = 0; x < NG; ++x) gl[x] = g[crow((tid + 256 * x) / DK)];
-        } else {
-#pragma unroll
-            for (int x = 0; x < NG; ++x) gl[x] = 0.f;
+        for (int x = 0; x < NTT; ++x) {
+            const int u = tid + NT * x;
+            tv[x] = ck_t[unit * (long)C * C + (u < C * C ? u : 0)];
         }
         const float bt = tid < C ? beta[crow(tid)] : 0.f;
 #pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int u = tid + 256 * x;
+        for (int x = 0; x < NTT; ++x) {
+            const int u = tid + NT * x;
             if (u < C * C) sT[(u / C) * LC + u % C] = tv[x];
         }
         if (tid < C) sBeta[tid] = valid(tid) ? bt : 0.f;
-        for (int u = tid; u < 4 * C; u += 256) sDb3[u] = 0.f;
-        // prefix sums down the rows: thread t holds channel t % DK of rows
-        // NSEG x + t / DK; running sums of its own rows, then the other threads'
-        // running sums of the same channel complete each prefix
-        constexpr int NSEG = 256 / DK;
-        const int hs = tid / DK;
-        float run = 0.f;
-#pragma unroll
-        for (int x = 0; x < NG; ++x) {
-            run += valid(NSEG * x + hs) ? clamp_g(gl[x]) : 0.f;
-            gl[x] = run;
-            sG[tid + 256 * x] = run;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int x = 0; x < NG; ++x)
-#pragma unroll
-            for (int h2 = 0; h2 < NSEG; ++h2) {
-                if (h2 < hs) gl[x] += sG[(NSEG * x + h2) * DK + tid % DK];
-                else if (h2 > hs && x > 0) gl[x] += sG[(NSEG * (x - 1) + h2) * DK + tid % DK];
-            }
-        __syncthreads();
-#pragma unroll
-        for (int x = 0; x < NG; ++x) sG[tid + 256 * x] = gl[x];
+        for (int u = tid; u < NW * C; u += NT) sDb3[u] = 0.f;
     }
     __syncthreads();
 
     // ---- phase 1: dQt = dO S^T, dWk = -dW S^T, dKb = W dS'^T, dgam, dP = dO W^T,
-    // dW V^T, contracted over the DV value channels 16 at a time
+    // dW V^T, contracted over the value channels 32 at a time
     float* sWk = sXa;                       // dWk [C][DK]  (phase 3 operand)
     float* sKt = sXa + C * LK;              // Kt = e^G K [C][DK]
-    floatx4 aQ[NB][KPW], aKb[NB][KPW];      // kept to the end
-    float dgam[KPW];
+    floatx4 aQ[NB], aKb[NB];                // kept to the end
+    float dgam = 0.f;
+    // this wave's raw gates and k, loaded while the last products run
+    float gr[NB][4], kv[NB][4];
     {
-        floatx4 aWk[NB][KPW], aP[NB], aV[NB];
+        floatx4 aWk[NB], aP[NB], aV[NB];
 #pragma unroll
-        for (int R = 0; R < NB; ++R) {
-            aP[R] = zero4(); aV[R] = zero4();
-#pragma unroll
-            for (int p = 0; p < KPW; ++p) { aQ[R][p] = zero4(); aWk[R][p] = zero4(); aKb[R][p] = zero4(); }
-        }
-#pragma unroll
-        for (int p = 0; p < KPW; ++p) dgam[p] = 0.f;
+        for (int R = 0; R < NB; ++R) aQ[R] = aKb[R] = aWk[R] = aP[R] = aV[R] = zero4();
 
-#define KDA_BWD_LOAD1(F, JS)                                                                      \
-    {                                                                                             \
-        const int jb = 16 * (JS) + 4 * kg;                                                        \
-        _Pragma("unroll") for (int R = 0; R < NB; ++R) {                                          \
-            const int r = 16 * R + lr;                                                            \
-            const floatx4 o_ = *reinterpret_cast<const floatx4*>(dO + crow(r) * DV + jb);         \
-            F.o[R] = valid(r) ? o_ : zero4();                                                     \
-            F.w[R] = *reinterpret_cast<const floatx4*>(W + r * DV + jb);                          \
-            F.dw[R] = *reinterpret_cast<const floatx4*>(dW + r * DV + jb);                        \
-        }                                                                                         \
-        _Pragma("unroll") for (int p = 0; p < KPW; ++p) {                                         \
-            const int c = 16 * (wave + 4 * p) + lr;                                               \
-            F.s[p] = *reinterpret_cast<const floatx4*>(S + c * DV + jb);                          \
-            F.ds[p] = *reinterpret_cast<const floatx4*>(dSn + c * DV + jb);                       \
-        }                                                                                         \
-        {                                                                                         \
-            const int i = 16 * (tri ? wave : 0) + lr;                                             \
-            F.wi = *reinterpret_cast<const floatx4*>(W + i * DV + jb);                            \
-            F.v = *reinterpret_cast<const typename Raw4<T>::type*>(v + crow(i) * DV + jb);        \
-        }                                                                                         \
-    }
-#define KDA_BWD_MMA1(F)                                                                           \
-    {                                                                                             \
-        _Pragma("unroll") for (int R = 0; R < NB; ++R) {                                          \
-            _Pragma("unroll") for (int p = 0; p < KPW; ++p) {                                     \
-                aQ[R][p] = mfma16(aQ[R][p], F.o[R], F.s[p]);                                      \
-                aWk[R][p] = mfma16(aWk[R][p], F.dw[R], F.s[p]);                                   \
-                aKb[R][p] = mfma16(aKb[R][p], F.w[R], F.ds[p]);                                   \
-            }                                                                                     \
-            if (tri && R >= wave) {                                                               \
-                const floatx4 vf_ = vrow_ok ? Raw4<T>::f32(F.v) : zero4();                         \
-                aP[R] = mfma16(aP[R], F.o[R], F.wi);                                              \
-                aV[R] = mfma16(aV[R], F.dw[R], vf_);                                              \
-            }                                                                                     \
-        }                                                                                         \
-        _Pragma("unroll") for (int p = 0; p < KPW; ++p)                                           \
-            dgam[p] += F.s[p][0] * F.ds[p][0] + F.s[p][1] * F.ds[p][1] + F.s[p][2] * F.ds[p][2] + \
-                       F.s[p][3] * F.ds[p][3];                                                    \
-    }
-        BwdFrag<T, NB, KPW> fa, fb;
-        const bool vrow_ok = valid(16 * wave + lr);
-        KDA_BWD_LOAD1(fa, 0);
-#pragma unroll 1
-        for (int js = 0; js < NVB; js += 2) {
-            KDA_BWD_LOAD1(fb, js + 1);
-            KDA_BWD_MMA1(fa);
-            KDA_BWD_LOAD1(fa, js + 2 < NVB ? js + 2 : js);  // the last one is a harmless reload
-            KDA_BWD_MMA1(fb);
+        // k step js covers value channels 32 js .. 32 js + 31; in the MFMA operand
+        // layout lane l holds channels 32 js + 8(l/16) .. +7 of its row (every
+        // product contracts over the value channels, contiguous in every array).
+        // The rows of dO, W and dW feed every wave: each step they are loaded once
+        // per workgroup, split into bf16 hi + lo and staged in LDS (two buffers, one
+        // barrier a step), loaded two steps ahead.  A wave's own operands (its
+        // channel block of S and dS', row block I of W and V) go into registers one
+        // step ahead.
+        constexpr int NJS = DV / 32, LS1 = Cfg::LS1;
+        // thread t takes the float4 pieces (row (t + NT h) / 8, channels 4 (t % 8) ..)
+        // of each of dO, W and dW; with C x 8 < NT only the first C x 8 threads do
+        constexpr int PPA = (C * 8 + NT - 1) / NT;
+        bf16* sStage = reinterpret_cast<bf16*>(sXa);        // [2 buffers][3 arrays][hi, lo][C rows][LS1]
+        auto stage_row = [&](int buf, int arr, int hl, int row) {
+            return sStage + (((buf * 3 + arr) * 2 + hl) * C + row) * LS1;
+        };
+        const int ac4 = tid & 7;
+        const float* pa[3][PPA];
+        bool arow_in[PPA], arow_ok[PPA];
+#pragma unroll
+        for (int hh = 0; hh < PPA; ++hh) {
+            const int row = (tid + NT * hh) >> 3;
+            arow_in[hh] = row < C;
+            const int rr = arow_in[hh] ? row : 0;
+            arow_ok[hh] = valid(rr);
+            pa[0][hh] = dO + crow(rr) * DV + 4 * ac4;
+            pa[1][hh] = W + rr * DV + 4 * ac4;
+            pa[2][hh] = dW + rr * DV + 4 * ac4;
         }
-#undef KDA_BWD_LOAD1
-#undef KDA_BWD_MMA1
+        floatx4 ra[2][3][PPA];
+        BwdFragB<T> rb;
+        auto load_a = [&](auto SL, int js) __attribute__((always_inline)) {
+            constexpr int d = SL;
+            const int col = 32 * (js < NJS ? js : NJS - 1);
+#pragma unroll
+            for (int a = 0; a < 3; ++a)
+#pragma unroll
+                for (int hh = 0; hh < PPA; ++hh) ra[d][a][hh] = *reinterpret_cast<const floatx4*>(pa[a][hh] + col);
+        };
+        auto stage_a = [&](auto SL, int buf) __attribute__((always_inline)) {
+            constexpr int d = SL;
+#pragma unroll
+            for (int hh = 0; hh < PPA; ++hh) {
+                if (!arow_in[hh]) continue;
+                const int row = (tid + NT * hh) >> 3;
+#pragma unroll
+                for (int a = 0; a < 3; ++a) {
+                    const floatx4 x = a == 0 && !arow_ok[hh] ? zero4() : ra[d][a][hh];
+                    bf16x4 hi, lo;
+                    split4(x, hi, lo);
+                    *reinterpret_cast<bf16x4*>(stage_row(buf, a, 0, row) + 4 * ac4) = hi;
+                    *reinterpret_cast<bf16x4*>(stage_row(buf, a, 1, row) + 4 * ac4) = lo;
+                }
+            }
+        };
+        const int iw = 16 * (tri ? wave : 0) + lr;          // row of W, V in the operand of dP, dW V^T
+        auto load_b = [&](int js) __attribute__((always_inline)) {
+            const int jb = 32 * (js < NJS ? js : NJS - 1) + 8 * kg;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                rb.s[h2] = *reinterpret_cast<const floatx4*>(S + cw * DV + jb + 4 * h2);
+                rb.ds[h2] = *reinterpret_cast<const floatx4*>(dSn + cw * DV + jb + 4 * h2);
+                rb.wi[h2] = *reinterpret_cast<const floatx4*>(W + iw * DV + jb + 4 * h2);
+            }
+            if constexpr (Raw8<T>::EXACT) {
+                rb.v[0] = *reinterpret_cast<const bf16x8*>(v + crow(iw) * DV + jb);
+            } else {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) rb.v[h2] = *reinterpret_cast<const floatx4*>(v + crow(iw) * DV + jb + 4 * h2);
+            }
+        };
+        const bool vrow_ok = valid(iw);
+        // one k step: its shared operands in LDS buffer js % 2, its own in rb
+        auto step = [&](auto SL, int js) __attribute__((always_inline)) {
+            constexpr int d = SL, d1 = 1 - SL;
+            __syncthreads();                                // buffer d staged; buffer d1 no longer read
+            bf16x8 sh, sl, dsh, dsl, wih, wil, vh, vl;
+            split8(rb.s, sh, sl);
+            split8(rb.ds, dsh, dsl);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) dgam += rb.s[m >> 2][m & 3] * rb.ds[m >> 2][m & 3];
+            split8(rb.wi, wih, wil);
+            if constexpr (Raw8<T>::EXACT) {
+                vh = rb.v[0];
+            } else {
+                split8(rb.v, vh, vl);
+            }
+            if (!vrow_ok) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) { vh[m] = (bf16)0.f; vl[m] = (bf16)0.f; }
+            }
+            load_b(js + 1);
+#pragma unroll
+            for (int R = 0; R < NB; ++R) {
+                const int o = (16 * R + lr) * LS1 + 8 * kg;
+                const bf16x8 oh = *reinterpret_cast<const bf16x8*>(stage_row(d, 0, 0, 0) + o);
+                const bf16x8 ol = *reinterpret_cast<const bf16x8*>(stage_row(d, 0, 1, 0) + o);
+                const bf16x8 wh = *reinterpret_cast<const bf16x8*>(stage_row(d, 1, 0, 0) + o);
+                const bf16x8 wl = *reinterpret_cast<const bf16x8*>(stage_row(d, 1, 1, 0) + o);
+                const bf16x8 dwh = *reinterpret_cast<const bf16x8*>(stage_row(d, 2, 0, 0) + o);
+                const bf16x8 dwl = *reinterpret_cast<const bf16x8*>(stage_row(d, 2, 1, 0) + o);
+                aQ[R] = mfma_x3(aQ[R], oh, ol, sh, sl);
+                aWk[R] = mfma_x3(aWk[R], dwh, dwl, sh, sl);
+                aKb[R] = mfma_x3(aKb[R], wh, wl, dsh, dsl);
+                if (tri && R >= wave) {
+                    aP[R] = mfma_x3(aP[R], oh, ol, wih, wil);
+                    if constexpr (Raw8<T>::EXACT) {
+                        aV[R] = mfma32(mfma32(aV[R], dwl, vh), dwh, vh);
+                    } else {
+                        aV[R] = mfma_x3(aV[R], dwh, dwl, vh, vl);
+                    }
+                }
+            }
+            stage_a(std::integral_constant<int, d1>{}, d1);   // step js + 1, read after the next barrier
+            load_a(std::integral_constant<int, d1>{}, js + 3);
+        };
+        load_a(std::integral_constant<int, 0>{}, 0);
+        load_b(0);
+        load_a(std::integral_constant<int, 1>{}, 1);
+        stage_a(std::integral_constant<int, 0>{}, 0);
+        load_a(std::integral_constant<int, 0>{}, 2);
+#pragma unroll 1
+        for (int js = 0; js < NJS; js += 2) {
+            step(std::integral_constant<int, 0>{}, js);
+            step(std::integral_constant<int, 1>{}, js + 1);
+        }
+        // this wave's raw gates and k (for G and Kt after dV, and the last phase)
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                const long o = crow(r) * DK + cw;
+                gr[R][e] = gate == GATE_CHANNEL ? g[o] : (gate == GATE_HEAD ? g[crow(r)] : 0.f);
+                kv[R][e] = to_f32(k[o]);
+            }
+        __syncthreads();                                    // the staging area is phase 3's from here
 
 #pragma unroll
         for (int R = 0; R < NB; ++R)
 #pragma unroll
-            for (int p = 0; p < KPW; ++p)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sWk[(16 * R + 4 * kg + e) * LK + 16 * (wave + 4 * p) + lr] = -aWk[R][p][e];
-#pragma unroll
-        for (int p = 0; p < KPW; ++p) dgam[p] = col_sum4(dgam[p]);
+            for (int e = 0; e < 4; ++e) sWk[(16 * R + 4 * kg + e) * LK + cw] = -aWk[R][e];
+        dgam = col_sum4(dgam);
         if (tri) {
             // column block I = wave of dP and dW V^T (lower part; zero above), and
             // the first dbeta term: (T^T dW V^T)_ii = sum_r T_ri (dW V^T)_ri
@@ -829,10 +890,8 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
             if (kg == 0) sDb1[i] = db;
         }
     }
-    // dV = Diag(beta) T^T dW: output tiles (R, J), wave w taking J = w, w + 4, ...
-#pragma unroll
-    for (int qv = 0; qv < VPW; ++qv) {
-        const int J = wave + 4 * qv;
+    // dV = Diag(beta) T^T dW: output tiles (R, J), wave w taking J = w, w + NW, ...
+    for (int J = wave; J < NVB; J += NW) {
         float bcol[NB][4];
 #pragma unroll
         for (int I = 0; I < NB; ++I)
@@ -852,30 +911,57 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
             }
         }
     }
-    // ---- phase 2: Kt = e^G K
+
+    // ---- phase 2: this wave's prefix sums G of the clamped log-gate (rows past
+    // the sequence end add nothing), its block boundaries, Kt = e^G K
+    //   gs[R] = G before block R, gm[R] = G at the end of block R (= gs[R + 1]), GC = G_C
+    float G[NB][4], gs[NB + 1];
+    unsigned floored = 0u;                  // the forward floors the log-gate at G_FLOOR: no gradient there
     {
-        constexpr int NK = (C * DK / 4 + 255) / 256;
-        typename Raw4<T>::type kl[NK];
+        float run = 0.f;
 #pragma unroll
-        for (int x = 0; x < NK; ++x) {
-            const int u = tid + 256 * x, uu = u < C * DK / 4 ? u : 0, r = (4 * uu) / DK, c0 = (4 * uu) % DK;
-            kl[x] = *reinterpret_cast<const typename Raw4<T>::type*>(k + crow(r) * DK + c0);
-        }
+        for (int R = 0; R < NB; ++R) {
+            float p4[4], acc = 0.f;
 #pragma unroll
-        for (int x = 0; x < NK; ++x) {
-            const int u = tid + 256 * x, r = (4 * u) / DK, c0 = (4 * u) % DK;
-            if (u < C * DK / 4) {
-                floatx4 kk = valid(r) ? Raw4<T>::f32(kl[x]) : zero4();
-#pragma unroll
-                for (int y = 0; y < 4; ++y) kk[y] *= __expf(sG[r * DK + c0 + y]);
-                *reinterpret_cast<floatx4*>(sKt + r * LK + c0) = kk;
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                floored |= (gr[R][e] < G_FLOOR ? 1u : 0u) << (4 * R + e);
+                acc += valid(r) ? clamp_g(gr[R][e]) : 0.f;
+                p4[e] = acc;
             }
+            // the four row groups of the block: lanes l%16 + 16 j hold group j
+            const float t0 = __shfl(acc, lr), t1 = __shfl(acc, lr + 16), t2 = __shfl(acc, lr + 32),
+                        t3 = __shfl(acc, lr + 48);
+            const float before = (kg > 0 ? t0 : 0.f) + (kg > 1 ? t1 : 0.f) + (kg > 2 ? t2 : 0.f);
+            gs[R] = run;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) G[R][e] = run + before + p4[e];
+            run += ((t0 + t1) + t2) + t3;
         }
+        gs[NB] = run;
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * kg + e;
+                if (!valid(r)) kv[R][e] = 0.f;
+                sKt[r * LK + cw] = kv[R][e] * __expf(G[R][e]);
+            }
     }
+    // q of this wave's elements, for the last phase
+    float qv[NB][4];
+#pragma unroll
+    for (int R = 0; R < NB; ++R)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * R + 4 * kg + e;
+            const float qx = to_f32(q[crow(r) * DK + cw]);
+            qv[R][e] = valid(r) ? qx : 0.f;
+        }
     __syncthreads();
 
     // ---- phase 3: dT = Diag-columns(beta) (dW V^T + dWk Kt^T) on the lower tiles
-    // (R, I = wave); T^T dWk on this wave's channel blocks, with the second dbeta
+    // (R, I = wave); T^T dWk on this wave's channel block, with the second dbeta
     // term, rows of (T^T dWk) Kt
     if (tri) {
 #pragma unroll
@@ -894,69 +980,25 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
             }
         }
     }
-    floatx4 aTd[NB][KPW];                   // T^T dWk, kept to the end
+    floatx4 aTd[NB];                        // T^T dWk, kept to the end
     {
-        float db[NB][4];
 #pragma unroll
-        for (int R = 0; R < NB; ++R)
+        for (int R = 0; R < NB; ++R) {
+            floatx4 acc = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) db[R][e] = 0.f;
+            for (int I = R; I < NB; ++I)
 #pragma unroll
-        for (int p = 0; p < KPW; ++p) {
-            const int cb = 16 * (wave + 4 * p);
-#pragma unroll
-            for (int R = 0; R < NB; ++R) {
-                floatx4 acc = zero4();
-#pragma unroll
-                for (int I = R; I < NB; ++I)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int i = 16 * I + 4 * kg + m;
-                        acc = mfma4(acc, sT[i * LC + 16 * R + lr], sWk[i * LK + cb + lr]);
-                    }
-                aTd[R][p] = acc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) db[R][e] += acc[e] * sKt[(16 * R + 4 * kg + e) * LK + cb + lr];
-            }
-        }
-#pragma unroll
-        for (int R = 0; R < NB; ++R)
+                for (int m = 0; m < 4; ++m) {
+                    const int i = 16 * I + 4 * kg + m;
+                    acc = mfma4(acc, sT[i * LC + 16 * R + lr], sWk[i * LK + cw]);
+                }
+            aTd[R] = acc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float x = row_sum16(db[R][e]);
+                const float x = row_sum16(acc[e] * sKt[(16 * R + 4 * kg + e) * LK + cw]);
                 if (lr == 0) sDb2[wave * C + 16 * R + 4 * kg + e] = x;
             }
-    }
-    // inputs of the last phase for this wave's elements, loaded ahead
-    float kv[KPW][NB][4], qv[KPW][NB][4], gv[KPW][NB][4];
-#pragma unroll
-    for (int p = 0; p < KPW; ++p)
-#pragma unroll
-        for (int R = 0; R < NB; ++R)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * R + 4 * kg + e, c = 16 * (wave + 4 * p) + lr;
-                const bool ok = valid(r);
-                const long o = crow(r) * DK + c;
-                const float kx = to_f32(k[o]), qx = to_f32(q[o]);
-                kv[p][R][e] = ok ? kx : 0.f;
-                qv[p][R][e] = ok ? qx : 0.f;
-            }
-    if (gate == GATE_CHANNEL) {
-#pragma unroll
-        for (int p = 0; p < KPW; ++p)
-#pragma unroll
-            for (int R = 0; R < NB; ++R)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    gv[p][R][e] = g[crow(16 * R + 4 * kg + e) * DK + 16 * (wave + 4 * p) + lr];
-    } else {
-#pragma unroll
-        for (int p = 0; p < KPW; ++p)
-#pragma unroll
-            for (int R = 0; R < NB; ++R)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) gv[p][R][e] = 0.f;
+        }
     }
     __syncthreads();
 
@@ -1010,153 +1052,127 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
     }
     __syncthreads();
 
-    // ---- phase 5, per wave over its channel blocks: the decays, the pairwise decays
+    // ---- phase 5, per wave over its channel block: the decays, the pairwise decays
     // of A and P, the prefix-sum adjoint.  Pairwise factors e^{G_r - G_i} (i <= r)
-    // are split at 16-row block boundaries so that every stored factor is <= 1: with
-    // Gs(R) the prefix sum before block R and Gm(I) the one at the end of block I,
-    //   Er_r = e^{G_r - Gs(R(r))},  Ei_r = e^{Gm(R(r)) - G_r},  B_RI = e^{Gs(R) - Gm(I)} (I < R).
+    // are split at 16-row block boundaries so that every factor formed is <= 1:
+    //   Er_r = e^{G_r - gs(R(r))},  Ei_r = e^{gm(R(r)) - G_r},  B_RI = e^{gs(R) - gm(I)} (I < R).
     // Inside one block, e^{G_r - G_i} = Er_r / Er_i, exact while the block's log-gate
-    // sum stays above -SAFE_SPAN; otherwise that channel's block is done term by term.
-    float* sKm = sXa + wave * 4 * TL;       // [16 channels][C] each: K Ei
-    float* sKs = sKm + TL;                  // K Er
-    float* sQs = sKs + TL;                  // Q Er
-    float* sKi = sQs + TL;                  // K / Er (safe blocks)
-    float hsum[NB][4];
-#pragma unroll
-    for (int R = 0; R < NB; ++R)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hsum[R][e] = 0.f;
-#pragma unroll
-    for (int p = 0; p < KPW; ++p) {
-        const int c = 16 * (wave + 4 * p) + lr;
-        float gs[NB], gm[NB];
+    // sum stays above -SAFE_SPAN; otherwise that block is done term by term.
+    // The B operands of the products (K Ei, K Er, Q Er, K / Er of row block I) are
+    // this lane's own values: lane l holds rows 16I + 4(l/16) + m, channel l%16.
+    // The row blocks run last to first, so that the prefix-sum adjoint (dg_t =
+    // dG_C + sum_{r >= t} dG_r, with dG_C from gam = e^{G_C} and Kb = e^{G_C - G} K)
+    // is carried along: a suffix sum over the rows (rows past the sequence end
+    // have dG = 0).
+    {
+        floatx4 km[NB], ks[NB], qs[NB];
+        bool safe[NB];
+        float gcp = 0.f;
 #pragma unroll
         for (int R = 0; R < NB; ++R) {
-            gs[R] = R ? sG[(16 * R - 1) * DK + c] : 0.f;
-            gm[R] = sG[(16 * R + 15) * DK + c];
-        }
-        const float GC = sG[(C - 1) * DK + c];
-        wave_lds_sync();                                    // the previous block's readers are done
-#pragma unroll
-        for (int R = 0; R < NB; ++R) {
-            floatx4 km, ks, qs, ki;
-            const bool safe = gm[R] - gs[R] >= -SAFE_SPAN;
+            safe[R] = gs[R + 1] - gs[R] >= -SAFE_SPAN;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float G = sG[(16 * R + 4 * kg + e) * DK + c];
-                const float er = __expf(G - gs[R]), ei = __expf(gm[R] - G);
-                km[e] = kv[p][R][e] * ei;
-                ks[e] = kv[p][R][e] * er;
-                qs[e] = qv[p][R][e] * er;
-                ki[e] = safe ? kv[p][R][e] * __expf(gs[R] - G) : 0.f;
+                const float er = __expf(G[R][e] - gs[R]), ei = __expf(gs[R + 1] - G[R][e]);
+                km[R][e] = kv[R][e] * ei;
+                ks[R][e] = kv[R][e] * er;
+                qs[R][e] = qv[R][e] * er;
+                gcp += __expf(gs[NB] - G[R][e]) * kv[R][e] * aKb[R][e];
             }
-            const int o = lr * LC + 16 * R + 4 * kg;
-            *reinterpret_cast<floatx4*>(sKm + o) = km;
-            *reinterpret_cast<floatx4*>(sKs + o) = ks;
-            *reinterpret_cast<floatx4*>(sQs + o) = qs;
-            *reinterpret_cast<floatx4*>(sKi + o) = ki;
         }
-        wave_lds_sync();
-        float dGv[NB][4], gcp = 0.f;
+        float carry = dgam * __expf(gs[NB]) + col_sum4(gcp);
 #pragma unroll
-        for (int R = 0; R < NB; ++R) {
+        for (int R = NB - 1; R >= 0; --R) {
             floatx4 xa = zero4(), xp = zero4(), ya = zero4(), yp = zero4();
 #pragma unroll
             for (int I = 0; I < R; ++I) {                          // earlier column blocks
-                const floatx4 fk = lds4(sKm + lr * LC + 16 * I + 4 * kg);
-                const floatx4 ta = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * I + 4 * kg), fk);
-                const floatx4 tp = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * I + 4 * kg), fk);
-                const float b = __expf(gs[R] - gm[I]);
+                const floatx4 ta = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * I + 4 * kg), km[I]);
+                const floatx4 tp = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * I + 4 * kg), km[I]);
+                const float b = __expf(gs[R] - gs[I + 1]);
                 xa += b * ta;
                 xp += b * tp;
             }
 #pragma unroll
             for (int I = R + 1; I < NB; ++I) {                     // later row blocks
-                const floatx4 ta = mfma16(zero4(), col4(sdA + (16 * I + 4 * kg) * LC + 16 * R + lr, LC),
-                                          lds4(sKs + lr * LC + 16 * I + 4 * kg));
-                const floatx4 tp = mfma16(zero4(), col4(sdP + (16 * I + 4 * kg) * LC + 16 * R + lr, LC),
-                                          lds4(sQs + lr * LC + 16 * I + 4 * kg));
-                const float b = __expf(gs[I] - gm[R]);
+                const floatx4 ta = mfma16(zero4(), col4(sdA + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), ks[I]);
+                const floatx4 tp = mfma16(zero4(), col4(sdP + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), qs[I]);
+                const float b = __expf(gs[I] - gs[R + 1]);
                 ya += b * ta;
                 yp += b * tp;
             }
-            // the diagonal block
-            const floatx4 fki = lds4(sKi + lr * LC + 16 * R + 4 * kg);
-            const floatx4 xad = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * R + 4 * kg), fki);
-            const floatx4 xpd = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * R + 4 * kg), fki);
-            const floatx4 yad = mfma16(zero4(), col4(sdA + (16 * R + 4 * kg) * LC + 16 * R + lr, LC),
-                                       lds4(sKs + lr * LC + 16 * R + 4 * kg));
-            const floatx4 ypd = mfma16(zero4(), col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC),
-                                       lds4(sQs + lr * LC + 16 * R + 4 * kg));
-            const bool safe = gm[R] - gs[R] >= -SAFE_SPAN;
+            // the diagonal block, with K / Er (safe blocks only)
+            floatx4 ki;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ki[e] = safe[R] ? kv[R][e] * __expf(gs[R] - G[R][e]) : 0.f;
+            const floatx4 xad = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
+            const floatx4 xpd = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
+            const floatx4 yad = mfma16(zero4(), col4(sdA + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), ks[R]);
+            const floatx4 ypd = mfma16(zero4(), col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), qs[R]);
             float XA[4], XP[4], YA[4], YP[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float G = sG[(16 * R + 4 * kg + e) * DK + c];
-                const float er = __expf(G - gs[R]), ei = __expf(gm[R] - G);
+                const float er = __expf(G[R][e] - gs[R]), ei = __expf(gs[R + 1] - G[R][e]);
                 XA[e] = er * xa[e];
                 XP[e] = er * xp[e];
                 YA[e] = ei * ya[e];
                 YP[e] = ei * yp[e];
-                if (safe) {
-                    const float ier = __expf(gs[R] - G);            // 1 / er
+                if (safe[R]) {
+                    const float ier = __expf(gs[R] - G[R][e]);      // 1 / er
                     XA[e] += er * xad[e];
                     XP[e] += er * xpd[e];
                     YA[e] += yad[e] * ier;
                     YP[e] += ypd[e] * ier;
                 }
             }
-            if (!safe) {                                            // the diagonal block term by term
+            if (!safe[R]) {                                         // the diagonal block term by term
+                // row i's G, k and q of this channel, from the lane holding row i (the
+                // same channel: safe[R] is the same in both lanes)
 #pragma unroll 1
                 for (int i = 16 * R; i < 16 * R + 16; ++i) {
-                    const float Gi = sG[i * DK + c];
-                    const float ki = valid(i) ? to_f32(k[grow(i) * DK + c]) : 0.f;
-                    const float qi = valid(i) ? to_f32(q[grow(i) * DK + c]) : 0.f;
+                    const int src = lr + 16 * ((i >> 2) & 3), ei2 = i & 3;
+                    float gsel = 0.f, ksel = 0.f, qsel = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        if (m == ei2) { gsel = G[R][m]; ksel = kv[R][m]; qsel = qv[R][m]; }
+                    const float Gi = __shfl(gsel, src), ki2 = __shfl(ksel, src), qi = __shfl(qsel, src);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * R + 4 * kg + e;
-                        const float G = sG[r * DK + c];
                         if (i <= r) {
-                            const float wd = __expf(G - Gi);
-                            if (i < r) XA[e] += sdA[r * LC + i] * ki * wd;
-                            XP[e] += sdP[r * LC + i] * ki * wd;
+                            const float wd = __expf(G[R][e] - Gi);
+                            if (i < r) XA[e] += sdA[r * LC + i] * ki2 * wd;
+                            XP[e] += sdP[r * LC + i] * ki2 * wd;
                         }
                         if (i >= r) {
-                            const float wu = __expf(Gi - G);
-                            if (i > r) YA[e] += sdA[i * LC + r] * ki * wu;
+                            const float wu = __expf(Gi - G[R][e]);
+                            if (i > r) YA[e] += sdA[i * LC + r] * ki2 * wu;
                             YP[e] += sdP[i * LC + r] * qi * wu;
                         }
                     }
                 }
             }
+            float dGv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * R + 4 * kg + e;
-                const float G = sG[r * DK + c];
-                const float E = __expf(G), F = __expf(GC - G);
-                const float kc = kv[p][R][e], qc = qv[p][R][e];
-                const float dKt = sBeta[r] * aTd[R][p][e], dQt = aQ[R][p][e], dKb = aKb[R][p][e];
+                const float E = __expf(G[R][e]), F = __expf(gs[NB] - G[R][e]);
+                const float kc = kv[R][e], qc = qv[R][e];
+                const float dKt = sBeta[r] * aTd[R][e], dQt = aQ[R][e], dKb = aKb[R][e];
                 const float dK = E * dKt + F * dKb + XA[e] + YA[e] + YP[e], dQ = E * dQt + XP[e];
-                dGv[R][e] = E * kc * dKt + E * qc * dQt - F * kc * dKb + kc * XA[e] - kc * YA[e] + qc * XP[e] -
-                            kc * YP[e];
-                gcp += F * kc * dKb;
+                dGv[e] = E * kc * dKt + E * qc * dQt - F * kc * dKb + kc * XA[e] - kc * YA[e] + qc * XP[e] -
+                         kc * YP[e];
                 if (valid(r)) {
-                    dq[grow(r) * DK + c] = dQ;
-                    dk[grow(r) * DK + c] = dK;
+                    dq[grow(r) * DK + cw] = dQ;
+                    dk[grow(r) * DK + cw] = dK;
                 }
             }
-        }
-        // prefix-sum adjoint: dg_t = dG_C + sum_{r >= t} dG_r, with dG_C from gam =
-        // e^{G_C} and Kb = e^{G_C - G} K; a suffix sum over the rows, last block first
-        // (rows past the sequence end have dG = 0)
-        float carry = dgam[p] * __expf(GC) + col_sum4(gcp);
-#pragma unroll
-        for (int R = NB - 1; R >= 0; --R) {
+            // suffix sums of dG over this block's rows (4 in the lane, then the row
+            // groups after it), on top of everything after the block
             float sfx[4];
-            sfx[3] = dGv[R][3];
-            sfx[2] = sfx[3] + dGv[R][2];
-            sfx[1] = sfx[2] + dGv[R][1];
-            sfx[0] = sfx[1] + dGv[R][0];
+            sfx[3] = dGv[3];
+            sfx[2] = sfx[3] + dGv[2];
+            sfx[1] = sfx[2] + dGv[1];
+            sfx[0] = sfx[1] + dGv[0];
             const float t1 = __shfl(sfx[0], lane + 16), t2 = __shfl(sfx[0], lane + 32), t3 = __shfl(sfx[0], lane + 48);
             const float after = (kg < 3 ? t1 : 0.f) + (kg < 2 ? t2 : 0.f) + (kg < 1 ? t3 : 0.f);
             const float base = carry + after;
@@ -1166,30 +1182,23 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_intra_kernel(
                 const int r = 16 * R + 4 * kg + e;
                 const float val = base + sfx[e];
                 if (gate == GATE_CHANNEL) {
-                    // the forward floors the log-gate at G_FLOOR: no gradient below it
-                    if (valid(r)) dg[grow(r) * DK + c] = gv[p][R][e] < G_FLOOR ? 0.f : val;
+                    if (valid(r)) dg[grow(r) * DK + cw] = (floored >> (4 * R + e)) & 1u ? 0.f : val;
                 } else {
-                    hsum[R][e] += row_sum16(val);
+                    const float hs = row_sum16(val);
+                    if (gate == GATE_HEAD && lr == 0) sHd[wave * C + r] = hs;
                 }
             }
         }
     }
-    if (gate == GATE_HEAD) {
-#pragma unroll
-        for (int R = 0; R < NB; ++R)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (lr == 0) sHd[wave * C + 16 * R + 4 * kg + e] = hsum[R][e];
-    }
     __syncthreads();
     if (tid < C && valid(tid)) {
         float db = sDb1[tid];
-        for (int w = 0; w < 4; ++w) db += sDb2[w * C + tid];
-        for (int w = 0; w < 4; ++w) db += sDb3[w * C + tid];
+        for (int w = 0; w < NW; ++w) db += sDb2[w * C + tid];
+        for (int w = 0; w < NW; ++w) db += sDb3[w * C + tid];
         dbeta[grow(tid)] = db;
         if (gate == GATE_HEAD) {
             float s = 0.f;
-            for (int w = 0; w < 4; ++w) s += sHd[w * C + tid];
+            for (int w = 0; w < NW; ++w) s += sHd[w * C + tid];
             dg[grow(tid)] = g[grow(tid)] < G_FLOOR ? 0.f : s;
         }
     }
@@ -1223,7 +1232,7 @@ static hipError_t launch_bwd(const BwdArgs& b) {
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || units == 0) return e;
-        hipLaunchKernelGGL((chunk_bwd_intra_kernel<T, DK, DV, C>), dim3((unsigned)units), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((chunk_bwd_intra_kernel<T, DK, DV, C>), dim3((unsigned)units), dim3(IC::NT), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, b.dO, a.ck_state, b.ck_dS,
                            a.ck_w, b.ck_dW, a.ck_t, a.ck_a, b.dq, b.dk, b.dv, b.dg, b.dbeta,
                            unit_map(a), a.gate);
