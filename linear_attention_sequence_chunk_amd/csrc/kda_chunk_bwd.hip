@@ -40,12 +40,18 @@ __device__ __forceinline__ floatx4 lds4(const float* p) { return *reinterpret_ca
 __device__ __forceinline__ floatx4 col4(const float* p, int ld) {
     return floatx4{p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
-// Sum over the 16 lanes holding one accumulator row.
+// Sum over the 16 lanes holding one accumulator row (one DPP row): rotations by 8
+// and 4 within the row, then the swaps inside each quad.  Every lane of the row
+// ends with the sum (in a lane-dependent order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row_sum16(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    return x + __shfl_xor(x, 8);
+    x += dpp_f<0x128>(x);       // row_ror:8
+    x += dpp_f<0x124>(x);       // row_ror:4
+    x += dpp_f<0x4E>(x);        // quad_perm [2, 3, 0, 1]
+    return x + dpp_f<0xB1>(x);  // quad_perm [1, 0, 3, 2]
 }
 // Sum over the four lanes holding one accumulator column.
 __device__ __forceinline__ float col_sum4(float x) {
@@ -644,6 +650,9 @@ __device__ __forceinline__ floatx4 mfma_x3(floatx4 acc, bf16x8 ah, bf16x8 al, bf
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
 }
 
+// Row block of lower tile t, the tiles (R, I <= R) taken in row order
+constexpr int lower_row(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
+
 // One 32-deep k step of phase 1, the operands a wave reads alone: its channel
 // block of S and dS', and row block I of W and V (8 values a lane)
 template <typename T>
@@ -961,25 +970,22 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
     __syncthreads();
 
     // ---- phase 3: dT = Diag-columns(beta) (dW V^T + dWk Kt^T) on the lower tiles
-    // (R, I = wave); T^T dWk on this wave's channel block, with the second dbeta
-    // term, rows of (T^T dWk) Kt
-    if (tri) {
-#pragma unroll
-        for (int R = 0; R < NB; ++R) {
-            if (R < wave) continue;
-            floatx4 acc = zero4();
+    // (R, I), tile t (in row order) on wave t % NW; T^T dWk on this wave's channel
+    // block, with the second dbeta term, rows of (T^T dWk) Kt
+    static_for<NB * (NB + 1) / 2>([&](auto TI) {
+        constexpr int t = TI, R = lower_row(t), I = t - R * (R + 1) / 2;
+        if (t % NW != wave) return;
+        floatx4 acc = zero4();
 #pragma unroll 4
-            for (int c0 = 0; c0 < DK; c0 += 16)
-                acc = mfma16(acc, lds4(sWk + (16 * R + lr) * LK + c0 + 4 * kg),
-                             lds4(sKt + (16 * wave + lr) * LK + c0 + 4 * kg));
-            const int i = 16 * wave + lr;
+        for (int c0 = 0; c0 < DK; c0 += 16)
+            acc = mfma16(acc, lds4(sWk + (16 * R + lr) * LK + c0 + 4 * kg), lds4(sKt + (16 * I + lr) * LK + c0 + 4 * kg));
+        const int i = 16 * I + lr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * R + 4 * kg + e;
-                if (i <= r) sdA[r * LC + i] = sBeta[i] * (sdA[r * LC + i] + acc[e]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * R + 4 * kg + e;
+            if (i <= r) sdA[r * LC + i] = sBeta[i] * (sdA[r * LC + i] + acc[e]);
         }
-    }
+    });
     floatx4 aTd[NB];                        // T^T dWk, kept to the end
     {
 #pragma unroll
@@ -1003,53 +1009,44 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
     __syncthreads();
 
     // ---- phase 4: X = T^T dT (lower tiles), then dM = -strict_lower(X T^T),
-    // dbeta += rows of dM A, dA = Diag(beta) dM
+    // dbeta += rows of dM A (partials by column block), dA = Diag(beta) dM; tile t on
+    // wave t % NW
     float* sXm = sXa;
-    if (tri) {
+    static_for<NB * (NB + 1) / 2>([&](auto TI) {
+        constexpr int t = TI, R = lower_row(t), I = t - R * (R + 1) / 2;
+        if (t % NW != wave) return;
+        floatx4 acc = zero4();
 #pragma unroll
-        for (int R = 0; R < NB; ++R) {
-            if (R < wave) continue;
-            floatx4 acc = zero4();
+        for (int M = R; M < NB; ++M)                                // T[m][r] = 0 for m < r
 #pragma unroll
-            for (int M = R; M < NB; ++M)                            // T[m][r] = 0 for m < r
+            for (int mm = 0; mm < 4; ++mm) {
+                const int m = 16 * M + 4 * kg + mm;
+                acc = mfma4(acc, sT[m * LC + 16 * R + lr], sdA[m * LC + 16 * I + lr]);
+            }
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const int m = 16 * M + 4 * kg + mm;
-                    acc = mfma4(acc, sT[m * LC + 16 * R + lr], sdA[m * LC + 16 * wave + lr]);
-                }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sXm[(16 * R + 4 * kg + e) * LC + 16 * wave + lr] = acc[e];
-        }
-    }
+        for (int e = 0; e < 4; ++e) sXm[(16 * R + 4 * kg + e) * LC + 16 * I + lr] = acc[e];
+    });
     __syncthreads();
-    if (tri) {
-        const int i = 16 * wave + lr;
-        float avs[NB][4];
+    static_for<NB * (NB + 1) / 2>([&](auto TI) {
+        constexpr int t = TI, R = lower_row(t), I = t - R * (R + 1) / 2;
+        if (t % NW != wave) return;
+        const int i = 16 * I + lr;
+        float av[4];
 #pragma unroll
-        for (int R = 0; R < NB; ++R)
+        for (int e = 0; e < 4; ++e) av[e] = ck_a[unit * (long)C * C + (16 * R + 4 * kg + e) * C + i];
+        floatx4 acc = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) avs[R][e] = ck_a[unit * (long)C * C + (16 * R + 4 * kg + e) * C + i];
+        for (int M = 0; M <= I; ++M)                                // T[i][m] = 0 for m > i
+            acc = mfma16(acc, lds4(sXm + (16 * R + lr) * LC + 16 * M + 4 * kg), lds4(sT + (16 * I + lr) * LC + 16 * M + 4 * kg));
 #pragma unroll
-        for (int R = 0; R < NB; ++R) {
-            if (R < wave) continue;
-            const float* av = avs[R];
-            floatx4 acc = zero4();
-#pragma unroll
-            for (int M = 0; M < NB; ++M) {                          // T[i][m] = 0 for m > i
-                if (M > wave) break;
-                acc = mfma16(acc, lds4(sXm + (16 * R + lr) * LC + 16 * M + 4 * kg),
-                             lds4(sT + (16 * wave + lr) * LC + 16 * M + 4 * kg));
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * R + 4 * kg + e;
-                const float dm = i < r ? -acc[e] : 0.f;
-                const float x = row_sum16(dm * av[e]);
-                if (lr == 0) sDb3[wave * C + r] = x;
-                sdA[r * LC + i] = sBeta[r] * dm;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * R + 4 * kg + e;
+            const float dm = i < r ? -acc[e] : 0.f;
+            const float x = row_sum16(dm * av[e]);
+            if (lr == 0) sDb3[I * C + r] = x;
+            sdA[r * LC + i] = sBeta[r] * dm;
         }
-    }
+    });
     __syncthreads();
 
     // ---- phase 5, per wave over its channel block: the decays, the pairwise decays
@@ -1059,69 +1056,70 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
     // Inside one block, e^{G_r - G_i} = Er_r / Er_i, exact while the block's log-gate
     // sum stays above -SAFE_SPAN; otherwise that block is done term by term.
     // The B operands of the products (K Ei, K Er, Q Er, K / Er of row block I) are
-    // this lane's own values: lane l holds rows 16I + 4(l/16) + m, channel l%16.
+    // formed from this lane's own values: lane l holds rows 16I + 4(l/16) + m,
+    // channel l%16.  e^G = e^{gs(R)} Er and e^{G_C - G} = e^{G_C - gm(R)} Ei.
     // The row blocks run last to first, so that the prefix-sum adjoint (dg_t =
     // dG_C + sum_{r >= t} dG_r, with dG_C from gam = e^{G_C} and Kb = e^{G_C - G} K)
     // is carried along: a suffix sum over the rows (rows past the sequence end
     // have dG = 0).
     {
-        floatx4 km[NB], ks[NB], qs[NB];
+        floatx4 er[NB], ei[NB];
         bool safe[NB];
         float gcp = 0.f;
 #pragma unroll
         for (int R = 0; R < NB; ++R) {
             safe[R] = gs[R + 1] - gs[R] >= -SAFE_SPAN;
+            const float fb = __expf(gs[NB] - gs[R + 1]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float er = __expf(G[R][e] - gs[R]), ei = __expf(gs[R + 1] - G[R][e]);
-                km[R][e] = kv[R][e] * ei;
-                ks[R][e] = kv[R][e] * er;
-                qs[R][e] = qv[R][e] * er;
-                gcp += __expf(gs[NB] - G[R][e]) * kv[R][e] * aKb[R][e];
+                er[R][e] = __expf(G[R][e] - gs[R]);
+                ei[R][e] = __expf(gs[R + 1] - G[R][e]);
+                gcp += fb * ei[R][e] * kv[R][e] * aKb[R][e];
             }
         }
+        auto v4 = [&](const float (&x)[4]) { return floatx4{x[0], x[1], x[2], x[3]}; };
         float carry = dgam * __expf(gs[NB]) + col_sum4(gcp);
 #pragma unroll
         for (int R = NB - 1; R >= 0; --R) {
             floatx4 xa = zero4(), xp = zero4(), ya = zero4(), yp = zero4();
 #pragma unroll
             for (int I = 0; I < R; ++I) {                          // earlier column blocks
-                const floatx4 ta = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * I + 4 * kg), km[I]);
-                const floatx4 tp = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * I + 4 * kg), km[I]);
+                const floatx4 km = v4(kv[I]) * ei[I];
+                const floatx4 ta = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * I + 4 * kg), km);
+                const floatx4 tp = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * I + 4 * kg), km);
                 const float b = __expf(gs[R] - gs[I + 1]);
                 xa += b * ta;
                 xp += b * tp;
             }
 #pragma unroll
             for (int I = R + 1; I < NB; ++I) {                     // later row blocks
-                const floatx4 ta = mfma16(zero4(), col4(sdA + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), ks[I]);
-                const floatx4 tp = mfma16(zero4(), col4(sdP + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), qs[I]);
+                const floatx4 ta = mfma16(zero4(), col4(sdA + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), v4(kv[I]) * er[I]);
+                const floatx4 tp = mfma16(zero4(), col4(sdP + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), v4(qv[I]) * er[I]);
                 const float b = __expf(gs[I] - gs[R + 1]);
                 ya += b * ta;
                 yp += b * tp;
             }
             // the diagonal block, with K / Er (safe blocks only)
-            floatx4 ki;
+            floatx4 ier;                                            // 1 / Er (safe blocks only)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ki[e] = safe[R] ? kv[R][e] * __expf(gs[R] - G[R][e]) : 0.f;
+            for (int e = 0; e < 4; ++e) ier[e] = safe[R] ? __expf(gs[R] - G[R][e]) : 0.f;
+            const floatx4 ki = v4(kv[R]) * ier;
             const floatx4 xad = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
             const floatx4 xpd = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
-            const floatx4 yad = mfma16(zero4(), col4(sdA + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), ks[R]);
-            const floatx4 ypd = mfma16(zero4(), col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), qs[R]);
+            const floatx4 yad = mfma16(zero4(), col4(sdA + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), v4(kv[R]) * er[R]);
+            const floatx4 ypd = mfma16(zero4(), col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), v4(qv[R]) * er[R]);
             float XA[4], XP[4], YA[4], YP[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float er = __expf(G[R][e] - gs[R]), ei = __expf(gs[R + 1] - G[R][e]);
-                XA[e] = er * xa[e];
-                XP[e] = er * xp[e];
-                YA[e] = ei * ya[e];
-                YP[e] = ei * yp[e];
+                XA[e] = er[R][e] * xa[e];
+                XP[e] = er[R][e] * xp[e];
+                YA[e] = ei[R][e] * ya[e];
+                YP[e] = ei[R][e] * yp[e];
                 if (safe[R]) {
-                    const float ier = __expf(gs[R] - G[R][e]);      // 1 / er
-                    XA[e] += er * xad[e];
-                    XP[e] += er * xpd[e];
-                    YA[e] += yad[e] * ier;
-                    YP[e] += ypd[e] * ier;
+                    XA[e] += er[R][e] * xad[e];
+                    XP[e] += er[R][e] * xpd[e];
+                    YA[e] += yad[e] * ier[e];
+                    YP[e] += ypd[e] * ier[e];
                 }
             }
             if (!safe[R]) {                                         // the diagonal block term by term
@@ -1152,10 +1150,11 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
                 }
             }
             float dGv[4];
+            const float ea = __expf(gs[R]), fa = __expf(gs[NB] - gs[R + 1]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * R + 4 * kg + e;
-                const float E = __expf(G[R][e]), F = __expf(gs[NB] - G[R][e]);
+                const float E = ea * er[R][e], F = fa * ei[R][e];
                 const float kc = kv[R][e], qc = qv[R][e];
                 const float dKt = sBeta[r] * aTd[R][e], dQt = aQ[R][e], dKb = aKb[R][e];
                 const float dK = E * dKt + F * dKb + XA[e] + YA[e] + YP[e], dQ = E * dQt + XP[e];
