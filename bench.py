@@ -480,7 +480,8 @@ def bench_backward(torch, g, w, steps=5, warmup=2):
     del a, dO
     tps = lambda t: round(w.B * w.T / (t / 1e3), 1)
     return {"ms_per_call": round(ms, 3), "tokens_per_s": tps(ms), "calls": steps,
-            "note": "fp32 gradient arithmetic; includes re-running the forward stages",
+            "note": "gradients accumulated in fp32 (fp32 operands of bf16 MFMA split into hi + lo parts); "
+                    "includes re-running the forward stages",
             "fused_pre": {"ms_per_call": round(ms_pre, 3), "tokens_per_s": tps(ms_pre),
                           "note": "gradients of raw q, k and the bf16 gate pre-activation"}}
 

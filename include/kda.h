@@ -287,7 +287,9 @@ size_t kda_chunk_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
  *   dS0           [B,H,dk,dv] fp32 or NULL
  *   workspace     >= kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, in_dtype, C)
  * Supported: C in {16, 32, 64, 128} (C = 128 runs as 64-token chunks); dk, dv
- * in {64, 128}; in_dtype BF16 or F32 (the gradient arithmetic is fp32).  Outputs must not overlap any input, the
+ * in {64, 128}; in_dtype BF16 or F32.  Gradients accumulate in fp32; products of fp32
+ * operands run on bf16 MFMA with each operand split into bf16 hi + lo parts (about
+ * 16 significant bits, the lo x lo term dropped).  Outputs must not overlap any input, the
  * workspace or each other.  Alignment: q, k, v and the workspace 16 bytes,
  * per-channel g 16 bytes, everything else 4 bytes.  Deterministic (no
  * floating-point atomics).

@@ -13,11 +13,11 @@ from tests.parity import assert_close, cuda
 
 pytestmark = pytest.mark.gpu
 
-# fp32 inputs: the fp32-path bar of 1e-4 x scale (measured worst ~7e-6 x scale); bf16
-# inputs: 2e-2 x scale.  The gradient arithmetic is fp32 (for bf16 inputs with C >= 32 the reverse chain
-# runs on bf16 MFMA with its fp32 operands split into bf16 hi + lo parts); with
-# bf16 inputs the forward stages that are re-run for the backward use bf16 MFMA
-# operands (as in the forward pass)
+# fp32 inputs: the fp32-path bar of 1e-4 x scale; bf16 inputs: 2e-2 x scale.  Gradients
+# accumulate in fp32; the products over the value channels (and, for bf16 inputs with
+# C >= 32, the reverse chain) run on bf16 MFMA with their fp32 operands split into
+# bf16 hi + lo parts (about 16 significant bits); with bf16 inputs the forward stages
+# that are re-run for the backward use bf16 MFMA operands (as in the forward pass)
 BWD_TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 
 
