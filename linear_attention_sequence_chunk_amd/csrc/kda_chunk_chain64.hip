@@ -222,7 +222,8 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
         KDA_C64_PREFETCH_1(d, unit_of(n + D < NC ? n + D : NC - 1));
         __syncthreads();                                            // W^T complete
 
-        // ---- phase 2: O waves O += P W (stored); all waves S = gam S + Kb^T W
+        // ---- phase 2: O waves O += P W; all waves S = gam S + Kb^T W and the next
+        // S^T (what the next chunk waits for) before the O waves store their outputs
         if (!wW) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -233,20 +234,6 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
                     const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sWT + (jt * 16 + fr) * LDC + u * 32 + fk);
                     acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp, fb, acc[jt], 0, 0, 0);
                 }
-            }
-            // this wave's 16 x DVS output tile, through its own LDS rows, as 16-byte row pieces
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sO[(4 * (lane >> 4) + e) * DVS + jt * 16 + fr] = from_f32<TOut>(acc[jt][e]);
-            constexpr int EO = 16 / sizeof(TOut), PPR = DVS / EO, NUO = 16 * PPR;   // pieces per row, per tile
-#pragma unroll
-            for (int u = lane; u < NUO; u += 64) {
-                const int r = u / PPR, jj = (u % PPR) * EO;
-                const int tt = (c0 + n) * C + R * 16 + r;
-                if (sr.tok_begin + tt < sr.tok_end)
-                    *reinterpret_cast<u32x4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj) =
-                        *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
             }
         }
         {
@@ -266,6 +253,22 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
             }
         }
         write_state_operand();                                      // read only after the next barrier
+        if (!wW) {
+            // this wave's 16 x DVS output tile, through its own LDS rows, as 16-byte row pieces
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sO[(4 * (lane >> 4) + e) * DVS + jt * 16 + fr] = from_f32<TOut>(acc[jt][e]);
+            constexpr int EO = 16 / sizeof(TOut), PPR = DVS / EO, NUO = 16 * PPR;   // pieces per row, per tile
+#pragma unroll
+            for (int u = lane; u < NUO; u += 64) {
+                const int r = u / PPR, jj = (u % PPR) * EO;
+                const int tt = (c0 + n) * C + R * 16 + r;
+                if (sr.tok_begin + tt < sr.tok_end)
+                    *reinterpret_cast<u32x4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj) =
+                        *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
+            }
+        }
         KDA_C64_PREFETCH_2(d, unit_of(n + D < NC ? n + D : NC - 1));
     };
     // whole rounds of D chunks with no condition inside (the loads in flight are
