@@ -14,8 +14,9 @@
 // then through the decays Kt = e^G K, Qt = e^G Q, Kb = e^{G_C - G} K, gam =
 // e^{G_C}, the pairwise decays inside A and P, and the prefix sum G of g.
 // The forward state S and W of every chunk, and T and A, are kept by the forward
-// stages run in their generic format (fp32 checkpoints).  All gradient
-// arithmetic is fp32.
+// stages run in their generic format (fp32 checkpoints).  Gradients accumulate
+// in fp32; products of fp32 operands over the long dimensions run on bf16 MFMA
+// with each operand split into bf16 hi + lo parts (about 16 significant bits).
 #include "kda_chunk.h"
 
 namespace kda {
