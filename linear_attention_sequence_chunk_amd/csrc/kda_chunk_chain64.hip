@@ -308,7 +308,10 @@ template <int DV>
 struct Maps64Cfg {
     static constexpr int C = 64, DK = 128, N = DV + DK, NCT = N / 16, NVT = DV / 16;
     static constexpr int NJ1 = NCT / 4, NJ2 = NCT / 2;
-    static constexpr int LDK = DK + 24, LDC = C + 16;           // as Chain64Cfg
+    // padded bf16 rows of S^T and W^T: 40 and 8 elements, measured against the chain's
+    // 24 and 16 and other multiples of 8 (bank conflicts; 1M workload: chain stage
+    // 8.30-8.33 -> 8.02-8.05 ms, outputs bitwise unchanged)
+    static constexpr int LDK = DK + 40, LDC = C + 8;
     static constexpr int NWK = C * DK * 2 / 16 / 512, NUV = C * DV * 2 / 16 / 512;   // 16-byte loads a lane
     static constexpr size_t OFF_ST = 0;                                          // S^T [N][LDK]
     static constexpr size_t OFF_WT = OFF_ST + size_t(N) * LDK * 2;               // W^T [N][LDC]
