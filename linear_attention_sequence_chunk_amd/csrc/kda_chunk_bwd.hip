@@ -1082,33 +1082,34 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
         float carry = dgam * __expf(gs[NB]) + col_sum4(gcp);
 #pragma unroll
         for (int R = NB - 1; R >= 0; --R) {
+            // each term's block factor rides on its B operand, so that the terms of
+            // XA, XP, YA and YP each accumulate in one MFMA chain:
+            //   XA = Er (sum_{I<R} dA_RI (B_RI Km_I) + dA_RR Ki),
+            //   YA = Ei (sum_{I>R} dA^T_RI (B_IR Ks_I) + e^{-tot_R} dA^T_RR Ks_R),
+            // with Ki = K / Er and e^{-tot_R} = (1/Er) / Ei on safe blocks (at most
+            // e^SAFE_SPAN, finite in fp32), both zero on unsafe ones (done term by term)
             floatx4 xa = zero4(), xp = zero4(), ya = zero4(), yp = zero4();
 #pragma unroll
             for (int I = 0; I < R; ++I) {                          // earlier column blocks
-                const floatx4 km = v4(kv[I]) * ei[I];
-                const floatx4 ta = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * I + 4 * kg), km);
-                const floatx4 tp = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * I + 4 * kg), km);
-                const float b = __expf(gs[R] - gs[I + 1]);
-                xa += b * ta;
-                xp += b * tp;
+                const floatx4 km = v4(kv[I]) * ei[I] * __expf(gs[R] - gs[I + 1]);
+                xa = mfma16(xa, lds4(sdA + (16 * R + lr) * LC + 16 * I + 4 * kg), km);
+                xp = mfma16(xp, lds4(sdP + (16 * R + lr) * LC + 16 * I + 4 * kg), km);
             }
-#pragma unroll
-            for (int I = R + 1; I < NB; ++I) {                     // later row blocks
-                const floatx4 ta = mfma16(zero4(), col4(sdA + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), v4(kv[I]) * er[I]);
-                const floatx4 tp = mfma16(zero4(), col4(sdP + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), v4(qv[I]) * er[I]);
-                const float b = __expf(gs[I] - gs[R + 1]);
-                ya += b * ta;
-                yp += b * tp;
-            }
-            // the diagonal block, with K / Er (safe blocks only)
             floatx4 ier;                                            // 1 / Er (safe blocks only)
 #pragma unroll
             for (int e = 0; e < 4; ++e) ier[e] = safe[R] ? __expf(gs[R] - G[R][e]) : 0.f;
             const floatx4 ki = v4(kv[R]) * ier;
-            const floatx4 xad = mfma16(zero4(), lds4(sdA + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
-            const floatx4 xpd = mfma16(zero4(), lds4(sdP + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
-            const floatx4 yad = mfma16(zero4(), col4(sdA + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), v4(kv[R]) * er[R]);
-            const floatx4 ypd = mfma16(zero4(), col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), v4(qv[R]) * er[R]);
+            xa = mfma16(xa, lds4(sdA + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
+            xp = mfma16(xp, lds4(sdP + (16 * R + lr) * LC + 16 * R + 4 * kg), ki);
+#pragma unroll
+            for (int I = R + 1; I < NB; ++I) {                     // later row blocks
+                const float b = __expf(gs[I] - gs[R + 1]);
+                ya = mfma16(ya, col4(sdA + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), v4(kv[I]) * er[I] * b);
+                yp = mfma16(yp, col4(sdP + (16 * I + 4 * kg) * LC + 16 * R + lr, LC), v4(qv[I]) * er[I] * b);
+            }
+            const float td = safe[R] ? __expf(gs[R] - gs[R + 1]) : 0.f;
+            ya = mfma16(ya, col4(sdA + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), v4(kv[R]) * er[R] * td);
+            yp = mfma16(yp, col4(sdP + (16 * R + 4 * kg) * LC + 16 * R + lr, LC), v4(qv[R]) * er[R] * td);
             float XA[4], XP[4], YA[4], YP[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1116,12 +1117,6 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
                 XP[e] = er[R][e] * xp[e];
                 YA[e] = ei[R][e] * ya[e];
                 YP[e] = ei[R][e] * yp[e];
-                if (safe[R]) {
-                    XA[e] += er[R][e] * xad[e];
-                    XP[e] += er[R][e] * xpd[e];
-                    YA[e] += yad[e] * ier[e];
-                    YP[e] += ypd[e] * ier[e];
-                }
             }
             if (!safe[R]) {                                         // the diagonal block term by term
                 // row i's G, k and q of this channel, from the lane holding row i (the
