@@ -333,14 +333,18 @@ def gpu_clocks(torch, plan, steps=60, samples=12):
         for _ in range(steps):
             plan.run()
         time.sleep(0.05)
-        gfx, mem = [], []
+        gfx, mem, sleep = [], [], []
         while len(gfx) < samples and not stream.query():
-            gfx.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+            g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            gfx.append(g["clk"])
+            sleep.append(g.get("clk_deep_sleep"))
             mem.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"])
             time.sleep(0.02)
         torch.cuda.synchronize()
-        return {"gfx_mhz_samples": gfx, "gfx_max_mhz": gmax, "mem_mhz": max(mem) if mem else None,
-                "note": "sampled while untimed steps ran, after the timed region"}
+        return {"gfx_mhz_samples": gfx, "gfx_deep_sleep": sleep, "gfx_max_mhz": gmax,
+                "mem_mhz": max(mem) if mem else None,
+                "note": "sampled while untimed steps ran, after the timed region; each reading with "
+                        "the deep-sleep flag the management library reports beside it"}
     except Exception as e:                 # a clock reading must never fail the bench
         torch.cuda.synchronize()
         return {"error": type(e).__name__}
