@@ -104,8 +104,10 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv,
  * sequence in, for these sizes (0 if unsupported); host-only.  The recurrence
  * across chunks is serial (section 十五 of the explainer: one step at a time);
  * when B*H is too small to fill the GPU and T is long, each sequence is cut
- * into segments whose affine state maps S -> M S + E are computed side by side,
- * composed in order, and every segment then re-runs from its true start state.
+ * into segments: the first runs from the initial state while the affine state
+ * maps S -> M S + E of the others are computed side by side; the maps are
+ * composed in order, and every later segment then runs from its true start
+ * state.
  * 1 means the plain sequential chain.  The result equals the sequential chain
  * up to rounding; the workspace (kda_chunk_fwd_workspace_bytes) includes the
  * segments' maps and start states.

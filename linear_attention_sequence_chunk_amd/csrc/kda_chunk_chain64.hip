@@ -16,21 +16,23 @@
 //   all waves           : state rows 16*wave .. +15:  S <- gam S + Kb^T W
 // Two barriers per chunk: S^T ready -> (W, Qt S) -> W^T ready -> (P W, S update).
 //
-// Long sequences with few (sequence, head) pairs are cut into segments of L
-// chunks that run side by side (segment-affine form).  A segment maps its start
-// state to its end state affinely, S -> M S + E, with M = prod over its chunks of
-// (Diag(gam) - Kb^T Wk) and E its end state from a zero start.  Three launches:
-//   maps  (chain_maps64_kernel): each segment but the last runs the chain,
-//         without outputs, on the augmented state [S | I]: value columns from a
-//         zero start (segment 0 from the call's initial state) give E, the dk
-//         extra columns from the identity with U taken as 0 give M;
+// Long sequences with few (sequence, head) pairs are cut into segments (segment 0
+// of L0 chunks, the others of L) that run side by side (segment-affine form).  A
+// segment maps its start state to its end state affinely, S -> M S + E, with
+// M = prod over its chunks of (Diag(gam) - Kb^T Wk) and E its end state from a
+// zero start.  Three launches:
+//   first (chain_maps64_kernel): segment 0 runs the chain with outputs from the
+//         call's initial state and keeps its end state as E_0; beside it, each
+//         segment 1 .. nseg - 2 runs the chain without outputs on the augmented
+//         state [S | I]: value columns from a zero start give E, the dk extra
+//         columns from the identity with U taken as 0 give M;
 //   scan  (chain_seg_scan_kernel): start states Sst_0 = S0, Sst_1 = E_0,
 //         Sst_{s+1} = M_s Sst_s + E_s, in fp32;
-//   outputs (CHAIN_SEG): every segment runs the chain with outputs from its
-//         start state; the last writes the final state.
+//   outputs (CHAIN_SEG): segments 1 .. nseg - 1 run the chain with outputs from
+//         their start states; the last writes the final state.
 // This is the chunk recurrence regrouped (the state after a chunk is an affine
 // function of the state before it), so the result equals the sequential chain
-// up to rounding; the extra cost is the maps launch.
+// up to rounding; the extra cost is the maps.
 #include "kda_chunk.h"
 
 namespace kda {
@@ -64,54 +66,46 @@ struct Chain64Cfg {
 // Segments of a long sequence (maps and CHAIN_SEG launches); per (sequence, head) pair
 // bh and segment s, the arrays hold [bh][s][DK][...] fp32.
 struct Seg64 {
-    int L;                  // chunks per segment
+    int L0;                 // chunks of segment 0
+    int L;                  // chunks of every later segment (the last may have fewer)
     int nseg;               // segments per (sequence, head)
     float* E;               // end state from a zero start (segment 0: from S0), [.][.][DK][DV]
     float* M;               // linear part of the segment's map, [.][.][DK][DK]
     float* Sst;             // start state of each segment, [.][.][DK][DV]
 };
+__device__ inline int seg_first(const Seg64& sg, int s) { return s == 0 ? 0 : sg.L0 + (s - 1) * sg.L; }
+__device__ inline int seg_chunks(const Seg64& sg, int s, int nchunks) {
+    const int c0 = seg_first(sg, s), len = s == 0 ? sg.L0 : sg.L;
+    return nchunks - c0 < len ? nchunks - c0 : len;
+}
 
+// The chain of one work item and slice of DVS value columns: a (sequence, head)
+// pair (CHAIN_PLAIN), or segment seg_lo + item % seg_cnt of pair item / seg_cnt
+// (CHAIN_SEG).  smem holds Cfg::TOTAL bytes.
 template <typename TOut, int DV, int DVS, int MODE>
-__global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
+__device__ __forceinline__ void chain64_run(
+    char* smem, long item, int sl, int seg_lo, int seg_cnt,
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
-    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um, Seg64 sg) {
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, const UnitMap& um,
+    const Seg64& sg) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
-    constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, NSL = Cfg::NSL, LDK = Cfg::LDK, LDC = Cfg::LDC;
+    constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, LDK = Cfg::LDK, LDC = Cfg::LDC;
     constexpr int D = Cfg::DEPTH;
 
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
     bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
     bf16* sWT = reinterpret_cast<bf16*>(smem + Cfg::OFF_WT);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // Slices of one work item (a (sequence, head) pair, or one of its segments)
-    // share an XCD (workgroups are dealt to the 8 XCDs round-robin), so the
-    // per-chunk operands they all read come from one L2.
-    long item;
-    int sl;
-    {
-        const long nwg = (long)gridDim.x, id = blockIdx.x;
-        if (!um.cu_seqlens && nwg % (8 * NSL) == 0) {
-            const long xcd = id % 8, local = id / 8;
-            sl = (int)(local % NSL);
-            item = (local / NSL) * 8 + xcd;
-        } else {
-            item = id / NSL;
-            sl = (int)(id % NSL);
-        }
-    }
     // work item -> (sequence, head) pair and segment
-    const int nsegw = MODE == CHAIN_PLAIN ? 1 : sg.nseg;
-    const long bh = item / nsegw;
-    const int seg = (int)(item % nsegw);
+    const long bh = item / seg_cnt;
+    const int seg = seg_lo + (int)(item % seg_cnt);
     const int j0 = sl * DVS;                      // first value column of the slice
     // sequence (batch row, or packed sequence) and head; its chunks and tokens
     const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
     const SeqRange sr = seq_range(um, sq);
-    const int c0 = MODE == CHAIN_PLAIN ? 0 : seg * sg.L;                      // first chunk of the segment
-    const int NC = MODE == CHAIN_PLAIN ? sr.nchunks
-                                       : (sr.nchunks - c0 < sg.L ? sr.nchunks - c0 : sg.L);
+    const int c0 = MODE == CHAIN_PLAIN ? 0 : seg_first(sg, seg);              // first chunk of the segment
+    const int NC = MODE == CHAIN_PLAIN ? sr.nchunks : seg_chunks(sg, seg, sr.nchunks);
     auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, c0 + n, sr.chunk0); };
 
     const bool wW = wave < 4;                    // uniform per wave
@@ -166,9 +160,9 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
     }
 
     // ---- state rows 16*ct + 4(l/16) + e, columns j0 + 16 jt + l%16, fp32 in accumulators
-    // start: the call's initial state (plain), or the segment's start state (outputs launch)
-    const float* init = MODE == CHAIN_SEG ? sg.Sst + (bh * sg.nseg + seg) * (long)(DK * DV)
-                                          : (s0 ? s0 + bh * (long)(DK * DV) : nullptr);
+    // start: the call's initial state (plain; segment 0), or the segment's start state
+    const float* init = MODE == CHAIN_SEG && seg > 0 ? sg.Sst + (bh * sg.nseg + seg) * (long)(DK * DV)
+                                                     : (s0 ? s0 + bh * (long)(DK * DV) : nullptr);
     floatx4 accS[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
@@ -279,17 +273,47 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
         if (n0 + DI < NC) step(DI, n0 + DI);
     });
 
-    // end state: the call's final state (plain; the last segment of the outputs launch)
-    if (MODE == CHAIN_PLAIN || seg == sg.nseg - 1) {
-        if (sT) {
-            float* fin = sT + bh * (long)(DK * DV);
+    // end state: the call's final state (plain; the last segment), or segment 0's
+    // end state E_0, which the scan takes as segment 1's start state
+    float* fin = nullptr;
+    if (MODE == CHAIN_PLAIN || seg == sg.nseg - 1) fin = sT ? sT + bh * (long)(DK * DV) : nullptr;
+    else if (seg == 0) fin = sg.E + (bh * sg.nseg) * (long)(DK * DV);
+    if (fin) {
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
+        for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    fin[(ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr] = accS[jt][e];
+            for (int e = 0; e < 4; ++e)
+                fin[(ct * 16 + 4 * (lane >> 4) + e) * (long)DV + j0 + jt * 16 + fr] = accS[jt][e];
+    }
+}
+
+template <typename TOut, int DV, int DVS, int MODE>
+__global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
+    const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
+    const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
+    const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um, Seg64 sg,
+    int seg_lo, int seg_cnt) {
+    typedef Chain64Cfg<TOut, DV, DVS> Cfg;
+    constexpr int NSL = Cfg::NSL;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    // Slices of one work item (a (sequence, head) pair, or one of its segments)
+    // share an XCD (workgroups are dealt to the 8 XCDs round-robin), so the
+    // per-chunk operands they all read come from one L2.
+    long item;
+    int sl;
+    {
+        const long nwg = (long)gridDim.x, id = blockIdx.x;
+        if (!um.cu_seqlens && nwg % (8 * NSL) == 0) {
+            const long xcd = id % 8, local = id / 8;
+            sl = (int)(local % NSL);
+            item = (local / NSL) * 8 + xcd;
+        } else {
+            item = id / NSL;
+            sl = (int)(id % NSL);
         }
     }
+    chain64_run<TOut, DV, DVS, MODE>(smem, item, sl, seg_lo, seg_cnt, ws_qt, ws_wk, ws_kb, ws_p, ws_u, ws_gam,
+                                     s0, o, sT, um, sg);
 }
 
 // The maps launch with the whole augmented state [S | I] (DV + DK columns) in one
@@ -323,14 +347,24 @@ struct Maps64Cfg {
     static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
-template <int DV, int MD>
+// The first launch of the segmented chain: workgroups 0 .. nout - 1 run segment 0
+// of each (sequence, head) pair with its outputs (its start state is the call's
+// S0, and its end state is E_0); the others the maps of segments 1 .. nseg - 2.
+template <typename TOut, int DV, int MD>
 __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
-    const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb, const bf16* __restrict__ ws_u,
-    const float* __restrict__ ws_gam, const float* __restrict__ s0, UnitMap um, Seg64 sg) {
+    const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
+    const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
+    const float* __restrict__ s0, TOut* __restrict__ o, UnitMap um, Seg64 sg, long nout) {
     typedef Maps64Cfg<DV> Cfg;
+    typedef Chain64Cfg<TOut, DV, DV> OCfg;
     constexpr int C = Cfg::C, DK = Cfg::DK, NVT = Cfg::NVT, NJ1 = Cfg::NJ1, NJ2 = Cfg::NJ2;
     constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, NWK = Cfg::NWK, NUV = Cfg::NUV;
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL > OCfg::TOTAL ? Cfg::TOTAL : OCfg::TOTAL];
+    if (blockIdx.x < nout) {
+        chain64_run<TOut, DV, DV, CHAIN_SEG>(smem, blockIdx.x, 0, 0, 1, ws_qt, ws_wk, ws_kb, ws_p, ws_u, ws_gam,
+                                             s0, o, nullptr, um, sg);
+        return;
+    }
     bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
     bf16* sWT = reinterpret_cast<bf16*>(smem + Cfg::OFF_WT);
     u32x4* sWk = reinterpret_cast<u32x4*>(smem + Cfg::OFF_WK);
@@ -339,14 +373,14 @@ __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int fr = lane & 15, fk = 8 * (lane >> 4), fe = 4 * (lane >> 4);
-    const long item = blockIdx.x;
-    const int nsegw = sg.nseg - 1;                   // the last segment needs no map
+    const long item = blockIdx.x - nout;
+    const int nsegw = sg.nseg - 2;                   // segment 0 and the last segment need no map
     const long bh = item / nsegw;
-    const int seg = (int)(item % nsegw);
+    const int seg = 1 + (int)(item % nsegw);
     const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
     const SeqRange sr = seq_range(um, sq);
-    const int c0 = seg * sg.L;
-    const int NC = sr.nchunks - c0 < sg.L ? sr.nchunks - c0 : sg.L;
+    const int c0 = seg_first(sg, seg);
+    const int NC = seg_chunks(sg, seg, sr.nchunks);
     auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, c0 + (n < NC ? n : NC - 1), sr.chunk0); };
 
     const int R1 = 2 * (wave & 1), J1 = NJ1 * (wave >> 1);   // phase 1 tiles
@@ -393,9 +427,7 @@ __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
     }
 
     // state tiles (R2 + i, J2 + jt): rows 16(R2 + i) + fe + e, column 16(J2 + jt) + fr
-    // of [S | I]; value columns start from S0 (segment 0) or zero, identity columns
-    // from the identity
-    const float* init = seg == 0 && s0 ? s0 + bh * (long)(DK * DV) : nullptr;
+    // of [S | I]; value columns start from zero, identity columns from the identity
     floatx4 accS[2][NJ2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -405,7 +437,7 @@ __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * (R2 + i) + fe + e;
-                accS[i][jt][e] = col >= DV ? (row == col - DV ? 1.f : 0.f) : (init ? init[row * (long)DV + col] : 0.f);
+                accS[i][jt][e] = col >= DV && row == col - DV ? 1.f : 0.f;
             }
         }
     auto write_state_operand = [&]() __attribute__((always_inline)) {
@@ -494,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
         if (n0 + DI < NC) step(DI, n0 + DI);
     });
 
-    // E (value columns) and M (identity columns; segment 0's is never used)
+    // E (value columns) and M (identity columns)
     float* E = sg.E + (bh * sg.nseg + seg) * (long)(DK * DV);
     float* M = sg.M + (bh * sg.nseg + seg) * (long)(DK * DK);
 #pragma unroll
@@ -502,7 +534,6 @@ __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
 #pragma unroll
         for (int jt = 0; jt < NJ2; ++jt) {
             const int col = 16 * (J2 + jt) + fr;
-            if (col >= DV && seg == 0) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * (R2 + i) + fe + e;
@@ -580,7 +611,7 @@ __global__ __launch_bounds__(256) void chain_seg_scan_kernel(const float* __rest
 #undef KDA_C64_PREFETCH_2
 
 template <typename TOut, int DV, int DVS, int MODE>
-static hipError_t launch_chain64_mode(const ChunkArgs& a, long items, const Seg64& sg) {
+static hipError_t launch_chain64_mode(const ChunkArgs& a, long items, const Seg64& sg, int seg_lo, int seg_cnt) {
     const long nwg = items * (DV / DVS);
     if (nwg == 0) return hipSuccess;
     const WsLayout w = ws_layout_of(a);
@@ -588,7 +619,7 @@ static hipError_t launch_chain64_mode(const ChunkArgs& a, long items, const Seg6
     hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS, MODE>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                        (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
                        (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam),
-                       a.s0, (TOut*)a.o, a.sT, unit_map(a), sg);
+                       a.s0, (TOut*)a.o, a.sT, unit_map(a), sg, seg_lo, seg_cnt);
     return hipGetLastError();
 }
 
@@ -597,30 +628,31 @@ template <typename TOut, int DV>
 static hipError_t launch_chain64(const ChunkArgs& a) {
     const long bh = seq_head_count(a);
     const SegPlan plan = seg_plan_of(a);
-    if (plan.nseg > 1) {
-        // segments: maps of all but the last, their scan, then every segment's outputs
-        constexpr int DVS = SEG_DVS < DV ? SEG_DVS : DV;
+    if (plan.nseg > 2) {
+        // segments: segment 0's outputs beside the maps of segments 1 .. nseg - 2,
+        // the scan of the maps, then the outputs of segments 1 .. nseg - 1
+        static_assert(SEG_DVS >= DV, "one workgroup per segment holds every value column");
         const WsLayout w = ws_layout_of(a);
         char* ws = (char*)a.ws;
-        Seg64 sg{plan.L, plan.nseg, (float*)(ws + w.seg_e), (float*)(ws + w.seg_m), (float*)(ws + w.seg_s)};
-        // (the maps write no outputs: one kernel serves both output types); every
-        // segment's whole augmented state is one workgroup, so its Wk and Kb^T are
-        // fetched once
-        const long nmaps = bh * (plan.nseg - 1);
-        hipLaunchKernelGGL((chain_maps64_kernel<DV, 2>), dim3((unsigned)nmaps), dim3(512), 0, a.stream,
-                           (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb), (const bf16*)(ws + w.u),
-                           (const float*)(ws + w.gam), a.s0, unit_map(a), sg);
+        Seg64 sg{plan.L0, plan.L, plan.nseg, (float*)(ws + w.seg_e), (float*)(ws + w.seg_m), (float*)(ws + w.seg_s)};
+        // every segment's whole augmented state is one workgroup, so its Wk and
+        // Kb^T are fetched once
+        const long nwg = bh + bh * (plan.nseg - 2);
+        hipLaunchKernelGGL((chain_maps64_kernel<TOut, DV, 2>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
+                           (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
+                           (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam), a.s0,
+                           (TOut*)a.o, unit_map(a), sg, bh);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((chain_seg_scan_kernel<128, DV>), dim3((unsigned)(bh * (DV / 4))), dim3(256), 0,
                            a.stream, a.s0, sg);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        return launch_chain64_mode<TOut, DV, DVS, CHAIN_SEG>(a, bh * plan.nseg, sg);
+        return launch_chain64_mode<TOut, DV, DV, CHAIN_SEG>(a, bh * (plan.nseg - 1), sg, 1, plan.nseg - 1);
     }
-    const Seg64 none{0, 1, nullptr, nullptr, nullptr};
-    if (bh * (DV / 32) >= 256) return launch_chain64_mode<TOut, DV, 32, CHAIN_PLAIN>(a, bh, none);
-    return launch_chain64_mode<TOut, DV, 16, CHAIN_PLAIN>(a, bh, none);
+    const Seg64 none{0, 0, 1, nullptr, nullptr, nullptr};
+    if (bh * (DV / 32) >= 256) return launch_chain64_mode<TOut, DV, 32, CHAIN_PLAIN>(a, bh, none, 0, 1);
+    return launch_chain64_mode<TOut, DV, 16, CHAIN_PLAIN>(a, bh, none, 0, 1);
 }
 
 hipError_t run_chunk_chain64(const ChunkArgs& a) {

@@ -1049,24 +1049,32 @@ static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_
 
 // Segments for the hot chain.  The plain chain runs one workgroup per (sequence,
 // head, 32 value columns); when those number fewer than the 256 CUs and the
-// sequence is long, the chunks are cut into segments of at least SEG_MIN_CHUNKS
-// so that about SEG_TARGET_WG workgroups of SEG_DVS columns run the outputs.
+// sequence is long, its chunks are cut into segments.  Segment 0 starts from the
+// call's initial state, so its outputs run in the first launch beside the maps of
+// segments 1 .. nseg - 2; the outputs of segments 1 .. nseg - 1 follow the scan.
+// Each launch takes (nseg - 1) workgroups per pair, about SEG_TARGET_WG in all.
+// A chunk of outputs costs about 10/7 of a chunk of maps there, so segment 0 is
+// 7/10 as long as the others and the first launch's two kinds of work end together.
 SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
     const int NC = (T + C - 1) / C;
-    SegPlan p{NC, 1};
-    if (!hot_config(in_bf16, dk, C) || generic || NC < 2 * SEG_MIN_CHUNKS) return p;
+    SegPlan p{NC, 1, NC};
+    if (!hot_config(in_bf16, dk, C) || generic) return p;
     const long bh = (long)B * H;
     if (bh == 0 || bh * (dv / 32) >= 256) return p;
-    const long nsl = dv / (SEG_DVS < dv ? SEG_DVS : dv);
-    long nseg = (SEG_TARGET_WG + bh * nsl - 1) / (bh * nsl);
-    if (nseg > NC / SEG_MIN_CHUNKS) nseg = NC / SEG_MIN_CHUNKS;
-    if (nseg < 2) return p;
-    const int L = (int)((NC + nseg - 1) / nseg);
-    return SegPlan{L, (NC + L - 1) / L};
+    long n1 = SEG_TARGET_WG / bh;                            // segments after the first
+    if (n1 > NC / SEG_MIN_CHUNKS - 1) n1 = NC / SEG_MIN_CHUNKS - 1;
+    if (n1 < SEG_MIN_LATER) return p;
+    const long L = (10L * NC + 10 * n1 + 6) / (10 * n1 + 7);  // ceil(NC / (n1 + 0.7))
+    long L0 = 7 * L / 10 > 0 ? 7 * L / 10 : 1;
+    const long last = NC - L0 - (n1 - 1) * L;                // the last segment's chunks
+    if (last > L) L0 += last - L;
+    const long nseg = 1 + (NC - L0 + L - 1) / L;
+    if (nseg < 1 + SEG_MIN_LATER) return p;
+    return SegPlan{(int)L, (int)nseg, (int)L0};
 }
 
 SegPlan seg_plan_of(const ChunkArgs& a) {
-    if (a.cu_seqlens) return SegPlan{0, 1};
+    if (a.cu_seqlens) return SegPlan{0, 1, 0};
     return seg_plan(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.generic);
 }
 

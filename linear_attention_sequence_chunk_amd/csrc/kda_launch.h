@@ -63,15 +63,17 @@ inline bool hot_config(bool in_bf16, int dk, int C) { return in_bf16 && dk == 12
 struct WsLayout {
     size_t cu, qt, wk, kb, p, u, gam, seg_e, seg_m, seg_s, total;   // byte offsets of each array, total bytes
 };
-// Segments of the hot chain: nseg segments of L chunks per (sequence, head);
-// nseg = 1 is the plain sequential chain.
+// Segments of the hot chain per (sequence, head): segment 0 of L0 chunks, then
+// nseg - 1 segments of L chunks (the last may have fewer); nseg = 1 is the plain
+// sequential chain.
 struct SegPlan {
-    int L, nseg;
+    int L, nseg, L0;
 };
 SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic);
 constexpr int SEG_DVS = 128;         // value columns per workgroup of the segmented chain
-constexpr int SEG_TARGET_WG = 256;   // segments enough for this many output workgroups
-constexpr int SEG_MIN_CHUNKS = 32;   // no segment shorter than this
+constexpr int SEG_TARGET_WG = 256;   // segments enough for this many workgroups per launch
+constexpr int SEG_MIN_CHUNKS = 32;   // no segment after the first shorter than this
+constexpr int SEG_MIN_LATER = 4;     // fewer segments after the first: the plain chain is faster
 // generic = true: the format of the generic kernels even in the hot configuration
 WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic = false);
 // Packed variable-length batch of N sequences, T tokens in all: room for every

@@ -167,23 +167,26 @@ def test_segment_plan():
     """kda_chunk_fwd_segments: the chain runs in segments only in the hot
     configuration (bf16, dk = 128, 64-token chunks), for fixed-length batches
     whose sequential chain would have fewer than 256 workgroups of 32 columns,
-    and never in segments shorter than 32 chunks."""
+    with at least four segments after the first and none of them shorter than 32
+    chunks; each of the two segment launches takes (segments - 1) workgroups
+    per pair, at most 256."""
     seg = _lib.lib().kda_chunk_fwd_segments
     B16, F = _lib.BF16, _lib.F32
-    assert seg(1, 1 << 20, 16, 128, 128, B16, 64) == 16          # the 1M-token workload
+    assert seg(1, 1 << 20, 16, 128, 128, B16, 64) == 17          # the 1M-token workload
     assert seg(4, 8192, 16, 128, 128, B16, 64) == 1              # 64 pairs x 4 slices fill the GPU
-    assert seg(1, 65536, 32, 128, 128, B16, 128) == 8            # C = 128 runs as 64-token chunks
-    assert seg(1, 4096, 1, 128, 128, B16, 64) == 2               # 64 chunks: two segments of 32
-    assert seg(1, 4095, 1, 128, 128, B16, 64) == 2               # 64 chunks, the last one partial
-    assert seg(1, 4032, 1, 128, 128, B16, 64) == 1               # 63 chunks: sequential
-    assert seg(2, 8256, 1, 128, 64, B16, 64) == 4
+    assert seg(1, 65536, 32, 128, 128, B16, 128) == 9            # C = 128 runs as 64-token chunks
+    assert seg(1, 10240, 1, 128, 128, B16, 64) == 5              # 160 chunks: the fewest segments
+    assert seg(1, 10239, 1, 128, 128, B16, 64) == 5              # 160 chunks, the last one partial
+    assert seg(1, 10176, 1, 128, 128, B16, 64) == 1              # 159 chunks: sequential
+    assert seg(1, 4096, 1, 128, 128, B16, 64) == 1
+    assert seg(2, 12352, 1, 128, 64, B16, 64) == 6
     assert seg(1, 1 << 20, 16, 64, 64, B16, 64) == 1             # generic kernels: sequential chain
     assert seg(1, 1 << 20, 16, 128, 128, F, 64) == 1
     assert seg(1, 100, 1, 96, 128, B16, 64) == 0                 # unsupported
     L = _lib.lib()
     # segments add E, M and a start state per pair and segment to the workspace
     per_pair = lambda b, h, t: L.kda_chunk_fwd_workspace_bytes(b, t, h, 128, 128, B16, 64) // (b * h)
-    assert per_pair(1, 1, 4096) - per_pair(1, 64, 4096) >= 2 * 3 * 128 * 128 * 4
+    assert per_pair(1, 1, 10240) - per_pair(1, 64, 10240) >= 5 * 3 * 128 * 128 * 4
 
 
 def test_chunk_size_used():

@@ -22,10 +22,10 @@ pytestmark = pytest.mark.gpu
 # B, H, T, dv, out dtype, gates, S0 std
 CASES = [
     (1, 2, 16384 + 37, 128, torch.bfloat16, "tiny", 0.05),
-    (2, 1, 8192 + 64, 64, torch.bfloat16, "tiny", 0.0),
+    (2, 1, 12288 + 64, 64, torch.bfloat16, "tiny", 0.0),
     (1, 3, 12000, 128, torch.float32, "none", 0.02),       # alpha = 1: M is not damped by decay
-    (1, 1, 4096, 128, torch.bfloat16, "scalar", 0.05),      # 64 chunks: two segments
-    (3, 2, 9000, 128, torch.bfloat16, "long", 0.01),
+    (1, 1, 10240 + 5, 128, torch.bfloat16, "scalar", 0.05),  # 161 chunks: the fewest segments (5)
+    (3, 2, 12000, 128, torch.bfloat16, "long", 0.01),
 ]
 
 
@@ -79,7 +79,7 @@ def test_segmented_chain_random(seed):
     r = np.random.default_rng(400 + seed)
     B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
     dv = int(r.choice([64, 128]))
-    T = int(r.integers(64 * 64, 64 * 160)) + int(r.integers(0, 64))
+    T = int(r.integers(64 * 160, 64 * 256)) + int(r.integers(0, 64))
     layout = ["channel", "head", "none"][seed % 3]
     pre = seed >= 3
     nseg = _segments(B, T, H, dv)
