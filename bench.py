@@ -241,7 +241,7 @@ def main():
     hot = w.dtype == "bf16" and w.dk == 128 and plan.chunk_used == 64
     names = ("chunk_intra64_kernel", "chunk_chain64_kernel") if hot else ("chunk_intra_kernel", "chunk_chain_kernel")
     # The dominant kernel: the intra stage is one kernel; the chain stage is one
-    # kernel, or three (maps, scan, outputs) when the sequence runs in segments,
+    # kernel, or three (segment 0 with the maps, scan, outputs) when the sequence runs in segments,
     # none of them longer than the intra kernel there (profiles/kernel_stats_1m_prefill.txt).
     segmented = plan.segmented
     dom = (names[0], intra_alg, t_intra) if (t_intra >= t_chain or segmented) else (names[1], chain_alg, t_chain)
