@@ -285,8 +285,8 @@ PreLayout pre_layout(size_t base, size_t tok, int dk, int in_dtype, int gate, in
     return P;
 }
 
-// The backward pass: validation, the forward stages again (generic workspace
-// format, with checkpoints), then the backward stages.
+// The backward pass: validation, the forward stages again (with checkpoints),
+// then the backward stages.
 int run_bwd(BwdCall c) {
     const int dk = c.dk_size, dv = c.dv_size;
     c.C = bwd_chunk(c.C);
@@ -373,7 +373,7 @@ int run_bwd(BwdCall c) {
     a.ws = ws; a.ws_bytes = L.fwd.total; a.stream = (hipStream_t)c.stream;
     a.cu_seqlens = c.packed ? c.cu_seqlens : nullptr;
     a.N = c.packed ? c.N : 0;
-    a.generic = true;
+    a.checkpoints = true;
     a.ck_t = (float*)(ws + L.t); a.ck_a = (float*)(ws + L.a);
     a.ck_state = (float*)(ws + L.state); a.ck_w = (float*)(ws + L.w);
     if (kda::run_chunk_intra(a) != hipSuccess) return KDA_ERR_HIP;

@@ -14,7 +14,7 @@
 // then through the decays Kt = e^G K, Qt = e^G Q, Kb = e^{G_C - G} K, gam =
 // e^{G_C}, the pairwise decays inside A and P, and the prefix sum G of g.
 // The forward state S and W of every chunk, and T and A, are kept by the forward
-// stages run in their generic format (fp32 checkpoints).  Gradients accumulate
+// stages, which run again for this (fp32 checkpoints).  Gradients accumulate
 // in fp32; products of fp32 operands over the long dimensions run on bf16 MFMA
 // with each operand split into bf16 hi + lo parts (about 16 significant bits).
 #include "kda_chunk.h"
@@ -387,6 +387,10 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_chain_h_kernel(
     constexpr int DVS = Cfg::DVS, NSL = Cfg::NSL, NB = Cfg::NB, KPW = Cfg::KPW;
     constexpr int LKB = Cfg::LKB, LP = Cfg::LP, LW = Cfg::LW, LO = Cfg::LO, LS = Cfg::LS, LD = Cfg::LD;
     constexpr int PKB = Cfg::PKB, PP = Cfg::PP, PDO = Cfg::PDO;
+    // dk = 128, C = 64 (bf16): the forward stages wrote Kb^T, Wk, Qt and P in MFMA
+    // fragment order (16-byte pieces of 8 consecutive elements of a row; the two
+    // blocks of P above the diagonal not written, and never read here)
+    constexpr bool FRAG = DK == 128 && C == 64;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
     bf16* sKb = reinterpret_cast<bf16*>(smem + Cfg::O_KB);
     bf16* sP = reinterpret_cast<bf16*>(smem + Cfg::O_P);
@@ -471,19 +475,25 @@ __global__ __launch_bounds__(256, 1) void chunk_bwd_chain_h_kernel(
         _Pragma("unroll") for (int x = 0; x < PKB; ++x) {                                         \
             const int u = tid + 256 * x;                                                          \
             if (Cfg::U_KB % 256 == 0 || u < Cfg::U_KB) {                                          \
-                const int e0 = 8 * u;                                                             \
-                *reinterpret_cast<u32x4*>(sKb + (e0 / C) * LKB + e0 % C) = rKb[x];                \
+                const int e0 = 8 * u, lf = u & 63;                                                \
+                const int okb = FRAG ? (16 * (u >> 7) + (lf & 15)) * LKB + 32 * ((u >> 6) & 1) + 8 * (lf >> 4) \
+                                     : (e0 / C) * LKB + e0 % C;                                   \
+                const int ow = FRAG ? (16 * (u >> 8) + (lf & 15)) * LW + 32 * ((u >> 6) & 3) + 8 * (lf >> 4) \
+                                    : (e0 / DK) * LW + e0 % DK;                                   \
+                *reinterpret_cast<u32x4*>(sKb + okb) = rKb[x];                                    \
                 const u32x4 nw = {rWk[x][0] ^ 0x80008000u, rWk[x][1] ^ 0x80008000u,               \
                                   rWk[x][2] ^ 0x80008000u, rWk[x][3] ^ 0x80008000u};              \
-                *reinterpret_cast<u32x4*>(sWk + (e0 / DK) * LW + e0 % DK) = nw;                   \
-                *reinterpret_cast<u32x4*>(sQt + (e0 / DK) * LW + e0 % DK) = rQt[x];               \
+                *reinterpret_cast<u32x4*>(sWk + ow) = nw;                                         \
+                *reinterpret_cast<u32x4*>(sQt + ow) = rQt[x];                                     \
             }                                                                                     \
         }                                                                                         \
         _Pragma("unroll") for (int x = 0; x < PP; ++x) {                                          \
             const int u = tid + 256 * x;                                                          \
             if (Cfg::U_P % 256 == 0 || u < Cfg::U_P) {                                            \
-                const int e0 = 8 * u;                                                             \
-                *reinterpret_cast<u32x4*>(sP + (e0 / C) * LP + e0 % C) = rP[x];                   \
+                const int e0 = 8 * u, lf = u & 63;                                                \
+                const int op = FRAG ? (16 * (u >> 7) + (lf & 15)) * LP + 32 * ((u >> 6) & 1) + 8 * (lf >> 4) \
+                                    : (e0 / C) * LP + e0 % C;                                     \
+                *reinterpret_cast<u32x4*>(sP + op) = rP[x];                                       \
             }                                                                                     \
         }                                                                                         \
         const long t0 = sr.tok_begin + (long)(N) * C;                                             \

@@ -44,7 +44,9 @@ namespace kda {
 //                                                        never written, never read)
 //   U      [4 row tiles][DV/16 column tiles][64][4] bf16  lane l, element e: row 16R + 4(l/16) + e, column 16J + l%16
 //   gam    [DK] fp32
-enum ChainMode { CHAIN_PLAIN = 0, CHAIN_SEG = 1 };
+// CHAIN_CKPT: the plain chain without outputs, keeping the fp32 start state and W
+// of every chunk for the backward pass
+enum ChainMode { CHAIN_PLAIN = 0, CHAIN_SEG = 1, CHAIN_CKPT = 2 };
 
 template <typename TOut, int DV, int DVS>
 struct Chain64Cfg {
@@ -59,6 +61,11 @@ struct Chain64Cfg {
     static constexpr size_t OFF_WT = OFF_ST + size_t(DVS) * LDK * 2;
     static constexpr size_t OFF_O = OFF_WT + size_t(DVS) * LDC * 2;               // per O wave: [16][DVS]
     static constexpr size_t TOTAL = OFF_O + size_t(4) * 16 * DVS * sizeof(TOut);
+    // CHAIN_CKPT: each wave's 16 state rows, then the W waves' 16 rows of W, fp32,
+    // staged so that the checkpoints go out as 16-byte row pieces
+    static constexpr int LCK = DVS + 4;
+    static constexpr size_t OFF_CK = TOTAL;
+    static constexpr size_t TOTAL_CK = OFF_CK + size_t(12) * 16 * LCK * 4;
     static_assert((NJ == 1 || NJ == 2 || NJ == 4 || NJ == 8) && DV % DVS == 0, "slice width 16 .. 128");
     static_assert((16 * DVS * sizeof(TOut)) % 16 == 0, "output staging rows");
 };
@@ -88,15 +95,26 @@ __device__ __forceinline__ void chain64_run(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, const UnitMap& um,
-    const Seg64& sg) {
+    const Seg64& sg, float* __restrict__ ck_state, float* __restrict__ ck_w) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
     constexpr int C = Cfg::C, DK = Cfg::DK, NJ = Cfg::NJ, LDK = Cfg::LDK, LDC = Cfg::LDC;
     constexpr int D = Cfg::DEPTH;
 
     bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
     bf16* sWT = reinterpret_cast<bf16*>(smem + Cfg::OFF_WT);
+    float* sCk = reinterpret_cast<float*>(smem + Cfg::OFF_CK);    // CHAIN_CKPT only
+    constexpr int LCK = Cfg::LCK;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // 16 staged fp32 rows of DVS columns to global rows of DV floats, 16 bytes a lane
+    auto ckpt_rows = [&](const float* rows, float* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < DVS / 16; ++p) {
+            const int u = lane + 64 * p, r = u / (DVS / 4), c4 = u % (DVS / 4);
+            *reinterpret_cast<floatx4*>(dst + r * (long)DV + 4 * c4) =
+                *reinterpret_cast<const floatx4*>(rows + r * LCK + 4 * c4);
+        }
+    };
     // work item -> (sequence, head) pair and segment
     const long bh = item / seg_cnt;
     const int seg = seg_lo + (int)(item % seg_cnt);
@@ -104,8 +122,8 @@ __device__ __forceinline__ void chain64_run(
     // sequence (batch row, or packed sequence) and head; its chunks and tokens
     const int H = um.H, sq = (int)(bh / H), h = (int)(bh % H);
     const SeqRange sr = seq_range(um, sq);
-    const int c0 = MODE == CHAIN_PLAIN ? 0 : seg_first(sg, seg);              // first chunk of the segment
-    const int NC = MODE == CHAIN_PLAIN ? sr.nchunks : seg_chunks(sg, seg, sr.nchunks);
+    const int c0 = MODE != CHAIN_SEG ? 0 : seg_first(sg, seg);              // first chunk of the segment
+    const int NC = MODE != CHAIN_SEG ? sr.nchunks : seg_chunks(sg, seg, sr.nchunks);
     auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, c0 + n, sr.chunk0); };
 
     const bool wW = wave < 4;                    // uniform per wave
@@ -211,7 +229,22 @@ __device__ __forceinline__ void chain64_run(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w4[e] = (bf16)((float)uu[e] - acc[jt][e]);
                 *reinterpret_cast<bf16x4*>(sWT + (jt * 16 + fr) * LDC + R * 16 + 4 * (lane >> 4)) = w4;
+                if constexpr (MODE == CHAIN_CKPT) {                // W of chunk n, fp32, to this wave's rows
+                    float* wt = sCk + (8 + R) * 16 * LCK;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) wt[(4 * (lane >> 4) + e) * LCK + jt * 16 + fr] = (float)uu[e] - acc[jt][e];
+                }
             }
+            if constexpr (MODE == CHAIN_CKPT) ckpt_rows(sCk + (8 + R) * 16 * LCK, ck_w + unit_of(n) * (long)(C * DV) +
+                                                        (R * 16) * (long)DV + j0);
+        }
+        if constexpr (MODE == CHAIN_CKPT) {                        // the state chunk n starts from
+            float* st = sCk + wave * 16 * LCK;
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[(4 * (lane >> 4) + e) * LCK + jt * 16 + fr] = accS[jt][e];
+            ckpt_rows(st, ck_state + unit_of(n) * (long)(DK * DV) + (ct * 16) * (long)DV + j0);
         }
         KDA_C64_PREFETCH_1(d, unit_of(n + D < NC ? n + D : NC - 1));
         __syncthreads();                                            // W^T complete
@@ -247,7 +280,7 @@ __device__ __forceinline__ void chain64_run(
             }
         }
         write_state_operand();                                      // read only after the next barrier
-        if (!wW) {
+        if (MODE != CHAIN_CKPT && !wW) {
             // this wave's 16 x DVS output tile, through its own LDS rows, as 16-byte row pieces
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
@@ -276,7 +309,7 @@ __device__ __forceinline__ void chain64_run(
     // end state: the call's final state (plain; the last segment), or segment 0's
     // end state E_0, which the scan takes as segment 1's start state
     float* fin = nullptr;
-    if (MODE == CHAIN_PLAIN || seg == sg.nseg - 1) fin = sT ? sT + bh * (long)(DK * DV) : nullptr;
+    if (MODE != CHAIN_SEG || seg == sg.nseg - 1) fin = sT ? sT + bh * (long)(DK * DV) : nullptr;
     else if (seg == 0) fin = sg.E + (bh * sg.nseg) * (long)(DK * DV);
     if (fin) {
 #pragma unroll
@@ -292,10 +325,10 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, float* __restrict__ sT, UnitMap um, Seg64 sg,
-    int seg_lo, int seg_cnt) {
+    int seg_lo, int seg_cnt, float* __restrict__ ck_state, float* __restrict__ ck_w) {
     typedef Chain64Cfg<TOut, DV, DVS> Cfg;
     constexpr int NSL = Cfg::NSL;
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL];
+    __shared__ __attribute__((aligned(16))) char smem[MODE == CHAIN_CKPT ? Cfg::TOTAL_CK : Cfg::TOTAL];
     // Slices of one work item (a (sequence, head) pair, or one of its segments)
     // share an XCD (workgroups are dealt to the 8 XCDs round-robin), so the
     // per-chunk operands they all read come from one L2.
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
         }
     }
     chain64_run<TOut, DV, DVS, MODE>(smem, item, sl, seg_lo, seg_cnt, ws_qt, ws_wk, ws_kb, ws_p, ws_u, ws_gam,
-                                     s0, o, sT, um, sg);
+                                     s0, o, sT, um, sg, ck_state, ck_w);
 }
 
 // The maps launch with the whole augmented state [S | I] (DV + DK columns) in one
@@ -362,7 +395,7 @@ __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL > OCfg::TOTAL ? Cfg::TOTAL : OCfg::TOTAL];
     if (blockIdx.x < nout) {
         chain64_run<TOut, DV, DV, CHAIN_SEG>(smem, blockIdx.x, 0, 0, 1, ws_qt, ws_wk, ws_kb, ws_p, ws_u, ws_gam,
-                                             s0, o, nullptr, um, sg);
+                                             s0, o, nullptr, um, sg, nullptr, nullptr);
         return;
     }
     bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
@@ -619,7 +652,7 @@ static hipError_t launch_chain64_mode(const ChunkArgs& a, long items, const Seg6
     hipLaunchKernelGGL((chunk_chain64_kernel<TOut, DV, DVS, MODE>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                        (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
                        (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam),
-                       a.s0, (TOut*)a.o, a.sT, unit_map(a), sg, seg_lo, seg_cnt);
+                       a.s0, (TOut*)a.o, a.sT, unit_map(a), sg, seg_lo, seg_cnt, a.ck_state, a.ck_w);
     return hipGetLastError();
 }
 
@@ -651,6 +684,11 @@ static hipError_t launch_chain64(const ChunkArgs& a) {
         return launch_chain64_mode<TOut, DV, DV, CHAIN_SEG>(a, bh * (plan.nseg - 1), sg, 1, plan.nseg - 1);
     }
     const Seg64 none{0, 0, 1, nullptr, nullptr, nullptr};
+    if (a.checkpoints) {                                       // the backward pass's forward chain
+        if (!a.ck_state || !a.ck_w) return hipErrorInvalidValue;
+        if (bh * (DV / 32) >= 256) return launch_chain64_mode<TOut, DV, 32, CHAIN_CKPT>(a, bh, none, 0, 1);
+        return launch_chain64_mode<TOut, DV, 16, CHAIN_CKPT>(a, bh, none, 0, 1);
+    }
     if (bh * (DV / 32) >= 256) return launch_chain64_mode<TOut, DV, 32, CHAIN_PLAIN>(a, bh, none, 0, 1);
     return launch_chain64_mode<TOut, DV, 16, CHAIN_PLAIN>(a, bh, none, 0, 1);
 }

@@ -519,9 +519,8 @@ struct Intra64Cfg {
     static_assert(NITV >= 1 && (C * DV / 8) % NT == 0 && (DV / 8) % 4 == 0, "v unit mapping");
 };
 
-// GEN: the backward pass's forward stage.  The same results stored in the generic
-// workspace format (row-major, U in fp32) that the generic chain and the backward
-// kernels read, plus the fp32 checkpoints T and A per unit.
+// GEN: the backward pass's forward stage: the same workspace, plus the fp32
+// checkpoints T and A per unit.
 template <int DV, bool GEN>
 __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -739,8 +738,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             store_column8(sKtT, LDT, c, t, pack_bf16x8(kr), 2 * (lane >> 4));
             store_column8(sKbT, Cfg::LDP, c, t, pack_bf16x8(kf), 2 * (lane >> 4));
             // fragment order: unit (row tile R, k-step c/32), lane = row%16 + 16 * ((c%32)/8)
-            if constexpr (GEN) Vec8<bf16>::store(gQt + t * DK + c, o1);
-            else Vec8<bf16>::store(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
+            Vec8<bf16>::store(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
         });
         if (p == 0) {                                  // channel half 1, and beta
             prep_half(std::integral_constant<int, 1>{});
@@ -757,14 +755,9 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 
         if (p == 1) {                                  // Kb^T complete: to the workspace in fragment order
             for (int u = tid; u < DK * C / 8; u += NT) {
-                if constexpr (GEN) {                   // row-major [DK][C]
-                    reinterpret_cast<u32x4*>(gKb)[u] =
-                        *reinterpret_cast<const u32x4*>(sKbT + (u >> 3) * Cfg::LDP + 8 * (u & 7));
-                } else {
-                    const int ctile = u >> 7, ks = (u >> 6) & 1, lf = u & 63;
-                    reinterpret_cast<u32x4*>(gKb)[u] = *reinterpret_cast<const u32x4*>(
-                        sKbT + (ctile * 16 + (lf & 15)) * Cfg::LDP + ks * 32 + 8 * (lf >> 4));
-                }
+                const int ctile = u >> 7, ks = (u >> 6) & 1, lf = u & 63;
+                reinterpret_cast<u32x4*>(gKb)[u] = *reinterpret_cast<const u32x4*>(
+                    sKbT + (ctile * 16 + (lf & 15)) * Cfg::LDP + ks * 32 + 8 * (lf >> 4));
             }
         }
         // A and P over this channel half (K = 64: two MFMA steps)
@@ -871,11 +864,8 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     __syncthreads();
     {
         uint4* gP = reinterpret_cast<uint4*>(ws_p + ch * (long)C * C);
-        if constexpr (GEN) {                           // row-major [C][C], zeros above the diagonal
-            gP[tid] = *reinterpret_cast<const uint4*>(sPb + (tid >> 3) * Cfg::LDP + 8 * (tid & 7));
-        }
         // fragment order; the two blocks above the diagonal (row tiles 0, 1 at k-step 1) are not stored
-        else if (tid < 6 * 64) {
+        if (tid < 6 * 64) {
             const int bi = tid >> 6, lf = tid & 63;
             const int Rt = bi < 2 ? bi : 2 + (bi - 2) / 2, ks = bi < 2 ? 0 : (bi - 2) % 2;
             gP[(Rt * 2 + ks) * 64 + lf] = *reinterpret_cast<const uint4*>(
@@ -955,7 +945,6 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     {
         constexpr int NUT = DV / 16, NCT = NUT + DK / 16;        // column tiles: U then Wk
         bf16* gU = reinterpret_cast<bf16*>(ws_u) + ch * (long)C * DV;
-        float* gUf = reinterpret_cast<float*>(ws_u) + ch * (long)C * DV;
         bf16* gW = ws_wk + ch * (long)C * DK;
         const int r = lane & 15, kg = lane >> 4;
         constexpr int NTPW = (NCT + NW - 1) / NW;                  // column tiles per wave
@@ -988,16 +977,10 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             if (ct < NUT) {
 #pragma unroll
                 for (int R2 = 0; R2 < 4; ++R2) {
-                    if constexpr (GEN) {                 // fp32 [C][DV]
+                    bf16x4 u4;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            gUf[(R2 * 16 + 4 * kg + e) * DV + ct * 16 + r] = acc[sct][R2][e];
-                    } else {
-                        bf16x4 u4;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) u4[e] = (bf16)acc[sct][R2][e];
-                        reinterpret_cast<bf16x4*>(gU)[(R2 * (DV / 16) + ct) * 64 + lane] = u4;
-                    }
+                    for (int e = 0; e < 4; ++e) u4[e] = (bf16)acc[sct][R2][e];
+                    reinterpret_cast<bf16x4*>(gU)[(R2 * (DV / 16) + ct) * 64 + lane] = u4;
                 }
             }
         }
@@ -1015,15 +998,10 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             }
         }
         __syncthreads();
-        for (int u = tid; u < C * DK / 8; u += NT) {  // Wk in fragment order (GEN: row-major [C][DK])
-            if constexpr (GEN) {
-                reinterpret_cast<u32x4*>(gW)[u] =
-                    *reinterpret_cast<const u32x4*>(sWo + (u >> 4) * Cfg::LDW + 8 * (u & 15));
-            } else {
-                const int Rt = u >> 8, ks = (u >> 6) & 3, lf = u & 63;
-                reinterpret_cast<u32x4*>(gW)[u] = *reinterpret_cast<const u32x4*>(
-                    sWo + (Rt * 16 + (lf & 15)) * Cfg::LDW + ks * 32 + 8 * (lf >> 4));
-            }
+        for (int u = tid; u < C * DK / 8; u += NT) {  // Wk in fragment order
+            const int Rt = u >> 8, ks = (u >> 6) & 3, lf = u & 63;
+            reinterpret_cast<u32x4*>(gW)[u] = *reinterpret_cast<const u32x4*>(
+                sWo + (Rt * 16 + (lf & 15)) * Cfg::LDW + ks * 32 + 8 * (lf >> 4));
         }
     }
 }
@@ -1031,7 +1009,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 // ================================================================ host side
 static inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_bf16, int C, bool generic) {
+static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_bf16, int C) {
     WsLayout w{};
     const size_t es = in_bf16 ? 2 : 4;
     size_t off = 0;
@@ -1040,7 +1018,7 @@ static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_
     w.wk = off; off = al256(off + nch * C * dk * es);
     w.kb = off; off = al256(off + nch * C * dk * es);
     w.p = off;  off = al256(off + nch * C * C * es);
-    w.u = off;  off = al256(off + nch * C * dv * (hot_config(in_bf16, dk, C) && !generic ? 2 : 4));
+    w.u = off;  off = al256(off + nch * C * dv * (hot_config(in_bf16, dk, C) ? 2 : 4));
     w.gam = off; off = al256(off + nch * dk * 4);
     w.seg_e = w.seg_m = w.seg_s = off;
     w.total = off;
@@ -1055,10 +1033,10 @@ static WsLayout layout_units(size_t nch, size_t header, int dk, int dv, bool in_
 // Each launch takes (nseg - 1) workgroups per pair, about SEG_TARGET_WG in all.
 // A chunk of outputs costs about 10/7 of a chunk of maps there, so segment 0 is
 // 7/10 as long as the others and the first launch's two kinds of work end together.
-SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
+SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool checkpoints) {
     const int NC = (T + C - 1) / C;
     SegPlan p{NC, 1, NC};
-    if (!hot_config(in_bf16, dk, C) || generic) return p;
+    if (!hot_config(in_bf16, dk, C) || checkpoints) return p;
     const long bh = (long)B * H;
     if (bh == 0 || bh * (dv / 32) >= 256) return p;
     long n1 = SEG_TARGET_WG / bh;                            // segments after the first
@@ -1075,13 +1053,13 @@ SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool 
 
 SegPlan seg_plan_of(const ChunkArgs& a) {
     if (a.cu_seqlens) return SegPlan{0, 1, 0};
-    return seg_plan(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.generic);
+    return seg_plan(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.checkpoints);
 }
 
-WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
+WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool checkpoints) {
     const size_t NC = (size_t)((T + C - 1) / C);
-    WsLayout w = layout_units((size_t)B * H * NC, 0, dk, dv, in_bf16, C, generic);
-    const SegPlan sp = seg_plan(B, T, H, dk, dv, in_bf16, C, generic);
+    WsLayout w = layout_units((size_t)B * H * NC, 0, dk, dv, in_bf16, C);
+    const SegPlan sp = seg_plan(B, T, H, dk, dv, in_bf16, C, checkpoints);
     if (sp.nseg > 1) {
         const size_t items = (size_t)B * H * sp.nseg;
         w.seg_e = w.total;
@@ -1092,14 +1070,15 @@ WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, boo
     return w;
 }
 
-WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic) {
+WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool checkpoints) {
     const size_t chunks = (size_t)((T + C - 1) / C) + (size_t)N;
-    return layout_units(chunks * H, 2 * ((size_t)N + 1) * 4, dk, dv, in_bf16, C, generic);   // cu_chunks, cu_tok
+    (void)checkpoints;                                       // packed batches never run in segments
+    return layout_units(chunks * H, 2 * ((size_t)N + 1) * 4, dk, dv, in_bf16, C);   // cu_chunks, cu_tok
 }
 
 WsLayout ws_layout_of(const ChunkArgs& a) {
-    return a.cu_seqlens ? ws_layout_packed(a.N, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.generic)
-                        : ws_layout(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.generic);
+    return a.cu_seqlens ? ws_layout_packed(a.N, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.checkpoints)
+                        : ws_layout(a.B, a.T, a.H, a.dk, a.dv, a.in_bf16, a.C, a.checkpoints);
 }
 
 UnitMap unit_map(const ChunkArgs& a) {
@@ -1226,8 +1205,8 @@ static hipError_t intra_c(const ChunkArgs& a) {
     if constexpr (sizeof(T) == 2 && DK == 128) {
         if (hot_layout(a)) return launch_intra64<DV, false>(a);
         // the backward pass's forward stage in this configuration: the same kernel,
-        // storing the generic format and the checkpoints
-        if (hot_config(a.in_bf16, DK, a.C) && a.generic) return launch_intra64<DV, true>(a);
+        // also storing the checkpoints T and A
+        if (hot_config(a.in_bf16, DK, a.C) && a.checkpoints) return launch_intra64<DV, true>(a);
     }
     switch (a.C) {
         case 16: return launch_intra<T, DK, DV, 16>(a);
@@ -1253,7 +1232,7 @@ hipError_t run_chunk_intra(const ChunkArgs& a) {
 }
 
 hipError_t run_chunk_chain(const ChunkArgs& a) {
-    if (hot_layout(a)) return run_chunk_chain64(a);
+    if (hot_config(a.in_bf16, a.dk, a.C)) return run_chunk_chain64(a);   // with checkpoints in the backward pass
     return a.in_bf16 ? run_chunk_chain_bf16(a) : run_chunk_chain_f32(a);
 }
 

@@ -39,9 +39,9 @@ struct ChunkArgs {
     // token offsets cu_seqlens[N+1] (device memory); NULL for [B,T,H,d] batches
     const int* cu_seqlens = nullptr;
     int N = 0;
-    // backward pass only: the generic (row-major, fp32 U) workspace format even in
-    // the hot configuration, and fp32 checkpoints kept by the stages
-    bool generic = false;
+    // backward pass only: the stages also keep fp32 checkpoints (below), and the
+    // chain runs without segments
+    bool checkpoints = false;
     float* ck_state = nullptr;   // chain: state at each chunk start, [unit][dk][dv]
     float* ck_w = nullptr;       // chain: W of each chunk, [unit][C][dv]
     float* ck_t = nullptr;       // intra: T = (I + Diag(beta) A)^-1, [unit][C][C]
@@ -69,16 +69,16 @@ struct WsLayout {
 struct SegPlan {
     int L, nseg, L0;
 };
-SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic);
+SegPlan seg_plan(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool checkpoints);
 constexpr int SEG_DVS = 128;         // value columns per workgroup of the segmented chain
 constexpr int SEG_TARGET_WG = 256;   // segments enough for this many workgroups per launch
 constexpr int SEG_MIN_CHUNKS = 32;   // no segment after the first shorter than this
 constexpr int SEG_MIN_LATER = 4;     // fewer segments after the first: the plain chain is faster
-// generic = true: the format of the generic kernels even in the hot configuration
-WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic = false);
+// checkpoints = true: the backward pass's layout (no segment arrays)
+WsLayout ws_layout(int B, int T, int H, int dk, int dv, bool in_bf16, int C, bool checkpoints = false);
 // Packed variable-length batch of N sequences, T tokens in all: room for every
 // possible chunk (at most ceil(T/C) + N) and, first, the chunk offsets int [N+1].
-WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool generic = false);
+WsLayout ws_layout_packed(int N, int T, int H, int dk, int dv, bool in_bf16, int C, bool checkpoints = false);
 // The layout for a call's arguments (fixed-length or packed).
 WsLayout ws_layout_of(const ChunkArgs& a);
 SegPlan seg_plan_of(const ChunkArgs& a);
@@ -87,7 +87,7 @@ SegPlan seg_plan_of(const ChunkArgs& a);
 bool chunk_supported(int dk, int dv, int C, bool in_bf16);
 
 // Backward pass (kda_chunk_bwd.hip).  fwd: the forward arguments with
-// generic = true and the four checkpoint arrays; the rest is the backward's.
+// checkpoints = true and the four checkpoint arrays; the rest is the backward's.
 struct BwdArgs {
     ChunkArgs fwd;
     const float* dO;            // [B,T,H,dv] cotangent of o
@@ -99,8 +99,8 @@ struct BwdArgs {
     float* ck_dS;               // cotangent of each chunk's end state, [unit][dk][dv]
     float* ck_dW;               // dW of each chunk, [unit][C][dv]
 };
-// Workspace of the backward pass: the forward workspace (generic format) then
-// the checkpoints, per unit.
+// Workspace of the backward pass: the forward workspace then the checkpoints,
+// per unit.
 struct BwdLayout {
     WsLayout fwd;
     size_t t, a, state, w, dS, dW, total;
