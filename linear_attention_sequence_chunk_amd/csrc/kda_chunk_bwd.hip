@@ -719,9 +719,9 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
         constexpr int NTT = (C * C + NT - 1) / NT;
         float tv[NTT];
 #pragma unroll
-        for (int x = 0; x < NTT; ++x) {
-            const int u = tid + NT * x;
-            tv[x] = ck_t[unit * (long)C * C + (u < C * C ? u : 0)];
+        for (int x = 0; x < NTT; ++x) {                             // 16x16 blocks above the diagonal: 0
+            const int u = tid + NT * x, uu = u < C * C ? u : 0;
+            tv[x] = ((uu % C) >> 4) > ((uu / C) >> 4) ? 0.f : ck_t[unit * (long)C * C + uu];
         }
         const float bt = tid < C ? beta[crow(tid)] : 0.f;
 #pragma unroll

@@ -834,8 +834,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         const int bc = bi < 3 ? bi + 1 : (bi < 5 ? bi - 1 : 3);
         const int r = br * 16 + (e >> 4), i = bc * 16 + (e & 15);
         sA[r * LDA + i] = 0.f;
-        sPb[r * Cfg::LDP + i] = (bf16)0.f;
-        if constexpr (GEN) ck_a[ch * (long)(C * C) + r * C + i] = 0.f;
+        sPb[r * Cfg::LDP + i] = (bf16)0.f;                // (A's checkpoint: only the lower blocks are read)
     }
     if (wave < 6) {
         const int np = (wave == 0 || wave == 3) ? 1 : 2;
@@ -916,8 +915,9 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
         __syncthreads();
     });
 
-    if constexpr (GEN) {                               // T, for the backward pass
-        for (int u = tid; u < C * C; u += NT) ck_t[ch * (long)(C * C) + u] = sA[(u >> 6) * LDA + (u & 63)];
+    if constexpr (GEN) {                               // T, for the backward pass: its lower blocks
+        for (int u = tid; u < C * C; u += NT)
+            if (((u & 63) >> 4) <= (u >> 10)) ck_t[ch * (long)(C * C) + u] = sA[(u >> 6) * LDA + (u & 63)];
     }
 
     // ---------------------------------------------------------------- U = (T Diag(beta)) V, Wk = (T Diag(beta)) e^G K

@@ -46,6 +46,8 @@ struct ChunkArgs {
     float* ck_w = nullptr;       // chain: W of each chunk, [unit][C][dv]
     float* ck_t = nullptr;       // intra: T = (I + Diag(beta) A)^-1, [unit][C][C]
     float* ck_a = nullptr;       // intra: A (strictly lower), [unit][C][C]
+    // (of T and A only the 16x16 blocks on and below the diagonal are read; the
+    // hot intra kernel does not write the others)
 };
 
 // The hot configuration (bf16 inputs, C = 64, dk = 128) has its own pair of
