@@ -124,3 +124,34 @@ def test_backward_strong_gates():
     g[0, 40:42, 0, :5] = -30.0
     d["g"] = torch.tensor(g, dtype=torch.float32)
     _run(d, 64, "channel", torch.float32, 6, "bwd strong gates")
+
+
+def test_backward_mid_workload_full():
+    """The backward pass at the size bench.py times it (B=4, H=16, T=8192, d=128,
+    C=64, bf16 q/k/v, per-channel gates): every gradient of every (batch, head)
+    sequence against the oracle's fp64 adjoint, with a final-state cotangent as
+    well, so that dS0 is checked too."""
+    import time
+    w = inputs.WORKLOADS["mid"]
+    _say("backward mid workload: generating")
+    d = inputs.make_prefill(w)
+    rs = np.random.default_rng(8)
+    dO = torch.tensor(rs.standard_normal((w.B, w.T, w.H, w.dv)), dtype=torch.float32)
+    dST = torch.tensor(rs.standard_normal((w.B, w.H, w.dk, w.dv)), dtype=torch.float32)
+    _say("backward mid workload: GPU")
+    dg = cuda(d)
+    got = chunk_bwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], dO.cuda(), dg["S0"], dST.cuda(),
+                    chunk_size=w.C)
+    torch.cuda.synchronize()
+    got = {k: (None if v is None else v.cpu()) for k, v in got.items()}
+    del dg
+    _say("backward mid workload: oracle on all 64 sequences")
+    t0 = time.perf_counter()
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], dO, dST)
+    t1 = time.perf_counter()
+    tol = BWD_TOL[torch.bfloat16]
+    errs = {name: assert_close(f"bwd mid {name}", got[name], ref[name], tol)
+            for name in ("dq", "dk", "dv", "dg", "dbeta", "dS0")}
+    scales = {name: max(1.0, float(np.abs(ref[name]).max())) for name in errs}
+    _say(f"  oracle {t1 - t0:.1f} s;  max abs err / scale: " +
+         "  ".join(f"{k} {v:.2e}/{scales[k]:.3g}" for k, v in errs.items()))
