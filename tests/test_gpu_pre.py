@@ -144,3 +144,31 @@ def test_decode_gate_forms(T, dk, dv, layout, gdtype, sp, qk):
     eo = assert_close(f"{tag} o", o.cpu(), o_ref, TOL[torch.bfloat16])
     es = assert_close(f"{tag} S", S.cpu(), S_ref, TOL[torch.bfloat16])
     _say(f"  {tag}: max err o {eo:.2e}  S {es:.2e}")
+
+
+def test_prefill_pre_mid_workload_full():
+    """The fused pre-processing at the size bench.py times it (B=4, H=16, T=8192,
+    d=128, C=64): raw bf16 q and k (the workload's rows scaled by 0.2..5) and a
+    bf16 gate pre-activation whose -softplus is the workload's log-gate; every
+    output and final state of all 64 sequences against the oracle fed the
+    pre-processed inputs."""
+    from linear_attention_sequence_chunk_amd import inputs
+    w = inputs.WORKLOADS["mid"]
+    _say("pre mid workload: generating")
+    d = inputs.make_prefill(w)
+    rs = np.random.default_rng(12)
+    sc = lambda: torch.tensor(rs.uniform(0.2, 5.0, (w.B, w.T, w.H, 1)), dtype=torch.float32)
+    q = (d["q"].float() * sc()).to(torch.bfloat16)
+    k = (d["k"].float() * sc()).to(torch.bfloat16)
+    a = torch.log(torch.expm1(-d["g"].double())).to(torch.bfloat16)
+    _say("pre mid workload: GPU")
+    o, S = chunk_fwd(q.cuda(), k.cuda(), d["v"].cuda(), a.cuda(), d["beta"].cuda(),
+                     None if d["S0"] is None else d["S0"].cuda(), chunk_size=w.C, qk_l2norm=True,
+                     gate_act="softplus")
+    torch.cuda.synchronize()
+    _say("pre mid workload: oracle on all 64 sequences")
+    o_ref, S_ref = oracle.recurrent(oracle.l2_normalize(q), oracle.l2_normalize(k), d["v"],
+                                    oracle.gate_softplus(a), d["beta"], d["S0"])
+    eo = assert_close("pre mid o", o.cpu(), o_ref, TOL[torch.bfloat16])
+    es = assert_close("pre mid S", S.cpu(), S_ref, TOL[torch.bfloat16])
+    _say(f"  pre mid: max err o {eo:.2e}  S {es:.2e}")
