@@ -86,3 +86,22 @@ def test_prefill_without_decay_every_chunk_count(dk, dv, C, dtype):
             ref = dict(d)
             ref["g"] = torch.zeros_like(d["g"])
             check(ref, o.cpu(), S.cpu(), TOL[dtype], tag=f"no decay dk{dk} dv{dv} C{C} T{T}")
+
+
+@pytest.mark.parametrize("layout", ["head", "none"])
+def test_prefill_gate_layouts_mid_workload_full(layout):
+    """The gate layouts at the size bench.py times them (B=4, H=16, T=8192,
+    d=128, C=64, bf16): one gate per (token, head) given as [B,T,H], and no gate;
+    every output and final state of all 64 sequences against the oracle, and
+    bitwise against the per-channel call fed the broadcast gate."""
+    w = inputs.WORKLOADS["mid"]
+    d = inputs.make_prefill(w, gates="scalar" if layout == "head" else "none")
+    g_layout, g_channel = _layout_inputs(d, layout)
+    dg = cuda(d)
+    gl = None if g_layout is None else g_layout.cuda()
+    o, S = chunk_fwd(dg["q"], dg["k"], dg["v"], gl, dg["beta"], dg["S0"], chunk_size=w.C, gate_layout=layout)
+    o_c, S_c = chunk_fwd(dg["q"], dg["k"], dg["v"], g_channel.cuda(), dg["beta"], dg["S0"], chunk_size=w.C)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_c) and torch.equal(S, S_c), "layout differs from the per-channel call"
+    ref = dict(d); ref["g"] = g_channel
+    check(ref, o.cpu(), S.cpu(), TOL[torch.bfloat16], tag=f"mid {layout}")
