@@ -84,3 +84,33 @@ def test_varlen_no_states_and_empty():
     """No initial state (zeros), all-empty batch: final states are zero / copied."""
     _run_and_check([0, 0, 0], 2, 128, 128, 64, torch.bfloat16, s0_std=0.05, seed=5)
     _run_and_check([10, 0, 70], 2, 128, 128, 64, torch.bfloat16, s0_std=0.0, seed=6)
+
+
+def test_varlen_bench_batch_full():
+    """The packed batch bench.py times: the mid workload's batch rows 0 and 1
+    (16384 tokens, 16 heads) cut into sequences of 64..2047 tokens by the same
+    seeded draw; every output and final state of every sequence against the
+    oracle."""
+    w = inputs.WORKLOADS["mid"]
+    d = inputs.make_prefill(w)
+    T = 2 * w.T
+    rs = np.random.default_rng(11)
+    cuts = [0]
+    while cuts[-1] < T:
+        cuts.append(min(T, cuts[-1] + int(rs.integers(64, 2048))))
+    pk = {key: d[key][:2].reshape((T,) + tuple(d[key].shape[2:])).contiguous()
+          for key in ("q", "k", "v", "g", "beta")}
+    cu = torch.tensor(cuts, dtype=torch.int32)
+    print(f"varlen bench batch: {len(cuts) - 1} sequences, {T} tokens, {w.H} heads", flush=True)
+    o, S = chunk_fwd_varlen(*(pk[key].cuda() for key in ("q", "k", "v", "g", "beta")), cu.cuda(),
+                            chunk_size=w.C)
+    torch.cuda.synchronize()
+    o, S = o.cpu(), S.cpu()
+    worst_o = worst_s = 0.0
+    for i in range(len(cuts) - 1):
+        a, b = cuts[i], cuts[i + 1]
+        sl = lambda x: x[a:b][None]
+        o_ref, S_ref = oracle.recurrent(sl(pk["q"]), sl(pk["k"]), sl(pk["v"]), sl(pk["g"]), sl(pk["beta"]), None)
+        worst_o = max(worst_o, assert_close(f"seq {i} o", o[a:b][None], o_ref, TOL[torch.bfloat16]))
+        worst_s = max(worst_s, assert_close(f"seq {i} S", S[i:i + 1], S_ref, TOL[torch.bfloat16]))
+    print(f"  max err o {worst_o:.2e}  S {worst_s:.2e}", flush=True)
