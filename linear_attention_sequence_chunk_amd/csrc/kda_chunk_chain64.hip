@@ -350,62 +350,54 @@ __global__ __launch_bounds__(512, 1) void chunk_chain64_kernel(
 }
 
 // The maps launch with the whole augmented state [S | I] (DV + DK columns) in one
-// workgroup of 8 waves, register-tiled so that every S^T or W^T fragment read from
-// LDS feeds two MFMAs (one per row tile a wave holds):
-//   W = U - Wk S (64 x N):      wave w, row tiles 2(w%2), 2(w%2)+1, column tiles
-//                               NJ1 (w/2) .. +NJ1-1 (U taken as 0 on identity columns)
-//   S <- gam S + Kb^T W (DK x N): wave w, state row tiles 2(w%4), 2(w%4)+1, column
-//                               tiles NJ2 (w/4) .. +NJ2-1, fp32 in accumulators
-// Operands, MD chunks ahead: Wk, U and gam (read by several waves) come in once
-// per workgroup, 16 bytes a lane, and are copied to LDS one chunk before their
-// use (gam, read after the middle barrier, into one of two buffers by chunk
-// parity); each wave's Kb^T fragments go from memory straight into registers.
-// Two barriers per chunk, as in chunk_chain64_kernel.
+// workgroup of 8 waves.  Each wave owns 32 columns (waves 0 .. DV/32 - 1 value
+// columns, the next four the identity columns) and carries them through the
+// whole chunk step on its own:
+//   V = U - Wk S     (64 x 32; U taken as 0 on identity columns)
+//   S <- gam S + Kb^T V   (DK x 32, fp32 in accumulators)
+// so neither S nor V is exchanged between waves.  The B operand of each product
+// is built in registers from the accumulators of the previous one: a 16 x 16 fp32
+// accumulator gives lane l the rows 4(l/16) .. +3 of its column, so the B operand
+// of a 32-deep k-step is taken from two vertically adjacent tiles, lane l holding
+// rows {4(l/16) .. +3} and {16 + 4(l/16) .. +3}.  The A operands (Wk, Kb^T) are
+// read with the same order of k: two 8-byte pieces of their fragment-order rows.
+// Wk, Kb^T, U and gam are staged in LDS once per workgroup, double-buffered by
+// chunk parity, from registers loaded two chunks ahead.  One barrier per chunk.
 template <int DV>
 struct Maps64Cfg {
-    static constexpr int C = 64, DK = 128, N = DV + DK, NCT = N / 16, NVT = DV / 16;
-    static constexpr int NJ1 = NCT / 4, NJ2 = NCT / 2;
-    // padded bf16 rows of S^T and W^T: 40 and 8 elements, measured against the chain's
-    // 24 and 16 and other multiples of 8 (bank conflicts; 1M workload: chain stage
-    // 8.30-8.33 -> 8.02-8.05 ms, outputs bitwise unchanged)
-    static constexpr int LDK = DK + 40, LDC = C + 8;
+    static constexpr int C = 64, DK = 128;
+    static constexpr int NVW = DV / 32, NAW = NVW + DK / 32;     // value waves; waves holding columns
     static constexpr int NWK = C * DK * 2 / 16 / 512, NUV = C * DV * 2 / 16 / 512;   // 16-byte loads a lane
-    static constexpr size_t OFF_ST = 0;                                          // S^T [N][LDK]
-    static constexpr size_t OFF_WT = OFF_ST + size_t(N) * LDK * 2;               // W^T [N][LDC]
-    static constexpr size_t OFF_WK = OFF_WT + size_t(N) * LDC * 2;               // Wk, fragment order
-    static constexpr size_t OFF_U = OFF_WK + size_t(C) * DK * 2;                 // U, fragment order
-    static constexpr size_t OFF_G = OFF_U + size_t(C) * DV * 2;                 // gam [2][DK] fp32
-    static constexpr size_t TOTAL = OFF_G + size_t(2) * DK * 4;
-    static_assert(NCT % 4 == 0 && NWK >= 1 && NUV >= 1, "tile and load mapping");
+    static constexpr size_t OFF_WK = 0;                                  // Wk, fragment order
+    static constexpr size_t OFF_KB = OFF_WK + size_t(C) * DK * 2;       // Kb^T, fragment order
+    static constexpr size_t OFF_U = OFF_KB + size_t(DK) * C * 2;        // U, fragment order
+    static constexpr size_t OFF_G = OFF_U + size_t(C) * DV * 2;         // gam [DK] fp32
+    static constexpr size_t BUF = OFF_G + size_t(DK) * 4;
+    static constexpr size_t TOTAL = 2 * BUF;
+    static_assert(NAW <= 8 && NWK >= 1 && NUV >= 1, "wave and load mapping");
     static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
 // The first launch of the segmented chain: workgroups 0 .. nout - 1 run segment 0
 // of each (sequence, head) pair with its outputs (its start state is the call's
 // S0, and its end state is E_0); the others the maps of segments 1 .. nseg - 2.
-template <typename TOut, int DV, int MD>
+template <typename TOut, int DV>
 __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
     const bf16* __restrict__ ws_qt, const bf16* __restrict__ ws_wk, const bf16* __restrict__ ws_kb,
     const bf16* __restrict__ ws_p, const bf16* __restrict__ ws_u, const float* __restrict__ ws_gam,
     const float* __restrict__ s0, TOut* __restrict__ o, UnitMap um, Seg64 sg, long nout) {
     typedef Maps64Cfg<DV> Cfg;
     typedef Chain64Cfg<TOut, DV, DV> OCfg;
-    constexpr int C = Cfg::C, DK = Cfg::DK, NVT = Cfg::NVT, NJ1 = Cfg::NJ1, NJ2 = Cfg::NJ2;
-    constexpr int LDK = Cfg::LDK, LDC = Cfg::LDC, NWK = Cfg::NWK, NUV = Cfg::NUV;
+    constexpr int C = Cfg::C, DK = Cfg::DK, NVW = Cfg::NVW, NAW = Cfg::NAW, NWK = Cfg::NWK, NUV = Cfg::NUV;
+    constexpr size_t BUF = Cfg::BUF;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::TOTAL > OCfg::TOTAL ? Cfg::TOTAL : OCfg::TOTAL];
     if (blockIdx.x < nout) {
         chain64_run<TOut, DV, DV, CHAIN_SEG>(smem, blockIdx.x, 0, 0, 1, ws_qt, ws_wk, ws_kb, ws_p, ws_u, ws_gam,
                                              s0, o, nullptr, um, sg, nullptr, nullptr);
         return;
     }
-    bf16* sST = reinterpret_cast<bf16*>(smem + Cfg::OFF_ST);
-    bf16* sWT = reinterpret_cast<bf16*>(smem + Cfg::OFF_WT);
-    u32x4* sWk = reinterpret_cast<u32x4*>(smem + Cfg::OFF_WK);
-    u32x4* sU = reinterpret_cast<u32x4*>(smem + Cfg::OFF_U);
-    u32x4* sG = reinterpret_cast<u32x4*>(smem + Cfg::OFF_G);
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int fr = lane & 15, fk = 8 * (lane >> 4), fe = 4 * (lane >> 4);
+    const int fr = lane & 15, fg = lane >> 4;
     const long item = blockIdx.x - nout;
     const int nsegw = sg.nseg - 2;                   // segment 0 and the last segment need no map
     const long bh = item / nsegw;
@@ -416,164 +408,144 @@ __global__ __launch_bounds__(512, 1) void chain_maps64_kernel(
     const int NC = seg_chunks(sg, seg, sr.nchunks);
     auto unit_of = [&](int n) -> long { return unit_id(um, sq, h, c0 + (n < NC ? n : NC - 1), sr.chunk0); };
 
-    const int R1 = 2 * (wave & 1), J1 = NJ1 * (wave >> 1);   // phase 1 tiles
-    const int R2 = 2 * (wave & 3), J2 = NJ2 * (wave >> 2);   // phase 2 (state) tiles
-
-    // register slots, chunk m in slot m % MD (past the last chunk, the last one again)
-    u32x4 fW[MD][NWK], fV[MD][NUV];      // Wk and U, 16 bytes a lane of the whole chunk
-    u32x4 fG[MD];                        // gam, 16 bytes a lane (lane l: channels 4(l%32) ..)
-    u32x4 fK[MD][2][2];                  // Kb^T channel tiles R2, R2 + 1, 2 k-steps
-    auto load_shared = [&](auto DI, long ch) __attribute__((always_inline)) {
-        constexpr int d = DI;
+    // ---- staging: chunk m in register slot m % 2, then in LDS buffer m % 2
+    u32x4 fW[2][NWK], fK[2][NWK], fV[2][NUV], fG[2];
+    auto load = [&](auto SI, long ch) __attribute__((always_inline)) {
+        constexpr int sl = SI;
         const u32x4* a = reinterpret_cast<const u32x4*>(ws_wk + ch * (long)(C * DK)) + tid;
+        const u32x4* k = reinterpret_cast<const u32x4*>(ws_kb + ch * (long)(DK * C)) + tid;
         const u32x4* u = reinterpret_cast<const u32x4*>(ws_u + ch * (long)(C * DV)) + tid;
 #pragma unroll
-        for (int i = 0; i < NWK; ++i) fW[d][i] = a[512 * i];
+        for (int i = 0; i < NWK; ++i) { fW[sl][i] = a[512 * i]; fK[sl][i] = k[512 * i]; }
 #pragma unroll
-        for (int i = 0; i < NUV; ++i) fV[d][i] = u[512 * i];
-        fG[d] = reinterpret_cast<const u32x4*>(ws_gam + ch * (long)DK)[tid & (DK / 4 - 1)];
+        for (int i = 0; i < NUV; ++i) fV[sl][i] = u[512 * i];
+        fG[sl] = reinterpret_cast<const u32x4*>(ws_gam + ch * (long)DK)[tid & (DK / 4 - 1)];
     };
-    auto stage_shared = [&](auto DI, int buf) __attribute__((always_inline)) {
-        constexpr int d = DI;
+    auto stage = [&](auto SI) __attribute__((always_inline)) {
+        constexpr int sl = SI;
+        char* b = smem + sl * BUF;
 #pragma unroll
-        for (int i = 0; i < NWK; ++i) sWk[tid + 512 * i] = fW[d][i];
-#pragma unroll
-        for (int i = 0; i < NUV; ++i) sU[tid + 512 * i] = fV[d][i];
-        if (tid < DK / 4) sG[buf * (DK / 4) + tid] = fG[d];
-    };
-    auto load_own = [&](auto DI, long ch) __attribute__((always_inline)) {
-        constexpr int d = DI;
-        const u32x4* k = reinterpret_cast<const u32x4*>(ws_kb + ch * (long)(DK * C)) + lane;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            fK[d][i][0] = k[((R2 + i) * 2) * 64];
-            fK[d][i][1] = k[((R2 + i) * 2 + 1) * 64];
+        for (int i = 0; i < NWK; ++i) {
+            reinterpret_cast<u32x4*>(b + Cfg::OFF_WK)[tid + 512 * i] = fW[sl][i];
+            reinterpret_cast<u32x4*>(b + Cfg::OFF_KB)[tid + 512 * i] = fK[sl][i];
         }
+#pragma unroll
+        for (int i = 0; i < NUV; ++i) reinterpret_cast<u32x4*>(b + Cfg::OFF_U)[tid + 512 * i] = fV[sl][i];
+        if (tid < DK / 4) reinterpret_cast<u32x4*>(b + Cfg::OFF_G)[tid] = fG[sl];
     };
     if (NC > 0) {
-        static_for<MD>([&](auto DI) {
-            load_shared(DI, unit_of(DI));
-            load_own(DI, unit_of(DI));
-        });
-        stage_shared(std::integral_constant<int, 0>{}, 0);         // chunk 0
-        load_shared(std::integral_constant<int, 0>{}, unit_of(MD));
+        load(std::integral_constant<int, 0>{}, unit_of(0));
+        load(std::integral_constant<int, 1>{}, unit_of(1));
+        stage(std::integral_constant<int, 0>{});
+        load(std::integral_constant<int, 0>{}, unit_of(2));
     }
 
-    // state tiles (R2 + i, J2 + jt): rows 16(R2 + i) + fe + e, column 16(J2 + jt) + fr
-    // of [S | I]; value columns start from zero, identity columns from the identity
-    floatx4 accS[2][NJ2];
+    // ---- this wave's 32 columns of [S | I]: tiles (r, jt), rows 16r + 4(l/16) + e,
+    // column 32 w + 16 jt + l%16 of the value part (w < NVW) or of the identity part
+    const bool val = wave < NVW, act = wave < NAW;               // uniform per wave
+    const int cbase = 32 * (val ? wave : wave - NVW);
+    floatx4 accS[8][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < 8; ++r)
 #pragma unroll
-        for (int jt = 0; jt < NJ2; ++jt) {
-            const int col = 16 * (J2 + jt) + fr;
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * (R2 + i) + fe + e;
-                accS[i][jt][e] = col >= DV && row == col - DV ? 1.f : 0.f;
-            }
-        }
-    auto write_state_operand = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int jt = 0; jt < NJ2; ++jt) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = (bf16)accS[i][jt][e];
-                *reinterpret_cast<bf16x4*>(sST + (16 * (J2 + jt) + fr) * LDK + 16 * (R2 + i) + fe) = v4;
-            }
+            for (int e = 0; e < 4; ++e)
+                accS[r][jt][e] = !val && 16 * r + 4 * fg + e == cbase + 16 * jt + fr ? 1.f : 0.f;
+    // byte offset of lane l's first 8-byte A piece in a 1 KB fragment (the second is 512 bytes on)
+    const int aoff = (fr + 16 * (fg >> 1)) * 16 + 8 * (fg & 1);
+    auto afrag = [&](const char* f) __attribute__((always_inline)) -> bf16x8 {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(f + aoff), hi = *reinterpret_cast<const u32x2*>(f + aoff + 512);
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    write_state_operand();
 
-    // chunk n: Wk, U and gam in LDS, Kb^T in register slot d = n % MD
+    // chunk n, whose operands are in LDS buffer d = n % 2
     auto step = [&](auto DI, int n) __attribute__((always_inline)) {
-        constexpr int d = DI, d1 = (DI + 1) % MD;
-        __syncthreads();                                   // S^T, Wk, U and gam of chunk n in LDS
-
-        // ---- W = U - Wk S on tiles (R1 + i, J1 + jt), to LDS as W^T, in two
-        // halves of the column tiles (fewer live accumulators)
-        const u32x2* sU2 = reinterpret_cast<const u32x2*>(sU);
-        static_for<2>([&](auto HI) {
-            constexpr int NH = NJ1 / 2 + (HI == 0 ? NJ1 % 2 : 0), JH = HI == 0 ? 0 : NJ1 / 2 + NJ1 % 2;
-            floatx4 acc[2][NH];
+        constexpr int d = DI, d1 = 1 - DI;
+        __syncthreads();                                   // buffer d complete; buffer d1 no longer read
+        stage(std::integral_constant<int, d1>{});          // chunk n + 1
+        load(std::integral_constant<int, d1>{}, unit_of(n + 3));
+        if (!act) return;
+        const char* b = smem + d * BUF;
+        // V = U - Wk S: accumulators start from U (value columns) and add Wk (-S)
+        floatx4 accV[4][2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int R = 0; R < 4; ++R)
 #pragma unroll
-                for (int jt = 0; jt < NH; ++jt) acc[i][jt] = zero4();
+            for (int jt = 0; jt < 2; ++jt) {
+                accV[R][jt] = zero4();
+                if (val) {
+                    const bf16x4 uu = *reinterpret_cast<const bf16x4*>(
+                        b + Cfg::OFF_U + ((R * (DV / 16) + 2 * wave + jt) * 64 + lane) * 8);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 fa0 = __builtin_bit_cast(bf16x8, sWk[(R1 * 4 + s) * 64 + lane]);
-                const bf16x8 fa1 = __builtin_bit_cast(bf16x8, sWk[((R1 + 1) * 4 + s) * 64 + lane]);
-#pragma unroll
-                for (int jt = 0; jt < NH; ++jt) {
-                    const bf16x8 fb =
-                        *reinterpret_cast<const bf16x8*>(sST + (16 * (J1 + JH + jt) + fr) * LDK + 32 * s + fk);
-                    acc[0][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, fb, acc[0][jt], 0, 0, 0);
-                    acc[1][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, fb, acc[1][jt], 0, 0, 0);
+                    for (int e = 0; e < 4; ++e) accV[R][jt][e] = (float)uu[e];
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 bs[2];
 #pragma unroll
-                for (int jt = 0; jt < NH; ++jt) {
-                    const int J = J1 + JH + jt;
-                    bf16x4 uu{};
-                    if (J < NVT) uu = __builtin_bit_cast(bf16x4, sU2[((R1 + i) * NVT + J) * 64 + lane]);   // wave-uniform
-                    bf16x4 w4;
+            for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w4[e] = (bf16)((float)uu[e] - acc[i][jt][e]);
-                    *reinterpret_cast<bf16x4*>(sWT + (16 * J + fr) * LDC + 16 * (R1 + i) + fe) = w4;
+                for (int e = 0; e < 4; ++e) {
+                    bs[jt][e] = (bf16)(-accS[2 * s][jt][e]);
+                    bs[jt][4 + e] = (bf16)(-accS[2 * s + 1][jt][e]);
                 }
-        });
-        __syncthreads();                                   // W^T complete; Wk and U of chunk n read
-
-        // ---- S <- gam S + Kb^T W on tiles (R2 + i, J2 + jt)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const floatx4 gm = __builtin_bit_cast(floatx4, sG[(n & 1) * (DK / 4) + (R2 + i) * 4 + (lane >> 4)]);
-#pragma unroll
-            for (int jt = 0; jt < NJ2; ++jt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) accS[i][jt][e] *= gm[e];
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const bf16x8 fk0 = __builtin_bit_cast(bf16x8, fK[d][0][s]), fk1 = __builtin_bit_cast(bf16x8, fK[d][1][s]);
-#pragma unroll
-            for (int jt = 0; jt < NJ2; ++jt) {
-                const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sWT + (16 * (J2 + jt) + fr) * LDC + 32 * s + fk);
-                accS[0][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk0, fb, accS[0][jt], 0, 0, 0);
-                accS[1][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk1, fb, accS[1][jt], 0, 0, 0);
+            for (int R = 0; R < 4; ++R) {
+                const bf16x8 fa = afrag(b + Cfg::OFF_WK + (R * 4 + s) * 1024);
+                accV[R][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, bs[0], accV[R][0], 0, 0, 0);
+                accV[R][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, bs[1], accV[R][1], 0, 0, 0);
             }
         }
-        write_state_operand();                             // read only after the next barrier
-        load_own(DI, unit_of(n + MD));
-        stage_shared(std::integral_constant<int, d1>{}, (n + 1) & 1);   // chunk n + 1, read after the next barrier
-        load_shared(std::integral_constant<int, d1>{}, unit_of(n + 1 + MD));
+        // S <- gam S + Kb^T V
+        bf16x8 bv[2][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bv[s][jt][e] = (bf16)accV[2 * s][jt][e];
+                    bv[s][jt][4 + e] = (bf16)accV[2 * s + 1][jt][e];
+                }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const floatx4 gm = *reinterpret_cast<const floatx4*>(b + Cfg::OFF_G + (16 * r + 4 * fg) * 4);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) accS[r][jt][e] *= gm[e];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 fa = afrag(b + Cfg::OFF_KB + (r * 2 + s) * 1024);
+                accS[r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, bv[s][0], accS[r][0], 0, 0, 0);
+                accS[r][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, bv[s][1], accS[r][1], 0, 0, 0);
+            }
     };
-    // whole rounds of MD chunks, then the last NC % MD
+    // pairs of chunks (slot and buffer parities as constants), then an odd last one
     int n0 = 0;
-    for (; n0 + MD <= NC; n0 += MD) static_for<MD>([&](auto DI) { step(DI, n0 + DI); });
-    static_for<MD>([&](auto DI) {
-        if (n0 + DI < NC) step(DI, n0 + DI);
-    });
+    for (; n0 + 2 <= NC; n0 += 2) {
+        step(std::integral_constant<int, 0>{}, n0);
+        step(std::integral_constant<int, 1>{}, n0 + 1);
+    }
+    if (n0 < NC) step(std::integral_constant<int, 0>{}, n0);
 
     // E (value columns) and M (identity columns)
-    float* E = sg.E + (bh * sg.nseg + seg) * (long)(DK * DV);
-    float* M = sg.M + (bh * sg.nseg + seg) * (long)(DK * DK);
+    if (!act) return;
+    float* dst = val ? sg.E + (bh * sg.nseg + seg) * (long)(DK * DV)
+                     : sg.M + (bh * sg.nseg + seg) * (long)(DK * DK);
+    const int ld = val ? DV : DK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < 8; ++r)
 #pragma unroll
-        for (int jt = 0; jt < NJ2; ++jt) {
-            const int col = 16 * (J2 + jt) + fr;
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * (R2 + i) + fe + e;
-                if (col >= DV) M[row * (long)DK + col - DV] = accS[i][jt][e];
-                else E[row * (long)DV + col] = accS[i][jt][e];
-            }
-        }
+            for (int e = 0; e < 4; ++e)
+                dst[(16 * r + 4 * fg + e) * (long)ld + cbase + 16 * jt + fr] = accS[r][jt][e];
 }
 
 // Start states of the segments from their maps: Sst_0 = S0 (zeros when NULL),
@@ -671,7 +643,7 @@ static hipError_t launch_chain64(const ChunkArgs& a) {
         // every segment's whole augmented state is one workgroup, so its Wk and
         // Kb^T are fetched once
         const long nwg = bh + bh * (plan.nseg - 2);
-        hipLaunchKernelGGL((chain_maps64_kernel<TOut, DV, 2>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
+        hipLaunchKernelGGL((chain_maps64_kernel<TOut, DV>), dim3((unsigned)nwg), dim3(512), 0, a.stream,
                            (const bf16*)(ws + w.qt), (const bf16*)(ws + w.wk), (const bf16*)(ws + w.kb),
                            (const bf16*)(ws + w.p), (const bf16*)(ws + w.u), (const float*)(ws + w.gam), a.s0,
                            (TOut*)a.o, unit_map(a), sg, bh);
