@@ -37,6 +37,7 @@ XCDS = 8                    # GRBM_GUI_ACTIVE is summed over them
 KERNEL_SOURCES = {
     "chunk_intra64_kernel": ["kda_common.h", "kda_launch.h", "kda_chunk.h", "kda_chunk_intra.hip"],
     "chunk_chain64_kernel": ["kda_common.h", "kda_launch.h", "kda_chunk.h", "kda_chunk_chain64.hip"],
+    "chain_maps64_kernel": ["kda_common.h", "kda_launch.h", "kda_chunk.h", "kda_chunk_chain64.hip"],
 }
 
 
@@ -88,13 +89,11 @@ def measured_traffic(kernel):
     return None
 
 
-def measured_mfma(kernel, seconds):
-    """bf16 MFMA work and utilisation of one launch from the committed counter
-    summary (flops = 512 per MOPS unit; busy = MFMA-busy cycles over all SIMD
-    cycles), the rate at the live duration; None when absent or stale."""
+def counted_mfma(kernel):
+    """bf16 MFMA flops of one launch (512 per MOPS unit) and its MFMA-busy share of
+    all SIMD cycles, from the committed counter summary; None when absent or stale."""
     if kernel not in KERNEL_SOURCES or not os.path.exists(MFMA_FILE):
         return None
-    src = os.path.relpath(MFMA_FILE, ROOT)
     digest = source_digest(KERNEL_SOURCES[kernel])
     with open(MFMA_FILE) as f:
         for line in f:
@@ -106,11 +105,21 @@ def measured_mfma(kernel, seconds):
                 continue
             flops = 512.0 * float(kv["mops_bf16"])
             busy = float(kv["busy_cycles"]) / (float(kv["gui_active"]) / XCDS * SIMDS)
-            tflops = flops / seconds / 1e12
-            return {"kernel": kernel, "flops_per_launch": round(flops), "tflops": round(tflops, 1),
-                    "frac_bf16_peak": round(tflops / MFMA_PEAK_TFLOPS, 4), "busy_pct": round(100 * busy, 2),
-                    "source": src}
+            return flops, busy
     return None
+
+
+def measured_mfma(kernel, seconds):
+    """bf16 MFMA work and utilisation of one launch from the committed counter
+    summary, the rate at the live duration; None when absent or stale."""
+    c = counted_mfma(kernel)
+    if c is None:
+        return None
+    flops, busy = c
+    tflops = flops / seconds / 1e12
+    return {"kernel": kernel, "flops_per_launch": round(flops), "tflops": round(tflops, 1),
+            "frac_bf16_peak": round(tflops / MFMA_PEAK_TFLOPS, 4), "busy_pct": round(100 * busy, 2),
+            "source": os.path.relpath(MFMA_FILE, ROOT)}
 
 
 def mfma_summary(names, t_intra, t_chain, t_step):
@@ -125,10 +134,21 @@ def mfma_summary(names, t_intra, t_chain, t_step):
 
 
 def mfma_summary_segmented(t_intra, t_step):
-    """bf16 MFMA work of the intra kernel from the committed counters when the
-    chain runs in segments (its kernels have no counter lines of their own)."""
+    """bf16 MFMA work when the chain runs in segments: the intra kernel at its live
+    duration, the chain's first launch (segment 0 and the maps) and outputs launch
+    from their counters, and all three over the live step time; None when absent or stale."""
     intra = measured_mfma("chunk_intra64_kernel", t_intra)
-    return None if intra is None else {"intra": intra}
+    maps, outs = counted_mfma("chain_maps64_kernel"), counted_mfma("chunk_chain64_kernel")
+    if intra is None:
+        return None
+    out = {"intra": intra}
+    if maps is not None and outs is not None:
+        flops = intra["flops_per_launch"] + maps[0] + outs[0]
+        out["chain"] = {"maps_flops_per_launch": round(maps[0]), "maps_busy_pct": round(100 * maps[1], 2),
+                        "outputs_flops_per_launch": round(outs[0]), "outputs_busy_pct": round(100 * outs[1], 2)}
+        out["step_tflops"] = round(flops / t_step / 1e12, 1)
+        out["step_frac_bf16_peak"] = round(flops / t_step / 1e12 / MFMA_PEAK_TFLOPS, 4)
+    return out
 
 
 def prefill_bytes_per_token_head(dk, dv, in_bytes, out_bytes):
