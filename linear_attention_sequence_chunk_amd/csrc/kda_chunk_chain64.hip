@@ -281,7 +281,8 @@ __device__ __forceinline__ void chain64_run(
         }
         write_state_operand();                                      // read only after the next barrier
         if (MODE != CHAIN_CKPT && !wW) {
-            // this wave's 16 x DVS output tile, through its own LDS rows, as 16-byte row pieces
+            // this wave's 16 x DVS output tile, through its own LDS rows, as 16-byte row
+            // pieces with streaming stores (no later kernel here reads o)
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
@@ -292,8 +293,8 @@ __device__ __forceinline__ void chain64_run(
                 const int r = u / PPR, jj = (u % PPR) * EO;
                 const int tt = (c0 + n) * C + R * 16 + r;
                 if (sr.tok_begin + tt < sr.tok_end)
-                    *reinterpret_cast<u32x4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj) =
-                        *reinterpret_cast<const u32x4*>(sO + r * DVS + jj);
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sO + r * DVS + jj),
+                        reinterpret_cast<u32x4*>(o + ((sr.tok_begin + tt) * H + h) * DV + j0 + jj));
             }
         }
         KDA_C64_PREFETCH_2(d, unit_of(n + D < NC ? n + D : NC - 1));

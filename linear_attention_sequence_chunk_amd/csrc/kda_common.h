@@ -96,6 +96,14 @@ template <> struct Vec8<bf16> {
         for (int i = 0; i < 8; ++i) v[i] = (bf16)in[i];
         *reinterpret_cast<bf16x8*>(p) = v;
     }
+    // the same as a streaming (nontemporal) store: for data read back only by a
+    // later launch, so that it leaves the caches while this kernel still runs
+    __device__ static inline void store_nt(bf16* p, const float* in) {
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (bf16)in[i];
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+    }
 };
 template <> struct Vec8<float> {
     __device__ static inline void load(const float* p, float* out) {
