@@ -6,9 +6,10 @@ A step is one kda_chunk_fwd call (intra-chunk stage + chain stage) over the
 1M-token prefill workload: B=1, H=16, T=1,048,576, d_k=d_v=128, C=64, bf16 q/k/v,
 fp32 g/beta and state, recurring address keys, fast/slow channel gates (seeded
 synthetic inputs, resident in HBM before timing).  Prints one JSON line.  The
-mid (B=4, H=16, T=8192, C=64) and long (B=1, H=32, T=65536, C=128) prefill
-workloads are timed as well ("workloads"), and the decode step (256 sequences x
-32 heads, in-place 128x128 fp32 states) is reported under "decode".
+same step with the log-gate in bf16 too is timed beside it ("bf16_log_gates"),
+the mid (B=4, H=16, T=8192, C=64) and long (B=1, H=32, T=65536, C=128) prefill
+workloads as well ("workloads"), and the decode step (256 sequences x 32 heads,
+in-place 128x128 fp32 states) is reported under "decode".
 """
 from __future__ import annotations
 
@@ -53,7 +54,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-extras", action="store_true",
-                   help="only the step (and decode): no gate-layout, fused, varlen or backward lines")
+                   help="only the step (and decode): no bf16-gate, gate-layout, fused, varlen or backward lines")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 4 GiB device copy (to scale FETCH_SIZE/WRITE_SIZE counters)")
     p.add_argument("--survey", action="store_true",
@@ -303,6 +304,8 @@ def main():
         out["mfma"] = mfma_summary_segmented(t_intra, ms_per_step / 1e3)
 
     out["gpu_clocks"] = gpu_clocks(torch, plan)
+    if not args.no_extras:
+        out["bf16_log_gates"] = bench_bf16_gates(torch, ChunkPlan, g, w, K, args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -389,6 +392,20 @@ def bench_workload(torch, inputs, ChunkPlan, w, dev, steps, warmup):
     del plan, g
     torch.cuda.empty_cache()
     return res
+
+
+def bench_bf16_gates(torch, ChunkPlan, g, w, steps, warmup):
+    """The same step with the log-gate stored in bf16 as well, so that every input
+    is bf16 (the kernels widen the gate to fp32 on load): 1028 instead of 1284
+    bytes read per token-head.  The gate values are the workload's, rounded."""
+    gb = g["g"].to(torch.bfloat16)
+    plan = ChunkPlan(g["q"], g["k"], g["v"], gb, g["beta"], g["S0"], chunk_size=w.C)
+    ms, intra, chain, _ = time_step(torch, plan, steps, warmup)
+    del plan, gb
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1),
+            "intra_ms": round(intra, 4), "chain_ms": round(chain, 4),
+            "note": "q, k, v and the log-gate g in bf16; beta and the state fp32"}
 
 
 def bench_gate_layouts(torch, ChunkPlan, g, w, steps, warmup):

@@ -197,6 +197,22 @@ def test_mid_workload(gates):
     _say(f"  oracle + comparison {time.perf_counter() - t0:.1f} s")
 
 
+def test_mid_workload_bf16_log_gates():
+    """The mid workload with every input in bf16, the log-gate too (the kernels
+    widen it to fp32 on load): against the oracle on all 64 sequences (the oracle
+    reads the stored bf16 gates exactly), and bitwise equal to the call with
+    those same gate values handed over in fp32."""
+    w = inputs.WORKLOADS["mid"]
+    d = inputs.make_prefill(w)
+    d["g"] = d["g"].to(torch.bfloat16)
+    dg = cuda(d)
+    o, S = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], dg["S0"], chunk_size=w.C)
+    o32, S32 = chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"].float(), dg["beta"], dg["S0"], chunk_size=w.C)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o32) and torch.equal(S, S32), "bf16 gates differ from the same gates in fp32"
+    check(d, o.cpu(), S.cpu(), TOL[torch.bfloat16], tag="mid/bf16 log-gates")
+
+
 def test_long_workload():
     """B=1 H=32 T=65536 d=128 C=128 bf16, fast/slow channel gates, S0 ~ N(0,0.01);
     the oracle checks every output and final state of all 32 heads."""
