@@ -927,7 +927,7 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * R + 4 * kg + e;
-                if (valid(r)) dv[grow(r) * DV + 16 * J + lr] = sBeta[r] * acc[e];
+                if (valid(r)) __builtin_nontemporal_store(sBeta[r] * acc[e], dv + grow(r) * DV + 16 * J + lr);
             }
         }
     }
@@ -1166,9 +1166,9 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
                 const float dK = E * dKt + F * dKb + XA[e] + YA[e] + YP[e], dQ = E * dQt + XP[e];
                 dGv[e] = E * kc * dKt + E * qc * dQt - F * kc * dKb + kc * XA[e] - kc * YA[e] + qc * XP[e] -
                          kc * YP[e];
-                if (valid(r)) {
-                    dq[grow(r) * DK + cw] = dQ;
-                    dk[grow(r) * DK + cw] = dK;
+                if (valid(r)) {                    // gradients: streaming stores (nothing here reads them)
+                    __builtin_nontemporal_store(dQ, dq + grow(r) * DK + cw);
+                    __builtin_nontemporal_store(dK, dk + grow(r) * DK + cw);
                 }
             }
             // suffix sums of dG over this block's rows (4 in the lane, then the row
@@ -1187,7 +1187,7 @@ __global__ __launch_bounds__(DK * 4, 1) void chunk_bwd_intra_kernel(
                 const int r = 16 * R + 4 * kg + e;
                 const float val = base + sfx[e];
                 if (gate == GATE_CHANNEL) {
-                    if (valid(r)) dg[grow(r) * DK + cw] = (floored >> (4 * R + e)) & 1u ? 0.f : val;
+                    if (valid(r)) __builtin_nontemporal_store((floored >> (4 * R + e)) & 1u ? 0.f : val, dg + grow(r) * DK + cw);
                 } else {
                     const float hs = row_sum16(val);
                     if (gate == GATE_HEAD && lr == 0) sHd[wave * C + r] = hs;
