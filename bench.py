@@ -303,7 +303,7 @@ def main():
     if segmented and profiled:
         out["mfma"] = mfma_summary_segmented(t_intra, ms_per_step / 1e3)
 
-    out["gpu_clocks"] = gpu_clocks(torch, plan)
+    out["gpu_clocks"] = gpu_clocks(torch, plan, steps=min(5000, max(60, int(1200 / ms_per_step))))
     if not args.no_extras:
         out["bf16_log_gates"] = bench_bf16_gates(torch, ChunkPlan, g, w, K, args.warmup)
 
@@ -341,9 +341,9 @@ def main():
 
 def gpu_clocks(torch, plan, steps=60, samples=12):
     """GPU clocks while the step runs (amd-smi's library, in this process, after
-    the timed region): untimed steps are queued, and the graphics and memory
-    clocks are sampled only while the stream still has work pending.  None where
-    the library is missing."""
+    the timed region): about 1.2 s of untimed steps are queued, and the graphics
+    and memory clocks are sampled only while the stream still has work pending,
+    from 0.3 s after the queueing on.  None where the library is missing."""
     try:
         import amdsmi
     except Exception:
@@ -355,19 +355,22 @@ def gpu_clocks(torch, plan, steps=60, samples=12):
         stream = torch.cuda.current_stream()
         for _ in range(steps):
             plan.run()
-        time.sleep(0.05)
-        gfx, mem, sleep = [], [], []
+        time.sleep(0.3)          # both readings refresh about every 0.1 s: skip those taken while idle
+        gfx, mem, sleep, xcd = [], [], [], []
         while len(gfx) < samples and not stream.query():
             g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
             gfx.append(g["clk"])
             sleep.append(g.get("clk_deep_sleep"))
             mem.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"])
+            xcd.append(_current_gfx_mhz(amdsmi, h))
             time.sleep(0.02)
         torch.cuda.synchronize()
         return {"gfx_mhz_samples": gfx, "gfx_deep_sleep": sleep, "gfx_max_mhz": gmax,
                 "mem_mhz": max(mem) if mem else None,
-                "note": "sampled while untimed steps ran, after the timed region; each reading with "
-                        "the deep-sleep flag the management library reports beside it"}
+                "gfx_mhz_current_xcd_mean": xcd,
+                "note": "sampled while untimed steps ran, after the timed region: the clock the "
+                        "management library reports (with its deep-sleep flag), and the mean over "
+                        "the XCDs of the instantaneous clocks in its metrics table"}
     except Exception as e:                 # a clock reading must never fail the bench
         torch.cuda.synchronize()
         return {"error": type(e).__name__}
@@ -376,6 +379,20 @@ def gpu_clocks(torch, plan, steps=60, samples=12):
             amdsmi.amdsmi_shut_down()
         except Exception:
             pass
+
+
+def _current_gfx_mhz(amdsmi, h):
+    """Mean over the XCDs of the instantaneous graphics clocks in the metrics
+    table (entries the table marks as not available skipped), or None."""
+    try:
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+    except Exception:
+        return None
+    vals = m.get("current_gfxclks")
+    if not isinstance(vals, (list, tuple)):
+        vals = [m.get("current_gfxclk")]
+    vals = [v for v in vals if isinstance(v, (int, float)) and 0 < v < 0xFFFF]
+    return round(sum(vals) / len(vals)) if vals else None
 
 
 def bench_workload(torch, inputs, ChunkPlan, w, dev, steps, warmup):
