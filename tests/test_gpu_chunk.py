@@ -239,7 +239,11 @@ def test_1m_token_workload():
         the two calls cut the sequence into different segments).
     (iii) The oracle follows 2 sampled heads over all 1,048,576 tokens on 4
         sampled value columns (columns of the recurrence are independent), from
-        inputs regenerated on the host."""
+        inputs regenerated on the host.
+    (iv) The same call with the log-gates stored in bf16 (every input bf16):
+        bitwise equal to the call with those gate values in fp32, and its final
+        state and last 16,384 outputs against the oracle from the GPU state at
+        T-16384 of the bf16-gate split call, as in (i)."""
     w = inputs.WORKLOADS["1m"]
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
     dev = "cuda:0"
@@ -290,6 +294,22 @@ def test_1m_token_workload():
     eo = assert_close("1m o", og, o_ref, tol)
     es = assert_close("1m S", Sg, S_ref, tol)
     _say(f"  1m: max err o {eo:.2e}  S {es:.2e}")
+
+    _say("1m workload: bf16 log-gates")
+    del o, S, o1, o2, S2
+    gb = g.to(torch.bfloat16)
+    ob, Sb = chunk_fwd(q, k, v, gb, beta, None, chunk_size=w.C)
+    ob32, Sb32 = chunk_fwd(q, k, v, gb.float(), beta, None, chunk_size=w.C)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, ob32) and torch.equal(Sb, Sb32), "bf16 gates differ from the same gates in fp32"
+    del ob32, Sb32
+    _, Sb_mid = chunk_fwd(q[:, :T1], k[:, :T1], v[:, :T1], gb[:, :T1], beta[:, :T1], None, chunk_size=w.C)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.recurrent(tail_in["q"], tail_in["k"], tail_in["v"], tail_in["g"].to(torch.bfloat16),
+                                    tail_in["beta"], Sb_mid.cpu())
+    e = [assert_close("1m bf16-gate tail o", ob[:, T1:].cpu(), o_ref, tol),
+         assert_close("1m bf16-gate S_T", Sb.cpu(), S_ref, tol)]
+    _say("  1m bf16 log-gates, tail: max err o {:.2e} S {:.2e}".format(*e))
 
 
 def test_decode_steps_match_prefill():
