@@ -143,6 +143,10 @@ int kda_chunk_size_used(int dk, int dv, int in_dtype, int C, int backward);
  * Intermediate values use bf16 MFMA operands with fp32 accumulation when
  * in_dtype is BF16, fp32 MFMA operands when in_dtype is F32; the state is
  * carried in fp32.  Log-gates below -20 are treated as -20 (alpha >= 2e-9).
+ * A call of 2^31 or more (chunk, head) units, B * ceil(T/C) * H (packed
+ * batches: (ceil(T/C) + N) * H, with C the chunk that runs), returns
+ * KDA_ERR_SHAPE; the kernels index units with 32-bit arithmetic.  The same
+ * limit holds for every kda_chunk_* call, the backward ones included.
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v,
                   const float *g, const float *beta,

@@ -105,6 +105,15 @@ size_t esize(int d) { return d == KDA_BF16 ? 2 : 4; }
 int fwd_chunk(int C, int dk, int in_dtype) { return C == 128 && (in_dtype != KDA_BF16 || dk == 128) ? 64 : C; }
 int bwd_chunk(int C) { return C == 128 ? 64 : C; }
 
+// (chunk, head) units of a call: the kernels index them with 32-bit arithmetic,
+// so a call has fewer than 2^31 of them (72.5 KB of workspace each at d = 128,
+// far beyond any device's memory well before that)
+bool units_ok(bool packed, int B, int N, int T, int H, int C) {
+    const size_t nc = ((size_t)T + C - 1) / C;
+    const size_t units = (packed ? nc + (size_t)N : (size_t)B * nc) * (size_t)H;
+    return units < (size_t(1) << 31);
+}
+
 int validate_chunk(const ChunkCall& c) {
     if (c.B < 0 || c.T < 0 || c.H < 0 || c.N < 0) return KDA_ERR_SHAPE;
     if (!dtype_ok(c.in_dtype) || !dtype_ok(c.out_dtype) || !gate_ok(c.gate) || !pre_ok(c.pre))
@@ -112,6 +121,7 @@ int validate_chunk(const ChunkCall& c) {
     if ((c.dk != 64 && c.dk != 128) || (c.dv != 64 && c.dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (c.C != 16 && c.C != 32 && c.C != 64 && c.C != 128) return KDA_ERR_UNSUPPORTED;
     if (!kda::chunk_supported(c.dk, c.dv, c.C, c.in_dtype == KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if (!units_ok(c.packed, c.B, c.N, c.T, c.H, c.C)) return KDA_ERR_SHAPE;
 
     // token rows: [B,T,H] (fixed-length) or [T,H] (packed); states: [B,H] or [N,H]
     const size_t tok = (size_t)(c.packed ? 1 : c.B) * c.T * c.H;
@@ -295,6 +305,7 @@ int run_bwd(BwdCall c) {
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
     const bool bf = c.in_dtype == KDA_BF16;
     if (!kda::bwd_supported(dk, dv, c.C, bf) || !kda::chunk_supported(dk, dv, c.C, bf)) return KDA_ERR_UNSUPPORTED;
+    if (!units_ok(c.packed, c.B, c.N, c.T, c.H, c.C)) return KDA_ERR_SHAPE;
     // token rows: [B,T,H] (fixed-length) or [T,H] (packed); states: [B,H] or [N,H]
     const long nseqh = (long)(c.packed ? c.N : c.B) * c.H;
     const size_t tok = (size_t)(c.packed ? 1 : c.B) * c.T * c.H, nst = (size_t)nseqh * dk * dv;

@@ -97,7 +97,7 @@ def call_chunk(a, fn="kda_chunk_fwd", gate=None):
 def test_chunk_validation_codes(fn):
     a = chunk_args()
     cases = [
-        (dict(B=-1), SHAPE), (dict(T=-5), SHAPE),
+        (dict(B=-1), SHAPE), (dict(T=-5), SHAPE), (dict(T=2**31 - 1, H=64), SHAPE),   # 2^31 (chunk, head) units
         (dict(dk=96), UNSUP), (dict(dv=32), UNSUP), (dict(C=48), UNSUP), (dict(C=256), UNSUP),
         (dict(ind=5), UNSUP), (dict(outd=-1), UNSUP),
         (dict(q=None), NULL), (dict(beta=None), NULL), (dict(o=None), NULL),
@@ -411,7 +411,7 @@ def test_backward_validation_codes():
         return L.kda_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], x["dO"], x["dST"],
                                x["dq"], x["dk"], x["dv"], x["dg"], x["dbeta"], x["dS0"], x["B"], x["T"],
                                x["H"], x["dkk"], x["dvv"], x["ind"], x["ws"], x["wsb"], None, x["C"], x["gate"])
-    cases = [(dict(T=-1), SHAPE), (dict(dkk=96), UNSUP), (dict(C=48), UNSUP), (dict(ind=7), UNSUP),
+    cases = [(dict(T=-1), SHAPE), (dict(T=2**31 - 1, H=64), SHAPE), (dict(dkk=96), UNSUP), (dict(C=48), UNSUP), (dict(ind=7), UNSUP),
              (dict(gate=5), UNSUP), (dict(dq=None), NULL), (dict(dO=None), NULL), (dict(dg=None), NULL),
              (dict(q=a["q"] + 8), MISAL), (dict(g=a["g"] + 4), MISAL), (dict(g=a["g"] + 8), MISAL),
              (dict(dbeta=a["dbeta"] + 2), MISAL),
