@@ -524,7 +524,7 @@ struct Intra64Cfg {
 
 // GEN: the backward pass's forward stage: the same workspace, plus the fp32
 // checkpoints T and A per unit.
-template <int DV, bool GEN>
+template <int DV, bool GEN, bool QKN>
 __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
     prep_half(std::integral_constant<int, 0>{});
     // q and k row norms (pre-processing): a token's 128 channels are spread over the
     // four lane groups of this wave and the partner wave (wave ^ 1)
-    const bool qknorm = gate & MODE_QK_L2NORM;
+    constexpr bool qknorm = QKN;                      // the MODE_QK_L2NORM flag, as a constant
     if (qknorm) {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -1196,7 +1196,11 @@ static hipError_t launch_intra64(const ChunkArgs& a) {
     if (GEN && (!a.ck_t || !a.ck_a)) return hipErrorInvalidValue;
     const WsLayout w = ws_layout_of(a);
     char* ws = (char*)a.ws;
-    hipLaunchKernelGGL((chunk_intra64_kernel<DV, GEN>), dim3((unsigned)nch), dim3(512), 0, a.stream,
+    // the in-kernel q, k normalisation as a template constant: the plain call
+    // carries no multiplies by 1 and no row sums
+    auto kernel = (a.gate | a.pre) & MODE_QK_L2NORM ? chunk_intra64_kernel<DV, GEN, true>
+                                                     : chunk_intra64_kernel<DV, GEN, false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nch), dim3(512), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta,
                        (bf16*)(ws + w.qt), (bf16*)(ws + w.wk), (bf16*)(ws + w.kb), (bf16*)(ws + w.p),
                        (void*)(ws + w.u), (float*)(ws + w.gam), unit_map(a), a.gate | a.pre, a.ck_t, a.ck_a);
