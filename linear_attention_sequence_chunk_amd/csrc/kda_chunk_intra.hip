@@ -469,19 +469,20 @@ __device__ __forceinline__ float row_prefix_sum(float x) {
     return x;
 }
 
-// Writes the 8 bf16 of x to rows row0 .. row0+7 of one column of a row-major LDS
-// array (a transpose), element (m + rot) & 7 in the m-th store.  Lanes whose rows
-// sit a multiple of 32 banks apart get different even rotations, so each store
-// instruction spreads them over different banks.
-__device__ __forceinline__ void store_column8(bf16* base, int ld, int row0, int col, u32x4 x, int rot) {
-    u32x4 y = x;                                   // rotate the packed pairs left by rot / 2
-    y = (rot & 2) ? u32x4{y[1], y[2], y[3], y[0]} : y;
-    y = (rot & 4) ? u32x4{y[2], y[3], y[0], y[1]} : y;
+// The transposed LDS arrays (rows of 64 positions, 16-byte units of 8) keep unit
+// u of row r at unit u ^ swz8(r): lanes whose rows sit a multiple of 32 banks
+// apart (rows 8 apart) then write different banks, with no data moved between
+// registers.  Readers apply the same swizzle.
+__device__ __forceinline__ int swz8(int row) { return 2 * ((row >> 3) & 3); }
+// Writes the 8 bf16 of x to rows row0 .. row0+7 (row0 a multiple of 8) of column
+// col of such an array (a transpose).
+__device__ __forceinline__ void store_column8(bf16* base, int ld, int row0, int col, u32x4 x) {
+    const int cs = (((col >> 3) ^ swz8(row0)) << 3) | (col & 7);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const unsigned int pr = y[m >> 1];
+        const unsigned int pr = x[m >> 1];
         const unsigned short hv = (unsigned short)((m & 1) ? (pr >> 16) : (pr & 0xFFFFu));
-        *reinterpret_cast<unsigned short*>(base + (row0 + ((m + rot) & 7)) * ld + col) = hv;
+        *reinterpret_cast<unsigned short*>(base + (row0 + m) * ld + cs) = hv;
     }
 }
 __device__ __forceinline__ u32x4 pack_bf16x8(const float* x) {
@@ -738,8 +739,8 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
                 kr[M] *= eb;
                 kf[M] *= er;
             });
-            store_column8(sKtT, LDT, c, t, pack_bf16x8(kr), 2 * (lane >> 4));
-            store_column8(sKbT, Cfg::LDP, c, t, pack_bf16x8(kf), 2 * (lane >> 4));
+            store_column8(sKtT, LDT, c, t, pack_bf16x8(kr));
+            store_column8(sKbT, Cfg::LDP, c, t, pack_bf16x8(kf));
             // fragment order: unit (row tile R, k-step c/32), lane = row%16 + 16 * ((c%32)/8)
             Vec8<bf16>::store_nt(gQt + ((R * 4 + (c >> 5)) * 64 + lane) * 8, o1);
         });
@@ -760,7 +761,8 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             for (int u = tid; u < DK * C / 8; u += NT) {
                 const int ctile = u >> 7, ks = (u >> 6) & 1, lf = u & 63;
                 __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(
-                    sKbT + (ctile * 16 + (lf & 15)) * Cfg::LDP + ks * 32 + 8 * (lf >> 4)), reinterpret_cast<u32x4*>(gKb) + u);
+                    sKbT + (ctile * 16 + (lf & 15)) * Cfg::LDP + 8 * ((ks * 4 + (lf >> 4)) ^ swz8(ctile * 16 + (lf & 15)))),
+                    reinterpret_cast<u32x4*>(gKb) + u);
             }
         }
         // A and P over this channel half (K = 64: two MFMA steps)
@@ -942,7 +944,7 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
 #pragma unroll
             for (int m = 0; m < 8; ++m) vv[it][m] = (bf16)0.f;
         }
-        store_column8(sVt, LDT, j, tv, __builtin_bit_cast(u32x4, vv[it]), 2 * (lane >> 4));
+        store_column8(sVt, LDT, j, tv, __builtin_bit_cast(u32x4, vv[it]));
     }
     __syncthreads();
     {
@@ -959,10 +961,11 @@ __global__ __launch_bounds__(512, 4) void chunk_intra64_kernel(
             for (int R2 = 0; R2 < 4; ++R2) acc[sct][R2] = zero4();
             if (ct < NCT) {
                 const bool isU = ct < NUT;
-                const bf16* bsrc = isU ? sVt + ct * 16 * LDT : sKtT + (ct - NUT) * 16 * LDT;
+                const int brow = (isU ? ct : ct - NUT) * 16 + r;      // row of V^T or (e^G k)^T
+                const bf16* bsrc = (isU ? sVt : sKtT) + brow * LDT;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += 32) {
-                    const bf16x8 fb = *reinterpret_cast<const bf16x8*>(bsrc + r * LDT + k0 + 8 * kg);
+                    const bf16x8 fb = *reinterpret_cast<const bf16x8*>(bsrc + 8 * (((k0 >> 3) + kg) ^ swz8(brow)));
 #pragma unroll
                     for (int R2 = 0; R2 < 4; ++R2) {
                         if (k0 >= 16 * (R2 + 1)) continue;              // T is lower triangular
